@@ -1,0 +1,190 @@
+/*
+ * chimera_mshortconv.h -- C ABI of the KDA + mShortConv forward for AMD MI355X (gfx950).
+ *
+ * The method is the sequence mixer of the Chimera visual diffusion backbone
+ * ("Chimera: Designing and Chinchilla-Scaling Hybrid Visual Diffusion
+ * Transformers", arXiv 2607.28611; page 1, section 3.3, Eq. 12-15, and
+ * section 3.4):
+ *
+ *   (Q, K, V) = mShortConv(W_qkv x)                                   Eq. 13
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T   Eq. 14
+ *   o_t = S_t^T q_t                       (inner term of Eq. 15)
+ *
+ * over one packed token stream: text tokens first, then visual tokens in
+ * time-first raster order (Eq. 12). This library computes the mShortConv and
+ * the recurrence with its readout; the projections around them are not part
+ * of it.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device memory; "host" is ordinary host
+ *    memory. The caller allocates and frees every buffer and owns the stream.
+ *    No *_fwd call allocates memory, synchronises the device or keeps state
+ *    between calls; calls are reentrant.
+ *  - Errors are returned as status codes; nothing aborts or throws across the
+ *    ABI. All arguments are checked before any launch; on an error nothing is
+ *    written. A failed kernel launch returns CHIMERA_ERR_HIP. A fault inside a
+ *    kernel surfaces at the caller's next synchronisation.
+ *  - Values are not checked on the device: NaN and Inf propagate.
+ *  - All tensors are dense, row-major, with the innermost index last.
+ */
+#ifndef CHIMERA_MSHORTCONV_H
+#define CHIMERA_MSHORTCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum chimera_status {
+  CHIMERA_OK = 0,
+  CHIMERA_ERR_NULL = 1,         /* a required pointer is NULL */
+  CHIMERA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or too large */
+  CHIMERA_ERR_DTYPE = 3,        /* unknown dtype */
+  CHIMERA_ERR_SEGMENTS = 4,     /* the segment table does not tile [0, T) or a grid is malformed */
+  CHIMERA_ERR_UNSUPPORTED = 5,  /* a valid request this build does not implement */
+  CHIMERA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than chimera_kda_workspace_size() */
+  CHIMERA_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed */
+} chimera_status;
+
+typedef enum chimera_dtype {
+  CHIMERA_F32 = 0,              /* IEEE binary32 */
+  CHIMERA_BF16 = 1              /* bfloat16: the upper half of binary32 */
+} chimera_dtype;
+
+typedef enum chimera_seg_kind {
+  CHIMERA_SEG_TEXT = 0,         /* causal 1D segment */
+  CHIMERA_SEG_IMAGE = 1,        /* one-frame grid: frames == 1 */
+  CHIMERA_SEG_VIDEO = 2         /* frames x height x width grid, time-first raster order */
+} chimera_seg_kind;
+
+/*
+ * One modality segment of the packed stream, covering tokens
+ * [start, start + length). Text: frames = height = width = 0. Image and video:
+ * length == frames * height * width, and grid point (i, j, k) (time, height,
+ * width) is token start + i*height*width + j*width + k (Eq. 12). Segments
+ * must be listed in increasing start order and tile [0, T) with no gap or
+ * overlap (Chimera page 1, section 3.2: text first, then the visual tokens).
+ */
+typedef struct chimera_segment {
+  int32_t kind;                 /* chimera_seg_kind */
+  int32_t frames;
+  int32_t height;
+  int32_t width;
+  int64_t start;
+  int64_t length;
+} chimera_segment;
+
+/* Taps of the short convolution (Chimera page 1, section 3.4; sizes are this
+ * library's reading of "short"): text uses CHIMERA_TEXT_TAPS taps, tap j
+ * reading the token j - 3 places earlier in the text segment; visual grids use
+ * a 3x3x3 kernel, tap kt*9 + kh*3 + kw reading grid offset (kt-2, kh-1, kw-1):
+ * causal in time (current and two earlier frames), symmetric in space. Taps
+ * outside the segment read zero. An image uses only the kt = 2 slice. */
+#define CHIMERA_TEXT_TAPS 4
+#define CHIMERA_VIS_TAPS 27
+
+/*
+ * chimera_mshortconv_index -- the neighbour table of a segment layout.
+ * Chimera page 1, section 3.3 Eq. 12 (raster order) and section 3.4
+ * (per-segment views, causal in time, zero padding at segment edges).
+ *
+ *   segs  host, nseg entries (see chimera_segment)
+ *   T     total tokens; the segments must tile [0, T)
+ *   idx   host int32 [T][27], written: source token of tap j for token p, or
+ *         -1 where the tap reads zero padding. Text rows fill taps 0..3 and
+ *         hold -1 in taps 4..26.
+ *
+ * Host only and synchronous. Returns CHIMERA_ERR_NULL, CHIMERA_ERR_SHAPE or
+ * CHIMERA_ERR_SEGMENTS on bad input (idx untouched).
+ */
+chimera_status chimera_mshortconv_index(const chimera_segment* segs, int32_t nseg, int64_t T,
+                                        int32_t* idx);
+
+/*
+ * chimera_mshortconv_index_device -- the same table, computed on the device
+ * by the address arithmetic the convolution kernel itself uses to find its
+ * neighbours. For checking that arithmetic bit for bit.
+ *
+ *   idx_dev  device int32 [T][27], written asynchronously on `stream`.
+ */
+chimera_status chimera_mshortconv_index_device(const chimera_segment* segs, int32_t nseg, int64_t T,
+                                               int32_t* idx_dev, hipStream_t stream);
+
+/*
+ * chimera_mshortconv_fwd -- modality-aware short convolution (Eq. 13;
+ * Chimera page 1, section 3.4; page 2, mShortConv paragraph).
+ *
+ *   x       device [B][T][C], dtype dt: the projected q|k|v of every token
+ *           (any channel count; the conv is depthwise)
+ *   y       device [B][T][C], dtype dt, written: y[b,p,c] = sum over taps of
+ *           w[c,tap] * x[b, neighbour(p,tap), c], accumulated in fp32 and
+ *           rounded once to dt. Must not alias x.
+ *   w_text  device fp32 [C][4]
+ *   w_vis   device fp32 [C][27], (kt, kh, kw) row-major
+ *   segs    host, nseg entries; the same layout for every batch item
+ *
+ * No bias, no activation. Asynchronous on `stream`. Requires C % 8 == 0.
+ */
+chimera_status chimera_mshortconv_fwd(const void* x, void* y, int64_t B, int64_t T, int64_t C,
+                                      chimera_dtype dt, const float* w_text, const float* w_vis,
+                                      const chimera_segment* segs, int32_t nseg, hipStream_t stream);
+
+/* Flags of chimera_kda_fwd. */
+#define CHIMERA_KDA_L2NORM_QK 1u   /* divide q and k by sqrt(sum of squares over d_k + 1e-6) per
+                                      (token, head) before the recurrence (Chimera page 1, Fig. 2:
+                                      the "L2" boxes between mShortConv and the recurrence) */
+#define CHIMERA_KDA_SEQUENTIAL 2u  /* use the token-by-token fp32 kernel for every shape */
+#define CHIMERA_KDA_NO_SPLIT 4u    /* chunked kernel without splitting the sequence into segments */
+
+/*
+ * chimera_kda_workspace_size -- bytes of device workspace chimera_kda_fwd
+ * needs for these sizes and flags (0 when it needs none). Returns 0 for
+ * invalid sizes as well; chimera_kda_fwd reports those.
+ */
+size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                  chimera_dtype dt, uint32_t flags);
+
+/*
+ * chimera_kda_fwd -- KDA forward: Eq. 14 and the readout o_t = S_t^T q_t
+ * (Chimera page 1, section 3.3; Eq. 14's parentheses as printed on page 2).
+ * The decay Diag(alpha_t) acts first; the erase and the write then use the
+ * decayed state; the readout uses the state after token t.
+ *
+ *   q, k    device [B][T][H][dk], dtype dt, consecutive tokens qkv_stride
+ *           elements apart (the [H][dk] block of one token is contiguous);
+ *           element (b, t, h, i) at base + (b*T + t)*qkv_stride + h*dk + i
+ *   v       device [B][T][H][dv], same token stride
+ *   qkv_stride  elements between tokens: H*dk for separate tensors, or the
+ *           channel count of a fused q|k|v tensor such as mshortconv's output
+ *   alpha   device [B][T][H][dk], dtype dt, values in (0, 1]: per-channel decay
+ *   beta    device [B][T][H], dtype dt, values in (0, 1): erase/write strength
+ *   S0      device fp32 [B][H][dk][dv], or NULL for a zero initial state
+ *   o       device [B][T][H][dv], dtype dt, written (fp32 accumulation, one rounding)
+ *   S_final device fp32 [B][H][dk][dv], written, or NULL
+ *   flags   CHIMERA_KDA_* bits
+ *   workspace  device, at least chimera_kda_workspace_size(...) bytes, or
+ *           NULL when that size is 0; contents on entry do not matter
+ *
+ * Supported: dk, dv in 1..256 for the token-by-token kernel (fp32 and bf16);
+ * the chunked MFMA kernel runs for bf16 with dk = dv = 128. alpha <= 0 is
+ * undefined. The chunked kernel factors the decay inside 16-token blocks; it
+ * stays finite while log(alpha) >= -11 for every token and channel.
+ * Asynchronous on `stream`; o and S_final must not alias any input.
+ */
+chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                               const void* alpha, const void* beta, const float* S0,
+                               void* o, float* S_final,
+                               int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                               chimera_dtype dt, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* chimera_status_string(chimera_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CHIMERA_MSHORTCONV_H */

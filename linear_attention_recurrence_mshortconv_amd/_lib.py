@@ -1,0 +1,197 @@
+"""ctypes binding of ``libchimera_mshortconv.so`` (argument marshalling only).
+
+Each function here has the name of the C entry point it calls without the
+``chimera_`` prefix. torch tensors supply device memory and the current HIP
+stream; every step of the computation runs in the library's kernels. If the
+library is not built this raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libchimera_mshortconv.so")
+
+F32, BF16 = 0, 1
+KDA_L2NORM_QK = 1
+KDA_SEQUENTIAL = 2
+KDA_NO_SPLIT = 4
+TEXT_TAPS, VIS_TAPS = 4, 27
+
+STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad dtype", 4: "bad segments",
+          5: "unsupported", 6: "workspace", 7: "hip error"}
+
+
+class ChimeraError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} returned {status} ({msg})")
+        self.status = status
+
+
+class SegmentStruct(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("frames", ctypes.c_int32), ("height", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("start", ctypes.c_int64), ("length", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m linear_attention_recurrence_mshortconv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    seg_p = ctypes.POINTER(SegmentStruct)
+    L.chimera_status_string.restype = ctypes.c_char_p
+    L.chimera_status_string.argtypes = [ctypes.c_int]
+    L.chimera_mshortconv_index.restype = ctypes.c_int
+    L.chimera_mshortconv_index.argtypes = [seg_p, i32, i64, vp]
+    L.chimera_mshortconv_index_device.restype = ctypes.c_int
+    L.chimera_mshortconv_index_device.argtypes = [seg_p, i32, i64, vp, vp]
+    L.chimera_mshortconv_fwd.restype = ctypes.c_int
+    L.chimera_mshortconv_fwd.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, seg_p, i32, vp]
+    L.chimera_kda_workspace_size.restype = sz
+    L.chimera_kda_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, u32]
+    L.chimera_kda_fwd.restype = ctypes.c_int
+    L.chimera_kda_fwd.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                  ctypes.c_int, u32, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().chimera_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise ChimeraError(fn, status, status_string(status))
+
+
+def segment_array(segments: Sequence) -> "ctypes.Array":
+    """Pack segment descriptions (objects with kind/start/length/frames/height/width, or dicts)."""
+    arr = (SegmentStruct * max(1, len(segments)))()
+    for i, s in enumerate(segments):
+        get = (lambda k, d=0: s.get(k, d)) if isinstance(s, dict) else (lambda k, d=0: getattr(s, k, d))
+        arr[i].kind = int(get("kind"))
+        arr[i].frames = int(get("frames"))
+        arr[i].height = int(get("height"))
+        arr[i].width = int(get("width"))
+        arr[i].start = int(get("start"))
+        arr[i].length = int(get("length"))
+    return arr
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def mshortconv_index(segments: Sequence, T: int) -> np.ndarray:
+    """Host neighbour table int32 [T, 27] (chimera_mshortconv_index)."""
+    idx = np.empty((max(T, 0), VIS_TAPS), dtype=np.int32)
+    segs = segment_array(segments)
+    _check("chimera_mshortconv_index",
+           lib().chimera_mshortconv_index(segs, len(segments), T, idx.ctypes.data if T > 0 else None))
+    return idx
+
+
+def mshortconv_index_device(segments: Sequence, T: int, device="cuda"):
+    """Device neighbour table int32 [T, 27] from the kernels' own arithmetic."""
+    import torch
+    idx = torch.full((max(T, 0), VIS_TAPS), -7, dtype=torch.int32, device=device)
+    segs = segment_array(segments)
+    _check("chimera_mshortconv_index_device",
+           lib().chimera_mshortconv_index_device(segs, len(segments), T, _ptr(idx) if T > 0 else None, _stream(idx)))
+    return idx
+
+
+def mshortconv_fwd(x, w_text, w_vis, segments: Sequence, out=None):
+    """y = mShortConv(x) for x [B, T, C] (bf16 or fp32) on the GPU (chimera_mshortconv_fwd)."""
+    import torch
+    assert x.is_cuda and x.is_contiguous() and x.dim() == 3
+    B, T, C = x.shape
+    w_text = w_text.to(device=x.device, dtype=torch.float32).contiguous()
+    w_vis = w_vis.to(device=x.device, dtype=torch.float32).contiguous()
+    y = torch.empty_like(x) if out is None else out
+    assert y.shape == x.shape and y.dtype == x.dtype and y.is_contiguous()
+    segs = segment_array(segments)
+    _check("chimera_mshortconv_fwd",
+           lib().chimera_mshortconv_fwd(_ptr(x), _ptr(y), B, T, C, _dtype_code(x), _ptr(w_text), _ptr(w_vis),
+                                        segs, len(segments), _stream(x)))
+    return y
+
+
+def kda_workspace_size(B, T, H, dk, dv, dtype_code: int, flags: int) -> int:
+    return int(lib().chimera_kda_workspace_size(B, T, H, dk, dv, dtype_code, flags))
+
+
+def _token_view_stride(t, B, T, H, d) -> int:
+    """Token stride of a [B, T, H, d] view whose [H, d] block per token is contiguous."""
+    assert t.shape == (B, T, H, d), (t.shape, (B, T, H, d))
+    s = t.stride()
+    if T > 1 or B > 1:
+        assert s[3] == 1 and s[2] == d and (B == 1 or s[0] == T * s[1]), s
+    return s[1] if T > 0 else H * d
+
+
+def kda_fwd(q, k, v, alpha, beta, S0=None, *, l2norm: bool = True, sequential: bool = False,
+            no_split: bool = False, out=None, want_state: bool = True, workspace=None):
+    """KDA forward on the GPU (chimera_kda_fwd).
+
+    q, k [B, T, H, dk], v [B, T, H, dv] with a shared token stride (views into a
+    fused q|k|v tensor are accepted), alpha [B, T, H, dk], beta [B, T, H], S0
+    fp32 [B, H, dk, dv] or None. Returns (o [B, T, H, dv], S_final or None).
+    """
+    import torch
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    stride = _token_view_stride(q, B, T, H, dk)
+    assert _token_view_stride(k, B, T, H, dk) == stride and _token_view_stride(v, B, T, H, dv) == stride
+    assert alpha.shape == (B, T, H, dk) and alpha.is_contiguous()
+    assert beta.shape == (B, T, H) and beta.is_contiguous()
+    dt = _dtype_code(k)
+    assert q.dtype == k.dtype == v.dtype == alpha.dtype == beta.dtype
+    flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0) | (KDA_NO_SPLIT if no_split else 0)
+    o = torch.empty((B, T, H, dv), dtype=k.dtype, device=k.device) if out is None else out
+    Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=k.device) if want_state else None
+    if S0 is not None:
+        assert S0.dtype == torch.float32 and S0.is_contiguous() and S0.shape == (B, H, dk, dv)
+    need = kda_workspace_size(B, T, H, dk, dv, dt, flags)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("chimera_kda_fwd",
+           lib().chimera_kda_fwd(_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o),
+                                 _ptr(Sf), B, T, H, dk, dv, dt, flags, _ptr(workspace), wbytes, _stream(k)))
+    return o, Sf
+
+
+def split_qkv(y, H: int, d: int):
+    """Views q, k, v [B, T, H, d] into a fused [B, T, 3*H*d] conv output (no copy)."""
+    B, T, C = y.shape
+    assert C == 3 * H * d
+    parts = y.view(B, T, 3, H, d)
+    return parts[:, :, 0], parts[:, :, 1], parts[:, :, 2]

@@ -1,0 +1,182 @@
+// C ABI of the library: argument checks, the host neighbour table, dispatch.
+// Nothing here throws; every error becomes a chimera_status before any launch.
+#include "chimera_mshortconv.h"
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+using chm::Seg;
+
+namespace {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 40;
+
+chimera_status hip_status(hipError_t e) { return e == hipSuccess ? CHIMERA_OK : CHIMERA_ERR_HIP; }
+
+// The segments must tile [0, T) in order (Chimera page 1, section 3.2: one
+// packed stream, text first then the visual tokens; section 3.4: each segment
+// is a separate view). Grids must match their lengths (Eq. 12).
+chimera_status check_segments(const chimera_segment* segs, int32_t nseg, int64_t T, bool* any_text,
+                              bool* any_vis) {
+  if (T < 0 || T > kMaxTokens || nseg < 0) return CHIMERA_ERR_SHAPE;
+  if (nseg > 0 && segs == nullptr) return CHIMERA_ERR_NULL;
+  if (T > 0 && nseg == 0) return CHIMERA_ERR_SEGMENTS;
+  int64_t next = 0;
+  *any_text = *any_vis = false;
+  for (int32_t i = 0; i < nseg; ++i) {
+    const chimera_segment& s = segs[i];
+    if (s.start != next || s.length < 1 || s.length > kMaxTokens) return CHIMERA_ERR_SEGMENTS;
+    if (s.kind == CHIMERA_SEG_TEXT) {
+      if (s.frames != 0 || s.height != 0 || s.width != 0) return CHIMERA_ERR_SEGMENTS;
+      *any_text = true;
+    } else if (s.kind == CHIMERA_SEG_IMAGE || s.kind == CHIMERA_SEG_VIDEO) {
+      if (s.frames < 1 || s.height < 1 || s.width < 1) return CHIMERA_ERR_SEGMENTS;
+      if (s.kind == CHIMERA_SEG_IMAGE && s.frames != 1) return CHIMERA_ERR_SEGMENTS;
+      const int64_t n = int64_t(s.frames) * s.height * s.width;   // each factor < 2^31
+      if (n != s.length) return CHIMERA_ERR_SEGMENTS;
+      *any_vis = true;
+    } else {
+      return CHIMERA_ERR_SEGMENTS;
+    }
+    next = s.start + s.length;
+  }
+  if (next != T) return CHIMERA_ERR_SEGMENTS;
+  return CHIMERA_OK;
+}
+
+Seg to_seg(const chimera_segment& s) {
+  Seg g;
+  g.start = s.start;
+  g.length = s.length;
+  g.kind = s.kind;
+  g.frames = s.frames;
+  g.height = s.height;
+  g.width = s.width;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* chimera_status_string(chimera_status s) {
+  switch (s) {
+    case CHIMERA_OK: return "ok";
+    case CHIMERA_ERR_NULL: return "a required pointer is NULL";
+    case CHIMERA_ERR_SHAPE: return "invalid size";
+    case CHIMERA_ERR_DTYPE: return "unknown dtype";
+    case CHIMERA_ERR_SEGMENTS: return "segment table does not tile [0, T) or a grid is malformed";
+    case CHIMERA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case CHIMERA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CHIMERA_ERR_HIP: return "HIP runtime or launch failure";
+  }
+  return "unknown status";
+}
+
+chimera_status chimera_mshortconv_index(const chimera_segment* segs, int32_t nseg, int64_t T, int32_t* idx) {
+  bool any_text, any_vis;
+  const chimera_status st = check_segments(segs, nseg, T, &any_text, &any_vis);
+  if (st != CHIMERA_OK) return st;
+  if (T > 0 && idx == nullptr) return CHIMERA_ERR_NULL;
+  if (T > (int64_t(1) << 31) / chm::kVisTaps) return CHIMERA_ERR_SHAPE;   // int32 table entries
+  for (int32_t i = 0; i < nseg; ++i) {
+    const Seg s = to_seg(segs[i]);
+    if (s.kind == chm::SEG_TEXT) {
+      for (int64_t p = s.start; p < s.start + s.length; ++p) {
+        int32_t* row = idx + p * chm::kVisTaps;
+        for (int j = 0; j < chm::kVisTaps; ++j)
+          row[j] = j < chm::kTextTaps ? (int32_t)chm::text_tap_source(s, p, j) : -1;
+      }
+      continue;
+    }
+    for (int64_t f = 0; f < s.frames; ++f)
+      for (int64_t h = 0; h < s.height; ++h)
+        for (int64_t w = 0; w < s.width; ++w) {
+          int32_t* row = idx + chm::raster_index(s, f, h, w) * chm::kVisTaps;
+          for (int kt = 0; kt < 3; ++kt)
+            for (int kh = 0; kh < 3; ++kh)
+              for (int kw = 0; kw < 3; ++kw)
+                row[kt * 9 + kh * 3 + kw] = (int32_t)chm::vis_tap_source(s, f, h, w, kt, kh, kw);
+        }
+  }
+  return CHIMERA_OK;
+}
+
+chimera_status chimera_mshortconv_index_device(const chimera_segment* segs, int32_t nseg, int64_t T,
+                                               int32_t* idx_dev, hipStream_t stream) {
+  bool any_text, any_vis;
+  const chimera_status st = check_segments(segs, nseg, T, &any_text, &any_vis);
+  if (st != CHIMERA_OK) return st;
+  if (T > 0 && idx_dev == nullptr) return CHIMERA_ERR_NULL;
+  if (T > (int64_t(1) << 31) / chm::kVisTaps) return CHIMERA_ERR_SHAPE;
+  for (int32_t i = 0; i < nseg; ++i) {
+    const hipError_t e = chm::launch_index_device(to_seg(segs[i]), T, idx_dev, stream);
+    if (e != hipSuccess) return CHIMERA_ERR_HIP;
+  }
+  return CHIMERA_OK;
+}
+
+chimera_status chimera_mshortconv_fwd(const void* x, void* y, int64_t B, int64_t T, int64_t C, chimera_dtype dt,
+                                      const float* w_text, const float* w_vis, const chimera_segment* segs,
+                                      int32_t nseg, hipStream_t stream) {
+  if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
+  if (B < 0 || C < 0) return CHIMERA_ERR_SHAPE;
+  bool any_text, any_vis;
+  const chimera_status st = check_segments(segs, nseg, T, &any_text, &any_vis);
+  if (st != CHIMERA_OK) return st;
+  if (B == 0 || T == 0 || C == 0) return CHIMERA_OK;
+  if (C % 8 != 0 || C > (int64_t(1) << 24)) return CHIMERA_ERR_SHAPE;
+  if (x == nullptr || y == nullptr) return CHIMERA_ERR_NULL;
+  if ((any_text && w_text == nullptr) || (any_vis && w_vis == nullptr)) return CHIMERA_ERR_NULL;
+  if (x == y) return CHIMERA_ERR_UNSUPPORTED;
+  for (int32_t i = 0; i < nseg; ++i) {
+    const hipError_t e = chm::launch_conv_segment(x, y, B, T, C, dt == CHIMERA_BF16, w_text, w_vis,
+                                                  to_seg(segs[i]), false, stream);
+    if (e != hipSuccess) return CHIMERA_ERR_HIP;
+  }
+  return CHIMERA_OK;
+}
+
+static bool kda_sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+  return B >= 0 && T >= 0 && H >= 0 && dk >= 1 && dk <= 256 && dv >= 1 && dv <= 256 && T <= kMaxTokens &&
+         B <= (int64_t(1) << 20) && H <= (int64_t(1) << 16);
+}
+
+size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                                  uint32_t flags) {
+  if (!kda_sizes_ok(B, T, H, dk, dv) || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
+  chm::KdaArgs a{};
+  a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.bf16 = dt == CHIMERA_BF16;
+  if ((flags & CHIMERA_KDA_SEQUENTIAL) || !chm::kda_chunked_supported(a) || B * T * H == 0) return 0;
+  return chm::kda_chunked_workspace(B, T, H, (flags & CHIMERA_KDA_NO_SPLIT) != 0);
+}
+
+chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
+                               const void* beta, const float* S0, void* o, float* S_final, int64_t B, int64_t T,
+                               int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
+  if (!kda_sizes_ok(B, T, H, dk, dv)) return CHIMERA_ERR_SHAPE;
+  if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL | CHIMERA_KDA_NO_SPLIT)) return CHIMERA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return CHIMERA_OK;
+  if (T > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || o == nullptr)
+      return CHIMERA_ERR_NULL;
+    if (qkv_stride < H * dk || qkv_stride < H * dv) return CHIMERA_ERR_SHAPE;
+  }
+  chm::KdaArgs a;
+  a.q = q; a.k = k; a.v = v; a.qkv_stride = qkv_stride; a.alpha = alpha; a.beta = beta;
+  a.S0 = S0; a.o = o; a.S_final = S_final;
+  a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
+  a.bf16 = dt == CHIMERA_BF16;
+  a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
+  const bool chunked = !(flags & CHIMERA_KDA_SEQUENTIAL) && chm::kda_chunked_supported(a) && T > 0;
+  if (!chunked) return hip_status(chm::launch_kda_sequential(a, stream));
+  const bool no_split = (flags & CHIMERA_KDA_NO_SPLIT) != 0;
+  const size_t need = chm::kda_chunked_workspace(B, T, H, no_split);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
+  return hip_status(chm::launch_kda_chunked(a, no_split, workspace, stream));
+}
+
+}  // extern "C"

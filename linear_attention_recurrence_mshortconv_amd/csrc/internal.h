@@ -1,0 +1,45 @@
+// Internal declarations shared by the C ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "grid.h"
+
+namespace chm {
+
+// ---- mShortConv -------------------------------------------------------------
+// y = mShortConv(x) for one segment, x/y [B][T][C] with C % 8 == 0.
+hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t T, int64_t C, bool bf16,
+                               const float* w_text, const float* w_vis, const Seg& seg,
+                               bool force_gather, hipStream_t stream);
+
+// Device-side neighbour table [T][27] for one segment (the conv kernels' arithmetic).
+hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream);
+
+// ---- KDA ----------------------------------------------------------------------
+struct KdaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t qkv_stride;   // elements between consecutive tokens of q, k, v
+  const void* alpha;    // [B][T][H][dk]
+  const void* beta;     // [B][T][H]
+  const float* S0;      // [B][H][dk][dv] or null
+  void* o;              // [B][T][H][dv]
+  float* S_final;       // [B][H][dk][dv] or null
+  int64_t B, T, H, dk, dv;
+  bool bf16;
+  bool l2norm;
+};
+
+// Token-by-token fp32 kernel: any dk, dv in 1..256.
+hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream);
+
+// Chunked MFMA path (bf16, dk = dv = 128).
+bool kda_chunked_supported(const KdaArgs& a);
+int64_t kda_chunked_segments(int64_t B, int64_t T, int64_t H, bool no_split);
+size_t kda_chunked_workspace(int64_t B, int64_t T, int64_t H, bool no_split);
+hipError_t launch_kda_chunked(const KdaArgs& a, bool no_split, void* workspace, hipStream_t stream);
+
+}  // namespace chm

@@ -1,0 +1,288 @@
+// Modality-aware short convolution (mShortConv) on gfx950.
+//
+// Chimera page 1, section 3.3 Eq. 13 (the conv is applied to q, k and v) and
+// section 3.4 (text: causal 1D depthwise along the text segment; visual: depthwise
+// 3D over (time, height, width), causal in time and symmetric in space, an image
+// being a one-frame video; each segment convolved on its own with zero padding;
+// results written back to their packed positions). Eq. 12 gives the raster
+// order of a grid inside the stream.
+//
+// Two kernels:
+//  * conv_gather_kernel: one thread = 8 channels of one token; every tap is a
+//    direct 16-byte (bf16) or 32-byte (fp32) load from the packed stream. Used
+//    for text segments and for fp32 data.
+//  * conv_tile_kernel (bf16 grids): a block owns a spatial tile (TR rows x TW
+//    columns) x a 64-channel slab, stages each frame's tile plus its one-token
+//    halo in LDS, and streams over frames with a 3-frame LDS ring for the
+//    causal time taps. A thread keeps its channels' weights in registers and
+//    slides a 3-row window down its column, so each staged value is read from
+//    LDS once per (kw) and feeds up to three output rows.
+#include "dtypes.h"
+#include "internal.h"
+
+namespace chm {
+namespace {
+
+// ---- generic gather kernel ---------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void conv_gather_kernel(const T* __restrict__ x, T* __restrict__ y,
+                                                         const float* __restrict__ w_text,
+                                                         const float* __restrict__ w_vis, int64_t Ttot,
+                                                         int64_t C, Seg seg) {
+  const int64_t C8 = C / 8;
+  const int64_t cg = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t local = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t b = blockIdx.z;
+  if (cg >= C8 || local >= seg.length) return;
+  const int64_t p = seg.start + local;
+  const int64_t c0 = cg * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  const T* xb = x + b * Ttot * C;
+  if (seg.kind == SEG_TEXT) {
+    for (int j = 0; j < kTextTaps; ++j) {
+      const int64_t src = text_tap_source(seg, p, j);
+      if (src < 0) continue;
+      float v[8];
+      load8(xb + src * C + c0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w_text[(c0 + i) * kTextTaps + j], v[i], acc[i]);
+    }
+  } else {
+    const int64_t hw = (int64_t)seg.height * seg.width;
+    const int64_t f = local / hw, h = (local / seg.width) % seg.height, w = local % seg.width;  // Eq. 12
+    for (int kt = 0; kt < 3; ++kt)
+      for (int kh = 0; kh < 3; ++kh)
+        for (int kw = 0; kw < 3; ++kw) {
+          const int64_t src = vis_tap_source(seg, f, h, w, kt, kh, kw);
+          if (src < 0) continue;
+          const int tap = kt * 9 + kh * 3 + kw;
+          float v[8];
+          load8(xb + src * C + c0, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(w_vis[(c0 + i) * kVisTaps + tap], v[i], acc[i]);
+        }
+  }
+  store8(y + b * Ttot * C + p * C + c0, acc);
+}
+
+// ---- tiled grid kernel (bf16) ----------------------------------------------------
+// NF: 1 for a one-frame grid (only the kt = 2 taps can be non-zero), 3 for video.
+// CPT: channels per thread (8 -> 16-byte accesses, 4 -> 8-byte accesses).
+// A block = TW columns x (64 / CPT) channel groups = TW*64/CPT threads, each
+// computing TR output rows of one column.
+template <int NF, int CPT, int TR, int TW>
+struct TileCfg {
+  static constexpr int kGroups = 64 / CPT;            // channel groups per 64-channel slab
+  static constexpr int kThreads = TW * kGroups;
+  static constexpr int kSR = TR + 2, kSC = TW + 2;    // staged rows / columns (with halo)
+  static constexpr int kSlots = kSR * kSC;            // tokens per staged frame tile
+  static constexpr int kItems = kSlots * kGroups;     // CPT-channel items per staged frame tile
+};
+
+template <int CPT> struct Vec;
+template <> struct Vec<8> { using T = uint4; };
+template <> struct Vec<4> { using T = uint2; };
+
+__device__ __forceinline__ void unpack(const uint4& u, float* v) {
+  v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+  v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+}
+__device__ __forceinline__ void unpack(const uint2& u, float* v) {
+  v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+}
+__device__ __forceinline__ void pack(uint4& u, const float* v) {
+  u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
+}
+__device__ __forceinline__ void pack(uint2& u, const float* v) {
+  u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
+}
+
+template <int NF, int CPT, int TR, int TW>
+__global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, const float* __restrict__ w_vis, int64_t Ttot,
+    int64_t C, Seg seg, int n_slab, int n_tw, int n_th, int n_fr, int frames_per_block, int n_logical) {
+  using Cfg = TileCfg<NF, CPT, TR, TW>;
+  using V = typename Vec<CPT>::T;
+  __shared__ V tile[NF][Cfg::kSlots][Cfg::kGroups];
+
+  const int lid = (int)xcd_contiguous_id(blockIdx.x, gridDim.x);
+  if (lid >= n_logical) return;
+  int r = lid;
+  const int tw = r % n_tw; r /= n_tw;
+  const int th = r % n_th; r /= n_th;
+  const int slab = r % n_slab; r /= n_slab;
+  const int fr = r % n_fr; r /= n_fr;
+  const int64_t b = r;
+
+  const int tid = threadIdx.x;
+  const int g = tid % Cfg::kGroups;              // channel group inside the slab
+  const int col = tid / Cfg::kGroups;            // tile column 0..TW-1
+  const int64_t c0 = (int64_t)slab * 64 + g * CPT;
+  const int64_t h0 = (int64_t)th * TR, w0 = (int64_t)tw * TW;
+  const uint16_t* xb = x + b * Ttot * C;
+  uint16_t* yb = y + b * Ttot * C;
+
+  // weights of this thread's channels: wr[kt'][kh][kw][ch], kt' over the used time taps
+  float wr[NF][3][3][CPT];
+#pragma unroll
+  for (int t = 0; t < NF; ++t)
+#pragma unroll
+    for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          const int kt = 3 - NF + t;
+          wr[t][kh][kw][i] = w_vis[(c0 + i) * kVisTaps + kt * 9 + kh * 3 + kw];
+        }
+
+  const int f_begin = fr * frames_per_block;
+  const int f_end = min(seg.frames, f_begin + frames_per_block);
+
+  // stage frame ff's tile (with its halo) into ring slot `slot`
+  auto stage = [&](int ff, int slot) {
+    for (int it = tid; it < Cfg::kItems; it += Cfg::kThreads) {
+      const int s = it / Cfg::kGroups, gg = it % Cfg::kGroups;
+      const int64_t hh = h0 + s / Cfg::kSC - 1, ww = w0 + s % Cfg::kSC - 1;
+      V val;
+      if (grid_inside(seg, ff, hh, ww)) {
+        val = *reinterpret_cast<const V*>(xb + raster_index(seg, ff, hh, ww) * C + (int64_t)slab * 64 + gg * CPT);
+      } else {
+        val = V{};
+      }
+      tile[slot][s][gg] = val;
+    }
+  };
+
+  if (NF == 3) {
+    for (int ff = max(0, f_begin - 2); ff < f_begin; ++ff) stage(ff, ff % 3);
+  }
+  for (int f = f_begin; f < f_end; ++f) {
+    __syncthreads();                                  // previous frame's reads are done
+    stage(f, NF == 3 ? f % 3 : 0);
+    __syncthreads();
+    float acc[TR][CPT];
+#pragma unroll
+    for (int rr = 0; rr < TR; ++rr)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) acc[rr][i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NF; ++t) {
+      const int kt = 3 - NF + t;
+      const int fsrc = f + kt - 2;
+      if (fsrc < 0) continue;                        // frames before the first read zero
+      const int slot = NF == 3 ? fsrc % 3 : 0;
+#pragma unroll
+      for (int ir = 0; ir < TR + 2; ++ir) {          // staged row ir feeds output rows ir-2..ir
+#pragma unroll
+        for (int kw = 0; kw < 3; ++kw) {
+          float v[CPT];
+          unpack(tile[slot][ir * Cfg::kSC + col + kw][g], v);
+#pragma unroll
+          for (int kh = 0; kh < 3; ++kh) {
+            const int orow = ir - kh;
+            if (orow < 0 || orow >= TR) continue;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) acc[orow][i] = fmaf(wr[t][kh][kw][i], v[i], acc[orow][i]);
+          }
+        }
+      }
+    }
+    const int64_t ww = w0 + col;
+#pragma unroll
+    for (int rr = 0; rr < TR; ++rr) {
+      const int64_t hh = h0 + rr;
+      if (hh < seg.height && ww < seg.width) {
+        V out;
+        pack(out, acc[rr]);
+        *reinterpret_cast<V*>(yb + raster_index(seg, f, hh, ww) * C + c0) = out;
+      }
+    }
+  }
+}
+
+__global__ void index_device_kernel(Seg seg, int32_t* __restrict__ idx) {
+  const int64_t local = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (local >= seg.length) return;
+  const int64_t p = seg.start + local;
+  int32_t* row = idx + p * kVisTaps;
+  if (seg.kind == SEG_TEXT) {
+    for (int j = 0; j < kVisTaps; ++j) row[j] = j < kTextTaps ? (int32_t)text_tap_source(seg, p, j) : -1;
+    return;
+  }
+  // the tile kernel's path: grid point of the output, then the staged neighbour
+  const int64_t hw = (int64_t)seg.height * seg.width;
+  const int64_t f = local / hw, h = (local / seg.width) % seg.height, w = local % seg.width;
+  for (int kt = 0; kt < 3; ++kt)
+    for (int kh = 0; kh < 3; ++kh)
+      for (int kw = 0; kw < 3; ++kw) {
+        const int64_t ff = f + kt - 2, hh = h + kh - 1, ww = w + kw - 1;
+        row[kt * 9 + kh * 3 + kw] = grid_inside(seg, ff, hh, ww) ? (int32_t)raster_index(seg, ff, hh, ww) : -1;
+      }
+}
+
+template <int NF, int CPT, int TR, int TW>
+hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
+                       const Seg& seg, hipStream_t stream) {
+  using Cfg = TileCfg<NF, CPT, TR, TW>;
+  const int n_slab = (int)(C / 64);
+  const int n_tw = (int)((seg.width + TW - 1) / TW);
+  const int n_th = (int)((seg.height + TR - 1) / TR);
+  // video: split the frames so that there are enough blocks to fill the chip
+  int fpb = seg.frames;
+  if (NF == 3) {
+    const int64_t per_frame_range = (int64_t)n_slab * n_tw * n_th * B;
+    const int64_t want = 2048;
+    int64_t nfr = (want + per_frame_range - 1) / per_frame_range;
+    if (nfr > seg.frames) nfr = seg.frames;
+    if (nfr < 1) nfr = 1;
+    fpb = (int)((seg.frames + nfr - 1) / nfr);
+    if (fpb < 8) fpb = 8 < seg.frames ? 8 : seg.frames;
+  }
+  const int n_fr = (seg.frames + fpb - 1) / fpb;
+  const int64_t n_logical = (int64_t)n_slab * n_tw * n_th * n_fr * B;
+  if (n_logical <= 0) return hipSuccess;
+  if (n_logical > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int64_t grid = (n_logical + 7) / 8 * 8;
+  hipLaunchKernelGGL((conv_tile_kernel<NF, CPT, TR, TW>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, stream, x, y,
+                     w_vis, Ttot, C, seg, n_slab, n_tw, n_th, n_fr, fpb, (int)n_logical);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, int64_t C, bool bf16,
+                               const float* w_text, const float* w_vis, const Seg& seg, bool force_gather,
+                               hipStream_t stream) {
+  if (seg.length == 0 || B == 0) return hipSuccess;
+  const bool tiled = bf16 && seg.kind != SEG_TEXT && C % 64 == 0 && !force_gather;
+  if (tiled) {
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    uint16_t* ys = static_cast<uint16_t*>(y);
+    if (seg.frames == 1) return launch_tile<1, 8, 8, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream);
+    return launch_tile<3, 4, 8, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream);
+  }
+  const dim3 grid((unsigned)((C / 8 + 63) / 64), (unsigned)((seg.length + 3) / 4), (unsigned)B);
+  if (grid.y > 0x7fffffffu || B > 65535) return hipErrorInvalidValue;
+  if (bf16) {
+    hipLaunchKernelGGL(conv_gather_kernel<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+                       static_cast<uint16_t*>(y), w_text, w_vis, Ttot, C, seg);
+  } else {
+    hipLaunchKernelGGL(conv_gather_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(x),
+                       static_cast<float*>(y), w_text, w_vis, Ttot, C, seg);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream) {
+  (void)T;
+  if (seg.length == 0) return hipSuccess;
+  const int64_t blocks = (seg.length + 255) / 256;
+  hipLaunchKernelGGL(index_device_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, seg, idx);
+  return hipGetLastError();
+}
+
+}  // namespace chm

@@ -1,0 +1,148 @@
+"""The C-ABI library on the host: exported symbols, the host neighbour table
+against the oracle (bit-exact), and argument checking (CPU only, no kernel runs)."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import neighbours_ref
+import linear_attention_recurrence_mshortconv_amd as chm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "chimera_mshortconv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(chimera_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    L = chm.lib()
+    names = _declared_functions()
+    assert "chimera_kda_fwd" in names and "chimera_mshortconv_fwd" in names and len(names) >= 6
+    out = subprocess.run(["nm", "-D", "--defined-only", chm.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (chimera_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_status_strings():
+    for s in range(8):
+        assert len(chm.status_string(s)) > 0
+    assert chm.status_string(0) == "ok"
+
+
+def _layouts():
+    out = [w.segments for w in wl.WORKLOADS]
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "neighbours_worked_example.json")))
+    out.append(tuple(wl.Segment(**{"kind": s["kind"], "start": s["start"], "length": s["length"],
+                                    "frames": s.get("frames", 0), "height": s.get("height", 0),
+                                    "width": s.get("width", 0)}) for s in g["layout"]))
+    rng = np.random.default_rng(1234)
+    for _ in range(25):                                   # random packed layouts
+        segs, start = [], 0
+        for _ in range(int(rng.integers(1, 6))):
+            kind = int(rng.integers(0, 3))
+            if kind == wl.TEXT:
+                n = int(rng.integers(1, 40))
+                segs.append(wl.Segment(wl.TEXT, start, n))
+            else:
+                F = 1 if kind == wl.IMAGE else int(rng.integers(1, 6))
+                Hh, Ww = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+                n = F * Hh * Ww
+                segs.append(wl.Segment(kind, start, n, F, Hh, Ww))
+            start += n
+        out.append(tuple(segs))
+    return out
+
+
+def test_host_index_bit_exact_against_oracle():
+    for segs in _layouts():
+        T = sum(s.length for s in segs)
+        got = chm.mshortconv_index(segs, T)
+        want = neighbours_ref(segs, T)
+        assert got.dtype == np.int32 and np.array_equal(got, want), segs[:3]
+
+
+def test_host_index_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "neighbours_worked_example.json")))
+    idx = chm.mshortconv_index(g["layout"], g["T"])
+    for pos, row in g["rows"].items():
+        assert idx[int(pos)].tolist() == row
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_segment_validation_errors():
+    L = chm.lib()
+    buf = np.zeros((64, 27), dtype=np.int32)
+    p = buf.ctypes.data
+    cases = [
+        ([dict(kind=0, start=1, length=4)], 5, 4),                      # does not start at 0
+        ([dict(kind=0, start=0, length=4)], 5, 4),                      # does not reach T
+        ([dict(kind=0, start=0, length=3), dict(kind=0, start=2, length=3)], 5, 4),   # overlap
+        ([dict(kind=1, start=0, length=6, frames=2, height=1, width=3)], 6, 4),       # image with 2 frames
+        ([dict(kind=2, start=0, length=7, frames=1, height=2, width=3)], 7, 4),       # length != grid
+        ([dict(kind=0, start=0, length=4, height=2)], 4, 4),            # text with a grid
+        ([dict(kind=9, start=0, length=4)], 4, 4),                      # unknown kind
+        ([dict(kind=0, start=0, length=0)], 0, 4),                      # empty segment
+    ]
+    for segs, T, want in cases:
+        arr = chm.segment_array(segs)
+        assert L.chimera_mshortconv_index(arr, len(segs), T, p) == want, segs
+        assert L.chimera_mshortconv_fwd(1, 2, 1, T, 8, 1, 3, 4, arr, len(segs), None) == want, segs
+    arr = chm.segment_array([dict(kind=0, start=0, length=4)])
+    assert L.chimera_mshortconv_index(arr, 1, 4, None) == 1               # null output
+    assert L.chimera_mshortconv_index(None, 1, 4, p) == 1                 # null table
+    assert L.chimera_mshortconv_index(arr, 1, -1, p) == 2                 # negative T
+    assert L.chimera_mshortconv_index(chm.segment_array([]), 0, 0, None) == 0   # empty stream is fine
+
+
+def test_conv_argument_errors():
+    L = chm.lib()
+    arr = chm.segment_array([dict(kind=0, start=0, length=4)])
+    assert L.chimera_mshortconv_fwd(1, 2, 1, 4, 8, 7, 3, 4, arr, 1, None) == 3       # dtype
+    assert L.chimera_mshortconv_fwd(1, 2, 1, 4, 12, 1, 3, 4, arr, 1, None) == 2      # C % 8
+    assert L.chimera_mshortconv_fwd(None, 2, 1, 4, 8, 1, 3, 4, arr, 1, None) == 1    # null x
+    assert L.chimera_mshortconv_fwd(1, 2, 1, 4, 8, 1, None, 4, arr, 1, None) == 1    # text weights
+    assert L.chimera_mshortconv_fwd(1, 1, 1, 4, 8, 1, 3, 4, arr, 1, None) == 5       # in place
+    assert L.chimera_mshortconv_fwd(1, 2, -1, 4, 8, 1, 3, 4, arr, 1, None) == 2      # negative B
+    assert L.chimera_mshortconv_fwd(1, 2, 0, 4, 8, 1, 3, 4, arr, 1, None) == 0       # empty batch: no-op
+    vis = chm.segment_array([dict(kind=1, start=0, length=4, frames=1, height=2, width=2)])
+    assert L.chimera_mshortconv_fwd(1, 2, 1, 4, 8, 1, 3, None, vis, 1, None) == 1    # visual weights
+
+
+def test_kda_argument_errors():
+    L = chm.lib()
+    args = lambda **kw: dict(dict(q=1, k=2, v=3, stride=256, a=4, b=5, S0=None, o=6, Sf=None, B=1, T=8, H=2,
+                                  dk=128, dv=128, dt=1, flags=1, ws=None, wsb=0), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.chimera_kda_fwd(a["q"], a["k"], a["v"], a["stride"], a["a"], a["b"], a["S0"], a["o"], a["Sf"],
+                                 a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["flags"], a["ws"], a["wsb"],
+                                 None)
+    assert call(dt=5) == 3
+    assert call(dk=0) == 2 and call(dv=300) == 2 and call(T=-1) == 2
+    assert call(q=None) == 1 and call(o=None) == 1 and call(b=None) == 1
+    assert call(stride=100) == 2                                        # stride below H*d
+    assert call(flags=64) == 5                                          # unknown flag
+    assert call(B=0) == 0 and call(H=0) == 0                            # nothing to do
+
+
+def test_workspace_size_rules():
+    n = chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
+    assert n >= 0
+    assert chm.kda_workspace_size(1, 256, 2, 32, 32, chm.F32, 0) == 0            # sequential path
+    assert chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_SEQUENTIAL) == 0
+    assert chm.kda_workspace_size(1, 10, 1, 0, 128, chm.BF16, 0) == 0            # invalid sizes

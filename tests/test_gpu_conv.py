@@ -1,0 +1,103 @@
+"""GPU parity of mShortConv and its device neighbour arithmetic (through the C ABI)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import neighbours_ref, conv_ref
+from tests.gpu_util import assert_close, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def chm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_recurrence_mshortconv_amd as m
+    m.lib()
+    return m
+
+
+def _mixed_layout():
+    # every kind; grids with ragged edges against the 8x32 / 8x16 tiles
+    S = wl.Segment
+    return (S(wl.TEXT, 0, 19), S(wl.IMAGE, 19, 37 * 45, 1, 37, 45), S(wl.TEXT, 19 + 1665, 5),
+            S(wl.VIDEO, 1689, 5 * 19 * 23, 5, 19, 23))
+
+
+def _layouts():
+    out = [_mixed_layout()] + [w.segments for w in wl.WORKLOADS]
+    S = wl.Segment
+    out.append((S(wl.VIDEO, 0, 1 * 1 * 1, 1, 1, 1),))                  # a one-token video
+    out.append((S(wl.IMAGE, 0, 1 * 70, 1, 1, 70), S(wl.TEXT, 70, 1)))  # one-row image, one-token text
+    return out
+
+
+def test_device_neighbour_arithmetic_bit_exact(chm):
+    for segs in _layouts():
+        T = sum(s.length for s in segs)
+        got = chm.mshortconv_index_device(segs, T).cpu().numpy()
+        assert np.array_equal(got, neighbours_ref(segs, T)), segs[:2]
+
+
+def _conv_bound(x, wt, wv, segs, dtype):
+    """Element-wise error bound: fp32 accumulation of up to 27 terms plus one
+    rounding to the output dtype (half an ulp: 2^-8 relative for bf16, 2^-24 for fp32)."""
+    ref = conv_ref(x, wt, wv, segs)
+    mag = conv_ref(np.abs(x), np.abs(wt), np.abs(wv), segs)
+    unit = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    return ref, unit * np.abs(ref) + 28 * 2.0 ** -24 * mag + 1e-30
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("C", [64, 192])
+def test_conv_parity_mixed_layout(chm, dtype, C):
+    segs = _mixed_layout()
+    T = sum(s.length for s in segs)
+    rng = np.random.default_rng(C)
+    x = rng.standard_normal((2, T, C)).astype(np.float32)
+    if dtype == "bf16":
+        x = wl.round_to_bf16(x)
+    wt = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    wv = (0.5 * rng.standard_normal((C, 27))).astype(np.float32)
+    import torch
+    y = chm.mshortconv_fwd(to_device(x, dtype), torch.from_numpy(wt), torch.from_numpy(wv), segs)
+    got = to_host(y)
+    ref, bound = _conv_bound(x, wt, wv, segs, dtype)
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), f"worst excess {np.max(err - bound):.3e}"
+    assert_close(got, ref, dtype, "conv")
+
+
+def test_conv_centred_delta_is_identity_on_gpu(chm):
+    import torch
+    segs = _mixed_layout()
+    T = sum(s.length for s in segs)
+    C = 128
+    x = wl.round_to_bf16(np.random.default_rng(3).standard_normal((1, T, C)).astype(np.float32))
+    wt = np.zeros((C, 4), np.float32); wt[:, 3] = 1
+    wv = np.zeros((C, 27), np.float32); wv[:, 22] = 1
+    y = chm.mshortconv_fwd(to_device(x, "bf16"), torch.from_numpy(wt), torch.from_numpy(wv), segs)
+    assert np.array_equal(to_host(y), x.astype(np.float64))
+
+
+@pytest.mark.parametrize("wi", [1, 2, 3, 4])
+def test_conv_full_workload_sampled_channels(chm, wi):
+    """Full-size workloads in the bench's launch configuration; the oracle
+    recomputes a sample of 64-channel slabs (q, k and v blocks of two heads)."""
+    import torch
+    w = wl.WORKLOADS[wi]
+    inp = wl.make_inputs(w)
+    x = inp["x"]
+    segs = inp["segments"]
+    y = chm.mshortconv_fwd(to_device(x, "bf16"), torch.from_numpy(inp["w_text"]), torch.from_numpy(inp["w_vis"]), segs)
+    HD = w.H * w.d
+    heads = [0, w.H - 1]
+    chans = np.concatenate([part * HD + h * w.d + np.arange(w.d) for part in range(3) for h in heads])
+    sub = chans[::4]                                         # every 4th channel of those blocks
+    got = to_host(y[:, :, torch.from_numpy(sub).to(y.device)])
+    ref, bound = _conv_bound(x[:, :, sub], inp["w_text"][sub], inp["w_vis"][sub], segs, "bf16")
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), f"worst excess {np.max(err - bound):.3e}"
+    assert_close(got, ref, "bf16", w.name)
