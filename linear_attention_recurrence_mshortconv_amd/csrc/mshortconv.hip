@@ -7,10 +7,12 @@
 // results written back to their packed positions). Eq. 12 gives the raster
 // order of a grid inside the stream.
 //
-// Two kernels:
+// Three kernels:
+//  * conv_text_kernel: text segments; a thread slides a 4-token window over 16
+//    tokens of 8 channels.
 //  * conv_gather_kernel: one thread = 8 channels of one token; every tap is a
 //    direct 16-byte (bf16) or 32-byte (fp32) load from the packed stream. Used
-//    for text segments and for fp32 data.
+//    for grids of fp32 data (and as the plain reference arrangement).
 //  * conv_tile_kernel (bf16 grids): a block owns a spatial tile (TR rows x TW
 //    columns) x a 64-channel slab, stages each frame's tile plus its one-token
 //    halo in LDS, and streams over frames with a 3-frame LDS ring for the
@@ -142,28 +144,41 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
   const int f_begin = fr * frames_per_block;
   const int f_end = min(seg.frames, f_begin + frames_per_block);
 
-  // stage frame ff's tile (with its halo) into ring slot `slot`
-  auto stage = [&](int ff, int slot) {
-    for (int it = tid; it < Cfg::kItems; it += Cfg::kThreads) {
+  // Staging of one frame's tile plus halo: every thread first loads its items
+  // into registers (all loads in flight together), then stores them to LDS.
+  constexpr int NIT = (Cfg::kItems + Cfg::kThreads - 1) / Cfg::kThreads;
+  V pre[NIT];
+  auto fetch = [&](int ff) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int it = tid + j * Cfg::kThreads;
       const int s = it / Cfg::kGroups, gg = it % Cfg::kGroups;
       const int64_t hh = h0 + s / Cfg::kSC - 1, ww = w0 + s % Cfg::kSC - 1;
-      V val;
-      if (grid_inside(seg, ff, hh, ww)) {
-        val = *reinterpret_cast<const V*>(xb + raster_index(seg, ff, hh, ww) * C + (int64_t)slab * 64 + gg * CPT);
-      } else {
-        val = V{};
-      }
-      tile[slot][s][gg] = val;
+      pre[j] = V{};
+      if (it < Cfg::kItems && grid_inside(seg, ff, hh, ww))
+        pre[j] = *reinterpret_cast<const V*>(xb + raster_index(seg, ff, hh, ww) * C + (int64_t)slab * 64 + gg * CPT);
+    }
+  };
+  auto commit = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int it = tid + j * Cfg::kThreads;
+      if (it < Cfg::kItems) tile[slot][it / Cfg::kGroups][it % Cfg::kGroups] = pre[j];
     }
   };
 
   if (NF == 3) {
-    for (int ff = max(0, f_begin - 2); ff < f_begin; ++ff) stage(ff, ff % 3);
+    for (int ff = max(0, f_begin - 2); ff < f_begin; ++ff) {
+      fetch(ff);
+      commit(ff % 3);
+    }
   }
+  if (f_begin < f_end) fetch(f_begin);
   for (int f = f_begin; f < f_end; ++f) {
     __syncthreads();                                  // previous frame's reads are done
-    stage(f, NF == 3 ? f % 3 : 0);
+    commit(NF == 3 ? f % 3 : 0);
     __syncthreads();
+    if (f + 1 < f_end) fetch(f + 1);                  // next frame's loads overlap this frame's math
     float acc[TR][CPT];
 #pragma unroll
     for (int rr = 0; rr < TR; ++rr)
@@ -201,6 +216,57 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
         *reinterpret_cast<V*>(yb + raster_index(seg, f, hh, ww) * C + c0) = out;
       }
     }
+  }
+}
+
+// Text segments (causal, 4 taps): a thread owns 8 channels and 16 consecutive
+// tokens, keeps its weights and a 4-token window in registers, and loads each
+// input token once.
+constexpr int kTextRun = 16;
+template <typename T>
+__global__ __launch_bounds__(256) void conv_text_kernel(const T* __restrict__ x, T* __restrict__ y,
+                                                       const float* __restrict__ w_text, int64_t Ttot, int64_t C,
+                                                       Seg seg) {
+  const int64_t C8 = C / 8;
+  const int64_t cg = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t run = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t b = blockIdx.z;
+  const int64_t l0 = run * kTextRun;
+  if (cg >= C8 || l0 >= seg.length) return;
+  const int64_t c0 = cg * 8;
+  float w[8][kTextTaps];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 wv = *reinterpret_cast<const float4*>(w_text + (c0 + i) * kTextTaps);
+    w[i][0] = wv.x; w[i][1] = wv.y; w[i][2] = wv.z; w[i][3] = wv.w;
+  }
+  const T* xb = x + b * Ttot * C;
+  T* yb = y + b * Ttot * C;
+  float win[kTextTaps][8];                         // win[j] = token p - 3 + j
+#pragma unroll
+  for (int j = 0; j < kTextTaps - 1; ++j) {
+    const int64_t src = text_tap_source(seg, seg.start + l0, j);
+    if (src >= 0) load8(xb + src * C + c0, win[j + 1]);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) win[j + 1][i] = 0.f;
+  }
+  for (int u = 0; u < kTextRun; ++u) {
+    const int64_t local = l0 + u;
+    if (local >= seg.length) break;
+#pragma unroll
+    for (int j = 0; j < kTextTaps - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) win[j][i] = win[j + 1][i];
+    load8(xb + (seg.start + local) * C + c0, win[kTextTaps - 1]);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < kTextTaps; ++j) acc[i] = fmaf(w[i][j], win[j][i], acc[i]);
+    }
+    store8(yb + (seg.start + local) * C + c0, acc);
   }
 }
 
@@ -265,8 +331,21 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
     if (seg.frames == 1) return launch_tile<1, 8, 8, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream);
     return launch_tile<3, 4, 8, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream);
   }
+  if (B > 65535) return hipErrorInvalidValue;
+  if (seg.kind == SEG_TEXT) {
+    const int64_t runs = (seg.length + kTextRun - 1) / kTextRun;
+    const dim3 tgrid((unsigned)((C / 8 + 63) / 64), (unsigned)((runs + 3) / 4), (unsigned)B);
+    if (bf16) {
+      hipLaunchKernelGGL(conv_text_kernel<uint16_t>, tgrid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+                         static_cast<uint16_t*>(y), w_text, Ttot, C, seg);
+    } else {
+      hipLaunchKernelGGL(conv_text_kernel<float>, tgrid, dim3(256), 0, stream, static_cast<const float*>(x),
+                         static_cast<float*>(y), w_text, Ttot, C, seg);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((C / 8 + 63) / 64), (unsigned)((seg.length + 3) / 4), (unsigned)B);
-  if (grid.y > 0x7fffffffu || B > 65535) return hipErrorInvalidValue;
+  if (grid.y > 0x7fffffffu) return hipErrorInvalidValue;
   if (bf16) {
     hipLaunchKernelGGL(conv_gather_kernel<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
                        static_cast<uint16_t*>(y), w_text, w_vis, Ttot, C, seg);

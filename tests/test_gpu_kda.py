@@ -76,17 +76,23 @@ def test_kda_bf16_small(chm, sequential):
 
 
 def test_kda_fp32_small_dims(chm):
-    """fp32, odd head dims (dk != dv, not multiples of 16), several batch items."""
+    """fp32, odd head dims (dk != dv, not multiples of 16), several batch items; q, k, v
+    are views into one fused tensor (the ABI's shared token stride)."""
+    import torch
     rng = np.random.default_rng(5)
     B, T, H, dk, dv = 2, 77, 3, 20, 37
-    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
-    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
-    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    fused = rng.standard_normal((B, T, H * (2 * dk + dv))).astype(np.float32)
+    q = fused[:, :, :H * dk].reshape(B, T, H, dk)
+    k = fused[:, :, H * dk:2 * H * dk].reshape(B, T, H, dk)
+    v = fused[:, :, 2 * H * dk:].reshape(B, T, H, dv)
     alpha = np.exp(-np.logaddexp(0, rng.standard_normal((B, T, H, dk)))).astype(np.float32)
     beta = (1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
     S0 = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
-    import torch
-    o, Sf = chm.kda_fwd(*(torch.from_numpy(a).cuda() for a in (q, k, v, alpha, beta, S0)), l2norm=True)
+    fd = torch.from_numpy(fused).cuda()
+    qd = fd[:, :, :H * dk].view(B, T, H, dk)
+    kd = fd[:, :, H * dk:2 * H * dk].view(B, T, H, dk)
+    vd = fd[:, :, 2 * H * dk:].view(B, T, H, dv)
+    o, Sf = chm.kda_fwd(qd, kd, vd, *(torch.from_numpy(a).cuda() for a in (alpha, beta, S0)), l2norm=True)
     o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
     assert_close(to_host(o), o_ref, "f32", "o")
     assert_close(to_host(Sf), S_ref, "f32", "S_final")
@@ -100,3 +106,99 @@ def test_kda_empty_sequence_copies_state(chm):
     o, Sf = chm.kda_fwd(e, e, e, e, torch.empty(B, 0, H, dtype=torch.bfloat16, device="cuda"), S0)
     assert o.shape == (B, 0, H, d)
     assert torch.equal(Sf, S0)
+
+
+def _small_case(rng, B, T, H, d, s0, strong=False):
+    q = wl.round_to_bf16(rng.standard_normal((B, T, H, d)).astype(np.float32))
+    k = wl.round_to_bf16(rng.standard_normal((B, T, H, d)).astype(np.float32))
+    v = wl.round_to_bf16(rng.standard_normal((B, T, H, d)).astype(np.float32))
+    if strong:
+        la = np.full((B, T, H, d), -5.0, np.float32)          # log alpha = -5 everywhere
+    else:
+        la = -0.05 * np.logaddexp(0, rng.standard_normal((B, T, H, d))).astype(np.float32)
+    alpha = wl.round_to_bf16(np.exp(la).astype(np.float32))
+    beta = wl.round_to_bf16((1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32))
+    S0 = (0.1 * rng.standard_normal((B, H, d, d))).astype(np.float32) if s0 else None
+    return q, k, v, alpha, beta, S0
+
+
+def _gpu_kda(chm, q, k, v, alpha, beta, S0, **kw):
+    import torch
+    dev = lambda a: to_device(a, "bf16")
+    s0 = None if S0 is None else torch.from_numpy(S0).cuda()
+    return chm.kda_fwd(dev(q), dev(k), dev(v), dev(alpha), dev(beta), s0, l2norm=True, **kw)
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 200, 343, 1000])
+@pytest.mark.parametrize("no_split", [False, True])
+def test_kda_chunked_shapes(chm, T, no_split):
+    rng = np.random.default_rng(T)
+    B, H, d = 2, 2, 128
+    q, k, v, alpha, beta, S0 = _small_case(rng, B, T, H, d, s0=True)
+    o, Sf = _gpu_kda(chm, q, k, v, alpha, beta, S0, no_split=no_split)
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    assert_close(to_host(o), o_ref, "bf16", f"o T={T}")
+    assert_close(to_host(Sf), S_ref, "bf16", f"S_final T={T}")
+
+
+def test_kda_chunked_zero_state_and_no_norm(chm):
+    rng = np.random.default_rng(77)
+    B, T, H, d = 1, 300, 3, 128
+    q, k, v, alpha, beta, _ = _small_case(rng, B, T, H, d, s0=False)
+    q, k = (wl.round_to_bf16(l2norm_ref(x).astype(np.float32)) for x in (q, k))
+    o, Sf = _gpu_kda(chm, q, k, v, alpha, beta, None)
+    o2, Sf2 = chm.kda_fwd(*(to_device(a, "bf16") for a in (q, k, v, alpha, beta)), None, l2norm=False)
+    o_ref, S_ref = kda_ref(q, k, v, alpha, beta, None)
+    assert_close(to_host(o2), o_ref, "bf16", "o (no norm)")
+    assert_close(to_host(Sf2), S_ref, "bf16", "S (no norm)")
+    assert_close(to_host(o), o_ref, "bf16", "o (norm of unit rows)")
+
+
+def test_kda_chunked_strong_decay(chm):
+    """log alpha = -5 for every token and channel: the factored decays stay finite."""
+    rng = np.random.default_rng(5)
+    B, T, H, d = 1, 260, 2, 128
+    q, k, v, alpha, beta, S0 = _small_case(rng, B, T, H, d, s0=True, strong=True)
+    o, Sf = _gpu_kda(chm, q, k, v, alpha, beta, S0)
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    assert np.isfinite(to_host(o)).all()
+    assert_close(to_host(o), o_ref, "bf16", "o strong decay")
+    assert_close(to_host(Sf), S_ref, "bf16", "S strong decay")
+
+
+def test_kda_chunked_split_invariance(chm):
+    """Segmenting the sequence (three passes) and not segmenting it agree closely."""
+    rng = np.random.default_rng(8)
+    B, T, H, d = 1, 64 * 40 + 9, 4, 128
+    q, k, v, alpha, beta, S0 = _small_case(rng, B, T, H, d, s0=True)
+    o1, S1 = _gpu_kda(chm, q, k, v, alpha, beta, S0, no_split=False)
+    o2, S2 = _gpu_kda(chm, q, k, v, alpha, beta, S0, no_split=True)
+    assert rel_l2(to_host(o1), to_host(o2)) < 5e-3
+    assert rel_l2(to_host(S1), to_host(S2)) < 5e-3
+
+
+@pytest.mark.parametrize("wi", [1, 2, 3, 4])
+def test_pipeline_full_workload_sampled_heads(chm, wi):
+    """conv then chunked KDA at full size in the bench's launch configuration;
+    the oracle recomputes whole heads (every token) for a sample of heads."""
+    import torch
+    w = wl.WORKLOADS[wi]
+    inp = wl.make_inputs(w)
+    heads = [0] if wi == 4 else [0, w.H - 1]
+    x_dev = to_device(inp["x"], "bf16")
+    y = chm.mshortconv_fwd(x_dev, torch.from_numpy(inp["w_text"]), torch.from_numpy(inp["w_vis"]), inp["segments"])
+    del x_dev
+    o, Sf = _run_kda(chm, y, inp["alpha"], inp["beta"], inp["S0"], w)
+    o_got = to_host(o[:, :, heads])
+    S_got = to_host(Sf[:, heads])
+    del y, o, Sf
+    HD = w.H * w.d
+    chans = np.concatenate([part * HD + h * w.d + np.arange(w.d) for part in range(3) for h in heads])
+    y_ref = round_bf16_ref(conv_ref(inp["x"][:, :, chans], inp["w_text"][chans], inp["w_vis"][chans], inp["segments"]))
+    nh = len(heads)
+    parts = y_ref.reshape(w.B, w.T, 3, nh, w.d)
+    S0 = None if inp["S0"] is None else inp["S0"][:, heads]
+    o_ref, S_ref = kda_ref(l2norm_ref(parts[:, :, 0]), l2norm_ref(parts[:, :, 1]), parts[:, :, 2],
+                           inp["alpha"][:, :, heads], inp["beta"][:, :, heads], S0)
+    assert_close(o_got, o_ref, "bf16", f"{w.name} o")
+    assert_close(S_got, S_ref, "bf16", f"{w.name} S_final")
