@@ -38,7 +38,9 @@ def _args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=48,
+    ap.add_argument("--profile-once", action="store_true",
+                    help="for counter runs: one 1 GiB device copy (the scale reference), then one step, then exit")
+    ap.add_argument("--cpu-sample-rows", type=int, default=80,
                     help="image rows in the oracle's timed sample (plus the 256 text tokens)")
     return ap.parse_args()
 
@@ -101,6 +103,15 @@ def main():
     def step():
         chm.mshortconv_fwd(x, wt, wv, segs, out=y)
         chm.kda_fwd(q, k, v, alpha, beta, None, workspace=ws, out=o)
+
+    if args.profile_once:
+        ref_src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device=dev)   # 1 GiB
+        ref_dst = torch.empty_like(ref_src)
+        ref_dst.copy_(ref_src)
+        step()
+        torch.cuda.synchronize()
+        print("profile-once: 1 GiB copy + one step done")
+        return
 
     # the image-grid conv kernel alone: same launch as inside a step, on the image tokens
     img = segs[1]
