@@ -89,11 +89,8 @@ struct Lds {
   uint16_t at[CT * TRS];  // tr: -A in blocks below the diagonal, T_II on the diagonal blocks
   uint16_t aqk[CT * TRS]; // tr: Aqk, row i scaled by 1/|q_i|, column j by 1/|k_j|
   float adiag[NSB][SBT][20];   // strictly lower A_II, column k stored at 4*(k&3) + (k>>2)
-  float iem[NSB][D];      // e^{-m_I}
   float pb[NSB][D];       // per block and channel: product of alpha over block tokens 0..8
   float pf[NSB][D];       //                        ... over block tokens 9..15
-  float em[NSB][D];       // e^{m_I}
-  float enm[NSB][D];      // e^{g_n - m_I}
   float pij[6][D];        // e^{m_I - m_J}, I > J
   float egn[D];           // e^{g_n}
   float beta[CT];
@@ -325,40 +322,53 @@ __global__ __launch_bounds__(NTHR) void kda_chunk_kernel(ChunkArgs a) {
     }
     __syncthreads();
 
-    // ---- E2: block decay factors per channel; vote for the fast factorisation -------
-    int ok = 1;
-    if (tid < D) {
-      const int cch = tid;
-      float full[NSB];
+    // ---- E2: block decay factors of this wave's block and channels, in registers -------
+    // full_J = product of alpha over block J; em = e^{m_I}, iem = e^{-m_I},
+    // enm = e^{g_n - m_I}, egn = e^{g_n}. Every wave holds all 128 channels, so every
+    // wave reaches the same vote for the fast factorisation.
+    float em2[2], iem2[2], enm2[2], egn2[2];
+    {
+      float pbv[NSB][2], pfv[NSB][2], full[NSB][2];
 #pragma unroll
-      for (int J = 0; J < NSB; ++J) full[J] = L.pb[J][cch] * L.pf[J][cch];
-      float pre = 1.f;
-#pragma unroll
-      for (int I = 0; I < NSB; ++I) {
-        const float m = pre * L.pb[I][cch];
-        L.em[I][cch] = m;
-        L.iem[I][cch] = __builtin_amdgcn_rcpf(m);
-        pre *= full[I];
-      }
-      L.egn[cch] = pre;
-      ok = pre >= kFastMin;
-      float post = 1.f;
-#pragma unroll
-      for (int I = NSB - 1; I >= 0; --I) {
-        L.enm[I][cch] = L.pf[I][cch] * post;
-        post *= full[I];
+      for (int J = 0; J < NSB; ++J) {
+        const float2 pb2 = *reinterpret_cast<const float2*>(&L.pb[J][ch]);
+        const float2 pf2 = *reinterpret_cast<const float2*>(&L.pf[J][ch]);
+        pbv[J][0] = pb2.x; pbv[J][1] = pb2.y; pfv[J][0] = pf2.x; pfv[J][1] = pf2.y;
+        full[J][0] = pb2.x * pf2.x; full[J][1] = pb2.y * pf2.y;
       }
 #pragma unroll
-      for (int I = 1; I < NSB; ++I) {
-        float mid = 1.f;
+      for (int cc = 0; cc < 2; ++cc) {
+        float pre = 1.f, post = 1.f, all = 1.f;
 #pragma unroll
-        for (int J = I - 1; J >= 0; --J) {
-          L.pij[pair_index(I, J)][cch] = L.pf[J][cch] * mid * L.pb[I][cch];
-          mid *= full[J];
+        for (int J = 0; J < NSB; ++J) {
+          if (J < eI) pre *= full[J][cc];
+          if (J > eI) post *= full[J][cc];
+          all *= full[J][cc];
+        }
+        float pbI = pbv[0][cc], pfI = pfv[0][cc];
+#pragma unroll
+        for (int J = 1; J < NSB; ++J) if (J == eI) { pbI = pbv[J][cc]; pfI = pfv[J][cc]; }
+        em2[cc] = pre * pbI;
+        iem2[cc] = __builtin_amdgcn_rcpf(em2[cc]);
+        enm2[cc] = pfI * post;
+        egn2[cc] = all;
+      }
+      if (wave == 0) {
+        *reinterpret_cast<float2*>(&L.egn[ch]) = make_float2(egn2[0], egn2[1]);
+#pragma unroll
+        for (int I = 1; I < NSB; ++I) {
+          float mid0 = 1.f, mid1 = 1.f;
+#pragma unroll
+          for (int J = I - 1; J >= 0; --J) {
+            *reinterpret_cast<float2*>(&L.pij[pair_index(I, J)][ch]) =
+                make_float2(pfv[J][0] * mid0 * pbv[I][0], pfv[J][1] * mid1 * pbv[I][1]);
+            mid0 *= full[J][0];
+            mid1 *= full[J][1];
+          }
         }
       }
     }
-    const bool fast = __syncthreads_and(ok) != 0;
+    const bool fast = __all(egn2[0] >= kFastMin && egn2[1] >= kFastMin) != 0;
 
     // ---- E3: MFMA operands ------------------------------------------------------------
     {
@@ -368,13 +378,13 @@ __global__ __launch_bounds__(NTHR) void kda_chunk_kernel(ChunkArgs a) {
         kf[i][0] = bf_lo(R.k[i]); kf[i][1] = bf_hi(R.k[i]);
         qf[i][0] = bf_lo(R.q[i]); qf[i][1] = bf_hi(R.q[i]);
       }
-      const float em0 = L.em[eI][ch], em1 = L.em[eI][ch + 1];
+      const float em0 = em2[0], em1 = em2[1];
       uint32_t kb0[4], kb1[4], kt0[4], kt1[4];
       if (fast) {
         // K^ = K e^{g} (row operand of A and right-hand side of W), K_ = K e^{-g},
         // K~ = K_ e^{g_n}, Q^ = Q e^{g} (row operand of Aqk and of Q^ S)
-        const float iem0 = L.iem[eI][ch], iem1 = L.iem[eI][ch + 1];
-        const float gn0 = L.egn[ch], gn1 = L.egn[ch + 1];
+        const float iem0 = iem2[0], iem1 = iem2[1];
+        const float gn0 = egn2[0], gn1 = egn2[1];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           float kh[2][2], kl[2][2];
@@ -396,7 +406,7 @@ __global__ __launch_bounds__(NTHR) void kda_chunk_kernel(ChunkArgs a) {
           kt1[i / 2] = pack_bf16x2(kl[0][1] * gn1, kl[1][1] * gn1);
         }
       } else {
-        const float enm0 = L.enm[eI][ch], enm1 = L.enm[eI][ch + 1];
+        const float enm0 = enm2[0], enm1 = enm2[1];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           float kh[2][2], kl[2][2];
@@ -428,7 +438,29 @@ __global__ __launch_bounds__(NTHR) void kda_chunk_kernel(ChunkArgs a) {
     }
     __syncthreads();
 
-    // ---- M1: A and Aqk blocks on and below the diagonal ------------------------------
+    // ---- M1 + T: A and Aqk blocks; diagonal inverses; Q^ S for the output ------------
+    // Waves 0-3 compute A(I, I) for I = wave and invert that block right away (the
+    // same wave wrote it, so no block barrier is needed); waves 4-7 compute the Aqk
+    // diagonal blocks and every block below the diagonal.
+    f32x4 O[4];
+    auto qs_product = [&]() {
+      uint4 Sf0[4], qf[4][4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Sf0[s] = pack8(S[2 * s][0], S[2 * s + 1][0]);
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[I][s] = ld_perm(L.qh, rm(SBT * I + l16, 0), 32 * s + 4 * q4);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mma32(qf[I][s], Sf0[s], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= L.rq[SBT * I + 4 * q4 + r];
+        O[I] = acc;
+      }
+    };
     {
       auto tile = [&](bool is_a, int I, int J) {
         const uint16_t* rowop = is_a ? L.kr : (fast ? L.qh : L.qr);
@@ -474,59 +506,43 @@ __global__ __launch_bounds__(NTHR) void kda_chunk_kernel(ChunkArgs a) {
           for (int r = 0; r < 4; ++r) dst[tr(SBT * I + 4 * q4 + r, j)] = f2bf(sg * val[r]);
         }
       };
-      constexpr int NTILE = OUT ? 20 : 10;
-      for (int tix = wave; tix < NTILE; tix += 8) {
-        const bool is_a = tix < 10;
-        const int li = tix % 10;
-        int I = 0;
-        while ((I + 1) * (I + 2) / 2 <= li) ++I;
-        const int J = li - I * (I + 1) / 2;
-        tile(is_a, I, J);
+      if (wave < 4) {
+        const int I = wave;
+        tile(true, I, I);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        // forward substitution: lane = 16 part + j owns column j and the terms
+        // k = part + 4m of every row's sum; the four parts are summed with lane swaps
+        const int part = lane >> 4, jj = lane & 15;
+        float xs[4] = {0.f, 0.f, 0.f, 0.f};   // x[part + 4m] of column jj
+        float4 arow[SBT];
+#pragma unroll
+        for (int i = 0; i < SBT; ++i) arow[i] = *reinterpret_cast<const float4*>(&L.adiag[I][i][4 * part]);
+#pragma unroll
+        for (int i = 0; i < SBT; ++i) {
+          float ps = arow[i].x * xs[0] + arow[i].y * xs[1] + arow[i].z * xs[2] + arow[i].w * xs[3];
+          ps = halve16(ps, ps);
+          ps = halve32(ps, ps);
+          const float xi = (i == jj ? 1.f : 0.f) - ps;
+          if (part == (i & 3)) xs[i >> 2] = xi;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) L.at[tr(SBT * I + part + 4 * m, SBT * I + jj)] = f2bf(xs[m]);
+      } else {
+        const int w4 = wave - 4;
+        if (OUT) tile(false, w4, w4);
+        // pairs (I, J), I > J: waves 4, 5 take two, waves 6, 7 one
+        constexpr int PI[6] = {1, 2, 2, 3, 3, 3};
+        constexpr int PJ[6] = {0, 0, 1, 0, 1, 2};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int pi = u == 0 ? w4 : w4 + 4;
+          if (pi < 6) {
+            tile(true, PI[pi], PJ[pi]);
+            if (OUT) tile(false, PI[pi], PJ[pi]);
+          }
+        }
       }
-    }
-    __syncthreads();
-
-    // ---- T: diagonal blocks of (I + A)^{-1}; meanwhile Q^ S for the output -----------
-    // Wave I < 4 inverts block I by forward substitution: lane = 16 part + j owns
-    // column j and the terms k = part + 4m of each row's sum.
-    f32x4 O[4];
-    auto qs_product = [&]() {
-      uint4 Sf0[4], qf[4][4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Sf0[s] = pack8(S[2 * s][0], S[2 * s + 1][0]);
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qf[I][s] = ld_perm(L.qh, rm(SBT * I + l16, 0), 32 * s + 4 * q4);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mma32(qf[I][s], Sf0[s], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= L.rq[SBT * I + 4 * q4 + r];
-        O[I] = acc;
-      }
-    };
-    if (OUT && wave >= 4) qs_product();
-    if (wave < 4) {
-      // wave I inverts diagonal block I: lane = 16 part + j owns column j and the
-      // terms k = part + 4m of every row's sum; the four parts are summed with lane swaps
-      const int I = wave, part = lane >> 4, jj = lane & 15;
-      float xs[4] = {0.f, 0.f, 0.f, 0.f};   // x[part + 4m] of column jj
-      float4 arow[SBT];
-#pragma unroll
-      for (int i = 0; i < SBT; ++i) arow[i] = *reinterpret_cast<const float4*>(&L.adiag[I][i][4 * part]);
-#pragma unroll
-      for (int i = 0; i < SBT; ++i) {
-        float ps = arow[i].x * xs[0] + arow[i].y * xs[1] + arow[i].z * xs[2] + arow[i].w * xs[3];
-        ps = halve16(ps, ps);
-        ps = halve32(ps, ps);
-        const float xi = (i == jj ? 1.f : 0.f) - ps;
-        if (part == (i & 3)) xs[i >> 2] = xi;
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) L.at[tr(SBT * I + part + 4 * m, SBT * I + jj)] = f2bf(xs[m]);
       if (OUT) qs_product();
     }
     __syncthreads();

@@ -19,6 +19,8 @@
 //    causal time taps. A thread keeps its channels' weights in registers and
 //    slides a 3-row window down its column, so each staged value is read from
 //    LDS once per (kw) and feeds up to three output rows.
+#include <algorithm>
+
 #include "dtypes.h"
 #include "internal.h"
 
@@ -219,6 +221,115 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
   }
 }
 
+// One-frame grids (images): a block owns a column strip of TW columns (plus a
+// one-column halo on each side) and a 64-channel slab, and streams down a range
+// of rows TR at a time. Staged rows live in an LDS ring of TR + 2 rows, so the
+// two halo rows of each step are the last rows of the previous step (every input
+// row is read from HBM once per strip); the next TR rows are loaded into
+// registers while the current TR output rows are computed.
+template <int TR, int TW>
+__global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+                                                         const float* __restrict__ w_vis, int64_t Ttot, int64_t C,
+                                                         Seg seg, int n_slab, int n_tw, int n_rr, int rows_per_range,
+                                                         int n_logical) {
+  constexpr int NT = TW * 8, SC = TW + 2, RING = TR + 2;
+  constexpr int ITEMS = TR * SC * 8;                 // 16-byte items per TR staged rows
+  constexpr int NIT = (ITEMS + NT - 1) / NT;
+  __shared__ uint4 ring[RING][SC][8];
+
+  const int lid = (int)xcd_contiguous_id(blockIdx.x, gridDim.x);
+  if (lid >= n_logical) return;
+  int r = lid;
+  const int tw = r % n_tw; r /= n_tw;
+  const int slab = r % n_slab; r /= n_slab;
+  const int rr_ix = r % n_rr; r /= n_rr;
+  const int64_t b = r;
+
+  const int tid = threadIdx.x, g = tid & 7, col = tid >> 3;
+  const int64_t c0 = (int64_t)slab * 64 + g * 8;
+  const int64_t w0 = (int64_t)tw * TW;
+  const int r_begin = rr_ix * rows_per_range;
+  const int r_end = min(seg.height, r_begin + rows_per_range);
+  const uint16_t* xb = x + b * Ttot * C;
+  uint16_t* yb = y + b * Ttot * C;
+
+  float wr[3][3][8];
+#pragma unroll
+  for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wr[kh][kw][i] = w_vis[(c0 + i) * kVisTaps + 18 + kh * 3 + kw];
+
+  // ring slot of grid row hh (hh >= r_begin - 1)
+  auto slot_of = [&](int hh) { return (hh - r_begin + 1) % RING; };
+  uint4 pre[NIT];
+  // load grid rows first_row .. first_row + nrows - 1 (nrows <= TR) into registers
+  auto fetch = [&](int first_row, int nrows) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int it = tid + j * NT;
+      const int rowi = it / (SC * 8), rem = it % (SC * 8);
+      const int sc = rem >> 3, gg = rem & 7;
+      const int64_t hh = first_row + rowi, ww = w0 + sc - 1;
+      pre[j] = uint4{0u, 0u, 0u, 0u};
+      if (it < ITEMS && rowi < nrows && grid_inside(seg, 0, hh, ww))
+        pre[j] = *reinterpret_cast<const uint4*>(xb + raster_index(seg, 0, hh, ww) * C + (int64_t)slab * 64 + gg * 8);
+    }
+  };
+  auto commit = [&](int first_row, int nrows) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int it = tid + j * NT;
+      const int rowi = it / (SC * 8), rem = it % (SC * 8);
+      if (it < ITEMS && rowi < nrows) ring[slot_of(first_row + rowi)][rem >> 3][rem & 7] = pre[j];
+    }
+  };
+
+  // the first step needs rows r_begin - 1 .. r_begin + TR; rows outside the grid stage as zero
+  fetch(r_begin - 1, 2);
+  commit(r_begin - 1, 2);
+  fetch(r_begin + 1, TR);
+  for (int h0 = r_begin; h0 < r_end; h0 += TR) {
+    __syncthreads();                                 // the previous step's reads of the ring are done
+    commit(h0 + 1, TR);                              // rows h0+1 .. h0+TR
+    __syncthreads();
+    if (h0 + TR < r_end) fetch(h0 + TR + 1, TR);     // next step's new rows, in flight during the math
+    float acc[TR][8];
+#pragma unroll
+    for (int q = 0; q < TR; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
+#pragma unroll
+    for (int ir = 0; ir < TR + 2; ++ir) {            // staged row h0 - 1 + ir feeds output rows ir-2..ir
+      __builtin_amdgcn_sched_barrier(0);              // keep one staged row's values live at a time
+      const int sl = slot_of(h0 - 1 + ir);
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw) {
+        float v[8];
+        unpack(ring[sl][col + kw][g], v);
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+          const int orow = ir - kh;
+          if (orow < 0 || orow >= TR) continue;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[orow][i] = fmaf(wr[kh][kw][i], v[i], acc[orow][i]);
+        }
+      }
+    }
+    const int64_t ww = w0 + col;
+#pragma unroll
+    for (int q = 0; q < TR; ++q) {
+      const int64_t hh = h0 + q;
+      if (hh < r_end && ww < seg.width) {
+        uint4 out;
+        pack(out, acc[q]);
+        *reinterpret_cast<uint4*>(yb + raster_index(seg, 0, hh, ww) * C + c0) = out;
+      }
+    }
+  }
+}
+
 // Text segments (causal, 4 taps): a thread owns 8 channels and 16 consecutive
 // tokens, keeps its weights and a 4-token window in registers, and loads each
 // input token once.
@@ -318,6 +429,26 @@ hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64
   return hipGetLastError();
 }
 
+template <int TR, int TW>
+hipError_t launch_rows(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
+                       const Seg& seg, hipStream_t stream) {
+  const int n_slab = (int)(C / 64);
+  const int n_tw = (int)((seg.width + TW - 1) / TW);
+  // split the rows into ranges so that there are enough blocks (each range re-reads 2 halo rows)
+  const int64_t per_range = (int64_t)n_slab * n_tw * B;
+  int n_rr = (int)std::max<int64_t>(1, std::min<int64_t>((2048 + per_range - 1) / per_range, (seg.height + 4 * TR - 1) / (4 * TR)));
+  int rows_per_range = (seg.height + n_rr - 1) / n_rr;
+  rows_per_range = (rows_per_range + TR - 1) / TR * TR;
+  n_rr = (seg.height + rows_per_range - 1) / rows_per_range;
+  const int64_t n_logical = per_range * n_rr;
+  if (n_logical <= 0) return hipSuccess;
+  if (n_logical > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int64_t grid = (n_logical + 7) / 8 * 8;
+  hipLaunchKernelGGL((conv_rows_kernel<TR, TW>), dim3((unsigned)grid), dim3(TW * 8), 0, stream, x, y, w_vis, Ttot, C,
+                     seg, n_slab, n_tw, n_rr, rows_per_range, (int)n_logical);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, int64_t C, bool bf16,
@@ -328,7 +459,7 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
   if (tiled) {
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     uint16_t* ys = static_cast<uint16_t*>(y);
-    if (seg.frames == 1) return launch_tile<1, 8, 8, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream);
+    if (seg.frames == 1) return launch_rows<4, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream);
     return launch_tile<3, 4, 8, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream);
   }
   if (B > 65535) return hipErrorInvalidValue;
