@@ -242,17 +242,263 @@ __device__ __forceinline__ float4 pair_of(const Lds& L, int I, int J, int c) {
   return r;
 }
 
-// One pass over the chunks of one segment of one (batch, head).
-// OUT = true: output pass, state S, writes o (and S_final from the last segment).
-// OUT = false: summary pass; even logical blocks run S from 0, odd ones the
-// transition M from I (no v); both write their state at output-segment boundaries.
+// ---- pieces shared by the output and summary kernels ----------------------------------
+// Fragment conventions (16x16x32 MFMA): lane = 16 q4 + l16; a row fragment of block
+// `blk` holds row 16 blk + l16, positions 32 s + 8 q4 .. + 7 for s = 0..3.
+
+__device__ __forceinline__ void tile_frags(const uint16_t* arr, int blk, uint4 (&f)[4], int l16, int q4) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f[s] = ld128(arr, rm(SBT * blk + l16, 32 * s + 8 * q4));
+}
+// column-operand fragments of block J scaled by e^{m_I - m_J} (blocked factorisation)
+__device__ __forceinline__ void pair_frags(const Lds& L, bool fast, int I, int J, const uint4 (&in)[4],
+                                           uint4 (&out)[4], int q4) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    out[s] = fast ? in[s] : scale8(in[s], pair_of(L, I, J, 32 * s + 4 * q4), pair_of(L, I, J, 32 * s + 16 + 4 * q4));
+}
+__device__ __forceinline__ f32x4 mma4(const uint4 (&ra)[4], const uint4 (&cb)[4]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
+  return acc;
+}
+// A(I, J) = diag(b / |k|) (K^ K_^T)(I, J) diag(1 / |k|): below the diagonal -> at (negated),
+// on it (strictly lower part) -> adiag in fp32
+__device__ __forceinline__ void epi_a(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
+  const int j = SBT * J + l16;
+  const float rkj = L.rk[j];
+  const float4 b4 = ldf4(&L.beta[SBT * I + 4 * q4]), k4 = ldf4(&L.rk[SBT * I + 4 * q4]);
+  const float rowf[4] = {b4.x * k4.x, b4.y * k4.y, b4.z * k4.z, b4.w * k4.w};
+  if (I == J) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      L.adiag[I][4 * q4 + r][4 * (l16 & 3) + (l16 >> 2)] = 4 * q4 + r > l16 ? rowf[r] * rkj * acc[r] : 0.f;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.at[tr(SBT * I + 4 * q4 + r, j)] = f2bf(-rowf[r] * rkj * acc[r]);
+  }
+}
+// Aqk(I, J) = diag(1 / |q|) (Q^ K_^T)(I, J) diag(1 / |k|), lower triangle including the diagonal
+__device__ __forceinline__ void epi_q(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
+  const int j = SBT * J + l16;
+  const float rkj = L.rk[j];
+  const float4 rq4 = ldf4(&L.rq[SBT * I + 4 * q4]);
+  const float rowf[4] = {rq4.x, rq4.y, rq4.z, rq4.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool keep = I > J || 4 * q4 + r >= l16;
+    L.aqk[tr(SBT * I + 4 * q4 + r, cpos(j))] = f2bf(keep ? rowf[r] * rkj * acc[r] : 0.f);
+  }
+}
+// T_II = (I + A_II)^{-1} into the diagonal block of at, from adiag[I] written by this
+// wave. Forward substitution: lane = 16 part + j owns column j and the terms
+// k = part + 4m of every row's sum; the four parts are summed with lane swaps.
+__device__ __forceinline__ void invert_diag(Lds& L, int I, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  const int part = lane >> 4, jj = lane & 15;
+  float xs[4] = {0.f, 0.f, 0.f, 0.f};   // x[part + 4m] of column jj
+  constexpr int AH = 4;                  // rows of A_II read ahead
+  float4 arow[AH];
+#pragma unroll
+  for (int i = 0; i < AH; ++i) arow[i] = ldf4(&L.adiag[I][i][4 * part]);
+#pragma unroll
+  for (int i = 0; i < SBT; ++i) {
+    const float4 ar = arow[i % AH];
+    if (i + AH < SBT) arow[i % AH] = ldf4(&L.adiag[I][i + AH][4 * part]);
+    float ps = ar.x * xs[0] + ar.y * xs[1] + ar.z * xs[2] + ar.w * xs[3];
+    ps = halve16(ps, ps);
+    ps = halve32(ps, ps);
+    const float xi = (i == jj ? 1.f : 0.f) - ps;
+    if (part == (i & 3)) xs[i >> 2] = xi;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) L.at[tr(SBT * I + part + 4 * m, SBT * I + jj)] = f2bf(xs[m]);
+}
+// mma16 A fragments of at: block (I, J), J <= I, at I (I + 1) / 2 + J
+__device__ __forceinline__ void load_t_frags(const Lds& L, uint2 (&af)[10], int l16, int q4) {
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J)
+      af[I * (I + 1) / 2 + J] = *reinterpret_cast<const uint2*>(&L.at[tr(SBT * I + l16, SBT * J + 4 * q4)]);
+}
+// X = (I + A)^{-1} Y by block forward substitution, Y and X in the D layout
+__device__ __forceinline__ void block_solve(const uint2 (&af)[10], const f32x4 (&y0)[4], f32x4 (&X)[4]) {
+  uint2 Xb[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    f32x4 y = y0[I];
+#pragma unroll
+    for (int J = 0; J < I; ++J) y = mma16(af[I * (I + 1) / 2 + J], Xb[J], y);
+    X[I] = mma16(af[I * (I + 1) / 2 + I], pack4(y), f32x4{0.f, 0.f, 0.f, 0.f});
+    Xb[I] = pack4(X[I]);
+  }
+}
+// W = (I + A)^{-1} diag(b / |k|) K^ for channels 16 t .. 16 t + 15, negated and written
+// over the same kr channels (read transposed first; only this wave touches them)
+__device__ __forceinline__ void w_tile(Lds& L, bool fast, int t, const uint2 (&af)[10], int l16, int q4) {
+  const int tpos = 32 * (t >> 1) + 4 * (t & 1);      // cpos(16 t)
+  f32x4 y[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    // lane (l16, q4) receives channel 16 t + l16 of tokens 16 I + 4 q4 + 0..3
+    const float4 kv = unpack4(ld_tr(&L.kr[rm(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
+    float sc = 1.f;
+    if (!fast) sc = pick(em_of(L, I, 16 * t + (l16 & ~3)), l16 & 3);
+    const float4 kr4 = mul4(ldf4(&L.beta[SBT * I + 4 * q4]), ldf4(&L.rk[SBT * I + 4 * q4]));
+    y[I][0] = kv.x * kr4.x * sc; y[I][1] = kv.y * kr4.y * sc;
+    y[I][2] = kv.z * kr4.z * sc; y[I][3] = kv.w * kr4.w * sc;
+  }
+  f32x4 X[4];
+  block_solve(af, y, X);
+  const int wcol = tpos + 8 * (l16 >> 2) + (l16 & 3);   // cpos(16 t + l16)
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.kr[rm(SBT * I + 4 * q4 + r, wcol)] = f2bf(-X[I][r]);
+}
+// v of channels col0 .. col0 + 31 (vx: lane = tokens 4 (lane >> 2) + j, channels
+// col0 + 8 (lane & 3) ..) -> the same channels of qw, which only this wave uses now
+__device__ __forceinline__ void stage_v(Lds& L, int col0, const uint4 (&vx)[4], int lane) {
+  const int vp = col0 + 16 * (lane & 1) + 4 * ((lane >> 1) & 1);   // cpos(col0 + 8 (lane & 3))
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * (lane >> 2) + j;
+    *reinterpret_cast<uint2*>(&L.qw[rm(row, vp)]) = make_uint2(vx[j].x, vx[j].y);
+    *reinterpret_cast<uint2*>(&L.qw[rm(row, vp + 8)]) = make_uint2(vx[j].z, vx[j].w);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+}
+// U~ = (I + A)^{-1} diag(b) V for the state columns col0 .. col0 + 31 (staged in qw)
+__device__ __forceinline__ void u_tiles(const Lds& L, int col0, const uint2 (&af)[10], f32x4 (&Ut)[4][2], int l16,
+                                        int q4) {
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int t = col0 / 16 + ct;
+    const int tpos = 32 * (t >> 1) + 4 * (t & 1);      // cpos(16 t)
+    f32x4 y[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const float4 vv = unpack4(ld_tr(&L.qw[rm(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
+      const float4 br = ldf4(&L.beta[SBT * I + 4 * q4]);
+      y[I][0] = vv.x * br.x; y[I][1] = vv.y * br.y;
+      y[I][2] = vv.z * br.z; y[I][3] = vv.w * br.w;
+    }
+    f32x4 X[4];
+    block_solve(af, y, X);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) Ut[I][ct] = X[I];
+  }
+}
+// state as bf16 B operand: slots 0-3 rows 32 s + 4 q4 + r, 4-7 rows 32 s + 16 + 4 q4 + r
+__device__ __forceinline__ void pack_state(const f32x4 (&S)[8][2], uint4 (&Sf)[4][2]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) Sf[s][ct] = pack8(S[2 * s][ct], S[2 * s + 1][ct]);
+}
+// U += (-W) S (-W in kr)
+__device__ __forceinline__ void minus_ws(const Lds& L, const uint4 (&Sf)[4][2], f32x4 (&U)[4][2], int l16, int q4) {
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    uint4 wf[4];
+    tile_frags(L.kr, I, wf, l16, q4);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) U[I][ct] = mma32(wf[s], Sf[s][ct], U[I][ct]);
+  }
+}
+// S <- Diag(e^{g_n}) S + K~^T diag(1/|k|) U, K~ = K e^{g_n - g} read transposed from kc
+__device__ __forceinline__ void update_state(const Lds& L, bool fast, f32x4 (&S)[8][2], const f32x4 (&U)[4][2],
+                                             int l16, int q4) {
+  uint4 Upf[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float4 ka = ldf4(&L.rk[32 * s + 4 * q4]), kb = ldf4(&L.rk[32 * s + 16 + 4 * q4]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      f32x4 lo = U[2 * s][ct], hi = U[2 * s + 1][ct];
+      lo[0] *= ka.x; lo[1] *= ka.y; lo[2] *= ka.z; lo[3] *= ka.w;
+      hi[0] *= kb.x; hi[1] *= kb.y; hi[2] *= kb.z; hi[3] *= kb.w;
+      Upf[s][ct] = pack8(lo, hi);
+    }
+  }
+  // A operand K~^T: lane (l16, q4) = channel 16 rt + l16, tokens 32 s + 4 q4 + 0..3 and
+  // 32 s + 16 + 4 q4 + 0..3
+  const int kbase = rm(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt) {
+    const int cp = 32 * (rt >> 1) + 4 * (rt & 1);   // cpos(16 rt)
+    uint4 kt[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      kt[s] = cat(ld_tr(&L.kc[kbase + rm(32 * s, cp)]), ld_tr(&L.kc[kbase + rm(32 * s + 16, cp)]));
+    const float4 eg = ldf4(&L.egn[16 * rt + 4 * q4]);
+    if (fast) {   // K~ = K_ e^{g_n}: the factor is a row scaling of the product
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f32x4 acc = S[rt][ct];
+        acc = mma32(kt[0], Upf[0][ct], acc);
+        acc = mma32(kt[1], Upf[1][ct], acc);
+        acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
+        S[rt][ct] = acc;
+      }
+    } else {      // blocked: K~ = K_ e^{g_n - m_I} for the tokens of block I
+      const int cl = 16 * rt + (l16 & ~3), u = l16 & 3;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const float f0 = pick(enm_of(L, 2 * s, cl), u), f1 = pick(enm_of(L, 2 * s + 1, cl), u);
+        kt[s] = scale8(kt[s], make_float4(f0, f0, f0, f0), make_float4(f1, f1, f1, f1));
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f32x4 acc = S[rt][ct];
+        acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
+        acc = mma32(kt[0], Upf[0][ct], acc);
+        acc = mma32(kt[1], Upf[1][ct], acc);
+        S[rt][ct] = acc;
+      }
+    }
+  }
+}
+// the 32 state columns of this wave -> m ([D][D] fp32); svo = lane part of the offset
+__device__ __forceinline__ void store_state(const f32x4 (&S)[8][2], float* m, int svo) {
+  float* dst = m + svo;
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * rt + r) * D + 16 * ct] = S[rt][ct][r];
+}
+// v of the state columns col0 .. col0 + 31 of the chunk: lane = tokens 4 (lane >> 2) + j,
+// channels col0 + 8 (lane & 3) .. + 7; tokens past the end read as zero
+__device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t b, int64_t h, int64_t t0, int n, int col0,
+                                       int lane, uint4 (&vx)[4]) {
+  const int st2 = (int)a.stride * 2;
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (b * a.T + t0) * a.stride + h * D), 0, n * st2,
+                                                    kRsrcW3);
+  const int vo = (4 * (lane >> 2)) * st2 + 2 * (col0 + 8 * (lane & 3));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, j * st2, 0);
+    vx[j] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
+  }
+}
+
+// Output pass over the chunks of one segment of one (batch, head): 4 waves, wave w
+// owns state columns 32 w .. 32 w + 31; writes o, and S_final from the last segment.
 //
 // Per chunk, phases and the barriers after them:
-//   loads; E1: norms and block decay products           | B
-//   E2/E3: decay factors, operands kr kc qw; v loads     | C
-//   M1T: A / Aqk tiles, diagonal inverses, Q^ S          | D
-//   X: block substitution for U~ (registers) and W       | E
-//   S: U = U~ - W S, O += Aqk U, state update            | F   (then the o store)
+//   loads; E1: norms and block decay products              | B
+//   E2/E3: decay factors, operands kr kc qw                 | C
+//   M1T: A / Aqk tiles, diagonal inverses, Q^ S; v loads    | D
+//   X: block substitution for W (into kr) and U~            | E
+//   S: U = U~ - W S, O += Aqk U, state update, o store      | F
 //
 // Two factorisations of the pairwise decay e^{g_i - g_j} are used:
 //  * fast: one reference at the chunk start (K^ = K e^{g}, K_ = K e^{-g}); valid
@@ -261,8 +507,7 @@ __device__ __forceinline__ float4 pair_of(const Lds& L, int I, int J, int c) {
 //  * blocked: references at token 8 of each 16-token block, with the factors
 //    e^{m_I - m_J}, e^{m_I}, e^{g_n - m_I} applied to fragments as they are
 //    read; valid while log(alpha) >= -11 per token.
-template <bool OUT>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_out_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   Lds& L = *reinterpret_cast<Lds*>(lds_raw);
 
@@ -271,53 +516,28 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int l16 = lane & 15, q4 = lane >> 4;
-  int64_t bh;
-  int p;
-  bool mkind = false;
-  if (OUT) {
-    bh = lid / a.P;
-    p = lid % a.P;
-  } else {
-    mkind = lid & 1;
-    bh = (lid >> 1) / a.P;
-    p = (lid >> 1) % a.P;
-  }
-  const bool has_v = OUT || !mkind;
+  const int64_t bh = lid / a.P;
+  const int p = lid % a.P;
   const int64_t b = bh / a.H, h = bh % a.H;
   const int64_t NC = (a.T + CT - 1) / CT;
   const int64_t c_begin = (int64_t)p * a.L;
-  int64_t c_end = min<int64_t>(NC, c_begin + a.L);
-  if (!OUT) c_end = min<int64_t>(c_end, a.c_stop);
+  const int64_t c_end = min<int64_t>(NC, c_begin + a.L);
 
   // ---- state: rows 16 rt + 4 q4 + r, columns col0 + 16 ct + l16 -----------------
   const int col0 = 32 * wave;
-  const int svo = ((4 * q4) * D + col0 + l16) * 4;   // lane part of a state element's byte offset
+  const int svo = (4 * q4) * D + col0 + l16;   // lane part of a state element's offset
   f32x4 S[8][2];
   {
-    const float* src = nullptr;
-    if (OUT) src = a.P > 1 ? a.Sstart + (bh * a.P + p) * D * D : (a.S0 ? a.S0 + bh * D * D : nullptr);
-    if (src) {
-      const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, D * D * 4, kRsrcW3);
+    const float* src = a.P > 1 ? a.Sstart + (bh * a.P + p) * D * D : (a.S0 ? a.S0 + bh * D * D : nullptr);
+    if (a.P > 1 && p % kSub != 0) src = nullptr;   // formed below
 #pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
+    for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            S[rt][ct][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, svo, ((16 * rt + r) * D + 16 * ct) * 4, 0));
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rt + 4 * q4 + r, col = col0 + 16 * ct + l16;
-            S[rt][ct][r] = (!OUT && mkind && row == col) ? 1.f : 0.f;
-          }
-    }
+        for (int r = 0; r < 4; ++r) S[rt][ct][r] = src ? src[svo + (16 * rt + r) * D + 16 * ct] : 0.f;
   }
-  if (OUT && a.P > 1 && p % kSub != 0) {
+  if (a.P > 1 && p % kSub != 0) {
     // a start inside a summary segment: S_start(p) = M_e S_start(p - p % kSub) + S_e with
     // e = p - 1, in fp32-accurate MFMA (bf16 high and low parts, three products)
     const int e = p - 1;
@@ -356,7 +576,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       for (int ct = 0; ct < 2; ++ct) {
         f32x4 acc0, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc0[r] = Sp[(16 * rt + 4 * q4 + r) * D + col0 + 16 * ct + l16];
+        for (int r = 0; r < 4; ++r) acc0[r] = Sp[svo + (16 * rt + r) * D + 16 * ct];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           acc1 = mma32(aL[s], bH[s][ct], acc1);
@@ -367,33 +587,23 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       }
     }
   }
-  auto store_state = [&](float* m) {
-    float* dst = m + svo / 4;
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * rt + r) * D + 16 * ct] = S[rt][ct][r];
-  };
-  if (OUT) {   // the Aqk blocks (0,1) and (2,3) above the diagonal are read as zeros
-    for (int e = tid; e < 2 * SBT * SBT; e += NTHR) {
-      const int I = (e >> 8) * 2, i = (e >> 4) & 15, j = e & 15;
-      L.aqk[tr(SBT * I + i, cpos(SBT * (I + 1) + j))] = 0;
-    }
+  // the Aqk blocks (0,1) and (2,3) above the diagonal are read as zeros
+  for (int e = tid; e < 2 * SBT * SBT; e += NTHR) {
+    const int I = (e >> 8) * 2, i = (e >> 4) & 15, j = e & 15;
+    L.aqk[tr(SBT * I + i, cpos(SBT * (I + 1) + j))] = 0;
   }
 
   const uint2 kOnes = make_uint2(0x3F803F80u, 0x3F803F80u);   // alpha = 1 past the end
 
   for (int64_t c = c_begin; c < c_end; ++c) {
     // Lane-derived addresses are recomputed every chunk (cheap) rather than kept live
-    // across the loop: the lane_c id passes through an empty asm so that they cannot be
+    // across the loop: the lane id passes through an empty asm so that they cannot be
     // hoisted out of it.
     int lane_c = lane;
     asm volatile("" : "+v"(lane_c));
     const int l16 = lane_c & 15, q4 = lane_c >> 4;
     // elementwise mapping: wave = decay block; half-wave hf = tokens 8 hf .. 8 hf + 7
-    // of the block; lane_c cg = channels 4 cg .. 4 cg + 3
+    // of the block; lane cg = channels 4 cg .. 4 cg + 3
     const int hf = lane_c >> 5, cg = lane_c & 31, c0 = 4 * cg, p0 = cpos(c0);
     const int tk0 = SBT * wave + 8 * hf;
     const int64_t t0 = c * CT;
@@ -401,10 +611,9 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 
     // ---- loads ----------------------------------------------------------------------
     // Buffer loads: block-uniform base and bounds (the chunk's first n tokens), byte
-    // offsets split into a lane_c part and a uniform part. Reads past the bound return
+    // offsets split into a lane part and a uniform part. Reads past the bound return
     // zero, which is k = q = v = beta = 0 for tokens past the end; alpha is set to 1.
     uint2 kx[8], qx[8], ax[8], a8;
-    uint4 vx[4];
     float bt;
     {
       const int64_t row0 = b * a.T + t0;
@@ -418,7 +627,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         kx[i] = ld_buf64(rk_, vk, (tb + i) * st2);
-        qx[i] = OUT ? ld_buf64(rq_, vk, (tb + i) * st2) : make_uint2(0u, 0u);
+        qx[i] = ld_buf64(rq_, vk, (tb + i) * st2);
         const uint2 av = ld_buf64(ra_, va, (tb + i) * sa2);
         ax[i] = tk0 + i < n ? av : kOnes;
       }
@@ -434,7 +643,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         ss[i] = dot4(kx[i]);
-        ss[i + 8] = OUT ? dot4(qx[i]) : 0.f;
+        ss[i + 8] = dot4(qx[i]);
       }
       const float tot = half_sum16(ss, lane_c);
       if ((lane_c & 1) == 0) {
@@ -487,7 +696,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
         const int tk = tk0 + i;
         *reinterpret_cast<uint2*>(&L.kr[rm(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fr));
         *reinterpret_cast<uint2*>(&L.kc[rm(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fc));
-        if (OUT) *reinterpret_cast<uint2*>(&L.qw[rm(tk, p0)]) = pack4(mul4(unpack4(qx[i]), fr));
+        *reinterpret_cast<uint2*>(&L.qw[rm(tk, p0)]) = pack4(mul4(unpack4(qx[i]), fr));
       };
       if (hf == 1) {
         float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
@@ -506,375 +715,128 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       }
     }
     lds_barrier();   // C
+
     // ---- M1T: A and Aqk blocks, diagonal inverses, Q^ S ---------------------------------
-    // state as bf16 B operand: slots 0-3 rows 32s+4q+r, 4-7 rows 32s+16+4q+r
-    auto pack_state = [&](uint4(&Sf)[4][2]) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Sf[s][ct] = pack8(S[2 * s][ct], S[2 * s + 1][ct]);
-    };
     f32x4 O[4][2];
+    uint4 vx[4];
     {
-      auto frags = [&](const uint16_t* arr, int blk, uint4(&f)[4]) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) f[s] = ld128(arr, rm(SBT * blk + l16, 32 * s + 8 * q4));
-      };
-      auto paired = [&](int I, int J, const uint4(&in)[4], uint4(&out)[4]) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (fast) {
-            out[s] = in[s];
-          } else {
-            out[s] = scale8(in[s], pair_of(L, I, J, 32 * s + 4 * q4), pair_of(L, I, J, 32 * s + 16 + 4 * q4));
-          }
-        }
-      };
-      auto mma4 = [&](const uint4(&ra)[4], const uint4(&cb)[4]) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
-        return acc;
-      };
-      // A(I, J) below the diagonal -> at (negated); A(I, I) -> adiag (fp32)
-      auto epi_a = [&](int I, int J, f32x4 acc) {
-        const int j = SBT * J + l16;
-        const float rkj = L.rk[j];
-        const float4 b4 = ldf4(&L.beta[SBT * I + 4 * q4]), k4 = ldf4(&L.rk[SBT * I + 4 * q4]);
-        const float rowf[4] = {b4.x * k4.x, b4.y * k4.y, b4.z * k4.z, b4.w * k4.w};
-        if (I == J) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            L.adiag[I][4 * q4 + r][4 * (l16 & 3) + (l16 >> 2)] = 4 * q4 + r > l16 ? rowf[r] * rkj * acc[r] : 0.f;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) L.at[tr(SBT * I + 4 * q4 + r, j)] = f2bf(-rowf[r] * rkj * acc[r]);
-        }
-      };
-      auto epi_q = [&](int I, int J, f32x4 acc) {
-        const int j = SBT * J + l16;
-        const float rkj = L.rk[j];
-        const float4 rq4 = ldf4(&L.rq[SBT * I + 4 * q4]);
-        const float rowf[4] = {rq4.x, rq4.y, rq4.z, rq4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool keep = I > J || 4 * q4 + r >= l16;
-          L.aqk[tr(SBT * I + 4 * q4 + r, cpos(j))] = f2bf(keep ? rowf[r] * rkj * acc[r] : 0.f);
-        }
-      };
       uint4 cA[4], cB[4], rA[4], sc[4];
-      if (OUT) {
-        // wave 0: A00 Aqk00 A10 A30 Aqk30;  wave 1: A11 Aqk11 Aqk10 A31 Aqk31;
-        // wave 2: A22 A20 Aqk22 A32 Aqk32;  wave 3: A33 Aqk33 A21 Aqk21 Aqk20
-        if (wave == 0) {
-          frags(L.kc, 0, cA);
-          frags(L.kr, 0, rA); epi_a(0, 0, mma4(rA, cA));
-          frags(L.qw, 0, rA); epi_q(0, 0, mma4(rA, cA));
-          frags(L.kr, 1, rA); paired(1, 0, cA, sc); epi_a(1, 0, mma4(rA, sc));
-          paired(3, 0, cA, sc);
-          frags(L.kr, 3, rA); epi_a(3, 0, mma4(rA, sc));
-          frags(L.qw, 3, rA); epi_q(3, 0, mma4(rA, sc));
-        } else if (wave == 1) {
-          frags(L.kc, 1, cA);
-          frags(L.kr, 1, rA); epi_a(1, 1, mma4(rA, cA));
-          frags(L.qw, 1, rA); epi_q(1, 1, mma4(rA, cA));
-          frags(L.kc, 0, cB); paired(1, 0, cB, sc); epi_q(1, 0, mma4(rA, sc));
-          paired(3, 1, cA, sc);
-          frags(L.kr, 3, rA); epi_a(3, 1, mma4(rA, sc));
-          frags(L.qw, 3, rA); epi_q(3, 1, mma4(rA, sc));
-        } else if (wave == 2) {
-          frags(L.kc, 2, cA);
-          frags(L.kr, 2, rA); epi_a(2, 2, mma4(rA, cA));
-          frags(L.kc, 0, cB); paired(2, 0, cB, sc); epi_a(2, 0, mma4(rA, sc));
-          frags(L.qw, 2, rA); epi_q(2, 2, mma4(rA, cA));
-          paired(3, 2, cA, sc);
-          frags(L.kr, 3, rA); epi_a(3, 2, mma4(rA, sc));
-          frags(L.qw, 3, rA); epi_q(3, 2, mma4(rA, sc));
-        } else {
-          frags(L.kc, 3, cA);
-          frags(L.kr, 3, rA); epi_a(3, 3, mma4(rA, cA));
-          frags(L.qw, 3, rA); epi_q(3, 3, mma4(rA, cA));
-          frags(L.kc, 1, cB); paired(2, 1, cB, sc);
-          frags(L.kr, 2, rA); epi_a(2, 1, mma4(rA, sc));
-          frags(L.qw, 2, rA); epi_q(2, 1, mma4(rA, sc));
-          frags(L.kc, 0, cB); paired(2, 0, cB, sc); epi_q(2, 0, mma4(rA, sc));
-        }
+      // wave 0: A00 Aqk00 A10 A30 Aqk30;  wave 1: A11 Aqk11 Aqk10 A31 Aqk31;
+      // wave 2: A22 A20 Aqk22 A32 Aqk32;  wave 3: A33 Aqk33 A21 Aqk21 Aqk20
+      if (wave == 0) {
+        tile_frags(L.kc, 0, cA, l16, q4);
+        tile_frags(L.kr, 0, rA, l16, q4); epi_a(L, 0, 0, mma4(rA, cA), l16, q4);
+        tile_frags(L.qw, 0, rA, l16, q4); epi_q(L, 0, 0, mma4(rA, cA), l16, q4);
+        tile_frags(L.kr, 1, rA, l16, q4); pair_frags(L, fast, 1, 0, cA, sc, q4); epi_a(L, 1, 0, mma4(rA, sc), l16, q4);
+        pair_frags(L, fast, 3, 0, cA, sc, q4);
+        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 0, mma4(rA, sc), l16, q4);
+        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 0, mma4(rA, sc), l16, q4);
+      } else if (wave == 1) {
+        tile_frags(L.kc, 1, cA, l16, q4);
+        tile_frags(L.kr, 1, rA, l16, q4); epi_a(L, 1, 1, mma4(rA, cA), l16, q4);
+        tile_frags(L.qw, 1, rA, l16, q4); epi_q(L, 1, 1, mma4(rA, cA), l16, q4);
+        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 1, 0, cB, sc, q4); epi_q(L, 1, 0, mma4(rA, sc), l16, q4);
+        pair_frags(L, fast, 3, 1, cA, sc, q4);
+        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 1, mma4(rA, sc), l16, q4);
+        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 1, mma4(rA, sc), l16, q4);
+      } else if (wave == 2) {
+        tile_frags(L.kc, 2, cA, l16, q4);
+        tile_frags(L.kr, 2, rA, l16, q4); epi_a(L, 2, 2, mma4(rA, cA), l16, q4);
+        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 2, 0, cB, sc, q4); epi_a(L, 2, 0, mma4(rA, sc), l16, q4);
+        tile_frags(L.qw, 2, rA, l16, q4); epi_q(L, 2, 2, mma4(rA, cA), l16, q4);
+        pair_frags(L, fast, 3, 2, cA, sc, q4);
+        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 2, mma4(rA, sc), l16, q4);
+        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 2, mma4(rA, sc), l16, q4);
       } else {
-        // wave 0: A00 A10 A20;  wave 1: A11 A21 A31;  wave 2: A22 A32;  wave 3: A33 A30
-        if (wave == 0) {
-          frags(L.kc, 0, cA);
-          frags(L.kr, 0, rA); epi_a(0, 0, mma4(rA, cA));
-          frags(L.kr, 1, rA); paired(1, 0, cA, sc); epi_a(1, 0, mma4(rA, sc));
-          frags(L.kr, 2, rA); paired(2, 0, cA, sc); epi_a(2, 0, mma4(rA, sc));
-        } else if (wave == 1) {
-          frags(L.kc, 1, cA);
-          frags(L.kr, 1, rA); epi_a(1, 1, mma4(rA, cA));
-          frags(L.kr, 2, rA); paired(2, 1, cA, sc); epi_a(2, 1, mma4(rA, sc));
-          frags(L.kr, 3, rA); paired(3, 1, cA, sc); epi_a(3, 1, mma4(rA, sc));
-        } else if (wave == 2) {
-          frags(L.kc, 2, cA);
-          frags(L.kr, 2, rA); epi_a(2, 2, mma4(rA, cA));
-          frags(L.kr, 3, rA); paired(3, 2, cA, sc); epi_a(3, 2, mma4(rA, sc));
-        } else {
-          frags(L.kc, 3, cA);
-          frags(L.kr, 3, rA); epi_a(3, 3, mma4(rA, cA));
-          frags(L.kc, 0, cB); paired(3, 0, cB, sc); epi_a(3, 0, mma4(rA, sc));
+        tile_frags(L.kc, 3, cA, l16, q4);
+        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 3, mma4(rA, cA), l16, q4);
+        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 3, mma4(rA, cA), l16, q4);
+        tile_frags(L.kc, 1, cB, l16, q4); pair_frags(L, fast, 2, 1, cB, sc, q4);
+        tile_frags(L.kr, 2, rA, l16, q4); epi_a(L, 2, 1, mma4(rA, sc), l16, q4);
+        tile_frags(L.qw, 2, rA, l16, q4); epi_q(L, 2, 1, mma4(rA, sc), l16, q4);
+        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 2, 0, cB, sc, q4); epi_q(L, 2, 0, mma4(rA, sc), l16, q4);
+      }
+      invert_diag(L, wave, lane_c);
+      // O = diag(1/|q|) Q^ S; the blocked factorisation scales Q^'s channels by e^{m_I}
+      uint4 Sf[4][2];
+      pack_state(S, Sf);
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        uint4 qf[4];
+        tile_frags(L.qw, I, qf, l16, q4);
+        if (!fast) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            qf[s] = scale8(qf[s], em_of(L, I, 32 * s + 4 * q4), em_of(L, I, 32 * s + 16 + 4 * q4));
+        }
+        const float4 rq4 = ldf4(&L.rq[SBT * I + 4 * q4]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mma32(qf[s], Sf[s][ct], acc);
+          acc[0] *= rq4.x; acc[1] *= rq4.y; acc[2] *= rq4.z; acc[3] *= rq4.w;
+          O[I][ct] = acc;
         }
       }
-      // A_II was written by this wave: order its LDS writes before the reads below
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      {
-        // T_II = (I + A_II)^{-1}, I = wave, by forward substitution: lane_c = 16 part + j
-        // owns column j and the terms k = part + 4m of every row's sum; the four parts
-        // are summed with lane_c swaps
-        const int I = wave;
-        const int part = lane_c >> 4, jj = lane_c & 15;
-        float xs[4] = {0.f, 0.f, 0.f, 0.f};   // x[part + 4m] of column jj
-        constexpr int AH = 4;                  // rows of A_II read ahead
-        float4 arow[AH];
-#pragma unroll
-        for (int i = 0; i < AH; ++i) arow[i] = ldf4(&L.adiag[I][i][4 * part]);
-#pragma unroll
-        for (int i = 0; i < SBT; ++i) {
-          const float4 ar = arow[i % AH];
-          if (i + AH < SBT) arow[i % AH] = ldf4(&L.adiag[I][i + AH][4 * part]);
-          float ps = ar.x * xs[0] + ar.y * xs[1] + ar.z * xs[2] + ar.w * xs[3];
-          ps = halve16(ps, ps);
-          ps = halve32(ps, ps);
-          const float xi = (i == jj ? 1.f : 0.f) - ps;
-          if (part == (i & 3)) xs[i >> 2] = xi;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) L.at[tr(SBT * I + part + 4 * m, SBT * I + jj)] = f2bf(xs[m]);
-      }
-      if (OUT) {
-        // O = diag(1/|q|) Q^ S; the blocked factorisation scales Q^'s channels by e^{m_I}
-        uint4 Sf[4][2];
-        pack_state(Sf);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          uint4 qf[4];
-          frags(L.qw, I, qf);
-          if (!fast) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              qf[s] = scale8(qf[s], em_of(L, I, 32 * s + 4 * q4), em_of(L, I, 32 * s + 16 + 4 * q4));
-          }
-          const float4 rq4 = ldf4(&L.rq[SBT * I + 4 * q4]);
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mma32(qf[s], Sf[s][ct], acc);
-            acc[0] *= rq4.x; acc[1] *= rq4.y; acc[2] *= rq4.z; acc[3] *= rq4.w;
-            O[I][ct] = acc;
-          }
-        }
-      }
-    }
-    {
-      const int st2 = (int)a.stride * 2;
-      if (has_v) {
-        // this wave's v columns col0 .. col0 + 31: lane_c = tokens 4 (l >> 2) + j, channels col0 + 8 (l & 3) ..
-        const auto rv_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (b * a.T + t0) * a.stride + h * D), 0, n * st2, kRsrcW3);
-        const int vo = (4 * (lane_c >> 2)) * st2 + 2 * (col0 + 8 * (lane_c & 3));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(rv_, vo, j * st2, 0);
-          vx[j] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
-        }
-      }
+      load_v(a, b, h, t0, n, col0, lane_c, vx);
     }
     lds_barrier();   // D
 
     // ---- X: block substitution X = (I + A)^{-1} diag(sigma) R --------------------------
-    // right-hand sides: this wave's v columns (U~, kept in registers) and the K^
-    // channel tiles 2 wave, 2 wave + 1 (W, negated, written over those kr channels:
-    // no other wave reads them in this phase)
+    // right-hand sides: K^ channel tiles 2 wave, 2 wave + 1 (W, negated, into kr) and
+    // this wave's v columns (U~, kept in registers)
     f32x4 Ut[4][2];
     {
-      uint2 af[10];   // block (I, J) at I (I + 1) / 2 + J
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int J = 0; J <= I; ++J)
-          af[I * (I + 1) / 2 + J] = *reinterpret_cast<const uint2*>(&L.at[tr(SBT * I + l16, SBT * J + 4 * q4)]);
-      auto solve = [&](const f32x4(&y0)[4], f32x4(&X)[4]) {
-        uint2 Xb[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          f32x4 y = y0[I];
-#pragma unroll
-          for (int J = 0; J < I; ++J) y = mma16(af[I * (I + 1) / 2 + J], Xb[J], y);
-          X[I] = mma16(af[I * (I + 1) / 2 + I], pack4(y), f32x4{0.f, 0.f, 0.f, 0.f});
-          Xb[I] = pack4(X[I]);
-        }
-      };
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int t = 2 * wave + tt;                       // channels 16 t .. 16 t + 15
-        const int tpos = 32 * (t >> 1) + 4 * (t & 1);      // cpos(16 t)
-        f32x4 y[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          // lane_c (l16, q4) receives channel 16 t + l16 of tokens 16 I + 4 q4 + 0..3
-          const float4 kv = unpack4(ld_tr(&L.kr[rm(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
-          float sc = 1.f;
-          if (!fast) sc = pick(em_of(L, I, 16 * t + (l16 & ~3)), l16 & 3);
-          const float4 kr4 = mul4(ldf4(&L.beta[SBT * I + 4 * q4]), ldf4(&L.rk[SBT * I + 4 * q4]));
-          y[I][0] = kv.x * kr4.x * sc; y[I][1] = kv.y * kr4.y * sc;
-          y[I][2] = kv.z * kr4.z * sc; y[I][3] = kv.w * kr4.w * sc;
-        }
-        f32x4 X[4];
-        solve(y, X);
-        const int wcol = tpos + 8 * (l16 >> 2) + (l16 & 3);   // cpos(16 t + l16)
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) L.kr[rm(SBT * I + 4 * q4 + r, wcol)] = f2bf(-X[I][r]);
-      }
-      if (has_v) {
-        // v -> channels col0 .. col0 + 31 of qw (Q^ is no longer read; no other wave
-        // touches these channels in this phase), then read back transposed
-        {
-          const int vp = col0 + 16 * (lane_c & 1) + 4 * ((lane_c >> 1) & 1);   // cpos(col0 + 8 (l & 3))
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = 4 * (lane_c >> 2) + j;
-            *reinterpret_cast<uint2*>(&L.qw[rm(row, vp)]) = make_uint2(vx[j].x, vx[j].y);
-            *reinterpret_cast<uint2*>(&L.qw[rm(row, vp + 8)]) = make_uint2(vx[j].z, vx[j].w);
-          }
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-          __builtin_amdgcn_wave_barrier();
-        }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int t = 2 * wave + ct;
-          const int tpos = 32 * (t >> 1) + 4 * (t & 1);      // cpos(16 t)
-          f32x4 y[4];
-#pragma unroll
-          for (int I = 0; I < 4; ++I) {
-            const float4 vv = unpack4(ld_tr(&L.qw[rm(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
-            const float4 br = ldf4(&L.beta[SBT * I + 4 * q4]);
-            y[I][0] = vv.x * br.x; y[I][1] = vv.y * br.y;
-            y[I][2] = vv.z * br.z; y[I][3] = vv.w * br.w;
-          }
-          f32x4 X[4];
-          solve(y, X);
-#pragma unroll
-          for (int I = 0; I < 4; ++I) Ut[I][ct] = X[I];
-        }
-      } else {
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) Ut[I][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      uint2 af[10];
+      load_t_frags(L, af, l16, q4);
+      w_tile(L, fast, 2 * wave, af, l16, q4);
+      w_tile(L, fast, 2 * wave + 1, af, l16, q4);
+      stage_v(L, col0, vx, lane_c);
+      u_tiles(L, col0, af, Ut, l16, q4);
     }
     lds_barrier();   // E
 
-    // ---- S: U = U~ - W S;  O = diag(1/|q|) Q^ S + Aqk U;  S <- Diag(e^{g_n}) S + K~^T diag(1/|k|) U
+    // ---- S: U = U~ - W S;  O += Aqk U;  S <- Diag(e^{g_n}) S + K~^T diag(1/|k|) U ----------
     {
       uint4 Sf[4][2];
-      pack_state(Sf);
+      pack_state(S, Sf);
+      minus_ws(L, Sf, Ut, l16, q4);
+    }
+    {
+      uint4 Uf[2][2], qa[6];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        uint4 wf[4];
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) wf[s] = ld128(L.kr, rm(SBT * I + l16, 32 * s + 8 * q4));
+        for (int ct = 0; ct < 2; ++ct) Uf[s][ct] = pack8(Ut[2 * s][ct], Ut[2 * s + 1][ct]);
+      qa[0] = ld128(L.aqk, tr(l16, 8 * q4));
+      qa[1] = ld128(L.aqk, tr(SBT + l16, 8 * q4));
+      qa[2] = ld128(L.aqk, tr(2 * SBT + l16, 8 * q4));
+      qa[3] = ld128(L.aqk, tr(2 * SBT + l16, 32 + 8 * q4));
+      qa[4] = ld128(L.aqk, tr(3 * SBT + l16, 8 * q4));
+      qa[5] = ld128(L.aqk, tr(3 * SBT + l16, 32 + 8 * q4));
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        O[0][ct] = mma32(qa[0], Uf[0][ct], O[0][ct]);
+        O[1][ct] = mma32(qa[1], Uf[0][ct], O[1][ct]);
+        O[2][ct] = mma32(qa[2], Uf[0][ct], O[2][ct]);
+        O[2][ct] = mma32(qa[3], Uf[1][ct], O[2][ct]);
+        O[3][ct] = mma32(qa[4], Uf[0][ct], O[3][ct]);
+        O[3][ct] = mma32(qa[5], Uf[1][ct], O[3][ct]);
+      }
+      // output tile -> this wave's channels of qw (natural order; v is consumed)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) Ut[I][ct] = mma32(wf[s], Sf[s][ct], Ut[I][ct]);
-      }
-      if (OUT) {
-        uint4 Uf[2][2], qa[6];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) Uf[s][ct] = pack8(Ut[2 * s][ct], Ut[2 * s + 1][ct]);
-        qa[0] = ld128(L.aqk, tr(l16, 8 * q4));
-        qa[1] = ld128(L.aqk, tr(SBT + l16, 8 * q4));
-        qa[2] = ld128(L.aqk, tr(2 * SBT + l16, 8 * q4));
-        qa[3] = ld128(L.aqk, tr(2 * SBT + l16, 32 + 8 * q4));
-        qa[4] = ld128(L.aqk, tr(3 * SBT + l16, 8 * q4));
-        qa[5] = ld128(L.aqk, tr(3 * SBT + l16, 32 + 8 * q4));
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          O[0][ct] = mma32(qa[0], Uf[0][ct], O[0][ct]);
-          O[1][ct] = mma32(qa[1], Uf[0][ct], O[1][ct]);
-          O[2][ct] = mma32(qa[2], Uf[0][ct], O[2][ct]);
-          O[2][ct] = mma32(qa[3], Uf[1][ct], O[2][ct]);
-          O[3][ct] = mma32(qa[4], Uf[0][ct], O[3][ct]);
-          O[3][ct] = mma32(qa[5], Uf[1][ct], O[3][ct]);
-        }
-        // output tile -> this wave's channels of qw (natural order) -> o rows, 16 bytes per lane_c;
-        // rows past the end fall outside the buffer bound and are dropped
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.qw[rm(SBT * I + 4 * q4 + r, col0 + 16 * ct + l16)] = f2bf(O[I][ct][r]);
-      }
+          for (int r = 0; r < 4; ++r) L.qw[rm(SBT * I + 4 * q4 + r, col0 + 16 * ct + l16)] = f2bf(O[I][ct][r]);
     }
+    update_state(L, fast, S, Ut, l16, q4);
     {
-      uint4 Upf[2][2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const float4 ka = ldf4(&L.rk[32 * s + 4 * q4]), kb = ldf4(&L.rk[32 * s + 16 + 4 * q4]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          f32x4 lo = Ut[2 * s][ct], hi = Ut[2 * s + 1][ct];
-          lo[0] *= ka.x; lo[1] *= ka.y; lo[2] *= ka.z; lo[3] *= ka.w;
-          hi[0] *= kb.x; hi[1] *= kb.y; hi[2] *= kb.z; hi[3] *= kb.w;
-          Upf[s][ct] = pack8(lo, hi);
-        }
-      }
-      // A operand K~^T: lane_c (l16, q4) = channel 16 rt + l16, tokens 32 s + 4 q4 + 0..3
-      // and 32 s + 16 + 4 q4 + 0..3, read transposed from kc
-      const int kbase = rm(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt) {
-        const int cp = 32 * (rt >> 1) + 4 * (rt & 1);   // cpos(16 rt)
-        uint4 kt[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          kt[s] = cat(ld_tr(&L.kc[kbase + rm(32 * s, cp)]), ld_tr(&L.kc[kbase + rm(32 * s + 16, cp)]));
-        const float4 eg = ldf4(&L.egn[16 * rt + 4 * q4]);
-        if (fast) {
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            f32x4 acc = S[rt][ct];
-            acc = mma32(kt[0], Upf[0][ct], acc);
-            acc = mma32(kt[1], Upf[1][ct], acc);
-            acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
-            S[rt][ct] = acc;
-          }
-        } else {
-          // blocked: K~ = K_ e^{g_n - m_I} for the tokens of block I
-          const int cl = 16 * rt + (l16 & ~3), u = l16 & 3;
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const float f0 = pick(enm_of(L, 2 * s, cl), u), f1 = pick(enm_of(L, 2 * s + 1, cl), u);
-            kt[s] = scale8(kt[s], make_float4(f0, f0, f0, f0), make_float4(f1, f1, f1, f1));
-          }
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            f32x4 acc = S[rt][ct];
-            acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
-            acc = mma32(kt[0], Upf[0][ct], acc);
-            acc = mma32(kt[1], Upf[1][ct], acc);
-            S[rt][ct] = acc;
-          }
-        }
-      }
-    }
-    if (OUT) {
       // staged output rows -> o, 16 bytes per lane; rows past the end fall outside the
       // buffer bound and are dropped
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       const int so2 = (int)(a.H * D) * 2;
       const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((b * a.T + t0) * a.H + h) * D), 0, n * so2,
@@ -890,17 +852,238 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       }
     }
     lds_barrier();   // F
-
-    if (!OUT) {
-      const int64_t rel = c - c_begin;
-      if ((rel + 1) % a.Lo == 0) {
-        const int e = p * kSub + (int)(rel / a.Lo);
-        store_state((mkind ? a.WM : a.WS) + (bh * a.E + e) * D * D);
-      }
-    }
   }
 
-  if (OUT && a.S_final != nullptr && p == a.P - 1) store_state(a.S_final + bh * D * D);
+  if (a.S_final != nullptr && p == a.P - 1) store_state(S, a.S_final + bh * D * D, svo);
+}
+
+// Summary pass: one block of 8 waves per (batch, head, summary segment). Waves 0-3 run
+// S from 0 (state columns 32 w ..), waves 4-7 the transition M from I (columns
+// 32 (w - 4) ..); the chunk operands, A, T and W are formed once for both. The state
+// is written at every output-segment boundary (every Lo chunks).
+//
+// Per chunk, phases and the barriers after them:
+//   loads; E1: partial norms, block decay products            | B
+//   E2/E3: norms, decay factors, operands kr kc; v loads       | C
+//   M1T: A blocks, diagonal inverses                           | D
+//   X: W (channel tile w, into kr); U~ (waves 0-3)             | E
+//   S: U = U~ - W S (or -W M), state update                    | F
+__global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_sum_kernel(ChunkArgs a) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  Lds& L = *reinterpret_cast<Lds*>(lds_raw);
+  float (&nk)[2][CT] = *reinterpret_cast<float(*)[2][CT]>(lds_raw + sizeof(Lds));   // partial |k|^2
+
+  const uint32_t lid = (a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid) : blockIdx.x;
+  if (lid >= (uint32_t)a.nblk) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const bool mkind = wave >= 4;
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int64_t bh = lid / a.P;
+  const int p = lid % a.P;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int64_t NC = (a.T + CT - 1) / CT;
+  const int64_t c_begin = (int64_t)p * a.L;
+  const int64_t c_end = min<int64_t>(min<int64_t>(NC, c_begin + a.L), a.c_stop);
+
+  const int col0 = 32 * (wave & 3);
+  const int svo = (4 * q4) * D + col0 + l16;
+  f32x4 S[8][2];
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * q4 + r, col = col0 + 16 * ct + l16;
+        S[rt][ct][r] = (mkind && row == col) ? 1.f : 0.f;
+      }
+
+  const uint32_t kOne = 0x3F803F80u;   // alpha = 1 past the end
+
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    int lane_c = lane;
+    asm volatile("" : "+v"(lane_c));
+    const int l16 = lane_c & 15, q4 = lane_c >> 4;
+    // elementwise mapping: wave -> decay block I = wave & 3 and channel half hc;
+    // half-wave hf = tokens 8 hf .. 8 hf + 7 of the block; lane cg = channels c0, c0 + 1
+    const int I = wave & 3, hc = wave >> 2;
+    const int hf = lane_c >> 5, cg = lane_c & 31, c0 = 64 * hc + 2 * cg, p0 = cpos(c0);
+    const int tk0 = SBT * I + 8 * hf;
+    const int64_t t0 = c * CT;
+    const int n = (int)min<int64_t>(CT, a.T - t0);
+
+    // ---- loads ----------------------------------------------------------------------
+    uint32_t kx[8], ax[8], a8;
+    float bt;
+    {
+      const int64_t row0 = b * a.T + t0;
+      const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
+      const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
+      const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
+      const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
+      const int vk = (8 * hf) * st2 + 2 * c0, va = (8 * hf) * sa2 + 2 * c0;
+      const int tb = SBT * I;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kx[i] = __builtin_amdgcn_raw_buffer_load_b32(rk_, vk, (tb + i) * st2, 0);
+        const uint32_t av = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + i) * sa2, 0);
+        ax[i] = tk0 + i < n ? av : kOne;
+      }
+      const uint32_t av8 = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + 8) * sa2, 0);
+      a8 = (hf == 0 && tk0 + 8 < n) ? av8 : kOne;
+      bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb_, (tid & 63) * (int)a.H * 2, 0, 0));
+    }
+
+    // ---- E1: partial norms, block decay products ---------------------------------------
+    if (tid < CT) L.beta[tid] = bt;
+    if (a.l2norm) {
+      float ss[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float k0 = bf_lo(kx[i]), k1 = bf_hi(kx[i]);
+        ss[i] = k0 * k0 + k1 * k1;
+        ss[i + 8] = 0.f;
+      }
+      const float tot = half_sum16(ss, lane_c);
+      const int vv = (lane_c >> 1) & 15;
+      if ((lane_c & 1) == 0 && vv < 8) nk[hc][tk0 + vv] = tot;
+    }
+    {
+      float r0, r1;
+      if (hf == 1) {
+        r0 = bf_lo(ax[1]); r1 = bf_hi(ax[1]);
+#pragma unroll
+        for (int i = 2; i < 8; ++i) { r0 *= bf_lo(ax[i]); r1 *= bf_hi(ax[i]); }
+        *reinterpret_cast<float2*>(&L.pf[I][c0]) = make_float2(r0, r1);
+      } else {
+        r0 = bf_lo(a8); r1 = bf_hi(a8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { r0 *= bf_lo(ax[i]); r1 *= bf_hi(ax[i]); }
+        *reinterpret_cast<float2*>(&L.pb[I][c0]) = make_float2(r0, r1);
+      }
+    }
+    lds_barrier();   // B
+
+    // ---- E2 / E3: norms, decay factors, MFMA operands ---------------------------------
+    if (wave < 4 && lane_c < SBT) {
+      const int t = SBT * wave + lane_c;
+      L.rk[t] = a.l2norm ? __builtin_amdgcn_rsqf(nk[0][t] + nk[1][t] + kL2Eps) : 1.f;
+    }
+    bool fast;
+    {
+      float2 full[NSB];
+      float2 pbw = make_float2(1.f, 1.f), eo = make_float2(1.f, 1.f);
+#pragma unroll
+      for (int J = 0; J < NSB; ++J) {
+        const float2 pbJ = *reinterpret_cast<const float2*>(&L.pb[J][c0]);
+        const float2 pfJ = *reinterpret_cast<const float2*>(&L.pf[J][c0]);
+        full[J] = make_float2(pbJ.x * pfJ.x, pbJ.y * pfJ.y);
+        if (J == I) pbw = pbJ;
+        // the other channel half, formed the same way, so that every wave votes alike
+        const float2 pbo = *reinterpret_cast<const float2*>(&L.pb[J][c0 ^ 64]);
+        const float2 pfo = *reinterpret_cast<const float2*>(&L.pf[J][c0 ^ 64]);
+        eo.x *= pbo.x * pfo.x;
+        eo.y *= pbo.y * pfo.y;
+      }
+      float2 egn2 = full[0], em2 = pbw;
+#pragma unroll
+      for (int J = 1; J < NSB; ++J) { egn2.x *= full[J].x; egn2.y *= full[J].y; }
+#pragma unroll
+      for (int J = 0; J < NSB - 1; ++J)
+        if (J < I) { em2.x *= full[J].x; em2.y *= full[J].y; }
+      fast = __all(fminf(fminf(egn2.x, egn2.y), fminf(eo.x, eo.y)) >= kFastMin) != 0;
+      if (I == 0 && hf == 0) *reinterpret_cast<float2*>(&L.egn[c0]) = egn2;
+      const float2 one2 = make_float2(1.f, 1.f);
+      const float2 mr = fast ? em2 : one2;
+      const float2 mc = fast ? make_float2(__builtin_amdgcn_rcpf(em2.x), __builtin_amdgcn_rcpf(em2.y)) : one2;
+      auto put = [&](int i, float er0, float er1, float ec0, float ec1) {
+        const int tk = tk0 + i;
+        const float k0 = bf_lo(kx[i]), k1 = bf_hi(kx[i]);
+        *reinterpret_cast<uint32_t*>(&L.kr[rm(tk, p0)]) = pack_bf16x2(k0 * er0 * mr.x, k1 * er1 * mr.y);
+        *reinterpret_cast<uint32_t*>(&L.kc[rm(tk, p0)]) = pack_bf16x2(k0 * ec0 * mc.x, k1 * ec1 * mc.y);
+      };
+      if (hf == 1) {
+        float r0 = 1.f, r1 = 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i > 0) { r0 *= bf_lo(ax[i]); r1 *= bf_hi(ax[i]); }
+          put(i, r0, r1, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1));
+        }
+      } else {
+        float r0 = bf_lo(a8), r1 = bf_hi(a8);
+#pragma unroll
+        for (int i = 7; i >= 0; --i) {
+          if (i < 7) { r0 *= bf_lo(ax[i + 1]); r1 *= bf_hi(ax[i + 1]); }
+          put(i, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1), r0, r1);
+        }
+      }
+    }
+    uint4 vx[4];
+    if (!mkind) load_v(a, b, h, t0, n, col0, lane_c, vx);
+    lds_barrier();   // C
+
+    // ---- M1T: A blocks, diagonal inverses ------------------------------------------------
+    {
+      uint4 cA[4], rA[4], sc[4];
+      // waves 0-3: A(w, w) and its inverse; wave 4: A10 A30; 5: A20 A31; 6: A21; 7: A32
+      if (wave < 4) {
+        tile_frags(L.kc, wave, cA, l16, q4);
+        tile_frags(L.kr, wave, rA, l16, q4);
+        epi_a(L, wave, wave, mma4(rA, cA), l16, q4);
+        invert_diag(L, wave, lane_c);
+      } else if (wave == 4) {
+        tile_frags(L.kc, 0, cA, l16, q4);
+        tile_frags(L.kr, 1, rA, l16, q4); pair_frags(L, fast, 1, 0, cA, sc, q4); epi_a(L, 1, 0, mma4(rA, sc), l16, q4);
+        tile_frags(L.kr, 3, rA, l16, q4); pair_frags(L, fast, 3, 0, cA, sc, q4); epi_a(L, 3, 0, mma4(rA, sc), l16, q4);
+      } else if (wave == 5) {
+        tile_frags(L.kc, 0, cA, l16, q4);
+        tile_frags(L.kr, 2, rA, l16, q4); pair_frags(L, fast, 2, 0, cA, sc, q4); epi_a(L, 2, 0, mma4(rA, sc), l16, q4);
+        tile_frags(L.kc, 1, cA, l16, q4);
+        tile_frags(L.kr, 3, rA, l16, q4); pair_frags(L, fast, 3, 1, cA, sc, q4); epi_a(L, 3, 1, mma4(rA, sc), l16, q4);
+      } else if (wave == 6) {
+        tile_frags(L.kc, 1, cA, l16, q4);
+        tile_frags(L.kr, 2, rA, l16, q4); pair_frags(L, fast, 2, 1, cA, sc, q4); epi_a(L, 2, 1, mma4(rA, sc), l16, q4);
+      } else {
+        tile_frags(L.kc, 2, cA, l16, q4);
+        tile_frags(L.kr, 3, rA, l16, q4); pair_frags(L, fast, 3, 2, cA, sc, q4); epi_a(L, 3, 2, mma4(rA, sc), l16, q4);
+      }
+    }
+    lds_barrier();   // D
+
+    // ---- X: W channel tile w (into kr); U~ for the S columns ----------------------------
+    f32x4 Ut[4][2];
+    {
+      uint2 af[10];
+      load_t_frags(L, af, l16, q4);
+      w_tile(L, fast, wave, af, l16, q4);
+      if (!mkind) {
+        stage_v(L, col0, vx, lane_c);
+        u_tiles(L, col0, af, Ut, l16, q4);
+      } else {
+#pragma unroll
+        for (int I2 = 0; I2 < 4; ++I2)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) Ut[I2][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    lds_barrier();   // E
+
+    // ---- S: U = U~ - W S (M: U = -W M), state update ------------------------------------
+    {
+      uint4 Sf[4][2];
+      pack_state(S, Sf);
+      minus_ws(L, Sf, Ut, l16, q4);
+    }
+    update_state(L, fast, S, Ut, l16, q4);
+    lds_barrier();   // F
+
+    const int64_t rel = c - c_begin;
+    if ((rel + 1) % a.Lo == 0) {
+      const int e = p * kSub + (int)(rel / a.Lo);
+      store_state(S, (mkind ? a.WM : a.WS) + (bh * a.E + e) * D * D, svo);
+    }
+  }
 }
 
 // The chain of segment starts, S_start(0) = S0 (or 0) and
@@ -1059,17 +1242,17 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   a.T = x.T;
   a.H = x.H;
   a.l2norm = x.l2norm ? 1 : 0;
-  const size_t lds = sizeof(Lds);
+  const size_t lds = sizeof(Lds), lds_sum = sizeof(Lds) + 2 * CT * sizeof(float);
   int dev = 0;
   hipError_t de = hipGetDevice(&dev);
   if (de != hipSuccess) return de;
   static bool attr_done[64] = {};
   if (dev < 0 || dev >= 64 || !attr_done[dev]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<true>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_out_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_chunk_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_sum_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds_sum);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_done[dev] = true;
   }
@@ -1087,9 +1270,9 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
     s.Lo = sp.Lo;
     s.E = (int)E;
     s.c_stop = (int64_t)(sp.Po - 1) * sp.Lo;
-    s.nblk = (int)(2 * BH * sp.Ps);
+    s.nblk = (int)(BH * sp.Ps);
     s.grid = round8(s.nblk);
-    hipLaunchKernelGGL(kda_chunk_kernel<false>, dim3((unsigned)s.grid), dim3(NTHR), lds, stream, s);
+    hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(2 * NTHR), lds_sum, stream, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kda_combine_kernel, dim3((unsigned)(BH * 8)), dim3(CB_T), 0, stream, WS, WM, x.S0, Sst, sp.Po,
@@ -1107,7 +1290,7 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   a.c_stop = 0;
   a.nblk = (int)(BH * sp.Po);
   a.grid = round8(a.nblk);
-  hipLaunchKernelGGL(kda_chunk_kernel<true>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
+  hipLaunchKernelGGL(kda_out_kernel, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
   return hipGetLastError();
 }
 
