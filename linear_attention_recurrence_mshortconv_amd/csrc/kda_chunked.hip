@@ -475,6 +475,28 @@ __device__ __forceinline__ void store_state(const f32x4 (&S)[8][2], float* m, in
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(16 * rt + r) * D + 16 * ct] = S[rt][ct][r];
 }
+// Workspace matrices ([D][D] fp32 states and transitions) are kept tile-major: the
+// 16 x 16 tile (rt, column block cb, ct) is 256 contiguous floats, lane l = 16 q4 + l16
+// holding rows 16 rt + 4 q4 .. + 3 of column 32 cb + 16 ct + l16 (the MFMA D layout),
+// so that states move as 16-byte pieces.
+__device__ __forceinline__ int tile_off(int cb, int rt, int ct, int lane) {
+  return (((cb * 8 + rt) * 2 + ct) * 64 + lane) * 4;
+}
+__device__ __forceinline__ void store_tiles(const f32x4 (&S)[8][2], float* m, int cb, int lane) {
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) *reinterpret_cast<f32x4*>(m + tile_off(cb, rt, ct, lane)) = S[rt][ct];
+}
+__device__ __forceinline__ f32x4 load_tile4(const float* m, int cb, int rt, int ct, int lane) {
+  return *reinterpret_cast<const f32x4*>(m + tile_off(cb, rt, ct, lane));
+}
+// m[row][k .. k + 3] of a tile-major matrix, k a multiple of 4
+__device__ __forceinline__ float4 load_row4(const float* m, int row, int k) {
+  const float* p = m + tile_off(k >> 5, row >> 4, (k >> 4) & 1, 16 * ((row & 15) >> 2) + (k & 15)) + (row & 3);
+  return make_float4(p[0], p[4], p[8], p[12]);
+}
+
 // v of the state columns col0 .. col0 + 31 of the chunk: lane = tokens 4 (lane >> 2) + j,
 // channels col0 + 8 (lane & 3) .. + 7; tokens past the end read as zero
 __device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t b, int64_t h, int64_t t0, int n, int col0,
@@ -527,9 +549,16 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   const int col0 = 32 * wave;
   const int svo = (4 * q4) * D + col0 + l16;   // lane part of a state element's offset
   f32x4 S[8][2];
-  {
-    const float* src = a.P > 1 ? a.Sstart + (bh * a.P + p) * D * D : (a.S0 ? a.S0 + bh * D * D : nullptr);
-    if (a.P > 1 && p % kSub != 0) src = nullptr;   // formed below
+  if (a.P > 1) {
+    if (p % kSub == 0) {   // a chain start (tile-major)
+      const float* src = a.Sstart + (bh * a.P + p) * D * D;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) S[rt][ct] = load_tile4(src, wave, rt, ct, lane);
+    }
+  } else {                 // S0 ([D][D] row-major) or zero
+    const float* src = a.S0 ? a.S0 + bh * D * D : nullptr;
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -549,34 +578,27 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const int col = col0 + 16 * ct + l16;
-        float4 v0, v1;
-        v0.x = base[(32 * s + 4 * q4 + 0) * D + col]; v0.y = base[(32 * s + 4 * q4 + 1) * D + col];
-        v0.z = base[(32 * s + 4 * q4 + 2) * D + col]; v0.w = base[(32 * s + 4 * q4 + 3) * D + col];
-        v1.x = base[(32 * s + 16 + 4 * q4 + 0) * D + col]; v1.y = base[(32 * s + 16 + 4 * q4 + 1) * D + col];
-        v1.z = base[(32 * s + 16 + 4 * q4 + 2) * D + col]; v1.w = base[(32 * s + 16 + 4 * q4 + 3) * D + col];
+        const f32x4 v0 = load_tile4(base, wave, 2 * s, ct, lane), v1 = load_tile4(base, wave, 2 * s + 1, ct, lane);
         uint2 l0, l1;
-        const uint2 h0 = pack_split(v0, l0), h1 = pack_split(v1, l1);
+        const uint2 h0 = pack_split(make_float4(v0[0], v0[1], v0[2], v0[3]), l0);
+        const uint2 h1 = pack_split(make_float4(v1[0], v1[1], v1[2], v1[3]), l1);
         bH[s][ct] = cat(h0, h1);
         bL[s][ct] = cat(l0, l1);
       }
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt) {
       uint4 aH[4], aL[4];
-      const float* mrow = Mp + (16 * rt + l16) * D;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint2 l0, l1;
-        const uint2 h0 = pack_split(ldf4(mrow + 32 * s + 4 * q4), l0);
-        const uint2 h1 = pack_split(ldf4(mrow + 32 * s + 16 + 4 * q4), l1);
+        const uint2 h0 = pack_split(load_row4(Mp, 16 * rt + l16, 32 * s + 4 * q4), l0);
+        const uint2 h1 = pack_split(load_row4(Mp, 16 * rt + l16, 32 * s + 16 + 4 * q4), l1);
         aH[s] = cat(h0, h1);
         aL[s] = cat(l0, l1);
       }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        f32x4 acc0, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc0[r] = Sp[svo + (16 * rt + r) * D + 16 * ct];
+        f32x4 acc0 = load_tile4(Sp, wave, rt, ct, lane), acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           acc1 = mma32(aL[s], bH[s][ct], acc1);
@@ -900,6 +922,36 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
       }
 
   const uint32_t kOne = 0x3F803F80u;   // alpha = 1 past the end
+  // Raw inputs of one chunk for this lane: k and alpha of tokens tk0 .. tk0 + 7 at
+  // channels c0, c0 + 1, alpha of the block's token 8, beta of token (tid & 63).
+  // Buffer loads bounded by the chunk's valid tokens (zero past the end). The next
+  // chunk's loads are issued during the state update of the current one.
+  struct Raw {
+    uint32_t k[8], a[8], a8;
+    uint16_t bt;
+  };
+  auto issue = [&](int64_t c, Raw& R, int lane_c) {
+    const int I = wave & 3, hc = wave >> 2;
+    const int hf = lane_c >> 5, c0 = 64 * hc + 2 * (lane_c & 31);
+    const int64_t t0 = c * CT;
+    const int n = (int)min<int64_t>(CT, a.T - t0);
+    const int64_t row0 = b * a.T + t0;
+    const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
+    const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
+    const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
+    const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
+    const int vk = (8 * hf) * st2 + 2 * c0, va = (8 * hf) * sa2 + 2 * c0;
+    const int tb = SBT * I;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      R.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk_, vk, (tb + i) * st2, 0);
+      R.a[i] = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + i) * sa2, 0);
+    }
+    R.a8 = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + 8) * sa2, 0);
+    R.bt = __builtin_amdgcn_raw_buffer_load_b16(rb_, (lane_c & 63) * (int)a.H * 2, 0, 0);
+  };
+  Raw nxt;
+  if (c_begin < c_end) issue(c_begin, nxt, lane);
 
   for (int64_t c = c_begin; c < c_end; ++c) {
     int lane_c = lane;
@@ -913,27 +965,15 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t t0 = c * CT;
     const int n = (int)min<int64_t>(CT, a.T - t0);
 
-    // ---- loads ----------------------------------------------------------------------
-    uint32_t kx[8], ax[8], a8;
-    float bt;
-    {
-      const int64_t row0 = b * a.T + t0;
-      const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
-      const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
-      const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
-      const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
-      const int vk = (8 * hf) * st2 + 2 * c0, va = (8 * hf) * sa2 + 2 * c0;
-      const int tb = SBT * I;
+    const Raw cur = nxt;
+    uint32_t kx[8], ax[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        kx[i] = __builtin_amdgcn_raw_buffer_load_b32(rk_, vk, (tb + i) * st2, 0);
-        const uint32_t av = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + i) * sa2, 0);
-        ax[i] = tk0 + i < n ? av : kOne;
-      }
-      const uint32_t av8 = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + 8) * sa2, 0);
-      a8 = (hf == 0 && tk0 + 8 < n) ? av8 : kOne;
-      bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb_, (tid & 63) * (int)a.H * 2, 0, 0));
+    for (int i = 0; i < 8; ++i) {
+      kx[i] = cur.k[i];
+      ax[i] = tk0 + i < n ? cur.a[i] : kOne;
     }
+    const uint32_t a8 = (hf == 0 && tk0 + 8 < n) ? cur.a8 : kOne;
+    const float bt = bf2f(cur.bt);
 
     // ---- E1: partial norms, block decay products ---------------------------------------
     if (tid < CT) L.beta[tid] = bt;
@@ -1070,6 +1110,7 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     lds_barrier();   // E
 
     // ---- S: U = U~ - W S (M: U = -W M), state update ------------------------------------
+    if (c + 1 < c_end) issue(c + 1, nxt, lane_c);
     {
       uint4 Sf[4][2];
       pack_state(S, Sf);
@@ -1081,7 +1122,7 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t rel = c - c_begin;
     if ((rel + 1) % a.Lo == 0) {
       const int e = p * kSub + (int)(rel / a.Lo);
-      store_state(S, (mkind ? a.WM : a.WS) + (bh * a.E + e) * D * D, svo);
+      store_tiles(S, (mkind ? a.WM : a.WS) + (bh * a.E + e) * D * D, wave & 3, lane);
     }
   }
 }
@@ -1117,10 +1158,8 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
   f32x4 cur;
 #pragma unroll
   for (int r = 0; r < 4; ++r) cur[r] = S0 ? S0[(bh * D + row0 + r) * D + col] : 0.f;
-  auto store = [&](int po, const f32x4& v) {
-    float* dst = Sst + (bh * P + po) * D * D;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(row0 + r) * D + col] = v[r];
+  auto store = [&](int po, const f32x4& v) {   // tile-major
+    *reinterpret_cast<f32x4*>(Sst + (bh * P + po) * D * D + tile_off(slice >> 1, wave, slice & 1, lane)) = v;
   };
   store(0, cur);
   const int nsteps = (P - 1) / kSub;   // chain starts kSub, 2 kSub, .. below P
@@ -1130,15 +1169,13 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
   auto fetch = [&](int step, float4(&m)[8], f32x4& sv) {
     if (step < nsteps) {
       const int e = step * kSub + kSub - 1;
-      const float* mp = WM + ((bh * E + e) * D + arow) * D;
+      const float* mp = WM + (bh * E + e) * D * D;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        m[2 * s] = ldf4(mp + 32 * s + 4 * q4);
-        m[2 * s + 1] = ldf4(mp + 32 * s + 16 + 4 * q4);
+        m[2 * s] = load_row4(mp, arow, 32 * s + 4 * q4);
+        m[2 * s + 1] = load_row4(mp, arow, 32 * s + 16 + 4 * q4);
       }
-      const float* sp = WS + (bh * E + e) * D * D;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sv[k] = sp[(row0 + k) * D + col];
+      sv = load_tile4(WS + (bh * E + e) * D * D, slice >> 1, wave, slice & 1, lane);
     }
   };
 #pragma unroll
