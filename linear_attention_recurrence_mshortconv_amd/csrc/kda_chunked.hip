@@ -82,10 +82,13 @@ __device__ __forceinline__ float4 rcp4(float4 a) {
   return make_float4(__builtin_amdgcn_rcpf(a.x), __builtin_amdgcn_rcpf(a.y), __builtin_amdgcn_rcpf(a.z),
                      __builtin_amdgcn_rcpf(a.w));
 }
-__device__ __forceinline__ float dot4(uint2 u) {
-  const float4 f = unpack4(u);
-  return f.x * f.x + f.y * f.y + f.z * f.z + f.w * f.w;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// sum of squares of the bf16 pair(s) in u (v_dot2_f32_bf16)
+__device__ __forceinline__ float sq2(uint32_t u, float c) {
+  const bf16x2_t v = __builtin_bit_cast(bf16x2_t, u);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, c, false);
 }
+__device__ __forceinline__ float dot4(uint2 u) { return sq2(u.y, sq2(u.x, 0.f)); }
 __device__ __forceinline__ float pick(float4 v, int u) { return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w; }
 // v split into bf16 high parts (returned) and low parts v - hi (in lo)
 __device__ __forceinline__ uint2 pack_split(const float4& v, uint2& lo) {
@@ -119,8 +122,8 @@ struct Lds {
   float rk[CT];           // 1/|k_t| (1 without normalisation)
   float rq[CT];
   float egn[D];           // e^{g_n}
-  float pb[NSB][D];       // per block and channel: product of alpha over block tokens 0..8
-  float pf[NSB][D];       //                        ... over block tokens 9..15
+  float pb[NSB][D];       // per block and channel: product of alpha over block tokens 0..7
+  float pf[NSB][D];       //                        ... over block tokens 8..15
   float adiag[NSB][SBT][20];   // strictly lower A_II in fp32, column k at 4*(k&3) + (k>>2)
   uint16_t at[CT * TRS];  // -A in the blocks below the diagonal, T_II on it (natural order)
   uint16_t aqk[CT * TRS]; // Aqk (rows scaled 1/|q|, columns 1/|k|), token columns at cpos
@@ -216,9 +219,9 @@ __device__ __forceinline__ uint2 ld_tr(const uint16_t* p) {
 }
 
 // Decay factors of the blocked factorisation for channels c..c+3 (from pb, pf):
-//   em(I)     = e^{m_I}         product of alpha from the chunk start to block I's token 8
-//   enm(I)    = e^{g_n - m_I}   ... after block I's token 8 to the chunk end
-//   pair(I,J) = e^{m_I - m_J}   ... after block J's token 8 to block I's token 8
+//   em(I)     = e^{m_I}         product of alpha from the chunk start to block I's token 7
+//   enm(I)    = e^{g_n - m_I}   ... after block I's token 7 to the chunk end
+//   pair(I,J) = e^{m_I - m_J}   ... after block J's token 7 to block I's token 7
 __device__ __forceinline__ float4 ldf4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ float4 em_of(const Lds& L, int I, int c) {
   float4 r = ldf4(&L.pb[I][c]);
@@ -523,10 +526,11 @@ __device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t b, int64_t h,
 //   S: U = U~ - W S, O += Aqk U, state update, o store      | F
 //
 // Two factorisations of the pairwise decay e^{g_i - g_j} are used:
-//  * fast: one reference at the chunk start (K^ = K e^{g}, K_ = K e^{-g}); valid
+//  * fast: one reference at the chunk start (K^ = K e^{g}, K_ = K e^{-g}, formed from
+//    prefix and suffix products of alpha); valid
 //    while every channel decays by less than e^{-80} over the chunk, chosen per
 //    chunk by a block-wide vote;
-//  * blocked: references at token 8 of each 16-token block, with the factors
+//  * blocked: references at token 7 of each 16-token block, with the factors
 //    e^{m_I - m_J}, e^{m_I}, e^{g_n - m_I} applied to fragments as they are
 //    read; valid while log(alpha) >= -11 per token.
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_out_kernel(ChunkArgs a) {
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     // Buffer loads: block-uniform base and bounds (the chunk's first n tokens), byte
     // offsets split into a lane part and a uniform part. Reads past the bound return
     // zero, which is k = q = v = beta = 0 for tokens past the end; alpha is set to 1.
-    uint2 kx[8], qx[8], ax[8], a8;
+    uint2 kx[8], qx[8], ax[8];
     float bt;
     {
       const int64_t row0 = b * a.T + t0;
@@ -653,8 +657,6 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
         const uint2 av = ld_buf64(ra_, va, (tb + i) * sa2);
         ax[i] = tk0 + i < n ? av : kOnes;
       }
-      const uint2 av8 = ld_buf64(ra_, va, (tb + 8) * sa2);
-      a8 = (hf == 0 && tk0 + 8 < n) ? av8 : kOnes;
       bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb_, tid * (int)a.H * 2, 0, 0));
     }
 
@@ -677,62 +679,83 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       L.rk[tk0 + cg] = 1.f;
       L.rq[tk0 + cg] = 1.f;
     }
-    if (hf == 1) {
-      float4 run = unpack4(ax[1]);
+    float4 al[8];   // alpha of the lane's tokens
 #pragma unroll
-      for (int i = 2; i < 8; ++i) run = mul4(run, unpack4(ax[i]));
-      *reinterpret_cast<float4*>(&L.pf[wave][c0]) = run;
-    } else {
-      float4 run = unpack4(a8);
+    for (int i = 0; i < 8; ++i) al[i] = unpack4(ax[i]);
+    {
+      float4 hp = al[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) run = mul4(run, unpack4(ax[i]));
-      *reinterpret_cast<float4*>(&L.pb[wave][c0]) = run;
+      for (int i = 1; i < 8; ++i) hp = mul4(hp, al[i]);
+      *reinterpret_cast<float4*>(hf ? &L.pf[wave][c0] : &L.pb[wave][c0]) = hp;
     }
     lds_barrier();   // B
 
     // ---- E2 / E3: decay factors and MFMA operands --------------------------------------
     bool fast;
     {
-      float4 full[NSB], pbw = make_float4(1.f, 1.f, 1.f, 1.f);
+      // per channel: before = decay over the blocks before this one, after = over the
+      // blocks after it; the lane's half adds its block's other half on one side
+      float4 full[NSB], h0w = make_float4(1.f, 1.f, 1.f, 1.f), h1w = h0w;
 #pragma unroll
       for (int J = 0; J < NSB; ++J) {
-        const float4 pbJ = ldf4(&L.pb[J][c0]);
-        full[J] = mul4(pbJ, ldf4(&L.pf[J][c0]));
-        if (J == wave) pbw = pbJ;
+        const float4 h0 = ldf4(&L.pb[J][c0]), h1 = ldf4(&L.pf[J][c0]);
+        full[J] = mul4(h0, h1);
+        if (J == wave) { h0w = h0; h1w = h1; }
       }
-      float4 egn4 = full[0], em4 = pbw;
+      float4 egn4 = full[0], before = make_float4(1.f, 1.f, 1.f, 1.f), after = before;
 #pragma unroll
       for (int J = 1; J < NSB; ++J) egn4 = mul4(egn4, full[J]);
 #pragma unroll
-      for (int J = 0; J < NSB - 1; ++J)
-        if (J < wave) em4 = mul4(em4, full[J]);
+      for (int J = 0; J < NSB; ++J) {
+        if (J < wave) before = mul4(before, full[J]);
+        if (J > wave) after = mul4(after, full[J]);
+      }
       // every wave holds all 128 channels, so every wave reaches the same vote
       fast = __all(fminf(fminf(egn4.x, egn4.y), fminf(egn4.z, egn4.w)) >= kFastMin) != 0;
       if (wave == 0 && hf == 0) *reinterpret_cast<float4*>(&L.egn[c0]) = egn4;
-      const float4 iem4 = rcp4(em4);
-      // er = e^{g - m_I}, ec = e^{m_I - g}: running products from the block's token 8
-      const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
-      const float4 mr = fast ? em4 : one4, mc = fast ? iem4 : one4;
-      auto put = [&](int i, float4 er, float4 ec) {
-        const float4 fr = mul4(er, mr), fc = mul4(ec, mc);
+      auto put = [&](int i, float4 fr, float4 fc) {
         const int tk = tk0 + i;
         *reinterpret_cast<uint2*>(&L.kr[rm(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fr));
         *reinterpret_cast<uint2*>(&L.kc[rm(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fc));
         *reinterpret_cast<uint2*>(&L.qw[rm(tk, p0)]) = pack4(mul4(unpack4(qx[i]), fr));
       };
-      if (hf == 1) {
-        float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (fast) {
+        // e^{g_t} as a prefix product from the chunk start and e^{g_n - g_t} / e^{g_n} as a
+        // suffix product towards the chunk end: no per-element reciprocal, and the same
+        // instruction stream in both half-waves
+        const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
+        float4 fw = hf ? mul4(before, h0w) : before;
+        float4 bw = mul4(hf ? after : mul4(after, h1w), rcp4(egn4));
+        float4 fr[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          if (i > 0) run = mul4(run, unpack4(ax[i]));
-          put(i, run, rcp4(run));
+          fw = mul4(fw, al[i]);
+          fr[i] = fw;
         }
-      } else {
-        float4 run = unpack4(a8);
 #pragma unroll
         for (int i = 7; i >= 0; --i) {
-          if (i < 7) run = mul4(run, unpack4(ax[i + 1]));
-          put(i, rcp4(run), run);
+          put(i, fr[i], bw);
+          if (i > 0) bw = mul4(bw, al[i]);
+        }
+        (void)one4;
+      } else {
+        // blocked: reference m_I = g at the block's token 7; half 1 runs forward
+        // (e^{g - m_I} = product over tokens 8..t), half 0 backward (e^{m_I - g} =
+        // product over tokens t+1..7)
+        if (hf == 1) {
+          float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            run = mul4(run, al[i]);
+            put(i, run, rcp4(run));
+          }
+        } else {
+          float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+          for (int i = 7; i >= 0; --i) {
+            put(i, rcp4(run), run);
+            run = mul4(run, al[i]);
+          }
         }
       }
     }
@@ -923,11 +946,11 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
 
   const uint32_t kOne = 0x3F803F80u;   // alpha = 1 past the end
   // Raw inputs of one chunk for this lane: k and alpha of tokens tk0 .. tk0 + 7 at
-  // channels c0, c0 + 1, alpha of the block's token 8, beta of token (tid & 63).
+  // channels c0, c0 + 1, beta of token (tid & 63).
   // Buffer loads bounded by the chunk's valid tokens (zero past the end). The next
   // chunk's loads are issued during the state update of the current one.
   struct Raw {
-    uint32_t k[8], a[8], a8;
+    uint32_t k[8], a[8];
     uint16_t bt;
   };
   auto issue = [&](int64_t c, Raw& R, int lane_c) {
@@ -947,7 +970,6 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
       R.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk_, vk, (tb + i) * st2, 0);
       R.a[i] = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + i) * sa2, 0);
     }
-    R.a8 = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + 8) * sa2, 0);
     R.bt = __builtin_amdgcn_raw_buffer_load_b16(rb_, (lane_c & 63) * (int)a.H * 2, 0, 0);
   };
   Raw nxt;
@@ -972,7 +994,6 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
       kx[i] = cur.k[i];
       ax[i] = tk0 + i < n ? cur.a[i] : kOne;
     }
-    const uint32_t a8 = (hf == 0 && tk0 + 8 < n) ? cur.a8 : kOne;
     const float bt = bf2f(cur.bt);
 
     // ---- E1: partial norms, block decay products ---------------------------------------
@@ -981,27 +1002,21 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
       float ss[16];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float k0 = bf_lo(kx[i]), k1 = bf_hi(kx[i]);
-        ss[i] = k0 * k0 + k1 * k1;
+        ss[i] = sq2(kx[i], 0.f);
         ss[i + 8] = 0.f;
       }
       const float tot = half_sum16(ss, lane_c);
       const int vv = (lane_c >> 1) & 15;
       if ((lane_c & 1) == 0 && vv < 8) nk[hc][tk0 + vv] = tot;
     }
+    float2 al[8];   // alpha of the lane's tokens
+#pragma unroll
+    for (int i = 0; i < 8; ++i) al[i] = make_float2(bf_lo(ax[i]), bf_hi(ax[i]));
     {
-      float r0, r1;
-      if (hf == 1) {
-        r0 = bf_lo(ax[1]); r1 = bf_hi(ax[1]);
+      float2 hp = al[0];
 #pragma unroll
-        for (int i = 2; i < 8; ++i) { r0 *= bf_lo(ax[i]); r1 *= bf_hi(ax[i]); }
-        *reinterpret_cast<float2*>(&L.pf[I][c0]) = make_float2(r0, r1);
-      } else {
-        r0 = bf_lo(a8); r1 = bf_hi(a8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { r0 *= bf_lo(ax[i]); r1 *= bf_hi(ax[i]); }
-        *reinterpret_cast<float2*>(&L.pb[I][c0]) = make_float2(r0, r1);
-      }
+      for (int i = 1; i < 8; ++i) { hp.x *= al[i].x; hp.y *= al[i].y; }
+      *reinterpret_cast<float2*>(hf ? &L.pf[I][c0] : &L.pb[I][c0]) = hp;
     }
     lds_barrier();   // B
 
@@ -1013,49 +1028,66 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     bool fast;
     {
       float2 full[NSB];
-      float2 pbw = make_float2(1.f, 1.f), eo = make_float2(1.f, 1.f);
+      float2 h0w = make_float2(1.f, 1.f), h1w = h0w, eo = h0w;
 #pragma unroll
       for (int J = 0; J < NSB; ++J) {
-        const float2 pbJ = *reinterpret_cast<const float2*>(&L.pb[J][c0]);
-        const float2 pfJ = *reinterpret_cast<const float2*>(&L.pf[J][c0]);
-        full[J] = make_float2(pbJ.x * pfJ.x, pbJ.y * pfJ.y);
-        if (J == I) pbw = pbJ;
+        const float2 h0 = *reinterpret_cast<const float2*>(&L.pb[J][c0]);
+        const float2 h1 = *reinterpret_cast<const float2*>(&L.pf[J][c0]);
+        full[J] = make_float2(h0.x * h1.x, h0.y * h1.y);
+        if (J == I) { h0w = h0; h1w = h1; }
         // the other channel half, formed the same way, so that every wave votes alike
-        const float2 pbo = *reinterpret_cast<const float2*>(&L.pb[J][c0 ^ 64]);
-        const float2 pfo = *reinterpret_cast<const float2*>(&L.pf[J][c0 ^ 64]);
-        eo.x *= pbo.x * pfo.x;
-        eo.y *= pbo.y * pfo.y;
+        const float2 h0o = *reinterpret_cast<const float2*>(&L.pb[J][c0 ^ 64]);
+        const float2 h1o = *reinterpret_cast<const float2*>(&L.pf[J][c0 ^ 64]);
+        const float2 fo = make_float2(h0o.x * h1o.x, h0o.y * h1o.y);
+        eo = J == 0 ? fo : make_float2(eo.x * fo.x, eo.y * fo.y);
       }
-      float2 egn2 = full[0], em2 = pbw;
+      float2 egn2 = full[0], before = make_float2(1.f, 1.f), after = before;
 #pragma unroll
       for (int J = 1; J < NSB; ++J) { egn2.x *= full[J].x; egn2.y *= full[J].y; }
 #pragma unroll
-      for (int J = 0; J < NSB - 1; ++J)
-        if (J < I) { em2.x *= full[J].x; em2.y *= full[J].y; }
+      for (int J = 0; J < NSB; ++J) {
+        if (J < I) { before.x *= full[J].x; before.y *= full[J].y; }
+        if (J > I) { after.x *= full[J].x; after.y *= full[J].y; }
+      }
       fast = __all(fminf(fminf(egn2.x, egn2.y), fminf(eo.x, eo.y)) >= kFastMin) != 0;
       if (I == 0 && hf == 0) *reinterpret_cast<float2*>(&L.egn[c0]) = egn2;
-      const float2 one2 = make_float2(1.f, 1.f);
-      const float2 mr = fast ? em2 : one2;
-      const float2 mc = fast ? make_float2(__builtin_amdgcn_rcpf(em2.x), __builtin_amdgcn_rcpf(em2.y)) : one2;
-      auto put = [&](int i, float er0, float er1, float ec0, float ec1) {
+      auto put = [&](int i, float fr0, float fr1, float fc0, float fc1) {
         const int tk = tk0 + i;
         const float k0 = bf_lo(kx[i]), k1 = bf_hi(kx[i]);
-        *reinterpret_cast<uint32_t*>(&L.kr[rm(tk, p0)]) = pack_bf16x2(k0 * er0 * mr.x, k1 * er1 * mr.y);
-        *reinterpret_cast<uint32_t*>(&L.kc[rm(tk, p0)]) = pack_bf16x2(k0 * ec0 * mc.x, k1 * ec1 * mc.y);
+        *reinterpret_cast<uint32_t*>(&L.kr[rm(tk, p0)]) = pack_bf16x2(k0 * fr0, k1 * fr1);
+        *reinterpret_cast<uint32_t*>(&L.kc[rm(tk, p0)]) = pack_bf16x2(k0 * fc0, k1 * fc1);
       };
-      if (hf == 1) {
-        float r0 = 1.f, r1 = 1.f;
+      if (fast) {
+        // prefix products e^{g_t}, suffix products e^{g_n - g_t} / e^{g_n}
+        float f0 = before.x * (hf ? h0w.x : 1.f), f1 = before.y * (hf ? h0w.y : 1.f);
+        float b0 = (after.x * (hf ? 1.f : h1w.x)) * __builtin_amdgcn_rcpf(egn2.x);
+        float b1 = (after.y * (hf ? 1.f : h1w.y)) * __builtin_amdgcn_rcpf(egn2.y);
+        float fr0[8], fr1[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          if (i > 0) { r0 *= bf_lo(ax[i]); r1 *= bf_hi(ax[i]); }
-          put(i, r0, r1, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1));
+          f0 *= al[i].x; f1 *= al[i].y;
+          fr0[i] = f0; fr1[i] = f1;
         }
-      } else {
-        float r0 = bf_lo(a8), r1 = bf_hi(a8);
 #pragma unroll
         for (int i = 7; i >= 0; --i) {
-          if (i < 7) { r0 *= bf_lo(ax[i + 1]); r1 *= bf_hi(ax[i + 1]); }
-          put(i, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1), r0, r1);
+          put(i, fr0[i], fr1[i], b0, b1);
+          if (i > 0) { b0 *= al[i].x; b1 *= al[i].y; }
+        }
+      } else {
+        // blocked: reference m_I = g at the block's token 7
+        float r0 = 1.f, r1 = 1.f;
+        if (hf == 1) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            r0 *= al[i].x; r1 *= al[i].y;
+            put(i, r0, r1, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1));
+          }
+        } else {
+#pragma unroll
+          for (int i = 7; i >= 0; --i) {
+            put(i, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1), r0, r1);
+            r0 *= al[i].x; r1 *= al[i].y;
+          }
         }
       }
     }
