@@ -124,9 +124,9 @@ struct Lds {
   float egn[D];           // e^{g_n}
   float pb[NSB][D];       // per block and channel: product of alpha over block tokens 0..7
   float pf[NSB][D];       //                        ... over block tokens 8..15
-  float adiag[NSB][SBT][20];   // strictly lower A_II in fp32, column k at 4*(k&3) + (k>>2)
-  uint16_t at[CT * TRS];  // -A in the blocks below the diagonal, T_II on it (natural order)
-  uint16_t aqk[CT * TRS]; // Aqk (rows scaled 1/|q|, columns 1/|k|), token columns at cpos
+  float adiag[NSB][SBT][SBT + 4];   // strictly lower A_II in fp32, row-major
+  uint16_t at[CT * TRS];  // column-major: at[tr(j, i)] = -A(i, j) below the diagonal blocks, T_II on them
+  uint16_t aqk[CT * TRS]; // column-major: aqk[tr(j, i)] = Aqk(i, j) (rows scaled 1/|q|, columns 1/|k|)
   uint16_t kr[CT * RMS];  // K^ = k e^{g} (fast) or k e^{g - m_I} (blocked); output staging at the end
   uint16_t kc[CT * RMS];  // K_ = k e^{-g} (fast) or k e^{m_I - g} (blocked)
   uint16_t qw[CT * RMS];  // Q^ = q e^{g} / q e^{g - m_I} (output pass); then -W
@@ -266,8 +266,9 @@ __device__ __forceinline__ f32x4 mma4(const uint4 (&ra)[4], const uint4 (&cb)[4]
   for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
   return acc;
 }
-// A(I, J) = diag(b / |k|) (K^ K_^T)(I, J) diag(1 / |k|): below the diagonal -> at (negated),
-// on it (strictly lower part) -> adiag in fp32
+// A(I, J) = diag(b / |k|) (K^ K_^T)(I, J) diag(1 / |k|): below the diagonal -> at (negated,
+// column-major: a lane's four rows are one 8-byte write), on it (strictly lower part) ->
+// adiag in fp32
 __device__ __forceinline__ void epi_a(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
   const int j = SBT * J + l16;
   const float rkj = L.rk[j];
@@ -275,57 +276,68 @@ __device__ __forceinline__ void epi_a(Lds& L, int I, int J, f32x4 acc, int l16, 
   const float rowf[4] = {b4.x * k4.x, b4.y * k4.y, b4.z * k4.z, b4.w * k4.w};
   if (I == J) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      L.adiag[I][4 * q4 + r][4 * (l16 & 3) + (l16 >> 2)] = 4 * q4 + r > l16 ? rowf[r] * rkj * acc[r] : 0.f;
+    for (int r = 0; r < 4; ++r) L.adiag[I][4 * q4 + r][l16] = 4 * q4 + r > l16 ? rowf[r] * rkj * acc[r] : 0.f;
   } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.at[tr(SBT * I + 4 * q4 + r, j)] = f2bf(-rowf[r] * rkj * acc[r]);
+    const float nk = -rkj;
+    *reinterpret_cast<uint2*>(&L.at[tr(j, SBT * I + 4 * q4)]) = pack4(
+        make_float4(rowf[0] * nk * acc[0], rowf[1] * nk * acc[1], rowf[2] * nk * acc[2], rowf[3] * nk * acc[3]));
   }
 }
-// Aqk(I, J) = diag(1 / |q|) (Q^ K_^T)(I, J) diag(1 / |k|), lower triangle including the diagonal
+// Aqk(I, J) = diag(1 / |q|) (Q^ K_^T)(I, J) diag(1 / |k|), lower triangle including the
+// diagonal, column-major
 __device__ __forceinline__ void epi_q(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
   const int j = SBT * J + l16;
   const float rkj = L.rk[j];
   const float4 rq4 = ldf4(&L.rq[SBT * I + 4 * q4]);
   const float rowf[4] = {rq4.x, rq4.y, rq4.z, rq4.w};
+  float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool keep = I > J || 4 * q4 + r >= l16;
-    L.aqk[tr(SBT * I + 4 * q4 + r, cpos(j))] = f2bf(keep ? rowf[r] * rkj * acc[r] : 0.f);
+    v[r] = keep ? rowf[r] * rkj * acc[r] : 0.f;
   }
+  *reinterpret_cast<uint2*>(&L.aqk[tr(j, SBT * I + 4 * q4)]) = pack4(make_float4(v[0], v[1], v[2], v[3]));
 }
-// T_II = (I + A_II)^{-1} into the diagonal block of at, from adiag[I] written by this
-// wave. Forward substitution: lane = 16 part + j owns column j and the terms
-// k = part + 4m of every row's sum; the four parts are summed with lane swaps.
-__device__ __forceinline__ void invert_diag(Lds& L, int I, int lane) {
+// T_II = (I + A_II)^{-1} for the four diagonal blocks at once: lane = 16 I + j forms
+// column j of T_II by forward substitution, x_i = [i = j] - sum_{k < i} A_II(i, k) x_k,
+// reading the rows of A_II (written by this wave) as broadcasts; the column goes to at
+// as two 16-byte writes.
+__device__ __forceinline__ void invert_diag4(Lds& L, int lane) {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  const int part = lane >> 4, jj = lane & 15;
-  float xs[4] = {0.f, 0.f, 0.f, 0.f};   // x[part + 4m] of column jj
-  constexpr int AH = 4;                  // rows of A_II read ahead
-  float4 arow[AH];
-#pragma unroll
-  for (int i = 0; i < AH; ++i) arow[i] = ldf4(&L.adiag[I][i][4 * part]);
+  const int I = lane >> 4, jj = lane & 15;
+  float x[SBT];
 #pragma unroll
   for (int i = 0; i < SBT; ++i) {
-    const float4 ar = arow[i % AH];
-    if (i + AH < SBT) arow[i % AH] = ldf4(&L.adiag[I][i + AH][4 * part]);
-    float ps = ar.x * xs[0] + ar.y * xs[1] + ar.z * xs[2] + ar.w * xs[3];
-    ps = halve16(ps, ps);
-    ps = halve32(ps, ps);
-    const float xi = (i == jj ? 1.f : 0.f) - ps;
-    if (part == (i & 3)) xs[i >> 2] = xi;
-  }
+    float acc0 = i == jj ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) L.at[tr(SBT * I + part + 4 * m, SBT * I + jj)] = f2bf(xs[m]);
+    for (int k4 = 0; k4 < (i + 3) / 4; ++k4) {
+      const float4 a4 = ldf4(&L.adiag[I][i][4 * k4]);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * k4 + e;
+        if (k < i) {
+          if (e & 1) acc1 -= av[e] * x[k];
+          else acc0 -= av[e] * x[k];
+        }
+      }
+    }
+    x[i] = acc0 + acc1;
+  }
+  uint4 lo, hi;
+  lo.x = pack_bf16x2(x[0], x[1]); lo.y = pack_bf16x2(x[2], x[3]); lo.z = pack_bf16x2(x[4], x[5]); lo.w = pack_bf16x2(x[6], x[7]);
+  hi.x = pack_bf16x2(x[8], x[9]); hi.y = pack_bf16x2(x[10], x[11]); hi.z = pack_bf16x2(x[12], x[13]); hi.w = pack_bf16x2(x[14], x[15]);
+  *reinterpret_cast<uint4*>(&L.at[tr(SBT * I + jj, SBT * I)]) = lo;
+  *reinterpret_cast<uint4*>(&L.at[tr(SBT * I + jj, SBT * I + 8)]) = hi;
 }
-// mma16 A fragments of at: block (I, J), J <= I, at I (I + 1) / 2 + J
+// mma16 A fragments of at (transposed reads): block (I, J), J <= I, at I (I + 1) / 2 + J
 __device__ __forceinline__ void load_t_frags(const Lds& L, uint2 (&af)[10], int l16, int q4) {
 #pragma unroll
   for (int I = 0; I < 4; ++I)
 #pragma unroll
     for (int J = 0; J <= I; ++J)
-      af[I * (I + 1) / 2 + J] = *reinterpret_cast<const uint2*>(&L.at[tr(SBT * I + l16, SBT * J + 4 * q4)]);
+      af[I * (I + 1) / 2 + J] = ld_tr(&L.at[tr(SBT * J + 4 * q4 + (l16 >> 2), SBT * I + 4 * (l16 & 3))]);
 }
 // X = (I + A)^{-1} Y by block forward substitution, Y and X in the D layout
 __device__ __forceinline__ void block_solve(const uint2 (&af)[10], const f32x4 (&y0)[4], f32x4 (&X)[4]) {
@@ -616,7 +628,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   // the Aqk blocks (0,1) and (2,3) above the diagonal are read as zeros
   for (int e = tid; e < 2 * SBT * SBT; e += NTHR) {
     const int I = (e >> 8) * 2, i = (e >> 4) & 15, j = e & 15;
-    L.aqk[tr(SBT * I + i, cpos(SBT * (I + 1) + j))] = 0;
+    L.aqk[tr(SBT * (I + 1) + j, SBT * I + i)] = 0;
   }
 
   const uint2 kOnes = make_uint2(0x3F803F80u, 0x3F803F80u);   // alpha = 1 past the end
@@ -766,42 +778,45 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     uint4 vx[4];
     {
       uint4 cA[4], cB[4], rA[4], sc[4];
-      // wave 0: A00 Aqk00 A10 A30 Aqk30;  wave 1: A11 Aqk11 Aqk10 A31 Aqk31;
-      // wave 2: A22 A20 Aqk22 A32 Aqk32;  wave 3: A33 Aqk33 A21 Aqk21 Aqk20
+      // wave 0: the four diagonal A blocks and their inverses;
+      // wave 1: Aqk00 A10 Aqk10 A20 Aqk20 A30;  wave 2: Aqk11 A21 Aqk21 A31 Aqk31;
+      // wave 3: Aqk22 A32 Aqk32 Aqk33 Aqk30
       if (wave == 0) {
-        tile_frags(L.kc, 0, cA, l16, q4);
-        tile_frags(L.kr, 0, rA, l16, q4); epi_a(L, 0, 0, mma4(rA, cA), l16, q4);
-        tile_frags(L.qw, 0, rA, l16, q4); epi_q(L, 0, 0, mma4(rA, cA), l16, q4);
-        tile_frags(L.kr, 1, rA, l16, q4); pair_frags(L, fast, 1, 0, cA, sc, q4); epi_a(L, 1, 0, mma4(rA, sc), l16, q4);
-        pair_frags(L, fast, 3, 0, cA, sc, q4);
-        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 0, mma4(rA, sc), l16, q4);
-        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 0, mma4(rA, sc), l16, q4);
+#pragma unroll
+        for (int I = 0; I < NSB; ++I) {
+          tile_frags(L.kc, I, cA, l16, q4);
+          tile_frags(L.kr, I, rA, l16, q4);
+          epi_a(L, I, I, mma4(rA, cA), l16, q4);
+        }
+        invert_diag4(L, lane_c);
       } else if (wave == 1) {
-        tile_frags(L.kc, 1, cA, l16, q4);
-        tile_frags(L.kr, 1, rA, l16, q4); epi_a(L, 1, 1, mma4(rA, cA), l16, q4);
-        tile_frags(L.qw, 1, rA, l16, q4); epi_q(L, 1, 1, mma4(rA, cA), l16, q4);
-        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 1, 0, cB, sc, q4); epi_q(L, 1, 0, mma4(rA, sc), l16, q4);
-        pair_frags(L, fast, 3, 1, cA, sc, q4);
-        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 1, mma4(rA, sc), l16, q4);
-        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 1, mma4(rA, sc), l16, q4);
+        tile_frags(L.kc, 0, cA, l16, q4);
+        tile_frags(L.qw, 0, rA, l16, q4); epi_q(L, 0, 0, mma4(rA, cA), l16, q4);
+#pragma unroll
+        for (int I = 1; I < NSB; ++I) {
+          pair_frags(L, fast, I, 0, cA, sc, q4);
+          tile_frags(L.kr, I, rA, l16, q4); epi_a(L, I, 0, mma4(rA, sc), l16, q4);
+          if (I < 3) { tile_frags(L.qw, I, rA, l16, q4); epi_q(L, I, 0, mma4(rA, sc), l16, q4); }
+        }
       } else if (wave == 2) {
+        tile_frags(L.kc, 1, cA, l16, q4);
+        tile_frags(L.qw, 1, rA, l16, q4); epi_q(L, 1, 1, mma4(rA, cA), l16, q4);
+#pragma unroll
+        for (int I = 2; I < NSB; ++I) {
+          pair_frags(L, fast, I, 1, cA, sc, q4);
+          tile_frags(L.kr, I, rA, l16, q4); epi_a(L, I, 1, mma4(rA, sc), l16, q4);
+          tile_frags(L.qw, I, rA, l16, q4); epi_q(L, I, 1, mma4(rA, sc), l16, q4);
+        }
+      } else {
         tile_frags(L.kc, 2, cA, l16, q4);
-        tile_frags(L.kr, 2, rA, l16, q4); epi_a(L, 2, 2, mma4(rA, cA), l16, q4);
-        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 2, 0, cB, sc, q4); epi_a(L, 2, 0, mma4(rA, sc), l16, q4);
         tile_frags(L.qw, 2, rA, l16, q4); epi_q(L, 2, 2, mma4(rA, cA), l16, q4);
         pair_frags(L, fast, 3, 2, cA, sc, q4);
         tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 2, mma4(rA, sc), l16, q4);
         tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 2, mma4(rA, sc), l16, q4);
-      } else {
-        tile_frags(L.kc, 3, cA, l16, q4);
-        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 3, mma4(rA, cA), l16, q4);
-        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 3, mma4(rA, cA), l16, q4);
-        tile_frags(L.kc, 1, cB, l16, q4); pair_frags(L, fast, 2, 1, cB, sc, q4);
-        tile_frags(L.kr, 2, rA, l16, q4); epi_a(L, 2, 1, mma4(rA, sc), l16, q4);
-        tile_frags(L.qw, 2, rA, l16, q4); epi_q(L, 2, 1, mma4(rA, sc), l16, q4);
-        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 2, 0, cB, sc, q4); epi_q(L, 2, 0, mma4(rA, sc), l16, q4);
+        tile_frags(L.kc, 3, cB, l16, q4); epi_q(L, 3, 3, mma4(rA, cB), l16, q4);
+        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 3, 0, cB, sc, q4);
+        epi_q(L, 3, 0, mma4(rA, sc), l16, q4);
       }
-      invert_diag(L, wave, lane_c);
       // O = diag(1/|q|) Q^ S; the blocked factorisation scales Q^'s channels by e^{m_I}
       uint4 Sf[4][2];
       pack_state(S, Sf);
@@ -854,12 +869,17 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) Uf[s][ct] = pack8(Ut[2 * s][ct], Ut[2 * s + 1][ct]);
-      qa[0] = ld128(L.aqk, tr(l16, 8 * q4));
-      qa[1] = ld128(L.aqk, tr(SBT + l16, 8 * q4));
-      qa[2] = ld128(L.aqk, tr(2 * SBT + l16, 8 * q4));
-      qa[3] = ld128(L.aqk, tr(2 * SBT + l16, 32 + 8 * q4));
-      qa[4] = ld128(L.aqk, tr(3 * SBT + l16, 8 * q4));
-      qa[5] = ld128(L.aqk, tr(3 * SBT + l16, 32 + 8 * q4));
+      // A operand rows 16 I + l16, tokens 32 s + 4 q4 + 0..3 and 32 s + 16 + 4 q4 + 0..3
+      auto qfrag = [&](int I, int s) {
+        const int base = tr(32 * s + 4 * q4 + (l16 >> 2), SBT * I + 4 * (l16 & 3));
+        return cat(ld_tr(&L.aqk[base]), ld_tr(&L.aqk[base + tr(16, 0)]));
+      };
+      qa[0] = qfrag(0, 0);
+      qa[1] = qfrag(1, 0);
+      qa[2] = qfrag(2, 0);
+      qa[3] = qfrag(2, 1);
+      qa[4] = qfrag(3, 0);
+      qa[5] = qfrag(3, 1);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         O[0][ct] = mma32(qa[0], Uf[0][ct], O[0][ct]);
@@ -1098,27 +1118,23 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     // ---- M1T: A blocks, diagonal inverses ------------------------------------------------
     {
       uint4 cA[4], rA[4], sc[4];
-      // waves 0-3: A(w, w) and its inverse; wave 4: A10 A30; 5: A20 A31; 6: A21; 7: A32
-      if (wave < 4) {
-        tile_frags(L.kc, wave, cA, l16, q4);
-        tile_frags(L.kr, wave, rA, l16, q4);
-        epi_a(L, wave, wave, mma4(rA, cA), l16, q4);
-        invert_diag(L, wave, lane_c);
-      } else if (wave == 4) {
-        tile_frags(L.kc, 0, cA, l16, q4);
-        tile_frags(L.kr, 1, rA, l16, q4); pair_frags(L, fast, 1, 0, cA, sc, q4); epi_a(L, 1, 0, mma4(rA, sc), l16, q4);
-        tile_frags(L.kr, 3, rA, l16, q4); pair_frags(L, fast, 3, 0, cA, sc, q4); epi_a(L, 3, 0, mma4(rA, sc), l16, q4);
-      } else if (wave == 5) {
-        tile_frags(L.kc, 0, cA, l16, q4);
-        tile_frags(L.kr, 2, rA, l16, q4); pair_frags(L, fast, 2, 0, cA, sc, q4); epi_a(L, 2, 0, mma4(rA, sc), l16, q4);
-        tile_frags(L.kc, 1, cA, l16, q4);
-        tile_frags(L.kr, 3, rA, l16, q4); pair_frags(L, fast, 3, 1, cA, sc, q4); epi_a(L, 3, 1, mma4(rA, sc), l16, q4);
-      } else if (wave == 6) {
-        tile_frags(L.kc, 1, cA, l16, q4);
-        tile_frags(L.kr, 2, rA, l16, q4); pair_frags(L, fast, 2, 1, cA, sc, q4); epi_a(L, 2, 1, mma4(rA, sc), l16, q4);
-      } else {
-        tile_frags(L.kc, 2, cA, l16, q4);
-        tile_frags(L.kr, 3, rA, l16, q4); pair_frags(L, fast, 3, 2, cA, sc, q4); epi_a(L, 3, 2, mma4(rA, sc), l16, q4);
+      // wave 0: the four diagonal A blocks and their inverses; waves 1-6: one block below
+      // the diagonal each: A10 A20 A30 A21 A31 A32
+      if (wave == 0) {
+#pragma unroll
+        for (int I = 0; I < NSB; ++I) {
+          tile_frags(L.kc, I, cA, l16, q4);
+          tile_frags(L.kr, I, rA, l16, q4);
+          epi_a(L, I, I, mma4(rA, cA), l16, q4);
+        }
+        invert_diag4(L, lane_c);
+      } else if (wave < 7) {
+        const int I = wave < 4 ? wave : (wave == 6 ? 3 : wave - 2);
+        const int J = wave < 4 ? 0 : (wave == 6 ? 2 : 1);
+        tile_frags(L.kc, J, cA, l16, q4);
+        pair_frags(L, fast, I, J, cA, sc, q4);
+        tile_frags(L.kr, I, rA, l16, q4);
+        epi_a(L, I, J, mma4(rA, sc), l16, q4);
       }
     }
     lds_barrier();   // D
