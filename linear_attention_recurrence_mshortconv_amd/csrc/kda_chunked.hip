@@ -104,10 +104,15 @@ __device__ __forceinline__ uint4 scale8(uint4 u, float4 lo, float4 hi) {
 }
 
 // LDS arrays are flat with padded rows (the padding folds into instruction offsets).
-//   rm: [CT][D] row-major, row stride D + 8 elements (272 bytes)
-//   tr: [CT][CT], row stride CT + 8 elements (144 bytes: 16-byte reads stay aligned)
+//   rk: [CT][D] row-major (kr, kc), row stride D + 16 elements (288 bytes)
+//   rm: [CT][D] row-major (qw), row stride D + 8 elements (272 bytes)
+//   tr: [CT][CT], row stride CT + 4 elements (136 bytes)
+// (measured: the transposing reads and the 16-byte fragment reads of kr and kc
+// conflict least at a 288-byte row.)
+constexpr int RKS = D + 16;
 constexpr int RMS = D + 8;
-constexpr int TRS = CT + 8;
+constexpr int TRS = CT + 4;
+__device__ __forceinline__ constexpr int rk(int row, int col) { return row * RKS + col; }
 __device__ __forceinline__ constexpr int rm(int row, int col) { return row * RMS + col; }
 __device__ __forceinline__ constexpr int tr(int row, int col) { return row * TRS + col; }
 // Position of channel (or token) c inside its row: within each group of 32 the
@@ -124,11 +129,11 @@ struct Lds {
   float egn[D];           // e^{g_n}
   float pb[NSB][D];       // per block and channel: product of alpha over block tokens 0..7
   float pf[NSB][D];       //                        ... over block tokens 8..15
-  float adiag[NSB][SBT][SBT + 4];   // strictly lower A_II in fp32, row-major
+  float adiag[NSB * 272];  // strictly lower A_II in fp32: A_II(i, k) at 272 I + 16 i + k
   uint16_t at[CT * TRS];  // column-major: at[tr(j, i)] = -A(i, j) below the diagonal blocks, T_II on them
   uint16_t aqk[CT * TRS]; // column-major: aqk[tr(j, i)] = Aqk(i, j) (rows scaled 1/|q|, columns 1/|k|)
-  uint16_t kr[CT * RMS];  // K^ = k e^{g} (fast) or k e^{g - m_I} (blocked); output staging at the end
-  uint16_t kc[CT * RMS];  // K_ = k e^{-g} (fast) or k e^{m_I - g} (blocked)
+  uint16_t kr[CT * RKS];  // K^ = k e^{g} (fast) or k e^{g - m_I} (blocked); output staging at the end
+  uint16_t kc[CT * RKS];  // K_ = k e^{-g} (fast) or k e^{m_I - g} (blocked)
   uint16_t qw[CT * RMS];  // Q^ = q e^{g} / q e^{g - m_I} (output pass); then -W
 };
 static_assert(sizeof(Lds) <= 81920, "two blocks per CU");
@@ -249,9 +254,10 @@ __device__ __forceinline__ float4 pair_of(const Lds& L, int I, int J, int c) {
 // Fragment conventions (16x16x32 MFMA): lane = 16 q4 + l16; a row fragment of block
 // `blk` holds row 16 blk + l16, positions 32 s + 8 q4 .. + 7 for s = 0..3.
 
+template <int STRIDE = RKS>
 __device__ __forceinline__ void tile_frags(const uint16_t* arr, int blk, uint4 (&f)[4], int l16, int q4) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) f[s] = ld128(arr, rm(SBT * blk + l16, 32 * s + 8 * q4));
+  for (int s = 0; s < 4; ++s) f[s] = ld128(arr, (SBT * blk + l16) * STRIDE + 32 * s + 8 * q4);
 }
 // column-operand fragments of block J scaled by e^{m_I - m_J} (blocked factorisation)
 __device__ __forceinline__ void pair_frags(const Lds& L, bool fast, int I, int J, const uint4 (&in)[4],
@@ -276,7 +282,7 @@ __device__ __forceinline__ void epi_a(Lds& L, int I, int J, f32x4 acc, int l16, 
   const float rowf[4] = {b4.x * k4.x, b4.y * k4.y, b4.z * k4.z, b4.w * k4.w};
   if (I == J) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) L.adiag[I][4 * q4 + r][l16] = 4 * q4 + r > l16 ? rowf[r] * rkj * acc[r] : 0.f;
+    for (int r = 0; r < 4; ++r) L.adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? rowf[r] * rkj * acc[r] : 0.f;
   } else {
     const float nk = -rkj;
     *reinterpret_cast<uint2*>(&L.at[tr(j, SBT * I + 4 * q4)]) = pack4(
@@ -301,7 +307,7 @@ __device__ __forceinline__ void epi_q(Lds& L, int I, int J, f32x4 acc, int l16, 
 // T_II = (I + A_II)^{-1} for the four diagonal blocks at once: lane = 16 I + j forms
 // column j of T_II by forward substitution, x_i = [i = j] - sum_{k < i} A_II(i, k) x_k,
 // reading the rows of A_II (written by this wave) as broadcasts; the column goes to at
-// as two 16-byte writes.
+// as four 8-byte writes.
 __device__ __forceinline__ void invert_diag4(Lds& L, int lane) {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
@@ -312,7 +318,7 @@ __device__ __forceinline__ void invert_diag4(Lds& L, int lane) {
     float acc0 = i == jj ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
     for (int k4 = 0; k4 < (i + 3) / 4; ++k4) {
-      const float4 a4 = ldf4(&L.adiag[I][i][4 * k4]);
+      const float4 a4 = ldf4(&L.adiag[272 * I + 16 * i + 4 * k4]);
       const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -325,11 +331,10 @@ __device__ __forceinline__ void invert_diag4(Lds& L, int lane) {
     }
     x[i] = acc0 + acc1;
   }
-  uint4 lo, hi;
-  lo.x = pack_bf16x2(x[0], x[1]); lo.y = pack_bf16x2(x[2], x[3]); lo.z = pack_bf16x2(x[4], x[5]); lo.w = pack_bf16x2(x[6], x[7]);
-  hi.x = pack_bf16x2(x[8], x[9]); hi.y = pack_bf16x2(x[10], x[11]); hi.z = pack_bf16x2(x[12], x[13]); hi.w = pack_bf16x2(x[14], x[15]);
-  *reinterpret_cast<uint4*>(&L.at[tr(SBT * I + jj, SBT * I)]) = lo;
-  *reinterpret_cast<uint4*>(&L.at[tr(SBT * I + jj, SBT * I + 8)]) = hi;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    *reinterpret_cast<uint2*>(&L.at[tr(SBT * I + jj, SBT * I + 4 * m)]) =
+        make_uint2(pack_bf16x2(x[4 * m], x[4 * m + 1]), pack_bf16x2(x[4 * m + 2], x[4 * m + 3]));
 }
 // mma16 A fragments of at (transposed reads): block (I, J), J <= I, at I (I + 1) / 2 + J
 __device__ __forceinline__ void load_t_frags(const Lds& L, uint2 (&af)[10], int l16, int q4) {
@@ -359,7 +364,7 @@ __device__ __forceinline__ void w_tile(Lds& L, bool fast, int t, const uint2 (&a
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
     // lane (l16, q4) receives channel 16 t + l16 of tokens 16 I + 4 q4 + 0..3
-    const float4 kv = unpack4(ld_tr(&L.kr[rm(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
+    const float4 kv = unpack4(ld_tr(&L.kr[rk(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
     float sc = 1.f;
     if (!fast) sc = pick(em_of(L, I, 16 * t + (l16 & ~3)), l16 & 3);
     const float4 kr4 = mul4(ldf4(&L.beta[SBT * I + 4 * q4]), ldf4(&L.rk[SBT * I + 4 * q4]));
@@ -372,7 +377,7 @@ __device__ __forceinline__ void w_tile(Lds& L, bool fast, int t, const uint2 (&a
 #pragma unroll
   for (int I = 0; I < 4; ++I)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) L.kr[rm(SBT * I + 4 * q4 + r, wcol)] = f2bf(-X[I][r]);
+    for (int r = 0; r < 4; ++r) L.kr[rk(SBT * I + 4 * q4 + r, wcol)] = f2bf(-X[I][r]);
 }
 // v of channels col0 .. col0 + 31 (vx: lane = tokens 4 (lane >> 2) + j, channels
 // col0 + 8 (lane & 3) ..) -> the same channels of qw, which only this wave uses now
@@ -444,14 +449,14 @@ __device__ __forceinline__ void update_state(const Lds& L, bool fast, f32x4 (&S)
   }
   // A operand K~^T: lane (l16, q4) = channel 16 rt + l16, tokens 32 s + 4 q4 + 0..3 and
   // 32 s + 16 + 4 q4 + 0..3
-  const int kbase = rm(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
+  const int kbase = rk(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
 #pragma unroll
   for (int rt = 0; rt < 8; ++rt) {
     const int cp = 32 * (rt >> 1) + 4 * (rt & 1);   // cpos(16 rt)
     uint4 kt[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      kt[s] = cat(ld_tr(&L.kc[kbase + rm(32 * s, cp)]), ld_tr(&L.kc[kbase + rm(32 * s + 16, cp)]));
+      kt[s] = cat(ld_tr(&L.kc[kbase + rk(32 * s, cp)]), ld_tr(&L.kc[kbase + rk(32 * s + 16, cp)]));
     const float4 eg = ldf4(&L.egn[16 * rt + 4 * q4]);
     if (fast) {   // K~ = K_ e^{g_n}: the factor is a row scaling of the product
 #pragma unroll
@@ -727,8 +732,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       if (wave == 0 && hf == 0) *reinterpret_cast<float4*>(&L.egn[c0]) = egn4;
       auto put = [&](int i, float4 fr, float4 fc) {
         const int tk = tk0 + i;
-        *reinterpret_cast<uint2*>(&L.kr[rm(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fr));
-        *reinterpret_cast<uint2*>(&L.kc[rm(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fc));
+        *reinterpret_cast<uint2*>(&L.kr[rk(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fr));
+        *reinterpret_cast<uint2*>(&L.kc[rk(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fc));
         *reinterpret_cast<uint2*>(&L.qw[rm(tk, p0)]) = pack4(mul4(unpack4(qx[i]), fr));
       };
       if (fast) {
@@ -791,28 +796,28 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
         invert_diag4(L, lane_c);
       } else if (wave == 1) {
         tile_frags(L.kc, 0, cA, l16, q4);
-        tile_frags(L.qw, 0, rA, l16, q4); epi_q(L, 0, 0, mma4(rA, cA), l16, q4);
+        tile_frags<RMS>(L.qw, 0, rA, l16, q4); epi_q(L, 0, 0, mma4(rA, cA), l16, q4);
 #pragma unroll
         for (int I = 1; I < NSB; ++I) {
           pair_frags(L, fast, I, 0, cA, sc, q4);
           tile_frags(L.kr, I, rA, l16, q4); epi_a(L, I, 0, mma4(rA, sc), l16, q4);
-          if (I < 3) { tile_frags(L.qw, I, rA, l16, q4); epi_q(L, I, 0, mma4(rA, sc), l16, q4); }
+          if (I < 3) { tile_frags<RMS>(L.qw, I, rA, l16, q4); epi_q(L, I, 0, mma4(rA, sc), l16, q4); }
         }
       } else if (wave == 2) {
         tile_frags(L.kc, 1, cA, l16, q4);
-        tile_frags(L.qw, 1, rA, l16, q4); epi_q(L, 1, 1, mma4(rA, cA), l16, q4);
+        tile_frags<RMS>(L.qw, 1, rA, l16, q4); epi_q(L, 1, 1, mma4(rA, cA), l16, q4);
 #pragma unroll
         for (int I = 2; I < NSB; ++I) {
           pair_frags(L, fast, I, 1, cA, sc, q4);
           tile_frags(L.kr, I, rA, l16, q4); epi_a(L, I, 1, mma4(rA, sc), l16, q4);
-          tile_frags(L.qw, I, rA, l16, q4); epi_q(L, I, 1, mma4(rA, sc), l16, q4);
+          tile_frags<RMS>(L.qw, I, rA, l16, q4); epi_q(L, I, 1, mma4(rA, sc), l16, q4);
         }
       } else {
         tile_frags(L.kc, 2, cA, l16, q4);
-        tile_frags(L.qw, 2, rA, l16, q4); epi_q(L, 2, 2, mma4(rA, cA), l16, q4);
+        tile_frags<RMS>(L.qw, 2, rA, l16, q4); epi_q(L, 2, 2, mma4(rA, cA), l16, q4);
         pair_frags(L, fast, 3, 2, cA, sc, q4);
         tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 2, mma4(rA, sc), l16, q4);
-        tile_frags(L.qw, 3, rA, l16, q4); epi_q(L, 3, 2, mma4(rA, sc), l16, q4);
+        tile_frags<RMS>(L.qw, 3, rA, l16, q4); epi_q(L, 3, 2, mma4(rA, sc), l16, q4);
         tile_frags(L.kc, 3, cB, l16, q4); epi_q(L, 3, 3, mma4(rA, cB), l16, q4);
         tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 3, 0, cB, sc, q4);
         epi_q(L, 3, 0, mma4(rA, sc), l16, q4);
@@ -823,7 +828,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         uint4 qf[4];
-        tile_frags(L.qw, I, qf, l16, q4);
+        tile_frags<RMS>(L.qw, I, qf, l16, q4);
         if (!fast) {
 #pragma unroll
           for (int s = 0; s < 4; ++s)
@@ -1074,8 +1079,8 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
       auto put = [&](int i, float fr0, float fr1, float fc0, float fc1) {
         const int tk = tk0 + i;
         const float k0 = bf_lo(kx[i]), k1 = bf_hi(kx[i]);
-        *reinterpret_cast<uint32_t*>(&L.kr[rm(tk, p0)]) = pack_bf16x2(k0 * fr0, k1 * fr1);
-        *reinterpret_cast<uint32_t*>(&L.kc[rm(tk, p0)]) = pack_bf16x2(k0 * fc0, k1 * fc1);
+        *reinterpret_cast<uint32_t*>(&L.kr[rk(tk, p0)]) = pack_bf16x2(k0 * fr0, k1 * fr1);
+        *reinterpret_cast<uint32_t*>(&L.kc[rk(tk, p0)]) = pack_bf16x2(k0 * fc0, k1 * fc1);
       };
       if (fast) {
         // prefix products e^{g_t}, suffix products e^{g_n - g_t} / e^{g_n}
