@@ -5,17 +5,27 @@ One step = one pass of the whole hot path over the 65,792-token workload
 16x16 patches; B=1, H=16, d=128, bf16 inputs, fp32 state):
 
   1. mShortConv on the fused q|k|v tensor (chimera_mshortconv_fwd), and
-  2. the KDA forward with per-head q/k L2 normalisation (chimera_kda_fwd).
+  2. the KDA forward with per-head q/k L2 normalisation, o and S_final
+     (chimera_kda_fwd).
 
-The neighbour layout is derived arithmetically inside the conv kernel; the
-host-side index table is not part of a step. Inputs are synthetic, seeded,
-and resident in HBM before the timed region.
+The neighbour layout is derived arithmetically inside the conv kernels; no
+host-side index table is part of a step. Inputs are synthetic, seeded, and
+resident in HBM before the timed region.
+
+The timed steps call the timing variants of both entry points, which record a
+HIP event on the launch stream around every kernel; the per-kernel averages
+give the roofline line of the kernel that takes the most time per step.
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Two helper modes turn rocprofv3 output into the summaries kept with the code:
+  python bench.py --summarize-stats <kernel_stats.csv>
+  python bench.py --summarize-pmc <fetch counter_collection.csv> <write counter_collection.csv>
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -30,6 +40,31 @@ METRIC = "KDA+mShortConv fwd tokens/sec/GPU at 65K tok, H=16 d=128; % of rooflin
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 WORKLOAD_INDEX = 2
+CSRC = os.path.join(ROOT, "linear_attention_recurrence_mshortconv_amd", "csrc")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "image_4096_hbm_traffic.md")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+# kernel -> the source file that defines it (for the staleness check of stored counters)
+KERNEL_SOURCE = {
+    "conv_rows_kernel": "mshortconv.hip", "conv_tile_kernel": "mshortconv.hip",
+    "conv_text_kernel": "mshortconv.hip", "conv_gather_kernel": "mshortconv.hip",
+    "kda_sum_kernel": "kda_chunked.hip", "kda_combine_kernel": "kda_chunked.hip",
+    "kda_out_kernel": "kda_chunked.hip", "kda_seq_kernel": "kda_sequential.hip",
+}
+
+
+def short_name(full: str) -> str:
+    """'void chm::(anonymous namespace)::conv_rows_kernel<4, 32>(...)' -> 'conv_rows_kernel'."""
+    s = full.replace("(anonymous namespace)::", "")
+    s = s.split("(")[0].split("<")[0].strip()
+    return s.split("::")[-1].split(" ")[-1]
+
+
+def source_hash(kernel: str) -> str:
+    f = KERNEL_SOURCE.get(kernel)
+    if f is None:
+        return "-"
+    return hashlib.sha256(open(os.path.join(CSRC, f), "rb").read()).hexdigest()[:16]
 
 
 def _args():
@@ -42,12 +77,125 @@ def _args():
                     help="for counter runs: one 1 GiB device copy (the scale reference), then one step, then exit")
     ap.add_argument("--cpu-sample-rows", type=int, default=80,
                     help="image rows in the oracle's timed sample (plus the 256 text tokens)")
+    ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="markdown HBM traffic table from FETCH_SIZE and WRITE_SIZE counter_collection.csv files")
     return ap.parse_args()
 
 
+# ----------------------------------------------------------------------------------------------------------
+# algorithmic work per launch (bytes that the kernel's job must move, or flops it must do)
+
+def kda_split(B: int, T: int, H: int, target_blocks: int = 512, sub: int = 2):
+    """Chunks covered by the summary pass of the chunked KDA: the library splits every sequence into
+    P segments of Lo 64-token chunks (about 512 output blocks over B*H) and summarises all but the last."""
+    nc = (T + 63) // 64
+    bh = B * H
+    if nc <= 1 or bh >= target_blocks:
+        return nc, 0
+    p = min((target_blocks + bh - 1) // bh, nc)
+    lo = (nc + p - 1) // p
+    p = (nc + lo - 1) // lo
+    if p <= 1:
+        return nc, 0
+    return nc, (p - 1) * lo
+
+
+def kernel_work(name: str, w) -> dict:
+    """Algorithmic bytes (HBM-bound kernels) of one launch on the bench workload, with the recipe."""
+    B, T, H, d, C = w.B, w.T, w.H, w.d, w.C
+    text = sum(s.length for s in w.segments if s.kind == 0)
+    vis = T - text
+    e = 2                                                         # bf16
+    if name in ("conv_rows_kernel", "conv_tile_kernel"):
+        return {"bytes": 2 * B * vis * C * e,
+                "recipe": f"read + write every q|k|v channel of the {vis} visual tokens once: 2 x {C} x 2 B/token"}
+    if name == "conv_text_kernel":
+        return {"bytes": 2 * B * text * C * e,
+                "recipe": f"read + write every channel of the {text} text tokens once"}
+    if name == "kda_out_kernel":
+        per = 4 * d * e + e + d * e                               # q, k, v, alpha in; beta in; o out
+        return {"bytes": B * T * H * per + B * H * d * d * 4,
+                "recipe": f"q, k, v, alpha ({4 * d * e} B) + beta (2 B) in, o ({d * e} B) out per token-head, "
+                          f"+ S_final (fp32 d x d per head)"}
+    if name == "kda_sum_kernel":
+        nc, c_stop = kda_split(B, T, H)
+        toks = min(T, c_stop * 64)
+        return {"bytes": B * toks * H * (3 * d * e + e),
+                "recipe": f"k, v, alpha + beta in ({3 * d * e + e} B per token-head) over the {toks} tokens "
+                          f"({c_stop} of {nc} chunks) the segment summaries cover"}
+    return {"bytes": None, "recipe": "workspace only (no algorithmic HBM traffic)"}
+
+
+def stored_traffic(kernel: str):
+    """Scaled HBM bytes per launch from the committed counter summary, or None when the kernel's source
+    changed since the counters were taken (or no row exists)."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    for line in open(TRAFFIC_SUMMARY):
+        cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 6 and cells[0] == kernel:
+            if cells[1] != source_hash(kernel):
+                return None
+            try:
+                return float(cells[4]) * 1e6
+            except ValueError:
+                return None
+    return None
+
+
+# ----------------------------------------------------------------------------------------------------------
+# summaries of rocprofv3 output
+
+def summarize_stats(path: str):
+    rows = list(csv.DictReader(open(path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |")
+    print("|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+              f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+
+
+def _pmc(path: str, counter: str):
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(short_name(r["Kernel_Name"]) if r["Kernel_Name"] != COPY_KERNEL else COPY_KERNEL,
+                       []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str):
+    import workloads as wl
+    w = wl.WORKLOADS[WORKLOAD_INDEX]
+    f, wr = _pmc(fetch_csv, "FETCH_SIZE"), _pmc(write_csv, "WRITE_SIZE")
+    gib_kib = 1024.0 * 1024.0                                    # a 1 GiB copy reads and writes 1 GiB
+    f_scale = gib_kib / max(f[COPY_KERNEL])
+    w_scale = gib_kib / max(wr[COPY_KERNEL])
+    print(f"Scale: the 1 GiB device copy reads FETCH_SIZE = {max(f[COPY_KERNEL]):.0f} KiB and "
+          f"WRITE_SIZE = {max(wr[COPY_KERNEL]):.0f} KiB, so the factors are {f_scale:.3f} (fetch) and "
+          f"{w_scale:.3f} (write).\n")
+    print("| Kernel | Source sha256 (16) | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | Scaled HBM bytes (MB) | "
+          "Algorithmic bytes (MB) | Ratio |")
+    print("|---|---|---|---|---|---|---|")
+    for k in f:
+        if k == COPY_KERNEL or k not in KERNEL_SOURCE or k not in wr:
+            continue
+        fk, wk = sum(f[k]) / len(f[k]), sum(wr[k]) / len(wr[k])
+        scaled = (fk * f_scale + wk * w_scale) * 1024.0
+        alg = kernel_work(k, w)["bytes"]
+        ratio = f"{scaled / alg:.3f}" if alg else "-"
+        algs = f"{alg / 1e6:.1f}" if alg else "-"
+        print(f"| `{k}` | {source_hash(k)} | {fk:.0f} | {wk:.0f} | {scaled / 1e6:.1f} | {algs} | {ratio} |")
+
+
+# ----------------------------------------------------------------------------------------------------------
+
 def _cpu_baseline(inp, w, rows: int):
     """The oracle as it stands, on the first 256 + rows*256 tokens of the workload, one host core."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
     import workloads as wl
     from oracle import conv_ref, kda_ref, l2norm_ref, round_bf16_ref
@@ -72,11 +220,16 @@ def _cpu_baseline(inp, w, rows: int):
 
 def main():
     args = _args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); nothing here runs on more than one.",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import workloads as wl
     import linear_attention_recurrence_mshortconv_amd as chm
@@ -97,12 +250,13 @@ def main():
     y = torch.empty_like(x)
     q, k, v = chm.split_qkv(y, H, d)
     o = torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev)
+    s_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
     need = chm.kda_workspace_size(B, T, H, d, d, chm.BF16, chm.KDA_L2NORM_QK)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
-    def step():
-        chm.mshortconv_fwd(x, wt, wv, segs, out=y)
-        chm.kda_fwd(q, k, v, alpha, beta, None, workspace=ws, out=o)
+    def step(mc=None, mk=None):
+        chm.mshortconv_fwd(x, wt, wv, segs, out=y, marks=mc)
+        chm.kda_fwd(q, k, v, alpha, beta, None, workspace=ws, out=o, marks=mk, state_out=s_final)
 
     if args.profile_once:
         ref_src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device=dev)   # 1 GiB
@@ -110,57 +264,58 @@ def main():
         ref_dst.copy_(ref_src)
         step()
         torch.cuda.synchronize()
-        print("profile-once: 1 GiB copy + one step done")
+        print("profile-once: 1 GiB copy + one step done", flush=True)
         return
-
-    # the image-grid conv kernel alone: same launch as inside a step, on the image tokens
-    img = segs[1]
-    x_img = x[:, img.start:]
-    y_img = y[:, img.start:]
-    img_only = (wl.Segment(wl.IMAGE, 0, img.length, 1, img.height, img.width),)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    marks = [(chm.Marks(len(segs) + 1), chm.Marks(4)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for mc, mk in marks:
+        step(mc, mk)
     e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # per-call split of a step, and the conv grid kernel alone (events on the launch stream)
-    def avg_ms(fn, n):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(n):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
+    # per-kernel device time, from the marks of the timed steps
+    per_kernel = {}
+    for mc, mk in marks:
+        for name, ms in mc.kernels() + mk.kernels():
+            per_kernel.setdefault(name, []).append(ms)
+    kernels = {n: {"ms_per_launch": sum(v) / len(v), "launches_per_step": len(v) / args.steps}
+               for n, v in per_kernel.items()}
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"])
 
-    n_rep = max(5, args.steps)
-    ms_conv = avg_ms(lambda: chm.mshortconv_fwd(x, wt, wv, segs, out=y), n_rep)
-    ms_kda = avg_ms(lambda: chm.kda_fwd(q, k, v, alpha, beta, None, workspace=ws, out=o), n_rep)
-    ms_conv_grid = avg_ms(lambda: chm.mshortconv_fwd(x_img, wt, wv, img_only, out=y_img), n_rep)
+    # the same steps without marks, for the marks' overhead
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step_unmarked = a.elapsed_time(b) / args.steps
 
-    # algorithmic bytes of the conv grid kernel: read and write every q|k|v channel of every image token once
-    conv_bytes = 2 * B * img.length * 3 * H * d * 2
-    achieved = conv_bytes / (ms_conv_grid * 1e-3) / 1e9
-    kda_bytes = B * T * H * (3 * d * 2 + d * 2 + 2 + d * 2)
+    work = kernel_work(dom, w)
+    ms_dom = kernels[dom]["ms_per_launch"]
+    achieved = work["bytes"] / (ms_dom * 1e-3) / 1e9 if work["bytes"] else None
+    traffic = stored_traffic(dom)
+    conv_ms = sum(kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
+                  if n.startswith("conv_"))
+    kda_ms = sum(kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
+                 if n.startswith("kda_"))
+    conv_bytes = 2 * B * T * w.C * 2
+    kda_bytes = B * T * H * (4 * d * 2 + 2 + d * 2) + B * H * d * d * 4
     tokens = B * T
-    value = tokens / (ms_step * 1e-3)
-    src = os.path.join(ROOT, "linear_attention_recurrence_mshortconv_amd", "csrc", "mshortconv.hip")
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": tokens / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -172,19 +327,25 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; bf16 q|k|v, alpha, beta; fp32 conv weights; fp32 state)",
         "config": {"workload": f"{w.name}: 256 text tokens + 256x256 image grid = {T} tokens, B={B}, H={H}, "
-                               f"d_k=d_v={d}, chunk 64, conv 4-tap text / 3x3 image, q/k L2-normalised",
-                   "tokens_per_step": tokens, "ms_conv": ms_conv, "ms_kda": ms_kda,
-                   "kda_GBps_algorithmic": kda_bytes / (ms_kda * 1e-3) / 1e9,
+                               f"d_k=d_v={d}, chunk 64, conv 4-tap text / 3x3 image, q/k L2-normalised, "
+                               f"o and S_final written",
+                   "tokens_per_step": tokens,
+                   "ms_per_step_without_marks": ms_step_unmarked,
+                   "kernels": kernels,
+                   "conv_call": {"ms": conv_ms, "GBps_algorithmic": conv_bytes / (conv_ms * 1e-3) / 1e9,
+                                 "frac_hbm": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                   "kda_call": {"ms": kda_ms, "GBps_algorithmic": kda_bytes / (kda_ms * 1e-3) / 1e9,
+                                "frac_hbm": kda_bytes / (kda_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
                    "wall_s_timed": t_wall},
-        "roofline": {"bound": "hbm", "kernel": "conv_tile_kernel (image grid, 3x3, bf16)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "ms_per_launch": ms_conv_grid,
-                     "algorithmic_bytes_per_launch": conv_bytes},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS if achieved else None,
+                     "traffic": traffic, "ms_per_launch": ms_dom,
+                     "algorithmic_bytes_per_launch": work["bytes"], "recipe": work["recipe"]},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_sample_rows)
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

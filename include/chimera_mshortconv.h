@@ -181,6 +181,38 @@ chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int6
                                chimera_dtype dt, uint32_t flags,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Per-kernel timing variants. Each runs exactly the launches of the call it is
+ * named after, with the same arguments and results, and additionally records
+ * HIP events on `stream`: marks[0] before the first kernel, then marks[i] right
+ * after the i-th kernel is enqueued, with names[i-1] set to a static,
+ * NUL-terminated name of that kernel. The elapsed time between marks[i-1] and
+ * marks[i] is then the device time of kernel i (plus the gap between
+ * launches). *used receives the number of marks recorded (0 when nothing was
+ * launched).
+ *
+ *   marks     host array of `capacity` events, created by the caller with
+ *             timing enabled (hipEventCreate), owned by the caller
+ *   names     host array of `capacity` pointers, written
+ *   capacity  at least nseg + 1 for the conv, CHIMERA_KDA_MAX_KERNELS + 1 for
+ *             KDA; otherwise CHIMERA_ERR_SHAPE before any launch
+ *
+ * Errors as for the untimed call; a failed event record is CHIMERA_ERR_HIP.
+ * The marks serve measurement: they add a few microseconds of event overhead
+ * per kernel.
+ */
+#define CHIMERA_KDA_MAX_KERNELS 3
+chimera_status chimera_mshortconv_fwd_timed(const void* x, void* y, int64_t B, int64_t T, int64_t C,
+                                            chimera_dtype dt, const float* w_text, const float* w_vis,
+                                            const chimera_segment* segs, int32_t nseg, hipStream_t stream,
+                                            hipEvent_t* marks, const char** names, int32_t capacity,
+                                            int32_t* used);
+chimera_status chimera_kda_fwd_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                     const void* alpha, const void* beta, const float* S0, void* o, float* S_final,
+                                     int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                                     uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                     hipEvent_t* marks, const char** names, int32_t capacity, int32_t* used);
+
 /* Static, NUL-terminated description of a status code. */
 const char* chimera_status_string(chimera_status s);
 

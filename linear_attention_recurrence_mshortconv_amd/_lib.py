@@ -64,6 +64,12 @@ def lib() -> ctypes.CDLL:
     L.chimera_kda_fwd.restype = ctypes.c_int
     L.chimera_kda_fwd.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                   ctypes.c_int, u32, vp, sz, vp]
+    pp, cp = ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_char_p)
+    L.chimera_mshortconv_fwd_timed.restype = ctypes.c_int
+    L.chimera_mshortconv_fwd_timed.argtypes = L.chimera_mshortconv_fwd.argtypes + [pp, cp, i32,
+                                                                                     ctypes.POINTER(i32)]
+    L.chimera_kda_fwd_timed.restype = ctypes.c_int
+    L.chimera_kda_fwd_timed.argtypes = L.chimera_kda_fwd.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
     _lib = L
     return L
 
@@ -128,8 +134,34 @@ def mshortconv_index_device(segments: Sequence, T: int, device="cuda"):
     return idx
 
 
-def mshortconv_fwd(x, w_text, w_vis, segments: Sequence, out=None):
-    """y = mShortConv(x) for x [B, T, C] (bf16 or fp32) on the GPU (chimera_mshortconv_fwd)."""
+class Marks:
+    """Timing marks for the *_fwd_timed calls: `capacity` torch.cuda.Events with timing enabled.
+
+    After a call, ``kernels()`` gives (kernel name, milliseconds) for each kernel
+    the call launched, read from the events (this synchronises on them).
+    """
+
+    def __init__(self, capacity: int, device="cuda"):
+        import torch
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        stream = torch.cuda.current_stream(device)
+        for e in self.events:           # torch creates the HIP event on its first record
+            e.record(stream)
+        self.handles = (ctypes.c_void_p * capacity)(*[e.cuda_event for e in self.events])
+        self.names = (ctypes.c_char_p * capacity)()
+        self.used = ctypes.c_int32(0)
+        self.capacity = capacity
+
+    def kernels(self):
+        n = self.used.value
+        return [(self.names[i].decode(), self.events[i].elapsed_time(self.events[i + 1])) for i in range(n - 1)]
+
+
+def mshortconv_fwd(x, w_text, w_vis, segments: Sequence, out=None, marks: Optional[Marks] = None):
+    """y = mShortConv(x) for x [B, T, C] (bf16 or fp32) on the GPU (chimera_mshortconv_fwd).
+
+    With `marks`, calls chimera_mshortconv_fwd_timed instead and records them.
+    """
     import torch
     assert x.is_cuda and x.is_contiguous() and x.dim() == 3
     B, T, C = x.shape
@@ -138,9 +170,13 @@ def mshortconv_fwd(x, w_text, w_vis, segments: Sequence, out=None):
     y = torch.empty_like(x) if out is None else out
     assert y.shape == x.shape and y.dtype == x.dtype and y.is_contiguous()
     segs = segment_array(segments)
-    _check("chimera_mshortconv_fwd",
-           lib().chimera_mshortconv_fwd(_ptr(x), _ptr(y), B, T, C, _dtype_code(x), _ptr(w_text), _ptr(w_vis),
-                                        segs, len(segments), _stream(x)))
+    args = (_ptr(x), _ptr(y), B, T, C, _dtype_code(x), _ptr(w_text), _ptr(w_vis), segs, len(segments), _stream(x))
+    if marks is None:
+        _check("chimera_mshortconv_fwd", lib().chimera_mshortconv_fwd(*args))
+    else:
+        _check("chimera_mshortconv_fwd_timed",
+               lib().chimera_mshortconv_fwd_timed(*args, marks.handles, marks.names, marks.capacity,
+                                                  ctypes.byref(marks.used)))
     return y
 
 
@@ -158,12 +194,14 @@ def _token_view_stride(t, B, T, H, d) -> int:
 
 
 def kda_fwd(q, k, v, alpha, beta, S0=None, *, l2norm: bool = True, sequential: bool = False,
-            no_split: bool = False, out=None, want_state: bool = True, workspace=None):
-    """KDA forward on the GPU (chimera_kda_fwd).
+            no_split: bool = False, out=None, want_state: bool = True, workspace=None,
+            marks: Optional[Marks] = None, state_out=None):
+    """KDA forward on the GPU (chimera_kda_fwd; chimera_kda_fwd_timed with `marks`).
 
     q, k [B, T, H, dk], v [B, T, H, dv] with a shared token stride (views into a
     fused q|k|v tensor are accepted), alpha [B, T, H, dk], beta [B, T, H], S0
-    fp32 [B, H, dk, dv] or None. Returns (o [B, T, H, dv], S_final or None).
+    fp32 [B, H, dk, dv] or None. Returns (o [B, T, H, dv], S_final or None);
+    `out` and `state_out` are written in place when given.
     """
     import torch
     B, T, H, dk = k.shape
@@ -176,16 +214,25 @@ def kda_fwd(q, k, v, alpha, beta, S0=None, *, l2norm: bool = True, sequential: b
     assert q.dtype == k.dtype == v.dtype == alpha.dtype == beta.dtype
     flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0) | (KDA_NO_SPLIT if no_split else 0)
     o = torch.empty((B, T, H, dv), dtype=k.dtype, device=k.device) if out is None else out
-    Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=k.device) if want_state else None
+    Sf = state_out
+    if Sf is None and want_state:
+        Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=k.device)
+    if Sf is not None:
+        assert Sf.dtype == torch.float32 and Sf.is_contiguous() and Sf.shape == (B, H, dk, dv)
     if S0 is not None:
         assert S0.dtype == torch.float32 and S0.is_contiguous() and S0.shape == (B, H, dk, dv)
     need = kda_workspace_size(B, T, H, dk, dv, dt, flags)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("chimera_kda_fwd",
-           lib().chimera_kda_fwd(_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o),
-                                 _ptr(Sf), B, T, H, dk, dv, dt, flags, _ptr(workspace), wbytes, _stream(k)))
+    args = (_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(Sf),
+            B, T, H, dk, dv, dt, flags, _ptr(workspace), wbytes, _stream(k))
+    if marks is None:
+        _check("chimera_kda_fwd", lib().chimera_kda_fwd(*args))
+    else:
+        _check("chimera_kda_fwd_timed",
+               lib().chimera_kda_fwd_timed(*args, marks.handles, marks.names, marks.capacity,
+                                           ctypes.byref(marks.used)))
     return o, Sf
 
 

@@ -117,9 +117,9 @@ chimera_status chimera_mshortconv_index_device(const chimera_segment* segs, int3
   return CHIMERA_OK;
 }
 
-chimera_status chimera_mshortconv_fwd(const void* x, void* y, int64_t B, int64_t T, int64_t C, chimera_dtype dt,
-                                      const float* w_text, const float* w_vis, const chimera_segment* segs,
-                                      int32_t nseg, hipStream_t stream) {
+static chimera_status conv_fwd(const void* x, void* y, int64_t B, int64_t T, int64_t C, chimera_dtype dt,
+                               const float* w_text, const float* w_vis, const chimera_segment* segs, int32_t nseg,
+                               hipStream_t stream, chm::Marks* marks) {
   if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
   if (B < 0 || C < 0) return CHIMERA_ERR_SHAPE;
   bool any_text, any_vis;
@@ -130,12 +130,33 @@ chimera_status chimera_mshortconv_fwd(const void* x, void* y, int64_t B, int64_t
   if (x == nullptr || y == nullptr) return CHIMERA_ERR_NULL;
   if ((any_text && w_text == nullptr) || (any_vis && w_vis == nullptr)) return CHIMERA_ERR_NULL;
   if (x == y) return CHIMERA_ERR_UNSUPPORTED;
+  if (marks != nullptr && chm::mark_begin(marks, stream) != hipSuccess) return CHIMERA_ERR_HIP;
   for (int32_t i = 0; i < nseg; ++i) {
     const hipError_t e = chm::launch_conv_segment(x, y, B, T, C, dt == CHIMERA_BF16, w_text, w_vis,
-                                                  to_seg(segs[i]), false, stream);
+                                                  to_seg(segs[i]), false, stream, marks);
     if (e != hipSuccess) return CHIMERA_ERR_HIP;
   }
   return CHIMERA_OK;
+}
+
+chimera_status chimera_mshortconv_fwd(const void* x, void* y, int64_t B, int64_t T, int64_t C, chimera_dtype dt,
+                                      const float* w_text, const float* w_vis, const chimera_segment* segs,
+                                      int32_t nseg, hipStream_t stream) {
+  return conv_fwd(x, y, B, T, C, dt, w_text, w_vis, segs, nseg, stream, nullptr);
+}
+
+chimera_status chimera_mshortconv_fwd_timed(const void* x, void* y, int64_t B, int64_t T, int64_t C,
+                                            chimera_dtype dt, const float* w_text, const float* w_vis,
+                                            const chimera_segment* segs, int32_t nseg, hipStream_t stream,
+                                            hipEvent_t* marks, const char** names, int32_t capacity,
+                                            int32_t* used) {
+  if (marks == nullptr || names == nullptr || used == nullptr) return CHIMERA_ERR_NULL;
+  *used = 0;
+  if (nseg < 0 || capacity < nseg + 1) return CHIMERA_ERR_SHAPE;
+  chm::Marks m{marks, names, capacity, 0};
+  const chimera_status st = conv_fwd(x, y, B, T, C, dt, w_text, w_vis, segs, nseg, stream, &m);
+  *used = m.n;
+  return st;
 }
 
 static bool kda_sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
@@ -152,10 +173,10 @@ size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, i
   return chm::kda_chunked_workspace(B, T, H, (flags & CHIMERA_KDA_NO_SPLIT) != 0);
 }
 
-chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
-                               const void* beta, const float* S0, void* o, float* S_final, int64_t B, int64_t T,
-                               int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
+                              const void* beta, const float* S0, void* o, float* S_final, int64_t B, int64_t T,
+                              int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, chm::Marks* marks) {
   if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
   if (!kda_sizes_ok(B, T, H, dk, dv)) return CHIMERA_ERR_SHAPE;
   if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL | CHIMERA_KDA_NO_SPLIT)) return CHIMERA_ERR_UNSUPPORTED;
@@ -172,11 +193,37 @@ chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int6
   a.bf16 = dt == CHIMERA_BF16;
   a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
   const bool chunked = !(flags & CHIMERA_KDA_SEQUENTIAL) && chm::kda_chunked_supported(a) && T > 0;
-  if (!chunked) return hip_status(chm::launch_kda_sequential(a, stream));
   const bool no_split = (flags & CHIMERA_KDA_NO_SPLIT) != 0;
-  const size_t need = chm::kda_chunked_workspace(B, T, H, no_split);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
-  return hip_status(chm::launch_kda_chunked(a, no_split, workspace, stream));
+  if (chunked) {
+    const size_t need = chm::kda_chunked_workspace(B, T, H, no_split);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
+  }
+  if (marks != nullptr && chm::mark_begin(marks, stream) != hipSuccess) return CHIMERA_ERR_HIP;
+  if (!chunked) return hip_status(chm::launch_kda_sequential(a, stream, marks));
+  return hip_status(chm::launch_kda_chunked(a, no_split, workspace, stream, marks));
+}
+
+chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
+                               const void* beta, const float* S0, void* o, float* S_final, int64_t B, int64_t T,
+                               int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags, workspace,
+                 workspace_bytes, stream, nullptr);
+}
+
+chimera_status chimera_kda_fwd_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                     const void* alpha, const void* beta, const float* S0, void* o, float* S_final,
+                                     int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                                     uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                     hipEvent_t* marks, const char** names, int32_t capacity, int32_t* used) {
+  if (marks == nullptr || names == nullptr || used == nullptr) return CHIMERA_ERR_NULL;
+  *used = 0;
+  if (capacity < CHIMERA_KDA_MAX_KERNELS + 1) return CHIMERA_ERR_SHAPE;
+  chm::Marks m{marks, names, capacity, 0};
+  const chimera_status st = kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags,
+                                    workspace, workspace_bytes, stream, &m);
+  *used = m.n;
+  return st;
 }
 
 }  // extern "C"

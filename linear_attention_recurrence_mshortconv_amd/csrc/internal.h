@@ -8,11 +8,33 @@
 
 namespace chm {
 
+// ---- Per-kernel timing marks ----------------------------------------------------
+// Optional. When a launcher gets a non-null Marks, it records ev[n] on the launch
+// stream after each kernel it launches and names that kernel in names[n - 1]; the
+// entry point records ev[0] before the first launch. The caller checks `cap`
+// against the launch count before any launch, so these never run out.
+struct Marks {
+  hipEvent_t* ev;
+  const char** names;
+  int32_t cap;
+  int32_t n;
+};
+inline hipError_t mark_begin(Marks* m, hipStream_t s) {
+  if (m == nullptr) return hipSuccess;
+  m->n = 1;
+  return hipEventRecord(m->ev[0], s);
+}
+inline hipError_t mark_after(Marks* m, const char* kernel, hipStream_t s) {
+  if (m == nullptr || m->n >= m->cap) return hipSuccess;
+  m->names[m->n - 1] = kernel;
+  return hipEventRecord(m->ev[m->n++], s);
+}
+
 // ---- mShortConv -------------------------------------------------------------
 // y = mShortConv(x) for one segment, x/y [B][T][C] with C % 8 == 0.
 hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t T, int64_t C, bool bf16,
                                const float* w_text, const float* w_vis, const Seg& seg,
-                               bool force_gather, hipStream_t stream);
+                               bool force_gather, hipStream_t stream, Marks* marks = nullptr);
 
 // Device-side neighbour table [T][27] for one segment (the conv kernels' arithmetic).
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream);
@@ -34,12 +56,13 @@ struct KdaArgs {
 };
 
 // Token-by-token fp32 kernel: any dk, dv in 1..256.
-hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream);
+hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr);
 
 // Chunked MFMA path (bf16, dk = dv = 128).
 bool kda_chunked_supported(const KdaArgs& a);
 int64_t kda_chunked_segments(int64_t B, int64_t T, int64_t H, bool no_split);
 size_t kda_chunked_workspace(int64_t B, int64_t T, int64_t H, bool no_split);
-hipError_t launch_kda_chunked(const KdaArgs& a, bool no_split, void* workspace, hipStream_t stream);
+hipError_t launch_kda_chunked(const KdaArgs& a, bool no_split, void* workspace, hipStream_t stream,
+                              Marks* marks = nullptr);
 
 }  // namespace chm

@@ -957,7 +957,6 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
   const int64_t c_end = min<int64_t>(min<int64_t>(NC, c_begin + a.L), a.c_stop);
 
   const int col0 = 32 * (wave & 3);
-  const int svo = (4 * q4) * D + col0 + l16;
   f32x4 S[8][2];
 #pragma unroll
   for (int rt = 0; rt < 8; ++rt)
@@ -1311,7 +1310,7 @@ size_t kda_chunked_workspace(int64_t B, int64_t T, int64_t H, bool no_split) {
   return (size_t)(B * H) * (2 * E + sp.Po) * mat;
 }
 
-hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, hipStream_t stream) {
+hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, hipStream_t stream, Marks* marks) {
   const Split sp = choose_split(x.B, x.T, x.H, no_split);
   const int64_t BH = x.B * x.H;
   if (BH * sp.Po * 2 > 0x7fffff00) return hipErrorInvalidValue;
@@ -1364,10 +1363,12 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
     s.grid = round8(s.nblk);
     hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(2 * NTHR), lds_sum, stream, s);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark_after(marks, "kda_sum_kernel", stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kda_combine_kernel, dim3((unsigned)(BH * 8)), dim3(CB_T), 0, stream, WS, WM, x.S0, Sst, sp.Po,
                        (int)E);
     e = hipGetLastError();
+    if (e == hipSuccess) e = mark_after(marks, "kda_combine_kernel", stream);
     if (e != hipSuccess) return e;
     a.Sstart = Sst;
     a.WS = WS;
@@ -1381,7 +1382,8 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   a.nblk = (int)(BH * sp.Po);
   a.grid = round8(a.nblk);
   hipLaunchKernelGGL(kda_out_kernel, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : mark_after(marks, "kda_out_kernel", stream);
 }
 
 }  // namespace chm

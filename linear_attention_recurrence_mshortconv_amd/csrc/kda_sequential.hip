@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
 
 }  // namespace
 
-hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream) {
+hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks) {
   if (a.B * a.H == 0) return hipSuccess;
   const int n_vs = (int)((a.dv + 15) / 16);
   const int64_t blocks = a.B * a.H * n_vs;
@@ -144,7 +144,8 @@ hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream) {
                        a.qkv_stride, static_cast<const float*>(a.alpha), static_cast<const float*>(a.beta), a.S0,
                        static_cast<float*>(a.o), a.S_final, a.T, a.H, (int)a.dk, (int)a.dv, (int)a.l2norm);
   }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : mark_after(marks, "kda_seq_kernel", stream);
 }
 
 }  // namespace chm

@@ -403,7 +403,7 @@ __global__ void index_device_kernel(Seg seg, int32_t* __restrict__ idx) {
 
 template <int NF, int CPT, int TR, int TW>
 hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
-                       const Seg& seg, hipStream_t stream) {
+                       const Seg& seg, hipStream_t stream, Marks* marks) {
   using Cfg = TileCfg<NF, CPT, TR, TW>;
   const int n_slab = (int)(C / 64);
   const int n_tw = (int)((seg.width + TW - 1) / TW);
@@ -426,12 +426,13 @@ hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64
   const int64_t grid = (n_logical + 7) / 8 * 8;
   hipLaunchKernelGGL((conv_tile_kernel<NF, CPT, TR, TW>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, stream, x, y,
                      w_vis, Ttot, C, seg, n_slab, n_tw, n_th, n_fr, fpb, (int)n_logical);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : mark_after(marks, "conv_tile_kernel", stream);
 }
 
 template <int TR, int TW>
 hipError_t launch_rows(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
-                       const Seg& seg, hipStream_t stream) {
+                       const Seg& seg, hipStream_t stream, Marks* marks) {
   const int n_slab = (int)(C / 64);
   const int n_tw = (int)((seg.width + TW - 1) / TW);
   // split the rows into ranges so that there are enough blocks (each range re-reads 2 halo rows)
@@ -446,21 +447,22 @@ hipError_t launch_rows(const uint16_t* x, uint16_t* y, const float* w_vis, int64
   const int64_t grid = (n_logical + 7) / 8 * 8;
   hipLaunchKernelGGL((conv_rows_kernel<TR, TW>), dim3((unsigned)grid), dim3(TW * 8), 0, stream, x, y, w_vis, Ttot, C,
                      seg, n_slab, n_tw, n_rr, rows_per_range, (int)n_logical);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : mark_after(marks, "conv_rows_kernel", stream);
 }
 
 }  // namespace
 
 hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, int64_t C, bool bf16,
                                const float* w_text, const float* w_vis, const Seg& seg, bool force_gather,
-                               hipStream_t stream) {
+                               hipStream_t stream, Marks* marks) {
   if (seg.length == 0 || B == 0) return hipSuccess;
   const bool tiled = bf16 && seg.kind != SEG_TEXT && C % 64 == 0 && !force_gather;
   if (tiled) {
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     uint16_t* ys = static_cast<uint16_t*>(y);
-    if (seg.frames == 1) return launch_rows<4, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream);
-    return launch_tile<3, 4, 8, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream);
+    if (seg.frames == 1) return launch_rows<4, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
+    return launch_tile<3, 4, 8, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
   }
   if (B > 65535) return hipErrorInvalidValue;
   if (seg.kind == SEG_TEXT) {
@@ -473,7 +475,8 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
       hipLaunchKernelGGL(conv_text_kernel<float>, tgrid, dim3(256), 0, stream, static_cast<const float*>(x),
                          static_cast<float*>(y), w_text, Ttot, C, seg);
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : mark_after(marks, "conv_text_kernel", stream);
   }
   const dim3 grid((unsigned)((C / 8 + 63) / 64), (unsigned)((seg.length + 3) / 4), (unsigned)B);
   if (grid.y > 0x7fffffffu) return hipErrorInvalidValue;
@@ -484,7 +487,8 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
     hipLaunchKernelGGL(conv_gather_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(x),
                        static_cast<float*>(y), w_text, w_vis, Ttot, C, seg);
   }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : mark_after(marks, "conv_gather_kernel", stream);
 }
 
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream) {

@@ -146,3 +146,24 @@ def test_workspace_size_rules():
     assert chm.kda_workspace_size(1, 256, 2, 32, 32, chm.F32, 0) == 0            # sequential path
     assert chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_SEQUENTIAL) == 0
     assert chm.kda_workspace_size(1, 10, 1, 0, 128, chm.BF16, 0) == 0            # invalid sizes
+
+
+def test_timed_variants_check_their_marks_first():
+    """The timing variants refuse missing or too few marks before any launch."""
+    L = chm.lib()
+    arr = chm.segment_array([dict(kind=0, start=0, length=4), dict(kind=1, start=4, length=4, frames=1, height=2,
+                                                                    width=2)])
+    ev = (ctypes.c_void_p * 8)()
+    names = (ctypes.c_char_p * 8)()
+    used = ctypes.c_int32(5)
+    conv = lambda ev_, cap: L.chimera_mshortconv_fwd_timed(1, 2, 1, 8, 8, 1, 3, 4, arr, 2, None, ev_, names, cap,
+                                                           ctypes.byref(used))
+    assert conv(None, 8) == 1
+    assert conv(ev, 2) == 2 and used.value == 0                          # needs nseg + 1 = 3
+    kda = lambda ev_, cap: L.chimera_kda_fwd_timed(1, 2, 3, 256, 4, 5, None, 6, None, 1, 8, 2, 128, 128, 1, 1,
+                                                   None, 0, None, ev_, names, cap, ctypes.byref(used))
+    assert kda(None, 8) == 1
+    assert kda(ev, 3) == 2                                                 # needs 3 kernels + 1
+    used.value = 9
+    assert L.chimera_kda_fwd_timed(1, 2, 3, 256, 4, 5, None, 6, None, 0, 8, 2, 128, 128, 1, 1, None, 0, None, ev,
+                                   names, 4, ctypes.byref(used)) == 0 and used.value == 0   # B = 0: nothing launched

@@ -202,3 +202,24 @@ def test_pipeline_full_workload_sampled_heads(chm, wi):
                            inp["alpha"][:, :, heads], inp["beta"][:, :, heads], S0)
     assert_close(o_got, o_ref, "bf16", f"{w.name} o")
     assert_close(S_got, S_ref, "bf16", f"{w.name} S_final")
+
+
+def test_timed_variants_match_untimed(chm):
+    """The timing entry points launch the same kernels: identical outputs, one mark per kernel."""
+    import torch
+    w = wl.WORKLOADS[1]
+    inp = wl.make_inputs(w)
+    x_dev = to_device(inp["x"], "bf16")
+    wt, wv = torch.from_numpy(inp["w_text"]), torch.from_numpy(inp["w_vis"])
+    y1 = chm.mshortconv_fwd(x_dev, wt, wv, inp["segments"])
+    mc = chm.Marks(len(inp["segments"]) + 1)
+    y2 = chm.mshortconv_fwd(x_dev, wt, wv, inp["segments"], marks=mc)
+    o1, S1 = _run_kda(chm, y1, inp["alpha"], inp["beta"], inp["S0"], w)
+    mk = chm.Marks(4)
+    o2, S2 = _run_kda(chm, y1, inp["alpha"], inp["beta"], inp["S0"], w, marks=mk)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(o1, o2) and torch.equal(S1, S2)
+    conv_k, kda_k = mc.kernels(), mk.kernels()
+    assert [n for n, _ in conv_k] == ["conv_text_kernel", "conv_rows_kernel"]
+    assert [n for n, _ in kda_k] == ["kda_sum_kernel", "kda_combine_kernel", "kda_out_kernel"]
+    assert all(ms > 0 for _, ms in conv_k + kda_k)
