@@ -53,6 +53,16 @@ __device__ __forceinline__ float to_f32(float f) { return f; }
 __device__ __forceinline__ void from_f32(uint16_t* p, float f) { *p = f2bf(f); }
 __device__ __forceinline__ void from_f32(float* p, float f) { *p = f; }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for outstanding global loads and stores, so prefetches and
+// write-backs stay in flight across it (the compiler still waits for a load
+// before its result is used).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Work is spread over the 8 XCDs round-robin by block id; this maps the
 // hardware block id to a logical id so that each XCD gets one contiguous range
 // of logical ids (neighbouring tiles then share that XCD's L2). `nblk` must be

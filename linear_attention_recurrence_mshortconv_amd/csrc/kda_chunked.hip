@@ -206,13 +206,6 @@ __device__ __forceinline__ uint2 ld_buf64(__amdgpu_buffer_rsrc_t r, int voff, in
   return make_uint2(v[0], v[1]);
 }
 
-// Block barrier that orders LDS only: global loads in flight stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __device__ __forceinline__ uint4 ld128(const uint16_t* base, int idx) {
   return *reinterpret_cast<const uint4*>(base + idx);
 }
@@ -304,14 +297,12 @@ __device__ __forceinline__ void epi_q(Lds& L, int I, int J, f32x4 acc, int l16, 
   }
   *reinterpret_cast<uint2*>(&L.aqk[tr(j, SBT * I + 4 * q4)]) = pack4(make_float4(v[0], v[1], v[2], v[3]));
 }
-// T_II = (I + A_II)^{-1} for the four diagonal blocks at once: lane = 16 I + j forms
-// column j of T_II by forward substitution, x_i = [i = j] - sum_{k < i} A_II(i, k) x_k,
-// reading the rows of A_II (written by this wave) as broadcasts; the column goes to at
-// as four 8-byte writes.
-__device__ __forceinline__ void invert_diag4(Lds& L, int lane) {
+// T_II = (I + A_II)^{-1}: lane j of a 16-lane group forms column j of T_II by forward
+// substitution, x_i = [i = j] - sum_{k < i} A_II(i, k) x_k, reading the rows of A_II
+// (written by this wave) as broadcasts; the column goes to at as four 8-byte writes.
+__device__ __forceinline__ void invert_diag(Lds& L, int I, int jj, bool write) {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  const int I = lane >> 4, jj = lane & 15;
   float x[SBT];
 #pragma unroll
   for (int i = 0; i < SBT; ++i) {
@@ -331,11 +322,15 @@ __device__ __forceinline__ void invert_diag4(Lds& L, int lane) {
     }
     x[i] = acc0 + acc1;
   }
+  if (write) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    *reinterpret_cast<uint2*>(&L.at[tr(SBT * I + jj, SBT * I + 4 * m)]) =
-        make_uint2(pack_bf16x2(x[4 * m], x[4 * m + 1]), pack_bf16x2(x[4 * m + 2], x[4 * m + 3]));
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<uint2*>(&L.at[tr(SBT * I + jj, SBT * I + 4 * m)]) =
+          make_uint2(pack_bf16x2(x[4 * m], x[4 * m + 1]), pack_bf16x2(x[4 * m + 2], x[4 * m + 3]));
+  }
 }
+// the four diagonal blocks at once, lane = 16 I + j
+__device__ __forceinline__ void invert_diag4(Lds& L, int lane) { invert_diag(L, lane >> 4, lane & 15, true); }
 // mma16 A fragments of at (transposed reads): block (I, J), J <= I, at I (I + 1) / 2 + J
 __device__ __forceinline__ void load_t_frags(const Lds& L, uint2 (&af)[10], int l16, int q4) {
 #pragma unroll
@@ -1122,23 +1117,32 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     // ---- M1T: A blocks, diagonal inverses ------------------------------------------------
     {
       uint4 cA[4], rA[4], sc[4];
-      // wave 0: the four diagonal A blocks and their inverses; waves 1-6: one block below
-      // the diagonal each: A10 A20 A30 A21 A31 A32
-      if (wave == 0) {
-#pragma unroll
-        for (int I = 0; I < NSB; ++I) {
-          tile_frags(L.kc, I, cA, l16, q4);
-          tile_frags(L.kr, I, rA, l16, q4);
-          epi_a(L, I, I, mma4(rA, cA), l16, q4);
-        }
-        invert_diag4(L, lane_c);
-      } else if (wave < 7) {
-        const int I = wave < 4 ? wave : (wave == 6 ? 3 : wave - 2);
-        const int J = wave < 4 ? 0 : (wave == 6 ? 2 : 1);
-        tile_frags(L.kc, J, cA, l16, q4);
-        pair_frags(L, fast, I, J, cA, sc, q4);
+      // waves 4-7: diagonal block I = wave - 4 and its inverse; waves 0-3: the blocks below
+      // the diagonal (wave 0: A10 A32, wave 1: A20, wave 2: A30 A21, wave 3: A31)
+      if (wave >= 4) {
+        const int I = wave - 4;
+        tile_frags(L.kc, I, cA, l16, q4);
         tile_frags(L.kr, I, rA, l16, q4);
-        epi_a(L, I, J, mma4(rA, sc), l16, q4);
+        epi_a(L, I, I, mma4(rA, cA), l16, q4);
+        invert_diag(L, I, l16, q4 == 0);
+      } else {
+        auto below = [&](int I, int J) {
+          tile_frags(L.kc, J, cA, l16, q4);
+          pair_frags(L, fast, I, J, cA, sc, q4);
+          tile_frags(L.kr, I, rA, l16, q4);
+          epi_a(L, I, J, mma4(rA, sc), l16, q4);
+        };
+        if (wave == 0) {
+          below(1, 0);
+          below(3, 2);
+        } else if (wave == 1) {
+          below(2, 0);
+        } else if (wave == 2) {
+          below(3, 0);
+          below(2, 1);
+        } else {
+          below(3, 1);
+        }
       }
     }
     lds_barrier();   // D

@@ -177,9 +177,9 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
   }
   if (f_begin < f_end) fetch(f_begin);
   for (int f = f_begin; f < f_end; ++f) {
-    __syncthreads();                                  // previous frame's reads are done
+    lds_barrier();                                    // previous frame's reads are done
     commit(NF == 3 ? f % 3 : 0);
-    __syncthreads();
+    lds_barrier();
     if (f + 1 < f_end) fetch(f + 1);                  // next frame's loads overlap this frame's math
     float acc[TR][CPT];
 #pragma unroll
@@ -227,6 +227,12 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
 // two halo rows of each step are the last rows of the previous step (every input
 // row is read from HBM once per strip); the next TR rows are loaded into
 // registers while the current TR output rows are computed.
+// Loads and stores are buffer accesses relative to the block's first row, with
+// 32-bit offsets: taps outside the grid get an offset past the buffer's end and
+// read zero, output positions outside it are dropped the same way, so there is
+// no branch around a memory access and every wait counts only what it needs.
+constexpr uint32_t kOutside = 0x80000000u;   // past every buffer: the launcher keeps them under 2 GiB
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 data format
 template <int TR, int TW>
 __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                          const float* __restrict__ w_vis, int64_t Ttot, int64_t C,
@@ -235,7 +241,9 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
   constexpr int NT = TW * 8, SC = TW + 2, RING = TR + 2;
   constexpr int ITEMS = TR * SC * 8;                 // 16-byte items per TR staged rows
   constexpr int NIT = (ITEMS + NT - 1) / NT;
-  __shared__ uint4 ring[RING][SC][8];
+  // ring[slot][column][group] flat, plus one slot per thread for the items past
+  // ITEMS of the last load round (so that every staging write is unconditional)
+  __shared__ uint4 ring[RING * SC * 8 + NT];
 
   const int lid = (int)xcd_contiguous_id(blockIdx.x, gridDim.x);
   if (lid >= n_logical) return;
@@ -246,12 +254,17 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
   const int64_t b = r;
 
   const int tid = threadIdx.x, g = tid & 7, col = tid >> 3;
-  const int64_t c0 = (int64_t)slab * 64 + g * 8;
-  const int64_t w0 = (int64_t)tw * TW;
+  const int w0 = tw * TW;
   const int r_begin = rr_ix * rows_per_range;
   const int r_end = min(seg.height, r_begin + rows_per_range);
-  const uint16_t* xb = x + b * Ttot * C;
-  uint16_t* yb = y + b * Ttot * C;
+  // buffers span grid rows base_row .. last_row - 1 of this batch item's segment
+  const int base_row = max(r_begin - 1, 0), last_row = min(seg.height, r_end + 1);
+  const int row_bytes = seg.width * (int)C * 2;
+  const int64_t base_tok = b * Ttot + seg.start + (int64_t)base_row * seg.width;
+  const auto xr = __builtin_amdgcn_make_buffer_rsrc((void*)(x + base_tok * C), 0, (last_row - base_row) * row_bytes,
+                                                    kRsrcWord3);
+  const auto yr = __builtin_amdgcn_make_buffer_rsrc((void*)(y + base_tok * C), 0, (last_row - base_row) * row_bytes,
+                                                    kRsrcWord3);
 
   float wr[3][3][8];
 #pragma unroll
@@ -259,8 +272,13 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
 #pragma unroll
     for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wr[kh][kw][i] = w_vis[(c0 + i) * kVisTaps + 18 + kh * 3 + kw];
+      for (int i = 0; i < 8; ++i) wr[kh][kw][i] = w_vis[((int64_t)slab * 64 + g * 8 + i) * kVisTaps + 18 + kh * 3 + kw];
 
+  // byte offset of (grid row hh, grid column ww, channel group gg), or kOutside
+  auto offset = [&](int hh, int ww, int gg) -> uint32_t {
+    const bool in = (hh >= 0) & (hh < seg.height) & (ww >= 0) & (ww < seg.width);
+    return in ? (uint32_t)((hh - base_row) * row_bytes + ww * (int)C * 2 + slab * 128 + gg * 16) : kOutside;
+  };
   // ring slot of grid row hh (hh >= r_begin - 1)
   auto slot_of = [&](int hh) { return (hh - r_begin + 1) % RING; };
   uint4 pre[NIT];
@@ -271,29 +289,28 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
       const int it = tid + j * NT;
       const int rowi = it / (SC * 8), rem = it % (SC * 8);
       const int sc = rem >> 3, gg = rem & 7;
-      const int64_t hh = first_row + rowi, ww = w0 + sc - 1;
-      pre[j] = uint4{0u, 0u, 0u, 0u};
-      if (it < ITEMS && rowi < nrows && grid_inside(seg, 0, hh, ww))
-        pre[j] = *reinterpret_cast<const uint4*>(xb + raster_index(seg, 0, hh, ww) * C + (int64_t)slab * 64 + gg * 8);
+      const uint32_t off = ((it < ITEMS) & (rowi < nrows)) ? offset(first_row + rowi, w0 + sc - 1, gg) : kOutside;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0);
+      pre[j] = uint4{v[0], v[1], v[2], v[3]};
     }
   };
+  // stage what fetch loaded; items of rows at or past nrows land in the spare slots
   auto commit = [&](int first_row, int nrows) {
 #pragma unroll
     for (int j = 0; j < NIT; ++j) {
       const int it = tid + j * NT;
       const int rowi = it / (SC * 8), rem = it % (SC * 8);
-      if (it < ITEMS && rowi < nrows) ring[slot_of(first_row + rowi)][rem >> 3][rem & 7] = pre[j];
+      const bool real = (it < ITEMS) & (rowi < nrows);
+      ring[real ? slot_of(first_row + rowi) * (SC * 8) + rem : RING * SC * 8 + tid] = pre[j];
     }
   };
 
-  // the first step needs rows r_begin - 1 .. r_begin + TR; rows outside the grid stage as zero
-  fetch(r_begin - 1, 2);
-  commit(r_begin - 1, 2);
-  fetch(r_begin + 1, TR);
-  for (int h0 = r_begin; h0 < r_end; h0 += TR) {
-    __syncthreads();                                 // the previous step's reads of the ring are done
+  // One step: stage rows h0 + 1 .. h0 + TR (loaded during the previous step), start
+  // loading the next step's rows, and compute output rows h0 .. h0 + TR - 1.
+  auto step = [&](int h0) {
+    lds_barrier();                                   // the previous step's reads of the ring are done
     commit(h0 + 1, TR);                              // rows h0+1 .. h0+TR
-    __syncthreads();
+    lds_barrier();
     if (h0 + TR < r_end) fetch(h0 + TR + 1, TR);     // next step's new rows, in flight during the math
     float acc[TR][8];
 #pragma unroll
@@ -307,7 +324,7 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
 #pragma unroll
       for (int kw = 0; kw < 3; ++kw) {
         float v[8];
-        unpack(ring[sl][col + kw][g], v);
+        unpack(ring[(sl * SC + col + kw) * 8 + g], v);
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh) {
           const int orow = ir - kh;
@@ -317,17 +334,25 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
         }
       }
     }
-    const int64_t ww = w0 + col;
 #pragma unroll
     for (int q = 0; q < TR; ++q) {
-      const int64_t hh = h0 + q;
-      if (hh < r_end && ww < seg.width) {
-        uint4 out;
-        pack(out, acc[q]);
-        *reinterpret_cast<uint4*>(yb + raster_index(seg, 0, hh, ww) * C + c0) = out;
-      }
+      uint4 out;
+      pack(out, acc[q]);
+      const uint32_t off = h0 + q < r_end ? offset(h0 + q, w0 + col, g) : kOutside;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, out), yr, (int)off, 0, 0);
     }
-  }
+  };
+
+  // the first step needs rows r_begin - 1 .. r_begin + TR; rows outside the grid stage as zero
+  fetch(r_begin - 1, 2);
+  commit(r_begin - 1, 2);
+  fetch(r_begin + 1, TR);
+  // The first step runs outside the loop: every step then starts with the same
+  // outstanding accesses (the staged loads, then the previous stores), so the waits
+  // before staging count the loads only and the stores stay in flight.
+  step(r_begin);
+  for (int h0 = r_begin + TR; h0 < r_end; h0 += TR) step(h0);
 }
 
 // Text segments (causal, 4 taps): a thread owns 8 channels and 16 consecutive
@@ -430,16 +455,45 @@ hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64
   return e != hipSuccess ? e : mark_after(marks, "conv_tile_kernel", stream);
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Byte span of one rows-kernel buffer: (rows_per_range + 2) grid rows; kept
+// below kOutside so that the out-of-grid offset always reads zero.
+constexpr int64_t kRowsSpanMax = (int64_t)kOutside - 64;
+
+template <int TR, int TW>
+bool rows_fit(const Seg& seg, int64_t C) {
+  return (int64_t)(TR + 2) * seg.width * C * 2 <= kRowsSpanMax;
+}
+
 template <int TR, int TW>
 hipError_t launch_rows(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
                        const Seg& seg, hipStream_t stream, Marks* marks) {
   const int n_slab = (int)(C / 64);
   const int n_tw = (int)((seg.width + TW - 1) / TW);
-  // split the rows into ranges so that there are enough blocks (each range re-reads 2 halo rows)
+  // Split the rows into ranges (each re-reads 2 halo rows) so that the grid is about
+  // six rounds of the blocks that fit on the chip at once (two per CU): blocks are
+  // long-lived, and a grid of a few whole rounds keeps the last round full.
   const int64_t per_range = (int64_t)n_slab * n_tw * B;
-  int n_rr = (int)std::max<int64_t>(1, std::min<int64_t>((2048 + per_range - 1) / per_range, (seg.height + 4 * TR - 1) / (4 * TR)));
+  const int64_t want = 12 * (int64_t)device_cus();
+  int n_rr = (int)std::max<int64_t>(1, std::min<int64_t>((want + per_range - 1) / per_range, (seg.height + 4 * TR - 1) / (4 * TR)));
   int rows_per_range = (seg.height + n_rr - 1) / n_rr;
   rows_per_range = (rows_per_range + TR - 1) / TR * TR;
+  // the buffers of one block span rows_per_range + 2 rows
+  const int64_t row_bytes = (int64_t)seg.width * C * 2;
+  const int64_t max_rows = (kRowsSpanMax / row_bytes - 2) / TR * TR;
+  if (max_rows < TR) return hipErrorInvalidValue;
+  if (rows_per_range > max_rows) rows_per_range = (int)max_rows;
   n_rr = (seg.height + rows_per_range - 1) / rows_per_range;
   const int64_t n_logical = per_range * n_rr;
   if (n_logical <= 0) return hipSuccess;
@@ -461,7 +515,7 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
   if (tiled) {
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     uint16_t* ys = static_cast<uint16_t*>(y);
-    if (seg.frames == 1) return launch_rows<4, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
+    if (seg.frames == 1 && rows_fit<4, 32>(seg, C)) return launch_rows<4, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
     return launch_tile<3, 4, 8, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
   }
   if (B > 65535) return hipErrorInvalidValue;
