@@ -33,6 +33,8 @@
 //   combine pass: S_start(e + 1) = M_e S_start(base) + S_e, fp32-accurate MFMA;
 //   output pass:  each output segment reruns from S_start(p), writing o.
 // With one output segment only the output pass runs, starting from S0.
+#include <cstddef>
+
 #include "dtypes.h"
 #include "internal.h"
 
@@ -506,10 +508,44 @@ __device__ __forceinline__ void store_tiles(const f32x4 (&S)[8][2], float* m, in
 __device__ __forceinline__ f32x4 load_tile4(const float* m, int cb, int rt, int ct, int lane) {
   return *reinterpret_cast<const f32x4*>(m + tile_off(cb, rt, ct, lane));
 }
-// m[row][k .. k + 3] of a tile-major matrix, k a multiple of 4
-__device__ __forceinline__ float4 load_row4(const float* m, int row, int k) {
-  const float* p = m + tile_off(k >> 5, row >> 4, (k >> 4) & 1, 16 * ((row & 15) >> 2) + (k & 15)) + (row & 3);
-  return make_float4(p[0], p[4], p[8], p[12]);
+
+// Transitions M_e are kept as MFMA A operands, already split into bf16 high and
+// low parts: fragment (row tile rt, k slot s) of lane l = 16 q4 + l16 holds row
+// 16 rt + l16, columns 32 s + 4 q4 + 0..3 (slots 0-3) and 32 s + 16 + 4 q4 + 0..3
+// (slots 4-7); the high uint4 is followed by the low uint4 (64 KiB per matrix).
+__device__ __forceinline__ int mfrag_off(int rt, int s, int lane) { return ((rt * 4 + s) * 64 + lane) * 2; }
+// Store the 32 columns 32 cb .. 32 cb + 31 held by this wave (D layout) in that form:
+// they make up the k slot s = cb of every row tile. Each row tile is transposed
+// through this wave's LDS scratch `scr` (two 32 x 40 bf16 arrays, high and low
+// parts, laid out like kc: [k][cpos(row)]) and read back with the transposing
+// read, so that every global store is a 16-byte piece.
+constexpr int kMsP = 40;                            // scratch row pitch (elements)
+constexpr int kMsWave = 2 * 32 * kMsP;              // scratch elements per wave
+static_assert(offsetof(Lds, kc) == offsetof(Lds, kr) + sizeof(Lds::kr) && 4 * kMsWave <= 2 * CT * RKS,
+              "the four M waves' scratch lies in kr and kc");
+__device__ __forceinline__ void store_mfrag(const f32x4 (&S)[8][2], uint4* m, int cb, int lane, uint16_t* scr) {
+  uint16_t* hiB = scr;
+  uint16_t* loB = scr + 32 * kMsP;
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int kbase = (4 * q4 + (l16 >> 2)) * kMsP + 8 * (l16 & 3);
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      uint2 lo;
+      const uint2 hi = pack_split(make_float4(S[rt][ct][0], S[rt][ct][1], S[rt][ct][2], S[rt][ct][3]), lo);
+      *reinterpret_cast<uint2*>(&hiB[(16 * ct + l16) * kMsP + 8 * q4]) = hi;   // rows 4 q4 .. + 3 at cpos
+      *reinterpret_cast<uint2*>(&loB[(16 * ct + l16) * kMsP + 8 * q4]) = lo;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    const uint4 h = cat(ld_tr(&hiB[kbase]), ld_tr(&hiB[kbase + 16 * kMsP]));
+    const uint4 l = cat(ld_tr(&loB[kbase]), ld_tr(&loB[kbase + 16 * kMsP]));
+    m[mfrag_off(rt, cb, lane)] = h;
+    m[mfrag_off(rt, cb, lane) + 1] = l;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 // v of the state columns col0 .. col0 + 31 of the chunk: lane = tokens 4 (lane >> 2) + j,
@@ -604,13 +640,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt) {
       uint4 aH[4], aL[4];
+      const uint4* Mf = reinterpret_cast<const uint4*>(Mp);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        uint2 l0, l1;
-        const uint2 h0 = pack_split(load_row4(Mp, 16 * rt + l16, 32 * s + 4 * q4), l0);
-        const uint2 h1 = pack_split(load_row4(Mp, 16 * rt + l16, 32 * s + 16 + 4 * q4), l1);
-        aH[s] = cat(h0, h1);
-        aL[s] = cat(l0, l1);
+        aH[s] = Mf[mfrag_off(rt, s, lane)];
+        aL[s] = Mf[mfrag_off(rt, s, lane) + 1];
       }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -1178,7 +1212,12 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t rel = c - c_begin;
     if ((rel + 1) % a.Lo == 0) {
       const int e = p * kSub + (int)(rel / a.Lo);
-      store_tiles(S, (mkind ? a.WM : a.WS) + (bh * a.E + e) * D * D, wave & 3, lane);
+      // M: the chunk's kr and kc are free until the next chunk's barrier B
+      if (mkind)
+        store_mfrag(S, reinterpret_cast<uint4*>(a.WM + (bh * a.E + e) * D * D), wave & 3, lane_c,
+                    L.kr + (wave - 4) * kMsWave);
+      else
+        store_tiles(S, a.WS + (bh * a.E + e) * D * D, wave & 3, lane_c);
     }
   }
 }
@@ -1209,7 +1248,6 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = 16 * slice + l16;
   const int row0 = 16 * wave + 4 * q4;       // D-layout rows of this lane: row0 .. row0 + 3
-  const int arow = 16 * wave + l16;          // A-operand row of this lane
 
   f32x4 cur;
 #pragma unroll
@@ -1219,17 +1257,17 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
   };
   store(0, cur);
   const int nsteps = (P - 1) / kSub;   // chain starts kSub, 2 kSub, .. below P
-  // rows of M_e of a step: slots 0-3 columns 32 s + 4 q4 .., 4-7 columns 32 s + 16 + 4 q4 ..
-  float4 mq[kAhead][8];
+  // A fragments of M_e for this wave's rows (split bf16, slot s: high 2 s, low 2 s + 1)
+  uint4 mq[kAhead][8];
   f32x4 sq[kAhead];
-  auto fetch = [&](int step, float4(&m)[8], f32x4& sv) {
+  auto fetch = [&](int step, uint4(&m)[8], f32x4& sv) {
     if (step < nsteps) {
       const int e = step * kSub + kSub - 1;
-      const float* mp = WM + (bh * E + e) * D * D;
+      const uint4* mp = reinterpret_cast<const uint4*>(WM + (bh * E + e) * D * D);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        m[2 * s] = load_row4(mp, arow, 32 * s + 4 * q4);
-        m[2 * s + 1] = load_row4(mp, arow, 32 * s + 16 + 4 * q4);
+        m[2 * s] = mp[mfrag_off(wave, s, lane)];
+        m[2 * s + 1] = mp[mfrag_off(wave, s, lane) + 1];
       }
       sv = load_tile4(WS + (bh * E + e) * D * D, slice >> 1, wave, slice & 1, lane);
     }
@@ -1255,9 +1293,7 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
     f32x4 acc0 = sq[0], acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint2 l0, l1;
-      const uint2 h0 = pack_split(mq[0][2 * s], l0), h1 = pack_split(mq[0][2 * s + 1], l1);
-      const uint4 ah = cat(h0, h1), al = cat(l0, l1);
+      const uint4 ah = mq[0][2 * s], al = mq[0][2 * s + 1];
       acc1 = mma32(al, bH[s], acc1);
       acc2 = mma32(ah, bL[s], acc2);
       acc0 = mma32(ah, bH[s], acc0);

@@ -355,10 +355,11 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
   for (int h0 = r_begin + TR; h0 < r_end; h0 += TR) step(h0);
 }
 
-// Text segments (causal, 4 taps): a thread owns 8 channels and 16 consecutive
-// tokens, keeps its weights and a 4-token window in registers, and loads each
-// input token once.
-constexpr int kTextRun = 16;
+// Text segments (causal, 4 taps): a thread owns 8 channels and kTextRun
+// consecutive tokens and keeps its weights and a 4-token window in registers.
+// Short runs give enough blocks for a few hundred text tokens; the three window
+// tokens before a run are re-read (from L2) by the run that also owns them.
+constexpr int kTextRun = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void conv_text_kernel(const T* __restrict__ x, T* __restrict__ y,
                                                        const float* __restrict__ w_text, int64_t Ttot, int64_t C,
