@@ -882,11 +882,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     // this wave's v columns (U~, kept in registers)
     f32x4 Ut[4][2];
     {
+      stage_v(L, col0, vx, lane_c);   // first: v (loaded during M1T) leaves the registers
       uint2 af[10];
       load_t_frags(L, af, l16, q4);
       w_tile(L, fast, 2 * wave, af, l16, q4);
       w_tile(L, fast, 2 * wave + 1, af, l16, q4);
-      stage_v(L, col0, vx, lane_c);
       u_tiles(L, col0, af, Ut, l16, q4);
     }
     lds_barrier();   // E
