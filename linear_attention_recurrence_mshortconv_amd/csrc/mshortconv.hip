@@ -76,6 +76,12 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(const T* __restrict__ 
 // CPT: channels per thread (8 -> 16-byte accesses, 4 -> 8-byte accesses).
 // A block = TW columns x (64 / CPT) channel groups = TW*64/CPT threads, each
 // computing TR output rows of one column.
+// Buffer accesses: offsets past a buffer's end read zero and drop stores. Every
+// buffer the conv kernels build spans less than kOutside bytes (the launchers
+// check), so kOutside marks a position outside the grid.
+constexpr uint32_t kOutside = 0x80000000u;   // past every buffer: the launcher keeps them under 2 GiB
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 data format
+
 template <int NF, int CPT, int TR, int TW>
 struct TileCfg {
   static constexpr int kGroups = 64 / CPT;            // channel groups per 64-channel slab
@@ -110,7 +116,10 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
     int64_t C, Seg seg, int n_slab, int n_tw, int n_th, int n_fr, int frames_per_block, int n_logical) {
   using Cfg = TileCfg<NF, CPT, TR, TW>;
   using V = typename Vec<CPT>::T;
-  __shared__ V tile[NF][Cfg::kSlots][Cfg::kGroups];
+  constexpr int NIT = (Cfg::kItems + Cfg::kThreads - 1) / Cfg::kThreads;
+  // staged frames [slot][token][group], plus one spare item per thread for the items
+  // past kItems of the last load round (every staging write is unconditional)
+  __shared__ V tile[NF * Cfg::kSlots * Cfg::kGroups + Cfg::kThreads];
 
   const int lid = (int)xcd_contiguous_id(blockIdx.x, gridDim.x);
   if (lid >= n_logical) return;
@@ -124,10 +133,10 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
   const int tid = threadIdx.x;
   const int g = tid % Cfg::kGroups;              // channel group inside the slab
   const int col = tid / Cfg::kGroups;            // tile column 0..TW-1
-  const int64_t c0 = (int64_t)slab * 64 + g * CPT;
-  const int64_t h0 = (int64_t)th * TR, w0 = (int64_t)tw * TW;
-  const uint16_t* xb = x + b * Ttot * C;
-  uint16_t* yb = y + b * Ttot * C;
+  const int h0 = th * TR, w0 = tw * TW;
+  const int frame_bytes = seg.height * seg.width * (int)C * 2;
+  const uint16_t* xb = x + (b * Ttot + seg.start) * C;
+  uint16_t* yb = y + (b * Ttot + seg.start) * C;
 
   // weights of this thread's channels: wr[kt'][kh][kw][ch], kt' over the used time taps
   float wr[NF][3][3][CPT];
@@ -140,43 +149,48 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
           const int kt = 3 - NF + t;
-          wr[t][kh][kw][i] = w_vis[(c0 + i) * kVisTaps + kt * 9 + kh * 3 + kw];
+          wr[t][kh][kw][i] = w_vis[((int64_t)slab * 64 + g * CPT + i) * kVisTaps + kt * 9 + kh * 3 + kw];
         }
 
   const int f_begin = fr * frames_per_block;
   const int f_end = min(seg.frames, f_begin + frames_per_block);
 
+  // byte offset inside a frame of (row hh, column ww, channel group gg), or kOutside
+  auto offset = [&](int hh, int ww, int gg) -> uint32_t {
+    const bool in = (hh >= 0) & (hh < seg.height) & (ww >= 0) & (ww < seg.width);
+    return in ? (uint32_t)(((hh * seg.width + ww) * (int)C + slab * 64 + gg * CPT) * 2) : kOutside;
+  };
   // Staging of one frame's tile plus halo: every thread first loads its items
   // into registers (all loads in flight together), then stores them to LDS.
-  constexpr int NIT = (Cfg::kItems + Cfg::kThreads - 1) / Cfg::kThreads;
   V pre[NIT];
   auto fetch = [&](int ff) {
+    const auto xr = __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (int64_t)ff * seg.height * seg.width * C), 0,
+                                                      frame_bytes, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < NIT; ++j) {
       const int it = tid + j * Cfg::kThreads;
       const int s = it / Cfg::kGroups, gg = it % Cfg::kGroups;
-      const int64_t hh = h0 + s / Cfg::kSC - 1, ww = w0 + s % Cfg::kSC - 1;
-      pre[j] = V{};
-      if (it < Cfg::kItems && grid_inside(seg, ff, hh, ww))
-        pre[j] = *reinterpret_cast<const V*>(xb + raster_index(seg, ff, hh, ww) * C + (int64_t)slab * 64 + gg * CPT);
+      const uint32_t off = it < Cfg::kItems ? offset(h0 + s / Cfg::kSC - 1, w0 + s % Cfg::kSC - 1, gg) : kOutside;
+      if constexpr (CPT == 8) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0);
+        pre[j] = V{v[0], v[1], v[2], v[3]};
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(xr, (int)off, 0, 0);
+        pre[j] = V{v[0], v[1]};
+      }
     }
   };
   auto commit = [&](int slot) {
 #pragma unroll
     for (int j = 0; j < NIT; ++j) {
       const int it = tid + j * Cfg::kThreads;
-      if (it < Cfg::kItems) tile[slot][it / Cfg::kGroups][it % Cfg::kGroups] = pre[j];
+      tile[it < Cfg::kItems ? slot * Cfg::kSlots * Cfg::kGroups + it : NF * Cfg::kSlots * Cfg::kGroups + tid] = pre[j];
     }
   };
 
-  if (NF == 3) {
-    for (int ff = max(0, f_begin - 2); ff < f_begin; ++ff) {
-      fetch(ff);
-      commit(ff % 3);
-    }
-  }
-  if (f_begin < f_end) fetch(f_begin);
-  for (int f = f_begin; f < f_end; ++f) {
+  // One step: stage frame f (loaded during the previous step), start loading the
+  // next frame, compute the output tile of frame f.
+  auto step = [&](int f) {
     lds_barrier();                                    // previous frame's reads are done
     commit(NF == 3 ? f % 3 : 0);
     lds_barrier();
@@ -197,7 +211,7 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
 #pragma unroll
         for (int kw = 0; kw < 3; ++kw) {
           float v[CPT];
-          unpack(tile[slot][ir * Cfg::kSC + col + kw][g], v);
+          unpack(tile[(slot * Cfg::kSlots + ir * Cfg::kSC + col + kw) * Cfg::kGroups + g], v);
 #pragma unroll
           for (int kh = 0; kh < 3; ++kh) {
             const int orow = ir - kh;
@@ -208,16 +222,35 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
         }
       }
     }
-    const int64_t ww = w0 + col;
+    const auto yr = __builtin_amdgcn_make_buffer_rsrc((void*)(yb + (int64_t)f * seg.height * seg.width * C), 0,
+                                                      frame_bytes, kRsrcWord3);
 #pragma unroll
     for (int rr = 0; rr < TR; ++rr) {
-      const int64_t hh = h0 + rr;
-      if (hh < seg.height && ww < seg.width) {
-        V out;
-        pack(out, acc[rr]);
-        *reinterpret_cast<V*>(yb + raster_index(seg, f, hh, ww) * C + c0) = out;
+      V out;
+      pack(out, acc[rr]);
+      const uint32_t off = offset(h0 + rr, w0 + col, g);
+      if constexpr (CPT == 8) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, out), yr, (int)off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, out), yr, (int)off, 0, 0);
       }
     }
+  };
+
+  if (NF == 3) {
+    for (int ff = max(0, f_begin - 2); ff < f_begin; ++ff) {
+      fetch(ff);
+      commit(ff % 3);
+    }
+  }
+  if (f_begin < f_end) {
+    fetch(f_begin);
+    // the first step runs outside the loop, so that every step in it starts with the
+    // same outstanding accesses (staged loads, then stores) and waits for loads only
+    step(f_begin);
+    for (int f = f_begin + 1; f < f_end; ++f) step(f);
   }
 }
 
@@ -231,8 +264,6 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
 // 32-bit offsets: taps outside the grid get an offset past the buffer's end and
 // read zero, output positions outside it are dropped the same way, so there is
 // no branch around a memory access and every wait counts only what it needs.
-constexpr uint32_t kOutside = 0x80000000u;   // past every buffer: the launcher keeps them under 2 GiB
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 data format
 template <int TR, int TW>
 __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                          const float* __restrict__ w_vis, int64_t Ttot, int64_t C,
@@ -427,6 +458,18 @@ __global__ void index_device_kernel(Seg seg, int32_t* __restrict__ idx) {
       }
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
 template <int NF, int CPT, int TR, int TW>
 hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
                        const Seg& seg, hipStream_t stream, Marks* marks) {
@@ -438,7 +481,7 @@ hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64
   int fpb = seg.frames;
   if (NF == 3) {
     const int64_t per_frame_range = (int64_t)n_slab * n_tw * n_th * B;
-    const int64_t want = 2048;
+    const int64_t want = 12 * (int64_t)device_cus();   // about six rounds of resident blocks
     int64_t nfr = (want + per_frame_range - 1) / per_frame_range;
     if (nfr > seg.frames) nfr = seg.frames;
     if (nfr < 1) nfr = 1;
@@ -454,18 +497,6 @@ hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64
                      w_vis, Ttot, C, seg, n_slab, n_tw, n_th, n_fr, fpb, (int)n_logical);
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : mark_after(marks, "conv_tile_kernel", stream);
-}
-
-// Compute units of the current device (cached per device; 256 on MI355X).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
-  }
-  return cus[dev];
 }
 
 // Byte span of one rows-kernel buffer: (rows_per_range + 2) grid rows; kept
@@ -517,7 +548,8 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     uint16_t* ys = static_cast<uint16_t*>(y);
     if (seg.frames == 1 && rows_fit<4, 32>(seg, C)) return launch_rows<4, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
-    return launch_tile<3, 4, 8, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
+    if ((int64_t)seg.height * seg.width * C * 2 <= (int64_t)kOutside - 64)
+      return launch_tile<3, 4, 4, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
   }
   if (B > 65535) return hipErrorInvalidValue;
   if (seg.kind == SEG_TEXT) {
