@@ -17,6 +17,8 @@ HIP event on the launch stream around every kernel; the per-kernel averages
 give the roofline line of the kernel that takes the most time per step.
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+[--workload NAME]; the other four synthetic workloads (tiny_text_fp32,
+image_1024, video_5s, video_30s) are measured the same way with --workload.
 
 Two helper modes turn rocprofv3 output into the summaries kept with the code:
   python bench.py --summarize-stats <kernel_stats.csv>
@@ -75,8 +77,10 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="for counter runs: one 1 GiB device copy (the scale reference), then one step, then exit")
-    ap.add_argument("--cpu-sample-rows", type=int, default=80,
-                    help="image rows in the oracle's timed sample (plus the 256 text tokens)")
+    ap.add_argument("--workload", default="image_4096",
+                    help="synthetic workload (name or index); the metric is quoted on image_4096")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=20736,
+                    help="tokens per sequence in the oracle's timed sample (text + whole grid rows/frames)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="markdown HBM traffic table from FETCH_SIZE and WRITE_SIZE counter_collection.csv files")
@@ -102,22 +106,23 @@ def kda_split(B: int, T: int, H: int, target_blocks: int = 512, sub: int = 2):
 
 
 def kernel_work(name: str, w) -> dict:
-    """Algorithmic bytes (HBM-bound kernels) of one launch on the bench workload, with the recipe."""
+    """Algorithmic bytes (HBM-bound kernels) of one launch on a workload, with the recipe."""
     B, T, H, d, C = w.B, w.T, w.H, w.d, w.C
     text = sum(s.length for s in w.segments if s.kind == 0)
     vis = T - text
-    e = 2                                                         # bf16
+    e = 2 if w.dtype == "bf16" else 4
+    state = B * H * d * d * 4 * (2 if w.s0_std is not None else 1)     # S_final (+ S0)
     if name in ("conv_rows_kernel", "conv_tile_kernel"):
         return {"bytes": 2 * B * vis * C * e,
-                "recipe": f"read + write every q|k|v channel of the {vis} visual tokens once: 2 x {C} x 2 B/token"}
-    if name == "conv_text_kernel":
-        return {"bytes": 2 * B * text * C * e,
-                "recipe": f"read + write every channel of the {text} text tokens once"}
-    if name == "kda_out_kernel":
+                "recipe": f"read + write every q|k|v channel of the {vis} visual tokens once: 2 x {C} x {e} B/token"}
+    if name in ("conv_text_kernel", "conv_gather_kernel"):
+        n = text if name == "conv_text_kernel" else vis
+        return {"bytes": 2 * B * n * C * e, "recipe": f"read + write every channel of the {n} tokens once"}
+    if name in ("kda_out_kernel", "kda_seq_kernel"):
         per = 4 * d * e + e + d * e                               # q, k, v, alpha in; beta in; o out
-        return {"bytes": B * T * H * per + B * H * d * d * 4,
-                "recipe": f"q, k, v, alpha ({4 * d * e} B) + beta (2 B) in, o ({d * e} B) out per token-head, "
-                          f"+ S_final (fp32 d x d per head)"}
+        return {"bytes": B * T * H * per + state,
+                "recipe": f"q, k, v, alpha ({4 * d * e} B) + beta ({e} B) in, o ({d * e} B) out per token-head, "
+                          f"+ the fp32 d x d states per head"}
     if name == "kda_sum_kernel":
         nc, c_stop = kda_split(B, T, H)
         toks = min(T, c_stop * 64)
@@ -194,27 +199,50 @@ def summarize_pmc(fetch_csv: str, write_csv: str):
 
 # ----------------------------------------------------------------------------------------------------------
 
-def _cpu_baseline(inp, w, rows: int):
-    """The oracle as it stands, on the first 256 + rows*256 tokens of the workload, one host core."""
-    from threadpoolctl import threadpool_limits
+def _sample_segments(w, budget: int):
+    """The first tokens of the workload's layout: the text, then whole grid rows (image) or frames
+    (video) up to about `budget` tokens per sequence."""
     import workloads as wl
+    out, n = [], 0
+    for sg in w.segments:
+        if sg.kind == wl.TEXT:
+            take = min(sg.length, max(budget - n, 0))
+            if take > 0:
+                out.append(wl.Segment(wl.TEXT, n, take))
+                n += take
+            continue
+        unit = sg.width if sg.frames == 1 else sg.height * sg.width
+        k = max(1, min(sg.height if sg.frames == 1 else sg.frames, (budget - n) // unit))
+        if sg.frames == 1:
+            out.append(wl.Segment(sg.kind, n, k * unit, 1, k, sg.width))
+        else:
+            out.append(wl.Segment(sg.kind, n, k * unit, k, sg.height, sg.width))
+        n += k * unit
+        break
+    return tuple(out), n
+
+
+def _cpu_baseline(inp, w, budget: int):
+    """The oracle as it stands, on the first tokens of the workload, one host core."""
+    from threadpoolctl import threadpool_limits
     from oracle import conv_ref, kda_ref, l2norm_ref, round_bf16_ref
 
-    img = w.segments[1]
-    n_text = w.segments[0].length
-    n = n_text + rows * img.width
-    segs = (wl.Segment(wl.TEXT, 0, n_text), wl.Segment(wl.IMAGE, n_text, rows * img.width, 1, rows, img.width))
+    segs, n = _sample_segments(w, budget)
     x = inp["x"][:, :n]
+    S0 = inp["S0"]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        y = round_bf16_ref(conv_ref(x, inp["w_text"], inp["w_vis"], segs))
+        y = conv_ref(x, inp["w_text"], inp["w_vis"], segs)
+        if w.dtype == "bf16":
+            y = round_bf16_ref(y)
         parts = y.reshape(w.B, n, 3, w.H, w.d)
         kda_ref(l2norm_ref(parts[:, :, 0]), l2norm_ref(parts[:, :, 1]), parts[:, :, 2],
-                inp["alpha"][:, :n], inp["beta"][:, :n], None)
+                inp["alpha"][:, :n], inp["beta"][:, :n], S0)
         dt = time.perf_counter() - t0
+    desc = " + ".join(f"{sg.length} {'text' if sg.kind == 0 else 'grid'}" for sg in segs)
     return {"value": n * w.B / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} tokens of the workload (256 text + {rows} image rows x {img.width}), "
-                      f"all {w.H} heads, conv + L2 norm + token-by-token KDA in fp64 numpy; {dt:.1f} s on "
+            "sample": f"first {n} tokens of each of the {w.B} sequence(s) ({desc}), all {w.H} heads, conv + L2 norm "
+                      f"+ token-by-token KDA in fp64 numpy; {dt:.1f} s on "
                       f"{platform.processor() or platform.machine()}, BLAS limited to 1 thread"}
 
 
@@ -235,28 +263,31 @@ def main():
     import linear_attention_recurrence_mshortconv_amd as chm
 
     chm.lib()
-    w = wl.WORKLOADS[WORKLOAD_INDEX]
+    by_name = {w.name: w for w in wl.WORKLOADS}
+    w = by_name[args.workload] if args.workload in by_name else wl.WORKLOADS[int(args.workload)]
     B, T, H, d = w.B, w.T, w.H, w.d
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = wl.make_inputs(w)
-    to_dev = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    to_dev = lambda a: torch.from_numpy(a).to(tdt).to(dev)
     x = to_dev(inp["x"])
     alpha = to_dev(inp["alpha"])
     beta = to_dev(inp["beta"])
+    S0 = None if inp["S0"] is None else torch.from_numpy(inp["S0"]).to(dev)
     wt = torch.from_numpy(inp["w_text"]).to(dev)
     wv = torch.from_numpy(inp["w_vis"]).to(dev)
     segs = w.segments
     y = torch.empty_like(x)
     q, k, v = chm.split_qkv(y, H, d)
-    o = torch.empty(B, T, H, d, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(B, T, H, d, dtype=tdt, device=dev)
     s_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
-    need = chm.kda_workspace_size(B, T, H, d, d, chm.BF16, chm.KDA_L2NORM_QK)
+    need = chm.kda_workspace_size(B, T, H, d, d, chm.BF16 if w.dtype == "bf16" else chm.F32, chm.KDA_L2NORM_QK)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def step(mc=None, mk=None):
         chm.mshortconv_fwd(x, wt, wv, segs, out=y, marks=mc)
-        chm.kda_fwd(q, k, v, alpha, beta, None, workspace=ws, out=o, marks=mk, state_out=s_final)
+        chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, marks=mk, state_out=s_final)
 
     if args.profile_once:
         ref_src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device=dev)   # 1 GiB
@@ -305,14 +336,17 @@ def main():
     work = kernel_work(dom, w)
     ms_dom = kernels[dom]["ms_per_launch"]
     achieved = work["bytes"] / (ms_dom * 1e-3) / 1e9 if work["bytes"] else None
-    traffic = stored_traffic(dom)
+    traffic = stored_traffic(dom) if w.name == wl.WORKLOADS[WORKLOAD_INDEX].name else None
     conv_ms = sum(kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
                   if n.startswith("conv_"))
     kda_ms = sum(kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
                  if n.startswith("kda_"))
-    conv_bytes = 2 * B * T * w.C * 2
-    kda_bytes = B * T * H * (4 * d * 2 + 2 + d * 2) + B * H * d * d * 4
+    e = 2 if w.dtype == "bf16" else 4
+    conv_bytes = 2 * B * T * w.C * e
+    kda_bytes = B * T * H * (4 * d * e + e + d * e) + B * H * d * d * 4 * (2 if S0 is not None else 1)
     tokens = B * T
+    layout = " + ".join(("text" if sg.kind == 0 else f"{sg.frames}x{sg.height}x{sg.width} grid") + f" ({sg.length})"
+                        for sg in segs)
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -324,11 +358,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; bf16 q|k|v, alpha, beta; fp32 conv weights; fp32 state)",
-        "config": {"workload": f"{w.name}: 256 text tokens + 256x256 image grid = {T} tokens, B={B}, H={H}, "
-                               f"d_k=d_v={d}, chunk 64, conv 4-tap text / 3x3 image, q/k L2-normalised, "
-                               f"o and S_final written",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": f"synthetic (seeded; {w.dtype} q|k|v, alpha, beta; fp32 conv weights; fp32 state)",
+        "config": {"workload": f"{w.name}: {layout} = {T} tokens per sequence, B={B}, H={H}, d_k=d_v={d}, "
+                               f"chunk 64, conv 4-tap text / 3x3 image / 3x3x3 video, q/k L2-normalised, "
+                               f"o and S_final written" + (", S0 given" if S0 is not None else ""),
                    "tokens_per_step": tokens,
                    "ms_per_step_without_marks": ms_step_unmarked,
                    "kernels": kernels,
@@ -344,7 +378,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_sample_rows)
+        out["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_sample_tokens // max(B, 1))
     print(json.dumps(out), flush=True)
 
 
