@@ -816,6 +816,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       // wave 1: Aqk00 A10 Aqk10 A20 Aqk20 A30;  wave 2: Aqk11 A21 Aqk21 A31 Aqk31;
       // wave 3: Aqk22 A32 Aqk32 Aqk33 Aqk30
       if (wave == 0) {
+        __builtin_amdgcn_s_setprio(3);   // the chunk's critical path
 #pragma unroll
         for (int I = 0; I < NSB; ++I) {
           tile_frags(L.kc, I, cA, l16, q4);
@@ -823,6 +824,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
           epi_a(L, I, I, mma4(rA, cA), l16, q4);
         }
         invert_diag4(L, lane_c);
+        __builtin_amdgcn_s_setprio(0);
       } else if (wave == 1) {
         tile_frags(L.kc, 0, cA, l16, q4);
         tile_frags<RMS>(L.qw, 0, rA, l16, q4); epi_q(L, 0, 0, mma4(rA, cA), l16, q4);
@@ -1157,8 +1159,10 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
         const int I = wave - 4;
         tile_frags(L.kc, I, cA, l16, q4);
         tile_frags(L.kr, I, rA, l16, q4);
+        __builtin_amdgcn_s_setprio(3);
         epi_a(L, I, I, mma4(rA, cA), l16, q4);
         invert_diag(L, I, l16, q4 == 0);
+        __builtin_amdgcn_s_setprio(0);
       } else {
         auto below = [&](int I, int J) {
           tile_frags(L.kc, J, cA, l16, q4);
