@@ -7,9 +7,11 @@
 // (page 1, section 5.6: FP32 KDA state).
 //
 // One block per (batch, head, 16-column slice of d_v); 256 threads = 16 columns
-// x 16 row-threads. A row-thread holds rows rt, rt+16, ... of its column in
-// registers; the two reductions over d_k per token are 16-lane shuffles. Tokens
-// are staged in LDS 16 at a time.
+// x 16 row-threads. A row-thread holds rows rt, rt+16, ... (RPT of them) of its
+// column in registers; the 16 row-threads of a column are one DPP row, so the two
+// reductions over d_k per token are four DPP adds each. Tokens are staged in LDS
+// 16 at a time, double-buffered: the next batch's loads are in flight while the
+// current batch runs.
 #include "dtypes.h"
 #include "internal.h"
 
@@ -17,20 +19,35 @@ namespace chm {
 namespace {
 
 constexpr int kTokBatch = 16;
-constexpr int kMaxRowsPerThread = 16;   // dk <= 256
 
-template <typename T>
+// x moved from the lane given by the DPP control CTRL (all rows and banks)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of a DPP row, in every lane: xor 1, xor 2 (quad
+// permutes), then the half-row and row mirrors
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+
+template <typename T, int RPT>
 __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                       const T* __restrict__ v, int64_t stride,
                                                       const T* __restrict__ alpha, const T* __restrict__ beta,
                                                       const float* __restrict__ S0, T* __restrict__ o,
                                                       float* __restrict__ S_final, int64_t Tn, int64_t H, int dk,
                                                       int dv, int l2norm) {
-  __shared__ float sk[kTokBatch][256];
-  __shared__ float sq[kTokBatch][256];
-  __shared__ float sa[kTokBatch][256];
-  __shared__ float sv[kTokBatch][16];
-  __shared__ float sb[kTokBatch];
+  constexpr int DKP = 16 * RPT;   // staged rows; rows past dk hold k = q = 0, alpha = 1
+  __shared__ float sk[2][kTokBatch][DKP];
+  __shared__ float sq[2][kTokBatch][DKP];
+  __shared__ float sa[2][kTokBatch][DKP];
+  __shared__ float sv[2][kTokBatch][16];
+  __shared__ float sb[2][kTokBatch];
 
   const int n_vs = (dv + 15) / 16;
   const int64_t bh = blockIdx.x / n_vs;
@@ -41,87 +58,122 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
   const int col = vs * 16 + colid;
   const bool col_ok = col < dv;
 
-  float s[kMaxRowsPerThread];
+  float s[RPT];
 #pragma unroll
-  for (int i = 0; i < kMaxRowsPerThread; ++i) {
+  for (int i = 0; i < RPT; ++i) {
     const int row = rt + 16 * i;
     s[i] = (S0 != nullptr && col_ok && row < dk) ? S0[(bh * dk + row) * dv + col] : 0.f;
   }
 
+  // one batch of tokens: thread (colid, rt) loads token colid, rows rt + 16 i
+  float rk[RPT], rq[RPT], ra[RPT], rv, rb;
+  auto load = [&](int64_t t0) {
+    const int nt = (int)min<int64_t>(kTokBatch, Tn - t0);
+    const bool tok_ok = colid < nt;
+    const int64_t tok = b * Tn + t0 + colid;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rt + 16 * i;
+      const bool ok = tok_ok && row < dk;
+      rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
+      rq[i] = ok ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
+      ra[i] = ok ? to_f32(alpha[(tok * H + h) * dk + row]) : 1.f;
+    }
+    // v: token colid, column vs * 16 + rt; beta: token colid
+    const int vc = vs * 16 + rt;
+    rv = (tok_ok && vc < dv) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
+    rb = tok_ok ? to_f32(beta[tok * H + h]) : 0.f;
+  };
+  // store a loaded batch to buffer `buf` and normalise its q and k rows
+  auto stage = [&](int buf) {
+    if (l2norm) {
+      float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        ssk = fmaf(rk[i], rk[i], ssk);
+        ssq = fmaf(rq[i], rq[i], ssq);
+      }
+      const float nk = 1.f / sqrtf(sum16(ssk) + 1e-6f), nq = 1.f / sqrtf(sum16(ssq) + 1e-6f);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        rk[i] *= nk;
+        rq[i] *= nq;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      sk[buf][colid][rt + 16 * i] = rk[i];
+      sq[buf][colid][rt + 16 * i] = rq[i];
+      sa[buf][colid][rt + 16 * i] = ra[i];
+    }
+    sv[buf][colid][rt] = rv;
+    if (rt == 0) sb[buf][colid] = rb;
+  };
+
+  if (Tn > 0) {
+    load(0);
+    stage(0);
+  }
+  __syncthreads();
+  int buf = 0;
   for (int64_t t0 = 0; t0 < Tn; t0 += kTokBatch) {
     const int nt = (int)min<int64_t>(kTokBatch, Tn - t0);
-    __syncthreads();
-    for (int e = tid; e < kTokBatch * 256; e += 256) {
-      const int tt = e / 256, i = e % 256;
-      float kv = 0.f, qv = 0.f, av = 1.f;
-      if (tt < nt && i < dk) {
-        const int64_t tok = b * Tn + t0 + tt;
-        kv = to_f32(k[tok * stride + h * dk + i]);
-        qv = to_f32(q[tok * stride + h * dk + i]);
-        av = to_f32(alpha[(tok * H + h) * dk + i]);
-      }
-      sk[tt][i] = kv; sq[tt][i] = qv; sa[tt][i] = av;
-    }
-    for (int e = tid; e < kTokBatch * 16; e += 256) {
-      const int tt = e / 16, c = vs * 16 + e % 16;
-      const int64_t tok = b * Tn + t0 + tt;
-      sv[tt][e % 16] = (tt < nt && c < dv) ? to_f32(v[tok * stride + h * dv + c]) : 0.f;
-    }
-    for (int e = tid; e < kTokBatch; e += 256) {
-      const int64_t tok = b * Tn + t0 + e;
-      sb[e] = e < nt ? to_f32(beta[tok * H + h]) : 0.f;
-    }
-    __syncthreads();
-    if (l2norm) {
-      // one wave per 4 tokens: x / sqrt(sum x^2 + 1e-6) over d_k, for q and k
-      const int wave = tid >> 6, lane = tid & 63;
-      for (int tt = wave; tt < nt; tt += 4) {
-        float ssk = 0.f, ssq = 0.f;
-        for (int i = lane; i < dk; i += 64) { ssk += sk[tt][i] * sk[tt][i]; ssq += sq[tt][i] * sq[tt][i]; }
-        for (int off = 32; off > 0; off >>= 1) { ssk += __shfl_xor(ssk, off); ssq += __shfl_xor(ssq, off); }
-        const float rk = 1.f / sqrtf(ssk + 1e-6f), rq = 1.f / sqrtf(ssq + 1e-6f);
-        for (int i = lane; i < dk; i += 64) { sk[tt][i] *= rk; sq[tt][i] *= rq; }
-      }
-      __syncthreads();
-    }
+    const bool more = t0 + kTokBatch < Tn;
+    if (more) load(t0 + kTokBatch);                  // in flight during this batch
     for (int tt = 0; tt < nt; ++tt) {
       float pred = 0.f;
 #pragma unroll
-      for (int i = 0; i < kMaxRowsPerThread; ++i) {
+      for (int i = 0; i < RPT; ++i) {
         const int row = rt + 16 * i;
-        if (row < dk) {
-          s[i] *= sa[tt][row];
-          pred = fmaf(s[i], sk[tt][row], pred);
-        }
+        s[i] *= sa[buf][tt][row];
+        pred = fmaf(s[i], sk[buf][tt][row], pred);
       }
-      pred += __shfl_xor(pred, 1, 16);
-      pred += __shfl_xor(pred, 2, 16);
-      pred += __shfl_xor(pred, 4, 16);
-      pred += __shfl_xor(pred, 8, 16);
-      const float u = sb[tt] * (sv[tt][colid] - pred);
+      pred = sum16(pred);
+      const float u = sb[buf][tt] * (sv[buf][tt][colid] - pred);
       float out = 0.f;
 #pragma unroll
-      for (int i = 0; i < kMaxRowsPerThread; ++i) {
+      for (int i = 0; i < RPT; ++i) {
         const int row = rt + 16 * i;
-        if (row < dk) {
-          s[i] = fmaf(sk[tt][row], u, s[i]);
-          out = fmaf(s[i], sq[tt][row], out);
-        }
+        s[i] = fmaf(sk[buf][tt][row], u, s[i]);
+        out = fmaf(s[i], sq[buf][tt][row], out);
       }
-      out += __shfl_xor(out, 1, 16);
-      out += __shfl_xor(out, 2, 16);
-      out += __shfl_xor(out, 4, 16);
-      out += __shfl_xor(out, 8, 16);
+      out = sum16(out);
       if (rt == 0 && col_ok) from_f32(o + ((b * Tn + t0 + tt) * H + h) * dv + col, out);
     }
+    if (more) stage(buf ^ 1);                        // the other buffer was last read a batch ago
+    __syncthreads();
+    buf ^= 1;
   }
   if (S_final != nullptr && col_ok) {
 #pragma unroll
-    for (int i = 0; i < kMaxRowsPerThread; ++i) {
+    for (int i = 0; i < RPT; ++i) {
       const int row = rt + 16 * i;
       if (row < dk) S_final[(bh * dk + row) * dv + col] = s[i];
     }
   }
+}
+
+template <typename T>
+hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream) {
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const T* al = static_cast<const T*>(a.alpha);
+  const T* be = static_cast<const T*>(a.beta);
+  T* o = static_cast<T*>(a.o);
+  const dim3 g((unsigned)blocks), t(256);
+  const int dk = (int)a.dk, dv = (int)a.dv, nrm = (int)a.l2norm;
+  if (dk <= 16)
+    hipLaunchKernelGGL((kda_seq_kernel<T, 1>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+  else if (dk <= 32)
+    hipLaunchKernelGGL((kda_seq_kernel<T, 2>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+  else if (dk <= 64)
+    hipLaunchKernelGGL((kda_seq_kernel<T, 4>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+  else if (dk <= 128)
+    hipLaunchKernelGGL((kda_seq_kernel<T, 8>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+  else
+    hipLaunchKernelGGL((kda_seq_kernel<T, 16>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -132,19 +184,7 @@ hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* ma
   const int64_t blocks = a.B * a.H * n_vs;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (a.T == 0 && a.S_final == nullptr) return hipSuccess;
-  if (a.bf16) {
-    hipLaunchKernelGGL(kda_seq_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.qkv_stride, static_cast<const uint16_t*>(a.alpha),
-                       static_cast<const uint16_t*>(a.beta), a.S0, static_cast<uint16_t*>(a.o), a.S_final, a.T, a.H,
-                       (int)a.dk, (int)a.dv, (int)a.l2norm);
-  } else {
-    hipLaunchKernelGGL(kda_seq_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-                       a.qkv_stride, static_cast<const float*>(a.alpha), static_cast<const float*>(a.beta), a.S0,
-                       static_cast<float*>(a.o), a.S_final, a.T, a.H, (int)a.dk, (int)a.dv, (int)a.l2norm);
-  }
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = a.bf16 ? launch_seq<uint16_t>(a, blocks, stream) : launch_seq<float>(a, blocks, stream);
   return e != hipSuccess ? e : mark_after(marks, "kda_seq_kernel", stream);
 }
 
