@@ -1278,7 +1278,10 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
   };
 #pragma unroll
   for (int j = 0; j < kAhead; ++j) fetch(j, mq[j], sq[j]);
-  for (int step = 0; step < nsteps; ++step) {
+  // one step of the chain with the operands in slot j; the slot is refilled for the step
+  // kAhead later. The loop is unrolled by kAhead so that the slots stay in place: moving a
+  // register that a load still targets would wait for that load.
+  auto chain_step = [&](int step, int j) {
     const int buf = step & 1;
     {   // base rows row0 .. row0 + 3 of column l16 -> LDS, transposed, split
       uint2 lo;
@@ -1294,23 +1297,22 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
       bH[s] = *reinterpret_cast<const uint4*>(&bhi[buf][l16 * BTS + 32 * s + 8 * q4]);
       bL[s] = *reinterpret_cast<const uint4*>(&blo[buf][l16 * BTS + 32 * s + 8 * q4]);
     }
-    f32x4 acc0 = sq[0], acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0 = sq[j], acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint4 ah = mq[0][2 * s], al = mq[0][2 * s + 1];
+      const uint4 ah = mq[j][2 * s], al = mq[j][2 * s + 1];
       acc1 = mma32(al, bH[s], acc1);
       acc2 = mma32(ah, bL[s], acc2);
       acc0 = mma32(ah, bH[s], acc0);
     }
     cur = acc0 + (acc1 + acc2);
     store(kSub * (step + 1), cur);
+    fetch(step + kAhead, mq[j], sq[j]);
+  };
+  for (int step = 0; step < nsteps; step += kAhead) {
 #pragma unroll
-    for (int j = 0; j + 1 < kAhead; ++j) {
-      sq[j] = sq[j + 1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mq[j][i] = mq[j + 1][i];
-    }
-    fetch(step + kAhead, mq[kAhead - 1], sq[kAhead - 1]);
+    for (int j = 0; j < kAhead; ++j)
+      if (step + j < nsteps) chain_step(step + j, j);
   }
 }
 
