@@ -101,3 +101,34 @@ def test_conv_full_workload_sampled_channels(chm, wi):
     err = np.abs(got - ref)
     assert (err <= bound).all(), f"worst excess {np.max(err - bound):.3e}"
     assert_close(got, ref, "bf16", w.name)
+
+
+@pytest.mark.parametrize("height,kernel", [(2, "conv_tile_kernel"), (4, "conv_gather_kernel")])
+def test_conv_wide_grid_fallbacks(chm, height, kernel):
+    """A 4096-wide image with 65,536 channels. The rows kernel's buffers (six staged
+    rows) would pass 2 GiB, so at height 2 the frame-tile kernel runs; at height 4 a
+    whole frame passes 2 GiB as well and the gather kernel runs. Sampled channels
+    (every token) against the oracle."""
+    import torch
+    W, C = 4096, 65536
+    segs = (wl.Segment(wl.IMAGE, 0, height * W, 1, height, W),)
+    T = height * W
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11 + height)
+    x = torch.randn(1, T, C, device="cuda", generator=g).to(torch.bfloat16)
+    rng = np.random.default_rng(height)
+    wt = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    wv = (0.5 * rng.standard_normal((C, 27))).astype(np.float32)
+    marks = chm.Marks(2)
+    y = chm.mshortconv_fwd(x, torch.from_numpy(wt), torch.from_numpy(wv), segs, marks=marks)
+    torch.cuda.synchronize()
+    assert [n for n, _ in marks.kernels()] == [kernel]
+    sub = np.unique(np.concatenate([np.arange(0, C, C // 16) + np.arange(16) * 37, [C - 1]]))
+    idx = torch.from_numpy(sub).to("cuda")
+    got = to_host(y[:, :, idx])
+    xs = to_host(x[:, :, idx])
+    del x, y
+    ref, bound = _conv_bound(xs, wt[sub], wv[sub], segs, "bf16")
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), f"worst excess {np.max(err - bound):.3e}"
+    assert_close(got, ref, "bf16", f"wide grid h={height}")
