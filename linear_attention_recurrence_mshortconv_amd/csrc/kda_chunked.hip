@@ -14,8 +14,9 @@
 //
 // so with T = (I + A)^{-1}, W = T diag(b) K e^g and U~ = T diag(b) V, the chunk
 // step is U = U~ - W S. Decays are running products of alpha (no log / exp).
-// The per-(token, head) L2 normalisation of q and k (page 1, Fig. 2) enters as
-// row / column scalings of A, Aqk, W, U and O rather than through the operands.
+// The per-(token, head) L2 normalisation of q and k (page 1, Fig. 2) is folded
+// into the bf16 operands as they are formed (K^, K_ and Q^ carry 1 / |k| and
+// 1 / |q|), so no product needs a separate norm scaling.
 //
 // Work layout. A block of 4 waves runs one segment of chunks of one (batch,
 // head); wave w owns state columns 32w..32w+31 in registers, and under 80 KB of
@@ -267,35 +268,30 @@ __device__ __forceinline__ f32x4 mma4(const uint4 (&ra)[4], const uint4 (&cb)[4]
   for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
   return acc;
 }
-// A(I, J) = diag(b / |k|) (K^ K_^T)(I, J) diag(1 / |k|): below the diagonal -> at (negated,
-// column-major: a lane's four rows are one 8-byte write), on it (strictly lower part) ->
-// adiag in fp32
+// A(I, J) = diag(b) (K^ K_^T)(I, J) (the operands carry 1 / |k|): below the diagonal -> at
+// (negated, column-major: a lane's four rows are one 8-byte write), on it (strictly lower
+// part) -> adiag in fp32
 __device__ __forceinline__ void epi_a(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
   const int j = SBT * J + l16;
-  const float rkj = L.rk[j];
-  const float4 b4 = ldf4(&L.beta[SBT * I + 4 * q4]), k4 = ldf4(&L.rk[SBT * I + 4 * q4]);
-  const float rowf[4] = {b4.x * k4.x, b4.y * k4.y, b4.z * k4.z, b4.w * k4.w};
+  const float4 b4 = ldf4(&L.beta[SBT * I + 4 * q4]);
+  const float rowf[4] = {b4.x, b4.y, b4.z, b4.w};
   if (I == J) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) L.adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? rowf[r] * rkj * acc[r] : 0.f;
+    for (int r = 0; r < 4; ++r) L.adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? rowf[r] * acc[r] : 0.f;
   } else {
-    const float nk = -rkj;
     *reinterpret_cast<uint2*>(&L.at[tr(j, SBT * I + 4 * q4)]) = pack4(
-        make_float4(rowf[0] * nk * acc[0], rowf[1] * nk * acc[1], rowf[2] * nk * acc[2], rowf[3] * nk * acc[3]));
+        make_float4(-rowf[0] * acc[0], -rowf[1] * acc[1], -rowf[2] * acc[2], -rowf[3] * acc[3]));
   }
 }
-// Aqk(I, J) = diag(1 / |q|) (Q^ K_^T)(I, J) diag(1 / |k|), lower triangle including the
-// diagonal, column-major
+// Aqk(I, J) = (Q^ K_^T)(I, J) (the operands carry 1 / |q| and 1 / |k|), lower triangle
+// including the diagonal, column-major
 __device__ __forceinline__ void epi_q(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
   const int j = SBT * J + l16;
-  const float rkj = L.rk[j];
-  const float4 rq4 = ldf4(&L.rq[SBT * I + 4 * q4]);
-  const float rowf[4] = {rq4.x, rq4.y, rq4.z, rq4.w};
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool keep = I > J || 4 * q4 + r >= l16;
-    v[r] = keep ? rowf[r] * rkj * acc[r] : 0.f;
+    v[r] = keep ? acc[r] : 0.f;
   }
   *reinterpret_cast<uint2*>(&L.aqk[tr(j, SBT * I + 4 * q4)]) = pack4(make_float4(v[0], v[1], v[2], v[3]));
 }
@@ -353,7 +349,7 @@ __device__ __forceinline__ void block_solve(const uint2 (&af)[10], const f32x4 (
     Xb[I] = pack4(X[I]);
   }
 }
-// W = (I + A)^{-1} diag(b / |k|) K^ for channels 16 t .. 16 t + 15, negated and written
+// W = (I + A)^{-1} diag(b) K^ (K^ carries 1 / |k|) for channels 16 t .. 16 t + 15, negated and written
 // over the same kr channels (read transposed first; only this wave touches them)
 __device__ __forceinline__ void w_tile(Lds& L, bool fast, int t, const uint2 (&af)[10], int l16, int q4) {
   const int tpos = 32 * (t >> 1) + 4 * (t & 1);      // cpos(16 t)
@@ -364,7 +360,7 @@ __device__ __forceinline__ void w_tile(Lds& L, bool fast, int t, const uint2 (&a
     const float4 kv = unpack4(ld_tr(&L.kr[rk(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
     float sc = 1.f;
     if (!fast) sc = pick(em_of(L, I, 16 * t + (l16 & ~3)), l16 & 3);
-    const float4 kr4 = mul4(ldf4(&L.beta[SBT * I + 4 * q4]), ldf4(&L.rk[SBT * I + 4 * q4]));
+    const float4 kr4 = ldf4(&L.beta[SBT * I + 4 * q4]);
     y[I][0] = kv.x * kr4.x * sc; y[I][1] = kv.y * kr4.y * sc;
     y[I][2] = kv.z * kr4.z * sc; y[I][3] = kv.w * kr4.w * sc;
   }
@@ -429,21 +425,14 @@ __device__ __forceinline__ void minus_ws(const Lds& L, const uint4 (&Sf)[4][2], 
       for (int s = 0; s < 4; ++s) U[I][ct] = mma32(wf[s], Sf[s][ct], U[I][ct]);
   }
 }
-// S <- Diag(e^{g_n}) S + K~^T diag(1/|k|) U, K~ = K e^{g_n - g} read transposed from kc
+// S <- Diag(e^{g_n}) S + K~^T U, K~ = (K / |k|) e^{g_n - g} read transposed from kc
 __device__ __forceinline__ void update_state(const Lds& L, bool fast, f32x4 (&S)[8][2], const f32x4 (&U)[4][2],
                                              int l16, int q4) {
   uint4 Upf[2][2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const float4 ka = ldf4(&L.rk[32 * s + 4 * q4]), kb = ldf4(&L.rk[32 * s + 16 + 4 * q4]);
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      f32x4 lo = U[2 * s][ct], hi = U[2 * s + 1][ct];
-      lo[0] *= ka.x; lo[1] *= ka.y; lo[2] *= ka.z; lo[3] *= ka.w;
-      hi[0] *= kb.x; hi[1] *= kb.y; hi[2] *= kb.z; hi[3] *= kb.w;
-      Upf[s][ct] = pack8(lo, hi);
-    }
-  }
+    for (int ct = 0; ct < 2; ++ct) Upf[s][ct] = pack8(U[2 * s][ct], U[2 * s + 1][ct]);
   // A operand K~^T: lane (l16, q4) = channel 16 rt + l16, tokens 32 s + 4 q4 + 0..3 and
   // 32 s + 16 + 4 q4 + 0..3
   const int kbase = rk(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
@@ -759,11 +748,19 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       // every wave holds all 128 channels, so every wave reaches the same vote
       fast = __all(fminf(fminf(egn4.x, egn4.y), fminf(egn4.z, egn4.w)) >= kFastMin) != 0;
       if (wave == 0 && hf == 0) *reinterpret_cast<float4*>(&L.egn[c0]) = egn4;
+      // 1 / |k| and 1 / |q| of the lane's tokens (from E1) go into the operands, so that
+      // no product downstream needs a norm scaling
+      const float4 rk0 = ldf4(&L.rk[tk0]), rk1 = ldf4(&L.rk[tk0 + 4]);
+      const float4 rq0 = ldf4(&L.rq[tk0]), rq1 = ldf4(&L.rq[tk0 + 4]);
+      const float rkt[8] = {rk0.x, rk0.y, rk0.z, rk0.w, rk1.x, rk1.y, rk1.z, rk1.w};
+      const float rqt[8] = {rq0.x, rq0.y, rq0.z, rq0.w, rq1.x, rq1.y, rq1.z, rq1.w};
       auto put = [&](int i, float4 fr, float4 fc) {
         const int tk = tk0 + i;
-        *reinterpret_cast<uint2*>(&L.kr[rk(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fr));
-        *reinterpret_cast<uint2*>(&L.kc[rk(tk, p0)]) = pack4(mul4(unpack4(kx[i]), fc));
-        *reinterpret_cast<uint2*>(&L.qw[rm(tk, p0)]) = pack4(mul4(unpack4(qx[i]), fr));
+        const float4 ks = mul4(unpack4(kx[i]), make_float4(rkt[i], rkt[i], rkt[i], rkt[i]));
+        const float4 qs = mul4(unpack4(qx[i]), make_float4(rqt[i], rqt[i], rqt[i], rqt[i]));
+        *reinterpret_cast<uint2*>(&L.kr[rk(tk, p0)]) = pack4(mul4(ks, fr));
+        *reinterpret_cast<uint2*>(&L.kc[rk(tk, p0)]) = pack4(mul4(ks, fc));
+        *reinterpret_cast<uint2*>(&L.qw[rm(tk, p0)]) = pack4(mul4(qs, fr));
       };
       if (fast) {
         // e^{g_t} as a prefix product from the chunk start and e^{g_n - g_t} / e^{g_n} as a
@@ -853,7 +850,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
         tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 3, 0, cB, sc, q4);
         epi_q(L, 3, 0, mma4(rA, sc), l16, q4);
       }
-      // O = diag(1/|q|) Q^ S; the blocked factorisation scales Q^'s channels by e^{m_I}
+      // O = Q^ S (Q^ carries 1 / |q|); the blocked factorisation scales Q^'s channels by e^{m_I}
       uint4 Sf[4][2];
       pack_state(S, Sf);
 #pragma unroll
@@ -865,13 +862,11 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
           for (int s = 0; s < 4; ++s)
             qf[s] = scale8(qf[s], em_of(L, I, 32 * s + 4 * q4), em_of(L, I, 32 * s + 16 + 4 * q4));
         }
-        const float4 rq4 = ldf4(&L.rq[SBT * I + 4 * q4]);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) acc = mma32(qf[s], Sf[s][ct], acc);
-          acc[0] *= rq4.x; acc[1] *= rq4.y; acc[2] *= rq4.z; acc[3] *= rq4.w;
           O[I][ct] = acc;
         }
       }
@@ -1076,10 +1071,6 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     lds_barrier();   // B
 
     // ---- E2 / E3: norms, decay factors, MFMA operands ---------------------------------
-    if (wave < 4 && lane_c < SBT) {
-      const int t = SBT * wave + lane_c;
-      L.rk[t] = a.l2norm ? __builtin_amdgcn_rsqf(nk[0][t] + nk[1][t] + kL2Eps) : 1.f;
-    }
     bool fast;
     {
       float2 full[NSB];
@@ -1106,9 +1097,23 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       fast = __all(fminf(fminf(egn2.x, egn2.y), fminf(eo.x, eo.y)) >= kFastMin) != 0;
       if (I == 0 && hf == 0) *reinterpret_cast<float2*>(&L.egn[c0]) = egn2;
+      // 1 / |k| of the lane's tokens from the two channel halves' partial sums (E1),
+      // folded into the operands
+      float rkt[8];
+      if (a.l2norm) {
+        const float4 a0 = ldf4(&nk[0][tk0]), a1 = ldf4(&nk[0][tk0 + 4]);
+        const float4 b0 = ldf4(&nk[1][tk0]), b1 = ldf4(&nk[1][tk0 + 4]);
+        const float ss[8] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w,
+                             a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rkt[i] = __builtin_amdgcn_rsqf(ss[i] + kL2Eps);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rkt[i] = 1.f;
+      }
       auto put = [&](int i, float fr0, float fr1, float fc0, float fc1) {
         const int tk = tk0 + i;
-        const float k0 = bf_lo(kx[i]), k1 = bf_hi(kx[i]);
+        const float k0 = bf_lo(kx[i]) * rkt[i], k1 = bf_hi(kx[i]) * rkt[i];
         *reinterpret_cast<uint32_t*>(&L.kr[rk(tk, p0)]) = pack_bf16x2(k0 * fr0, k1 * fr1);
         *reinterpret_cast<uint32_t*>(&L.kc[rk(tk, p0)]) = pack_bf16x2(k0 * fc0, k1 * fc1);
       };
