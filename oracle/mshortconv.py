@@ -18,7 +18,7 @@ paragraph):
 * Eq. 12: grid point (i, j, k) (time, height, width) sits at raster index
   m = i*H*W + j*W + k inside its segment.
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
 
 * Kernel sizes: 4 taps for text; 3x3x3 for visual grids.
 * Tap j of the text kernel reads offset j - 3 (taps 0..3 read p-3 .. p).
