@@ -169,9 +169,12 @@ size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, i
  *           NULL when that size is 0; contents on entry do not matter
  *
  * Supported: dk, dv in 1..256 for the token-by-token kernel (fp32 and bf16);
- * the chunked MFMA kernel runs for bf16 with dk = dv = 128. alpha <= 0 is
- * undefined. The chunked kernel factors the decay inside 16-token blocks; it
- * stays finite while log(alpha) >= -11 for every token and channel.
+ * the chunked MFMA kernel runs for bf16 with dk = dv = 128. alpha < 0 is
+ * undefined. The chunked kernel factors the decay inside 16-token blocks and
+ * raises alpha below e^-7.5 (5.5e-4) to that value as it loads it, which keeps
+ * every factor within bf16 range and precision: a token with alpha = 0 (complete
+ * forgetting) then keeps 5.5e-4 of each decayed state channel, below bf16
+ * resolution. The token-by-token kernel uses alpha as given.
  * Asynchronous on `stream`; o and S_final must not alias any input.
  */
 chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride,

@@ -55,6 +55,18 @@ constexpr int kTargetBlocks = 512;   // two blocks per CU
 constexpr int kSub = 2;              // output segments per summary segment
 constexpr float kL2Eps = 1e-6f;
 constexpr float kFastMin = 1.8e-35f; // ~e^{-80}: the chunk-start factorisation is safe above this
+// alpha is raised to at least e^{-7.5} (bf16 0x3A11) as it is loaded. The blocked
+// factorisation scales k by products of up to 8 alphas and their reciprocals, so its
+// bf16 operands then stay within e^{+-60} of k: both factors of every product keep full
+// precision (far from the bf16 denormal range), and the reciprocals stay finite. A token
+// with a smaller alpha (alpha = 0 included) then keeps 5.5e-4 of each decayed channel
+// instead of less, which is below the bf16 resolution of the result.
+constexpr uint32_t kAlphaMin2 = 0x3A113A11u;
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t clamp_alpha2(uint32_t u) {   // both bf16 halves (positive)
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, u),
+                                                                 __builtin_bit_cast(u16x2_t, kAlphaMin2)));
+}
 
 __device__ __forceinline__ f32x4 mma32(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -569,7 +581,7 @@ __device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t b, int64_t h,
 //    chunk by a block-wide vote;
 //  * blocked: references at token 7 of each 16-token block, with the factors
 //    e^{m_I - m_J}, e^{m_I}, e^{g_n - m_I} applied to fragments as they are
-//    read; valid while log(alpha) >= -11 per token.
+//    read; accurate for every alpha once alpha is raised to e^{-7.5} (kAlphaMin2).
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_out_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   Lds& L = *reinterpret_cast<Lds*>(lds_raw);
@@ -716,7 +728,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     }
     float4 al[8];   // alpha of the lane's tokens
 #pragma unroll
-    for (int i = 0; i < 8; ++i) al[i] = unpack4(ax[i]);
+    for (int i = 0; i < 8; ++i) al[i] = unpack4(make_uint2(clamp_alpha2(ax[i].x), clamp_alpha2(ax[i].y)));
     {
       float4 hp = al[0];
 #pragma unroll
@@ -1061,7 +1073,10 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     float2 al[8];   // alpha of the lane's tokens
 #pragma unroll
-    for (int i = 0; i < 8; ++i) al[i] = make_float2(bf_lo(ax[i]), bf_hi(ax[i]));
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ac = clamp_alpha2(ax[i]);
+      al[i] = make_float2(bf_lo(ac), bf_hi(ac));
+    }
     {
       float2 hp = al[0];
 #pragma unroll

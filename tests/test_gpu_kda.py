@@ -166,6 +166,27 @@ def test_kda_chunked_strong_decay(chm):
     assert_close(to_host(Sf), S_ref, "bf16", "S strong decay")
 
 
+@pytest.mark.parametrize("no_split", [False, True])
+def test_kda_chunked_degenerate_decay(chm, no_split):
+    """Decays far beyond the blocked factorisation's range: log alpha uniform in [-30, 0],
+    a tenth of the entries exactly 0 (complete forgetting), and one chunk with alpha = 1.
+    The chunked kernel raises alpha to e^-10.5 as it loads it; against the exact oracle
+    the result stays finite and within the bf16 tolerances."""
+    rng = np.random.default_rng(31)
+    B, T, H, d = 1, 64 * 9 + 17, 2, 128
+    q, k, v, _, beta, S0 = _small_case(rng, B, T, H, d, s0=True)
+    la = rng.uniform(-30.0, 0.0, (B, T, H, d)).astype(np.float32)
+    alpha = np.exp(la).astype(np.float32)
+    alpha[rng.random((B, T, H, d)) < 0.1] = 0.0
+    alpha[:, 64 * 3:64 * 4] = 1.0
+    alpha = wl.round_to_bf16(alpha)
+    o, Sf = _gpu_kda(chm, q, k, v, alpha, beta, S0, no_split=no_split)
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    assert np.isfinite(to_host(o)).all() and np.isfinite(to_host(Sf)).all()
+    assert_close(to_host(o), o_ref, "bf16", "o degenerate decay")
+    assert_close(to_host(Sf), S_ref, "bf16", "S degenerate decay")
+
+
 def test_kda_chunked_split_invariance(chm):
     """Segmenting the sequence (three passes) and not segmenting it agree closely."""
     rng = np.random.default_rng(8)
