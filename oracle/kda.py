@@ -23,12 +23,21 @@ Expanding the product gives the form the loop uses, with no other change:
 ``l2norm_ref`` is the per-(token, head) L2 normalisation that Fig. 2 (page 1)
 draws between mShortConv and the recurrence; its epsilon (1e-6 inside the
 square root) is this build's reading, not the pages'.
+
+``gated_rmsnorm_ref`` is the rest of the KDA output in Eq. 15 (page 1, section
+3.3) short of the output projection W_o: Sigmoid(gate) times RMSNorm(S_t^T q_t),
+where gate is the W_gate projection of the layer input (taken as an input
+here). Eq. 15 does not say over which channels the norm runs, whether it has a
+gain or what its epsilon is; the reading here is the usual one for a
+multi-head output: each head's d_v channels on their own, a gain vector of
+length d_v shared by the heads, epsilon inside the square root.
 """
 from __future__ import annotations
 
 import numpy as np
 
 L2_EPS = 1e-6
+RMS_EPS = 1e-6
 
 
 def l2norm_ref(x: np.ndarray, eps: float = L2_EPS) -> np.ndarray:
@@ -61,3 +70,16 @@ def kda_ref(q, k, v, alpha, beta, S0=None):
         S += kt[:, :, :, None] * u[:, :, None, :]                  # + k_t u^T
         o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])           # S_t^T q_t
     return o, S
+
+
+def gated_rmsnorm_ref(o, gate, weight=None, eps: float = RMS_EPS):
+    """Sigmoid(gate) * RMSNorm(o) per (token, head), in fp64 (Eq. 15 without W_o).
+
+    o, gate: [..., dv]; weight: [dv] or None (ones).
+    RMSNorm(x) = x / sqrt(mean(x^2) + eps) * weight over the last axis.
+    """
+    o = np.asarray(o, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    w = np.ones(o.shape[-1]) if weight is None else np.asarray(weight, dtype=np.float64)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o / rms * w / (1.0 + np.exp(-g))
