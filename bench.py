@@ -17,8 +17,10 @@ HIP event on the launch stream around every kernel; the per-kernel averages
 give the roofline line of the kernel that takes the most time per step.
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-[--workload NAME]; the other four synthetic workloads (tiny_text_fp32,
+[--workload NAME] [--gated]; the other four synthetic workloads (tiny_text_fp32,
 image_1024, video_5s, video_30s) are measured the same way with --workload.
+--gated times the KDA call with the output gate and norm of Eq. 15
+(chimera_kda_fwd_gated: Sigmoid(gate) * RMSNorm(o), a synthetic gate input).
 
 Two helper modes turn rocprofv3 output into the summaries kept with the code:
   python bench.py --summarize-stats <kernel_stats.csv>
@@ -52,14 +54,17 @@ KERNEL_SOURCE = {
     "conv_text_kernel": "mshortconv.hip", "conv_gather_kernel": "mshortconv.hip",
     "kda_sum_kernel": "kda_chunked.hip", "kda_combine_kernel": "kda_chunked.hip",
     "kda_out_kernel": "kda_chunked.hip", "kda_seq_kernel": "kda_sequential.hip",
+    "kda_out_gated_kernel": "kda_chunked.hip", "kda_gate_norm_kernel": "kda_sequential.hip",
 }
 
 
 def short_name(full: str) -> str:
     """'void chm::(anonymous namespace)::conv_rows_kernel<4, 32>(...)' -> 'conv_rows_kernel'."""
     s = full.replace("(anonymous namespace)::", "")
+    gated = "kda_out_kernel<true>" in s
     s = s.split("(")[0].split("<")[0].strip()
-    return s.split("::")[-1].split(" ")[-1]
+    s = s.split("::")[-1].split(" ")[-1]
+    return "kda_out_gated_kernel" if gated else s
 
 
 def source_hash(kernel: str) -> str:
@@ -79,6 +84,8 @@ def _args():
                     help="for counter runs: one 1 GiB device copy (the scale reference), then one step, then exit")
     ap.add_argument("--workload", default="image_4096",
                     help="synthetic workload (name or index); the metric is quoted on image_4096")
+    ap.add_argument("--gated", action="store_true",
+                    help="KDA with the output gate and norm of Eq. 15 (Sigmoid(gate) * RMSNorm(o))")
     ap.add_argument("--cpu-sample-tokens", type=int, default=20736,
                     help="tokens per sequence in the oracle's timed sample (text + whole grid rows/frames)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
@@ -118,11 +125,14 @@ def kernel_work(name: str, w) -> dict:
     if name in ("conv_text_kernel", "conv_gather_kernel"):
         n = text if name == "conv_text_kernel" else vis
         return {"bytes": 2 * B * n * C * e, "recipe": f"read + write every channel of the {n} tokens once"}
-    if name in ("kda_out_kernel", "kda_seq_kernel"):
+    if name in ("kda_out_kernel", "kda_seq_kernel", "kda_out_gated_kernel"):
         per = 4 * d * e + e + d * e                               # q, k, v, alpha in; beta in; o out
-        return {"bytes": B * T * H * per + state,
-                "recipe": f"q, k, v, alpha ({4 * d * e} B) + beta ({e} B) in, o ({d * e} B) out per token-head, "
-                          f"+ the fp32 d x d states per head"}
+        gate = d * e if name == "kda_out_gated_kernel" else 0     # + the gate in
+        return {"bytes": B * T * H * (per + gate) + state,
+                "recipe": f"q, k, v, alpha ({4 * d * e} B) + beta ({e} B)" + (f" + gate ({gate} B)" if gate else "")
+                          + f" in, o ({d * e} B) out per token-head, + the fp32 d x d states per head"}
+    if name == "kda_gate_norm_kernel":
+        return {"bytes": 3 * B * T * H * d * e, "recipe": f"o and the gate in, o out: {3 * d * e} B per token-head"}
     if name == "kda_sum_kernel":
         nc, c_stop = kda_split(B, T, H)
         toks = min(T, c_stop * 64)
@@ -222,10 +232,10 @@ def _sample_segments(w, budget: int):
     return tuple(out), n
 
 
-def _cpu_baseline(inp, w, budget: int):
+def _cpu_baseline(inp, w, budget: int, gate=None):
     """The oracle as it stands, on the first tokens of the workload, one host core."""
     from threadpoolctl import threadpool_limits
-    from oracle import conv_ref, kda_ref, l2norm_ref, round_bf16_ref
+    from oracle import conv_ref, gated_rmsnorm_ref, kda_ref, l2norm_ref, round_bf16_ref
 
     segs, n = _sample_segments(w, budget)
     x = inp["x"][:, :n]
@@ -236,13 +246,16 @@ def _cpu_baseline(inp, w, budget: int):
         if w.dtype == "bf16":
             y = round_bf16_ref(y)
         parts = y.reshape(w.B, n, 3, w.H, w.d)
-        kda_ref(l2norm_ref(parts[:, :, 0]), l2norm_ref(parts[:, :, 1]), parts[:, :, 2],
-                inp["alpha"][:, :n], inp["beta"][:, :n], S0)
+        o_ref, _ = kda_ref(l2norm_ref(parts[:, :, 0]), l2norm_ref(parts[:, :, 1]), parts[:, :, 2],
+                           inp["alpha"][:, :n], inp["beta"][:, :n], S0)
+        if gate is not None:
+            gated_rmsnorm_ref(o_ref, gate[0][:, :n], gate[1], 1e-6)
         dt = time.perf_counter() - t0
     desc = " + ".join(f"{sg.length} {'text' if sg.kind == 0 else 'grid'}" for sg in segs)
     return {"value": n * w.B / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} tokens of each of the {w.B} sequence(s) ({desc}), all {w.H} heads, conv + L2 norm "
-                      f"+ token-by-token KDA in fp64 numpy; {dt:.1f} s on "
+                      f"+ token-by-token KDA" + (" + gate and norm" if gate is not None else "") +
+                      f" in fp64 numpy; {dt:.1f} s on "
                       f"{platform.processor() or platform.machine()}, BLAS limited to 1 thread"}
 
 
@@ -284,10 +297,14 @@ def main():
     s_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
     need = chm.kda_workspace_size(B, T, H, d, d, chm.BF16 if w.dtype == "bf16" else chm.F32, chm.KDA_L2NORM_QK)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    gate_np = wl.make_gate(w) if args.gated else None
+    gkw = {}
+    if args.gated:
+        gkw = dict(gate=to_dev(gate_np[0]), norm_weight=torch.from_numpy(gate_np[1]).to(dev), norm_eps=1e-6)
 
     def step(mc=None, mk=None):
         chm.mshortconv_fwd(x, wt, wv, segs, out=y, marks=mc)
-        chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, marks=mk, state_out=s_final)
+        chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, marks=mk, state_out=s_final, **gkw)
 
     if args.profile_once:
         ref_src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device=dev)   # 1 GiB
@@ -302,7 +319,7 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    marks = [(chm.Marks(len(segs) + 1), chm.Marks(4)) for _ in range(args.steps)]
+    marks = [(chm.Marks(len(segs) + 1), chm.Marks(5 if args.gated else 4)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -343,7 +360,8 @@ def main():
                  if n.startswith("kda_"))
     e = 2 if w.dtype == "bf16" else 4
     conv_bytes = 2 * B * T * w.C * e
-    kda_bytes = B * T * H * (4 * d * e + e + d * e) + B * H * d * d * 4 * (2 if S0 is not None else 1)
+    kda_bytes = B * T * H * (4 * d * e + e + d * e + (d * e if args.gated else 0)) \
+        + B * H * d * d * 4 * (2 if S0 is not None else 1)
     tokens = B * T
     layout = " + ".join(("text" if sg.kind == 0 else f"{sg.frames}x{sg.height}x{sg.width} grid") + f" ({sg.length})"
                         for sg in segs)
@@ -362,7 +380,8 @@ def main():
         "data": f"synthetic (seeded; {w.dtype} q|k|v, alpha, beta; fp32 conv weights; fp32 state)",
         "config": {"workload": f"{w.name}: {layout} = {T} tokens per sequence, B={B}, H={H}, d_k=d_v={d}, "
                                f"chunk 64, conv 4-tap text / 3x3 image / 3x3x3 video, q/k L2-normalised, "
-                               f"o and S_final written" + (", S0 given" if S0 is not None else ""),
+                               f"o and S_final written" + (", S0 given" if S0 is not None else "")
+                               + (", output gate and per-head RMSNorm of Eq. 15 fused" if args.gated else ""),
                    "tokens_per_step": tokens,
                    "ms_per_step_without_marks": ms_step_unmarked,
                    "kernels": kernels,
@@ -378,7 +397,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_sample_tokens // max(B, 1))
+        out["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_sample_tokens // max(B, 1), gate_np)
     print(json.dumps(out), flush=True)
 
 

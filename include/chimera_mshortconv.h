@@ -9,6 +9,7 @@
  *   (Q, K, V) = mShortConv(W_qkv x)                                   Eq. 13
  *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T   Eq. 14
  *   o_t = S_t^T q_t                       (inner term of Eq. 15)
+ *   y_t = Sigmoid(g_t) * RMSNorm(o_t)     (Eq. 15 short of the output projection)
  *
  * over one packed token stream: text tokens first, then visual tokens in
  * time-first raster order (Eq. 12). This library computes the mShortConv and
@@ -215,6 +216,50 @@ chimera_status chimera_kda_fwd_timed(const void* q, const void* k, const void* v
                                      int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
                                      uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream,
                                      hipEvent_t* marks, const char** names, int32_t capacity, int32_t* used);
+
+/*
+ * chimera_kda_fwd_gated -- chimera_kda_fwd followed by the output gate and norm of
+ * Eq. 15 (Chimera page 1, section 3.3) short of the output projection W_o:
+ *
+ *   y_t = Sigmoid(gate_t) * RMSNorm(S_t^T q_t),
+ *   RMSNorm(x)_c = x_c / sqrt(mean over the head's dv channels of x^2 + norm_eps) * w_c
+ *
+ * per (token, head). gate_t is the layer's W_gate projection, given as an input
+ * (the projection itself is not part of this library). Eq. 15 does not fix the norm's
+ * extent, gain or epsilon: here it runs over each head's dv channels on their own,
+ * with one gain vector shared by the heads and epsilon inside the square root.
+ *
+ *   gate         device [B][T][H][dv], dtype dt, consecutive tokens gate_stride
+ *                elements apart (gate_stride >= H*dv; a view into a wider
+ *                projection output is accepted)
+ *   norm_weight  device fp32 [dv], or NULL for a gain of 1
+ *   norm_eps     >= 0 and finite, else CHIMERA_ERR_SHAPE
+ *   o            receives y, dtype dt
+ *
+ * All other arguments, the workspace (chimera_kda_workspace_size with the same
+ * flags), S_final and the errors are those of chimera_kda_fwd; a NULL gate with
+ * T > 0 is CHIMERA_ERR_NULL. The chunked kernel applies the gate and norm to its fp32
+ * output before the one rounding to dt when gate is 16-byte aligned and gate_stride
+ * is a multiple of 8; otherwise, and on the token-by-token kernel, a separate pass
+ * applies them to o in place after the recurrence (o is then rounded to dt twice).
+ */
+chimera_status chimera_kda_fwd_gated(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                     const void* alpha, const void* beta, const float* S0, const void* gate,
+                                     int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                     float* S_final, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                     chimera_dtype dt, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* Timing variant of chimera_kda_fwd_gated, as the ones above; capacity at least
+ * CHIMERA_KDA_GATED_MAX_KERNELS + 1. */
+#define CHIMERA_KDA_GATED_MAX_KERNELS 4
+chimera_status chimera_kda_fwd_gated_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                           const void* alpha, const void* beta, const float* S0, const void* gate,
+                                           int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                           float* S_final, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                           chimera_dtype dt, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream, hipEvent_t* marks, const char** names,
+                                           int32_t capacity, int32_t* used);
 
 /* Static, NUL-terminated description of a status code. */
 const char* chimera_status_string(chimera_status s);

@@ -70,6 +70,11 @@ def lib() -> ctypes.CDLL:
                                                                                      ctypes.POINTER(i32)]
     L.chimera_kda_fwd_timed.restype = ctypes.c_int
     L.chimera_kda_fwd_timed.argtypes = L.chimera_kda_fwd.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
+    L.chimera_kda_fwd_gated.restype = ctypes.c_int
+    L.chimera_kda_fwd_gated.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, vp, ctypes.c_float, vp, vp,
+                                        i64, i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.chimera_kda_fwd_gated_timed.restype = ctypes.c_int
+    L.chimera_kda_fwd_gated_timed.argtypes = L.chimera_kda_fwd_gated.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
     _lib = L
     return L
 
@@ -195,13 +200,18 @@ def _token_view_stride(t, B, T, H, d) -> int:
 
 def kda_fwd(q, k, v, alpha, beta, S0=None, *, l2norm: bool = True, sequential: bool = False,
             no_split: bool = False, out=None, want_state: bool = True, workspace=None,
-            marks: Optional[Marks] = None, state_out=None):
+            marks: Optional[Marks] = None, state_out=None, gate=None, norm_weight=None,
+            norm_eps: float = 1e-6):
     """KDA forward on the GPU (chimera_kda_fwd; chimera_kda_fwd_timed with `marks`).
 
     q, k [B, T, H, dk], v [B, T, H, dv] with a shared token stride (views into a
     fused q|k|v tensor are accepted), alpha [B, T, H, dk], beta [B, T, H], S0
     fp32 [B, H, dk, dv] or None. Returns (o [B, T, H, dv], S_final or None);
     `out` and `state_out` are written in place when given.
+
+    With `gate` ([B, T, H, dv] in the same dtype, any token stride) the output is
+    Sigmoid(gate) * RMSNorm(o) per (token, head), with gain `norm_weight` (fp32
+    [dv] or None) and `norm_eps` (chimera_kda_fwd_gated / _gated_timed).
     """
     import torch
     B, T, H, dk = k.shape
@@ -225,8 +235,22 @@ def kda_fwd(q, k, v, alpha, beta, S0=None, *, l2norm: bool = True, sequential: b
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = (_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(Sf),
-            B, T, H, dk, dv, dt, flags, _ptr(workspace), wbytes, _stream(k))
+    tail = (B, T, H, dk, dv, dt, flags, _ptr(workspace), wbytes, _stream(k))
+    if gate is not None:
+        assert gate.dtype == k.dtype and gate.is_cuda
+        gstride = _token_view_stride(gate, B, T, H, dv)
+        if norm_weight is not None:
+            assert norm_weight.dtype == torch.float32 and norm_weight.is_contiguous() and norm_weight.shape == (dv,)
+        args = (_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(gate), gstride,
+                _ptr(norm_weight), float(norm_eps), _ptr(o), _ptr(Sf)) + tail
+        if marks is None:
+            _check("chimera_kda_fwd_gated", lib().chimera_kda_fwd_gated(*args))
+        else:
+            _check("chimera_kda_fwd_gated_timed",
+                   lib().chimera_kda_fwd_gated_timed(*args, marks.handles, marks.names, marks.capacity,
+                                                     ctypes.byref(marks.used)))
+        return o, Sf
+    args = (_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(Sf)) + tail
     if marks is None:
         _check("chimera_kda_fwd", lib().chimera_kda_fwd(*args))
     else:

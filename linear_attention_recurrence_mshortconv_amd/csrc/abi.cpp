@@ -173,10 +173,19 @@ size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, i
   return chm::kda_chunked_workspace(B, T, H, (flags & CHIMERA_KDA_NO_SPLIT) != 0);
 }
 
+// Output gate and norm of Eq. 15 (absent when gate == null and gated == false).
+struct GateArgs {
+  bool gated;
+  const void* gate;
+  int64_t gate_stride;
+  const float* norm_w;
+  float norm_eps;
+};
+
 static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
                               const void* beta, const float* S0, void* o, float* S_final, int64_t B, int64_t T,
                               int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream, chm::Marks* marks) {
+                              size_t workspace_bytes, hipStream_t stream, chm::Marks* marks, const GateArgs& g) {
   if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
   if (!kda_sizes_ok(B, T, H, dk, dv)) return CHIMERA_ERR_SHAPE;
   if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL | CHIMERA_KDA_NO_SPLIT)) return CHIMERA_ERR_UNSUPPORTED;
@@ -185,13 +194,24 @@ static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64
     if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || o == nullptr)
       return CHIMERA_ERR_NULL;
     if (qkv_stride < H * dk || qkv_stride < H * dv) return CHIMERA_ERR_SHAPE;
+    if (g.gated) {
+      if (g.gate == nullptr) return CHIMERA_ERR_NULL;
+      if (g.gate_stride < H * dv || g.gate_stride > (int64_t(1) << 40)) return CHIMERA_ERR_SHAPE;
+    }
   }
+  if (g.gated && !(g.norm_eps >= 0.f && g.norm_eps < 3.0e38f)) return CHIMERA_ERR_SHAPE;   // NaN fails too
   chm::KdaArgs a;
   a.q = q; a.k = k; a.v = v; a.qkv_stride = qkv_stride; a.alpha = alpha; a.beta = beta;
   a.S0 = S0; a.o = o; a.S_final = S_final;
   a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
   a.bf16 = dt == CHIMERA_BF16;
   a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
+  if (g.gated && T > 0) {
+    a.gate = g.gate;
+    a.gate_stride = g.gate_stride;
+    a.norm_w = g.norm_w;
+    a.norm_eps = g.norm_eps;
+  }
   const bool chunked = !(flags & CHIMERA_KDA_SEQUENTIAL) && chm::kda_chunked_supported(a) && T > 0;
   const bool no_split = (flags & CHIMERA_KDA_NO_SPLIT) != 0;
   if (chunked) {
@@ -208,7 +228,7 @@ chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int6
                                int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
   return kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags, workspace,
-                 workspace_bytes, stream, nullptr);
+                 workspace_bytes, stream, nullptr, GateArgs{false, nullptr, 0, nullptr, 0.f});
 }
 
 chimera_status chimera_kda_fwd_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
@@ -221,7 +241,35 @@ chimera_status chimera_kda_fwd_timed(const void* q, const void* k, const void* v
   if (capacity < CHIMERA_KDA_MAX_KERNELS + 1) return CHIMERA_ERR_SHAPE;
   chm::Marks m{marks, names, capacity, 0};
   const chimera_status st = kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags,
-                                    workspace, workspace_bytes, stream, &m);
+                                    workspace, workspace_bytes, stream, &m, GateArgs{false, nullptr, 0, nullptr, 0.f});
+  *used = m.n;
+  return st;
+}
+
+chimera_status chimera_kda_fwd_gated(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                     const void* alpha, const void* beta, const float* S0, const void* gate,
+                                     int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                     float* S_final, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                     chimera_dtype dt, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  return kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags, workspace,
+                 workspace_bytes, stream, nullptr, GateArgs{true, gate, gate_stride, norm_weight, norm_eps});
+}
+
+chimera_status chimera_kda_fwd_gated_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                           const void* alpha, const void* beta, const float* S0, const void* gate,
+                                           int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                           float* S_final, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                           chimera_dtype dt, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream, hipEvent_t* marks, const char** names,
+                                           int32_t capacity, int32_t* used) {
+  if (marks == nullptr || names == nullptr || used == nullptr) return CHIMERA_ERR_NULL;
+  *used = 0;
+  if (capacity < CHIMERA_KDA_GATED_MAX_KERNELS + 1) return CHIMERA_ERR_SHAPE;
+  chm::Marks m{marks, names, capacity, 0};
+  const chimera_status st =
+      kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags, workspace,
+              workspace_bytes, stream, &m, GateArgs{true, gate, gate_stride, norm_weight, norm_eps});
   *used = m.n;
   return st;
 }

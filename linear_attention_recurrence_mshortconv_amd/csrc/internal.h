@@ -53,10 +53,18 @@ struct KdaArgs {
   int64_t B, T, H, dk, dv;
   bool bf16;
   bool l2norm;
+  // Output gate and norm (Eq. 15 short of W_o), applied to o when gate != null:
+  // o <- Sigmoid(gate) * o / sqrt(mean over the head's dv channels of o^2 + norm_eps) * norm_w
+  const void* gate = nullptr;   // [B][T][H][dv], consecutive tokens gate_stride elements apart
+  int64_t gate_stride = 0;
+  const float* norm_w = nullptr;  // [dv] or null (ones)
+  float norm_eps = 0.f;
 };
 
-// Token-by-token fp32 kernel: any dk, dv in 1..256.
+// Token-by-token fp32 kernel: any dk, dv in 1..256 (with a gate: then the gate/norm kernel on o).
 hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr);
+// o <- Sigmoid(gate) * RMSNorm(o) in place, one wave per (token, head): a.o, a.gate, a.norm_w.
+hipError_t launch_kda_gate_norm(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr);
 
 // Chunked MFMA path (bf16, dk = dv = 128).
 bool kda_chunked_supported(const KdaArgs& a);

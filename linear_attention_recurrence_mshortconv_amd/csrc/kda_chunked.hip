@@ -166,6 +166,10 @@ struct ChunkArgs {
   float* WM;              // summary: transitions to those boundaries [BH][E][D][D]
   uint16_t* o;
   float* S_final;
+  const uint16_t* gate;   // output gate [B][T][H][D] (token stride gate_stride), or null
+  int64_t gate_stride;
+  const float* norm_w;    // [D] or null
+  float norm_eps;
   int64_t T;
   int64_t H;
   int64_t c_stop;         // summary: chunks from here on are not needed
@@ -212,6 +216,20 @@ __device__ __forceinline__ float half_sum16(const float (&a)[16], int lane) {
   float b1 = (u1 ? b2[1] : b2[0]) + lane_xor2(u1 ? b2[0] : b2[1]);
   b1 += lane_xor1(b1);
   return b1;
+}
+
+// Sum 16 per-lane values over the 16 lanes of each DPP row by recursive halving; lane
+// l16 of the row returns the row total of value l16.
+__device__ __forceinline__ float row_sum16(const float (&a)[16], int l16) {
+  float b8[8], b4[4], b2[2];
+  const bool u3 = (l16 >> 3) & 1, u2 = (l16 >> 2) & 1, u1 = (l16 >> 1) & 1, u0 = l16 & 1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b8[j] = (u3 ? a[j + 8] : a[j]) + lane_xor8(u3 ? a[j] : a[j + 8]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b4[j] = (u2 ? b8[j + 4] : b8[j]) + lane_xor4(u2 ? b8[j] : b8[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b2[j] = (u1 ? b4[j + 2] : b4[j]) + lane_xor2(u1 ? b4[j] : b4[j + 2]);
+  return (u0 ? b2[1] : b2[0]) + lane_xor1(u0 ? b2[0] : b2[1]);
 }
 
 // third descriptor word of a raw buffer resource on gfx9
@@ -582,6 +600,20 @@ __device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t b, int64_t h,
 //  * blocked: references at token 7 of each 16-token block, with the factors
 //    e^{m_I - m_J}, e^{m_I}, e^{g_n - m_I} applied to fragments as they are
 //    read; accurate for every alpha once alpha is raised to e^{-7.5} (kAlphaMin2).
+//
+// GATED adds the rest of Eq. 15 short of W_o to the output: o <- Sigmoid(gate) *
+// o / sqrt(mean over the head's channels of o^2 + eps) * w. Each wave holds 32 of the
+// 128 channels of the fp32 output; their per-row sums of squares meet in LDS (adiag)
+// behind the chunk's last barrier (F). The output of chunk c is then normalised,
+// staged in fp32 over kr and kc (free until the next chunk's operands are formed,
+// barrier B) and stored with the gate applied, rounded once, while the loads of chunk
+// c + 1 are in flight; the last chunk's after the loop.
+constexpr int kStP = 36;   // fp32 output staging pitch (floats per row)
+static_assert(offsetof(Lds, kc) == offsetof(Lds, kr) + sizeof(Lds::kr) &&
+                  4 * CT * kStP * sizeof(float) <= sizeof(Lds::kr) + sizeof(Lds::kc) &&
+                  4 * CT * sizeof(float) <= sizeof(Lds::adiag),
+              "gated output staging in kr and kc, row partial sums in adiag");
+template <bool GATED>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_out_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   Lds& L = *reinterpret_cast<Lds*>(lds_raw);
@@ -667,6 +699,52 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   }
 
   const uint2 kOnes = make_uint2(0x3F803F80u, 0x3F803F80u);   // alpha = 1 past the end
+  // GATED: the previous chunk's fp32 output (D layout) and its gate (rows 4 (lane >> 2) + j,
+  // channels col0 + 8 (lane & 3) .. + 7), carried into the next chunk step
+  f32x4 Og[4][2];
+  uint4 gx[4];
+  auto gate_epilogue = [&](int64_t cp) {
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int e16 = lane_e & 15, e4 = lane_e >> 4;
+    const int64_t tp = cp * CT;
+    const int np = (int)min<int64_t>(CT, a.T - tp);
+    const int oc = 8 * (lane_e & 3);
+    float4 w0 = make_float4(1.f, 1.f, 1.f, 1.f), w1 = w0;   // gain of the lane's output channels
+    if (a.norm_w != nullptr) {
+      w0 = ldf4(a.norm_w + col0 + oc);
+      w1 = ldf4(a.norm_w + col0 + oc + 4);
+    }
+    float* st = reinterpret_cast<float*>(L.kr) + wave * CT * kStP;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) st[(16 * I + 4 * e4 + r) * kStP + 16 * ct + e16] = Og[I][ct][r];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    // rows -> o, scaled by 1 / rms and the gain, with the gate; 16 bytes per lane; rows
+    // past the end are dropped
+    const int so2 = (int)(a.H * D) * 2;
+    const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((b * a.T + tp) * a.H + h) * D), 0, np * so2,
+                                                      kRsrcW3);
+    auto sig = [](float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * (lane_e >> 2) + j;
+      const float4 p4 = ldf4(&L.adiag[row * 4]);
+      const float rinv = __builtin_amdgcn_rsqf((p4.x + p4.y + p4.z + p4.w) * (1.f / D) + a.norm_eps);
+      const float4 y0 = mul4(ldf4(&st[row * kStP + oc]), w0), y1 = mul4(ldf4(&st[row * kStP + oc + 4]), w1);
+      const float4 g0 = unpack4(make_uint2(gx[j].x, gx[j].y)), g1 = unpack4(make_uint2(gx[j].z, gx[j].w));
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t w4 = {pack_bf16x2(y0.x * rinv * sig(g0.x), y0.y * rinv * sig(g0.y)),
+                          pack_bf16x2(y0.z * rinv * sig(g0.z), y0.w * rinv * sig(g0.w)),
+                          pack_bf16x2(y1.x * rinv * sig(g1.x), y1.y * rinv * sig(g1.y)),
+                          pack_bf16x2(y1.z * rinv * sig(g1.z), y1.w * rinv * sig(g1.w))};
+      __builtin_amdgcn_raw_buffer_store_b128(w4, ro, row * so2 + 2 * (col0 + oc), 0, 0);
+    }
+  };
 
   for (int64_t c = c_begin; c < c_end; ++c) {
     // Lane-derived addresses are recomputed every chunk (cheap) rather than kept live
@@ -706,6 +784,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       }
       bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb_, tid * (int)a.H * 2, 0, 0));
     }
+    if (GATED && c > c_begin) gate_epilogue(c - 1);   // the previous chunk's output, while the loads fly
 
     // ---- E1: norms, block decay products -------------------------------------------
     if (tid < CT) L.beta[tid] = bt;
@@ -932,16 +1011,42 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
         O[3][ct] = mma32(qa[4], Uf[0][ct], O[3][ct]);
         O[3][ct] = mma32(qa[5], Uf[1][ct], O[3][ct]);
       }
-      // output tile -> this wave's channels of qw (natural order; v is consumed)
+      if (!GATED) {
+        // output tile -> this wave's channels of qw (natural order; v is consumed)
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L.qw[rm(SBT * I + 4 * q4 + r, col0 + 16 * ct + l16)] = f2bf(O[I][ct][r]);
+      }
+    }
+    if (GATED) {
+      const int sg2 = (int)a.gate_stride * 2;
+      const auto rg = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.gate + (b * a.T + t0) * a.gate_stride + h * D), 0, n * sg2, kRsrcW3);
+      const int gc = col0 + 8 * (lane_c & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto g4 = __builtin_amdgcn_raw_buffer_load_b128(rg, (4 * (lane_c >> 2) + j) * sg2 + 2 * gc, 0, 0);
+        gx[j] = make_uint4(g4[0], g4[1], g4[2], g4[3]);
+      }
+      // this wave's part of each row's sum of squares: lane l16 of a DPP row ends with row
+      // 16 (l16 >> 2) + 4 q4 + (l16 & 3); adiag is free after the inverses
+      float ss[16];
 #pragma unroll
       for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int r = 0; r < 4; ++r) ss[4 * I + r] = O[I][0][r] * O[I][0][r] + O[I][1][r] * O[I][1][r];
+      const float part = row_sum16(ss, l16);
+      L.adiag[(16 * (l16 >> 2) + 4 * q4 + (l16 & 3)) * 4 + wave] = part;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) L.qw[rm(SBT * I + 4 * q4 + r, col0 + 16 * ct + l16)] = f2bf(O[I][ct][r]);
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) Og[I][ct] = O[I][ct];
     }
     update_state(L, fast, S, Ut, l16, q4);
-    {
+    if (!GATED) {
       // staged output rows -> o, 16 bytes per lane; rows past the end fall outside the
       // buffer bound and are dropped
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
@@ -961,6 +1066,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     }
     lds_barrier();   // F
   }
+  if (GATED && c_end > c_begin) gate_epilogue(c_end - 1);
 
   if (a.S_final != nullptr && p == a.P - 1) store_state(S, a.S_final + bh * D * D, svo);
 }
@@ -1394,6 +1500,15 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   a.E = 0;
   a.o = static_cast<uint16_t*>(x.o);
   a.S_final = x.S_final;
+  // the gate is fused into the output pass when its rows and the gain are read as 16-byte
+  // pieces; otherwise the separate in-place gate/norm pass runs after it
+  const bool gated = x.gate != nullptr;
+  const bool fuse_gate = gated && x.gate_stride % 8 == 0 && (reinterpret_cast<uintptr_t>(x.gate) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(x.norm_w) & 15) == 0 && x.gate_stride <= (int64_t(1) << 24);
+  a.gate = static_cast<const uint16_t*>(x.gate);
+  a.gate_stride = x.gate_stride;
+  a.norm_w = x.norm_w;
+  a.norm_eps = x.norm_eps;
   a.T = x.T;
   a.H = x.H;
   a.l2norm = x.l2norm ? 1 : 0;
@@ -1403,8 +1518,11 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   if (de != hipSuccess) return de;
   static bool attr_done[64] = {};
   if (dev < 0 || dev >= 64 || !attr_done[dev]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_out_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_out_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_out_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_sum_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds_sum);
@@ -1447,9 +1565,14 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   a.c_stop = 0;
   a.nblk = (int)(BH * sp.Po);
   a.grid = round8(a.nblk);
-  hipLaunchKernelGGL(kda_out_kernel, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
-  const hipError_t e = hipGetLastError();
-  return e != hipSuccess ? e : mark_after(marks, "kda_out_kernel", stream);
+  if (fuse_gate)
+    hipLaunchKernelGGL(kda_out_kernel<true>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
+  else
+    hipLaunchKernelGGL(kda_out_kernel<false>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = mark_after(marks, fuse_gate ? "kda_out_gated_kernel" : "kda_out_kernel", stream);
+  if (e == hipSuccess && gated && !fuse_gate) e = launch_kda_gate_norm(x, stream, marks);
+  return e;
 }
 
 }  // namespace chm

@@ -1,4 +1,5 @@
-// Token-by-token KDA forward in fp32 (any dk, dv <= 256; fp32 or bf16 storage).
+// Token-by-token KDA forward in fp32 (any dk, dv <= 256; fp32 or bf16 storage), and the
+// output gate and norm of Eq. 15 as a separate in-place pass over o.
 //
 // Chimera page 1, section 3.3: Eq. 14 with page 2's parenthesisation,
 //   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
@@ -153,6 +154,39 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
   }
 }
 
+// Output gate and norm of Eq. 15 (page 1, section 3.3) short of W_o, in place on o:
+//   o <- Sigmoid(gate) * o / sqrt(mean_c o_c^2 + eps) * w_c   over the dv channels of one head.
+// One wave per (token, head) row; lane l holds channels l, l + 64, ... (dv <= 256).
+template <typename T>
+__global__ __launch_bounds__(256) void kda_gate_norm_kernel(T* __restrict__ o, const T* __restrict__ gate,
+                                                            int64_t gate_stride, const float* __restrict__ w,
+                                                            float eps, int64_t rows, int64_t H, int dv) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = row / H, h = row % H;
+  T* orow = o + row * dv;
+  const T* grow = gate + tok * gate_stride + h * dv;
+  float x[4], ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    x[i] = c < dv ? to_f32(orow[c]) : 0.f;
+    ss = fmaf(x[i], x[i], ss);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  const float r = 1.f / sqrtf(ss / (float)dv + eps);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    if (c < dv) {
+      const float sg = 1.f / (1.f + expf(-to_f32(grow[c])));
+      from_f32(orow + c, x[i] * r * (w != nullptr ? w[c] : 1.f) * sg);
+    }
+  }
+}
+
 template <typename T>
 hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream) {
   const T* q = static_cast<const T*>(a.q);
@@ -178,14 +212,32 @@ hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_kda_gate_norm(const KdaArgs& a, hipStream_t stream, Marks* marks) {
+  const int64_t rows = a.B * a.T * a.H;
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 g((unsigned)blocks), t(256);
+  if (a.bf16)
+    hipLaunchKernelGGL(kda_gate_norm_kernel<uint16_t>, g, t, 0, stream, static_cast<uint16_t*>(a.o),
+                       static_cast<const uint16_t*>(a.gate), a.gate_stride, a.norm_w, a.norm_eps, rows, a.H, (int)a.dv);
+  else
+    hipLaunchKernelGGL(kda_gate_norm_kernel<float>, g, t, 0, stream, static_cast<float*>(a.o),
+                       static_cast<const float*>(a.gate), a.gate_stride, a.norm_w, a.norm_eps, rows, a.H, (int)a.dv);
+  const hipError_t e = hipGetLastError();
+  return e != hipSuccess ? e : mark_after(marks, "kda_gate_norm_kernel", stream);
+}
+
 hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks) {
   if (a.B * a.H == 0) return hipSuccess;
   const int n_vs = (int)((a.dv + 15) / 16);
   const int64_t blocks = a.B * a.H * n_vs;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (a.T == 0 && a.S_final == nullptr) return hipSuccess;
-  const hipError_t e = a.bf16 ? launch_seq<uint16_t>(a, blocks, stream) : launch_seq<float>(a, blocks, stream);
-  return e != hipSuccess ? e : mark_after(marks, "kda_seq_kernel", stream);
+  hipError_t e = a.bf16 ? launch_seq<uint16_t>(a, blocks, stream) : launch_seq<float>(a, blocks, stream);
+  if (e == hipSuccess) e = mark_after(marks, "kda_seq_kernel", stream);
+  if (e == hipSuccess && a.gate != nullptr) e = launch_kda_gate_norm(a, stream, marks);
+  return e;
 }
 
 }  // namespace chm

@@ -140,6 +140,27 @@ def test_kda_argument_errors():
     assert call(B=0) == 0 and call(H=0) == 0                            # nothing to do
 
 
+def test_kda_gated_argument_errors():
+    """chimera_kda_fwd_gated checks its gate arguments before any launch (no kernel runs here)."""
+    L = chm.lib()
+    f = ctypes.c_float
+
+    def call(gate=7, gstride=256, eps=1e-6, T=8, B=1):
+        return L.chimera_kda_fwd_gated(1, 2, 3, 256, 4, 5, None, gate, gstride, None, f(eps), 6, None, B, T, 2, 128,
+                                       128, 1, 1, None, 0, None)
+    assert call(gate=None) == 1                                         # gate required when T > 0
+    assert call(gstride=200) == 2                                       # stride below H*dv
+    assert call(eps=-1.0) == 2 and call(eps=float("nan")) == 2 and call(eps=float("inf")) == 2
+    assert call(B=0) == 0                                               # nothing to do
+    ev = (ctypes.c_void_p * 8)()
+    names = (ctypes.c_char_p * 8)()
+    used = ctypes.c_int32(3)
+    timed = lambda cap: L.chimera_kda_fwd_gated_timed(1, 2, 3, 256, 4, 5, None, 7, 256, None, f(1e-6), 6, None, 1,
+                                                      8, 2, 128, 128, 1, 1, None, 0, None, ev, names, cap,
+                                                      ctypes.byref(used))
+    assert timed(4) == 2 and used.value == 0                            # needs 4 kernels + 1
+
+
 def test_workspace_size_rules():
     n = chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
     assert n >= 0

@@ -173,3 +173,17 @@ def small_layout(kind: str, n_text: int, frames: int = 1, height: int = 1, width
     if kind == "text":
         return (Segment(TEXT, 0, n_text),)
     return text_then_grid(n_text, frames, height, width)
+
+
+def make_gate(w: Workload, T: Optional[int] = None, seed: Optional[int] = None):
+    """Inputs of the output gate and norm (Eq. 15): the gate projection g [B, T, H, d]
+    ~ N(0, 1) and the norm gain [d] ~ 1 + 0.1 N(0, 1) (fp32). Drawn from their own
+    stream (seed + 1000), so the workload's other inputs do not change. The gate is
+    bf16-representable for bf16 workloads."""
+    T = w.T if T is None else T
+    rng = np.random.default_rng((w.index if seed is None else seed) + 1000)
+    gate = _normal(rng, (w.B, T, w.H, w.d))
+    weight = (np.float32(1.0) + np.float32(0.1) * _normal(rng, (w.d,))).astype(np.float32)
+    if w.dtype == "bf16":
+        gate = round_to_bf16(gate)
+    return gate, weight
