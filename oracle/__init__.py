@@ -19,6 +19,8 @@ pages (arXiv 2607.28611):
 * ``kda_ref``         -- the token-by-token gated delta rule, Eq. 14 with the
   parenthesisation of page 2's LaTeX, and the inner readout S_t^T q_t of
   Eq. 15 (page 1, section 3.3).
+* ``kda_varlen_ref``  -- several samples packed in one row, the state restarting at
+  every sample boundary (page 1, section 3.3).
 * ``gated_rmsnorm_ref`` -- Sigmoid(gate) times the per-head RMSNorm of the
   readout, the rest of Eq. 15 before the output projection (page 1, section 3.3).
 * ``round_bf16_ref``  -- rounding to the bf16 output dtype (round to nearest,
@@ -28,10 +30,10 @@ Every function here is pinned by ``-m "not gpu"`` tests against hand-derived
 fixtures, closed forms, library routines or brute force; see ``tests/``.
 """
 from .mshortconv import neighbours_ref, conv_ref, conv_gather_ref, TEXT, IMAGE, VIDEO
-from .kda import l2norm_ref, kda_ref, gated_rmsnorm_ref
+from .kda import l2norm_ref, kda_ref, kda_varlen_ref, gated_rmsnorm_ref
 from .rounding import round_bf16_ref
 
 __all__ = [
-    "neighbours_ref", "conv_ref", "conv_gather_ref", "l2norm_ref", "kda_ref", "gated_rmsnorm_ref",
+    "neighbours_ref", "conv_ref", "conv_gather_ref", "l2norm_ref", "kda_ref", "kda_varlen_ref", "gated_rmsnorm_ref",
     "round_bf16_ref", "TEXT", "IMAGE", "VIDEO",
 ]

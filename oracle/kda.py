@@ -24,6 +24,11 @@ Expanding the product gives the form the loop uses, with no other change:
 draws between mShortConv and the recurrence; its epsilon (1e-6 inside the
 square root) is this build's reading, not the pages'.
 
+``kda_varlen_ref`` runs several samples packed into one token row: the state
+restarts (from that sample's S0, zero by default) at every packed sample
+boundary (page 1, section 3.3), so each sample is the plain recurrence on its
+own tokens.
+
 ``gated_rmsnorm_ref`` is the rest of the KDA output in Eq. 15 (page 1, section
 3.3) short of the output projection W_o: Sigmoid(gate) times RMSNorm(S_t^T q_t),
 where gate is the W_gate projection of the layer input (taken as an input
@@ -83,3 +88,25 @@ def gated_rmsnorm_ref(o, gate, weight=None, eps: float = RMS_EPS):
     w = np.ones(o.shape[-1]) if weight is None else np.asarray(weight, dtype=np.float64)
     rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
     return o / rms * w / (1.0 + np.exp(-g))
+
+
+def kda_varlen_ref(q, k, v, alpha, beta, cu_seqlens, S0=None):
+    """Packed samples: q, k, alpha [T, H, dk]; v [T, H, dv]; beta [T, H]; cu_seqlens the N + 1
+    sample offsets (0 = c_0 <= c_1 <= ... <= c_N = T); S0 [N, H, dk, dv] or None.
+    Sample n is kda_ref on tokens [c_n, c_{n+1}) from S0[n] (zeros if None).
+    Returns (o [T, H, dv], S_final [N, H, dk, dv]) in fp64."""
+    v = np.asarray(v, dtype=np.float64)
+    T, H, dv = v.shape
+    dk = np.shape(k)[-1]
+    cu = [int(c) for c in cu_seqlens]
+    N = len(cu) - 1
+    o = np.empty((T, H, dv))
+    S = np.empty((N, H, dk, dv))
+    for n in range(N):
+        a, b = cu[n], cu[n + 1]
+        s0 = None if S0 is None else np.asarray(S0, dtype=np.float64)[n:n + 1]
+        on, Sn = kda_ref(np.asarray(q)[None, a:b], np.asarray(k)[None, a:b], v[None, a:b],
+                         np.asarray(alpha)[None, a:b], np.asarray(beta)[None, a:b], s0)
+        o[a:b] = on[0]
+        S[n] = Sn[0]
+    return o, S

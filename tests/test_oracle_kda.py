@@ -14,7 +14,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import kda_ref, l2norm_ref
+from oracle import kda_ref, kda_varlen_ref, l2norm_ref
 
 
 def _rand_inputs(rng, B, T, H, dk, dv, s0=True, log_alpha_scale=1.0):
@@ -237,3 +237,38 @@ def test_fixtures_reject_plausible_misreadings(golden_dir, mode):
         if not (np.allclose(o.reshape(T, dv), ex["o"]) and np.allclose(S.reshape(dk, dv), ex["S_final"])):
             caught = True
     assert caught
+
+
+def test_varlen_one_sample_is_the_plain_recurrence():
+    rng = np.random.default_rng(60)
+    q, k, v, alpha, beta, S0 = _rand_inputs(rng, 1, 23, 2, 5, 3)
+    o, S = kda_ref(q, k, v, alpha, beta, S0)
+    o2, S2 = kda_varlen_ref(q[0], k[0], v[0], alpha[0], beta[0], [0, 23], S0)
+    assert np.array_equal(o2, o[0]) and np.array_equal(S2, S)
+
+
+def test_varlen_equal_samples_are_a_batch():
+    rng = np.random.default_rng(61)
+    q, k, v, alpha, beta, S0 = _rand_inputs(rng, 3, 11, 2, 4, 4)
+    o, S = kda_ref(q, k, v, alpha, beta, S0)
+    flat = lambda x: x.reshape((33,) + x.shape[2:])
+    o2, S2 = kda_varlen_ref(flat(q), flat(k), flat(v), flat(alpha), flat(beta), [0, 11, 22, 33], S0)
+    assert np.array_equal(o2, flat(o)) and np.array_equal(S2, S)
+
+
+def test_varlen_state_restarts_at_every_boundary():
+    """A sample's outputs depend on nothing outside it; without the restart (one sample over
+    the whole row) the second sample's outputs change."""
+    rng = np.random.default_rng(62)
+    q, k, v, alpha, beta, _ = _rand_inputs(rng, 1, 30, 2, 4, 3, s0=False)
+    cu = [0, 9, 9, 30]                                          # an empty sample in the middle
+    o, S = kda_varlen_ref(q[0], k[0], v[0], alpha[0], beta[0], cu)
+    v2 = v.copy()
+    v2[0, :9] += 5.0                                            # perturb sample 0 only
+    o2, S2 = kda_varlen_ref(q[0], k[0], v2[0], alpha[0], beta[0], cu)
+    assert np.array_equal(o2[9:], o[9:]) and np.array_equal(S2[1:], S[1:])
+    assert np.array_equal(S[1], np.zeros_like(S[1]))            # the empty sample keeps S0 = 0
+    oa, _ = kda_ref(q[:, 9:], k[:, 9:], v[:, 9:], alpha[:, 9:], beta[:, 9:], None)
+    np.testing.assert_array_equal(o[9:], oa[0])
+    ow, _ = kda_ref(q, k, v, alpha, beta, None)                 # no restart
+    assert not np.allclose(ow[0, 9:], o[9:])
