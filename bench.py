@@ -97,18 +97,13 @@ def _args():
 # ----------------------------------------------------------------------------------------------------------
 # algorithmic work per launch (bytes that the kernel's job must move, or flops it must do)
 
-def kda_split(B: int, T: int, H: int, target_blocks: int = 512, sub: int = 2):
-    """Chunks covered by the summary pass of the chunked KDA: the library splits every sequence into
-    P segments of Lo 64-token chunks (about 512 output blocks over B*H) and summarises all but the last."""
+def kda_split(B: int, T: int, H: int, target_blocks: int = 512):
+    """Chunks covered by the summary pass of the chunked KDA: the library cuts every sequence into
+    segments of Lo 64-token chunks, Lo chosen so that about 512 output blocks cover the B*H
+    sequence-heads, and summarises all segments but the last. Returns (chunks, summarised chunks)."""
     nc = (T + 63) // 64
-    bh = B * H
-    if nc <= 1 or bh >= target_blocks:
-        return nc, 0
-    p = min((target_blocks + bh - 1) // bh, nc)
-    lo = (nc + p - 1) // p
-    p = (nc + lo - 1) // lo
-    if p <= 1:
-        return nc, 0
+    lo = max(1, (B * H * nc + target_blocks - 1) // target_blocks)
+    p = 1 if nc <= 1 else (nc + lo - 1) // lo
     return nc, (p - 1) * lo
 
 

@@ -261,6 +261,48 @@ chimera_status chimera_kda_fwd_gated_timed(const void* q, const void* k, const v
                                            hipStream_t stream, hipEvent_t* marks, const char** names,
                                            int32_t capacity, int32_t* used);
 
+/*
+ * chimera_kda_fwd_varlen -- KDA forward over samples packed in one token row, with the
+ * state restarting at every packed sample boundary (Chimera page 1, section 3.3: S0 = 0
+ * at each sample boundary; section 5.1: mixed-resolution samples of different lengths
+ * packed together), and optionally the output gate and norm of chimera_kda_fwd_gated.
+ *
+ *   q, k, v, alpha, beta, o, gate
+ *               as for chimera_kda_fwd(_gated) with B = 1 and T = cu_seqlens[nseq]
+ *               (row-major [T][H][d], [T][H] for beta; token strides qkv_stride and
+ *               gate_stride)
+ *   cu_seqlens  host int64 [nseq + 1]: sample n is rows cu_seqlens[n] .. cu_seqlens[n+1]-1;
+ *               cu_seqlens[0] = 0 and the offsets never decrease (empty samples are
+ *               allowed: their S_final is their S0), else CHIMERA_ERR_SHAPE
+ *   S0          device fp32 [nseq][H][dk][dv], or NULL for zero initial states
+ *   S_final     device fp32 [nseq][H][dk][dv], written, or NULL
+ *   gate        NULL for the plain readout; otherwise as in chimera_kda_fwd_gated (then
+ *               norm_weight and norm_eps are used, and checked likewise)
+ *   workspace   at least chimera_kda_varlen_workspace_size(...) bytes with the same
+ *               cu_seqlens, sizes, dtype and flags
+ *
+ * A packed row of equal-length samples gives the same result as chimera_kda_fwd with
+ * B = nseq. The chunked kernel launches once for up to 48 stretches of equal-length
+ * consecutive samples; the token-by-token kernel once per such stretch. Errors as for
+ * chimera_kda_fwd; host only until the launches, asynchronous on `stream`.
+ */
+size_t chimera_kda_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
+                                         int64_t dv, chimera_dtype dt, uint32_t flags);
+chimera_status chimera_kda_fwd_varlen(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                      const void* alpha, const void* beta, const float* S0, const void* gate,
+                                      int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                      float* S_final, const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
+                                      int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+/* Timing variant, as the ones above; capacity at least 2 * nseq + 4. */
+chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                            const void* alpha, const void* beta, const float* S0, const void* gate,
+                                            int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                            float* S_final, const int64_t* cu_seqlens, int32_t nseq, int64_t H,
+                                            int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks,
+                                            const char** names, int32_t capacity, int32_t* used);
+
 /* Static, NUL-terminated description of a status code. */
 const char* chimera_status_string(chimera_status s);
 

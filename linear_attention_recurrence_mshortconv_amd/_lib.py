@@ -75,6 +75,13 @@ def lib() -> ctypes.CDLL:
                                         i64, i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
     L.chimera_kda_fwd_gated_timed.restype = ctypes.c_int
     L.chimera_kda_fwd_gated_timed.argtypes = L.chimera_kda_fwd_gated.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
+    L.chimera_kda_varlen_workspace_size.restype = sz
+    L.chimera_kda_varlen_workspace_size.argtypes = [vp, i32, i64, i64, i64, ctypes.c_int, u32]
+    L.chimera_kda_fwd_varlen.restype = ctypes.c_int
+    L.chimera_kda_fwd_varlen.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, vp, ctypes.c_float, vp, vp,
+                                         vp, i32, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.chimera_kda_fwd_varlen_timed.restype = ctypes.c_int
+    L.chimera_kda_fwd_varlen_timed.argtypes = L.chimera_kda_fwd_varlen.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
     _lib = L
     return L
 
@@ -257,6 +264,70 @@ def kda_fwd(q, k, v, alpha, beta, S0=None, *, l2norm: bool = True, sequential: b
         _check("chimera_kda_fwd_timed",
                lib().chimera_kda_fwd_timed(*args, marks.handles, marks.names, marks.capacity,
                                            ctypes.byref(marks.used)))
+    return o, Sf
+
+
+def _cu_array(cu_seqlens) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+
+
+def kda_varlen_workspace_size(cu_seqlens, H, dk, dv, dtype_code: int, flags: int) -> int:
+    cu = _cu_array(cu_seqlens)
+    return int(lib().chimera_kda_varlen_workspace_size(cu.ctypes.data, len(cu) - 1, H, dk, dv, dtype_code, flags))
+
+
+def kda_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, l2norm: bool = True, sequential: bool = False,
+                   no_split: bool = False, out=None, want_state: bool = True, workspace=None,
+                   marks: Optional[Marks] = None, state_out=None, gate=None, norm_weight=None,
+                   norm_eps: float = 1e-6):
+    """KDA forward over samples packed in one row (chimera_kda_fwd_varlen; _timed with `marks`).
+
+    q, k [T, H, dk], v [T, H, dv] (a shared token stride; views into a fused q|k|v
+    tensor are accepted), alpha [T, H, dk], beta [T, H]; `cu_seqlens` the N + 1 sample
+    offsets (host sequence, 0 first, nondecreasing, T last). The state restarts at every
+    sample start, from S0[n] (fp32 [N, H, dk, dv]) or zero. Returns (o [T, H, dv],
+    S_final [N, H, dk, dv] or None). `gate`, `norm_weight`, `norm_eps` as in kda_fwd.
+    """
+    import torch
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    cu = _cu_array(cu_seqlens)
+    N = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T
+    stride = _token_view_stride(q.unsqueeze(0), 1, T, H, dk)
+    assert _token_view_stride(k.unsqueeze(0), 1, T, H, dk) == stride
+    assert _token_view_stride(v.unsqueeze(0), 1, T, H, dv) == stride
+    assert alpha.shape == (T, H, dk) and alpha.is_contiguous() and beta.shape == (T, H) and beta.is_contiguous()
+    dt = _dtype_code(k)
+    assert q.dtype == k.dtype == v.dtype == alpha.dtype == beta.dtype
+    flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0) | (KDA_NO_SPLIT if no_split else 0)
+    o = torch.empty((T, H, dv), dtype=k.dtype, device=k.device) if out is None else out
+    Sf = state_out
+    if Sf is None and want_state:
+        Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=k.device)
+    if Sf is not None:
+        assert Sf.dtype == torch.float32 and Sf.is_contiguous() and Sf.shape == (N, H, dk, dv)
+    if S0 is not None:
+        assert S0.dtype == torch.float32 and S0.is_contiguous() and S0.shape == (N, H, dk, dv)
+    need = kda_varlen_workspace_size(cu, H, dk, dv, dt, flags)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    gstride = 0
+    if gate is not None:
+        assert gate.dtype == k.dtype and gate.is_cuda
+        gstride = _token_view_stride(gate.unsqueeze(0), 1, T, H, dv)
+        if norm_weight is not None:
+            assert norm_weight.dtype == torch.float32 and norm_weight.is_contiguous() and norm_weight.shape == (dv,)
+    args = (_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(gate), gstride,
+            _ptr(norm_weight), float(norm_eps), _ptr(o), _ptr(Sf), cu.ctypes.data, N, H, dk, dv, dt, flags,
+            _ptr(workspace), wbytes, _stream(k))
+    if marks is None:
+        _check("chimera_kda_fwd_varlen", lib().chimera_kda_fwd_varlen(*args))
+    else:
+        _check("chimera_kda_fwd_varlen_timed",
+               lib().chimera_kda_fwd_varlen_timed(*args, marks.handles, marks.names, marks.capacity,
+                                                  ctypes.byref(marks.used)))
     return o, Sf
 
 

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "internal.h"
 
 using chm::Seg;
@@ -164,13 +166,53 @@ static bool kda_sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv
          B <= (int64_t(1) << 20) && H <= (int64_t(1) << 16);
 }
 
+// Packed samples as runs of consecutive samples of equal length (chunked kernels take runs).
+// cu_seqlens must already be checked.
+static std::vector<chm::KdaRun> varlen_runs(const int64_t* cu, int32_t nseq) {
+  std::vector<chm::KdaRun> runs;
+  for (int32_t n = 0; n < nseq; ++n) {
+    const int64_t len = cu[n + 1] - cu[n];
+    if (!runs.empty() && runs.back().len == len) {
+      ++runs.back().count;
+    } else {
+      runs.push_back(chm::KdaRun{cu[n], len, 1, n});
+    }
+  }
+  return runs;
+}
+
+// 0 = c_0 <= c_1 <= ... <= c_nseq, the last at most kMaxTokens
+static chimera_status check_cu(const int64_t* cu, int32_t nseq) {
+  if (nseq < 0) return CHIMERA_ERR_SHAPE;
+  if (cu == nullptr) return CHIMERA_ERR_NULL;
+  if (cu[0] != 0) return CHIMERA_ERR_SHAPE;
+  for (int32_t n = 0; n < nseq; ++n)
+    if (cu[n + 1] < cu[n] || cu[n + 1] > kMaxTokens) return CHIMERA_ERR_SHAPE;
+  return CHIMERA_OK;
+}
+
+static size_t runs_workspace(const std::vector<chm::KdaRun>& runs, int64_t rows, int64_t H, int64_t dk, int64_t dv,
+                             chimera_dtype dt, uint32_t flags) {
+  chm::KdaArgs a{};
+  a.B = 1; a.T = rows; a.H = H; a.dk = dk; a.dv = dv; a.bf16 = dt == CHIMERA_BF16;
+  if ((flags & CHIMERA_KDA_SEQUENTIAL) || !chm::kda_chunked_supported(a) || rows * H == 0) return 0;
+  return chm::kda_chunked_workspace(runs.data(), (int64_t)runs.size(), H, (flags & CHIMERA_KDA_NO_SPLIT) != 0);
+}
+
 size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
                                   uint32_t flags) {
   if (!kda_sizes_ok(B, T, H, dk, dv) || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
-  chm::KdaArgs a{};
-  a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.bf16 = dt == CHIMERA_BF16;
-  if ((flags & CHIMERA_KDA_SEQUENTIAL) || !chm::kda_chunked_supported(a) || B * T * H == 0) return 0;
-  return chm::kda_chunked_workspace(B, T, H, (flags & CHIMERA_KDA_NO_SPLIT) != 0);
+  if (B * T == 0) return 0;
+  const std::vector<chm::KdaRun> runs{chm::KdaRun{0, T, B, 0}};
+  return runs_workspace(runs, B * T, H, dk, dv, dt, flags);
+}
+
+size_t chimera_kda_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
+                                         int64_t dv, chimera_dtype dt, uint32_t flags) {
+  if (check_cu(cu_seqlens, nseq) != CHIMERA_OK || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
+  const int64_t rows = cu_seqlens[nseq];
+  if (!kda_sizes_ok(1, rows, H, dk, dv) || rows == 0) return 0;
+  return runs_workspace(varlen_runs(cu_seqlens, nseq), rows, H, dk, dv, dt, flags);
 }
 
 // Output gate and norm of Eq. 15 (absent when gate == null and gated == false).
@@ -182,14 +224,17 @@ struct GateArgs {
   float norm_eps;
 };
 
+// One KDA call over `runs` (see chm::KdaRun) of a [B][T] = [1][rows] or [B][T] token array;
+// `varlen` calls come with B = 1 and T = rows.
 static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
                               const void* beta, const float* S0, void* o, float* S_final, int64_t B, int64_t T,
                               int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream, chm::Marks* marks, const GateArgs& g) {
+                              size_t workspace_bytes, hipStream_t stream, chm::Marks* marks, const GateArgs& g,
+                              const std::vector<chm::KdaRun>* varlen = nullptr) {
   if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
   if (!kda_sizes_ok(B, T, H, dk, dv)) return CHIMERA_ERR_SHAPE;
   if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL | CHIMERA_KDA_NO_SPLIT)) return CHIMERA_ERR_UNSUPPORTED;
-  if (B == 0 || H == 0) return CHIMERA_OK;
+  if (B == 0 || H == 0 || (varlen != nullptr && varlen->empty())) return CHIMERA_OK;
   if (T > 0) {
     if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || o == nullptr)
       return CHIMERA_ERR_NULL;
@@ -212,15 +257,41 @@ static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64
     a.norm_w = g.norm_w;
     a.norm_eps = g.norm_eps;
   }
-  const bool chunked = !(flags & CHIMERA_KDA_SEQUENTIAL) && chm::kda_chunked_supported(a) && T > 0;
+  const std::vector<chm::KdaRun> uniform{chm::KdaRun{0, T, B, 0}};
+  const std::vector<chm::KdaRun>& runs = varlen != nullptr ? *varlen : uniform;
+  const bool chunked = !(flags & CHIMERA_KDA_SEQUENTIAL) && chm::kda_chunked_supported(a) && B * T > 0;
   const bool no_split = (flags & CHIMERA_KDA_NO_SPLIT) != 0;
   if (chunked) {
-    const size_t need = chm::kda_chunked_workspace(B, T, H, no_split);
+    if (!chm::kda_chunked_plan_ok(runs.data(), (int64_t)runs.size(), H, no_split)) return CHIMERA_ERR_SHAPE;
+    const size_t need = chm::kda_chunked_workspace(runs.data(), (int64_t)runs.size(), H, no_split);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
   }
   if (marks != nullptr && chm::mark_begin(marks, stream) != hipSuccess) return CHIMERA_ERR_HIP;
-  if (!chunked) return hip_status(chm::launch_kda_sequential(a, stream, marks));
-  return hip_status(chm::launch_kda_chunked(a, no_split, workspace, stream, marks));
+  if (chunked) return hip_status(chm::launch_kda_chunked(a, runs.data(), (int64_t)runs.size(), no_split, workspace,
+                                                         stream, marks));
+  if (varlen == nullptr) return hip_status(chm::launch_kda_sequential(a, stream, marks));
+  // token-by-token kernel: one launch per run, on views of the packed tensors
+  const int64_t e = dt == CHIMERA_BF16 ? 2 : 4;
+  for (const chm::KdaRun& r : runs) {
+    chm::KdaArgs s = a;
+    auto at = [&](const void* p, int64_t elems) {
+      return p == nullptr ? nullptr : static_cast<const void*>(static_cast<const char*>(p) + elems * e);
+    };
+    s.q = at(q, r.start * qkv_stride);
+    s.k = at(k, r.start * qkv_stride);
+    s.v = at(v, r.start * qkv_stride);
+    s.alpha = at(alpha, r.start * H * dk);
+    s.beta = at(beta, r.start * H);
+    s.o = const_cast<void*>(at(o, r.start * H * dv));
+    s.gate = a.gate == nullptr ? nullptr : at(a.gate, r.start * a.gate_stride);
+    s.S0 = S0 == nullptr ? nullptr : S0 + r.sidx0 * H * dk * dv;
+    s.S_final = S_final == nullptr ? nullptr : S_final + r.sidx0 * H * dk * dv;
+    s.B = r.count;
+    s.T = r.len;
+    const hipError_t he = chm::launch_kda_sequential(s, stream, marks);
+    if (he != hipSuccess) return CHIMERA_ERR_HIP;
+  }
+  return CHIMERA_OK;
 }
 
 chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
@@ -270,6 +341,48 @@ chimera_status chimera_kda_fwd_gated_timed(const void* q, const void* k, const v
   const chimera_status st =
       kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags, workspace,
               workspace_bytes, stream, &m, GateArgs{true, gate, gate_stride, norm_weight, norm_eps});
+  *used = m.n;
+  return st;
+}
+
+static chimera_status kda_fwd_varlen(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                     const void* alpha, const void* beta, const float* S0, const void* gate,
+                                     int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                     float* S_final, const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
+                                     int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream, chm::Marks* marks) {
+  const chimera_status cs = check_cu(cu_seqlens, nseq);
+  if (cs != CHIMERA_OK) return cs;
+  const std::vector<chm::KdaRun> runs = varlen_runs(cu_seqlens, nseq);
+  const GateArgs g{gate != nullptr, gate, gate_stride, norm_weight, norm_eps};
+  return kda_fwd(q, k, v, qkv_stride, alpha, beta, S0, o, S_final, 1, cu_seqlens[nseq], H, dk, dv, dt, flags,
+                 workspace, workspace_bytes, stream, marks, g, &runs);
+}
+
+chimera_status chimera_kda_fwd_varlen(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                      const void* alpha, const void* beta, const float* S0, const void* gate,
+                                      int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                      float* S_final, const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
+                                      int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return kda_fwd_varlen(q, k, v, qkv_stride, alpha, beta, S0, gate, gate_stride, norm_weight, norm_eps, o, S_final,
+                        cu_seqlens, nseq, H, dk, dv, dt, flags, workspace, workspace_bytes, stream, nullptr);
+}
+
+chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                            const void* alpha, const void* beta, const float* S0, const void* gate,
+                                            int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,
+                                            float* S_final, const int64_t* cu_seqlens, int32_t nseq, int64_t H,
+                                            int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks,
+                                            const char** names, int32_t capacity, int32_t* used) {
+  if (marks == nullptr || names == nullptr || used == nullptr) return CHIMERA_ERR_NULL;
+  *used = 0;
+  if (nseq < 0 || (int64_t)capacity < 2 * (int64_t)nseq + 4) return CHIMERA_ERR_SHAPE;
+  chm::Marks m{marks, names, capacity, 0};
+  const chimera_status st =
+      kda_fwd_varlen(q, k, v, qkv_stride, alpha, beta, S0, gate, gate_stride, norm_weight, norm_eps, o, S_final,
+                     cu_seqlens, nseq, H, dk, dv, dt, flags, workspace, workspace_bytes, stream, &m);
   *used = m.n;
   return st;
 }

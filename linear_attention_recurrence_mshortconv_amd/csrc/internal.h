@@ -66,11 +66,17 @@ hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* ma
 // o <- Sigmoid(gate) * RMSNorm(o) in place, one wave per (token, head): a.o, a.gate, a.norm_w.
 hipError_t launch_kda_gate_norm(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr);
 
-// Chunked MFMA path (bf16, dk = dv = 128).
+// Chunked MFMA path (bf16, dk = dv = 128). The sequences come as runs: `count` consecutive
+// sequences of `len` tokens from row `start` on, whose S0 / S_final entries start at `sidx0`.
+// A batch of B sequences of T tokens is the single run {0, T, B, 0}; samples packed in one
+// row are one run per stretch of equal lengths.
+struct KdaRun {
+  int64_t start, len, count, sidx0;
+};
 bool kda_chunked_supported(const KdaArgs& a);
-int64_t kda_chunked_segments(int64_t B, int64_t T, int64_t H, bool no_split);
-size_t kda_chunked_workspace(int64_t B, int64_t T, int64_t H, bool no_split);
-hipError_t launch_kda_chunked(const KdaArgs& a, bool no_split, void* workspace, hipStream_t stream,
-                              Marks* marks = nullptr);
+bool kda_chunked_plan_ok(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split);   // grid sizes fit
+size_t kda_chunked_workspace(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split);
+hipError_t launch_kda_chunked(const KdaArgs& a, const KdaRun* runs, int64_t nruns, bool no_split, void* workspace,
+                              hipStream_t stream, Marks* marks = nullptr);
 
 }  // namespace chm

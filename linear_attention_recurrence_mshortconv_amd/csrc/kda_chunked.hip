@@ -35,6 +35,8 @@
 //   output pass:  each output segment reruns from S_start(p), writing o.
 // With one output segment only the output pass runs, starting from S0.
 #include <cstddef>
+#include <algorithm>
+#include <vector>
 
 #include "dtypes.h"
 #include "internal.h"
@@ -153,6 +155,24 @@ struct Lds {
 };
 static_assert(sizeof(Lds) <= 81920, "two blocks per CU");
 
+// A run of `count` consecutive sequences of `len` tokens each in the packed row dimension
+// (rows start .. start + count * len - 1): a batch of B sequences is one run, and samples
+// packed in one row with lengths of their own make one run per stretch of equal lengths.
+// Each sequence is cut into P output segments (Ps summary segments) of the launch's Lo
+// chunks; its per-head workspace region holds E = kSub * Ps summary states, E transitions
+// and P start states.
+struct SeqDesc {
+  int64_t start;          // first row of the run
+  int64_t len;            // tokens per sequence
+  int64_t ws0;            // first workspace matrix (D x D fp32) of the run
+  int32_t count;          // sequences
+  int32_t sidx0;          // S0 / S_final index of the run's first sequence
+  int32_t P, Ps;          // output and summary segments per (sequence, head)
+  int32_t out0, sum0, comb0;   // the run's first block in each pass's grid
+  int32_t pad;
+};
+constexpr int kMaxRuns = 48;   // runs per launch (the kernel arguments stay under 4 KiB)
+
 struct ChunkArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -160,27 +180,60 @@ struct ChunkArgs {
   int64_t stride;
   const uint16_t* alpha;
   const uint16_t* beta;
-  const float* S0;        // output pass without split: [BH][D][D] or null
-  const float* Sstart;    // output pass with split: [BH][P][D][D]
-  float* WS;              // summary: S at output-segment boundaries [BH][E][D][D]
-  float* WM;              // summary: transitions to those boundaries [BH][E][D][D]
+  const float* S0;        // [sequences][H][D][D] or null
+  float* ws;              // workspace: D x D fp32 matrices in per-(sequence, head) regions
   uint16_t* o;
   float* S_final;
-  const uint16_t* gate;   // output gate [B][T][H][D] (token stride gate_stride), or null
+  const uint16_t* gate;   // output gate [rows][H][D] (token stride gate_stride), or null
   int64_t gate_stride;
   const float* norm_w;    // [D] or null
   float norm_eps;
-  int64_t T;
   int64_t H;
-  int64_t c_stop;         // summary: chunks from here on are not needed
-  int P;                  // segments per (batch, head)
-  int L;                  // chunks per segment
   int Lo;                 // chunks per output segment
-  int E;                  // entries per (batch, head) in WS / WM
-  int nblk;               // logical blocks
+  int nblk;               // logical blocks of this pass
   int grid;               // launched blocks
   int l2norm;
+  int nruns;
+  SeqDesc run[kMaxRuns];
 };
+
+// The run that logical block `lid` of a pass belongs to: the last run whose first block is
+// at most lid (runs without a block in this pass share the next run's first block).
+template <int PASS>   // 0 output, 1 summary, 2 combine
+__device__ __forceinline__ int run_of(const ChunkArgs& a, uint32_t lid) {
+  int r = 0;
+  for (int i = 1; i < a.nruns; ++i) {
+    const int32_t first = PASS == 0 ? a.run[i].out0 : PASS == 1 ? a.run[i].sum0 : a.run[i].comb0;
+    if ((int64_t)lid >= first) r = i;
+  }
+  return r;
+}
+// One (sequence, head) of a run: its first row, length, S0 / S_final index and workspace
+// region ([E] summary states, [E] transitions, [P] start states, each D x D fp32).
+struct SeqView {
+  int64_t row0, T, sidx;
+  int P, Ps, E;
+  float* ws;
+};
+// (bhl = sequence within the run * H + head; grids stay below 2^31 blocks, so 32-bit
+// index arithmetic is enough up to here). Quotients and remainders of block indices pass
+// through readfirstlane: the division expands into vector instructions, and a buffer
+// descriptor built from a value the compiler cannot see is wave-uniform gets a loop
+// around every load that uses it.
+__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ SeqView seq_view(const ChunkArgs& a, const SeqDesc& d, int32_t bhl) {
+  SeqView v;
+  const int32_t H = (int32_t)a.H;
+  const int32_t seq = uni(bhl / H);
+  v.row0 = d.start + (int64_t)seq * d.len;
+  v.T = d.len;
+  v.sidx = (int64_t)(d.sidx0 + seq) * H + uni(bhl % H);
+  v.P = d.P;
+  v.Ps = d.Ps;
+  v.E = d.Ps * kSub;
+  v.ws = a.ws + (d.ws0 + bhl * (int64_t)(2 * v.E + v.P)) * (int64_t)(D * D);
+  return v;
+}
 
 // Register-level lane exchanges.
 template <int CTRL>
@@ -569,11 +622,10 @@ __device__ __forceinline__ void store_mfrag(const f32x4 (&S)[8][2], uint4* m, in
 
 // v of the state columns col0 .. col0 + 31 of the chunk: lane = tokens 4 (lane >> 2) + j,
 // channels col0 + 8 (lane & 3) .. + 7; tokens past the end read as zero
-__device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t b, int64_t h, int64_t t0, int n, int col0,
-                                       int lane, uint4 (&vx)[4]) {
+__device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t row, int64_t h, int n, int col0, int lane,
+                                       uint4 (&vx)[4]) {
   const int st2 = (int)a.stride * 2;
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (b * a.T + t0) * a.stride + h * D), 0, n * st2,
-                                                    kRsrcW3);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + row * a.stride + h * D), 0, n * st2, kRsrcW3);
   const int vo = (4 * (lane >> 2)) * st2 + 2 * (col0 + 8 * (lane & 3));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -623,27 +675,30 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int64_t bh = lid / a.P;
-  const int p = lid % a.P;
-  const int64_t b = bh / a.H, h = bh % a.H;
-  const int64_t NC = (a.T + CT - 1) / CT;
-  const int64_t c_begin = (int64_t)p * a.L;
-  const int64_t c_end = min<int64_t>(NC, c_begin + a.L);
+  const SeqDesc& rd = a.run[run_of<0>(a, lid)];
+  const int32_t local = (int32_t)lid - rd.out0;
+  const int p = uni(local % rd.P);
+  const int32_t bhl = uni(local / rd.P);
+  const SeqView sv = seq_view(a, rd, bhl);
+  const int64_t h = uni(bhl % (int32_t)a.H);
+  const int64_t NC = (sv.T + CT - 1) / CT;
+  const int64_t c_begin = (int64_t)p * a.Lo;
+  const int64_t c_end = min<int64_t>(NC, c_begin + a.Lo);
 
   // ---- state: rows 16 rt + 4 q4 + r, columns col0 + 16 ct + l16 -----------------
   const int col0 = 32 * wave;
   const int svo = (4 * q4) * D + col0 + l16;   // lane part of a state element's offset
   f32x4 S[8][2];
-  if (a.P > 1) {
+  if (sv.P > 1) {
     if (p % kSub == 0) {   // a chain start (tile-major)
-      const float* src = a.Sstart + (bh * a.P + p) * D * D;
+      const float* src = sv.ws + (2 * sv.E + p) * D * D;
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) S[rt][ct] = load_tile4(src, wave, rt, ct, lane);
     }
   } else {                 // S0 ([D][D] row-major) or zero
-    const float* src = a.S0 ? a.S0 + bh * D * D : nullptr;
+    const float* src = a.S0 ? a.S0 + sv.sidx * D * D : nullptr;
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -651,13 +706,13 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[rt][ct][r] = src ? src[svo + (16 * rt + r) * D + 16 * ct] : 0.f;
   }
-  if (a.P > 1 && p % kSub != 0) {
+  if (sv.P > 1 && p % kSub != 0) {
     // a start inside a summary segment: S_start(p) = M_e S_start(p - p % kSub) + S_e with
     // e = p - 1, in fp32-accurate MFMA (bf16 high and low parts, three products)
     const int e = p - 1;
-    const float* Mp = a.WM + (bh * a.E + e) * D * D;
-    const float* Sp = a.WS + (bh * a.E + e) * D * D;
-    const float* base = a.Sstart + (bh * a.P + (p - p % kSub)) * D * D;
+    const float* Mp = sv.ws + (sv.E + e) * D * D;
+    const float* Sp = sv.ws + e * D * D;
+    const float* base = sv.ws + (2 * sv.E + p - p % kSub) * D * D;
     uint4 bH[4][2], bL[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -708,7 +763,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     asm volatile("" : "+v"(lane_e));
     const int e16 = lane_e & 15, e4 = lane_e >> 4;
     const int64_t tp = cp * CT;
-    const int np = (int)min<int64_t>(CT, a.T - tp);
+    const int np = (int)min<int64_t>(CT, sv.T - tp);
     const int oc = 8 * (lane_e & 3);
     float4 w0 = make_float4(1.f, 1.f, 1.f, 1.f), w1 = w0;   // gain of the lane's output channels
     if (a.norm_w != nullptr) {
@@ -727,7 +782,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     // rows -> o, scaled by 1 / rms and the gain, with the gate; 16 bytes per lane; rows
     // past the end are dropped
     const int so2 = (int)(a.H * D) * 2;
-    const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((b * a.T + tp) * a.H + h) * D), 0, np * so2,
+    const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((sv.row0 + tp) * a.H + h) * D), 0, np * so2,
                                                       kRsrcW3);
     auto sig = [](float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); };
 #pragma unroll
@@ -758,7 +813,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     const int hf = lane_c >> 5, cg = lane_c & 31, c0 = 4 * cg, p0 = cpos(c0);
     const int tk0 = SBT * wave + 8 * hf;
     const int64_t t0 = c * CT;
-    const int n = (int)min<int64_t>(CT, a.T - t0);
+    const int n = (int)min<int64_t>(CT, sv.T - t0);
 
     // ---- loads ----------------------------------------------------------------------
     // Buffer loads: block-uniform base and bounds (the chunk's first n tokens), byte
@@ -767,7 +822,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     uint2 kx[8], qx[8], ax[8];
     float bt;
     {
-      const int64_t row0 = b * a.T + t0;
+      const int64_t row0 = sv.row0 + t0;
       const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
       const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
       const auto rq_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
@@ -961,7 +1016,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
           O[I][ct] = acc;
         }
       }
-      load_v(a, b, h, t0, n, col0, lane_c, vx);
+      load_v(a, sv.row0 + t0, h, n, col0, lane_c, vx);
     }
     lds_barrier();   // D
 
@@ -1024,7 +1079,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     if (GATED) {
       const int sg2 = (int)a.gate_stride * 2;
       const auto rg = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.gate + (b * a.T + t0) * a.gate_stride + h * D), 0, n * sg2, kRsrcW3);
+          (void*)(a.gate + (sv.row0 + t0) * a.gate_stride + h * D), 0, n * sg2, kRsrcW3);
       const int gc = col0 + 8 * (lane_c & 3);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1052,7 +1107,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       const int so2 = (int)(a.H * D) * 2;
-      const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((b * a.T + t0) * a.H + h) * D), 0, n * so2,
+      const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((sv.row0 + t0) * a.H + h) * D), 0, n * so2,
                                                         kRsrcW3);
       const int oc = col0 + 8 * (lane_c & 3);
 #pragma unroll
@@ -1068,7 +1123,7 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   }
   if (GATED && c_end > c_begin) gate_epilogue(c_end - 1);
 
-  if (a.S_final != nullptr && p == a.P - 1) store_state(S, a.S_final + bh * D * D, svo);
+  if (a.S_final != nullptr && p == sv.P - 1) store_state(S, a.S_final + sv.sidx * D * D, svo);
 }
 
 // Summary pass: one block of 8 waves per (batch, head, summary segment). Waves 0-3 run
@@ -1093,12 +1148,17 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const bool mkind = wave >= 4;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int64_t bh = lid / a.P;
-  const int p = lid % a.P;
-  const int64_t b = bh / a.H, h = bh % a.H;
-  const int64_t NC = (a.T + CT - 1) / CT;
-  const int64_t c_begin = (int64_t)p * a.L;
-  const int64_t c_end = min<int64_t>(min<int64_t>(NC, c_begin + a.L), a.c_stop);
+  const SeqDesc& rd = a.run[run_of<1>(a, lid)];
+  const int32_t local = (int32_t)lid - rd.sum0;
+  const int p = uni(local % rd.Ps);
+  const int32_t bhl = uni(local / rd.Ps);
+  const SeqView sv = seq_view(a, rd, bhl);
+  const int64_t h = uni(bhl % (int32_t)a.H);
+  const int64_t NC = (sv.T + CT - 1) / CT;
+  const int64_t Ls = (int64_t)kSub * a.Lo;            // chunks per summary segment
+  const int64_t c_stop = (int64_t)(sv.P - 1) * a.Lo;  // the last output segment needs no summary
+  const int64_t c_begin = (int64_t)p * Ls;
+  const int64_t c_end = min<int64_t>(min<int64_t>(NC, c_begin + Ls), c_stop);
 
   const int col0 = 32 * (wave & 3);
   f32x4 S[8][2];
@@ -1125,8 +1185,8 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const int I = wave & 3, hc = wave >> 2;
     const int hf = lane_c >> 5, c0 = 64 * hc + 2 * (lane_c & 31);
     const int64_t t0 = c * CT;
-    const int n = (int)min<int64_t>(CT, a.T - t0);
-    const int64_t row0 = b * a.T + t0;
+    const int n = (int)min<int64_t>(CT, sv.T - t0);
+    const int64_t row0 = sv.row0 + t0;
     const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
     const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
     const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
@@ -1142,6 +1202,8 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   Raw nxt;
   if (c_begin < c_end) issue(c_begin, nxt, lane);
+  int to_boundary = a.Lo;    // chunks left to the next output-segment boundary
+  int e_next = p * kSub;     // its workspace entry
 
   for (int64_t c = c_begin; c < c_end; ++c) {
     int lane_c = lane;
@@ -1153,7 +1215,7 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     const int hf = lane_c >> 5, cg = lane_c & 31, c0 = 64 * hc + 2 * cg, p0 = cpos(c0);
     const int tk0 = SBT * I + 8 * hf;
     const int64_t t0 = c * CT;
-    const int n = (int)min<int64_t>(CT, a.T - t0);
+    const int n = (int)min<int64_t>(CT, sv.T - t0);
 
     const Raw cur = nxt;
     uint32_t kx[8], ax[8];
@@ -1273,7 +1335,7 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
     uint4 vx[4];
-    if (!mkind) load_v(a, b, h, t0, n, col0, lane_c, vx);
+    if (!mkind) load_v(a, sv.row0 + t0, h, n, col0, lane_c, vx);
     lds_barrier();   // C
 
     // ---- M1T: A blocks, diagonal inverses ------------------------------------------------
@@ -1339,15 +1401,15 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
     update_state(L, fast, S, Ut, l16, q4);
     lds_barrier();   // F
 
-    const int64_t rel = c - c_begin;
-    if ((rel + 1) % a.Lo == 0) {
-      const int e = p * kSub + (int)(rel / a.Lo);
+    if (--to_boundary == 0) {
+      to_boundary = a.Lo;
+      const int e = e_next++;   // the entry of this output-segment boundary
       // M: the chunk's kr and kc are free until the next chunk's barrier B
       if (mkind)
-        store_mfrag(S, reinterpret_cast<uint4*>(a.WM + (bh * a.E + e) * D * D), wave & 3, lane_c,
+        store_mfrag(S, reinterpret_cast<uint4*>(sv.ws + (sv.E + e) * D * D), wave & 3, lane_c,
                     L.kr + (wave - 4) * kMsWave);
       else
-        store_tiles(S, a.WS + (bh * a.E + e) * D * D, wave & 3, lane_c);
+        store_tiles(S, sv.ws + e * D * D, wave & 3, lane_c);
     }
   }
 }
@@ -1367,13 +1429,20 @@ constexpr int BTS = D + 8;      // padded row of the transposed base state
 constexpr int kAhead = 3;
 
 
-__global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restrict__ WS, const float* __restrict__ WM,
-                                                           const float* __restrict__ S0, float* __restrict__ Sst,
-                                                           int P, int E) {
+__global__ __launch_bounds__(CB_T) void kda_combine_kernel(ChunkArgs a) {
   __shared__ __align__(16) uint16_t bhi[2][16 * BTS];   // [column][cpos(row)], double-buffered
   __shared__ __align__(16) uint16_t blo[2][16 * BTS];
-  const int64_t bh = blockIdx.x / 8;
-  const int slice = blockIdx.x % 8;
+  const uint32_t lid = blockIdx.x;
+  if (lid >= (uint32_t)a.nblk) return;
+  const SeqDesc& rd = a.run[run_of<2>(a, lid)];
+  const int32_t local = (int32_t)lid - rd.comb0;
+  const int slice = local % 8;
+  const SeqView sv = seq_view(a, rd, local / 8);
+  const int P = sv.P;
+  const float* WS = sv.ws;                  // [E] summary states
+  const float* WM = sv.ws + sv.E * D * D;   // [E] transitions
+  float* Sst = sv.ws + 2 * sv.E * D * D;    // [P] start states
+  const float* S0 = a.S0 ? a.S0 + sv.sidx * D * D : nullptr;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = 16 * slice + l16;
@@ -1381,25 +1450,25 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
 
   f32x4 cur;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) cur[r] = S0 ? S0[(bh * D + row0 + r) * D + col] : 0.f;
+  for (int r = 0; r < 4; ++r) cur[r] = S0 ? S0[(row0 + r) * D + col] : 0.f;
   auto store = [&](int po, const f32x4& v) {   // tile-major
-    *reinterpret_cast<f32x4*>(Sst + (bh * P + po) * D * D + tile_off(slice >> 1, wave, slice & 1, lane)) = v;
+    *reinterpret_cast<f32x4*>(Sst + po * D * D + tile_off(slice >> 1, wave, slice & 1, lane)) = v;
   };
   store(0, cur);
   const int nsteps = (P - 1) / kSub;   // chain starts kSub, 2 kSub, .. below P
   // A fragments of M_e for this wave's rows (split bf16, slot s: high 2 s, low 2 s + 1)
   uint4 mq[kAhead][8];
   f32x4 sq[kAhead];
-  auto fetch = [&](int step, uint4(&m)[8], f32x4& sv) {
+  auto fetch = [&](int step, uint4(&m)[8], f32x4& s_e) {
     if (step < nsteps) {
       const int e = step * kSub + kSub - 1;
-      const uint4* mp = reinterpret_cast<const uint4*>(WM + (bh * E + e) * D * D);
+      const uint4* mp = reinterpret_cast<const uint4*>(WM + e * D * D);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         m[2 * s] = mp[mfrag_off(wave, s, lane)];
         m[2 * s + 1] = mp[mfrag_off(wave, s, lane) + 1];
       }
-      sv = load_tile4(WS + (bh * E + e) * D * D, slice >> 1, wave, slice & 1, lane);
+      s_e = load_tile4(WS + e * D * D, slice >> 1, wave, slice & 1, lane);
     }
   };
 #pragma unroll
@@ -1442,22 +1511,56 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(const float* __restri
   }
 }
 
-struct Split {
-  int Po, Lo;   // output segments, chunks per output segment
-  int Ps, Ls;   // summary segments, chunks per summary segment
+// Host-side plan of a launch: one chunks-per-segment value Lo for all runs (so that every
+// block has at most Lo chunks), chosen to give about kTargetBlocks output blocks; then per run
+// its segment counts and workspace region.
+struct Plan {
+  int Lo = 1;
+  std::vector<SeqDesc> desc;   // per run; the first-block fields are filled per launch set
+  int64_t ws_mats = 0;         // workspace matrices (D x D fp32)
 };
 
-Split choose_split(int64_t B, int64_t T, int64_t H, bool no_split) {
-  const int64_t NC = (T + CT - 1) / CT;
-  const int64_t BH = B * H;
-  if (no_split || NC <= 1 || BH >= kTargetBlocks) return Split{1, (int)NC, 0, 0};
-  int64_t P = (kTargetBlocks + BH - 1) / BH;
-  if (P > NC) P = NC;
-  const int64_t Lo = (NC + P - 1) / P;
-  P = (NC + Lo - 1) / Lo;
-  if (P <= 1) return Split{1, (int)NC, 0, 0};
-  const int64_t Ps = (P - 1 + kSub - 1) / kSub;   // summaries up to the last needed boundary
-  return Split{(int)P, (int)Lo, (int)Ps, (int)(kSub * Lo)};
+Plan make_plan(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
+  Plan pl;
+  int64_t chunks = 0;
+  for (int64_t r = 0; r < nruns; ++r) chunks += runs[r].count * ((runs[r].len + CT - 1) / CT);
+  const int64_t work = H * chunks;
+  int64_t Lo = no_split ? (int64_t(1) << 30) : (work + kTargetBlocks - 1) / kTargetBlocks;
+  if (Lo < 1) Lo = 1;
+  if (Lo > (int64_t(1) << 30)) Lo = int64_t(1) << 30;
+  pl.Lo = (int)Lo;
+  pl.desc.resize((size_t)nruns);
+  for (int64_t r = 0; r < nruns; ++r) {
+    const int64_t NC = (runs[r].len + CT - 1) / CT;
+    const int64_t P = NC <= 1 ? 1 : (NC + Lo - 1) / Lo;
+    const int64_t Ps = P > 1 ? (P - 1 + kSub - 1) / kSub : 0;   // summaries up to the last needed boundary
+    SeqDesc& d = pl.desc[(size_t)r];
+    d.start = runs[r].start;
+    d.len = runs[r].len;
+    d.ws0 = pl.ws_mats;
+    d.count = (int32_t)runs[r].count;
+    d.sidx0 = (int32_t)runs[r].sidx0;
+    d.P = (int32_t)P;
+    d.Ps = (int32_t)Ps;
+    d.out0 = d.sum0 = d.comb0 = d.pad = 0;
+    if (P > 1) pl.ws_mats += runs[r].count * H * (2 * kSub * Ps + P);
+  }
+  return pl;
+}
+
+// blocks of each pass for the runs [r0, r1) of a plan
+struct SetBlocks {
+  int64_t out = 0, sum = 0, comb = 0;
+};
+SetBlocks set_blocks(const Plan& pl, size_t r0, size_t r1, int64_t H) {
+  SetBlocks b;
+  for (size_t r = r0; r < r1; ++r) {
+    const SeqDesc& d = pl.desc[r];
+    b.out += (int64_t)d.count * H * d.P;
+    b.sum += (int64_t)d.count * H * d.Ps;
+    if (d.P > 1) b.comb += (int64_t)d.count * H * 8;
+  }
+  return b;
 }
 
 }  // namespace
@@ -1470,22 +1573,22 @@ bool kda_chunked_supported(const KdaArgs& a) {
          (al & 7) == 0;
 }
 
-int64_t kda_chunked_segments(int64_t B, int64_t T, int64_t H, bool no_split) {
-  return choose_split(B, T, H, no_split).Po;
+bool kda_chunked_plan_ok(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
+  const Plan pl = make_plan(runs, nruns, H, no_split);
+  for (size_t r0 = 0; r0 < pl.desc.size(); r0 += kMaxRuns) {
+    const SetBlocks b = set_blocks(pl, r0, std::min(pl.desc.size(), r0 + (size_t)kMaxRuns), H);
+    if (b.out > 0x7fffff00 || b.sum > 0x7fffff00 || b.comb > 0x7fffff00) return false;
+  }
+  return true;
 }
 
-size_t kda_chunked_workspace(int64_t B, int64_t T, int64_t H, bool no_split) {
-  const Split sp = choose_split(B, T, H, no_split);
-  if (sp.Po <= 1) return 0;
-  const size_t mat = (size_t)D * D * sizeof(float);
-  const size_t E = (size_t)sp.Ps * kSub;
-  return (size_t)(B * H) * (2 * E + sp.Po) * mat;
+size_t kda_chunked_workspace(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
+  return (size_t)make_plan(runs, nruns, H, no_split).ws_mats * D * D * sizeof(float);
 }
 
-hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, hipStream_t stream, Marks* marks) {
-  const Split sp = choose_split(x.B, x.T, x.H, no_split);
-  const int64_t BH = x.B * x.H;
-  if (BH * sp.Po * 2 > 0x7fffff00) return hipErrorInvalidValue;
+hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nruns, bool no_split, void* workspace,
+                              hipStream_t stream, Marks* marks) {
+  const Plan pl = make_plan(runs, nruns, x.H, no_split);
   ChunkArgs a;
   a.q = static_cast<const uint16_t*>(x.q);
   a.k = static_cast<const uint16_t*>(x.k);
@@ -1494,10 +1597,7 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   a.alpha = static_cast<const uint16_t*>(x.alpha);
   a.beta = static_cast<const uint16_t*>(x.beta);
   a.S0 = x.S0;
-  a.Sstart = nullptr;
-  a.WS = nullptr;
-  a.WM = nullptr;
-  a.E = 0;
+  a.ws = static_cast<float*>(workspace);
   a.o = static_cast<uint16_t*>(x.o);
   a.S_final = x.S_final;
   // the gate is fused into the output pass when its rows and the gain are read as 16-byte
@@ -1509,8 +1609,8 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
   a.gate_stride = x.gate_stride;
   a.norm_w = x.norm_w;
   a.norm_eps = x.norm_eps;
-  a.T = x.T;
   a.H = x.H;
+  a.Lo = pl.Lo;
   a.l2norm = x.l2norm ? 1 : 0;
   const size_t lds = sizeof(Lds), lds_sum = sizeof(Lds) + 2 * CT * sizeof(float);
   int dev = 0;
@@ -1530,49 +1630,49 @@ hipError_t launch_kda_chunked(const KdaArgs& x, bool no_split, void* workspace, 
     if (dev >= 0 && dev < 64) attr_done[dev] = true;
   }
   auto round8 = [](int64_t n) { return (int)((n + 7) / 8 * 8); };
-  if (sp.Po > 1) {
-    const int64_t E = (int64_t)sp.Ps * kSub;
-    float* WS = static_cast<float*>(workspace);
-    float* WM = WS + BH * E * D * D;
-    float* Sst = WM + BH * E * D * D;
-    ChunkArgs s = a;
-    s.WS = WS;
-    s.WM = WM;
-    s.P = sp.Ps;
-    s.L = sp.Ls;
-    s.Lo = sp.Lo;
-    s.E = (int)E;
-    s.c_stop = (int64_t)(sp.Po - 1) * sp.Lo;
-    s.nblk = (int)(BH * sp.Ps);
-    s.grid = round8(s.nblk);
-    hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(2 * NTHR), lds_sum, stream, s);
+  // runs go to the kernels kMaxRuns at a time (the table travels in the kernel arguments)
+  for (size_t r0 = 0; r0 < pl.desc.size(); r0 += kMaxRuns) {
+    const size_t r1 = std::min(pl.desc.size(), r0 + (size_t)kMaxRuns);
+    a.nruns = (int)(r1 - r0);
+    int64_t out0 = 0, sum0 = 0, comb0 = 0;
+    for (size_t r = r0; r < r1; ++r) {
+      SeqDesc d = pl.desc[r];
+      d.out0 = (int32_t)out0;
+      d.sum0 = (int32_t)sum0;
+      d.comb0 = (int32_t)comb0;
+      a.run[r - r0] = d;
+      out0 += (int64_t)d.count * x.H * d.P;
+      sum0 += (int64_t)d.count * x.H * d.Ps;
+      if (d.P > 1) comb0 += (int64_t)d.count * x.H * 8;
+    }
+    if (out0 > 0x7fffff00 || sum0 > 0x7fffff00 || comb0 > 0x7fffff00) return hipErrorInvalidValue;
+    if (sum0 > 0) {
+      ChunkArgs s = a;
+      s.nblk = (int)sum0;
+      s.grid = round8(sum0);
+      hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(2 * NTHR), lds_sum, stream, s);
+      hipError_t e = hipGetLastError();
+      if (e == hipSuccess) e = mark_after(marks, "kda_sum_kernel", stream);
+      if (e != hipSuccess) return e;
+      s.nblk = (int)comb0;
+      s.grid = (int)comb0;
+      hipLaunchKernelGGL(kda_combine_kernel, dim3((unsigned)comb0), dim3(CB_T), 0, stream, s);
+      e = hipGetLastError();
+      if (e == hipSuccess) e = mark_after(marks, "kda_combine_kernel", stream);
+      if (e != hipSuccess) return e;
+    }
+    if (out0 == 0) continue;
+    a.nblk = (int)out0;
+    a.grid = round8(out0);
+    if (fuse_gate)
+      hipLaunchKernelGGL(kda_out_kernel<true>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
+    else
+      hipLaunchKernelGGL(kda_out_kernel<false>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess) e = mark_after(marks, "kda_sum_kernel", stream);
+    if (e == hipSuccess) e = mark_after(marks, fuse_gate ? "kda_out_gated_kernel" : "kda_out_kernel", stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_combine_kernel, dim3((unsigned)(BH * 8)), dim3(CB_T), 0, stream, WS, WM, x.S0, Sst, sp.Po,
-                       (int)E);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = mark_after(marks, "kda_combine_kernel", stream);
-    if (e != hipSuccess) return e;
-    a.Sstart = Sst;
-    a.WS = WS;
-    a.WM = WM;
-    a.E = (int)E;
   }
-  a.P = sp.Po;
-  a.L = sp.Lo;
-  a.Lo = sp.Lo;
-  a.c_stop = 0;
-  a.nblk = (int)(BH * sp.Po);
-  a.grid = round8(a.nblk);
-  if (fuse_gate)
-    hipLaunchKernelGGL(kda_out_kernel<true>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
-  else
-    hipLaunchKernelGGL(kda_out_kernel<false>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) e = mark_after(marks, fuse_gate ? "kda_out_gated_kernel" : "kda_out_kernel", stream);
-  if (e == hipSuccess && gated && !fuse_gate) e = launch_kda_gate_norm(x, stream, marks);
-  return e;
+  return gated && !fuse_gate ? launch_kda_gate_norm(x, stream, marks) : hipSuccess;
 }
 
 }  // namespace chm

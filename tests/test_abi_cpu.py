@@ -161,6 +161,41 @@ def test_kda_gated_argument_errors():
     assert timed(4) == 2 and used.value == 0                            # needs 4 kernels + 1
 
 
+def test_kda_varlen_argument_errors_and_workspace():
+    """chimera_kda_fwd_varlen checks the sample offsets before any launch (no kernel runs here);
+    its workspace for equal samples equals the batched call's."""
+    L = chm.lib()
+    f = ctypes.c_float
+
+    def call(cu, nseq=None):
+        arr = np.ascontiguousarray(np.asarray(cu, dtype=np.int64))
+        n = len(cu) - 1 if nseq is None else nseq
+        return L.chimera_kda_fwd_varlen(1, 2, 3, 256, 4, 5, None, None, 0, None, f(1e-6), 6, None, arr.ctypes.data,
+                                        n, 2, 128, 128, 1, 1, None, 0, None)
+    assert call([1, 5]) == 2                                            # must start at 0
+    assert call([0, 9, 4]) == 2                                         # decreasing
+    assert call([0, 4], nseq=-1) == 2
+    assert L.chimera_kda_fwd_varlen(1, 2, 3, 256, 4, 5, None, None, 0, None, f(1e-6), 6, None, None, 1, 2, 128,
+                                    128, 1, 1, None, 0, None) == 1      # no offsets
+    assert call([0]) == 0                                               # no sample: nothing to do
+    big = 64 * 300
+    need = chm.kda_varlen_workspace_size([0, big, 2 * big, 3 * big], 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
+    assert need > 0
+    assert need == chm.kda_workspace_size(3, big, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
+    mixed = [0, 1000, 1000, 5000, 5300, 20000]
+    assert chm.kda_varlen_workspace_size(mixed, 16, 128, 128, chm.BF16, chm.KDA_SEQUENTIAL) == 0
+    assert chm.kda_varlen_workspace_size(mixed, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK) > 0
+    assert chm.kda_varlen_workspace_size([0, 3, 2], 16, 128, 128, chm.BF16, 0) == 0     # invalid offsets
+    ev = (ctypes.c_void_p * 16)()
+    names = (ctypes.c_char_p * 16)()
+    used = ctypes.c_int32(3)
+    arr = np.array([0, 5, 9], dtype=np.int64)
+    timed = lambda cap: L.chimera_kda_fwd_varlen_timed(1, 2, 3, 256, 4, 5, None, None, 0, None, f(1e-6), 6, None,
+                                                       arr.ctypes.data, 2, 2, 128, 128, 1, 1, None, 0, None, ev,
+                                                       names, cap, ctypes.byref(used))
+    assert timed(7) == 2 and used.value == 0                            # needs 2 * nseq + 4 = 8
+
+
 def test_workspace_size_rules():
     n = chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
     assert n >= 0
