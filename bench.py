@@ -107,13 +107,28 @@ def kda_split(B: int, T: int, H: int, target_blocks: int = 512):
     return nc, (p - 1) * lo
 
 
+def kda_summarised_tokens(w) -> int:
+    """Tokens (per head) that the summary pass reads: every sequence's chunks but those of its last
+    output segment, with the library's plan (one Lo for all sequences of the call)."""
+    lens = ([w.samples[i + 1] - w.samples[i] for i in range(len(w.samples) - 1)] if w.samples
+            else [w.T] * w.B)
+    ncs = [(n + 63) // 64 for n in lens]
+    lo = max(1, (w.H * sum(ncs) + 511) // 512)
+    toks = 0
+    for n, nc in zip(lens, ncs):
+        p = 1 if nc <= 1 else (nc + lo - 1) // lo
+        toks += min(n, (p - 1) * lo * 64)
+    return toks
+
+
 def kernel_work(name: str, w) -> dict:
     """Algorithmic bytes (HBM-bound kernels) of one launch on a workload, with the recipe."""
     B, T, H, d, C = w.B, w.T, w.H, w.d, w.C
     text = sum(s.length for s in w.segments if s.kind == 0)
     vis = T - text
     e = 2 if w.dtype == "bf16" else 4
-    state = B * H * d * d * 4 * (2 if w.s0_std is not None else 1)     # S_final (+ S0)
+    nseq = len(w.samples) - 1 if w.samples else B
+    state = nseq * H * d * d * 4 * (2 if w.s0_std is not None else 1)  # S_final (+ S0) per sequence
     if name in ("conv_rows_kernel", "conv_tile_kernel"):
         return {"bytes": 2 * B * vis * C * e,
                 "recipe": f"read + write every q|k|v channel of the {vis} visual tokens once: 2 x {C} x {e} B/token"}
@@ -129,11 +144,10 @@ def kernel_work(name: str, w) -> dict:
     if name == "kda_gate_norm_kernel":
         return {"bytes": 3 * B * T * H * d * e, "recipe": f"o and the gate in, o out: {3 * d * e} B per token-head"}
     if name == "kda_sum_kernel":
-        nc, c_stop = kda_split(B, T, H)
-        toks = min(T, c_stop * 64)
-        return {"bytes": B * toks * H * (3 * d * e + e),
+        toks = kda_summarised_tokens(w)
+        return {"bytes": toks * H * (3 * d * e + e),
                 "recipe": f"k, v, alpha + beta in ({3 * d * e + e} B per token-head) over the {toks} tokens "
-                          f"({c_stop} of {nc} chunks) the segment summaries cover"}
+                          f"(of {B * T}) the segment summaries cover"}
     return {"bytes": None, "recipe": "workspace only (no algorithmic HBM traffic)"}
 
 
@@ -206,8 +220,12 @@ def summarize_pmc(fetch_csv: str, write_csv: str):
 
 def _sample_segments(w, budget: int):
     """The first tokens of the workload's layout: the text, then whole grid rows (image) or frames
-    (video) up to about `budget` tokens per sequence."""
+    (video) up to about `budget` tokens per sequence; for a packed row, its first whole samples."""
     import workloads as wl
+    if w.samples:
+        k = max(1, sum(1 for c in w.samples[1:] if c <= budget))
+        n = w.samples[k]
+        return tuple(sg for sg in w.segments if sg.start < n), n
     out, n = [], 0
     for sg in w.segments:
         if sg.kind == wl.TEXT:
@@ -230,7 +248,7 @@ def _sample_segments(w, budget: int):
 def _cpu_baseline(inp, w, budget: int, gate=None):
     """The oracle as it stands, on the first tokens of the workload, one host core."""
     from threadpoolctl import threadpool_limits
-    from oracle import conv_ref, gated_rmsnorm_ref, kda_ref, l2norm_ref, round_bf16_ref
+    from oracle import conv_ref, gated_rmsnorm_ref, kda_ref, kda_varlen_ref, l2norm_ref, round_bf16_ref
 
     segs, n = _sample_segments(w, budget)
     x = inp["x"][:, :n]
@@ -241,12 +259,19 @@ def _cpu_baseline(inp, w, budget: int, gate=None):
         if w.dtype == "bf16":
             y = round_bf16_ref(y)
         parts = y.reshape(w.B, n, 3, w.H, w.d)
-        o_ref, _ = kda_ref(l2norm_ref(parts[:, :, 0]), l2norm_ref(parts[:, :, 1]), parts[:, :, 2],
-                           inp["alpha"][:, :n], inp["beta"][:, :n], S0)
+        if w.samples:
+            cu = [c for c in w.samples if c <= n]
+            o_ref, _ = kda_varlen_ref(l2norm_ref(parts[0, :, 0]), l2norm_ref(parts[0, :, 1]), parts[0, :, 2],
+                                      inp["alpha"][0, :n], inp["beta"][0, :n], cu, None)
+            o_ref = o_ref[None]
+        else:
+            o_ref, _ = kda_ref(l2norm_ref(parts[:, :, 0]), l2norm_ref(parts[:, :, 1]), parts[:, :, 2],
+                               inp["alpha"][:, :n], inp["beta"][:, :n], S0)
         if gate is not None:
             gated_rmsnorm_ref(o_ref, gate[0][:, :n], gate[1], 1e-6)
         dt = time.perf_counter() - t0
-    desc = " + ".join(f"{sg.length} {'text' if sg.kind == 0 else 'grid'}" for sg in segs)
+    desc = (f"{sum(1 for c in w.samples[1:] if c <= n)} whole packed samples" if w.samples else
+            " + ".join(f"{sg.length} {'text' if sg.kind == 0 else 'grid'}" for sg in segs))
     return {"value": n * w.B / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} tokens of each of the {w.B} sequence(s) ({desc}), all {w.H} heads, conv + L2 norm "
                       f"+ token-by-token KDA" + (" + gate and norm" if gate is not None else "") +
@@ -289,8 +314,11 @@ def main():
     y = torch.empty_like(x)
     q, k, v = chm.split_qkv(y, H, d)
     o = torch.empty(B, T, H, d, dtype=tdt, device=dev)
-    s_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
-    need = chm.kda_workspace_size(B, T, H, d, d, chm.BF16 if w.dtype == "bf16" else chm.F32, chm.KDA_L2NORM_QK)
+    nseq = len(w.samples) - 1 if w.samples else B
+    s_final = torch.empty(nseq if w.samples else B, H, d, d, dtype=torch.float32, device=dev)
+    dcode = chm.BF16 if w.dtype == "bf16" else chm.F32
+    need = (chm.kda_varlen_workspace_size(w.samples, H, d, d, dcode, chm.KDA_L2NORM_QK) if w.samples else
+            chm.kda_workspace_size(B, T, H, d, d, dcode, chm.KDA_L2NORM_QK))
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     gate_np = wl.make_gate(w) if args.gated else None
     gkw = {}
@@ -299,7 +327,11 @@ def main():
 
     def step(mc=None, mk=None):
         chm.mshortconv_fwd(x, wt, wv, segs, out=y, marks=mc)
-        chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, marks=mk, state_out=s_final, **gkw)
+        if w.samples:
+            chm.kda_fwd_varlen(q[0], k[0], v[0], alpha[0], beta[0], w.samples, None, workspace=ws, out=o[0],
+                               marks=mk, state_out=s_final, **gkw)
+        else:
+            chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, marks=mk, state_out=s_final, **gkw)
 
     if args.profile_once:
         ref_src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device=dev)   # 1 GiB
@@ -314,7 +346,8 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    marks = [(chm.Marks(len(segs) + 1), chm.Marks(5 if args.gated else 4)) for _ in range(args.steps)]
+    kda_cap = 2 * nseq + 4 if w.samples else (5 if args.gated else 4)
+    marks = [(chm.Marks(len(segs) + 1), chm.Marks(kda_cap)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -356,10 +389,14 @@ def main():
     e = 2 if w.dtype == "bf16" else 4
     conv_bytes = 2 * B * T * w.C * e
     kda_bytes = B * T * H * (4 * d * e + e + d * e + (d * e if args.gated else 0)) \
-        + B * H * d * d * 4 * (2 if S0 is not None else 1)
+        + nseq * H * d * d * 4 * (2 if S0 is not None else 1)
     tokens = B * T
-    layout = " + ".join(("text" if sg.kind == 0 else f"{sg.frames}x{sg.height}x{sg.width} grid") + f" ({sg.length})"
-                        for sg in segs)
+    if w.samples:
+        layout = (f"{nseq} packed samples (a text prompt of 32..300 tokens, then a 16x16, 32x32 or 64x64 image "
+                  f"grid at 4:2:2), the state restarting at each sample")
+    else:
+        layout = " + ".join(("text" if sg.kind == 0 else f"{sg.frames}x{sg.height}x{sg.width} grid") +
+                            f" ({sg.length})" for sg in segs)
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),

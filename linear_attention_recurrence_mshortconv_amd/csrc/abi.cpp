@@ -133,12 +133,9 @@ static chimera_status conv_fwd(const void* x, void* y, int64_t B, int64_t T, int
   if ((any_text && w_text == nullptr) || (any_vis && w_vis == nullptr)) return CHIMERA_ERR_NULL;
   if (x == y) return CHIMERA_ERR_UNSUPPORTED;
   if (marks != nullptr && chm::mark_begin(marks, stream) != hipSuccess) return CHIMERA_ERR_HIP;
-  for (int32_t i = 0; i < nseg; ++i) {
-    const hipError_t e = chm::launch_conv_segment(x, y, B, T, C, dt == CHIMERA_BF16, w_text, w_vis,
-                                                  to_seg(segs[i]), false, stream, marks);
-    if (e != hipSuccess) return CHIMERA_ERR_HIP;
-  }
-  return CHIMERA_OK;
+  std::vector<Seg> sv((size_t)nseg);
+  for (int32_t i = 0; i < nseg; ++i) sv[(size_t)i] = to_seg(segs[i]);
+  return hip_status(chm::launch_conv(x, y, B, T, C, dt == CHIMERA_BF16, w_text, w_vis, sv.data(), nseg, stream, marks));
 }
 
 chimera_status chimera_mshortconv_fwd(const void* x, void* y, int64_t B, int64_t T, int64_t C, chimera_dtype dt,

@@ -36,6 +36,11 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t T, int
                                const float* w_text, const float* w_vis, const Seg& seg,
                                bool force_gather, hipStream_t stream, Marks* marks = nullptr);
 
+// y = mShortConv(x) for all segments of a layout: the text segments in one batched launch,
+// the image grids of the rows kernel in another, every other segment on its own.
+hipError_t launch_conv(const void* x, void* y, int64_t B, int64_t T, int64_t C, bool bf16, const float* w_text,
+                       const float* w_vis, const Seg* segs, int nseg, hipStream_t stream, Marks* marks = nullptr);
+
 // Device-side neighbour table [T][27] for one segment (the conv kernels' arithmetic).
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream);
 

@@ -194,19 +194,26 @@ struct ChunkArgs {
   int grid;               // launched blocks
   int l2norm;
   int nruns;
+  int xcd_ranges;         // give each XCD a contiguous range of logical blocks (one run only)
   SeqDesc run[kMaxRuns];
 };
 
 // The run that logical block `lid` of a pass belongs to: the last run whose first block is
-// at most lid (runs without a block in this pass share the next run's first block).
+// at most lid (runs without a block in this pass share the next run's first block), by
+// binary search over the nondecreasing first blocks.
 template <int PASS>   // 0 output, 1 summary, 2 combine
+__device__ __forceinline__ int32_t first_block(const SeqDesc& d) {
+  return PASS == 0 ? d.out0 : PASS == 1 ? d.sum0 : d.comb0;
+}
+template <int PASS>
 __device__ __forceinline__ int run_of(const ChunkArgs& a, uint32_t lid) {
-  int r = 0;
-  for (int i = 1; i < a.nruns; ++i) {
-    const int32_t first = PASS == 0 ? a.run[i].out0 : PASS == 1 ? a.run[i].sum0 : a.run[i].comb0;
-    if ((int64_t)lid >= first) r = i;
+  int lo = 0, hi = a.nruns - 1;   // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)lid >= first_block<PASS>(a.run[mid])) lo = mid;
+    else hi = mid - 1;
   }
-  return r;
+  return lo;
 }
 // One (sequence, head) of a run: its first row, length, S0 / S_final index and workspace
 // region ([E] summary states, [E] transitions, [P] start states, each D x D fp32).
@@ -670,7 +677,8 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   extern __shared__ __align__(16) unsigned char lds_raw[];
   Lds& L = *reinterpret_cast<Lds*>(lds_raw);
 
-  const uint32_t lid = (a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid) : blockIdx.x;
+  const uint32_t lid = (a.xcd_ranges && a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid)
+                                                         : blockIdx.x;
   if (lid >= (uint32_t)a.nblk) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
@@ -1142,7 +1150,8 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
   Lds& L = *reinterpret_cast<Lds*>(lds_raw);
   float (&nk)[2][CT] = *reinterpret_cast<float(*)[2][CT]>(lds_raw + sizeof(Lds));   // partial |k|^2
 
-  const uint32_t lid = (a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid) : blockIdx.x;
+  const uint32_t lid = (a.xcd_ranges && a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid)
+                                                         : blockIdx.x;
   if (lid >= (uint32_t)a.nblk) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
@@ -1511,14 +1520,35 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(ChunkArgs a) {
   }
 }
 
-// Host-side plan of a launch: one chunks-per-segment value Lo for all runs (so that every
-// block has at most Lo chunks), chosen to give about kTargetBlocks output blocks; then per run
-// its segment counts and workspace region.
+// Host-side plan of a launch: one chunks-per-segment value Lo for all runs (so that no block
+// has more than Lo chunks), then per run its segment counts and workspace region, and the runs
+// in the order their blocks are handed out (longest blocks first).
 struct Plan {
   int Lo = 1;
   std::vector<SeqDesc> desc;   // per run; the first-block fields are filled per launch set
   int64_t ws_mats = 0;         // workspace matrices (D x D fp32)
 };
+
+// Estimated time of the two passes for a segment length Lo, in chunk steps of an output block
+// (two per CU, about kTargetBlocks at once): the longest block or the total work spread over
+// the chip, whichever is larger; a summary block (one per CU, about 0.55 of an output block's
+// time per chunk) covers up to kSub * Lo chunks. For a batch of equal sequences the smallest
+// Lo that gives about kTargetBlocks output blocks is always best; for packed samples of mixed
+// lengths a shorter Lo can spread the few long samples' summaries over more blocks.
+double plan_cost(const KdaRun* runs, int64_t nruns, int64_t H, int64_t Lo) {
+  double w_out = 0, w_sum = 0, max_out = 0, max_sum = 0;
+  for (int64_t r = 0; r < nruns; ++r) {
+    const int64_t NC = (runs[r].len + CT - 1) / CT;
+    const int64_t P = NC <= 1 ? 1 : (NC + Lo - 1) / Lo;
+    w_out += (double)runs[r].count * H * NC;
+    max_out = std::max(max_out, (double)std::min(NC, Lo));
+    if (P > 1) {
+      w_sum += (double)runs[r].count * H * (P - 1) * Lo;
+      max_sum = std::max(max_sum, (double)std::min((P - 1) * Lo, (int64_t)kSub * Lo));
+    }
+  }
+  return std::max(max_out, w_out / kTargetBlocks) + 0.55 * std::max(max_sum, w_sum / (kTargetBlocks / 2));
+}
 
 Plan make_plan(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
   Plan pl;
@@ -1528,22 +1558,40 @@ Plan make_plan(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
   int64_t Lo = no_split ? (int64_t(1) << 30) : (work + kTargetBlocks - 1) / kTargetBlocks;
   if (Lo < 1) Lo = 1;
   if (Lo > (int64_t(1) << 30)) Lo = int64_t(1) << 30;
+  if (!no_split && nruns > 1) {   // mixed lengths: a shorter segment if it is clearly cheaper
+    const int64_t L0 = Lo;
+    double best = plan_cost(runs, nruns, H, L0);
+    for (const int div : {2, 3, 4, 6, 8}) {
+      const int64_t cand = std::max<int64_t>(1, (L0 + div - 1) / div);
+      const double c = plan_cost(runs, nruns, H, cand);
+      if (c < 0.97 * best) {
+        best = c;
+        Lo = cand;
+      }
+    }
+  }
   pl.Lo = (int)Lo;
+  // longest blocks first: the run order is only the order in which blocks are handed out
+  std::vector<int64_t> order((size_t)nruns);
+  for (int64_t r = 0; r < nruns; ++r) order[(size_t)r] = r;
+  auto longest = [&](int64_t r) { return std::min((runs[r].len + CT - 1) / CT, Lo); };
+  std::stable_sort(order.begin(), order.end(), [&](int64_t x, int64_t y) { return longest(x) > longest(y); });
   pl.desc.resize((size_t)nruns);
-  for (int64_t r = 0; r < nruns; ++r) {
-    const int64_t NC = (runs[r].len + CT - 1) / CT;
+  for (int64_t i = 0; i < nruns; ++i) {
+    const KdaRun& run = runs[order[(size_t)i]];
+    const int64_t NC = (run.len + CT - 1) / CT;
     const int64_t P = NC <= 1 ? 1 : (NC + Lo - 1) / Lo;
     const int64_t Ps = P > 1 ? (P - 1 + kSub - 1) / kSub : 0;   // summaries up to the last needed boundary
-    SeqDesc& d = pl.desc[(size_t)r];
-    d.start = runs[r].start;
-    d.len = runs[r].len;
+    SeqDesc& d = pl.desc[(size_t)i];
+    d.start = run.start;
+    d.len = run.len;
     d.ws0 = pl.ws_mats;
-    d.count = (int32_t)runs[r].count;
-    d.sidx0 = (int32_t)runs[r].sidx0;
+    d.count = (int32_t)run.count;
+    d.sidx0 = (int32_t)run.sidx0;
     d.P = (int32_t)P;
     d.Ps = (int32_t)Ps;
     d.out0 = d.sum0 = d.comb0 = d.pad = 0;
-    if (P > 1) pl.ws_mats += runs[r].count * H * (2 * kSub * Ps + P);
+    if (P > 1) pl.ws_mats += run.count * H * (2 * kSub * Ps + P);
   }
   return pl;
 }
@@ -1612,6 +1660,7 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
   a.H = x.H;
   a.Lo = pl.Lo;
   a.l2norm = x.l2norm ? 1 : 0;
+  a.xcd_ranges = pl.desc.size() == 1 ? 1 : 0;   // blocks of unequal length: the hardware's round robin
   const size_t lds = sizeof(Lds), lds_sum = sizeof(Lds) + 2 * CT * sizeof(float);
   int dev = 0;
   hipError_t de = hipGetDevice(&dev);

@@ -20,6 +20,7 @@
 //    slides a 3-row window down its column, so each staged value is read from
 //    LDS once per (kw) and feeds up to three output rows.
 #include <algorithm>
+#include <vector>
 
 #include "dtypes.h"
 #include "internal.h"
@@ -81,6 +82,40 @@ __global__ __launch_bounds__(256) void conv_gather_kernel(const T* __restrict__ 
 // check), so kOutside marks a position outside the grid.
 constexpr uint32_t kOutside = 0x80000000u;   // past every buffer: the launcher keeps them under 2 GiB
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 data format
+
+// Segments of one kind go to one launch, up to kMaxBatch at a time, with a table in the
+// kernel arguments: each entry holds the segment, its block decomposition and its first
+// block; a block finds its entry by binary search over the first blocks. (Packed rows
+// of many samples have many short segments, each far too small to fill the chip alone.)
+constexpr int kMaxBatch = 48;
+struct RowsEntry {
+  Seg seg;
+  int32_t n_tw, n_rr, rows_per_range, blk0;
+};
+struct RowsBatch {
+  int n, n_slab, n_logical, pad;
+  RowsEntry e[kMaxBatch];
+};
+struct TextEntry {
+  Seg seg;
+  int32_t n_run4, blk0, pad0, pad1;   // run groups (4 runs of kTextRun tokens each), first block
+};
+struct TextBatch {
+  int n, n_cg, n_logical, pad;        // n_cg: groups of 64 x 8 channels
+  TextEntry e[kMaxBatch];
+};
+__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+// the last entry whose first block is at most lid
+template <typename Batch>
+__device__ __forceinline__ int entry_of(const Batch& t, int32_t lid) {
+  int lo = 0, hi = t.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (lid >= t.e[mid].blk0) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
 
 template <int NF, int CPT, int TR, int TW>
 struct TileCfg {
@@ -267,8 +302,7 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
 template <int TR, int TW>
 __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                          const float* __restrict__ w_vis, int64_t Ttot, int64_t C,
-                                                         Seg seg, int n_slab, int n_tw, int n_rr, int rows_per_range,
-                                                         int n_logical) {
+                                                         RowsBatch tb) {
   constexpr int NT = TW * 8, SC = TW + 2, RING = TR + 2;
   constexpr int ITEMS = TR * SC * 8;                 // 16-byte items per TR staged rows
   constexpr int NIT = (ITEMS + NT - 1) / NT;
@@ -277,11 +311,14 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
   __shared__ uint4 ring[RING * SC * 8 + NT];
 
   const int lid = (int)xcd_contiguous_id(blockIdx.x, gridDim.x);
-  if (lid >= n_logical) return;
-  int r = lid;
-  const int tw = r % n_tw; r /= n_tw;
-  const int slab = r % n_slab; r /= n_slab;
-  const int rr_ix = r % n_rr; r /= n_rr;
+  if (lid >= tb.n_logical) return;
+  const RowsEntry& ent = tb.e[entry_of(tb, lid)];
+  const Seg seg = ent.seg;
+  const int n_tw = ent.n_tw, n_slab = tb.n_slab, n_rr = ent.n_rr, rows_per_range = ent.rows_per_range;
+  int r = lid - ent.blk0;
+  const int tw = uni(r % n_tw); r = uni(r / n_tw);
+  const int slab = uni(r % n_slab); r = uni(r / n_slab);
+  const int rr_ix = uni(r % n_rr); r = uni(r / n_rr);
   const int64_t b = r;
 
   const int tid = threadIdx.x, g = tid & 7, col = tid >> 3;
@@ -394,11 +431,18 @@ constexpr int kTextRun = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void conv_text_kernel(const T* __restrict__ x, T* __restrict__ y,
                                                        const float* __restrict__ w_text, int64_t Ttot, int64_t C,
-                                                       Seg seg) {
+                                                       TextBatch tb) {
+  const int lid = blockIdx.x;
+  if (lid >= tb.n_logical) return;
+  const TextEntry& ent = tb.e[entry_of(tb, lid)];
+  const Seg seg = ent.seg;
+  int r = lid - ent.blk0;                     // (batch item, run group, channel group)
+  const int bx = uni(r % tb.n_cg); r = uni(r / tb.n_cg);
+  const int by = uni(r % ent.n_run4);
+  const int64_t b = uni(r / ent.n_run4);
   const int64_t C8 = C / 8;
-  const int64_t cg = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-  const int64_t run = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int64_t b = blockIdx.z;
+  const int64_t cg = (int64_t)bx * 64 + (threadIdx.x & 63);
+  const int64_t run = (int64_t)by * 4 + (threadIdx.x >> 6);
   const int64_t l0 = run * kTextRun;
   if (cg >= C8 || l0 >= seg.length) return;
   const int64_t c0 = cg * 8;
@@ -508,15 +552,16 @@ bool rows_fit(const Seg& seg, int64_t C) {
   return (int64_t)(TR + 2) * seg.width * C * 2 <= kRowsSpanMax;
 }
 
+// The row split of one image segment: rows in ranges (each re-reads 2 halo rows) so that
+// the segment alone would be about six rounds of the blocks that fit on the chip at once
+// (two per CU): blocks are long-lived, and a grid of a few whole rounds keeps the last
+// round full. Returns false when no range fits a buffer.
 template <int TR, int TW>
-hipError_t launch_rows(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
-                       const Seg& seg, hipStream_t stream, Marks* marks) {
+bool rows_entry(const Seg& seg, int64_t B, int64_t C, RowsEntry& ent, int64_t& blocks) {
   const int n_slab = (int)(C / 64);
-  const int n_tw = (int)((seg.width + TW - 1) / TW);
-  // Split the rows into ranges (each re-reads 2 halo rows) so that the grid is about
-  // six rounds of the blocks that fit on the chip at once (two per CU): blocks are
-  // long-lived, and a grid of a few whole rounds keeps the last round full.
-  const int64_t per_range = (int64_t)n_slab * n_tw * B;
+  ent.seg = seg;
+  ent.n_tw = (int)((seg.width + TW - 1) / TW);
+  const int64_t per_range = (int64_t)n_slab * ent.n_tw * B;
   const int64_t want = 12 * (int64_t)device_cus();
   int n_rr = (int)std::max<int64_t>(1, std::min<int64_t>((want + per_range - 1) / per_range, (seg.height + 4 * TR - 1) / (4 * TR)));
   int rows_per_range = (seg.height + n_rr - 1) / n_rr;
@@ -524,17 +569,72 @@ hipError_t launch_rows(const uint16_t* x, uint16_t* y, const float* w_vis, int64
   // the buffers of one block span rows_per_range + 2 rows
   const int64_t row_bytes = (int64_t)seg.width * C * 2;
   const int64_t max_rows = (kRowsSpanMax / row_bytes - 2) / TR * TR;
-  if (max_rows < TR) return hipErrorInvalidValue;
+  if (max_rows < TR) return false;
   if (rows_per_range > max_rows) rows_per_range = (int)max_rows;
-  n_rr = (seg.height + rows_per_range - 1) / rows_per_range;
-  const int64_t n_logical = per_range * n_rr;
-  if (n_logical <= 0) return hipSuccess;
-  if (n_logical > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  const int64_t grid = (n_logical + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_rows_kernel<TR, TW>), dim3((unsigned)grid), dim3(TW * 8), 0, stream, x, y, w_vis, Ttot, C,
-                     seg, n_slab, n_tw, n_rr, rows_per_range, (int)n_logical);
-  const hipError_t e = hipGetLastError();
-  return e != hipSuccess ? e : mark_after(marks, "conv_rows_kernel", stream);
+  ent.n_rr = (seg.height + rows_per_range - 1) / rows_per_range;
+  ent.rows_per_range = rows_per_range;
+  blocks = per_range * ent.n_rr;
+  return true;
+}
+
+template <int TR, int TW>
+hipError_t launch_rows_batch(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
+                             const Seg* segs, int n, hipStream_t stream, Marks* marks) {
+  for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
+    RowsBatch tb;
+    tb.n = std::min(kMaxBatch, n - i0);
+    tb.n_slab = (int)(C / 64);
+    tb.pad = 0;
+    int64_t total = 0;
+    for (int i = 0; i < tb.n; ++i) {
+      int64_t blocks = 0;
+      if (!rows_entry<TR, TW>(segs[i0 + i], B, C, tb.e[i], blocks)) return hipErrorInvalidValue;
+      tb.e[i].blk0 = (int32_t)total;
+      total += blocks;
+      if (total > (int64_t(1) << 30)) return hipErrorInvalidValue;
+    }
+    if (total == 0) continue;
+    tb.n_logical = (int)total;
+    const int64_t grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL((conv_rows_kernel<TR, TW>), dim3((unsigned)grid), dim3(TW * 8), 0, stream, x, y, w_vis, Ttot,
+                       C, tb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const hipError_t me = mark_after(marks, "conv_rows_kernel", stream);
+    if (me != hipSuccess) return me;
+  }
+  return hipSuccess;
+}
+
+template <typename T>
+hipError_t launch_text_batch(const T* x, T* y, const float* w_text, int64_t B, int64_t Ttot, int64_t C,
+                             const Seg* segs, int n, hipStream_t stream, Marks* marks) {
+  for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
+    TextBatch tb;
+    tb.n = std::min(kMaxBatch, n - i0);
+    tb.n_cg = (int)((C / 8 + 63) / 64);
+    tb.pad = 0;
+    int64_t total = 0;
+    for (int i = 0; i < tb.n; ++i) {
+      const Seg& sg = segs[i0 + i];
+      const int64_t runs = (sg.length + kTextRun - 1) / kTextRun;
+      TextEntry& e = tb.e[i];
+      e.seg = sg;
+      e.n_run4 = (int32_t)((runs + 3) / 4);
+      e.blk0 = (int32_t)total;
+      e.pad0 = e.pad1 = 0;
+      total += (int64_t)tb.n_cg * e.n_run4 * B;
+      if (total > 0x7fffff00) return hipErrorInvalidValue;
+    }
+    if (total == 0) continue;
+    tb.n_logical = (int)total;
+    hipLaunchKernelGGL(conv_text_kernel<T>, dim3((unsigned)total), dim3(256), 0, stream, x, y, w_text, Ttot, C, tb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const hipError_t me = mark_after(marks, "conv_text_kernel", stream);
+    if (me != hipSuccess) return me;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -547,23 +647,18 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
   if (tiled) {
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     uint16_t* ys = static_cast<uint16_t*>(y);
-    if (seg.frames == 1 && rows_fit<4, 32>(seg, C)) return launch_rows<4, 32>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
+    if (seg.frames == 1 && rows_fit<4, 32>(seg, C))
+      return launch_rows_batch<4, 32>(xs, ys, w_vis, B, Ttot, C, &seg, 1, stream, marks);
     if ((int64_t)seg.height * seg.width * C * 2 <= (int64_t)kOutside - 64)
       return launch_tile<3, 4, 4, 16>(xs, ys, w_vis, B, Ttot, C, seg, stream, marks);
   }
   if (B > 65535) return hipErrorInvalidValue;
   if (seg.kind == SEG_TEXT) {
-    const int64_t runs = (seg.length + kTextRun - 1) / kTextRun;
-    const dim3 tgrid((unsigned)((C / 8 + 63) / 64), (unsigned)((runs + 3) / 4), (unsigned)B);
-    if (bf16) {
-      hipLaunchKernelGGL(conv_text_kernel<uint16_t>, tgrid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
-                         static_cast<uint16_t*>(y), w_text, Ttot, C, seg);
-    } else {
-      hipLaunchKernelGGL(conv_text_kernel<float>, tgrid, dim3(256), 0, stream, static_cast<const float*>(x),
-                         static_cast<float*>(y), w_text, Ttot, C, seg);
-    }
-    const hipError_t e = hipGetLastError();
-    return e != hipSuccess ? e : mark_after(marks, "conv_text_kernel", stream);
+    if (bf16)
+      return launch_text_batch<uint16_t>(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), w_text, B, Ttot,
+                                         C, &seg, 1, stream, marks);
+    return launch_text_batch<float>(static_cast<const float*>(x), static_cast<float*>(y), w_text, B, Ttot, C, &seg, 1,
+                                    stream, marks);
   }
   const dim3 grid((unsigned)((C / 8 + 63) / 64), (unsigned)((seg.length + 3) / 4), (unsigned)B);
   if (grid.y > 0x7fffffffu) return hipErrorInvalidValue;
@@ -576,6 +671,41 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t Ttot, 
   }
   const hipError_t e = hipGetLastError();
   return e != hipSuccess ? e : mark_after(marks, "conv_gather_kernel", stream);
+}
+
+hipError_t launch_conv(const void* x, void* y, int64_t B, int64_t Ttot, int64_t C, bool bf16, const float* w_text,
+                       const float* w_vis, const Seg* segs, int nseg, hipStream_t stream, Marks* marks) {
+  if (B == 0) return hipSuccess;
+  // text segments: one batched launch; image grids that the rows kernel takes: another;
+  // every other segment (video, fp32 or oversized grids) on its own
+  std::vector<Seg> text, rows, rest;
+  const bool tiled_ok = bf16 && C % 64 == 0;
+  for (int i = 0; i < nseg; ++i) {
+    const Seg& sg = segs[i];
+    if (sg.length == 0) continue;
+    if (sg.kind == SEG_TEXT) text.push_back(sg);
+    else if (tiled_ok && sg.frames == 1 && rows_fit<4, 32>(sg, C)) rows.push_back(sg);
+    else rest.push_back(sg);
+  }
+  hipError_t e = hipSuccess;
+  if (!text.empty()) {
+    if (B > 65535) return hipErrorInvalidValue;
+    e = bf16 ? launch_text_batch<uint16_t>(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), w_text, B,
+                                           Ttot, C, text.data(), (int)text.size(), stream, marks)
+             : launch_text_batch<float>(static_cast<const float*>(x), static_cast<float*>(y), w_text, B, Ttot, C,
+                                        text.data(), (int)text.size(), stream, marks);
+    if (e != hipSuccess) return e;
+  }
+  if (!rows.empty()) {
+    e = launch_rows_batch<4, 32>(static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), w_vis, B, Ttot, C,
+                                 rows.data(), (int)rows.size(), stream, marks);
+    if (e != hipSuccess) return e;
+  }
+  for (const Seg& sg : rest) {
+    e = launch_conv_segment(x, y, B, Ttot, C, bf16, w_text, w_vis, sg, false, stream, marks);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream) {

@@ -40,6 +40,23 @@ def test_small_inputs_deterministic_and_shaped():
 
 def test_workload_sizes():
     T = [w.T for w in wl.WORKLOADS]
-    assert T == [256, 4352, 65792, 37888, 255406]
+    assert T == [256, 4352, 65792, 37888, 255406, 62796]
     assert wl.WORKLOADS[3].B == 2 and wl.WORKLOADS[3].s0_std == 0.1
     assert wl.WORKLOADS[0].dtype == "f32" and wl.WORKLOADS[0].d == 32
+
+
+def test_packed_workload_layout():
+    """The packed row: 40 samples, each a text segment then an image grid, the sample offsets
+    on the text starts, segments tiling the row."""
+    w = wl.WORKLOADS[5]
+    cu = w.samples
+    assert len(cu) == 41 and cu[0] == 0 and cu[-1] == w.T
+    segs = w.segments
+    assert len(segs) == 80
+    for n in range(40):
+        t, g = segs[2 * n], segs[2 * n + 1]
+        assert t.kind == wl.TEXT and t.start == cu[n] and 32 <= t.length <= 300
+        assert g.kind == wl.IMAGE and g.start == t.start + t.length and g.start + g.length == cu[n + 1]
+        assert g.height == g.width and g.height in (16, 32, 64)
+    sides = [segs[2 * n + 1].height for n in range(8)]
+    assert sides == [16, 16, 16, 16, 32, 32, 64, 64]                 # 4:2:2 per group of eight

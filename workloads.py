@@ -5,13 +5,16 @@ none of the method's arithmetic: no convolution, no recurrence. Both the CPU
 oracle (through the tests and the bench) and the HIP library consume what it
 returns, so the two sides always see bit-identical inputs.
 
-Five workloads, each named by what it is:
+Six workloads, each named by what it is:
 
 * ``tiny_text_fp32``   B=1, H=2,  d=32,  T=256 text tokens, fp32.
 * ``image_1024``       B=1, H=16, d=128, 256 text + 64x64 image grid (4,352 tokens), bf16.
 * ``image_4096``       B=1, H=16, d=128, 256 text + 256x256 image grid (65,792 tokens), bf16.
 * ``video_5s``         B=2, H=16, d=128, 256 text + 21x32x56 video grid (37,888 tokens), bf16, S0 != 0.
 * ``video_30s``        B=1, H=16, d=128, 256 text + 126x45x45 video grid (255,406 tokens), bf16.
+* ``packed_mixed``     one row of 40 packed samples, H=16, d=128, bf16: the 256^2, 512^2 and
+  1024^2 image buckets at 4:2:2 (16x16, 32x32 and 64x64 grids), each after its own text
+  prompt of 32..300 tokens (62,796 tokens in all); the state restarts at every sample.
 
 Grid sizes follow the packing the Chimera pages describe (page 1, section 3.2
 and Eq. 12): text tokens first, then visual tokens in time-first raster order.
@@ -68,6 +71,7 @@ class Workload:
     log_alpha_scale: float
     s0_std: Optional[float]
     chunk: int = 64
+    samples: Optional[tuple] = None   # packed sample offsets (N + 1, from 0 to T), or None
 
     @property
     def T(self) -> int:
@@ -86,12 +90,32 @@ def text_then_grid(n_text: int, frames: int, height: int, width: int) -> tuple:
     return tuple(segs)
 
 
+def packed_samples(groups: int = 5, seed: int = 5) -> tuple:
+    """Segments and sample offsets of a row of packed image samples: per group of eight, four
+    16x16, two 32x32 and two 64x64 grids (the 256^2 / 512^2 / 1024^2 buckets at 4:2:2 after
+    16x16 patches), each after a text prompt of 32..300 tokens drawn from its own stream."""
+    rng = np.random.default_rng(seed + 2000)
+    sides = [16, 16, 16, 16, 32, 32, 64, 64]
+    segs, cu, off = [], [0], 0
+    for _ in range(groups):
+        for side in sides:
+            n_text = int(rng.integers(32, 301))
+            segs.append(Segment(TEXT, off, n_text))
+            segs.append(Segment(IMAGE, off + n_text, side * side, 1, side, side))
+            off += n_text + side * side
+            cu.append(off)
+    return tuple(segs), tuple(cu)
+
+
+_PACKED_SEGS, _PACKED_CU = packed_samples()
+
 WORKLOADS: List[Workload] = [
     Workload(0, "tiny_text_fp32", 1, 2, 32, "f32", (Segment(TEXT, 0, 256),), 1.0, None),
     Workload(1, "image_1024", 1, 16, 128, "bf16", text_then_grid(256, 1, 64, 64), 0.05, None),
     Workload(2, "image_4096", 1, 16, 128, "bf16", text_then_grid(256, 1, 256, 256), 0.05, None),
     Workload(3, "video_5s", 2, 16, 128, "bf16", text_then_grid(256, 21, 32, 56), 0.05, 0.1),
     Workload(4, "video_30s", 1, 16, 128, "bf16", text_then_grid(256, 126, 45, 45), 0.05, None),
+    Workload(5, "packed_mixed", 1, 16, 128, "bf16", _PACKED_SEGS, 0.05, None, samples=_PACKED_CU),
 ]
 
 
