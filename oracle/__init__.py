@@ -23,6 +23,9 @@ pages (arXiv 2607.28611):
   every sample boundary (page 1, section 3.3).
 * ``gated_rmsnorm_ref`` -- Sigmoid(gate) times the per-head RMSNorm of the
   readout, the rest of Eq. 15 before the output projection (page 1, section 3.3).
+* ``backward``        -- gradients of the conv and of the recurrence (with the L2
+  normalisation), as torch fp64 autograd of the same definitions
+  (``conv_backward_ref``, ``kda_backward_ref``); import ``oracle.backward``.
 * ``round_bf16_ref``  -- rounding to the bf16 output dtype (round to nearest,
   ties to even), used where a path stores a bf16 intermediate.
 
