@@ -21,6 +21,10 @@ Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 image_1024, video_5s, video_30s) are measured the same way with --workload.
 --gated times the KDA call with the output gate and norm of Eq. 15
 (chimera_kda_fwd_gated: Sigmoid(gate) * RMSNorm(o), a synthetic gate input).
+--backward times a training step instead: the two forward calls, then
+chimera_kda_bwd (writing dq, dk, dv straight into one fused q|k|v gradient) and
+chimera_mshortconv_bwd on it, against a synthetic dL/do; each call is bracketed
+by HIP events on the stream.
 
 Two helper modes turn rocprofv3 output into the summaries kept with the code:
   python bench.py --summarize-stats <kernel_stats.csv>
@@ -36,6 +40,8 @@ import os
 import platform
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -86,6 +92,8 @@ def _args():
                     help="synthetic workload (name or index); the metric is quoted on image_4096")
     ap.add_argument("--gated", action="store_true",
                     help="KDA with the output gate and norm of Eq. 15 (Sigmoid(gate) * RMSNorm(o))")
+    ap.add_argument("--backward", action="store_true",
+                    help="a training step: forward, then the KDA and conv backward (gradients of a synthetic dL/do)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=20736,
                     help="tokens per sequence in the oracle's timed sample (text + whole grid rows/frames)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
@@ -279,6 +287,100 @@ def _cpu_baseline(inp, w, budget: int, gate=None):
                       f"{platform.processor() or platform.machine()}, BLAS limited to 1 thread"}
 
 
+def bench_backward(args, w):
+    """One training step on the workload: conv fwd, KDA fwd, KDA bwd (into a fused q|k|v gradient),
+    conv bwd. Call-level timing with HIP events on the stream; the oracle baseline times the fp64
+    autograd backward on a bounded sample."""
+    import torch
+    import workloads as wl
+    import linear_attention_recurrence_mshortconv_amd as chm
+    assert not w.samples, "the backward runs on batched (not packed) workloads"
+    B, T, H, d = w.B, w.T, w.H, w.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    to_dev = lambda a: torch.from_numpy(a).to(tdt).to(dev)
+    x, alpha, beta = to_dev(inp["x"]), to_dev(inp["alpha"]), to_dev(inp["beta"])
+    S0 = None if inp["S0"] is None else torch.from_numpy(inp["S0"]).to(dev)
+    wt, wv = torch.from_numpy(inp["w_text"]).to(dev), torch.from_numpy(inp["w_vis"]).to(dev)
+    rng = np.random.default_rng(w.index + 3000)
+    do = to_dev(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    segs = w.segments
+    y, dy, dx = torch.empty_like(x), torch.zeros_like(x), torch.empty_like(x)
+    q, k, v = chm.split_qkv(y, H, d)
+    gq, gk, gv = chm.split_qkv(dy, H, d)
+    o = torch.empty(B, T, H, d, dtype=tdt, device=dev)
+    s_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    dcode = chm.BF16 if w.dtype == "bf16" else chm.F32
+    ws = torch.empty(max(chm.kda_workspace_size(B, T, H, d, d, dcode, chm.KDA_L2NORM_QK), 1), dtype=torch.uint8,
+                     device=dev)
+    wsb = torch.empty(max(int(chm.lib().chimera_kda_bwd_workspace_size(B, T, H, d, d, dcode, chm.KDA_L2NORM_QK)), 1),
+                      dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    calls = ["conv_fwd", "kda_fwd", "kda_bwd", "conv_bwd"]
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        mark(0)
+        chm.mshortconv_fwd(x, wt, wv, segs, out=y)
+        mark(1)
+        chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, state_out=s_final)
+        mark(2)
+        chm.kda_bwd(q, k, v, alpha, beta, S0, do, None, grads=(gq, gk, gv), workspace=wsb)
+        mark(3)
+        chm.mshortconv_bwd(x, dy, wt, wv, segs, dx=dx)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {c: sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / args.steps for i, c in enumerate(calls)}
+    ms_step = sum(ev[0].elapsed_time(ev[4]) for ev in evs) / args.steps
+    e = 2 if w.dtype == "bf16" else 4
+    # the KDA backward's minimal traffic per token-head: q, k, v, alpha, beta, dL/do in, dq, dk, dv, dalpha,
+    # dbeta out
+    bwd_bytes = B * T * H * ((4 * d + 1 + d) * e + (4 * d + 1) * e)
+    ms_bwd = per["kda_bwd"]
+    out = {
+        "metric": "KDA+mShortConv training step (fwd + bwd) tokens/sec/GPU",
+        "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": f"synthetic (seeded; {w.dtype} inputs and dL/do; fp32 state)",
+        "config": {"workload": f"{w.name}: {T} tokens per sequence, B={B}, H={H}, d={d}; forward (conv, chunked KDA), "
+                               f"then the checkpointed token-by-token KDA backward and the conv backward",
+                   "tokens_per_step": B * T, "calls_ms": per, "wall_s_timed": wall},
+        "roofline": {"bound": "hbm", "kernel": "kda_bwd (call: checkpoint forward, reverse pass, slice sums)",
+                     "achieved": bwd_bytes / (ms_bwd * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": bwd_bytes / (ms_bwd * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "ms_per_launch": ms_bwd, "algorithmic_bytes_per_launch": bwd_bytes,
+                     "recipe": f"q, k, v, alpha, beta, dL/do in and dq, dk, dv, dalpha, dbeta out: "
+                               f"{(9 * d + 2) * e} B per token-head"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle.backward import kda_backward_ref
+        n = min(T, 64)
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            parts = inp["x"][:, :n].reshape(B, n, 3, H, d)
+            kda_backward_ref(parts[:, :, 0], parts[:, :, 1], parts[:, :, 2], inp["alpha"][:, :n], inp["beta"][:, :n],
+                             None if S0 is None else inp["S0"], do[:, :n].float().cpu().numpy())
+            dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": B * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"fp64 autograd KDA backward (with its forward) over the first {n} tokens, "
+                                         f"all {H} heads; {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = _args()
     if args.summarize_stats:
@@ -298,6 +400,9 @@ def main():
     chm.lib()
     by_name = {w.name: w for w in wl.WORKLOADS}
     w = by_name[args.workload] if args.workload in by_name else wl.WORKLOADS[int(args.workload)]
+    if args.backward:
+        bench_backward(args, w)
+        return
     B, T, H, d = w.B, w.T, w.H, w.d
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -303,6 +303,56 @@ chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const 
                                             size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks,
                                             const char** names, int32_t capacity, int32_t* used);
 
+/*
+ * Backward pass (the gradients of the two forward calls), fp32 state and accumulation.
+ *
+ * chimera_kda_bwd -- gradients of (o, S_final) = chimera_kda_fwd(q, k, v, alpha, beta, S0)
+ * (Eq. 14 and the readout o_t = S_t^T q_t, with the per-head L2 normalisation of q and k
+ * when CHIMERA_KDA_L2NORM_QK is set) against dout = dL/do and dS_final = dL/dS_final:
+ *
+ *   q, k, v, qkv_stride, alpha, beta, S0   the forward's inputs, as for chimera_kda_fwd
+ *   dout      device [B][T][H][dv], dtype dt
+ *   dS_final  device fp32 [B][H][dk][dv], or NULL for zero
+ *   dq, dk    device, written, dtype dt, at the layout of q and k (token stride qkv_stride:
+ *             views into one fused q|k|v gradient are accepted)
+ *   dv        device, written, at the layout of v
+ *   dalpha    device [B][T][H][dk], written, dtype dt
+ *   dbeta     device [B][T][H], written, dtype dt
+ *   dS0       device fp32 [B][H][dk][dv], written, or NULL
+ *   workspace at least chimera_kda_bwd_workspace_size(...) bytes: the state before every
+ *             16th token (from a forward pass inside the call) and per-slice partial sums
+ *
+ * dk <= 128 (CHIMERA_ERR_UNSUPPORTED above). The recurrence runs token by token in fp32
+ * (a checkpointed reverse pass); the flags that choose forward kernels are ignored.
+ * Asynchronous on `stream`; the outputs must not alias the inputs.
+ */
+size_t chimera_kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                                      uint32_t flags);
+chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
+                               const void* beta, const float* S0, const void* dout, const float* dS_final, void* dq,
+                               void* dk_out, void* dv_out, void* dalpha, void* dbeta, float* dS0, int64_t B,
+                               int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * chimera_mshortconv_bwd -- gradients of y = chimera_mshortconv_fwd(x) against dy:
+ *
+ *   x, dy     device [B][T][C], dtype dt
+ *   dx        device [B][T][C], written, dtype dt: dx[s, c] = sum of w[c, tap] dy[p, c] over
+ *             the (p, tap) whose tap reads token s (fp32 accumulation, one rounding)
+ *   dw_text   device fp32 [C][4], written: sum over batch items and text tokens p of
+ *             x[src(p, tap), c] dy[p, c]
+ *   dw_vis    device fp32 [C][27], written, likewise over the visual tokens
+ *   w_text, w_vis, segs, nseg   as for the forward
+ *
+ * The weight gradients are summed with atomic adds (the order, and so the last bits, may
+ * differ from run to run). Asynchronous on `stream`; dx must not alias x or dy.
+ */
+chimera_status chimera_mshortconv_bwd(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis,
+                                      int64_t B, int64_t T, int64_t C, chimera_dtype dt, const float* w_text,
+                                      const float* w_vis, const chimera_segment* segs, int32_t nseg,
+                                      hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* chimera_status_string(chimera_status s);
 

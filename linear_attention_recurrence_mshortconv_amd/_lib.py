@@ -75,6 +75,13 @@ def lib() -> ctypes.CDLL:
                                         i64, i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
     L.chimera_kda_fwd_gated_timed.restype = ctypes.c_int
     L.chimera_kda_fwd_gated_timed.argtypes = L.chimera_kda_fwd_gated.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
+    L.chimera_kda_bwd_workspace_size.restype = sz
+    L.chimera_kda_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, u32]
+    L.chimera_kda_bwd.restype = ctypes.c_int
+    L.chimera_kda_bwd.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  i64, i64, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.chimera_mshortconv_bwd.restype = ctypes.c_int
+    L.chimera_mshortconv_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, seg_p, i32, vp]
     L.chimera_kda_varlen_workspace_size.restype = sz
     L.chimera_kda_varlen_workspace_size.argtypes = [vp, i32, i64, i64, i64, ctypes.c_int, u32]
     L.chimera_kda_fwd_varlen.restype = ctypes.c_int
@@ -329,6 +336,53 @@ def kda_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, l2norm: bool = 
                lib().chimera_kda_fwd_varlen_timed(*args, marks.handles, marks.names, marks.capacity,
                                                   ctypes.byref(marks.used)))
     return o, Sf
+
+
+def kda_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, l2norm: bool = True, grads=None, workspace=None):
+    """Gradients of kda_fwd (chimera_kda_bwd). Inputs as for kda_fwd; dout [B, T, H, dv]
+    (input dtype), dS_final fp32 [B, H, dk, dv] or None. `grads` = (dq, dk, dv) tensors with
+    the layout of q, k, v (views into one fused gradient are accepted), else fresh tensors.
+    Returns dict dq, dk, dv, dalpha, dbeta, dS0."""
+    import torch
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    stride = _token_view_stride(q, B, T, H, dk)
+    assert _token_view_stride(k, B, T, H, dk) == stride and _token_view_stride(v, B, T, H, dv) == stride
+    dt = _dtype_code(k)
+    if grads is None:
+        assert stride == H * dk and stride == H * dv, "strided (fused) inputs: pass `grads` with their layout"
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dkk, dvv = grads
+    for g, t in zip(grads, (q, k, v)):
+        assert g.shape == t.shape and g.stride() == t.stride()
+    dalpha = torch.empty_like(alpha)
+    dbeta = torch.empty_like(beta)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=k.device)
+    need = int(lib().chimera_kda_bwd_workspace_size(B, T, H, dk, dv, dt, KDA_L2NORM_QK if l2norm else 0))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("chimera_kda_bwd", lib().chimera_kda_bwd(
+        _ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dout), _ptr(dS_final),
+        _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), B, T, H, dk, dv, dt,
+        KDA_L2NORM_QK if l2norm else 0, _ptr(workspace), wbytes, _stream(k)))
+    return {"dq": dq, "dk": dkk, "dv": dvv, "dalpha": dalpha, "dbeta": dbeta, "dS0": dS0}
+
+
+def mshortconv_bwd(x, dy, w_text, w_vis, segments: Sequence, dx=None):
+    """Gradients of mshortconv_fwd (chimera_mshortconv_bwd): returns (dx, dw_text, dw_vis)."""
+    import torch
+    B, T, C = x.shape
+    w_text = w_text.to(device=x.device, dtype=torch.float32).contiguous()
+    w_vis = w_vis.to(device=x.device, dtype=torch.float32).contiguous()
+    dx = torch.empty_like(x) if dx is None else dx
+    dwt = torch.empty((C, TEXT_TAPS), dtype=torch.float32, device=x.device)
+    dwv = torch.empty((C, VIS_TAPS), dtype=torch.float32, device=x.device)
+    segs = segment_array(segments)
+    _check("chimera_mshortconv_bwd", lib().chimera_mshortconv_bwd(
+        _ptr(x), _ptr(dy), _ptr(dx), _ptr(dwt), _ptr(dwv), B, T, C, _dtype_code(x), _ptr(w_text), _ptr(w_vis),
+        segs, len(segments), _stream(x)))
+    return dx, dwt, dwv
 
 
 def split_qkv(y, H: int, d: int):

@@ -384,4 +384,61 @@ chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const 
   return st;
 }
 
+size_t chimera_kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                                      uint32_t flags) {
+  (void)flags;
+  if (!kda_sizes_ok(B, T, H, dk, dv) || dk > 128 || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
+  return chm::kda_bwd_workspace(B, T, H, dk, dv);
+}
+
+chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
+                               const void* beta, const float* S0, const void* dout, const float* dS_final, void* dq,
+                               void* dk_out, void* dv_out, void* dalpha, void* dbeta, float* dS0, int64_t B,
+                               int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
+  if (!kda_sizes_ok(B, T, H, dk, dv)) return CHIMERA_ERR_SHAPE;
+  if (dk > 128) return CHIMERA_ERR_UNSUPPORTED;
+  if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL | CHIMERA_KDA_NO_SPLIT)) return CHIMERA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return CHIMERA_OK;
+  if (T > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || dout == nullptr ||
+        dq == nullptr || dk_out == nullptr || dv_out == nullptr || dalpha == nullptr || dbeta == nullptr)
+      return CHIMERA_ERR_NULL;
+    if (qkv_stride < H * dk || qkv_stride < H * dv) return CHIMERA_ERR_SHAPE;
+  }
+  const size_t need = chm::kda_bwd_workspace(B, T, H, dk, dv);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
+  chm::KdaArgs a{};
+  a.q = q; a.k = k; a.v = v; a.qkv_stride = qkv_stride; a.alpha = alpha; a.beta = beta;
+  a.S0 = S0; a.o = nullptr; a.S_final = nullptr;
+  a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
+  a.bf16 = dt == CHIMERA_BF16;
+  a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
+  const chm::KdaGrads g{dout, dS_final, dq, dk_out, dv_out, dalpha, dbeta, dS0};
+  return hip_status(chm::launch_kda_backward(a, g, workspace, stream));
+}
+
+chimera_status chimera_mshortconv_bwd(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis,
+                                      int64_t B, int64_t T, int64_t C, chimera_dtype dt, const float* w_text,
+                                      const float* w_vis, const chimera_segment* segs, int32_t nseg,
+                                      hipStream_t stream) {
+  if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
+  if (B < 0 || C < 0) return CHIMERA_ERR_SHAPE;
+  bool any_text, any_vis;
+  const chimera_status st = check_segments(segs, nseg, T, &any_text, &any_vis);
+  if (st != CHIMERA_OK) return st;
+  if (C % 8 != 0 || C > (int64_t(1) << 24)) return CHIMERA_ERR_SHAPE;
+  if (dw_text == nullptr || dw_vis == nullptr) return CHIMERA_ERR_NULL;
+  if (B > 0 && T > 0) {
+    if (x == nullptr || dy == nullptr || dx == nullptr) return CHIMERA_ERR_NULL;
+    if ((any_text && w_text == nullptr) || (any_vis && w_vis == nullptr)) return CHIMERA_ERR_NULL;
+    if (dx == x || dx == dy) return CHIMERA_ERR_UNSUPPORTED;
+  }
+  std::vector<Seg> sv((size_t)nseg);
+  for (int32_t i = 0; i < nseg; ++i) sv[(size_t)i] = to_seg(segs[i]);
+  return hip_status(chm::launch_conv_backward(x, dy, dx, dw_text, dw_vis, B, T, C, dt == CHIMERA_BF16, w_text,
+                                              w_vis, sv.data(), nseg, stream));
+}
+
 }  // extern "C"

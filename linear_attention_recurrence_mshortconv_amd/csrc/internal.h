@@ -67,9 +67,31 @@ struct KdaArgs {
 };
 
 // Token-by-token fp32 kernel: any dk, dv in 1..256 (with a gate: then the gate/norm kernel on o).
-hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr);
+// With ckpt: also the state before every 16th token, [B][H][ceil(T/16)][dk][dv] fp32 (o may be null).
+hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr, float* ckpt = nullptr);
 // o <- Sigmoid(gate) * RMSNorm(o) in place, one wave per (token, head): a.o, a.gate, a.norm_w.
 hipError_t launch_kda_gate_norm(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr);
+
+// ---- Backward ---------------------------------------------------------------------
+// Gradients of one KDA call (the inputs in KdaArgs): dout [B][T][H][dv] in; dq, dk, dv out
+// at the inputs' token stride, dalpha [B][T][H][dk], dbeta [B][T][H] (dtype), dS0 fp32.
+struct KdaGrads {
+  const void* dout;
+  const float* dS_final;   // or null (zero)
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dalpha;
+  void* dbeta;
+  float* dS0;              // or null
+};
+size_t kda_bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* workspace, hipStream_t stream,
+                               Marks* marks = nullptr);
+// dx (dtype, [B][T][C]) and dw_text [C][4], dw_vis [C][27] (fp32, written) of y = mShortConv(x) against dy.
+hipError_t launch_conv_backward(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis, int64_t B,
+                                int64_t T, int64_t C, bool bf16, const float* w_text, const float* w_vis,
+                                const Seg* segs, int nseg, hipStream_t stream, Marks* marks = nullptr);
 
 // Chunked MFMA path (bf16, dk = dv = 128). The sequences come as runs: `count` consecutive
 // sequences of `len` tokens from row `start` on, whose S0 / S_final entries start at `sidx0`.

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
                                                       const T* __restrict__ alpha, const T* __restrict__ beta,
                                                       const float* __restrict__ S0, T* __restrict__ o,
                                                       float* __restrict__ S_final, int64_t Tn, int64_t H, int dk,
-                                                      int dv, int l2norm) {
+                                                      int dv, int l2norm, float* __restrict__ ckpt) {
   constexpr int DKP = 16 * RPT;   // staged rows; rows past dk hold k = q = 0, alpha = 1
   __shared__ float sk[2][kTokBatch][DKP];
   __shared__ float sq[2][kTokBatch][DKP];
@@ -121,6 +121,12 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
     const int nt = (int)min<int64_t>(kTokBatch, Tn - t0);
     const bool more = t0 + kTokBatch < Tn;
     if (more) load(t0 + kTokBatch);                  // in flight during this batch
+    if (ckpt != nullptr && col_ok) {                 // the state before this batch (for the backward)
+      float* dst = ckpt + ((bh * ((Tn + kTokBatch - 1) / kTokBatch) + t0 / kTokBatch) * dk) * dv + col;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        if (rt + 16 * i < dk) dst[(int64_t)(rt + 16 * i) * dv] = s[i];
+    }
     for (int tt = 0; tt < nt; ++tt) {
       float pred = 0.f;
 #pragma unroll
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
         out = fmaf(s[i], sq[buf][tt][row], out);
       }
       out = sum16(out);
-      if (rt == 0 && col_ok) from_f32(o + ((b * Tn + t0 + tt) * H + h) * dv + col, out);
+      if (rt == 0 && col_ok && o != nullptr) from_f32(o + ((b * Tn + t0 + tt) * H + h) * dv + col, out);
     }
     if (more) stage(buf ^ 1);                        // the other buffer was last read a batch ago
     __syncthreads();
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(256) void kda_gate_norm_kernel(T* __restrict__ o, c
 }
 
 template <typename T>
-hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream) {
+hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, float* ckpt) {
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
@@ -198,15 +204,15 @@ hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream) {
   const dim3 g((unsigned)blocks), t(256);
   const int dk = (int)a.dk, dv = (int)a.dv, nrm = (int)a.l2norm;
   if (dk <= 16)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 1>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 1>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
   else if (dk <= 32)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 2>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 2>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
   else if (dk <= 64)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 4>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 4>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
   else if (dk <= 128)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 8>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 8>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
   else
-    hipLaunchKernelGGL((kda_seq_kernel<T, 16>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 16>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
   return hipGetLastError();
 }
 
@@ -228,13 +234,13 @@ hipError_t launch_kda_gate_norm(const KdaArgs& a, hipStream_t stream, Marks* mar
   return e != hipSuccess ? e : mark_after(marks, "kda_gate_norm_kernel", stream);
 }
 
-hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks) {
+hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks, float* ckpt) {
   if (a.B * a.H == 0) return hipSuccess;
   const int n_vs = (int)((a.dv + 15) / 16);
   const int64_t blocks = a.B * a.H * n_vs;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (a.T == 0 && a.S_final == nullptr) return hipSuccess;
-  hipError_t e = a.bf16 ? launch_seq<uint16_t>(a, blocks, stream) : launch_seq<float>(a, blocks, stream);
+  hipError_t e = a.bf16 ? launch_seq<uint16_t>(a, blocks, stream, ckpt) : launch_seq<float>(a, blocks, stream, ckpt);
   if (e == hipSuccess) e = mark_after(marks, "kda_seq_kernel", stream);
   if (e == hipSuccess && a.gate != nullptr) e = launch_kda_gate_norm(a, stream, marks);
   return e;

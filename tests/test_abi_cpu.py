@@ -196,6 +196,27 @@ def test_kda_varlen_argument_errors_and_workspace():
     assert timed(7) == 2 and used.value == 0                            # needs 2 * nseq + 4 = 8
 
 
+def test_backward_argument_errors():
+    """The backward entry points check their arguments before any launch (no kernel runs here)."""
+    L = chm.lib()
+    call = lambda **kw: L.chimera_kda_bwd(*[kw.get(n, d) for n, d in (
+        ("q", 1), ("k", 2), ("v", 3), ("stride", 256), ("a", 4), ("b", 5), ("S0", None), ("do", 6), ("dS", None),
+        ("dq", 7), ("dk", 8), ("dv", 9), ("da", 10), ("db", 11), ("dS0", None), ("B", 1), ("T", 8), ("H", 2),
+        ("dkk", 128), ("dvv", 128), ("dt", 1), ("flags", 1), ("ws", None), ("wsb", 0), ("stream", None))])
+    assert call(dt=7) == 3
+    assert call(dkk=256, stride=1024) == 5                              # the backward takes dk <= 128
+    assert call(do=None) == 1 and call(dq=None) == 1 and call(db=None) == 1
+    assert call(stride=100) == 2
+    assert call() == 6                                                  # workspace missing
+    assert call(B=0) == 0
+    n = int(L.chimera_kda_bwd_workspace_size(1, 64 * 20 + 3, 16, 128, 128, 1, 1))
+    assert n >= 4 * (16 * 81 * 128 * 128 + 8 * 1283 * 16 * (3 * 128 + 1))   # checkpoints + slice partials
+    arr = chm.segment_array([dict(kind=0, start=0, length=4)])
+    cb = lambda **kw: L.chimera_mshortconv_bwd(kw.get("x", 1), kw.get("dy", 2), kw.get("dx", 3), kw.get("dwt", 4),
+                                               kw.get("dwv", 5), 1, 4, kw.get("C", 8), 1, 6, 7, arr, 1, None)
+    assert cb(C=12) == 2 and cb(dwt=None) == 1 and cb(dx=None) == 1 and cb(dx=1) == 5
+
+
 def test_workspace_size_rules():
     n = chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
     assert n >= 0

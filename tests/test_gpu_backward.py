@@ -1,0 +1,141 @@
+"""GPU parity of the backward pass (chimera_kda_bwd, chimera_mshortconv_bwd) against the
+fp64 autograd oracle (oracle.backward)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle.backward import conv_backward_ref, kda_backward_ref
+from tests.gpu_util import assert_close, rel_l2, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+# bf16 storage of the inputs and of the gradients: each gradient tensor within rel-L2 2e-2 of
+# the fp64 gradient of the same (bf16-valued) inputs, and every element within 2% of the
+# tensor's largest magnitude (one bf16 rounding is 2^-9 relative; the rest is fp32 reduction
+# order over d and over the sequence)
+BF16_BWD_REL_L2 = 2e-2
+BF16_BWD_MAX_REL = 2e-2
+
+
+def _close_bf16(got, want, what):
+    r = rel_l2(got, want)
+    m = float(np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30))
+    assert r <= BF16_BWD_REL_L2 and m <= BF16_BWD_MAX_REL, f"{what}: rel-L2 {r:.3e}, max/max {m:.3e}"
+
+
+@pytest.fixture(scope="module")
+def chm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_recurrence_mshortconv_amd as m
+    m.lib()
+    return m
+
+
+def _case(rng, B, T, H, dk, dv, dtype):
+    rnd = (lambda a: wl.round_to_bf16(a.astype(np.float32))) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    q, k = rnd(rng.standard_normal((B, T, H, dk))), rnd(rng.standard_normal((B, T, H, dk)))
+    v = rnd(rng.standard_normal((B, T, H, dv)))
+    alpha = rnd(np.exp(-0.3 * np.logaddexp(0, rng.standard_normal((B, T, H, dk)))))
+    beta = rnd(1 / (1 + np.exp(-rng.standard_normal((B, T, H)))))
+    S0 = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    do = rnd(rng.standard_normal((B, T, H, dv)))
+    dS = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    return q, k, v, alpha, beta, S0, do, dS
+
+
+def _run(chm, dtype, q, k, v, alpha, beta, S0, do, dS):
+    import torch
+    dev = lambda a: to_device(a, dtype)
+    g = chm.kda_bwd(dev(q), dev(k), dev(v), dev(alpha), dev(beta), torch.from_numpy(S0).cuda(), dev(do),
+                    torch.from_numpy(dS).cuda())
+    return {n: to_host(t) for n, t in g.items()}
+
+
+def test_kda_bwd_fp32_odd_dims(chm):
+    """fp32, dk != dv (not multiples of 16), two batch items; q, k, v and their gradients are
+    views into fused tensors (the shared token stride)."""
+    import torch
+    rng = np.random.default_rng(120)
+    B, T, H, dk, dv = 2, 77, 3, 20, 37
+    q, k, v, alpha, beta, S0, do, dS = _case(rng, B, T, H, dk, dv, "f32")
+    W = H * (2 * dk + dv)
+    fused = torch.from_numpy(np.concatenate([q.reshape(B, T, -1), k.reshape(B, T, -1), v.reshape(B, T, -1)],
+                                            axis=-1)).cuda()
+    views = lambda t: (t[:, :, :H * dk].view(B, T, H, dk), t[:, :, H * dk:2 * H * dk].view(B, T, H, dk),
+                       t[:, :, 2 * H * dk:].view(B, T, H, dv))
+    gfused = torch.zeros(B, T, W, device="cuda")
+    dev = lambda a: torch.from_numpy(a).cuda()
+    g = chm.kda_bwd(*views(fused), dev(alpha), dev(beta), dev(S0), dev(do), dev(dS), grads=views(gfused))
+    got = {n: to_host(t) for n, t in g.items()}
+    ref = kda_backward_ref(q, k, v, alpha, beta, S0, do, dS)
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        assert_close(got[n], ref[n], "f32", n)
+
+
+@pytest.mark.parametrize("T", [1, 16, 300])
+def test_kda_bwd_bf16_d128(chm, T):
+    rng = np.random.default_rng(121 + T)
+    args = _case(rng, 1, T, 2, 128, 128, "bf16")
+    got = _run(chm, "bf16", *args)
+    ref = kda_backward_ref(*args)
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        _close_bf16(got[n], ref[n], f"{n} T={T}")
+
+
+def test_conv_bwd_fp32_mixed_layout(chm):
+    import torch
+    S = wl.Segment
+    segs = (S(wl.TEXT, 0, 9), S(wl.IMAGE, 9, 7 * 6, 1, 7, 6), S(wl.TEXT, 51, 3), S(wl.VIDEO, 54, 3 * 4 * 5, 3, 4, 5))
+    T, C = 114, 24
+    rng = np.random.default_rng(122)
+    x = rng.standard_normal((2, T, C)).astype(np.float32)
+    dy = rng.standard_normal((2, T, C)).astype(np.float32)
+    wt = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    wv = (0.5 * rng.standard_normal((C, 27))).astype(np.float32)
+    dx, dwt, dwv = chm.mshortconv_bwd(to_device(x, "f32"), to_device(dy, "f32"), torch.from_numpy(wt),
+                                      torch.from_numpy(wv), segs)
+    ref = conv_backward_ref(x, wt, wv, segs, dy)
+    np.testing.assert_allclose(to_host(dx), ref["dx"], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(to_host(dwt), ref["dw_text"], rtol=1e-5, atol=1e-4)
+    np.testing.assert_allclose(to_host(dwv), ref["dw_vis"], rtol=1e-5, atol=1e-4)
+
+
+def test_pipeline_backward_bf16(chm):
+    """conv -> KDA forward, then the KDA gradients written straight into one fused q|k|v
+    gradient and the conv's backward on it, against the oracle's chain of the two."""
+    import torch
+    S = wl.Segment
+    H, d = 2, 128
+    segs = (S(wl.TEXT, 0, 30), S(wl.IMAGE, 30, 12 * 11, 1, 12, 11))
+    T, C = 162, 3 * H * d
+    rng = np.random.default_rng(123)
+    x = wl.round_to_bf16(rng.standard_normal((1, T, C)).astype(np.float32))
+    wt = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    wv = (0.5 * rng.standard_normal((C, 27))).astype(np.float32)
+    alpha = wl.round_to_bf16(np.exp(-0.05 * np.logaddexp(0, rng.standard_normal((1, T, H, d)))).astype(np.float32))
+    beta = wl.round_to_bf16((1 / (1 + np.exp(-rng.standard_normal((1, T, H))))).astype(np.float32))
+    do = wl.round_to_bf16(rng.standard_normal((1, T, H, d)).astype(np.float32))
+    xd = to_device(x, "bf16")
+    y = chm.mshortconv_fwd(xd, torch.from_numpy(wt), torch.from_numpy(wv), segs)
+    q, k, v = chm.split_qkv(y, H, d)
+    dy = torch.zeros_like(y)
+    gq, gk, gv = chm.split_qkv(dy, H, d)
+    g = chm.kda_bwd(q, k, v, to_device(alpha, "bf16"), to_device(beta, "bf16"), None, to_device(do, "bf16"),
+                    grads=(gq, gk, gv))
+    dx, dwt, dwv = chm.mshortconv_bwd(xd, dy, torch.from_numpy(wt), torch.from_numpy(wv), segs)
+    # oracle chain, from the inputs alone: the conv output rounded once to bf16, the KDA
+    # gradients in fp64, then the conv's backward of those
+    from oracle import conv_ref, round_bf16_ref
+    y_ref = round_bf16_ref(conv_ref(x, wt, wv, segs))
+    parts = y_ref.reshape(1, T, 3, H, d)
+    ref = kda_backward_ref(parts[:, :, 0], parts[:, :, 1], parts[:, :, 2], alpha, beta, None, do)
+    _close_bf16(to_host(g["dalpha"]), ref["dalpha"], "dalpha")
+    _close_bf16(to_host(g["dbeta"]), ref["dbeta"], "dbeta")
+    dy_ref = np.concatenate([ref[n].reshape(1, T, H * d) for n in ("dq", "dk", "dv")], axis=-1)
+    _close_bf16(to_host(dy), dy_ref, "dy")
+    cref = conv_backward_ref(x, wt, wv, segs, dy_ref)
+    _close_bf16(to_host(dx), cref["dx"], "dx")
+    _close_bf16(to_host(dwt), cref["dw_text"], "dw_text")
+    _close_bf16(to_host(dwv), cref["dw_vis"], "dw_vis")
