@@ -41,6 +41,12 @@ hipError_t launch_conv_segment(const void* x, void* y, int64_t B, int64_t T, int
 hipError_t launch_conv(const void* x, void* y, int64_t B, int64_t T, int64_t C, bool bf16, const float* w_text,
                        const float* w_vis, const Seg* segs, int nseg, hipStream_t stream, Marks* marks = nullptr);
 
+// The image conv's adjoint (dx from dy) on the rows kernel with mirrored taps, for the image
+// segments that conv_rows_adjoint_ok accepts (bf16, one frame, C a multiple of 64).
+bool conv_rows_adjoint_ok(const Seg& seg, int64_t C, bool bf16);
+hipError_t launch_conv_rows_adjoint(const void* dy, void* dx, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
+                                    const Seg* segs, int n, hipStream_t stream, Marks* marks = nullptr);
+
 // Device-side neighbour table [T][27] for one segment (the conv kernels' arithmetic).
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream);
 
@@ -66,9 +72,24 @@ struct KdaArgs {
   float norm_eps = 0.f;
 };
 
+// Optional cut of every sequence into nseg segments of len tokens (a multiple of 16; the last
+// one shorter), run by separate blocks, for the backward's passes. Segment p starts from S0
+// (p = 0) or from Sseg[b][h][p] (p > 0; null = zero), or from zero (zero_start), or from the
+// identity (identity: dv == dk, v taken as zero, so the end state is the segment's transition
+// product); Send[b][h][p] receives each segment's end state when not null.
+struct SeqSegs {
+  int64_t len = 0;
+  int nseg = 1;
+  const float* Sseg = nullptr;
+  float* Send = nullptr;
+  int zero_start = 0;
+  int identity = 0;
+};
 // Token-by-token fp32 kernel: any dk, dv in 1..256 (with a gate: then the gate/norm kernel on o).
 // With ckpt: also the state before every 16th token, [B][H][ceil(T/16)][dk][dv] fp32 (o may be null).
-hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr, float* ckpt = nullptr);
+// q, v and o may be null when no output is wanted (v null = zero values).
+hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr, float* ckpt = nullptr,
+                                 const SeqSegs* segs = nullptr);
 // o <- Sigmoid(gate) * RMSNorm(o) in place, one wave per (token, head): a.o, a.gate, a.norm_w.
 hipError_t launch_kda_gate_norm(const KdaArgs& a, hipStream_t stream, Marks* marks = nullptr);
 

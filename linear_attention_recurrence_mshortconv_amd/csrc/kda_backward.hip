@@ -25,6 +25,8 @@
 // gives dx[s, c] = sum over (p, tap) with src(p, tap) = s of w[c, tap] dy[p, c] (the
 // adjoint gather: p is s moved back by the tap's offset, inside the same segment) and
 // dw[c, tap] = sum_p x[src(p, tap), c] dy[p, c] (summed over tokens and batch items).
+#include <vector>
+
 #include "dtypes.h"
 #include "internal.h"
 
@@ -32,7 +34,7 @@ namespace chm {
 namespace {
 
 constexpr int kCk = 16;   // tokens per checkpoint (the forward kernel's token batch)
-constexpr int kHalf = 8;  // states recomputed and kept at a time
+constexpr int kHalf = 4;  // states recomputed and kept at a time
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -54,27 +56,96 @@ __device__ __forceinline__ float sum_cols4(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
+
+// Stages tokens tok0 .. tok0 + nt - 1 (rows of the [B*T] token axis) of one head in LDS: thread
+// (colid, rt) loads token colid, rows rt + 16 i of q and k (L2-normalised) and alpha, and
+// column vs * 16 + rt of v (when sv is given) and of dout; tokens past nt read as q = k = 0,
+// alpha = 1, beta = 0.
+template <typename T, int RPT>
+__device__ __forceinline__ void stage_tokens(const T* __restrict__ q, const T* __restrict__ k,
+                                             const T* __restrict__ v, int64_t stride, const T* __restrict__ alpha,
+                                             const T* __restrict__ beta, const T* __restrict__ dout, int64_t tok0,
+                                             int nt, int64_t h, int64_t H, int dk, int dv, int vs, int l2norm,
+                                             float (&sq)[kCk][16 * RPT], float (&sk)[kCk][16 * RPT],
+                                             float (&sa)[kCk][16 * RPT], float (*sv)[16], float (&sdo)[kCk][16],
+                                             float (&sb)[kCk]) {
+  const int colid = threadIdx.x >> 4, rt = threadIdx.x & 15;
+  const bool tok_ok = colid < nt;
+  const int64_t tok = tok0 + colid;
+  float rq[RPT], rk[RPT], ssq = 0.f, ssk = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rt + 16 * i;
+    const bool ok = tok_ok && row < dk;
+    rq[i] = ok ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
+    rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
+    sa[colid][row] = ok ? to_f32(alpha[(tok * H + h) * dk + row]) : 1.f;
+    ssq = fmaf(rq[i], rq[i], ssq);
+    ssk = fmaf(rk[i], rk[i], ssk);
+  }
+  const float nq = l2norm ? 1.f / sqrtf(sum16(ssq) + 1e-6f) : 1.f;
+  const float nk = l2norm ? 1.f / sqrtf(sum16(ssk) + 1e-6f) : 1.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    sq[colid][rt + 16 * i] = rq[i] * nq;
+    sk[colid][rt + 16 * i] = rk[i] * nk;
+  }
+  const int vc = vs * 16 + rt;   // token colid, column rt of the slice
+  if (sv != nullptr) sv[colid][rt] = (tok_ok && vc < dv) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
+  sdo[colid][rt] = (tok_ok && vc < dv) ? to_f32(dout[(tok * H + h) * dv + vc]) : 0.f;
+  if (rt == 0) sb[colid] = tok_ok ? to_f32(beta[tok * H + h]) : 0.f;
+}
+
+// Sums over the four columns of one wave (lanes l, l ^ 16, l ^ 32, l ^ 48) of NV values at
+// once (NV a multiple of 4): a permlane16 swap of two values leaves the first's pair sums in
+// wave rows 0 and 2 and the second's in rows 1 and 3, and a permlane32 swap of two such
+// results completes four values, one per wave row: out[n] in wave row w is the total of
+// v[4 n + w].
+template <int NV>
+__device__ __forceinline__ void sum_cols4_many(const float (&v)[NV], float (&out)[NV / 4]) {
+  float s1[NV / 2];
+#pragma unroll
+  for (int m = 0; m < NV / 2; ++m) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v[2 * m]), __float_as_int(v[2 * m + 1]), false,
+                                                    false);
+    s1[m] = __int_as_float(r[0]) + __int_as_float(r[1]);
+  }
+#pragma unroll
+  for (int n = 0; n < NV / 4; ++n) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(s1[2 * n]), __float_as_int(s1[2 * n + 1]), false,
+                                                    false);
+    out[n] = __int_as_float(r[0]) + __int_as_float(r[1]);
+  }
+}
+
 template <typename T, int RPT>
 __global__ __launch_bounds__(256) void kda_bwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t stride,
     const T* __restrict__ alpha, const T* __restrict__ beta, const T* __restrict__ dout,
-    const float* __restrict__ dS_final, T* __restrict__ dv_out, float* __restrict__ dS0,
-    const float* __restrict__ ckpt, float* __restrict__ part, int64_t Tn, int64_t H, int dk, int dv, int l2norm) {
+    const float* __restrict__ G_end, T* __restrict__ dv_out, float* __restrict__ dS0,
+    const float* __restrict__ ckpt, float* __restrict__ part, int64_t Tn, int64_t H, int dk, int dv, int l2norm,
+    int64_t seg_len, int nseg) {
   constexpr int DKP = 16 * RPT;
   __shared__ float sq[kCk][DKP], sk[kCk][DKP], sa[kCk][DKP];
   __shared__ float sv[kCk][16], sdo[kCk][16], sb[kCk];
-  __shared__ float red[kHalf][3][DKP];   // sums of dq, dk, dalpha over the block's 16 columns
-  __shared__ float redb[kHalf];
+  // per wave: sums of dq, dk, dalpha (and dbeta) over its 4 columns; the 4 waves' slots are
+  // added as they are written out
+  __shared__ float red[kHalf][4][3][DKP];
+  __shared__ float redb[kHalf][4];
 
   const int n_vs = (dv + 15) / 16;
-  const int64_t bh = blockIdx.x / n_vs;
   const int vs = blockIdx.x % n_vs;
+  const int p = (int)((blockIdx.x / n_vs) % nseg);      // segment of the sequence
+  const int64_t bh = blockIdx.x / n_vs / nseg;
   const int64_t b = bh / H, h = bh % H;
-  const int tid = threadIdx.x, colid = tid >> 4, rt = tid & 15;
+  const int tid = threadIdx.x, colid = tid >> 4, rt = tid & 15, cw = colid & 3, wave = tid >> 6;
   const int col = vs * 16 + colid;
   const bool col_ok = col < dv;
   const int64_t nb = (Tn + kCk - 1) / kCk;
-  const int64_t BTH = (int64_t)gridDim.x / n_vs * Tn;   // B * H * T: one partial array's rows
+  constexpr int kNV = (3 * RPT + 3) / 4 * 4;
+  const int64_t t_beg = nseg > 1 ? p * seg_len : 0;
+  const int64_t t_end = nseg > 1 ? min<int64_t>(Tn, t_beg + seg_len) : Tn;
+  const int64_t BTH = (int64_t)gridDim.x / n_vs / nseg * Tn;   // B * H * T: one partial array's rows
   float* pq = part + (int64_t)vs * 3 * BTH * dk;        // this slice's partials
   float* pk = pq + BTH * dk;
   float* pa = pk + BTH * dk;
@@ -84,10 +155,8 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int row = rt + 16 * i;
-    G[i] = (dS_final != nullptr && col_ok && row < dk) ? dS_final[(bh * dk + row) * dv + col] : 0.f;
+    G[i] = (G_end != nullptr && col_ok && row < dk) ? G_end[((bh * nseg + p) * dk + row) * dv + col] : 0.f;
   }
-  for (int e = tid; e < kHalf * 3 * DKP; e += 256) (&red[0][0][0])[e] = 0.f;
-  if (tid < kHalf) redb[tid] = 0.f;
 
   // forward step on the staged token tt: S <- S + k (beta w)^T after the decay; returns w
   auto step = [&](float (&S)[RPT], int tt) {
@@ -104,36 +173,12 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
     return w;
   };
 
-  for (int64_t kb = nb - 1; kb >= 0; --kb) {
+  for (int64_t kb = (t_end + kCk - 1) / kCk - 1; kb >= t_beg / kCk; --kb) {
     const int64_t t0 = kb * kCk;
-    const int nt = (int)min<int64_t>(kCk, Tn - t0);
+    const int nt = (int)min<int64_t>(kCk, t_end - t0);
     __syncthreads();   // the previous block's reads of the staging arrays are done
-    {  // stage: thread (colid, rt) loads token colid, rows rt + 16 i; q and k normalised
-      const bool tok_ok = colid < nt;
-      const int64_t tok = b * Tn + t0 + colid;
-      float rq[RPT], rk[RPT], ssq = 0.f, ssk = 0.f;
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int row = rt + 16 * i;
-        const bool ok = tok_ok && row < dk;
-        rq[i] = ok ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
-        rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
-        sa[colid][row] = ok ? to_f32(alpha[(tok * H + h) * dk + row]) : 1.f;
-        ssq = fmaf(rq[i], rq[i], ssq);
-        ssk = fmaf(rk[i], rk[i], ssk);
-      }
-      const float nq = l2norm ? 1.f / sqrtf(sum16(ssq) + 1e-6f) : 1.f;
-      const float nk = l2norm ? 1.f / sqrtf(sum16(ssk) + 1e-6f) : 1.f;
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        sq[colid][rt + 16 * i] = rq[i] * nq;
-        sk[colid][rt + 16 * i] = rk[i] * nk;
-      }
-      const int vc = vs * 16 + rt;   // token colid, column rt of the slice
-      sv[colid][rt] = (tok_ok && vc < dv) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
-      sdo[colid][rt] = (tok_ok && vc < dv) ? to_f32(dout[(tok * H + h) * dv + vc]) : 0.f;
-      if (rt == 0) sb[colid] = tok_ok ? to_f32(beta[tok * H + h]) : 0.f;
-    }
+    stage_tokens<T, RPT>(q, k, v, stride, alpha, beta, dout, b * Tn + t0, nt, h, H, dk, dv, vs, l2norm, sq, sk, sa,
+                         sv, sdo, sb);
     __syncthreads();
     float S0c[RPT];   // the state before token t0
 #pragma unroll
@@ -141,14 +186,14 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
       const int row = rt + 16 * i;
       S0c[i] = (col_ok && row < dk) ? ckpt[((bh * nb + kb) * dk + row) * dv + col] : 0.f;
     }
-    for (int half = 1; half >= 0; --half) {
-      const int h0 = half * kHalf;
+    for (int part = kCk / kHalf - 1; part >= 0; --part) {
+      const int h0 = part * kHalf;
       const int hn = min(kHalf, nt - h0);
       if (hn <= 0) continue;
       float S[RPT];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) S[i] = S0c[i];
-      for (int tt = 0; tt < h0; ++tt) step(S, tt);   // to the half's first token
+      for (int tt = 0; tt < h0; ++tt) step(S, tt);   // to the part's first token
       float Sp[kHalf][RPT], wv[kHalf];
 #pragma unroll
       for (int j = 0; j < kHalf; ++j) {
@@ -158,7 +203,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
           wv[j] = step(S, h0 + j);
         }
       }
-      // backward over the half; S is the state after its last token
+      // backward over the part; S is the state after its last token
 #pragma unroll
       for (int j = kHalf - 1; j >= 0; --j) {
         if (j >= hn) continue;
@@ -176,22 +221,26 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
         r = sum16(r);
         if (rt == 0 && col_ok) from_f32(dv_out + (b * Tn + t0 + tt) * stride + h * dv + col, bt * r);
         const float dbr = sum_cols4(r * w);
-        if ((tid & 63) == 0) atomicAdd(&redb[j], dbr);
+        if ((tid & 63) == 0) redb[j][wave] = dbr;
+        float vals[kNV];   // dq, dk, dalpha of the lane's rows (then zero padding)
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int row = rt + 16 * i;
           const float a = sa[tt][row];
-          const float dqv = St[i] * doc;
-          const float dkv = bt * (G[i] * w - a * Sp[j][i] * r);
           const float dP = G[i] - bt * sk[tt][row] * r;
-          const float dav = dP * Sp[j][i];
+          vals[i] = St[i] * doc;
+          vals[RPT + i] = bt * (G[i] * w - a * Sp[j][i] * r);
+          vals[2 * RPT + i] = dP * Sp[j][i];
           G[i] = a * dP;
-          const float s0 = sum_cols4(dqv), s1 = sum_cols4(dkv), s2 = sum_cols4(dav);
-          if ((tid & 63) < 16) {
-            atomicAdd(&red[j][0][row], s0);
-            atomicAdd(&red[j][1][row], s1);
-            atomicAdd(&red[j][2][row], s2);
-          }
+        }
+#pragma unroll
+        for (int f = 3 * RPT; f < kNV; ++f) vals[f] = 0.f;
+        float sums[kNV / 4];
+        sum_cols4_many<kNV>(vals, sums);
+#pragma unroll
+        for (int n = 0; n < kNV / 4; ++n) {   // lane of wave row cw holds value 4 n + cw
+          const int f = 4 * n + cw;
+          if (f < 3 * RPT) red[j][wave][f / RPT][rt + 16 * (f % RPT)] = sums[n];
         }
       }
       __syncthreads();
@@ -200,21 +249,136 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
         const int j = e / DKP, row = e % DKP;
         if (row >= dk) continue;
         const int64_t o = ((b * Tn + t0 + h0 + j) * H + h) * dk + row;
-        pq[o] = red[j][0][row];
-        pk[o] = red[j][1][row];
-        pa[o] = red[j][2][row];
+        pq[o] = red[j][0][0][row] + red[j][1][0][row] + red[j][2][0][row] + red[j][3][0][row];
+        pk[o] = red[j][0][1][row] + red[j][1][1][row] + red[j][2][1][row] + red[j][3][1][row];
+        pa[o] = red[j][0][2][row] + red[j][1][2][row] + red[j][2][2][row] + red[j][3][2][row];
       }
-      if (tid < hn) pb[(b * Tn + t0 + h0 + tid) * H + h] = redb[tid];
+      if (tid < hn) pb[(b * Tn + t0 + h0 + tid) * H + h] = redb[tid][0] + redb[tid][1] + redb[tid][2] + redb[tid][3];
       __syncthreads();
-      for (int e = tid; e < kHalf * 3 * DKP; e += 256) (&red[0][0][0])[e] = 0.f;
-      if (tid < kHalf) redb[tid] = 0.f;
     }
   }
-  if (dS0 != nullptr && col_ok) {
+  if (dS0 != nullptr && col_ok && p == 0) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rt + 16 * i;
       if (row < dk) dS0[(bh * dk + row) * dv + col] = G[i];
+    }
+  }
+}
+
+// The reverse recurrence alone over one segment, from G = 0 at its end and without the
+// states: G += q^_t do_t^T; r = G^T k^_t; G <- Diag(alpha_t) (G - beta_t k^_t r^T). Writes G
+// at the segment's start: the segment's own part of dL/dS before it.
+template <typename T, int RPT>
+__global__ __launch_bounds__(256) void kda_bwd_local_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, int64_t stride, const T* __restrict__ alpha,
+    const T* __restrict__ beta, const T* __restrict__ dout, float* __restrict__ E, int64_t Tn, int64_t H, int dk,
+    int dv, int l2norm, int64_t seg_len, int nseg) {
+  constexpr int DKP = 16 * RPT;
+  __shared__ float sq[kCk][DKP], sk[kCk][DKP], sa[kCk][DKP];
+  __shared__ float sdo[kCk][16], sb[kCk];
+  const int n_vs = (dv + 15) / 16;
+  const int vs = blockIdx.x % n_vs;
+  const int p = (int)((blockIdx.x / n_vs) % nseg);
+  const int64_t bh = blockIdx.x / n_vs / nseg;
+  const int64_t b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, colid = tid >> 4, rt = tid & 15;
+  const int col = vs * 16 + colid;
+  const int64_t t_beg = p * seg_len, t_end = min<int64_t>(Tn, t_beg + seg_len);
+  float G[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) G[i] = 0.f;
+  for (int64_t kb = (t_end + kCk - 1) / kCk - 1; kb >= t_beg / kCk; --kb) {
+    const int64_t t0 = kb * kCk;
+    const int nt = (int)min<int64_t>(kCk, t_end - t0);
+    __syncthreads();
+    stage_tokens<T, RPT>(q, k, nullptr, stride, alpha, beta, dout, b * Tn + t0, nt, h, H, dk, dv, vs, l2norm, sq, sk,
+                         sa, nullptr, sdo, sb);
+    __syncthreads();
+    for (int tt = nt - 1; tt >= 0; --tt) {
+      const float doc = sdo[tt][colid];
+      float r = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        G[i] = fmaf(sq[tt][rt + 16 * i], doc, G[i]);
+        r = fmaf(G[i], sk[tt][rt + 16 * i], r);
+      }
+      const float br = sb[tt] * sum16(r);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) G[i] = sa[tt][rt + 16 * i] * fmaf(-sk[tt][rt + 16 * i], br, G[i]);
+    }
+  }
+  if (col < dv) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rt + 16 * i;
+      if (row < dk) E[((bh * nseg + p) * dk + row) * dv + col] = G[i];
+    }
+  }
+}
+
+// Chains the segments of one (batch, head, 16-column slice of d_v), given each segment's
+// transition product M_p (dk x dk: its end state is M_p times its start state plus its own
+// term) and a term X_p per segment:
+//   forward (BACK false): Y_0 = init, Y_p = M_{p-1} Y_{p-1} + X_{p-1}: the state at each segment's start;
+//   backward (BACK true): Y_{P-1} = init, Y_p = M_{p+1}^T Y_{p+1} + X_{p+1}: dL/dS at each segment's end.
+// init may be null (zero). dk <= 128.
+template <bool BACK>
+__global__ __launch_bounds__(256) void kda_chain_kernel(const float* __restrict__ M, const float* __restrict__ X,
+                                                        const float* __restrict__ init, float* __restrict__ Y,
+                                                        int nseg, int dk, int dv) {
+  __shared__ float cur[128][16];
+  __shared__ float mt[16][129];
+  const int n_vs = (dv + 15) / 16;
+  const int vs = blockIdx.x % n_vs;
+  const int64_t bh = blockIdx.x / n_vs;
+  const int tid = threadIdx.x, colid = tid >> 4, rt = tid & 15;
+  const int col = vs * 16 + colid;
+  const bool col_ok = col < dv;
+  auto yat = [&](int p, int row) { return ((bh * nseg + p) * dk + row) * dv + col; };
+  {
+    const int p0 = BACK ? nseg - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = rt + 16 * i;
+      const bool ok = col_ok && row < dk;
+      const float val = (ok && init != nullptr) ? init[(bh * dk + row) * dv + col] : 0.f;
+      cur[row][colid] = val;
+      if (ok) Y[yat(p0, row)] = val;
+    }
+  }
+  for (int step = 1; step < nseg; ++step) {
+    const int p = BACK ? nseg - 1 - step : step;   // the entry formed
+    const int src = BACK ? p + 1 : p - 1;          // the segment whose M and X form it
+    const float* Mp = M + (bh * nseg + src) * dk * dk;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < dk; j0 += 16) {
+      __syncthreads();   // cur is written, the previous tile is read
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int e = tid + 256 * m;
+        const int jj = BACK ? e >> 7 : e & 15, r = BACK ? e & 127 : e >> 4;
+        const bool ok = j0 + jj < dk && r < dk;
+        mt[jj][r] = !ok ? 0.f : BACK ? Mp[(j0 + jj) * dk + r] : Mp[r * dk + j0 + jj];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float cj = cur[j0 + jj][colid];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(mt[jj][rt + 16 * i], cj, acc[i]);
+      }
+    }
+    __syncthreads();   // every read of cur is done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = rt + 16 * i;
+      const bool ok = col_ok && row < dk;
+      const float val = ok ? acc[i] + X[yat(src, row)] : 0.f;
+      cur[row][colid] = val;
+      if (ok) Y[yat(p, row)] = val;
     }
   }
 }
@@ -277,11 +441,14 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(
   }
 }
 
+// The reverse pass over every (batch, head, segment, column slice) from G_end ([B][H][nseg]
+// [dk][dv]; the sequence's dS_final when nseg = 1), then the sum over slices with the L2
+// backward.
 template <typename T>
-hipError_t launch_bwd_t(const KdaArgs& a, const KdaGrads& g, float* ckpt, float* part, hipStream_t stream,
-                        Marks* marks) {
+hipError_t launch_bwd_t(const KdaArgs& a, const KdaGrads& g, const float* G_end, int64_t seg_len, int nseg,
+                        float* ckpt, float* part, hipStream_t stream, Marks* marks) {
   const int n_vs = (int)((a.dv + 15) / 16);
-  const int64_t blocks = a.B * a.H * n_vs;
+  const int64_t blocks = a.B * a.H * n_vs * nseg;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), thr(256);
   const int dk = (int)a.dk, dv = (int)a.dv, nrm = a.l2norm ? 1 : 0;
@@ -293,8 +460,8 @@ hipError_t launch_bwd_t(const KdaArgs& a, const KdaGrads& g, float* ckpt, float*
   const T* dout = static_cast<const T*>(g.dout);
   T* dvo = static_cast<T*>(g.dv);
 #define CHM_BWD(R)                                                                                                   \
-  hipLaunchKernelGGL((kda_bwd_kernel<T, R>), grid, thr, 0, stream, q, k, v, a.qkv_stride, al, be, dout, g.dS_final, \
-                     dvo, g.dS0, ckpt, part, a.T, a.H, dk, dv, nrm)
+  hipLaunchKernelGGL((kda_bwd_kernel<T, R>), grid, thr, 0, stream, q, k, v, a.qkv_stride, al, be, dout, G_end,     \
+                     dvo, g.dS0, ckpt, part, a.T, a.H, dk, dv, nrm, seg_len, nseg)
   if (dk <= 16) CHM_BWD(1);
   else if (dk <= 32) CHM_BWD(2);
   else if (dk <= 64) CHM_BWD(4);
@@ -430,16 +597,25 @@ hipError_t conv_bwd_t(const void* x, const void* dy, void* dx, float* dw_text, f
   if (e == hipSuccess) e = zero(dw_vis, C * kVisTaps, stream);
   if (e != hipSuccess) return e;
   if (B > 65535) return hipErrorInvalidValue;
+  // dx of the image grids that the rows kernel takes: that kernel with mirrored taps, in one launch
+  std::vector<Seg> rows;
+  const bool bf16 = sizeof(T) == 2;
+  for (int i = 0; i < nseg; ++i)
+    if (segs[i].length > 0 && conv_rows_adjoint_ok(segs[i], C, bf16)) rows.push_back(segs[i]);
+  e = launch_conv_rows_adjoint(dy, dx, w_vis, B, Ttot, C, rows.data(), (int)rows.size(), stream, nullptr);
+  if (e != hipSuccess) return e;
   for (int i = 0; i < nseg; ++i) {
     const Seg& sg = segs[i];
     if (sg.length == 0) continue;
-    const dim3 gx((unsigned)((C / 8 + 63) / 64), (unsigned)((sg.length + 3) / 4), (unsigned)B);
-    hipLaunchKernelGGL(conv_bwd_dx_kernel<T>, gx, dim3(256), 0, stream, static_cast<const T*>(dy),
-                       static_cast<T*>(dx), w_text, w_vis, Ttot, C, sg);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // dw: about 64 token ranges per segment and batch item
-    const int64_t per = std::max<int64_t>(16, (sg.length + 63) / 64);
+    if (!conv_rows_adjoint_ok(sg, C, bf16)) {
+      const dim3 gx((unsigned)((C / 8 + 63) / 64), (unsigned)((sg.length + 3) / 4), (unsigned)B);
+      hipLaunchKernelGGL(conv_bwd_dx_kernel<T>, gx, dim3(256), 0, stream, static_cast<const T*>(dy),
+                         static_cast<T*>(dx), w_text, w_vis, Ttot, C, sg);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    // dw: about 512 token ranges per segment and batch item
+    const int64_t per = std::max<int64_t>(16, (sg.length + 511) / 512);
     const dim3 gw((unsigned)((C / 4 + 255) / 256), (unsigned)((sg.length + per - 1) / per), (unsigned)B);
     if (sg.kind == SEG_TEXT)
       hipLaunchKernelGGL((conv_bwd_dw_kernel<T, kTextTaps>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
@@ -453,29 +629,129 @@ hipError_t conv_bwd_t(const void* x, const void* dy, void* dx, float* dw_text, f
   return mark_after(marks, "conv_bwd_kernels", stream);
 }
 
+
+template <typename T>
+hipError_t launch_local_t(const KdaArgs& a, const KdaGrads& g, float* E, int64_t seg_len, int nseg,
+                          hipStream_t stream) {
+  const int n_vs = (int)((a.dv + 15) / 16);
+  const dim3 grid((unsigned)(a.B * a.H * n_vs * nseg)), thr(256);
+  const int dk = (int)a.dk, dv = (int)a.dv, nrm = a.l2norm ? 1 : 0;
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* al = static_cast<const T*>(a.alpha);
+  const T* be = static_cast<const T*>(a.beta);
+  const T* dout = static_cast<const T*>(g.dout);
+#define CHM_LOC(R)                                                                                            \
+  hipLaunchKernelGGL((kda_bwd_local_kernel<T, R>), grid, thr, 0, stream, q, k, a.qkv_stride, al, be, dout, E, \
+                     a.T, a.H, dk, dv, nrm, seg_len, nseg)
+  if (dk <= 16) CHM_LOC(1);
+  else if (dk <= 32) CHM_LOC(2);
+  else if (dk <= 64) CHM_LOC(4);
+  else if (dk <= 128) CHM_LOC(8);
+  else return hipErrorInvalidValue;
+#undef CHM_LOC
+  return hipGetLastError();
+}
+
+// How a sequence is cut for the backward: enough segments that the blocks of one pass fill
+// the chip about eight times over, each at least kMinSeg tokens, the length a multiple of
+// the 16-token checkpoint spacing.
+constexpr int64_t kBwdBlocks = 2048, kMinSeg = 64;
+struct BwdCut {
+  int64_t len;
+  int nseg;
+};
+BwdCut bwd_cut(int64_t B, int64_t T, int64_t H, int64_t dv) {
+  const int64_t base = B * H * ((dv + 15) / 16);
+  int64_t P = base > 0 ? (kBwdBlocks + base - 1) / base : 1;
+  P = std::min<int64_t>(P, std::max<int64_t>(1, T / kMinSeg));
+  if (P <= 1) return {T, 1};
+  const int64_t len = ((T + P - 1) / P + kCk - 1) / kCk * kCk;
+  P = (T + len - 1) / len;
+  return P <= 1 ? BwdCut{T, 1} : BwdCut{len, (int)P};
+}
+
 }  // namespace
 
 size_t kda_bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
   const int64_t n_vs = (dv + 15) / 16;
   const int64_t ck = B * H * ((T + kCk - 1) / kCk) * dk * dv;
   const int64_t parts = n_vs * B * T * H * (3 * dk + 1);
-  return (size_t)(ck + parts) * sizeof(float);
+  const BwdCut c = bwd_cut(B, T, H, dv);
+  const int64_t segs = c.nseg > 1 ? B * H * c.nseg * (4 * dk * dv + dk * dk) : 0;
+  return (size_t)(ck + parts + segs) * sizeof(float);
 }
 
+// Cut into segments, the reverse recurrence runs on all of them at once. Per segment p, on the
+// token-by-token kernels: its own end state from a zero start (L_p) and its transition product
+// (M_p, from the identity with v = 0); the chain gives every segment's start state, from which
+// the checkpoints are taken; the reverse recurrence from zero gives the segment's own part of
+// dL/dS at its start (E_p); the backward chain gives dL/dS at every segment's end; then the
+// reverse pass proper runs per segment from there.
 hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* workspace, hipStream_t stream,
                                Marks* marks) {
   if (a.B * a.H == 0) return hipSuccess;
+  const BwdCut c = bwd_cut(a.B, a.T, a.H, a.dv);
+  const int64_t sz = a.B * a.H * c.nseg * a.dk * a.dv;
   float* ckpt = static_cast<float*>(workspace);
   float* part = ckpt + a.B * a.H * ((a.T + kCk - 1) / kCk) * a.dk * a.dv;
-  // forward pass keeping the checkpoints (no o, no S_final, no gate)
+  float* Lw = part + ((a.dv + 15) / 16) * a.B * a.T * a.H * (3 * a.dk + 1);
+  float* Sst = Lw + sz;
+  float* Ew = Sst + sz;
+  float* Gend = Ew + sz;
+  float* Mw = Gend + sz;
+  // forward passes without o, S_final or gate
   KdaArgs f = a;
   f.o = nullptr;
   f.S_final = nullptr;
   f.gate = nullptr;
-  hipError_t e = launch_kda_sequential(f, stream, marks, ckpt);
-  if (e != hipSuccess) return e;
-  return a.bf16 ? launch_bwd_t<uint16_t>(a, g, ckpt, part, stream, marks)
-                : launch_bwd_t<float>(a, g, ckpt, part, stream, marks);
+  f.q = nullptr;
+  hipError_t e = hipSuccess;
+  const float* G_end = g.dS_final;
+  if (c.nseg > 1) {
+    const int64_t chains = a.B * a.H * ((a.dv + 15) / 16);
+    SeqSegs sl;
+    sl.len = c.len;
+    sl.nseg = c.nseg;
+    sl.Send = Lw;
+    sl.zero_start = 1;
+    e = launch_kda_sequential(f, stream, marks, nullptr, &sl);
+    if (e != hipSuccess) return e;
+    KdaArgs fm = f;
+    fm.v = nullptr;
+    fm.dv = a.dk;
+    SeqSegs sm = sl;
+    sm.Send = Mw;
+    sm.zero_start = 0;
+    sm.identity = 1;
+    e = launch_kda_sequential(fm, stream, marks, nullptr, &sm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_chain_kernel<false>, dim3((unsigned)chains), dim3(256), 0, stream, Mw, Lw, a.S0, Sst,
+                       c.nseg, (int)a.dk, (int)a.dv);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SeqSegs sc;
+    sc.len = c.len;
+    sc.nseg = c.nseg;
+    sc.Sseg = Sst;
+    e = launch_kda_sequential(f, stream, marks, ckpt, &sc);
+    if (e != hipSuccess) return e;
+    e = a.bf16 ? launch_local_t<uint16_t>(a, g, Ew, c.len, c.nseg, stream)
+               : launch_local_t<float>(a, g, Ew, c.len, c.nseg, stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_local_kernel", stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_chain_kernel<true>, dim3((unsigned)chains), dim3(256), 0, stream, Mw, Ew, g.dS_final, Gend,
+                       c.nseg, (int)a.dk, (int)a.dv);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
+    if (e != hipSuccess) return e;
+    G_end = Gend;
+  } else {
+    e = launch_kda_sequential(f, stream, marks, ckpt);
+    if (e != hipSuccess) return e;
+  }
+  return a.bf16 ? launch_bwd_t<uint16_t>(a, g, G_end, c.len, c.nseg, ckpt, part, stream, marks)
+                : launch_bwd_t<float>(a, g, G_end, c.len, c.nseg, ckpt, part, stream, marks);
 }
 
 hipError_t launch_conv_backward(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis, int64_t B,

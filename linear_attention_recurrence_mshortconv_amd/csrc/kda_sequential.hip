@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
                                                       const T* __restrict__ alpha, const T* __restrict__ beta,
                                                       const float* __restrict__ S0, T* __restrict__ o,
                                                       float* __restrict__ S_final, int64_t Tn, int64_t H, int dk,
-                                                      int dv, int l2norm, float* __restrict__ ckpt) {
+                                                      int dv, int l2norm, float* __restrict__ ckpt, SeqSegs sg) {
   constexpr int DKP = 16 * RPT;   // staged rows; rows past dk hold k = q = 0, alpha = 1
   __shared__ float sk[2][kTokBatch][DKP];
   __shared__ float sq[2][kTokBatch][DKP];
@@ -51,25 +51,33 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
   __shared__ float sb[2][kTokBatch];
 
   const int n_vs = (dv + 15) / 16;
-  const int64_t bh = blockIdx.x / n_vs;
   const int vs = blockIdx.x % n_vs;
+  const int p = (int)((blockIdx.x / n_vs) % sg.nseg);          // segment of the sequence
+  const int64_t bh = blockIdx.x / n_vs / sg.nseg;
   const int64_t b = bh / H, h = bh % H;
+  const int64_t t_beg = sg.nseg > 1 ? p * sg.len : 0;
+  const int64_t t_end = sg.nseg > 1 ? min<int64_t>(Tn, t_beg + sg.len) : Tn;
+  const int64_t seg_ix = bh * sg.nseg + p;
   const int tid = threadIdx.x;
   const int colid = tid >> 4, rt = tid & 15;
   const int col = vs * 16 + colid;
   const bool col_ok = col < dv;
 
+  const float* init = sg.zero_start || sg.identity ? nullptr
+                      : p == 0                     ? (S0 != nullptr ? S0 + bh * dk * dv : nullptr)
+                      : (sg.Sseg != nullptr ? sg.Sseg + seg_ix * dk * dv : nullptr);
   float s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int row = rt + 16 * i;
-    s[i] = (S0 != nullptr && col_ok && row < dk) ? S0[(bh * dk + row) * dv + col] : 0.f;
+    s[i] = sg.identity ? (col_ok && row == col ? 1.f : 0.f)
+                       : (init != nullptr && col_ok && row < dk) ? init[row * dv + col] : 0.f;
   }
 
   // one batch of tokens: thread (colid, rt) loads token colid, rows rt + 16 i
   float rk[RPT], rq[RPT], ra[RPT], rv, rb;
   auto load = [&](int64_t t0) {
-    const int nt = (int)min<int64_t>(kTokBatch, Tn - t0);
+    const int nt = (int)min<int64_t>(kTokBatch, t_end - t0);
     const bool tok_ok = colid < nt;
     const int64_t tok = b * Tn + t0 + colid;
 #pragma unroll
@@ -77,12 +85,12 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
       const int row = rt + 16 * i;
       const bool ok = tok_ok && row < dk;
       rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
-      rq[i] = ok ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
+      rq[i] = ok && q != nullptr ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
       ra[i] = ok ? to_f32(alpha[(tok * H + h) * dk + row]) : 1.f;
     }
     // v: token colid, column vs * 16 + rt; beta: token colid
     const int vc = vs * 16 + rt;
-    rv = (tok_ok && vc < dv) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
+    rv = (tok_ok && vc < dv && v != nullptr) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
     rb = tok_ok ? to_f32(beta[tok * H + h]) : 0.f;
   };
   // store a loaded batch to buffer `buf` and normalise its q and k rows
@@ -111,15 +119,15 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
     if (rt == 0) sb[buf][colid] = rb;
   };
 
-  if (Tn > 0) {
-    load(0);
+  if (t_beg < t_end) {
+    load(t_beg);
     stage(0);
   }
   __syncthreads();
   int buf = 0;
-  for (int64_t t0 = 0; t0 < Tn; t0 += kTokBatch) {
-    const int nt = (int)min<int64_t>(kTokBatch, Tn - t0);
-    const bool more = t0 + kTokBatch < Tn;
+  for (int64_t t0 = t_beg; t0 < t_end; t0 += kTokBatch) {
+    const int nt = (int)min<int64_t>(kTokBatch, t_end - t0);
+    const bool more = t0 + kTokBatch < t_end;
     if (more) load(t0 + kTokBatch);                  // in flight during this batch
     if (ckpt != nullptr && col_ok) {                 // the state before this batch (for the backward)
       float* dst = ckpt + ((bh * ((Tn + kTokBatch - 1) / kTokBatch) + t0 / kTokBatch) * dk) * dv + col;
@@ -151,11 +159,18 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
     __syncthreads();
     buf ^= 1;
   }
-  if (S_final != nullptr && col_ok) {
+  if (S_final != nullptr && col_ok && p == sg.nseg - 1) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rt + 16 * i;
       if (row < dk) S_final[(bh * dk + row) * dv + col] = s[i];
+    }
+  }
+  if (sg.Send != nullptr && col_ok) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rt + 16 * i;
+      if (row < dk) sg.Send[(seg_ix * dk + row) * dv + col] = s[i];
     }
   }
 }
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(256) void kda_gate_norm_kernel(T* __restrict__ o, c
 }
 
 template <typename T>
-hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, float* ckpt) {
+hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, float* ckpt, const SeqSegs& sg) {
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
@@ -204,15 +219,15 @@ hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, floa
   const dim3 g((unsigned)blocks), t(256);
   const int dk = (int)a.dk, dv = (int)a.dv, nrm = (int)a.l2norm;
   if (dk <= 16)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 1>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 1>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
   else if (dk <= 32)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 2>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 2>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
   else if (dk <= 64)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 4>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 4>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
   else if (dk <= 128)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 8>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 8>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
   else
-    hipLaunchKernelGGL((kda_seq_kernel<T, 16>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt);
+    hipLaunchKernelGGL((kda_seq_kernel<T, 16>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
   return hipGetLastError();
 }
 
@@ -234,13 +249,17 @@ hipError_t launch_kda_gate_norm(const KdaArgs& a, hipStream_t stream, Marks* mar
   return e != hipSuccess ? e : mark_after(marks, "kda_gate_norm_kernel", stream);
 }
 
-hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks, float* ckpt) {
+hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* marks, float* ckpt,
+                                 const SeqSegs* segs) {
   if (a.B * a.H == 0) return hipSuccess;
+  const SeqSegs sg = segs != nullptr ? *segs : SeqSegs{};
+  if (sg.nseg < 1 || (sg.nseg > 1 && (sg.len <= 0 || sg.len % kTokBatch != 0))) return hipErrorInvalidValue;
   const int n_vs = (int)((a.dv + 15) / 16);
-  const int64_t blocks = a.B * a.H * n_vs;
+  const int64_t blocks = a.B * a.H * n_vs * sg.nseg;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.T == 0 && a.S_final == nullptr) return hipSuccess;
-  hipError_t e = a.bf16 ? launch_seq<uint16_t>(a, blocks, stream, ckpt) : launch_seq<float>(a, blocks, stream, ckpt);
+  if (a.T == 0 && a.S_final == nullptr && sg.Send == nullptr) return hipSuccess;
+  hipError_t e = a.bf16 ? launch_seq<uint16_t>(a, blocks, stream, ckpt, sg)
+                        : launch_seq<float>(a, blocks, stream, ckpt, sg);
   if (e == hipSuccess) e = mark_after(marks, "kda_seq_kernel", stream);
   if (e == hipSuccess && a.gate != nullptr) e = launch_kda_gate_norm(a, stream, marks);
   return e;

@@ -299,7 +299,9 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
 // 32-bit offsets: taps outside the grid get an offset past the buffer's end and
 // read zero, output positions outside it are dropped the same way, so there is
 // no branch around a memory access and every wait counts only what it needs.
-template <int TR, int TW>
+// FLIP: the 3x3 taps mirrored in both directions, which makes the kernel the adjoint of
+// the image conv (dx from dy for the backward).
+template <int TR, int TW, bool FLIP>
 __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                          const float* __restrict__ w_vis, int64_t Ttot, int64_t C,
                                                          RowsBatch tb) {
@@ -340,7 +342,8 @@ __global__ __launch_bounds__(TW * 8) void conv_rows_kernel(const uint16_t* __res
 #pragma unroll
     for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wr[kh][kw][i] = w_vis[((int64_t)slab * 64 + g * 8 + i) * kVisTaps + 18 + kh * 3 + kw];
+      for (int i = 0; i < 8; ++i)
+        wr[kh][kw][i] = w_vis[((int64_t)slab * 64 + g * 8 + i) * kVisTaps + 18 + (FLIP ? 8 - kh * 3 - kw : kh * 3 + kw)];
 
   // byte offset of (grid row hh, grid column ww, channel group gg), or kOutside
   auto offset = [&](int hh, int ww, int gg) -> uint32_t {
@@ -577,7 +580,7 @@ bool rows_entry(const Seg& seg, int64_t B, int64_t C, RowsEntry& ent, int64_t& b
   return true;
 }
 
-template <int TR, int TW>
+template <int TR, int TW, bool FLIP = false>
 hipError_t launch_rows_batch(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
                              const Seg* segs, int n, hipStream_t stream, Marks* marks) {
   for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
@@ -596,11 +599,11 @@ hipError_t launch_rows_batch(const uint16_t* x, uint16_t* y, const float* w_vis,
     if (total == 0) continue;
     tb.n_logical = (int)total;
     const int64_t grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL((conv_rows_kernel<TR, TW>), dim3((unsigned)grid), dim3(TW * 8), 0, stream, x, y, w_vis, Ttot,
-                       C, tb);
+    hipLaunchKernelGGL((conv_rows_kernel<TR, TW, FLIP>), dim3((unsigned)grid), dim3(TW * 8), 0, stream, x, y, w_vis,
+                       Ttot, C, tb);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const hipError_t me = mark_after(marks, "conv_rows_kernel", stream);
+    const hipError_t me = mark_after(marks, FLIP ? "conv_rows_adjoint_kernel" : "conv_rows_kernel", stream);
     if (me != hipSuccess) return me;
   }
   return hipSuccess;
@@ -706,6 +709,17 @@ hipError_t launch_conv(const void* x, void* y, int64_t B, int64_t Ttot, int64_t 
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+bool conv_rows_adjoint_ok(const Seg& seg, int64_t C, bool bf16) {
+  return bf16 && seg.kind != SEG_TEXT && seg.frames == 1 && C % 64 == 0 && rows_fit<4, 32>(seg, C);
+}
+
+hipError_t launch_conv_rows_adjoint(const void* dy, void* dx, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
+                                    const Seg* segs, int n, hipStream_t stream, Marks* marks) {
+  if (B == 0 || n == 0) return hipSuccess;
+  return launch_rows_batch<4, 32, true>(static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dx), w_vis, B, Ttot,
+                                        C, segs, n, stream, marks);
 }
 
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream) {

@@ -84,6 +84,28 @@ def test_kda_bwd_bf16_d128(chm, T):
         _close_bf16(got[n], ref[n], f"{n} T={T}")
 
 
+def test_kda_bwd_fp32_segments(chm):
+    """fp32, T = 700 on two 32-wide heads: the sequence is cut into segments of 80 tokens (the
+    last 60) whose reverse passes run at once, joined by the chains of transition products;
+    with S0 and dS_final."""
+    rng = np.random.default_rng(124)
+    args = _case(rng, 1, 700, 2, 32, 32, "f32")
+    got = _run(chm, "f32", *args)
+    ref = kda_backward_ref(*args)
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        assert_close(got[n], ref[n], "f32", n)
+
+
+def test_kda_bwd_bf16_segments_batch(chm):
+    """bf16 d = 128, two sequences of 1000 tokens: 13 segments of 80 tokens per sequence."""
+    rng = np.random.default_rng(125)
+    args = _case(rng, 2, 1000, 2, 128, 128, "bf16")
+    got = _run(chm, "bf16", *args)
+    ref = kda_backward_ref(*args)
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        _close_bf16(got[n], ref[n], f"{n} segmented")
+
+
 def test_conv_bwd_fp32_mixed_layout(chm):
     import torch
     S = wl.Segment
@@ -100,6 +122,28 @@ def test_conv_bwd_fp32_mixed_layout(chm):
     np.testing.assert_allclose(to_host(dx), ref["dx"], rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(to_host(dwt), ref["dw_text"], rtol=1e-5, atol=1e-4)
     np.testing.assert_allclose(to_host(dwv), ref["dw_vis"], rtol=1e-5, atol=1e-4)
+
+
+def test_conv_bwd_bf16_grids(chm):
+    """bf16: image grids take the image conv's kernel with mirrored taps for dx (one launch for
+    both images), the video and the text the gather kernel; dx within one bf16 rounding of the
+    fp64 adjoint, dw within fp32 summation error."""
+    import torch
+    S = wl.Segment
+    segs = (S(wl.TEXT, 0, 5), S(wl.IMAGE, 5, 20 * 33, 1, 20, 33), S(wl.VIDEO, 665, 2 * 5 * 6, 2, 5, 6),
+            S(wl.IMAGE, 725, 7 * 64, 1, 7, 64))
+    T, C = 725 + 448, 128
+    rng = np.random.default_rng(126)
+    x = wl.round_to_bf16(rng.standard_normal((2, T, C)).astype(np.float32))
+    dy = wl.round_to_bf16(rng.standard_normal((2, T, C)).astype(np.float32))
+    wt = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    wv = (0.5 * rng.standard_normal((C, 27))).astype(np.float32)
+    dx, dwt, dwv = chm.mshortconv_bwd(to_device(x, "bf16"), to_device(dy, "bf16"), torch.from_numpy(wt),
+                                      torch.from_numpy(wv), segs)
+    ref = conv_backward_ref(x, wt, wv, segs, dy)
+    np.testing.assert_allclose(to_host(dx), ref["dx"], rtol=2.0 ** -8, atol=1e-4)
+    for got, want in ((dwt, ref["dw_text"]), (dwv, ref["dw_vis"])):
+        np.testing.assert_allclose(to_host(got), want, rtol=1e-4, atol=1e-4 * np.abs(want).max())
 
 
 def test_pipeline_backward_bf16(chm):
