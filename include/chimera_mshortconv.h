@@ -320,11 +320,14 @@ chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const 
  *   dbeta     device [B][T][H], written, dtype dt
  *   dS0       device fp32 [B][H][dk][dv], written, or NULL
  *   workspace at least chimera_kda_bwd_workspace_size(...) bytes: the state before every
- *             16th token (from a forward pass inside the call) and per-slice partial sums
+ *             16th token (from forward passes inside the call), per-slice partial sums, and
+ *             per-segment states when the sequences are cut into segments
  *
  * dk <= 128 (CHIMERA_ERR_UNSUPPORTED above). The recurrence runs token by token in fp32
- * (a checkpointed reverse pass); the flags that choose forward kernels are ignored.
- * Asynchronous on `stream`; the outputs must not alias the inputs.
+ * (a checkpointed reverse pass); long sequences are cut into segments that run at once,
+ * joined through each segment's transition product (the cut depends only on B, T, H and
+ * dv); the flags that choose forward kernels are ignored. Asynchronous on `stream`; the
+ * outputs must not alias the inputs.
  */
 size_t chimera_kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
                                       uint32_t flags);

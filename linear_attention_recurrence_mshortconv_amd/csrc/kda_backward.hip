@@ -10,20 +10,28 @@
 //   dalpha_t = rowsum(dP o S_{t-1});  G <- Diag(alpha_t) dP;  dS0 = G at the start.
 // The states S_{t-1} come from a forward pass that keeps the state before every
 // 16th token (kda_seq_kernel with a checkpoint buffer); each 16-token block is
-// recomputed from its checkpoint, eight states at a time in registers.
+// recomputed from its checkpoint, four states at a time in registers.
 //
-// One block per (batch, head, 16-column slice of d_v), 256 threads = 16 columns x
-// 16 row-threads as in the forward kernel: the column-wise quantities (dv) are
-// complete in a block, the row-wise ones (dq, dk, dalpha, dbeta) are sums over all
-// columns: each block sums its 16 columns (permlane swaps inside a wave, LDS atomic
-// adds across the four waves, written out once per eight tokens) and writes a
-// per-slice partial; a second kernel adds the slices and applies the L2
+// Both directions run on segments of each sequence at once. The map from a
+// segment's start state to its end state is S_end = M S_start + L, with M the
+// product of the segment's transitions (I - beta k k^T) Diag(alpha), so the start
+// states follow from every segment's (M, L) by a short chain, and dL/dS at the
+// segment ends from G_start = M^T G_end + E, E being the segment's own part (its
+// reverse recurrence from G = 0).
+//
+// One block per (batch, head, segment, 16-column slice of d_v), 256 threads = 16
+// columns x 16 row-threads as in the forward kernel: the column-wise quantities
+// (dv) are complete in a block, the row-wise ones (dq, dk, dalpha, dbeta) are sums
+// over all columns: each wave sums its 4 columns (permlane swaps) into its own LDS
+// slots, the four waves' slots are added as they are written out every four tokens
+// to a per-slice partial, and a second kernel adds the slices and applies the L2
 // normalisation's backward. Gradients of q, k and v are written at the inputs'
 // token stride, so that they can fill one fused q|k|v gradient for the conv.
 //
 // mShortConv (page 1, section 3.4; Eq. 13): y[p, c] = sum_taps w[c, tap] x[src(p, tap), c]
 // gives dx[s, c] = sum over (p, tap) with src(p, tap) = s of w[c, tap] dy[p, c] (the
-// adjoint gather: p is s moved back by the tap's offset, inside the same segment) and
+// adjoint gather: p is s moved back by the tap's offset, inside the same segment; for an
+// image grid, the same 3x3 conv with the taps mirrored in both directions) and
 // dw[c, tap] = sum_p x[src(p, tap), c] dy[p, c] (summed over tokens and batch items).
 #include <vector>
 
@@ -58,9 +66,9 @@ __device__ __forceinline__ float sum_cols4(float x) {
 
 
 // Stages tokens tok0 .. tok0 + nt - 1 (rows of the [B*T] token axis) of one head in LDS: thread
-// (colid, rt) loads token colid, rows rt + 16 i of q and k (L2-normalised) and alpha, and
-// column vs * 16 + rt of v (when sv is given) and of dout; tokens past nt read as q = k = 0,
-// alpha = 1, beta = 0.
+// (colid, rt) loads token colid, rows RPT rt .. RPT rt + RPT - 1 of q and k (L2-normalised)
+// and alpha, and column vs * 16 + rt of v (when sv is given) and of dout; tokens past nt
+// read as q = k = 0, alpha = 1, beta = 0.
 template <typename T, int RPT>
 __device__ __forceinline__ void stage_tokens(const T* __restrict__ q, const T* __restrict__ k,
                                              const T* __restrict__ v, int64_t stride, const T* __restrict__ alpha,
@@ -75,7 +83,7 @@ __device__ __forceinline__ void stage_tokens(const T* __restrict__ q, const T* _
   float rq[RPT], rk[RPT], ssq = 0.f, ssk = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rt + 16 * i;
+    const int row = RPT * rt + i;
     const bool ok = tok_ok && row < dk;
     rq[i] = ok ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
     rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
@@ -87,8 +95,8 @@ __device__ __forceinline__ void stage_tokens(const T* __restrict__ q, const T* _
   const float nk = l2norm ? 1.f / sqrtf(sum16(ssk) + 1e-6f) : 1.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    sq[colid][rt + 16 * i] = rq[i] * nq;
-    sk[colid][rt + 16 * i] = rk[i] * nk;
+    sq[colid][RPT * rt + i] = rq[i] * nq;
+    sk[colid][RPT * rt + i] = rk[i] * nk;
   }
   const int vc = vs * 16 + rt;   // token colid, column rt of the slice
   if (sv != nullptr) sv[colid][rt] = (tok_ok && vc < dv) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
   float G[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rt + 16 * i;
+    const int row = RPT * rt + i;
     G[i] = (G_end != nullptr && col_ok && row < dk) ? G_end[((bh * nseg + p) * dk + row) * dv + col] : 0.f;
   }
 
@@ -163,13 +171,13 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
     float pred = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      S[i] *= sa[tt][rt + 16 * i];
-      pred = fmaf(S[i], sk[tt][rt + 16 * i], pred);
+      S[i] *= sa[tt][RPT * rt + i];
+      pred = fmaf(S[i], sk[tt][RPT * rt + i], pred);
     }
     const float w = sv[tt][colid] - sum16(pred);
     const float bw = sb[tt] * w;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) S[i] = fmaf(sk[tt][rt + 16 * i], bw, S[i]);
+    for (int i = 0; i < RPT; ++i) S[i] = fmaf(sk[tt][RPT * rt + i], bw, S[i]);
     return w;
   };
 
@@ -183,7 +191,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
     float S0c[RPT];   // the state before token t0
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int row = rt + 16 * i;
+      const int row = RPT * rt + i;
       S0c[i] = (col_ok && row < dk) ? ckpt[((bh * nb + kb) * dk + row) * dv + col] : 0.f;
     }
     for (int part = kCk / kHalf - 1; part >= 0; --part) {
@@ -215,8 +223,8 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
         float r = 0.f;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          G[i] = fmaf(sq[tt][rt + 16 * i], doc, G[i]);
-          r = fmaf(G[i], sk[tt][rt + 16 * i], r);
+          G[i] = fmaf(sq[tt][RPT * rt + i], doc, G[i]);
+          r = fmaf(G[i], sk[tt][RPT * rt + i], r);
         }
         r = sum16(r);
         if (rt == 0 && col_ok) from_f32(dv_out + (b * Tn + t0 + tt) * stride + h * dv + col, bt * r);
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
         float vals[kNV];   // dq, dk, dalpha of the lane's rows (then zero padding)
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          const int row = rt + 16 * i;
+          const int row = RPT * rt + i;
           const float a = sa[tt][row];
           const float dP = G[i] - bt * sk[tt][row] * r;
           vals[i] = St[i] * doc;
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
 #pragma unroll
         for (int n = 0; n < kNV / 4; ++n) {   // lane of wave row cw holds value 4 n + cw
           const int f = 4 * n + cw;
-          if (f < 3 * RPT) red[j][wave][f / RPT][rt + 16 * (f % RPT)] = sums[n];
+          if (f < 3 * RPT) red[j][wave][f / RPT][RPT * rt + f % RPT] = sums[n];
         }
       }
       __syncthreads();
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(
   if (dS0 != nullptr && col_ok && p == 0) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int row = rt + 16 * i;
+      const int row = RPT * rt + i;
       if (row < dk) dS0[(bh * dk + row) * dv + col] = G[i];
     }
   }
@@ -300,18 +308,18 @@ __global__ __launch_bounds__(256) void kda_bwd_local_kernel(
       float r = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        G[i] = fmaf(sq[tt][rt + 16 * i], doc, G[i]);
-        r = fmaf(G[i], sk[tt][rt + 16 * i], r);
+        G[i] = fmaf(sq[tt][RPT * rt + i], doc, G[i]);
+        r = fmaf(G[i], sk[tt][RPT * rt + i], r);
       }
       const float br = sb[tt] * sum16(r);
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) G[i] = sa[tt][rt + 16 * i] * fmaf(-sk[tt][rt + 16 * i], br, G[i]);
+      for (int i = 0; i < RPT; ++i) G[i] = sa[tt][RPT * rt + i] * fmaf(-sk[tt][RPT * rt + i], br, G[i]);
     }
   }
   if (col < dv) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int row = rt + 16 * i;
+      const int row = RPT * rt + i;
       if (row < dk) E[((bh * nseg + p) * dk + row) * dv + col] = G[i];
     }
   }
@@ -520,12 +528,18 @@ __global__ __launch_bounds__(256) void conv_bwd_dx_kernel(const T* __restrict__ 
   store8(dx + (b * Ttot + s) * C + c0, acc);
 }
 
-// dw: a thread owns 4 channels and a range of tokens of one segment, accumulates every
-// tap's sum of x[src] dy in registers, then adds it to dw with one atomic per value
-template <typename T, int TAPS>
+// dw: a thread owns 4 channels and a range of tokens of one segment, walks the range in
+// raster order (grid coordinates advanced token by token, no divisions in the loop),
+// accumulates every tap's sum of x[src] dy in registers, then adds it to dw with one atomic
+// per value. KIND: text (4 taps), one-frame grid (the 9 taps of the current frame, dw_vis
+// taps 18..26: earlier frames do not exist), video (27 taps).
+template <typename T, int KIND>
 __global__ __launch_bounds__(256) void conv_bwd_dw_kernel(const T* __restrict__ x, const T* __restrict__ dy,
                                                           float* __restrict__ dw, int64_t Ttot, int64_t C, Seg seg,
                                                           int64_t tokens_per_range) {
+  constexpr int TAPS = KIND == SEG_TEXT ? kTextTaps : KIND == SEG_IMAGE ? 9 : kVisTaps;
+  constexpr int TAP0 = KIND == SEG_IMAGE ? 18 : 0;
+  constexpr int NW = KIND == SEG_TEXT ? kTextTaps : kVisTaps;
   const int64_t C4 = C / 4;
   const int64_t cg = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t p0 = (int64_t)blockIdx.y * tokens_per_range;
@@ -544,11 +558,18 @@ __global__ __launch_bounds__(256) void conv_bwd_dw_kernel(const T* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = to_f32(p[i]);
   };
+  int f = 0, hh = 0, ww = 0;   // grid point of token p0
+  if (KIND != SEG_TEXT) {
+    const int64_t hw = (int64_t)seg.height * seg.width;
+    f = (int)(p0 / hw);
+    hh = (int)((p0 / seg.width) % seg.height);
+    ww = (int)(p0 % seg.width);
+  }
   for (int64_t local = p0; local < p1; ++local) {
     const int64_t p = seg.start + local;
     float g[4];
     ld4(dyb + p * C + c0, g);
-    if (TAPS == kTextTaps) {
+    if (KIND == SEG_TEXT) {
 #pragma unroll
       for (int j = 0; j < TAPS; ++j) {
         const int64_t src = text_tap_source(seg, p, j);
@@ -559,23 +580,29 @@ __global__ __launch_bounds__(256) void conv_bwd_dw_kernel(const T* __restrict__ 
         for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(xv[i], g[i], acc[j][i]);
       }
     } else {
-      const int64_t hw = (int64_t)seg.height * seg.width;
-      const int64_t f = local / hw, hh = (local / seg.width) % seg.height, ww = local % seg.width;
 #pragma unroll
       for (int t = 0; t < TAPS; ++t) {
-        const int64_t src = vis_tap_source(seg, f, hh, ww, t / 9, (t / 3) % 3, t % 3);
-        if (src < 0) continue;
+        const int tap = TAP0 + t;
+        const int ff = f + tap / 9 - 2, h2 = hh + (tap / 3) % 3 - 1, w2 = ww + tap % 3 - 1;
+        if (ff < 0 || h2 < 0 || h2 >= seg.height || w2 < 0 || w2 >= seg.width) continue;
         float xv[4];
-        ld4(xb + src * C + c0, xv);
+        ld4(xb + raster_index(seg, ff, h2, w2) * C + c0, xv);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(xv[i], g[i], acc[t][i]);
+      }
+      if (++ww == seg.width) {
+        ww = 0;
+        if (++hh == seg.height) {
+          hh = 0;
+          ++f;
+        }
       }
     }
   }
 #pragma unroll
   for (int t = 0; t < TAPS; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) atomicAdd(dw + (c0 + i) * TAPS + t, acc[t][i]);
+    for (int i = 0; i < 4; ++i) atomicAdd(dw + (c0 + i) * NW + TAP0 + t, acc[t][i]);
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -618,10 +645,13 @@ hipError_t conv_bwd_t(const void* x, const void* dy, void* dx, float* dw_text, f
     const int64_t per = std::max<int64_t>(16, (sg.length + 511) / 512);
     const dim3 gw((unsigned)((C / 4 + 255) / 256), (unsigned)((sg.length + per - 1) / per), (unsigned)B);
     if (sg.kind == SEG_TEXT)
-      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, kTextTaps>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
+      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_TEXT>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
                          static_cast<const T*>(dy), dw_text, Ttot, C, sg, per);
+    else if (sg.frames == 1)
+      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_IMAGE>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
+                         static_cast<const T*>(dy), dw_vis, Ttot, C, sg, per);
     else
-      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, kVisTaps>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
+      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_VIDEO>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
                          static_cast<const T*>(dy), dw_vis, Ttot, C, sg, per);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

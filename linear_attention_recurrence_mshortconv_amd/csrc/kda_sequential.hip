@@ -8,7 +8,7 @@
 // (page 1, section 5.6: FP32 KDA state).
 //
 // One block per (batch, head, 16-column slice of d_v); 256 threads = 16 columns
-// x 16 row-threads. A row-thread holds rows rt, rt+16, ... (RPT of them) of its
+// x 16 row-threads. A row-thread holds rows RPT rt .. RPT rt + RPT - 1 of its
 // column in registers; the 16 row-threads of a column are one DPP row, so the two
 // reductions over d_k per token are four DPP adds each. Tokens are staged in LDS
 // 16 at a time, double-buffered: the next batch's loads are in flight while the
@@ -36,7 +36,8 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-template <typename T, int RPT>
+// OUT false: no readout (o is not written; the state passes of the backward).
+template <typename T, int RPT, bool OUT>
 __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                       const T* __restrict__ v, int64_t stride,
                                                       const T* __restrict__ alpha, const T* __restrict__ beta,
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
                                                       int dv, int l2norm, float* __restrict__ ckpt, SeqSegs sg) {
   constexpr int DKP = 16 * RPT;   // staged rows; rows past dk hold k = q = 0, alpha = 1
   __shared__ float sk[2][kTokBatch][DKP];
-  __shared__ float sq[2][kTokBatch][DKP];
+  __shared__ float sq[2][OUT ? kTokBatch : 1][OUT ? DKP : 1];   // q only for the readout
   __shared__ float sa[2][kTokBatch][DKP];
   __shared__ float sv[2][kTokBatch][16];
   __shared__ float sb[2][kTokBatch];
@@ -69,12 +70,12 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
   float s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rt + 16 * i;
+    const int row = RPT * rt + i;
     s[i] = sg.identity ? (col_ok && row == col ? 1.f : 0.f)
                        : (init != nullptr && col_ok && row < dk) ? init[row * dv + col] : 0.f;
   }
 
-  // one batch of tokens: thread (colid, rt) loads token colid, rows rt + 16 i
+  // one batch of tokens: thread (colid, rt) loads token colid, rows RPT rt .. RPT rt + RPT - 1
   float rk[RPT], rq[RPT], ra[RPT], rv, rb;
   auto load = [&](int64_t t0) {
     const int nt = (int)min<int64_t>(kTokBatch, t_end - t0);
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
     const int64_t tok = b * Tn + t0 + colid;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int row = rt + 16 * i;
+      const int row = RPT * rt + i;
       const bool ok = tok_ok && row < dk;
       rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
       rq[i] = ok && q != nullptr ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
@@ -111,9 +112,9 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      sk[buf][colid][rt + 16 * i] = rk[i];
-      sq[buf][colid][rt + 16 * i] = rq[i];
-      sa[buf][colid][rt + 16 * i] = ra[i];
+      sk[buf][colid][RPT * rt + i] = rk[i];
+      if (OUT) sq[buf][colid][RPT * rt + i] = rq[i];
+      sa[buf][colid][RPT * rt + i] = ra[i];
     }
     sv[buf][colid][rt] = rv;
     if (rt == 0) sb[buf][colid] = rb;
@@ -133,13 +134,13 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
       float* dst = ckpt + ((bh * ((Tn + kTokBatch - 1) / kTokBatch) + t0 / kTokBatch) * dk) * dv + col;
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
-        if (rt + 16 * i < dk) dst[(int64_t)(rt + 16 * i) * dv] = s[i];
+        if (RPT * rt + i < dk) dst[(int64_t)(RPT * rt + i) * dv] = s[i];
     }
     for (int tt = 0; tt < nt; ++tt) {
       float pred = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const int row = rt + 16 * i;
+        const int row = RPT * rt + i;
         s[i] *= sa[buf][tt][row];
         pred = fmaf(s[i], sk[buf][tt][row], pred);
       }
@@ -148,12 +149,14 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
       float out = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const int row = rt + 16 * i;
+        const int row = RPT * rt + i;
         s[i] = fmaf(sk[buf][tt][row], u, s[i]);
-        out = fmaf(s[i], sq[buf][tt][row], out);
+        if (OUT) out = fmaf(s[i], sq[buf][tt][row], out);
       }
-      out = sum16(out);
-      if (rt == 0 && col_ok && o != nullptr) from_f32(o + ((b * Tn + t0 + tt) * H + h) * dv + col, out);
+      if (OUT) {
+        out = sum16(out);
+        if (rt == 0 && col_ok) from_f32(o + ((b * Tn + t0 + tt) * H + h) * dv + col, out);
+      }
     }
     if (more) stage(buf ^ 1);                        // the other buffer was last read a batch ago
     __syncthreads();
@@ -162,14 +165,14 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
   if (S_final != nullptr && col_ok && p == sg.nseg - 1) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int row = rt + 16 * i;
+      const int row = RPT * rt + i;
       if (row < dk) S_final[(bh * dk + row) * dv + col] = s[i];
     }
   }
   if (sg.Send != nullptr && col_ok) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int row = rt + 16 * i;
+      const int row = RPT * rt + i;
       if (row < dk) sg.Send[(seg_ix * dk + row) * dv + col] = s[i];
     }
   }
@@ -218,16 +221,21 @@ hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, floa
   T* o = static_cast<T*>(a.o);
   const dim3 g((unsigned)blocks), t(256);
   const int dk = (int)a.dk, dv = (int)a.dv, nrm = (int)a.l2norm;
-  if (dk <= 16)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 1>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
-  else if (dk <= 32)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 2>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
-  else if (dk <= 64)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 4>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
-  else if (dk <= 128)
-    hipLaunchKernelGGL((kda_seq_kernel<T, 8>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
-  else
-    hipLaunchKernelGGL((kda_seq_kernel<T, 16>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o, a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);
+#define CHM_SEQ(R)                                                                                                  \
+  do {                                                                                                              \
+    if (o != nullptr)                                                                                               \
+      hipLaunchKernelGGL((kda_seq_kernel<T, R, true>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o,      \
+                         a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);                                               \
+    else                                                                                                            \
+      hipLaunchKernelGGL((kda_seq_kernel<T, R, false>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o,     \
+                         a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);                                               \
+  } while (0)
+  if (dk <= 16) CHM_SEQ(1);
+  else if (dk <= 32) CHM_SEQ(2);
+  else if (dk <= 64) CHM_SEQ(4);
+  else if (dk <= 128) CHM_SEQ(8);
+  else CHM_SEQ(16);
+#undef CHM_SEQ
   return hipGetLastError();
 }
 
