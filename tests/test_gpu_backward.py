@@ -53,13 +53,12 @@ def _run(chm, dtype, q, k, v, alpha, beta, S0, do, dS):
     return {n: to_host(t) for n, t in g.items()}
 
 
-def test_kda_bwd_fp32_odd_dims(chm):
-    """fp32, dk != dv (not multiples of 16), two batch items; q, k, v and their gradients are
-    views into fused tensors (the shared token stride)."""
+def _run_fused_fp32(chm, q, k, v, alpha, beta, S0, do, dS):
+    """q, k, v and their gradients as views into fused [B, T, H*(2 dk + dv)] tensors (the
+    shared token stride the entry point requires when dk != dv)."""
     import torch
-    rng = np.random.default_rng(120)
-    B, T, H, dk, dv = 2, 77, 3, 20, 37
-    q, k, v, alpha, beta, S0, do, dS = _case(rng, B, T, H, dk, dv, "f32")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
     W = H * (2 * dk + dv)
     fused = torch.from_numpy(np.concatenate([q.reshape(B, T, -1), k.reshape(B, T, -1), v.reshape(B, T, -1)],
                                             axis=-1)).cuda()
@@ -68,8 +67,16 @@ def test_kda_bwd_fp32_odd_dims(chm):
     gfused = torch.zeros(B, T, W, device="cuda")
     dev = lambda a: torch.from_numpy(a).cuda()
     g = chm.kda_bwd(*views(fused), dev(alpha), dev(beta), dev(S0), dev(do), dev(dS), grads=views(gfused))
-    got = {n: to_host(t) for n, t in g.items()}
-    ref = kda_backward_ref(q, k, v, alpha, beta, S0, do, dS)
+    return {n: to_host(t) for n, t in g.items()}
+
+
+def test_kda_bwd_fp32_odd_dims(chm):
+    """fp32, dk != dv (not multiples of 16), two batch items; q, k, v and their gradients are
+    views into fused tensors (the shared token stride)."""
+    rng = np.random.default_rng(120)
+    args = _case(rng, 2, 77, 3, 20, 37, "f32")
+    got = _run_fused_fp32(chm, *args)
+    ref = kda_backward_ref(*args)
     for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
         assert_close(got[n], ref[n], "f32", n)
 
@@ -91,6 +98,17 @@ def test_kda_bwd_fp32_segments(chm):
     rng = np.random.default_rng(124)
     args = _case(rng, 1, 700, 2, 32, 32, "f32")
     got = _run(chm, "f32", *args)
+    ref = kda_backward_ref(*args)
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        assert_close(got[n], ref[n], "f32", n)
+
+
+def test_kda_bwd_fp32_odd_dims_segments(chm):
+    """fp32, dk = 20, dv = 37 (the last 16-column slice partly outside), T = 400: five segments
+    of 80 tokens; chains over a ragged column slice."""
+    rng = np.random.default_rng(127)
+    args = _case(rng, 1, 400, 1, 20, 37, "f32")
+    got = _run_fused_fp32(chm, *args)
     ref = kda_backward_ref(*args)
     for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
         assert_close(got[n], ref[n], "f32", n)
