@@ -124,6 +124,15 @@ def test_kda_bwd_bf16_segments_batch(chm):
         _close_bf16(got[n], ref[n], f"{n} segmented")
 
 
+def test_kda_bwd_empty_sequence(chm):
+    """T = 0: nothing to carry back, so dS0 = dS_final and the token gradients are empty."""
+    rng = np.random.default_rng(128)
+    args = _case(rng, 1, 0, 2, 128, 128, "bf16")
+    got = _run(chm, "bf16", *args)
+    assert np.array_equal(got["dS0"], args[-1].astype(np.float64))
+    assert got["dq"].shape == (1, 0, 2, 128) and got["dbeta"].shape == (1, 0, 2)
+
+
 def test_conv_bwd_fp32_mixed_layout(chm):
     import torch
     S = wl.Segment
