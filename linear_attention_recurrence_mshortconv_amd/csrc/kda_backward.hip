@@ -37,6 +37,7 @@
 
 #include "dtypes.h"
 #include "internal.h"
+#include "lanes.h"
 
 namespace chm {
 namespace {
@@ -44,25 +45,6 @@ namespace {
 constexpr int kCk = 16;   // tokens per checkpoint (the forward kernel's token batch)
 constexpr int kHalf = 4;  // states recomputed and kept at a time
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-// sum over the 16 lanes of a DPP row (the row-threads of one column), in every lane
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  x += dpp<0x140>(x);
-  return x;
-}
-// sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four columns of one wave), in every lane
-__device__ __forceinline__ float sum_cols4(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-  x = __int_as_float(r[0]) + __int_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
 
 
 // Stages tokens tok0 .. tok0 + nt - 1 (rows of the [B*T] token axis) of one head in LDS: thread
@@ -102,28 +84,6 @@ __device__ __forceinline__ void stage_tokens(const T* __restrict__ q, const T* _
   if (sv != nullptr) sv[colid][rt] = (tok_ok && vc < dv) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
   sdo[colid][rt] = (tok_ok && vc < dv) ? to_f32(dout[(tok * H + h) * dv + vc]) : 0.f;
   if (rt == 0) sb[colid] = tok_ok ? to_f32(beta[tok * H + h]) : 0.f;
-}
-
-// Sums over the four columns of one wave (lanes l, l ^ 16, l ^ 32, l ^ 48) of NV values at
-// once (NV a multiple of 4): a permlane16 swap of two values leaves the first's pair sums in
-// wave rows 0 and 2 and the second's in rows 1 and 3, and a permlane32 swap of two such
-// results completes four values, one per wave row: out[n] in wave row w is the total of
-// v[4 n + w].
-template <int NV>
-__device__ __forceinline__ void sum_cols4_many(const float (&v)[NV], float (&out)[NV / 4]) {
-  float s1[NV / 2];
-#pragma unroll
-  for (int m = 0; m < NV / 2; ++m) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v[2 * m]), __float_as_int(v[2 * m + 1]), false,
-                                                    false);
-    s1[m] = __int_as_float(r[0]) + __int_as_float(r[1]);
-  }
-#pragma unroll
-  for (int n = 0; n < NV / 4; ++n) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(s1[2 * n]), __float_as_int(s1[2 * n + 1]), false,
-                                                    false);
-    out[n] = __int_as_float(r[0]) + __int_as_float(r[1]);
-  }
 }
 
 template <typename T, int RPT>

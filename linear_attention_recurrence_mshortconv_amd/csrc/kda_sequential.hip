@@ -15,26 +15,12 @@
 // current batch runs.
 #include "dtypes.h"
 #include "internal.h"
+#include "lanes.h"
 
 namespace chm {
 namespace {
 
 constexpr int kTokBatch = 16;
-
-// x moved from the lane given by the DPP control CTRL (all rows and banks)
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-// sum over the 16 lanes of a DPP row, in every lane: xor 1, xor 2 (quad
-// permutes), then the half-row and row mirrors
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  x += dpp<0x140>(x);
-  return x;
-}
 
 // OUT false: no readout (o is not written; the state passes of the backward).
 template <typename T, int RPT, bool OUT>
