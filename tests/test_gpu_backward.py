@@ -133,6 +133,57 @@ def test_kda_bwd_empty_sequence(chm):
     assert got["dq"].shape == (1, 0, 2, 128) and got["dbeta"].shape == (1, 0, 2)
 
 
+def test_kda_bwd_full_size_directional(chm):
+    """The image_4096 sizes in the training-step bench's configuration (65,792 tokens, 16 heads,
+    d = 128, q|k|v as views into one fused bf16 tensor: 16 segments of 4,112 tokens, both chains).
+    For head 5: the GPU gradients of all five inputs, paired with a random direction over the whole
+    sequence, against the central difference of the fp64 oracle's loss sum(o * do) +
+    sum(S_final * dS_final) along it; and the gradients of the last 2,048 tokens element by element
+    against the fp64 autograd oracle run from the oracle's state before them."""
+    import torch
+    from oracle import kda_ref, l2norm_ref
+    T, H, d, hd, tail = 65792, 16, 128, 5, 2048
+    rng = np.random.default_rng(129)
+    y = wl.round_to_bf16(rng.standard_normal((1, T, 3 * H * d), dtype=np.float32))
+    alpha = wl.round_to_bf16(np.exp(-0.05 * np.logaddexp(0, rng.standard_normal((1, T, H, d), dtype=np.float32))))
+    beta = wl.round_to_bf16(1 / (1 + np.exp(-rng.standard_normal((1, T, H), dtype=np.float32))))
+    do = wl.round_to_bf16(rng.standard_normal((1, T, H, d), dtype=np.float32))
+    dS = (0.1 * rng.standard_normal((1, H, d, d))).astype(np.float32)
+    yd = to_device(y, "bf16")
+    dy = torch.zeros_like(yd)
+    g = chm.kda_bwd(*chm.split_qkv(yd, H, d), to_device(alpha, "bf16"), to_device(beta, "bf16"), None,
+                    to_device(do, "bf16"), torch.from_numpy(dS).cuda(), grads=chm.split_qkv(dy, H, d))
+    gy = to_host(dy.view(T, 3, H, d)[:, :, hd])
+    grad = [gy[:, 0], gy[:, 1], gy[:, 2], to_host(g["dalpha"][0, :, hd]), to_host(g["dbeta"][0, :, hd])]
+    del yd, dy, g
+    y5 = y.reshape(T, 3, H, d)[:, :, hd].astype(np.float64)
+    theta = [y5[:, 0], y5[:, 1], y5[:, 2], alpha[0, :, hd].astype(np.float64), beta[0, :, hd].astype(np.float64)]
+    do5, dS5 = do[0, :, hd].astype(np.float64), dS[0, hd].astype(np.float64)
+
+    def loss(x):
+        e = lambda a: a[None, :, None]
+        o, S = kda_ref(l2norm_ref(e(x[0])), l2norm_ref(e(x[1])), e(x[2]), e(x[3]), x[4][None, :, None])
+        return float((o[0, :, 0] * do5).sum() + (S[0, 0] * dS5).sum())
+
+    h = 1e-5
+    dirs = [rng.standard_normal(t.shape) for t in theta]
+    fd = (loss([t + h * dd for t, dd in zip(theta, dirs)]) - loss([t - h * dd for t, dd in zip(theta, dirs)])) / (2 * h)
+    gpu = sum(float((gi * di).sum()) for gi, di in zip(grad, dirs))
+    print(f"all inputs, whole sequence: GPU {gpu:.6e}, oracle {fd:.6e}", flush=True)
+    assert abs(gpu - fd) <= 1e-2 * abs(fd), (gpu, fd)
+    # the last `tail` tokens element by element: their gradients depend on the tokens before
+    # them only through the state there
+    lo = T - tail
+    e = lambda a: a[None, :lo, None]
+    _, S_mid = kda_ref(l2norm_ref(e(theta[0])), l2norm_ref(e(theta[1])), e(theta[2]), e(theta[3]),
+                       theta[4][None, :lo, None])
+    t4 = lambda a: a[None, lo:, None]
+    ref = kda_backward_ref(t4(theta[0]), t4(theta[1]), t4(theta[2]), t4(theta[3]), theta[4][None, lo:, None], S_mid,
+                           t4(do5), dS5[None, None])
+    for i, name in enumerate(("dq", "dk", "dv", "dalpha", "dbeta")):
+        _close_bf16(grad[i][lo:], ref[name][0, :, 0], f"{name}, last {tail} tokens")
+
+
 def test_conv_bwd_fp32_mixed_layout(chm):
     import torch
     S = wl.Segment
