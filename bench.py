@@ -24,7 +24,9 @@ image_1024, video_5s, video_30s) are measured the same way with --workload.
 --backward times a training step instead: the two forward calls, then
 chimera_kda_bwd (writing dq, dk, dv straight into one fused q|k|v gradient) and
 chimera_mshortconv_bwd on it, against a synthetic dL/do; each call is bracketed
-by HIP events on the stream.
+by HIP events on the stream. --fused times chimera_kda_fwd_conv (the conv computed
+inside the token-by-token recurrence, q|k|v never stored) beside the same step as
+two calls on the same recurrence kernel.
 
 Two helper modes turn rocprofv3 output into the summaries kept with the code:
   python bench.py --summarize-stats <kernel_stats.csv>
@@ -94,6 +96,9 @@ def _args():
                     help="KDA with the output gate and norm of Eq. 15 (Sigmoid(gate) * RMSNorm(o))")
     ap.add_argument("--backward", action="store_true",
                     help="a training step: forward, then the KDA and conv backward (gradients of a synthetic dL/do)")
+    ap.add_argument("--fused", action="store_true",
+                    help="the conv fused into the token-by-token recurrence (chimera_kda_fwd_conv), against the "
+                         "two calls on the same recurrence kernel")
     ap.add_argument("--cpu-sample-tokens", type=int, default=20736,
                     help="tokens per sequence in the oracle's timed sample (text + whole grid rows/frames)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
@@ -381,6 +386,74 @@ def bench_backward(args, w):
     print(json.dumps(out), flush=True)
 
 
+def bench_fused(args, w):
+    """The fused conv + recurrence (one kernel, q|k|v never stored) on the workload, timed with HIP
+    events around each call on the stream; beside it the same step as two calls (conv, then the
+    token-by-token recurrence on the stored q|k|v)."""
+    import torch
+    import workloads as wl
+    import linear_attention_recurrence_mshortconv_amd as chm
+    assert not w.samples, "the fused call takes batched (not packed) workloads"
+    B, T, H, d = w.B, w.T, w.H, w.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    to_dev = lambda a: torch.from_numpy(a).to(tdt).to(dev)
+    x, alpha, beta = to_dev(inp["x"]), to_dev(inp["alpha"]), to_dev(inp["beta"])
+    S0 = None if inp["S0"] is None else torch.from_numpy(inp["S0"]).to(dev)
+    wt, wv = torch.from_numpy(inp["w_text"]).to(dev), torch.from_numpy(inp["w_vis"]).to(dev)
+    segs = w.segments
+    y = torch.empty_like(x)
+    q, k, v = chm.split_qkv(y, H, d)
+    o = torch.empty(B, T, H, d, dtype=tdt, device=dev)
+    s_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fused():
+        chm.kda_fwd_conv(x, wt, wv, segs, alpha, beta, S0, H=H, dk=d, dv=d, out=o, state_out=s_final)
+
+    def two_calls():
+        chm.mshortconv_fwd(x, wt, wv, segs, out=y)
+        chm.kda_fwd(q, k, v, alpha, beta, S0, sequential=True, out=o, state_out=s_final)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+
+    ms_fused = timed(fused)
+    ms_two = timed(two_calls)
+    e = 2 if w.dtype == "bf16" else 4
+    # minimal traffic per token-head: x's q|k|v channels, alpha, beta in; o out
+    fused_bytes = B * T * H * (5 * d + 1) * e
+    out = {
+        "metric": "KDA+mShortConv fused fwd tokens/sec/GPU",
+        "value": B * T / (ms_fused * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_fused, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": f"synthetic (seeded; {w.dtype} x, alpha, beta; fp32 conv weights; fp32 state)",
+        "config": {"workload": f"{w.name}: {T} tokens per sequence, B={B}, H={H}, d={d}; the conv computed in the "
+                               f"token-by-token recurrence's load stage (q|k|v never stored)",
+                   "tokens_per_step": B * T, "ms_two_calls_same_recurrence": ms_two,
+                   "two_calls_tokens_per_s": B * T / (ms_two * 1e-3)},
+        "roofline": {"bound": "hbm", "kernel": "kda_seq_kernel (fused conv)", "achieved":
+                     fused_bytes / (ms_fused * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": fused_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "ms_per_launch": ms_fused, "algorithmic_bytes_per_launch": fused_bytes,
+                     "recipe": f"x's q|k|v channels, alpha, beta in and o out: {(5 * d + 1) * e} B per token-head"},
+        "cpu_baseline": None if args.no_cpu_baseline else _cpu_baseline(inp, w, args.cpu_sample_tokens),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = _args()
     if args.summarize_stats:
@@ -402,6 +475,9 @@ def main():
     w = by_name[args.workload] if args.workload in by_name else wl.WORKLOADS[int(args.workload)]
     if args.backward:
         bench_backward(args, w)
+        return
+    if args.fused:
+        bench_fused(args, w)
         return
     B, T, H, d = w.B, w.T, w.H, w.d
     dev = torch.device("cuda:0")

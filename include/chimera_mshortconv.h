@@ -186,6 +186,31 @@ chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int6
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * chimera_kda_fwd_conv -- mShortConv and KDA in one pass (Chimera page 1, section 3.4:
+ * the conv on packed storage fused with the recurrence; Eq. 13 then Eq. 14): q, k and v of
+ * every token are computed from x in the recurrence's load stage, rounded to dt as
+ * chimera_mshortconv_fwd would store them, and never written to memory. The result equals
+ * chimera_mshortconv_fwd followed by chimera_kda_fwd with CHIMERA_KDA_SEQUENTIAL on the
+ * views q, k, v = y[..., 0:H*dk], y[..., H*dk:2*H*dk], y[..., 2*H*dk:] (up to the order of
+ * the conv's fp32 sums).
+ *
+ *   x         device [B][T][C], dt, C = H * (2 * dk + dv): the q, k, v channels in that
+ *             order, head-major inside each
+ *   w_text, w_vis, segs, nseg   as for chimera_mshortconv_fwd (nseg <= 32 here)
+ *   alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt   as for chimera_kda_fwd
+ *   flags     CHIMERA_KDA_L2NORM_QK (CHIMERA_KDA_SEQUENTIAL is accepted and implied)
+ *
+ * Runs on the token-by-token fp32 kernel (dk <= 128, else CHIMERA_ERR_UNSUPPORTED; more
+ * than 32 segments likewise); the chunked MFMA path keeps the two calls. No workspace; o
+ * must not alias x. Asynchronous on `stream`.
+ */
+chimera_status chimera_kda_fwd_conv(const void* x, const float* w_text, const float* w_vis,
+                                    const chimera_segment* segs, int32_t nseg, const void* alpha,
+                                    const void* beta, const float* S0, void* o, float* S_final,
+                                    int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                    chimera_dtype dt, uint32_t flags, hipStream_t stream);
+
+/*
  * Per-kernel timing variants. Each runs exactly the launches of the call it is
  * named after, with the same arguments and results, and additionally records
  * HIP events on `stream`: marks[0] before the first kernel, then marks[i] right

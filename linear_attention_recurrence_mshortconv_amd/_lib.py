@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
     L.chimera_kda_fwd_varlen.restype = ctypes.c_int
     L.chimera_kda_fwd_varlen.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, vp, ctypes.c_float, vp, vp,
                                          vp, i32, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.chimera_kda_fwd_conv.restype = ctypes.c_int
+    L.chimera_kda_fwd_conv.argtypes = [vp, vp, vp, seg_p, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                       ctypes.c_int, u32, vp]
     L.chimera_kda_fwd_varlen_timed.restype = ctypes.c_int
     L.chimera_kda_fwd_varlen_timed.argtypes = L.chimera_kda_fwd_varlen.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
     _lib = L
@@ -383,6 +386,24 @@ def mshortconv_bwd(x, dy, w_text, w_vis, segments: Sequence, dx=None):
         _ptr(x), _ptr(dy), _ptr(dx), _ptr(dwt), _ptr(dwv), B, T, C, _dtype_code(x), _ptr(w_text), _ptr(w_vis),
         segs, len(segments), _stream(x)))
     return dx, dwt, dwv
+
+
+def kda_fwd_conv(x, w_text, w_vis, segments: Sequence, alpha, beta, S0=None, *, H: int, dk: int, dv: int,
+                 l2norm: bool = True, out=None, state_out=None, want_state: bool = True):
+    """mShortConv and KDA in one pass (chimera_kda_fwd_conv): x [B, T, H*(2 dk + dv)] holds the
+    pre-conv q|k|v channels; returns (o [B, T, H, dv], S_final or None)."""
+    import torch
+    B, T, C = x.shape
+    assert C == H * (2 * dk + dv) and x.is_contiguous()
+    dt = _dtype_code(x)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=x.dtype, device=x.device)
+    Sf = state_out if state_out is not None else (
+        torch.empty((B, H, dk, dv), dtype=torch.float32, device=x.device) if want_state else None)
+    arr = segment_array(segments)
+    _check("chimera_kda_fwd_conv", lib().chimera_kda_fwd_conv(
+        _ptr(x), _ptr(w_text), _ptr(w_vis), arr, len(arr), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(Sf),
+        B, T, H, dk, dv, dt, KDA_L2NORM_QK if l2norm else 0, _stream(x)))
+    return o, Sf
 
 
 def split_qkv(y, H: int, d: int):

@@ -291,6 +291,43 @@ static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64
   return CHIMERA_OK;
 }
 
+chimera_status chimera_kda_fwd_conv(const void* x, const float* w_text, const float* w_vis,
+                                    const chimera_segment* segs, int32_t nseg, const void* alpha, const void* beta,
+                                    const float* S0, void* o, float* S_final, int64_t B, int64_t T, int64_t H,
+                                    int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, hipStream_t stream) {
+  if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
+  if (!kda_sizes_ok(B, T, H, dk, dv)) return CHIMERA_ERR_SHAPE;
+  if (dk > 128) return CHIMERA_ERR_UNSUPPORTED;
+  if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL)) return CHIMERA_ERR_UNSUPPORTED;
+  bool any_text, any_vis;
+  const chimera_status st = check_segments(segs, nseg, T, &any_text, &any_vis);
+  if (st != CHIMERA_OK) return st;
+  if (nseg > chm::kMaxFusedSegs) return CHIMERA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return CHIMERA_OK;
+  if (T > 0) {
+    if (x == nullptr || alpha == nullptr || beta == nullptr || o == nullptr) return CHIMERA_ERR_NULL;
+    if ((any_text && w_text == nullptr) || (any_vis && w_vis == nullptr)) return CHIMERA_ERR_NULL;
+    if (x == o) return CHIMERA_ERR_UNSUPPORTED;
+  }
+  chm::ConvSrc cs;
+  cs.x = x;
+  cs.C = H * (2 * dk + dv);
+  cs.w_text = w_text;
+  cs.w_vis = w_vis;
+  cs.nseg = nseg;
+  for (int32_t i = 0; i < nseg; ++i) cs.seg[i] = to_seg(segs[i]);
+  chm::KdaArgs a;
+  a.q = a.k = a.v = nullptr;
+  a.qkv_stride = cs.C;
+  a.alpha = alpha; a.beta = beta;
+  a.S0 = S0; a.o = o; a.S_final = S_final;
+  a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
+  a.bf16 = dt == CHIMERA_BF16;
+  a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
+  a.conv = &cs;
+  return hip_status(chm::launch_kda_sequential(a, stream));
+}
+
 chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
                                const void* beta, const float* S0, void* o, float* S_final, int64_t B, int64_t T,
                                int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,

@@ -51,6 +51,20 @@ hipError_t launch_conv_rows_adjoint(const void* dy, void* dx, const float* w_vis
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream);
 
 // ---- KDA ----------------------------------------------------------------------
+// Conv source of the fused conv + recurrence (token-by-token kernel): q|k|v of every token
+// are computed from x [B][T][C] (C = H (2 dk + dv); the q, k and v channels in that order)
+// by the mShortConv of the segment layout, rounded to the storage type as the conv call
+// would store them, and never written out.
+constexpr int kMaxFusedSegs = 32;
+struct ConvSrc {
+  const void* x = nullptr;
+  int64_t C = 0;
+  const float* w_text = nullptr;   // [C][4], or null when no segment is text
+  const float* w_vis = nullptr;    // [C][27], or null when no segment is visual
+  int nseg = 0;
+  Seg seg[kMaxFusedSegs];
+};
+
 struct KdaArgs {
   const void* q;
   const void* k;
@@ -70,6 +84,8 @@ struct KdaArgs {
   int64_t gate_stride = 0;
   const float* norm_w = nullptr;  // [dv] or null (ones)
   float norm_eps = 0.f;
+  // Fused conv (token-by-token kernel only): q, k, v are ignored and computed from conv->x.
+  const ConvSrc* conv = nullptr;
 };
 
 // Optional cut of every sequence into nseg segments of len tokens (a multiple of 16; the last

@@ -22,20 +22,33 @@ namespace {
 
 constexpr int kTokBatch = 16;
 
+// A value as the conv call would store it: rounded to bf16 for bf16 storage.
+__device__ __forceinline__ float stored(float v, const uint16_t*) { return bf2f(f2bf(v)); }
+__device__ __forceinline__ float stored(float v, const float*) { return v; }
+
 // OUT false: no readout (o is not written; the state passes of the backward).
-template <typename T, int RPT, bool OUT>
+// CONV: q, k, v computed in the load stage from the conv source cs (page 1, section 3.4:
+// each segment convolved on its own, zero outside it; Eq. 13), not read from q, k, v.
+template <typename T, int RPT, bool OUT, bool CONV>
 __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                       const T* __restrict__ v, int64_t stride,
                                                       const T* __restrict__ alpha, const T* __restrict__ beta,
                                                       const float* __restrict__ S0, T* __restrict__ o,
                                                       float* __restrict__ S_final, int64_t Tn, int64_t H, int dk,
-                                                      int dv, int l2norm, float* __restrict__ ckpt, SeqSegs sg) {
+                                                      int dv, int l2norm, float* __restrict__ ckpt, SeqSegs sg,
+                                                      ConvSrc cs) {
   constexpr int DKP = 16 * RPT;   // staged rows; rows past dk hold k = q = 0, alpha = 1
   __shared__ float sk[2][kTokBatch][DKP];
   __shared__ float sq[2][OUT ? kTokBatch : 1][OUT ? DKP : 1];   // q only for the readout
   __shared__ float sa[2][kTokBatch][DKP];
   __shared__ float sv[2][kTokBatch][16];
   __shared__ float sb[2][kTokBatch];
+  // CONV: the weights of this block's q and k rows and v columns, [tap][channel] with the 4
+  // text taps first and the 27 visual taps after them, and the segment table
+  constexpr int kTaps = kTextTaps + kVisTaps;
+  __shared__ float wq[CONV ? kTaps : 1][CONV ? DKP : 1], wk[CONV ? kTaps : 1][CONV ? DKP : 1];
+  __shared__ float wv[CONV ? kTaps : 1][16];
+  __shared__ Seg sseg[CONV ? kMaxFusedSegs : 1];
 
   const int n_vs = (dv + 15) / 16;
   const int vs = blockIdx.x % n_vs;
@@ -61,23 +74,128 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(const T* __restrict__ q, c
                        : (init != nullptr && col_ok && row < dk) ? init[row * dv + col] : 0.f;
   }
 
+  if constexpr (CONV) {
+    const int64_t qc = h * dk, kc = H * dk + h * dk, vch = 2 * H * dk + h * dv;
+    auto wgt = [&](int64_t c, int tap) {
+      return tap < kTextTaps ? (cs.w_text != nullptr ? cs.w_text[c * kTextTaps + tap] : 0.f)
+                             : (cs.w_vis != nullptr ? cs.w_vis[c * kVisTaps + tap - kTextTaps] : 0.f);
+    };
+    for (int e = tid; e < kTaps * DKP; e += 256) {
+      const int tap = e / DKP, row = e % DKP;
+      wq[tap][row] = row < dk ? wgt(qc + row, tap) : 0.f;
+      wk[tap][row] = row < dk ? wgt(kc + row, tap) : 0.f;
+    }
+    for (int e = tid; e < kTaps * 16; e += 256) {
+      const int tap = e / 16, c = vs * 16 + e % 16;
+      wv[tap][e % 16] = c < dv ? wgt(vch + c, tap) : 0.f;
+    }
+    if (tid == 0)
+      for (int i = 0; i < cs.nseg; ++i) sseg[i] = cs.seg[i];
+    __syncthreads();
+  }
+
   // one batch of tokens: thread (colid, rt) loads token colid, rows RPT rt .. RPT rt + RPT - 1
   float rk[RPT], rq[RPT], ra[RPT], rv, rb;
+  // CONV: q (rows), k (rows) and v (column vs * 16 + rt) of token t by the segment's taps
+  auto conv_token = [&](int64_t t) {
+    const T* xs = static_cast<const T*>(cs.x) + b * Tn * cs.C;
+    const int64_t qc = h * dk, kc = H * dk + h * dk, vc = 2 * H * dk + h * dv + vs * 16 + rt;
+    const bool v_ok = vs * 16 + rt < dv;
+    float aq[RPT], ak[RPT], av = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) aq[i] = ak[i] = 0.f;
+    // N taps at once: all their loads are issued before the first multiply (src < 0: zero padding)
+    auto add = [&](const int64_t (&src)[3], const int (&tap)[3], int N) {
+      float xq[3][RPT], xk[3][RPT], xv[3];
+#pragma unroll
+      for (int n = 0; n < 3; ++n) {
+        const bool in = n < N && src[n] >= 0;
+        const T* xr = xs + (in ? src[n] : 0) * cs.C;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const int row = RPT * rt + i;
+          xq[n][i] = in && row < dk ? to_f32(xr[qc + row]) : 0.f;
+          xk[n][i] = in && row < dk ? to_f32(xr[kc + row]) : 0.f;
+        }
+        xv[n] = in && v_ok ? to_f32(xr[vc]) : 0.f;
+      }
+#pragma unroll
+      for (int n = 0; n < 3; ++n) {
+        if (n >= N) break;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const int row = RPT * rt + i;
+          aq[i] = fmaf(wq[tap[n]][row], xq[n][i], aq[i]);
+          ak[i] = fmaf(wk[tap[n]][row], xk[n][i], ak[i]);
+        }
+        av = fmaf(wv[tap[n]][rt], xv[n], av);
+      }
+    };
+    int lo = 0, hi = cs.nseg - 1;   // the segment holding t: the last one starting at or before it
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sseg[mid].start <= t) lo = mid; else hi = mid - 1;
+    }
+    const Seg sgt = sseg[lo];
+    if (sgt.kind == SEG_TEXT) {
+      for (int j0 = 0; j0 < kTextTaps; j0 += 3) {
+        int64_t src[3];
+        int tap[3];
+#pragma unroll
+        for (int n = 0; n < 3; ++n) {
+          tap[n] = min(j0 + n, kTextTaps - 1);
+          src[n] = text_tap_source(sgt, t, tap[n]);
+        }
+        add(src, tap, min(3, kTextTaps - j0));
+      }
+    } else {
+      const int64_t local = t - sgt.start, hw = (int64_t)sgt.height * sgt.width;
+      const int64_t f = local / hw, hh = (local / sgt.width) % sgt.height, ww = local % sgt.width;
+      for (int kt = 3 - min(sgt.frames, 3); kt < 3; ++kt)
+        for (int kh = 0; kh < 3; ++kh) {
+          int64_t src[3];
+          int tap[3];
+#pragma unroll
+          for (int kw = 0; kw < 3; ++kw) {
+            src[kw] = vis_tap_source(sgt, f, hh, ww, kt, kh, kw);
+            tap[kw] = kTextTaps + kt * 9 + kh * 3 + kw;
+          }
+          add(src, tap, 3);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      rq[i] = stored(aq[i], xs);
+      rk[i] = stored(ak[i], xs);
+    }
+    rv = stored(av, xs);
+  };
   auto load = [&](int64_t t0) {
     const int nt = (int)min<int64_t>(kTokBatch, t_end - t0);
     const bool tok_ok = colid < nt;
     const int64_t tok = b * Tn + t0 + colid;
+    if constexpr (CONV) {
+      if (tok_ok) {
+        conv_token(t0 + colid);
+      } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) rq[i] = rk[i] = 0.f;
+        rv = 0.f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = RPT * rt + i;
       const bool ok = tok_ok && row < dk;
-      rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
-      rq[i] = ok && q != nullptr ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
+      if constexpr (!CONV) {
+        rk[i] = ok ? to_f32(k[tok * stride + h * dk + row]) : 0.f;
+        rq[i] = ok && q != nullptr ? to_f32(q[tok * stride + h * dk + row]) : 0.f;
+      }
       ra[i] = ok ? to_f32(alpha[(tok * H + h) * dk + row]) : 1.f;
     }
     // v: token colid, column vs * 16 + rt; beta: token colid
     const int vc = vs * 16 + rt;
-    rv = (tok_ok && vc < dv && v != nullptr) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
+    if constexpr (!CONV) rv = (tok_ok && vc < dv && v != nullptr) ? to_f32(v[tok * stride + h * dv + vc]) : 0.f;
     rb = tok_ok ? to_f32(beta[tok * H + h]) : 0.f;
   };
   // store a loaded batch to buffer `buf` and normalise its q and k rows
@@ -197,8 +315,8 @@ __global__ __launch_bounds__(256) void kda_gate_norm_kernel(T* __restrict__ o, c
   }
 }
 
-template <typename T>
-hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, float* ckpt, const SeqSegs& sg) {
+template <typename T, int R>
+hipError_t launch_seq_r(const KdaArgs& a, int64_t blocks, hipStream_t stream, float* ckpt, const SeqSegs& sg) {
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
@@ -207,22 +325,30 @@ hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, floa
   T* o = static_cast<T*>(a.o);
   const dim3 g((unsigned)blocks), t(256);
   const int dk = (int)a.dk, dv = (int)a.dv, nrm = (int)a.l2norm;
-#define CHM_SEQ(R)                                                                                                  \
-  do {                                                                                                              \
-    if (o != nullptr)                                                                                               \
-      hipLaunchKernelGGL((kda_seq_kernel<T, R, true>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o,      \
-                         a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);                                               \
-    else                                                                                                            \
-      hipLaunchKernelGGL((kda_seq_kernel<T, R, false>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o,     \
-                         a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg);                                               \
-  } while (0)
-  if (dk <= 16) CHM_SEQ(1);
-  else if (dk <= 32) CHM_SEQ(2);
-  else if (dk <= 64) CHM_SEQ(4);
-  else if (dk <= 128) CHM_SEQ(8);
-  else CHM_SEQ(16);
-#undef CHM_SEQ
+  const ConvSrc cs = a.conv != nullptr ? *a.conv : ConvSrc{};
+  if (a.conv != nullptr) {
+    if constexpr (R <= 8)   // the conv weights of wider heads do not fit the LDS
+      hipLaunchKernelGGL((kda_seq_kernel<T, R, true, true>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o,
+                         a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg, cs);
+    else
+      return hipErrorInvalidValue;
+  } else if (o != nullptr) {
+    hipLaunchKernelGGL((kda_seq_kernel<T, R, true, false>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o,
+                       a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg, cs);
+  } else {
+    hipLaunchKernelGGL((kda_seq_kernel<T, R, false, false>), g, t, 0, stream, q, k, v, a.qkv_stride, al, be, a.S0, o,
+                       a.S_final, a.T, a.H, dk, dv, nrm, ckpt, sg, cs);
+  }
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_seq(const KdaArgs& a, int64_t blocks, hipStream_t stream, float* ckpt, const SeqSegs& sg) {
+  if (a.dk <= 16) return launch_seq_r<T, 1>(a, blocks, stream, ckpt, sg);
+  if (a.dk <= 32) return launch_seq_r<T, 2>(a, blocks, stream, ckpt, sg);
+  if (a.dk <= 64) return launch_seq_r<T, 4>(a, blocks, stream, ckpt, sg);
+  if (a.dk <= 128) return launch_seq_r<T, 8>(a, blocks, stream, ckpt, sg);
+  return launch_seq_r<T, 16>(a, blocks, stream, ckpt, sg);
 }
 
 }  // namespace

@@ -217,6 +217,29 @@ def test_backward_argument_errors():
     assert cb(C=12) == 2 and cb(dwt=None) == 1 and cb(dx=None) == 1 and cb(dx=1) == 5
 
 
+def test_fused_conv_argument_errors():
+    """chimera_kda_fwd_conv checks its arguments before any launch (no kernel runs here)."""
+    L = chm.lib()
+    text = chm.segment_array([dict(kind=0, start=0, length=8)])
+    img = chm.segment_array([dict(kind=1, start=0, length=8, frames=1, height=2, width=4)])
+    many = chm.segment_array([dict(kind=0, start=i, length=1) for i in range(33)])
+    def call(segs=text, nseg=None, **kw):
+        a = dict(x=1, wt=2, wv=3, al=4, be=5, S0=None, o=6, Sf=None, B=1, T=8, H=2, dk=32, dv=32, dt=1, flags=1)
+        a.update(kw)
+        n = len(segs) if nseg is None else nseg
+        return L.chimera_kda_fwd_conv(a["x"], a["wt"], a["wv"], segs, n, a["al"], a["be"], a["S0"], a["o"], a["Sf"],
+                                      a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["flags"], None)
+    assert call(dt=7) == 3
+    assert call(dk=256) == 5                                            # the conv weights of dk > 128 do not fit
+    assert call(flags=4) == 5                                           # no chunked options
+    assert call(T=9) == 4                                               # segments must tile [0, T)
+    assert call(segs=many, T=33) == 5                                   # more than 32 segments
+    assert call(x=None) == 1 and call(o=None) == 1 and call(al=None) == 1
+    assert call(wt=None) == 1 and call(segs=img, wv=None) == 1          # the weights the layout uses
+    assert call(x=6) == 5                                               # o aliasing x
+    assert call(B=0) == 0
+
+
 def test_workspace_size_rules():
     n = chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
     assert n >= 0
