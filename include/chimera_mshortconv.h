@@ -45,7 +45,7 @@ typedef enum chimera_status {
   CHIMERA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or too large */
   CHIMERA_ERR_DTYPE = 3,        /* unknown dtype */
   CHIMERA_ERR_SEGMENTS = 4,     /* the segment table does not tile [0, T) or a grid is malformed */
-  CHIMERA_ERR_UNSUPPORTED = 5,  /* a valid request this build does not implement */
+  CHIMERA_ERR_UNSUPPORTED = 5,  /* a valid request this library does not implement */
   CHIMERA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than chimera_kda_workspace_size() */
   CHIMERA_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed */
 } chimera_status;

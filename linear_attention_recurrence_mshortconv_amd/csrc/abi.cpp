@@ -69,7 +69,7 @@ const char* chimera_status_string(chimera_status s) {
     case CHIMERA_ERR_SHAPE: return "invalid size";
     case CHIMERA_ERR_DTYPE: return "unknown dtype";
     case CHIMERA_ERR_SEGMENTS: return "segment table does not tile [0, T) or a grid is malformed";
-    case CHIMERA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case CHIMERA_ERR_UNSUPPORTED: return "request not supported by this library";
     case CHIMERA_ERR_WORKSPACE: return "workspace missing or too small";
     case CHIMERA_ERR_HIP: return "HIP runtime or launch failure";
   }

@@ -22,7 +22,7 @@ Expanding the product gives the form the loop uses, with no other change:
 
 ``l2norm_ref`` is the per-(token, head) L2 normalisation that Fig. 2 (page 1)
 draws between mShortConv and the recurrence; its epsilon (1e-6 inside the
-square root) is this build's reading, not the pages'.
+square root) is a reading made here, not the pages'.
 
 ``kda_varlen_ref`` runs several samples packed into one token row: the state
 restarts (from that sample's S0, zero by default) at every packed sample
