@@ -363,6 +363,24 @@ chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int6
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * chimera_kda_bwd_varlen -- gradients of chimera_kda_fwd_varlen (samples packed in one row,
+ * the state restarting at every sample; page 1, section 3.3) without a gate: the arguments
+ * of chimera_kda_bwd with B = 1 and T = cu_seqlens[nseq], and per sample its S0, dS_final
+ * and dS0 ([nseq][H][dk][dv] each; S0 and dS_final may be NULL for zero). Each run of
+ * consecutive samples of equal length is one batched backward on views of the packed
+ * tensors; the runs share the workspace (chimera_kda_bwd_varlen_workspace_size: the
+ * largest run's need). An empty sample gives dS0 = dS_final.
+ */
+size_t chimera_kda_bwd_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
+                                             int64_t dv, chimera_dtype dt, uint32_t flags);
+chimera_status chimera_kda_bwd_varlen(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                      const void* alpha, const void* beta, const float* S0, const void* dout,
+                                      const float* dS_final, void* dq, void* dk_out, void* dv_out, void* dalpha,
+                                      void* dbeta, float* dS0, const int64_t* cu_seqlens, int32_t nseq, int64_t H,
+                                      int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
  * chimera_mshortconv_bwd -- gradients of y = chimera_mshortconv_fwd(x) against dy:
  *
  *   x, dy     device [B][T][C], dtype dt

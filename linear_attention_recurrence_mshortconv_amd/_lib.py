@@ -87,6 +87,11 @@ def lib() -> ctypes.CDLL:
     L.chimera_kda_fwd_varlen.restype = ctypes.c_int
     L.chimera_kda_fwd_varlen.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, vp, ctypes.c_float, vp, vp,
                                          vp, i32, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.chimera_kda_bwd_varlen_workspace_size.restype = sz
+    L.chimera_kda_bwd_varlen_workspace_size.argtypes = [vp, i32, i64, i64, i64, ctypes.c_int, u32]
+    L.chimera_kda_bwd_varlen.restype = ctypes.c_int
+    L.chimera_kda_bwd_varlen.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, i32, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
     L.chimera_kda_fwd_conv.restype = ctypes.c_int
     L.chimera_kda_fwd_conv.argtypes = [vp, vp, vp, seg_p, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                        ctypes.c_int, u32, vp]
@@ -369,6 +374,41 @@ def kda_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, l2norm: bool = Tru
         _ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dout), _ptr(dS_final),
         _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), B, T, H, dk, dv, dt,
         KDA_L2NORM_QK if l2norm else 0, _ptr(workspace), wbytes, _stream(k)))
+    return {"dq": dq, "dk": dkk, "dv": dvv, "dalpha": dalpha, "dbeta": dbeta, "dS0": dS0}
+
+
+def kda_bwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0, dout, dS_final=None, *, l2norm: bool = True, grads=None,
+                   workspace=None):
+    """Gradients of kda_fwd_varlen without a gate (chimera_kda_bwd_varlen): q, k, v [T, H, d] (views
+    into one packed row), cu_seqlens the sample offsets; S0, dS_final, and the returned dS0 are
+    [nseq, H, dk, dv] fp32. Returns dict dq, dk, dv, dalpha, dbeta, dS0."""
+    import torch
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    stride = _token_view_stride(q[None], 1, T, H, dk)
+    assert _token_view_stride(k[None], 1, T, H, dk) == stride and _token_view_stride(v[None], 1, T, H, dv) == stride
+    cu = _cu_array(cu_seqlens)
+    nseq = len(cu) - 1
+    assert cu[-1] == T
+    dt = _dtype_code(k)
+    if grads is None:
+        assert stride == H * dk and stride == H * dv, "strided (fused) inputs: pass `grads` with their layout"
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dkk, dvv = grads
+    for g, t in zip(grads, (q, k, v)):
+        assert g.shape == t.shape and g.stride() == t.stride()
+    dalpha = torch.empty_like(alpha)
+    dbeta = torch.empty_like(beta)
+    dS0 = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=k.device)
+    flags = KDA_L2NORM_QK if l2norm else 0
+    need = int(lib().chimera_kda_bwd_varlen_workspace_size(cu.ctypes.data, nseq, H, dk, dv, dt, flags))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("chimera_kda_bwd_varlen", lib().chimera_kda_bwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dout), _ptr(dS_final),
+        _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), cu.ctypes.data, nseq, H, dk, dv, dt,
+        flags, _ptr(workspace), wbytes, _stream(k)))
     return {"dq": dq, "dk": dkk, "dv": dvv, "dalpha": dalpha, "dbeta": dbeta, "dS0": dS0}
 
 

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "internal.h"
@@ -454,6 +455,68 @@ chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int6
   a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
   const chm::KdaGrads g{dout, dS_final, dq, dk_out, dv_out, dalpha, dbeta, dS0};
   return hip_status(chm::launch_kda_backward(a, g, workspace, stream));
+}
+
+size_t chimera_kda_bwd_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
+                                             int64_t dv, chimera_dtype dt, uint32_t flags) {
+  (void)flags;
+  if (check_cu(cu_seqlens, nseq) != CHIMERA_OK || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
+  if (!kda_sizes_ok(1, cu_seqlens[nseq], H, dk, dv)) return 0;
+  size_t need = 0;
+  for (const chm::KdaRun& r : varlen_runs(cu_seqlens, nseq))
+    need = std::max(need, chm::kda_bwd_workspace(r.count, r.len, H, dk, dv));
+  return need;
+}
+
+chimera_status chimera_kda_bwd_varlen(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                      const void* alpha, const void* beta, const float* S0, const void* dout,
+                                      const float* dS_final, void* dq, void* dk_out, void* dv_out, void* dalpha,
+                                      void* dbeta, float* dS0, const int64_t* cu_seqlens, int32_t nseq, int64_t H,
+                                      int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
+  const chimera_status cs = check_cu(cu_seqlens, nseq);
+  if (cs != CHIMERA_OK) return cs;
+  const int64_t rows = cu_seqlens[nseq];
+  if (!kda_sizes_ok(1, rows, H, dk, dv)) return CHIMERA_ERR_SHAPE;
+  if (dk > 128) return CHIMERA_ERR_UNSUPPORTED;
+  if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL | CHIMERA_KDA_NO_SPLIT)) return CHIMERA_ERR_UNSUPPORTED;
+  if (nseq == 0 || H == 0) return CHIMERA_OK;
+  if (rows > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || alpha == nullptr || beta == nullptr || dout == nullptr ||
+        dq == nullptr || dk_out == nullptr || dv_out == nullptr || dalpha == nullptr || dbeta == nullptr)
+      return CHIMERA_ERR_NULL;
+    if (qkv_stride < H * dk || qkv_stride < H * dv) return CHIMERA_ERR_SHAPE;
+  }
+  const std::vector<chm::KdaRun> runs = varlen_runs(cu_seqlens, nseq);
+  size_t need = 0;
+  for (const chm::KdaRun& r : runs) need = std::max(need, chm::kda_bwd_workspace(r.count, r.len, H, dk, dv));
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
+  // each run of equal lengths is a batch on views of the packed tensors; the runs share the workspace
+  const int64_t e = dt == CHIMERA_BF16 ? 2 : 4;
+  auto at = [&](const void* p, int64_t elems) {
+    return p == nullptr ? nullptr : static_cast<const char*>(p) + elems * e;
+  };
+  auto mut = [&](void* p, int64_t elems) { return p == nullptr ? nullptr : static_cast<char*>(p) + elems * e; };
+  const int64_t state = H * dk * dv;
+  for (const chm::KdaRun& r : runs) {
+    chm::KdaArgs a{};
+    a.q = at(q, r.start * qkv_stride); a.k = at(k, r.start * qkv_stride); a.v = at(v, r.start * qkv_stride);
+    a.qkv_stride = qkv_stride;
+    a.alpha = at(alpha, r.start * H * dk); a.beta = at(beta, r.start * H);
+    a.S0 = S0 == nullptr ? nullptr : S0 + r.sidx0 * state;
+    a.o = nullptr; a.S_final = nullptr;
+    a.B = r.count; a.T = r.len; a.H = H; a.dk = dk; a.dv = dv;
+    a.bf16 = dt == CHIMERA_BF16;
+    a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
+    const chm::KdaGrads g{at(dout, r.start * H * dv), dS_final == nullptr ? nullptr : dS_final + r.sidx0 * state,
+                          mut(dq, r.start * qkv_stride), mut(dk_out, r.start * qkv_stride),
+                          mut(dv_out, r.start * qkv_stride), mut(dalpha, r.start * H * dk), mut(dbeta, r.start * H),
+                          dS0 == nullptr ? nullptr : dS0 + r.sidx0 * state};
+    const hipError_t he = chm::launch_kda_backward(a, g, workspace, stream);
+    if (he != hipSuccess) return CHIMERA_ERR_HIP;
+  }
+  return CHIMERA_OK;
 }
 
 chimera_status chimera_mshortconv_bwd(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis,

@@ -217,6 +217,33 @@ def test_backward_argument_errors():
     assert cb(C=12) == 2 and cb(dwt=None) == 1 and cb(dx=None) == 1 and cb(dx=1) == 5
 
 
+def test_backward_varlen_argument_errors():
+    """chimera_kda_bwd_varlen checks its arguments before any launch (no kernel runs here)."""
+    L = chm.lib()
+    cu = np.array([0, 5, 5, 12], dtype=np.int64)
+    bad0 = np.array([1, 5], dtype=np.int64)
+    down = np.array([0, 5, 4], dtype=np.int64)
+    def call(cu_arr=cu, nseq=3, **kw):
+        a = dict(q=1, k=2, v=3, stride=256, al=4, be=5, S0=None, do=6, dS=None, dq=7, dk=8, dv=9, da=10, db=11,
+                 dS0=None, H=2, dkk=128, dvv=128, dt=1, flags=1, ws=None, wsb=0)
+        a.update(kw)
+        ptr = None if cu_arr is None else cu_arr.ctypes.data
+        return L.chimera_kda_bwd_varlen(a["q"], a["k"], a["v"], a["stride"], a["al"], a["be"], a["S0"], a["do"],
+                                        a["dS"], a["dq"], a["dk"], a["dv"], a["da"], a["db"], a["dS0"], ptr, nseq,
+                                        a["H"], a["dkk"], a["dvv"], a["dt"], a["flags"], a["ws"], a["wsb"], None)
+    assert call(dt=7) == 3
+    assert call(cu_arr=None) == 1
+    assert call(cu_arr=bad0, nseq=1) == 2 and call(cu_arr=down, nseq=2) == 2 and call(nseq=-1) == 2
+    assert call(dkk=256, stride=1024) == 5
+    assert call(do=None) == 1 and call(db=None) == 1
+    assert call(stride=100) == 2
+    assert call() == 6                                                  # workspace missing
+    assert call(nseq=0) == 0
+    need = int(L.chimera_kda_bwd_varlen_workspace_size(cu.ctypes.data, 3, 2, 128, 128, 1, 1))
+    one = int(L.chimera_kda_bwd_workspace_size(1, 7, 2, 128, 128, 1, 1))
+    assert need >= one > 0                                              # the largest run's need
+
+
 def test_fused_conv_argument_errors():
     """chimera_kda_fwd_conv checks its arguments before any launch (no kernel runs here)."""
     L = chm.lib()

@@ -184,6 +184,58 @@ def test_kda_bwd_full_size_directional(chm):
         _close_bf16(grad[i][lo:], ref[name][0, :, 0], f"{name}, last {tail} tokens")
 
 
+def _packed(rng, cu, H, dk, dv, dtype):
+    rnd = (lambda a: wl.round_to_bf16(a.astype(np.float32))) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    T, N = cu[-1], len(cu) - 1
+    q, k = rnd(rng.standard_normal((T, H, dk))), rnd(rng.standard_normal((T, H, dk)))
+    v = rnd(rng.standard_normal((T, H, dv)))
+    alpha = rnd(np.exp(-0.05 * np.logaddexp(0, rng.standard_normal((T, H, dk)))))
+    beta = rnd(1 / (1 + np.exp(-rng.standard_normal((T, H)))))
+    S0 = (0.1 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    do = rnd(rng.standard_normal((T, H, dv)))
+    dS = (0.1 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    return q, k, v, alpha, beta, S0, do, dS
+
+
+def _check_packed(chm, cu, args, dtype):
+    import torch
+    q, k, v, alpha, beta, S0, do, dS = args
+    dev = lambda a: to_device(a, dtype)
+    g = chm.kda_bwd_varlen(dev(q), dev(k), dev(v), dev(alpha), dev(beta), cu, torch.from_numpy(S0).cuda(), dev(do),
+                           torch.from_numpy(dS).cuda())
+    got = {n: to_host(t) for n, t in g.items()}
+    for n in range(len(cu) - 1):
+        s, e = cu[n], cu[n + 1]
+        one = lambda a: a[None, s:e]
+        ref = kda_backward_ref(one(q), one(k), one(v), one(alpha), one(beta), S0[n:n + 1], one(do), dS[n:n + 1])
+        names = ("dq", "dk", "dv", "dalpha", "dbeta") if e > s else ()
+        for name in names:
+            if dtype == "bf16":
+                _close_bf16(got[name][s:e], ref[name][0], f"{name} of sample {n}")
+            else:
+                assert_close(got[name][s:e], ref[name][0], "f32", f"{name} of sample {n}")
+        if e == s:
+            assert np.array_equal(got["dS0"][n], dS[n].astype(np.float64))
+        elif dtype == "bf16":
+            _close_bf16(got["dS0"][n], ref["dS0"][0], f"dS0 of sample {n}")
+        else:
+            assert_close(got["dS0"][n], ref["dS0"][0], "f32", f"dS0 of sample {n}")
+
+
+def test_kda_bwd_varlen_mixed_lengths_bf16(chm):
+    """Samples of 1, 63, 65, 0, 371 and 200 tokens packed in one row, each with its own S0 and
+    dS_final (the 371-token sample cut into segments): every sample against the autograd oracle
+    on that sample alone."""
+    cu = [0, 1, 64, 129, 129, 500, 700]
+    _check_packed(chm, cu, _packed(np.random.default_rng(130), cu, 2, 128, 128, "bf16"), "bf16")
+
+
+def test_kda_bwd_varlen_equal_runs_fp32(chm):
+    """fp32, 32-wide heads: three samples of 50 tokens (one batched run of three), one of 1, one of 149."""
+    cu = [0, 50, 100, 150, 151, 300]
+    _check_packed(chm, cu, _packed(np.random.default_rng(131), cu, 3, 32, 32, "f32"), "f32")
+
+
 def test_conv_bwd_fp32_mixed_layout(chm):
     import torch
     S = wl.Segment
