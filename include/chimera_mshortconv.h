@@ -363,6 +363,27 @@ chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int6
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * chimera_gate_norm_bwd -- gradients of Eq. 15's gate and norm (page 1, section 3.3; the
+ * epilogue of chimera_kda_fwd_gated), y = Sigmoid(gate) * o / sqrt(mean(o^2) + norm_eps) *
+ * norm_weight per (token, head) row of dv channels, against dy:
+ *
+ *   o             device [B][T][H][dv], dt: the KDA output before the gate (as chimera_kda_fwd
+ *                 writes it)
+ *   gate          device, dt, [B*T][H][dv] with consecutive tokens gate_stride elements apart
+ *   norm_weight   device fp32 [dv], or NULL for ones
+ *   dy            device [B][T][H][dv], dt
+ *   dout          device [B][T][H][dv], written, dt: dL/do, the dout of chimera_kda_bwd
+ *   dgate         device, written, dt, at the gate's layout
+ *   dnorm_weight  device fp32 [dv], written (summed over every row), or NULL
+ *
+ * dv <= 256. The outputs must not alias the inputs. Asynchronous on `stream`.
+ */
+chimera_status chimera_gate_norm_bwd(const void* o, const void* gate, int64_t gate_stride, const float* norm_weight,
+                                     float norm_eps, const void* dy, void* dout, void* dgate, float* dnorm_weight,
+                                     int64_t B, int64_t T, int64_t H, int64_t dv, chimera_dtype dt,
+                                     hipStream_t stream);
+
+/*
  * chimera_kda_bwd_varlen -- gradients of chimera_kda_fwd_varlen (samples packed in one row,
  * the state restarting at every sample; page 1, section 3.3) without a gate: the arguments
  * of chimera_kda_bwd with B = 1 and T = cu_seqlens[nseq], and per sample its S0, dS_final

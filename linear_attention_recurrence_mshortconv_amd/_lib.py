@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
     L.chimera_kda_bwd_varlen.restype = ctypes.c_int
     L.chimera_kda_bwd_varlen.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, i32, i64, i64, i64, ctypes.c_int, u32, vp, sz, vp]
+    L.chimera_gate_norm_bwd.restype = ctypes.c_int
+    L.chimera_gate_norm_bwd.argtypes = [vp, vp, i64, vp, ctypes.c_float, vp, vp, vp, vp, i64, i64, i64, i64,
+                                        ctypes.c_int, vp]
     L.chimera_kda_fwd_conv.restype = ctypes.c_int
     L.chimera_kda_fwd_conv.argtypes = [vp, vp, vp, seg_p, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                        ctypes.c_int, u32, vp]
@@ -410,6 +413,22 @@ def kda_bwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0, dout, dS_final=None, *,
         _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), cu.ctypes.data, nseq, H, dk, dv, dt,
         flags, _ptr(workspace), wbytes, _stream(k)))
     return {"dq": dq, "dk": dkk, "dv": dvv, "dalpha": dalpha, "dbeta": dbeta, "dS0": dS0}
+
+
+def gate_norm_bwd(o, gate, norm_weight, dy, norm_eps: float = 1e-6, *, want_weight_grad: bool = True):
+    """Gradients of Sigmoid(gate) * RMSNorm(o) * norm_weight (chimera_gate_norm_bwd): o, dy
+    [B, T, H, dv]; gate [B, T, H, dv] with a token stride of its own. Returns (dout, dgate,
+    dnorm_weight or None)."""
+    import torch
+    B, T, H, dv = o.shape
+    gs = _token_view_stride(gate, B, T, H, dv)
+    dout = torch.empty_like(o)
+    dgate = torch.empty_strided(gate.shape, gate.stride(), dtype=gate.dtype, device=gate.device)
+    dw = torch.empty(dv, dtype=torch.float32, device=o.device) if want_weight_grad else None
+    _check("chimera_gate_norm_bwd", lib().chimera_gate_norm_bwd(
+        _ptr(o), _ptr(gate), gs, _ptr(norm_weight), float(norm_eps), _ptr(dy), _ptr(dout), _ptr(dgate), _ptr(dw),
+        B, T, H, dv, _dtype_code(o), _stream(o)))
+    return dout, dgate, dw
 
 
 def mshortconv_bwd(x, dy, w_text, w_vis, segments: Sequence, dx=None):

@@ -457,6 +457,25 @@ chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int6
   return hip_status(chm::launch_kda_backward(a, g, workspace, stream));
 }
 
+chimera_status chimera_gate_norm_bwd(const void* o, const void* gate, int64_t gate_stride, const float* norm_weight,
+                                     float norm_eps, const void* dy, void* dout, void* dgate, float* dnorm_weight,
+                                     int64_t B, int64_t T, int64_t H, int64_t dv, chimera_dtype dt,
+                                     hipStream_t stream) {
+  if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
+  if (!kda_sizes_ok(B, T, H, 1, dv)) return CHIMERA_ERR_SHAPE;
+  if (!(norm_eps >= 0.f && norm_eps < 3.0e38f)) return CHIMERA_ERR_SHAPE;   // NaN fails too
+  const int64_t rows = B * T * H;
+  if (rows > 0) {
+    if (o == nullptr || gate == nullptr || dy == nullptr || dout == nullptr || dgate == nullptr)
+      return CHIMERA_ERR_NULL;
+    if (gate_stride < H * dv || gate_stride > (int64_t(1) << 40)) return CHIMERA_ERR_SHAPE;
+    if (dout == o || dout == dy || dgate == gate) return CHIMERA_ERR_UNSUPPORTED;
+  }
+  if (rows == 0 && dnorm_weight == nullptr) return CHIMERA_OK;
+  return hip_status(chm::launch_gate_norm_backward(o, gate, gate_stride, norm_weight, norm_eps, dy, dout, dgate,
+                                                   dnorm_weight, rows, H, dv, dt == CHIMERA_BF16, stream));
+}
+
 size_t chimera_kda_bwd_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
                                              int64_t dv, chimera_dtype dt, uint32_t flags) {
   (void)flags;

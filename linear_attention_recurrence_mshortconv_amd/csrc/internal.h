@@ -125,6 +125,11 @@ struct KdaGrads {
 size_t kda_bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
 hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* workspace, hipStream_t stream,
                                Marks* marks = nullptr);
+// Backward of the gate and norm: do [rows][dv] and dgate (gate layout) in the dtype, dnorm_w [dv]
+// fp32 written (summed over rows) when not null; rows = B * T * H.
+hipError_t launch_gate_norm_backward(const void* o, const void* gate, int64_t gate_stride, const float* norm_w,
+                                     float eps, const void* dy, void* dout, void* dgate, float* dnorm_w, int64_t rows,
+                                     int64_t H, int64_t dv, bool bf16, hipStream_t stream);
 // dx (dtype, [B][T][C]) and dw_text [C][4], dw_vis [C][27] (fp32, written) of y = mShortConv(x) against dy.
 hipError_t launch_conv_backward(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis, int64_t B,
                                 int64_t T, int64_t C, bool bf16, const float* w_text, const float* w_vis,

@@ -565,6 +565,70 @@ __global__ __launch_bounds__(256) void conv_bwd_dw_kernel(const T* __restrict__ 
     for (int i = 0; i < 4; ++i) atomicAdd(dw + (c0 + i) * NW + TAP0 + t, acc[t][i]);
 }
 
+// Backward of Eq. 15's gate and norm (page 1, section 3.3), y = Sigmoid(g) * o r * w per
+// (token, head) row of dv channels, r = 1 / sqrt(mean(o^2) + eps): with n = o r, s = Sigmoid(g)
+// and dn = dy s w,
+//   dg = dy n w s (1 - s),   do = r (dn - n mean(dn n)),   dw = sum over rows of dy s n.
+// Waves walk the rows with a grid stride (lane l holds channels l, l + 64, ...), keep their dw
+// sums in registers and add them to dw with one atomic per channel at the end.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_norm_bwd_kernel(const T* __restrict__ o, const T* __restrict__ gate,
+                                                            int64_t gate_stride, const float* __restrict__ w,
+                                                            float eps, const T* __restrict__ dy, T* __restrict__ dout,
+                                                            T* __restrict__ dgate, float* __restrict__ dw,
+                                                            int64_t rows, int64_t H, int dv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  float wc[4], wsum[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    wc[i] = c < dv ? (w != nullptr ? w[c] : 1.f) : 0.f;
+    wsum[i] = 0.f;
+  }
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += nwaves) {
+    const int64_t tok = row / H, h = row % H;
+    const T* grow = gate + tok * gate_stride + h * dv;
+    float x[4], sg[4], d[4], ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lane + 64 * i;
+      const bool ok = c < dv;
+      x[i] = ok ? to_f32(o[row * dv + c]) : 0.f;
+      sg[i] = ok ? 1.f / (1.f + expf(-to_f32(grow[c]))) : 0.f;
+      d[i] = ok ? to_f32(dy[row * dv + c]) : 0.f;
+      ss = fmaf(x[i], x[i], ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = 1.f / sqrtf(ss / (float)dv + eps);
+    float n[4], dn[4], dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      n[i] = x[i] * r;
+      dn[i] = d[i] * sg[i] * wc[i];
+      dot = fmaf(dn[i], n[i], dot);
+      wsum[i] = fmaf(d[i] * sg[i], n[i], wsum[i]);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+    const float mean_dn_n = dot / (float)dv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lane + 64 * i;
+      if (c < dv) {
+        from_f32(dout + row * dv + c, r * (dn[i] - n[i] * mean_dn_n));
+        from_f32(dgate + tok * gate_stride + h * dv + c, d[i] * n[i] * wc[i] * sg[i] * (1.f - sg[i]));
+      }
+    }
+  }
+  if (dw != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < dv) atomicAdd(dw + lane + 64 * i, wsum[i]);
+  }
+}
+
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -742,6 +806,27 @@ hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* worksp
   }
   return a.bf16 ? launch_bwd_t<uint16_t>(a, g, G_end, c.len, c.nseg, ckpt, part, stream, marks)
                 : launch_bwd_t<float>(a, g, G_end, c.len, c.nseg, ckpt, part, stream, marks);
+}
+
+hipError_t launch_gate_norm_backward(const void* o, const void* gate, int64_t gate_stride, const float* norm_w,
+                                     float eps, const void* dy, void* dout, void* dgate, float* dnorm_w, int64_t rows,
+                                     int64_t H, int64_t dv, bool bf16, hipStream_t stream) {
+  if (dnorm_w != nullptr) {
+    const hipError_t e = zero(dnorm_w, dv, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((rows + 3) / 4, 4096);
+  const dim3 g((unsigned)blocks), t(256);
+  if (bf16)
+    hipLaunchKernelGGL(gate_norm_bwd_kernel<uint16_t>, g, t, 0, stream, static_cast<const uint16_t*>(o),
+                       static_cast<const uint16_t*>(gate), gate_stride, norm_w, eps, static_cast<const uint16_t*>(dy),
+                       static_cast<uint16_t*>(dout), static_cast<uint16_t*>(dgate), dnorm_w, rows, H, (int)dv);
+  else
+    hipLaunchKernelGGL(gate_norm_bwd_kernel<float>, g, t, 0, stream, static_cast<const float*>(o),
+                       static_cast<const float*>(gate), gate_stride, norm_w, eps, static_cast<const float*>(dy),
+                       static_cast<float*>(dout), static_cast<float*>(dgate), dnorm_w, rows, H, (int)dv);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv_backward(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis, int64_t B,

@@ -1,4 +1,4 @@
-"""Oracle for the backward pass of mShortConv and KDA, fp64 (torch autograd).
+"""Oracle for the backward pass of mShortConv, KDA and Eq. 15's gate and norm, fp64 (torch autograd).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -19,7 +19,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .kda import L2_EPS
+from .kda import L2_EPS, RMS_EPS
 from .mshortconv import TEXT, neighbours_ref, _seg_fields
 
 _F64 = torch.float64
@@ -94,3 +94,25 @@ def conv_backward_ref(x, w_text, w_vis, segments, dy):
     dx, dwt, dwv = torch.autograd.grad(loss, [xt, wt, wv], allow_unused=True)
     z = lambda g, ref: np.zeros(ref.shape) if g is None else g.detach().numpy()
     return {"dx": z(dx, xt), "dw_text": z(dwt, wt), "dw_vis": z(dwv, wv)}
+
+
+def gated_rmsnorm_torch(o, gate, weight=None, eps: float = RMS_EPS):
+    """Sigmoid(gate) * RMSNorm(o) over the last axis (Eq. 15 without W_o), differentiable."""
+    rms = torch.sqrt((o * o).mean(-1, keepdim=True) + eps)
+    y = o / rms
+    if weight is not None:
+        y = y * weight
+    return y * torch.sigmoid(gate)
+
+
+def gate_norm_backward_ref(o, gate, weight, dy, eps: float = RMS_EPS):
+    """Gradients of y = Sigmoid(gate) * RMSNorm(o) * weight against dy: dict of do, dgate (the
+    shapes of o and gate) and dweight ([dv], summed over all rows; with weight None, the
+    gradient with respect to a gain of ones), fp64 numpy."""
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), dtype=_F64, requires_grad=True)
+    ot, gt = t(o), t(gate)
+    wt = t(np.ones(np.shape(o)[-1]) if weight is None else weight)
+    y = gated_rmsnorm_torch(ot, gt, wt, eps)
+    loss = (y * torch.as_tensor(np.asarray(dy, dtype=np.float64))).sum()
+    do, dg, dw = torch.autograd.grad(loss, [ot, gt, wt])
+    return {"do": do.detach().numpy(), "dgate": dg.detach().numpy(), "dweight": dw.detach().numpy()}

@@ -1,10 +1,12 @@
-"""GPU parity of the backward pass (chimera_kda_bwd, chimera_mshortconv_bwd) against the
-fp64 autograd oracle (oracle.backward)."""
+"""GPU parity of the backward pass (chimera_kda_bwd, chimera_kda_bwd_varlen,
+chimera_gate_norm_bwd, chimera_mshortconv_bwd) against the fp64 autograd oracle
+(oracle.backward)."""
 import numpy as np
 import pytest
 
 import workloads as wl
-from oracle.backward import conv_backward_ref, kda_backward_ref
+from oracle import kda_ref, l2norm_ref
+from oracle.backward import conv_backward_ref, gate_norm_backward_ref, kda_backward_ref
 from tests.gpu_util import assert_close, rel_l2, to_device, to_host
 
 pytestmark = pytest.mark.gpu
@@ -141,7 +143,6 @@ def test_kda_bwd_full_size_directional(chm):
     sum(S_final * dS_final) along it; and the gradients of the last 2,048 tokens element by element
     against the fp64 autograd oracle run from the oracle's state before them."""
     import torch
-    from oracle import kda_ref, l2norm_ref
     T, H, d, hd, tail = 65792, 16, 128, 5, 2048
     rng = np.random.default_rng(129)
     y = wl.round_to_bf16(rng.standard_normal((1, T, 3 * H * d), dtype=np.float32))
@@ -234,6 +235,51 @@ def test_kda_bwd_varlen_equal_runs_fp32(chm):
     """fp32, 32-wide heads: three samples of 50 tokens (one batched run of three), one of 1, one of 149."""
     cu = [0, 50, 100, 150, 151, 300]
     _check_packed(chm, cu, _packed(np.random.default_rng(131), cu, 3, 32, 32, "f32"), "f32")
+
+
+@pytest.mark.parametrize("dtype,weighted", [("f32", True), ("bf16", True), ("bf16", False)])
+def test_gate_norm_bwd(chm, dtype, weighted):
+    """Eq. 15's gate and norm, backward: do, dgate (the gate a view with a wider token stride) and
+    the summed gain gradient against fp64 autograd of the definition."""
+    import torch
+    rng = np.random.default_rng(132)
+    B, T, H, dv = 2, 77, 3, 40
+    rnd = (lambda a: wl.round_to_bf16(a.astype(np.float32))) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    o, g, dy = (rnd(rng.standard_normal((B, T, H, dv))) for _ in range(3))
+    w = (1 + 0.1 * rng.standard_normal(dv)).astype(np.float32) if weighted else None
+    wide = torch.zeros(B, T, H * dv + 8, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    wide[:, :, 8:] = to_device(g.reshape(B, T, H * dv), dtype)
+    gd = wide[:, :, 8:].view(B, T, H, dv)
+    dout, dgate, dw = chm.gate_norm_bwd(to_device(o, dtype), gd, None if w is None else torch.from_numpy(w).cuda(),
+                                        to_device(dy, dtype), 1e-6)
+    ref = gate_norm_backward_ref(o, g, w, dy, 1e-6)
+    check = (lambda a, b, n: assert_close(a, b, "f32", n)) if dtype == "f32" else _close_bf16
+    check(to_host(dout), ref["do"], "do")
+    check(to_host(dgate), ref["dgate"], "dgate")
+    assert rel_l2(to_host(dw), ref["dweight"]) <= (1e-4 if dtype == "f32" else 1e-3)
+
+
+def test_gated_chain_backward_fp32(chm):
+    """The gated output's gradient through both backward calls: the KDA output, the gate and
+    norm's backward into dL/do, the KDA backward from it; against the oracle's chain rule in fp64
+    (its own output, the gate and norm's autograd, then the KDA autograd)."""
+    import torch
+    rng = np.random.default_rng(133)
+    B, T, H, d = 1, 150, 2, 32
+    q, k, v, alpha, beta, S0, _, _ = _case(rng, B, T, H, d, d, "f32")
+    g = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    dy = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    o, _ = chm.kda_fwd(dev(q), dev(k), dev(v), dev(alpha), dev(beta), dev(S0))
+    do, dgate, dw = chm.gate_norm_bwd(o, dev(g), dev(w), dev(dy), 1e-6)
+    got = {n: to_host(t) for n, t in chm.kda_bwd(dev(q), dev(k), dev(v), dev(alpha), dev(beta), dev(S0), do).items()}
+    o_ref, _ = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    gn = gate_norm_backward_ref(o_ref, g, w, dy, 1e-6)
+    ref = kda_backward_ref(q, k, v, alpha, beta, S0, gn["do"])
+    assert_close(to_host(dgate), gn["dgate"], "f32", "dgate")
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        assert_close(got[n], ref[n], "f32", n)
 
 
 def test_conv_bwd_fp32_mixed_layout(chm):

@@ -105,3 +105,34 @@ def test_identity_conv_passes_the_gradient_through():
     dy = rng.standard_normal(x.shape)
     g = conv_backward_ref(x, wt, wv, segs, dy)
     np.testing.assert_array_equal(g["dx"], dy)
+
+
+def test_gate_norm_restatement_and_gradients():
+    """The torch restatement equals the numpy gated_rmsnorm_ref; its gradients match central
+    differences of the numpy function; with a constant row and no gain the norm's gradient is
+    the closed form do = s (dy - mean(dy)) / |c| (c the constant, s = Sigmoid(gate))."""
+    from oracle import gated_rmsnorm_ref
+    from oracle.backward import gate_norm_backward_ref, gated_rmsnorm_torch
+    rng = np.random.default_rng(95)
+    o, g = rng.standard_normal((3, 2, 12)), rng.standard_normal((3, 2, 12))
+    w, dy = 1 + 0.1 * rng.standard_normal(12), rng.standard_normal((3, 2, 12))
+    f = lambda a: torch.tensor(a, dtype=torch.float64)
+    np.testing.assert_allclose(gated_rmsnorm_torch(f(o), f(g), f(w), 1e-6).numpy(), gated_rmsnorm_ref(o, g, w, 1e-6),
+                               rtol=1e-13, atol=1e-14)
+    got = gate_norm_backward_ref(o, g, w, dy, 1e-6)
+    loss = lambda o_, g_, w_: float((gated_rmsnorm_ref(o_, g_, w_, 1e-6) * dy).sum())
+    h = 1e-6
+    for name, i in (("do", 0), ("dgate", 1), ("dweight", 2)):
+        args = [o, g, w]
+        e = rng.standard_normal(args[i].shape)
+        plus = [a + h * e if j == i else a for j, a in enumerate(args)]
+        minus = [a - h * e if j == i else a for j, a in enumerate(args)]
+        fd = (loss(*plus) - loss(*minus)) / (2 * h)
+        np.testing.assert_allclose((got[name] * e).sum(), fd, rtol=1e-7, atol=1e-9, err_msg=name)
+    c, gc = -2.5, rng.standard_normal((1, 8))
+    dyc = rng.standard_normal((1, 8))
+    r = gate_norm_backward_ref(np.full((1, 8), c), gc, None, dyc, 0.0)
+    s = 1 / (1 + np.exp(-gc))
+    # y = s * sign(c): dy . dy/do_j = s_j dy_j / |c| - sign(c) sum_i s_i dy_i sign(c) / (8 |c|)
+    want = (s * dyc - (s * dyc).sum() / 8) / abs(c)
+    np.testing.assert_allclose(r["do"], want, rtol=1e-12)
