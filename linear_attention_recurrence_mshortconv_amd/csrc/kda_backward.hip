@@ -746,6 +746,9 @@ hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* worksp
                                Marks* marks) {
   if (a.B * a.H == 0) return hipSuccess;
   const BwdCut c = bwd_cut(a.B, a.T, a.H, a.dv);
+  // every pass's grid must fit before the first launch
+  const int64_t slices = std::max((a.dv + 15) / 16, (a.dk + 15) / 16);
+  if (a.B * a.H * slices * c.nseg > 0x7fffffff) return hipErrorInvalidValue;
   const int64_t sz = a.B * a.H * c.nseg * a.dk * a.dv;
   float* ckpt = static_cast<float*>(workspace);
   float* part = ckpt + a.B * a.H * ((a.T + kCk - 1) / kCk) * a.dk * a.dv;
