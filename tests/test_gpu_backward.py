@@ -116,6 +116,18 @@ def test_kda_bwd_fp32_odd_dims_segments(chm):
         assert_close(got[n], ref[n], "f32", n)
 
 
+def test_kda_bwd_fp32_extreme_dims(chm):
+    """fp32, dk = 16 (one row per thread) with dv = 256 (the largest: sixteen column slices), and
+    dk = 128 with dv = 1; T = 70 (ragged last checkpoint block)."""
+    rng = np.random.default_rng(134)
+    for dk, dv in ((16, 256), (128, 1)):
+        args = _case(rng, 1, 70, 2, dk, dv, "f32")
+        got = _run_fused_fp32(chm, *args)
+        ref = kda_backward_ref(*args)
+        for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+            assert_close(got[n], ref[n], "f32", f"{n} dk={dk} dv={dv}")
+
+
 def test_kda_bwd_bf16_segments_batch(chm):
     """bf16 d = 128, two sequences of 1000 tokens: 13 segments of 80 tokens per sequence."""
     rng = np.random.default_rng(125)
