@@ -19,8 +19,11 @@
  * Conventions for every entry point:
  *  - Pointers marked "device" are HIP device memory; "host" is ordinary host
  *    memory. The caller allocates and frees every buffer and owns the stream.
- *    No *_fwd call allocates memory, synchronises the device or keeps state
- *    between calls; calls are reentrant.
+ *    No *_fwd call allocates memory or synchronises the device. The library
+ *    keeps no state between calls beyond per-device facts it looks up once
+ *    (the compute-unit count, a kernel's LDS attribute), kept in atomics, so
+ *    calls from several host threads are safe; calls that share a workspace
+ *    or outputs on one device must not overlap.
  *  - Errors are returned as status codes; nothing aborts or throws across the
  *    ABI. All arguments are checked before any launch; on an error nothing is
  *    written. A failed kernel launch returns CHIMERA_ERR_HIP. A fault inside a
@@ -106,8 +109,11 @@ chimera_status chimera_mshortconv_index(const chimera_segment* segs, int32_t nse
 
 /*
  * chimera_mshortconv_index_device -- the same table, computed on the device
- * by the address arithmetic the convolution kernel itself uses to find its
- * neighbours. For checking that arithmetic bit for bit.
+ * from the segment descriptors with the device-side grid helpers (raster index
+ * and bounds of Eq. 12) that the convolution kernels are written with. The
+ * kernels' own gathers (staged tiles, buffer offsets, text windows) do not run
+ * here; their taps are checked through chimera_mshortconv_fwd itself, with
+ * one-hot weights and inputs that encode each token's position.
  *
  *   idx_dev  device int32 [T][27], written asynchronously on `stream`.
  */
@@ -171,11 +177,18 @@ size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, i
  *
  * Supported: dk, dv in 1..256 for the token-by-token kernel (fp32 and bf16);
  * the chunked MFMA kernel runs for bf16 with dk = dv = 128. alpha < 0 is
- * undefined. The chunked kernel factors the decay inside 16-token blocks and
- * raises alpha below e^-7.5 (5.5e-4) to that value as it loads it, which keeps
- * every factor within bf16 range and precision: a token with alpha = 0 (complete
- * forgetting) then keeps 5.5e-4 of each decayed state channel, below bf16
- * resolution. The token-by-token kernel uses alpha as given.
+ * undefined.
+ *
+ * Small alpha on the chunked kernel: it factors the decay inside 16-token
+ * blocks and raises every alpha below e^-7.5 (about 5.5e-4) to e^-7.5 as it
+ * loads it, which keeps every factor within bf16 range and precision. The result
+ * then departs from Eq. 14 only where an alpha is below that value: such a token
+ * keeps e^-7.5 of each decayed state channel instead of alpha of it, an absolute
+ * error of at most 5.5e-4 times that channel's magnitude (alpha = 0, complete
+ * forgetting, leaves 5.5e-4 of the old channel), under one bf16 rounding step of
+ * the channel (2^-8 relative). CHIMERA_KDA_SEQUENTIAL (the token-by-token
+ * kernel) uses alpha exactly as given, for callers that need hard resets to be
+ * exact.
  * Asynchronous on `stream`; o and S_final must not alias any input.
  */
 chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride,
@@ -308,8 +321,10 @@ chimera_status chimera_kda_fwd_gated_timed(const void* q, const void* k, const v
  *
  * A packed row of equal-length samples gives the same result as chimera_kda_fwd with
  * B = nseq. The chunked kernel launches once for up to 48 stretches of equal-length
- * consecutive samples; the token-by-token kernel once per such stretch. Errors as for
- * chimera_kda_fwd; host only until the launches, asynchronous on `stream`.
+ * consecutive samples; the token-by-token kernel once per such stretch. The chunked
+ * kernel raises alpha below e^-7.5 to that value, with the bound stated at
+ * chimera_kda_fwd (CHIMERA_KDA_SEQUENTIAL is exact). Errors as for chimera_kda_fwd;
+ * host only until the launches, asynchronous on `stream`.
  */
 size_t chimera_kda_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
                                          int64_t dv, chimera_dtype dt, uint32_t flags);

@@ -145,6 +145,41 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _need(cond: bool, msg: str):
+    """Argument check of the wrappers: raises before anything reaches the library."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dense(t, name: str, shape, dtype, device):
+    """t must be a dense (contiguous) tensor of this shape and dtype on `device`: the library
+    reads it through one pointer with the row-major strides of `shape`."""
+    _need(t is not None, f"{name} is required")
+    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _need(t.dtype == dtype, f"{name}: dtype {t.dtype}, expected {dtype}")
+    _need(t.device == device, f"{name}: on {t.device}, expected {device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous (no expanded or strided views)")
+
+
+def _opt_dense(t, name: str, shape, dtype, device):
+    if t is not None:
+        _dense(t, name, shape, dtype, device)
+
+
+def _on_gpu(t, name: str):
+    _need(t.is_cuda, f"{name} must be a GPU tensor: the library runs every step on the device")
+
+
+def _conv_weights(w_text, w_vis, C: int, device):
+    """The conv weights as device fp32 [C][4] and [C][27] (copied when they are not)."""
+    import torch
+    w_text = w_text.to(device=device, dtype=torch.float32).contiguous()
+    w_vis = w_vis.to(device=device, dtype=torch.float32).contiguous()
+    _need(tuple(w_text.shape) == (C, TEXT_TAPS), f"w_text: shape {tuple(w_text.shape)}, expected {(C, TEXT_TAPS)}")
+    _need(tuple(w_vis.shape) == (C, VIS_TAPS), f"w_vis: shape {tuple(w_vis.shape)}, expected {(C, VIS_TAPS)}")
+    return w_text, w_vis
+
+
 def mshortconv_index(segments: Sequence, T: int) -> np.ndarray:
     """Host neighbour table int32 [T, 27] (chimera_mshortconv_index)."""
     idx = np.empty((max(T, 0), VIS_TAPS), dtype=np.int32)
@@ -193,12 +228,13 @@ def mshortconv_fwd(x, w_text, w_vis, segments: Sequence, out=None, marks: Option
     With `marks`, calls chimera_mshortconv_fwd_timed instead and records them.
     """
     import torch
-    assert x.is_cuda and x.is_contiguous() and x.dim() == 3
+    _need(x.dim() == 3, "x must be [B, T, C]")
     B, T, C = x.shape
-    w_text = w_text.to(device=x.device, dtype=torch.float32).contiguous()
-    w_vis = w_vis.to(device=x.device, dtype=torch.float32).contiguous()
+    _dense(x, "x", (B, T, C), x.dtype, x.device)
+    _opt_dense(out, "out", (B, T, C), x.dtype, x.device)
+    w_text, w_vis = _conv_weights(w_text, w_vis, C, x.device)
+    _on_gpu(x, "x")
     y = torch.empty_like(x) if out is None else out
-    assert y.shape == x.shape and y.dtype == x.dtype and y.is_contiguous()
     segs = segment_array(segments)
     args = (_ptr(x), _ptr(y), B, T, C, _dtype_code(x), _ptr(w_text), _ptr(w_vis), segs, len(segments), _stream(x))
     if marks is None:
@@ -216,10 +252,11 @@ def kda_workspace_size(B, T, H, dk, dv, dtype_code: int, flags: int) -> int:
 
 def _token_view_stride(t, B, T, H, d) -> int:
     """Token stride of a [B, T, H, d] view whose [H, d] block per token is contiguous."""
-    assert t.shape == (B, T, H, d), (t.shape, (B, T, H, d))
+    _need(tuple(t.shape) == (B, T, H, d), f"shape {tuple(t.shape)}, expected {(B, T, H, d)}")
     s = t.stride()
     if T > 1 or B > 1:
-        assert s[3] == 1 and s[2] == d and (B == 1 or s[0] == T * s[1]), s
+        _need(s[3] == 1 and s[2] == d and (B == 1 or s[0] == T * s[1]) and (T <= 1 or s[1] >= H * d),
+              f"strides {s}: each token's [H, d] block must be dense, tokens evenly spaced")
     return s[1] if T > 0 else H * d
 
 
@@ -241,31 +278,32 @@ def kda_fwd(q, k, v, alpha, beta, S0=None, *, l2norm: bool = True, sequential: b
     import torch
     B, T, H, dk = k.shape
     dv = v.shape[-1]
+    dev, tdt = k.device, k.dtype
     stride = _token_view_stride(q, B, T, H, dk)
-    assert _token_view_stride(k, B, T, H, dk) == stride and _token_view_stride(v, B, T, H, dv) == stride
-    assert alpha.shape == (B, T, H, dk) and alpha.is_contiguous()
-    assert beta.shape == (B, T, H) and beta.is_contiguous()
+    _need(_token_view_stride(k, B, T, H, dk) == stride and _token_view_stride(v, B, T, H, dv) == stride,
+          "q, k, v must share one token stride")
+    _need(q.device == dev and v.device == dev and q.dtype == tdt and v.dtype == tdt, "q, k, v: one device and dtype")
+    _dense(alpha, "alpha", (B, T, H, dk), tdt, dev)
+    _dense(beta, "beta", (B, T, H), tdt, dev)
+    _opt_dense(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    _opt_dense(state_out, "state_out", (B, H, dk, dv), torch.float32, dev)
+    _opt_dense(out, "out", (B, T, H, dv), tdt, dev)
+    _on_gpu(k, "k")
     dt = _dtype_code(k)
-    assert q.dtype == k.dtype == v.dtype == alpha.dtype == beta.dtype
     flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0) | (KDA_NO_SPLIT if no_split else 0)
     o = torch.empty((B, T, H, dv), dtype=k.dtype, device=k.device) if out is None else out
     Sf = state_out
     if Sf is None and want_state:
         Sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=k.device)
-    if Sf is not None:
-        assert Sf.dtype == torch.float32 and Sf.is_contiguous() and Sf.shape == (B, H, dk, dv)
-    if S0 is not None:
-        assert S0.dtype == torch.float32 and S0.is_contiguous() and S0.shape == (B, H, dk, dv)
     need = kda_workspace_size(B, T, H, dk, dv, dt, flags)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     tail = (B, T, H, dk, dv, dt, flags, _ptr(workspace), wbytes, _stream(k))
     if gate is not None:
-        assert gate.dtype == k.dtype and gate.is_cuda
+        _need(gate.dtype == tdt and gate.device == dev, "gate: the dtype and device of q, k, v")
         gstride = _token_view_stride(gate, B, T, H, dv)
-        if norm_weight is not None:
-            assert norm_weight.dtype == torch.float32 and norm_weight.is_contiguous() and norm_weight.shape == (dv,)
+        _opt_dense(norm_weight, "norm_weight", (dv,), torch.float32, dev)
         args = (_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(gate), gstride,
                 _ptr(norm_weight), float(norm_eps), _ptr(o), _ptr(Sf)) + tail
         if marks is None:
@@ -309,34 +347,36 @@ def kda_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, l2norm: bool = 
     import torch
     T, H, dk = k.shape
     dv = v.shape[-1]
+    dev, tdt = k.device, k.dtype
     cu = _cu_array(cu_seqlens)
     N = len(cu) - 1
-    assert cu[0] == 0 and cu[-1] == T
+    _need(N >= 0 and cu[0] == 0 and cu[-1] == T and bool(np.all(np.diff(cu) >= 0)),
+          "cu_seqlens: 0 first, nondecreasing, T last")
     stride = _token_view_stride(q.unsqueeze(0), 1, T, H, dk)
-    assert _token_view_stride(k.unsqueeze(0), 1, T, H, dk) == stride
-    assert _token_view_stride(v.unsqueeze(0), 1, T, H, dv) == stride
-    assert alpha.shape == (T, H, dk) and alpha.is_contiguous() and beta.shape == (T, H) and beta.is_contiguous()
+    _need(_token_view_stride(k.unsqueeze(0), 1, T, H, dk) == stride and
+          _token_view_stride(v.unsqueeze(0), 1, T, H, dv) == stride, "q, k, v must share one token stride")
+    _need(q.device == dev and v.device == dev and q.dtype == tdt and v.dtype == tdt, "q, k, v: one device and dtype")
+    _dense(alpha, "alpha", (T, H, dk), tdt, dev)
+    _dense(beta, "beta", (T, H), tdt, dev)
+    _opt_dense(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    _opt_dense(state_out, "state_out", (N, H, dk, dv), torch.float32, dev)
+    _opt_dense(out, "out", (T, H, dv), tdt, dev)
+    _on_gpu(k, "k")
     dt = _dtype_code(k)
-    assert q.dtype == k.dtype == v.dtype == alpha.dtype == beta.dtype
     flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0) | (KDA_NO_SPLIT if no_split else 0)
     o = torch.empty((T, H, dv), dtype=k.dtype, device=k.device) if out is None else out
     Sf = state_out
     if Sf is None and want_state:
         Sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=k.device)
-    if Sf is not None:
-        assert Sf.dtype == torch.float32 and Sf.is_contiguous() and Sf.shape == (N, H, dk, dv)
-    if S0 is not None:
-        assert S0.dtype == torch.float32 and S0.is_contiguous() and S0.shape == (N, H, dk, dv)
     need = kda_varlen_workspace_size(cu, H, dk, dv, dt, flags)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     gstride = 0
     if gate is not None:
-        assert gate.dtype == k.dtype and gate.is_cuda
+        _need(gate.dtype == tdt and gate.device == dev, "gate: the dtype and device of q, k, v")
         gstride = _token_view_stride(gate.unsqueeze(0), 1, T, H, dv)
-        if norm_weight is not None:
-            assert norm_weight.dtype == torch.float32 and norm_weight.is_contiguous() and norm_weight.shape == (dv,)
+        _opt_dense(norm_weight, "norm_weight", (dv,), torch.float32, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(gate), gstride,
             _ptr(norm_weight), float(norm_eps), _ptr(o), _ptr(Sf), cu.ctypes.data, N, H, dk, dv, dt, flags,
             _ptr(workspace), wbytes, _stream(k))
@@ -357,15 +397,25 @@ def kda_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, l2norm: bool = Tru
     import torch
     B, T, H, dk = k.shape
     dv = v.shape[-1]
+    dev, tdt = k.device, k.dtype
     stride = _token_view_stride(q, B, T, H, dk)
-    assert _token_view_stride(k, B, T, H, dk) == stride and _token_view_stride(v, B, T, H, dv) == stride
+    _need(_token_view_stride(k, B, T, H, dk) == stride and _token_view_stride(v, B, T, H, dv) == stride,
+          "q, k, v must share one token stride")
+    _need(q.device == dev and v.device == dev and q.dtype == tdt and v.dtype == tdt, "q, k, v: one device and dtype")
+    _dense(alpha, "alpha", (B, T, H, dk), tdt, dev)
+    _dense(beta, "beta", (B, T, H), tdt, dev)
+    _dense(dout, "dout", (B, T, H, dv), tdt, dev)
+    _opt_dense(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    _opt_dense(dS_final, "dS_final", (B, H, dk, dv), torch.float32, dev)
+    _on_gpu(k, "k")
     dt = _dtype_code(k)
     if grads is None:
-        assert stride == H * dk and stride == H * dv, "strided (fused) inputs: pass `grads` with their layout"
+        _need(stride == H * dk and stride == H * dv, "strided (fused) inputs: pass `grads` with their layout")
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dkk, dvv = grads
     for g, t in zip(grads, (q, k, v)):
-        assert g.shape == t.shape and g.stride() == t.stride()
+        _need(g.shape == t.shape and g.stride() == t.stride() and g.dtype == tdt and g.device == dev,
+              "grads must have the layout, dtype and device of q, k, v")
     dalpha = torch.empty_like(alpha)
     dbeta = torch.empty_like(beta)
     dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=k.device)
@@ -388,18 +438,29 @@ def kda_bwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0, dout, dS_final=None, *,
     import torch
     T, H, dk = k.shape
     dv = v.shape[-1]
+    dev, tdt = k.device, k.dtype
     stride = _token_view_stride(q[None], 1, T, H, dk)
-    assert _token_view_stride(k[None], 1, T, H, dk) == stride and _token_view_stride(v[None], 1, T, H, dv) == stride
+    _need(_token_view_stride(k[None], 1, T, H, dk) == stride and _token_view_stride(v[None], 1, T, H, dv) == stride,
+          "q, k, v must share one token stride")
+    _need(q.device == dev and v.device == dev and q.dtype == tdt and v.dtype == tdt, "q, k, v: one device and dtype")
     cu = _cu_array(cu_seqlens)
     nseq = len(cu) - 1
-    assert cu[-1] == T
+    _need(nseq >= 0 and cu[0] == 0 and cu[-1] == T and bool(np.all(np.diff(cu) >= 0)),
+          "cu_seqlens: 0 first, nondecreasing, T last")
+    _dense(alpha, "alpha", (T, H, dk), tdt, dev)
+    _dense(beta, "beta", (T, H), tdt, dev)
+    _dense(dout, "dout", (T, H, dv), tdt, dev)
+    _opt_dense(S0, "S0", (nseq, H, dk, dv), torch.float32, dev)
+    _opt_dense(dS_final, "dS_final", (nseq, H, dk, dv), torch.float32, dev)
+    _on_gpu(k, "k")
     dt = _dtype_code(k)
     if grads is None:
-        assert stride == H * dk and stride == H * dv, "strided (fused) inputs: pass `grads` with their layout"
+        _need(stride == H * dk and stride == H * dv, "strided (fused) inputs: pass `grads` with their layout")
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dkk, dvv = grads
     for g, t in zip(grads, (q, k, v)):
-        assert g.shape == t.shape and g.stride() == t.stride()
+        _need(g.shape == t.shape and g.stride() == t.stride() and g.dtype == tdt and g.device == dev,
+              "grads must have the layout, dtype and device of q, k, v")
     dalpha = torch.empty_like(alpha)
     dbeta = torch.empty_like(beta)
     dS0 = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=k.device)
@@ -420,8 +481,15 @@ def gate_norm_bwd(o, gate, norm_weight, dy, norm_eps: float = 1e-6, *, want_weig
     [B, T, H, dv]; gate [B, T, H, dv] with a token stride of its own. Returns (dout, dgate,
     dnorm_weight or None)."""
     import torch
+    _need(o.dim() == 4, "o must be [B, T, H, dv]")
     B, T, H, dv = o.shape
+    dev, tdt = o.device, o.dtype
+    _dense(o, "o", (B, T, H, dv), tdt, dev)
+    _dense(dy, "dy", (B, T, H, dv), tdt, dev)
+    _need(gate.dtype == tdt and gate.device == dev, "gate: the dtype and device of o")
     gs = _token_view_stride(gate, B, T, H, dv)
+    _opt_dense(norm_weight, "norm_weight", (dv,), torch.float32, dev)
+    _on_gpu(o, "o")
     dout = torch.empty_like(o)
     dgate = torch.empty_strided(gate.shape, gate.stride(), dtype=gate.dtype, device=gate.device)
     dw = torch.empty(dv, dtype=torch.float32, device=o.device) if want_weight_grad else None
@@ -434,9 +502,13 @@ def gate_norm_bwd(o, gate, norm_weight, dy, norm_eps: float = 1e-6, *, want_weig
 def mshortconv_bwd(x, dy, w_text, w_vis, segments: Sequence, dx=None):
     """Gradients of mshortconv_fwd (chimera_mshortconv_bwd): returns (dx, dw_text, dw_vis)."""
     import torch
+    _need(x.dim() == 3, "x must be [B, T, C]")
     B, T, C = x.shape
-    w_text = w_text.to(device=x.device, dtype=torch.float32).contiguous()
-    w_vis = w_vis.to(device=x.device, dtype=torch.float32).contiguous()
+    _dense(x, "x", (B, T, C), x.dtype, x.device)
+    _dense(dy, "dy", (B, T, C), x.dtype, x.device)
+    _opt_dense(dx, "dx", (B, T, C), x.dtype, x.device)
+    w_text, w_vis = _conv_weights(w_text, w_vis, C, x.device)
+    _on_gpu(x, "x")
     dx = torch.empty_like(x) if dx is None else dx
     dwt = torch.empty((C, TEXT_TAPS), dtype=torch.float32, device=x.device)
     dwv = torch.empty((C, VIS_TAPS), dtype=torch.float32, device=x.device)
@@ -452,15 +524,25 @@ def kda_fwd_conv(x, w_text, w_vis, segments: Sequence, alpha, beta, S0=None, *, 
     """mShortConv and KDA in one pass (chimera_kda_fwd_conv): x [B, T, H*(2 dk + dv)] holds the
     pre-conv q|k|v channels; returns (o [B, T, H, dv], S_final or None)."""
     import torch
+    _need(x.dim() == 3, "x must be [B, T, C]")
     B, T, C = x.shape
-    assert C == H * (2 * dk + dv) and x.is_contiguous()
+    dev, tdt = x.device, x.dtype
+    _need(C == H * (2 * dk + dv), f"x has {C} channels, expected H * (2 dk + dv) = {H * (2 * dk + dv)}")
+    _dense(x, "x", (B, T, C), tdt, dev)
+    _dense(alpha, "alpha", (B, T, H, dk), tdt, dev)
+    _dense(beta, "beta", (B, T, H), tdt, dev)
+    _opt_dense(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    _opt_dense(out, "out", (B, T, H, dv), tdt, dev)
+    _opt_dense(state_out, "state_out", (B, H, dk, dv), torch.float32, dev)
+    w_text, w_vis = _conv_weights(w_text, w_vis, C, dev)
+    _on_gpu(x, "x")
     dt = _dtype_code(x)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=x.dtype, device=x.device)
     Sf = state_out if state_out is not None else (
         torch.empty((B, H, dk, dv), dtype=torch.float32, device=x.device) if want_state else None)
     arr = segment_array(segments)
     _check("chimera_kda_fwd_conv", lib().chimera_kda_fwd_conv(
-        _ptr(x), _ptr(w_text), _ptr(w_vis), arr, len(arr), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(Sf),
+        _ptr(x), _ptr(w_text), _ptr(w_vis), arr, len(segments), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(Sf),
         B, T, H, dk, dv, dt, KDA_L2NORM_QK if l2norm else 0, _stream(x)))
     return o, Sf
 
@@ -468,6 +550,6 @@ def kda_fwd_conv(x, w_text, w_vis, segments: Sequence, alpha, beta, S0=None, *, 
 def split_qkv(y, H: int, d: int):
     """Views q, k, v [B, T, H, d] into a fused [B, T, 3*H*d] conv output (no copy)."""
     B, T, C = y.shape
-    assert C == 3 * H * d
+    _need(C == 3 * H * d, f"y has {C} channels, expected 3 * H * d = {3 * H * d}")
     parts = y.view(B, T, 3, H, d)
     return parts[:, :, 0], parts[:, :, 1], parts[:, :, 2]

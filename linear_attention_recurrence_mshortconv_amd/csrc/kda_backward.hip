@@ -644,10 +644,10 @@ template <typename T>
 hipError_t conv_bwd_t(const void* x, const void* dy, void* dx, float* dw_text, float* dw_vis, int64_t B, int64_t Ttot,
                       int64_t C, const float* w_text, const float* w_vis, const Seg* segs, int nseg,
                       hipStream_t stream, Marks* marks) {
+  if (B > 65535) return hipErrorInvalidValue;   // grid z of the per-segment kernels; checked before any write
   hipError_t e = zero(dw_text, C * kTextTaps, stream);
   if (e == hipSuccess) e = zero(dw_vis, C * kVisTaps, stream);
   if (e != hipSuccess) return e;
-  if (B > 65535) return hipErrorInvalidValue;
   // dx of the image grids that the rows kernel takes: that kernel with mirrored taps, in one launch
   std::vector<Seg> rows;
   const bool bf16 = sizeof(T) == 2;

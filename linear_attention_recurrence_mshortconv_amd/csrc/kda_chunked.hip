@@ -36,6 +36,7 @@
 // With one output segment only the output pass runs, starting from S0.
 #include <cstddef>
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "dtypes.h"
@@ -1665,8 +1666,10 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
   int dev = 0;
   hipError_t de = hipGetDevice(&dev);
   if (de != hipSuccess) return de;
-  static bool attr_done[64] = {};
-  if (dev < 0 || dev >= 64 || !attr_done[dev]) {
+  // The LDS attribute is set once per device; the flag is atomic so that host threads calling
+  // at once on one device race on nothing (setting it twice is harmless).
+  static std::atomic<bool> attr_done[64];
+  if (dev < 0 || dev >= 64 || !attr_done[dev].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_out_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -1676,7 +1679,7 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_sum_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds_sum);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) attr_done[dev] = true;
+    if (dev >= 0 && dev < 64) attr_done[dev].store(true, std::memory_order_release);
   }
   auto round8 = [](int64_t n) { return (int)((n + 7) / 8 * 8); };
   // runs go to the kernels kMaxRuns at a time (the table travels in the kernel arguments)

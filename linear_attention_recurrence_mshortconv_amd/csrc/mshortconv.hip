@@ -20,6 +20,7 @@
 //    slides a 3-row window down its column, so each staged value is read from
 //    LDS once per (kw) and feeds up to three output rows.
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "dtypes.h"
@@ -505,16 +506,19 @@ __global__ void index_device_kernel(Seg seg, int32_t* __restrict__ idx) {
       }
 }
 
-// Compute units of the current device (cached per device; 256 on MI355X).
+// Compute units of the current device (256 on MI355X). The query is cached per device in an
+// atomic: concurrent first calls from several host threads store the same value.
 int device_cus() {
-  static int cus[64] = {};
+  static std::atomic<int> cus[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  int c = dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
+  if (c == 0) {
     int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    c = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    if (dev < 64) cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return c;
 }
 
 template <int NF, int CPT, int TR, int TW>

@@ -41,6 +41,71 @@ def test_device_neighbour_arithmetic_bit_exact(chm):
         assert np.array_equal(got, neighbours_ref(segs, T)), segs[:2]
 
 
+def _position_code(B, T, C):
+    """x[b, p, c] = digit (c mod 3) of b*T + p in base 256, plus 1: integers 1..256, exact in bf16
+    and fp32, so that a conv with a single unit tap copies its source token's code unchanged
+    (zero padding reads as 0, which no code takes)."""
+    pos = np.arange(B * T, dtype=np.int64).reshape(B, T, 1)
+    digit = np.arange(C) % 3
+    return ((pos >> (8 * digit)) & 255).astype(np.float32) + 1.0
+
+
+def _decode(y):
+    """Source token (b*T + p) of every output row from its first three channels, -1 for all-zero
+    rows; every channel must carry the code of the same source."""
+    y = np.asarray(y, dtype=np.float64)
+    C = y.shape[-1]
+    assert np.array_equal(y, y[..., np.arange(C) % 3]), "channels of one row gathered different sources"
+    d = y[..., :3].astype(np.int64)
+    zero = (d == 0).all(-1)
+    assert ((d >= 1) | zero[..., None]).all(), "partly padded row"
+    src = (d[..., 0] - 1) + ((d[..., 1] - 1) << 8) + ((d[..., 2] - 1) << 16)
+    return np.where(zero, -1, src)
+
+
+@pytest.mark.parametrize("dtype,C,kernels", [
+    ("bf16", 64, {"conv_text_kernel", "conv_rows_kernel", "conv_tile_kernel"}),
+    ("bf16", 72, {"conv_text_kernel", "conv_gather_kernel"}),
+    ("f32", 64, {"conv_text_kernel", "conv_gather_kernel"}),
+])
+def test_conv_gathers_bit_exact_one_hot(chm, dtype, C, kernels):
+    """The taps the product conv kernels actually read, bit for bit: for each tap, weights that are
+    1 on that tap and 0 elsewhere make y a copy of the tap's source token (Eq. 13 with a one-hot
+    kernel), and the inputs encode every token's position exactly, so decoding y gives the
+    neighbour table each kernel used. Compared with neighbours_ref (Eq. 12 raster order, zero
+    padding at segment edges, causal in time) for all 4 text and 27 visual taps, two batch items."""
+    import torch
+    S = wl.Segment
+    segs = _mixed_layout() + (S(wl.IMAGE, 1689 + 5 * 19 * 23, 1 * 70, 1, 1, 70),)
+    T = sum(s.length for s in segs)
+    B = 2
+    table = neighbours_ref(segs, T)
+    is_text = np.zeros(T, dtype=bool)
+    for sg in segs:
+        if sg.kind == wl.TEXT:
+            is_text[sg.start:sg.start + sg.length] = True
+    x = to_device(_position_code(B, T, C), dtype)
+    ran = set()
+    for part, ntaps in (("text", 4), ("vis", 27)):
+        for j in range(ntaps):
+            wt = np.zeros((C, 4), np.float32)
+            wv = np.zeros((C, 27), np.float32)
+            (wt if part == "text" else wv)[:, j] = 1.0
+            marks = chm.Marks(len(segs) + 1)
+            y = chm.mshortconv_fwd(x, torch.from_numpy(wt), torch.from_numpy(wv), segs, marks=marks)
+            torch.cuda.synchronize()
+            ran |= {n for n, _ in marks.kernels()}
+            got = _decode(to_host(y))
+            mine = is_text if part == "text" else ~is_text
+            want = np.where(mine, table[:, j], -1)
+            for b in range(B):
+                exp_b = np.where(want >= 0, want + b * T, -1)
+                bad = np.nonzero(got[b] != exp_b)[0]
+                assert bad.size == 0, (f"{part} tap {j}, batch {b}: token {bad[0]} read {got[b][bad[0]]}, "
+                                       f"expected {exp_b[bad[0]]}")
+    assert ran == kernels, ran
+
+
 def _conv_bound(x, wt, wv, segs, dtype):
     """Element-wise error bound: fp32 accumulation of up to 27 terms plus one
     rounding to the output dtype (half an ulp: 2^-8 relative for bf16, 2^-24 for fp32)."""

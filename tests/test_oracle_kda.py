@@ -194,6 +194,21 @@ def test_l2norm_unit_rows_and_eps():
     assert np.array_equal(l2norm_ref(np.zeros((2, 4))), np.zeros((2, 4)))
 
 
+def test_l2norm_hand_examples(golden_dir):
+    """l2norm_ref against hand-computed values (tests/golden/l2norm_hand_examples.json): the 3-4-5 and
+    1-2-2 triangles, the zero vector, a tiny vector that shows the epsilon inside the square root, signs,
+    and two heads of one token normalised on their own."""
+    import json
+    import os
+    g = json.load(open(os.path.join(golden_dir, "l2norm_hand_examples.json")))
+    for ex in g["examples"]:
+        np.testing.assert_allclose(l2norm_ref(np.array(ex["x"]), g["eps"]), ex["y"], rtol=1e-15, atol=0,
+                                   err_msg=ex["name"])
+    np.testing.assert_allclose(l2norm_ref(np.array(g["heads"]["x"])), g["heads"]["y"], rtol=1e-15, atol=0)
+    # the default epsilon is the fixture's
+    np.testing.assert_allclose(l2norm_ref(np.array([3.0, 4.0])), g["examples"][0]["y"], rtol=1e-15, atol=0)
+
+
 def _variant(q, k, v, alpha, beta, S0, mode):
     """Plausible misreadings of Eq. 14/15, used to show the fixtures catch them."""
     q, k, v, a, b = [np.asarray(z, dtype=np.float64) for z in (q, k, v, alpha, beta)]
