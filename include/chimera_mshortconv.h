@@ -199,6 +199,28 @@ chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int6
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * chimera_kda_fwd_noalloc -- chimera_kda_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * computation, kernels, results and errors as chimera_kda_fwd with the same arguments, except
+ * that the workspace is not an argument: it is a device array of
+ * CHIMERA_KDA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on (from the
+ * first use there until the process ends).
+ *
+ *   q .. flags, stream   as for chimera_kda_fwd
+ *
+ * Returns CHIMERA_ERR_WORKSPACE, before any launch and any HIP call, when
+ * chimera_kda_workspace_size() for these sizes and flags exceeds
+ * CHIMERA_KDA_NOALLOC_SCRATCH_BYTES (the batched workloads of this library need at most 96 MiB).
+ * Calls no hipMalloc or hipFree. Every call on one GPU uses that GPU's one array: calls that
+ * overlap on one device (on two streams, or from two host threads) race and must not be issued.
+ */
+#define CHIMERA_KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+chimera_status chimera_kda_fwd_noalloc(const void* q, const void* k, const void* v, int64_t qkv_stride,
+                                       const void* alpha, const void* beta, const float* S0, void* o,
+                                       float* S_final, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                       chimera_dtype dt, uint32_t flags, hipStream_t stream);
+
+/*
  * chimera_kda_fwd_conv -- mShortConv and KDA in one pass (Chimera page 1, section 3.4:
  * the conv on packed storage fused with the recurrence; Eq. 13 then Eq. 14): q, k and v of
  * every token are computed from x in the recurrence's load stage, rounded to dt as

@@ -20,6 +20,7 @@ F32, BF16 = 0, 1
 KDA_L2NORM_QK = 1
 KDA_SEQUENTIAL = 2
 KDA_NO_SPLIT = 4
+KDA_NOALLOC_SCRATCH_BYTES = 128 << 20   # CHIMERA_KDA_NOALLOC_SCRATCH_BYTES
 TEXT_TAPS, VIS_TAPS = 4, 27
 
 STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "bad dtype", 4: "bad segments",
@@ -98,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.chimera_kda_fwd_conv.restype = ctypes.c_int
     L.chimera_kda_fwd_conv.argtypes = [vp, vp, vp, seg_p, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                        ctypes.c_int, u32, vp]
+    L.chimera_kda_fwd_noalloc.restype = ctypes.c_int
+    L.chimera_kda_fwd_noalloc.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          ctypes.c_int, u32, vp]
     L.chimera_kda_fwd_varlen_timed.restype = ctypes.c_int
     L.chimera_kda_fwd_varlen_timed.argtypes = L.chimera_kda_fwd_varlen.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
     _lib = L
