@@ -66,6 +66,54 @@ KERNEL_SOURCE = {
 }
 
 
+def kda_flops_per_token_head(d: int, C: int = 64) -> float:
+    """Algorithmic FLOPs of the chunked KDA per token and head: the intra-chunk products A, Aqk,
+    W, U~ (2 C d each) and the triangular inverse (2 C^2 / 3), then U = U~ - W S, Q^ S, the state
+    update (2 d^2 each) and Aqk U (2 C d): 182,955 at d = 128, C = 64 (no dense T x T work)."""
+    return 6 * d * d + 10 * C * d + 2 * C * C / 3
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def pool_cores() -> int:
+    """Host threads for the oracle pool: the cores this process may run on, at most 16 (the host
+    share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _oracle_head_job(job):
+    """One head of the oracle sample (all batch items or packed samples): the conv of the head's q, k
+    and v channels, the rounding to the storage type, the L2 norms and the token loop, in fp64 on one
+    core. Runs in a pool worker."""
+    from threadpoolctl import threadpool_limits
+    from oracle import conv_ref, kda_ref, kda_varlen_ref, l2norm_ref, round_bf16_ref
+    x, wt, wv, segs, alpha, beta, S0, bf16, cu = job
+    with threadpool_limits(limits=1):
+        y = conv_ref(x, wt, wv, segs)
+        if bf16:
+            y = round_bf16_ref(y)
+        B, n = y.shape[:2]
+        parts = y.reshape(B, n, 3, 1, -1)
+        if cu is not None:
+            kda_varlen_ref(l2norm_ref(parts[0, :, 0]), l2norm_ref(parts[0, :, 1]), parts[0, :, 2], alpha[0], beta[0],
+                           cu, None)
+        else:
+            kda_ref(l2norm_ref(parts[:, :, 0]), l2norm_ref(parts[:, :, 1]), parts[:, :, 2], alpha, beta, S0)
+    return n * B
+
+
 def short_name(full: str) -> str:
     """'void chm::(anonymous namespace)::conv_rows_kernel<4, 32>(...)' -> 'conv_rows_kernel'."""
     s = full.replace("(anonymous namespace)::", "")
@@ -104,15 +152,20 @@ def _args():
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="markdown HBM traffic table from FETCH_SIZE and WRITE_SIZE counter_collection.csv files")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="markdown table of the SQ counters of the KDA kernels (image_4096, one step)")
     return ap.parse_args()
 
 
 # ----------------------------------------------------------------------------------------------------------
 # algorithmic work per launch (bytes that the kernel's job must move, or flops it must do)
 
-def kda_split(B: int, T: int, H: int, target_blocks: int = 512):
+KDA_TARGET_BLOCKS = 256   # the library's plan: about one block of each KDA pass per CU
+
+
+def kda_split(B: int, T: int, H: int, target_blocks: int = KDA_TARGET_BLOCKS):
     """Chunks covered by the summary pass of the chunked KDA: the library cuts every sequence into
-    segments of Lo 64-token chunks, Lo chosen so that about 512 output blocks cover the B*H
+    segments of Lo 64-token chunks, Lo chosen so that about 256 output blocks cover the B*H
     sequence-heads, and summarises all segments but the last. Returns (chunks, summarised chunks)."""
     nc = (T + 63) // 64
     lo = max(1, (B * H * nc + target_blocks - 1) // target_blocks)
@@ -122,11 +175,12 @@ def kda_split(B: int, T: int, H: int, target_blocks: int = 512):
 
 def kda_summarised_tokens(w) -> int:
     """Tokens (per head) that the summary pass reads: every sequence's chunks but those of its last
-    output segment, with the library's plan (one Lo for all sequences of the call)."""
+    output segment, with the library's plan (one Lo for all sequences of the call; for packed samples
+    of mixed lengths the library may pick a shorter Lo, which this estimate ignores)."""
     lens = ([w.samples[i + 1] - w.samples[i] for i in range(len(w.samples) - 1)] if w.samples
             else [w.T] * w.B)
     ncs = [(n + 63) // 64 for n in lens]
-    lo = max(1, (w.H * sum(ncs) + 511) // 512)
+    lo = max(1, (w.H * sum(ncs) + KDA_TARGET_BLOCKS - 1) // KDA_TARGET_BLOCKS)
     toks = 0
     for n, nc in zip(lens, ncs):
         p = 1 if nc <= 1 else (nc + lo - 1) // lo
@@ -229,6 +283,52 @@ def summarize_pmc(fetch_csv: str, write_csv: str):
         print(f"| `{k}` | {source_hash(k)} | {fk:.0f} | {wk:.0f} | {scaled / 1e6:.1f} | {algs} | {ratio} |")
 
 
+def summarize_counters(paths, chunk_heads: dict):
+    """Per-kernel table of SQ counters from rocprofv3 --pmc counter_collection.csv files (several passes).
+    Derived figures use the conventions of these counters on gfx9: SQ_WAVE_CYCLES and SQ_ACTIVE_INST_*
+    count quad-cycles (4 clocks), SQ_BUSY_CYCLES sums clocks over the 32 shader engines, and
+    SQ_VALU_MFMA_BUSY_CYCLES sums clocks over the 1024 SIMDs."""
+    vals = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"]) if r["Kernel_Name"] != COPY_KERNEL else COPY_KERNEL
+            if k not in KERNEL_SOURCE:
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+    names = sorted({c for d in avg.values() for c in d})
+    ks = [k for k in ("kda_sum_kernel", "kda_combine_kernel", "kda_out_kernel", "kda_out_gated_kernel") if k in avg]
+    print("| Counter | " + " | ".join(f"`{k}`" for k in ks) + " |")
+    print("|---|" + "---|" * len(ks))
+    for c in names:
+        print(f"| {c} | " + " | ".join(f"{avg[k].get(c, float('nan')):.4g}" for k in ks) + " |")
+    print()
+    print("| Derived | " + " | ".join(f"`{k}`" for k in ks) + " |")
+    print("|---|" + "---|" * len(ks))
+
+    def row(label, fn):
+        out = []
+        for k in ks:
+            try:
+                out.append(fn(avg[k], k))
+            except (KeyError, ZeroDivisionError):
+                out.append("-")
+        print(f"| {label} | " + " | ".join(out) + " |")
+
+    clocks = lambda a: a["SQ_BUSY_CYCLES"] / 32.0       # kernel clocks per shader engine
+    row("kernel clocks (SQ_BUSY_CYCLES / 32)", lambda a, k: f"{clocks(a):.3g}")
+    row("MFMA busy, share of SIMD clocks", lambda a, k: f"{a['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * clocks(a)):.1%}")
+    row("VALU issue, share of SIMD clocks", lambda a, k: f"{4 * a['SQ_ACTIVE_INST_VALU'] / (1024 * clocks(a)):.1%}")
+    row("LDS issue, share of SIMD clocks", lambda a, k: f"{4 * a['SQ_ACTIVE_INST_LDS'] / (1024 * clocks(a)):.1%}")
+    row("LDS bank-conflict clocks / LDS-active clocks",
+        lambda a, k: f"{a['SQ_LDS_BANK_CONFLICT'] / (4 * a['SQ_ACTIVE_INST_LDS']):.1%}")
+    row("waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES)", lambda a, k: f"{a['SQ_WAIT_ANY'] / a['SQ_WAVE_CYCLES']:.1%}")
+    for c, lab in (("SQ_INSTS_VALU", "VALU"), ("SQ_INSTS_MFMA", "MFMA"), ("SQ_INSTS_LDS", "LDS"),
+                   ("SQ_INSTS_SALU", "SALU")):
+        row(f"{lab} instructions per chunk-head", lambda a, k, c=c: f"{a[c] / chunk_heads[k]:.0f}"
+            if chunk_heads.get(k) else "-")
+
+
 # ----------------------------------------------------------------------------------------------------------
 
 def _sample_segments(w, budget: int):
@@ -288,8 +388,30 @@ def _cpu_baseline(inp, w, budget: int, gate=None):
     return {"value": n * w.B / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} tokens of each of the {w.B} sequence(s) ({desc}), all {w.H} heads, conv + L2 norm "
                       f"+ token-by-token KDA" + (" + gate and norm" if gate is not None else "") +
-                      f" in fp64 numpy; {dt:.1f} s on "
-                      f"{platform.processor() or platform.machine()}, BLAS limited to 1 thread"}
+                      f" in fp64 numpy; {dt:.1f} s on one core of {cpu_model()} ({os.cpu_count()} logical CPUs "
+                      f"reported), BLAS limited to 1 thread"}
+
+
+def _cpu_baseline_pool(pool, ncores, inp, w, budget: int):
+    """The oracle on the same sample as _cpu_baseline, its (batch, head) work split by head over a
+    pool of host processes (forked before the GPU was touched), one core each."""
+    segs, n = _sample_segments(w, budget)
+    H, d = w.H, w.d
+    x = inp["x"][:, :n]
+    cu = [c for c in w.samples if c <= n] if w.samples else None
+    jobs = []
+    for h in range(H):
+        ch = np.concatenate([np.arange(part * H * d + h * d, part * H * d + (h + 1) * d) for part in range(3)])
+        jobs.append((np.ascontiguousarray(x[..., ch]), inp["w_text"][ch], inp["w_vis"][ch], segs,
+                     np.ascontiguousarray(inp["alpha"][:, :n, h:h + 1]), np.ascontiguousarray(inp["beta"][:, :n, h:h + 1]),
+                     None if inp["S0"] is None else inp["S0"][:, h:h + 1], w.dtype == "bf16", cu))
+    t0 = time.perf_counter()
+    pool.map(_oracle_head_job, jobs, chunksize=1)
+    dt = time.perf_counter() - t0
+    return {"value": n * w.B / dt, "unit": "tokens/s", "cores": ncores, "kind": "oracle",
+            "sample": f"the same first {n} tokens of each sequence, {H} heads as {H} jobs on a pool of {ncores} "
+                      f"processes (one core each, BLAS limited to 1 thread); {dt:.1f} s wall including the transfer "
+                      f"of each head's inputs"}
 
 
 def bench_backward(args, w):
@@ -462,10 +584,24 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_counters:
+        import workloads as wl
+        w = wl.WORKLOADS[WORKLOAD_INDEX]
+        nc = (w.T + 63) // 64
+        chunks = w.B * w.H * nc
+        summ = w.B * kda_summarised_tokens(w) // 64 * w.H
+        summarize_counters(args.summarize_counters, {"kda_out_kernel": chunks, "kda_out_gated_kernel": chunks,
+                                                     "kda_sum_kernel": summ})
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); nothing here runs on more than one.",
               file=sys.stderr)
         sys.exit(2)
+    # the oracle's process pool is forked here, before anything touches the GPU
+    pool, ncores = None, pool_cores()
+    if not args.no_cpu_baseline and not args.profile_once and not args.backward and not args.fused:
+        import multiprocessing as mp
+        pool = mp.get_context("fork").Pool(ncores)
     import torch
     import workloads as wl
     import linear_attention_recurrence_mshortconv_amd as chm
@@ -559,18 +695,25 @@ def main():
     torch.cuda.synchronize()
     ms_step_unmarked = a.elapsed_time(b) / args.steps
 
-    work = kernel_work(dom, w)
-    ms_dom = kernels[dom]["ms_per_launch"]
-    achieved = work["bytes"] / (ms_dom * 1e-3) / 1e9 if work["bytes"] else None
-    traffic = stored_traffic(dom) if w.name == wl.WORKLOADS[WORKLOAD_INDEX].name else None
     conv_ms = sum(kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
                   if n.startswith("conv_"))
-    kda_ms = sum(kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"] for n in kernels
-                 if n.startswith("kda_"))
+    kda_names = [n for n in kernels if n.startswith("kda_")]
+    kda_ms = sum(kernels[n]["ms_per_launch"] * kernels[n]["launches_per_step"] for n in kda_names)
     e = 2 if w.dtype == "bf16" else 4
     conv_bytes = 2 * B * T * w.C * e
     kda_bytes = B * T * H * (4 * d * e + e + d * e + (d * e if args.gated else 0)) \
         + nseq * H * d * d * 4 * (2 if S0 is not None else 1)
+    kda_flops = B * T * H * kda_flops_per_token_head(d)
+    # HBM bytes the counters measured for the KDA call: every KDA kernel's stored figure, when all of them
+    # are current for this source
+    traffic = None
+    if w.name == wl.WORKLOADS[WORKLOAD_INDEX].name and not args.gated:
+        parts = [stored_traffic(n) for n in kda_names]
+        traffic = sum(parts) if parts and all(t is not None for t in parts) else None
+    t_roof = (conv_bytes + kda_bytes) / (HBM_PEAK_GBS * 1e9)
+    mem = {"peak_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)), "workspace_bytes": int(need),
+           "note": "torch's peak over the run: inputs, the conv output q|k|v, o, S_final and the KDA workspace (the "
+                   "library allocates nothing itself)"}
     tokens = B * T
     if w.samples:
         layout = (f"{nseq} packed samples (a text prompt of 32..300 tokens, then a 16x16, 32x32 or 64x64 image "
@@ -597,20 +740,43 @@ def main():
                                + (", output gate and per-head RMSNorm of Eq. 15 fused" if args.gated else ""),
                    "tokens_per_step": tokens,
                    "ms_per_step_without_marks": ms_step_unmarked,
+                   "dominant_kernel": dom,
                    "kernels": kernels,
                    "conv_call": {"ms": conv_ms, "GBps_algorithmic": conv_bytes / (conv_ms * 1e-3) / 1e9,
                                  "frac_hbm": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
                    "kda_call": {"ms": kda_ms, "GBps_algorithmic": kda_bytes / (kda_ms * 1e-3) / 1e9,
                                 "frac_hbm": kda_bytes / (kda_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                   "memory": mem,
                    "wall_s_timed": t_wall},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS if achieved else None,
-                     "traffic": traffic, "ms_per_launch": ms_dom,
-                     "algorithmic_bytes_per_launch": work["bytes"], "recipe": work["recipe"]},
+        "roofline": {"bound": "hbm", "kernel": "KDA call (" + " + ".join(kda_names) + ")",
+                     "achieved": kda_bytes / (kda_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kda_bytes / (kda_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic, "ms_per_launch": kda_ms, "algorithmic_bytes_per_launch": kda_bytes,
+                     "recipe": f"q, k, v, alpha ({4 * d * e} B) + beta ({e} B) in and o ({d * e} B) out per token-head"
+                               + (f" + the gate ({d * e} B)" if args.gated else "")
+                               + f", x {B * T} tokens x {H} heads, + the fp32 {d}x{d} S_final"
+                               + (" and S0" if S0 is not None else "") + " per head; ms_per_launch is the sum of the "
+                               "call's kernels' average durations per step",
+                     "mfma": {"achieved": kda_flops / (kda_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": kda_flops / (kda_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                              "flops_per_launch": kda_flops,
+                              "recipe": f"{kda_flops_per_token_head(d):.0f} FLOP per token-head (chunk 64: A, Aqk, W, "
+                                        f"U~, the inverse; U, Q^S, Aqk U, the state update)"},
+                     "pipeline": {"t_roof_us": t_roof * 1e6, "t_measured_us": ms_step * 1e3,
+                                  "frac": t_roof / (ms_step * 1e-3),
+                                  "recipe": "conv (read + write q|k|v) + KDA algorithmic bytes at 8 TB/s, against the "
+                                            "measured step"}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_sample_tokens // max(B, 1), gate_np)
+        if pool is not None and gate_np is None:
+            out["config"]["cpu_baseline_all_cores"] = _cpu_baseline_pool(pool, ncores, inp, w,
+                                                                         args.cpu_sample_tokens // max(B, 1))
+            out["config"]["cpu_baseline_all_cores"]["cpu"] = cpu_model()
+            out["config"]["cpu_baseline_all_cores"]["os_cpu_count"] = os.cpu_count()
+    if pool is not None:
+        pool.close()
     print(json.dumps(out), flush=True)
 
 

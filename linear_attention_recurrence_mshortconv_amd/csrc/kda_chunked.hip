@@ -8,32 +8,32 @@
 // incoming state S and u_r = b_r (v_r - S_{r-1}^T Diag(a_r) k_r):
 //
 //   S_r = Diag(e^{g_r}) (S + sum_{i<=r} (k_i e^{-g_i}) u_i^T)
-//   (I + A) U = diag(b) V - diag(b) (K e^g) S,  A_ri = b_r sum_c k_rc k_ic e^{g_rc - g_ic}  (i < r)
-//   O = (Q e^g) S + Aqk U,                      Aqk_ri = sum_c q_rc k_ic e^{g_rc - g_ic}  (i <= r)
+//   (I + A) U = diag(b) (V - (K e^g) S),      A_ri = b_r sum_c k_rc k_ic e^{g_rc - g_ic}  (i < r)
+//   O = (Q e^g) S + Aqk U,                    Aqk_ri = sum_c q_rc k_ic e^{g_rc - g_ic}  (i <= r)
 //   S_next = Diag(e^{g_n}) S + (K e^{g_n - g})^T U
 //
-// so with T = (I + A)^{-1}, W = T diag(b) K e^g and U~ = T diag(b) V, the chunk
-// step is U = U~ - W S. Decays are running products of alpha (no log / exp).
-// The per-(token, head) L2 normalisation of q and k (page 1, Fig. 2) is folded
-// into the bf16 operands as they are formed (K^, K_ and Q^ carry 1 / |k| and
-// 1 / |q|), so no product needs a separate norm scaling.
+// so with T = (I + A)^{-1} the chunk step is U = T diag(b) (V - (K e^g) S): the UT transform
+// is applied per state column to the residual, and no W = T diag(b) K e^g is formed. Decays are
+// running products of alpha (no log / exp). The per-(token, head) L2 normalisation of q and k
+// (page 1, Fig. 2) is folded into the bf16 operands as they are formed (K^, K_ and Q^ carry
+// 1 / |k| and 1 / |q|), so no product needs a separate norm scaling.
 //
-// Work layout. A block of 4 waves runs one segment of chunks of one (batch,
-// head); wave w owns state columns 32w..32w+31 in registers, and under 80 KB of
-// LDS lets two blocks share a CU. Operands live in LDS once, row-major
-// [token][channel]; products that contract over tokens read them with the
-// gfx950 transposing LDS read (ds_read_b64_tr_b16) instead of keeping
-// transposed copies. Channels are stored in a permuted order inside each group
-// of 32 (cpos) so that one 16-byte read returns the K order of a state fragment
-// packed from the MFMA D layout.
+// Work layout. A block of 8 waves runs one segment of chunks of one (sequence, head) and
+// fills a CU. Waves 0-3 produce: they load a chunk, form its operands and A / Aqk and invert
+// the diagonal blocks of I + A; waves 4-7 consume one chunk behind them, each holding 32 state
+// columns in registers for the whole segment. The two roles pass each other per-chunk
+// operands through two LDS stages, with three block barriers per chunk. Operands live in LDS
+// once, row-major [token][channel]; products that contract over tokens read them with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16) instead of keeping transposed copies.
+// Channels are stored in a permuted order inside each group of 32 (cpos) so that one 16-byte
+// read returns the K order of a state fragment packed from the MFMA D layout.
 //
-// The sequence is cut into segments so that the chip has enough blocks:
-//   summary pass: per summary segment, one block runs S from 0 and one runs the
-//                 transition M from I (a summary segment spans kSub output
-//                 segments; the state at each output-segment boundary is kept);
-//   combine pass: S_start(e + 1) = M_e S_start(base) + S_e, fp32-accurate MFMA;
-//   output pass:  each output segment reruns from S_start(p), writing o.
-// With one output segment only the output pass runs, starting from S0.
+// The sequence is cut into segments so that the chip has one block per CU:
+//   summary pass: per segment but the last, one block runs S from 0 and the transition M
+//                 from I over it;
+//   combine pass: S_start(p + 1) = M_p S_start(p) + S_p, fp32-accurate MFMA;
+//   output pass:  each segment reruns from S_start(p), writing o.
+// With one segment only the output pass runs, starting from S0.
 #include <cstddef>
 #include <algorithm>
 #include <atomic>
@@ -53,9 +53,8 @@ constexpr int D = 128;      // dk = dv
 constexpr int CT = 64;      // tokens per chunk
 constexpr int SBT = 16;     // tokens per decay block
 constexpr int NSB = CT / SBT;
-constexpr int NTHR = 256;   // 4 waves
-constexpr int kTargetBlocks = 512;   // two blocks per CU
-constexpr int kSub = 2;              // output segments per summary segment
+constexpr int kTargetBlocks = 256;   // one block per CU
+constexpr int kSub = 1;              // output segments per summary segment
 constexpr float kL2Eps = 1e-6f;
 constexpr float kFastMin = 1.8e-35f; // ~e^{-80}: the chunk-start factorisation is safe above this
 // alpha is raised to at least e^{-7.5} (bf16 0x3A11) as it is loaded. The blocked
@@ -140,22 +139,6 @@ __device__ __forceinline__ constexpr int cpos(int c) {
 }
 
 // Small arrays first: LDS instruction offsets reach 64 KB from a base register.
-struct Lds {
-  float beta[CT];
-  float rk[CT];           // 1/|k_t| (1 without normalisation)
-  float rq[CT];
-  float egn[D];           // e^{g_n}
-  float pb[NSB][D];       // per block and channel: product of alpha over block tokens 0..7
-  float pf[NSB][D];       //                        ... over block tokens 8..15
-  float adiag[NSB * 272];  // strictly lower A_II in fp32: A_II(i, k) at 272 I + 16 i + k
-  uint16_t at[CT * TRS];  // column-major: at[tr(j, i)] = -A(i, j) below the diagonal blocks, T_II on them
-  uint16_t aqk[CT * TRS]; // column-major: aqk[tr(j, i)] = Aqk(i, j) (rows scaled 1/|q|, columns 1/|k|)
-  uint16_t kr[CT * RKS];  // K^ = k e^{g} (fast) or k e^{g - m_I} (blocked); output staging at the end
-  uint16_t kc[CT * RKS];  // K_ = k e^{-g} (fast) or k e^{m_I - g} (blocked)
-  uint16_t qw[CT * RMS];  // Q^ = q e^{g} / q e^{g - m_I} (output pass); then -W
-};
-static_assert(sizeof(Lds) <= 81920, "two blocks per CU");
-
 // A run of `count` consecutive sequences of `len` tokens each in the packed row dimension
 // (rows start .. start + count * len - 1): a batch of B sequences is one run, and samples
 // packed in one row with lengths of their own make one run per stretch of equal lengths.
@@ -310,258 +293,6 @@ __device__ __forceinline__ uint2 ld_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// Decay factors of the blocked factorisation for channels c..c+3 (from pb, pf):
-//   em(I)     = e^{m_I}         product of alpha from the chunk start to block I's token 7
-//   enm(I)    = e^{g_n - m_I}   ... after block I's token 7 to the chunk end
-//   pair(I,J) = e^{m_I - m_J}   ... after block J's token 7 to block I's token 7
-__device__ __forceinline__ float4 ldf4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 em_of(const Lds& L, int I, int c) {
-  float4 r = ldf4(&L.pb[I][c]);
-#pragma unroll
-  for (int J = 0; J < NSB; ++J)
-    if (J < I) r = mul4(r, mul4(ldf4(&L.pb[J][c]), ldf4(&L.pf[J][c])));
-  return r;
-}
-__device__ __forceinline__ float4 enm_of(const Lds& L, int I, int c) {
-  float4 r = ldf4(&L.pf[I][c]);
-#pragma unroll
-  for (int J = 0; J < NSB; ++J)
-    if (J > I) r = mul4(r, mul4(ldf4(&L.pb[J][c]), ldf4(&L.pf[J][c])));
-  return r;
-}
-__device__ __forceinline__ float4 pair_of(const Lds& L, int I, int J, int c) {
-  float4 r = mul4(ldf4(&L.pf[J][c]), ldf4(&L.pb[I][c]));
-#pragma unroll
-  for (int K = 0; K < NSB; ++K)
-    if (K > J && K < I) r = mul4(r, mul4(ldf4(&L.pb[K][c]), ldf4(&L.pf[K][c])));
-  return r;
-}
-
-// ---- pieces shared by the output and summary kernels ----------------------------------
-// Fragment conventions (16x16x32 MFMA): lane = 16 q4 + l16; a row fragment of block
-// `blk` holds row 16 blk + l16, positions 32 s + 8 q4 .. + 7 for s = 0..3.
-
-template <int STRIDE = RKS>
-__device__ __forceinline__ void tile_frags(const uint16_t* arr, int blk, uint4 (&f)[4], int l16, int q4) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) f[s] = ld128(arr, (SBT * blk + l16) * STRIDE + 32 * s + 8 * q4);
-}
-// column-operand fragments of block J scaled by e^{m_I - m_J} (blocked factorisation)
-__device__ __forceinline__ void pair_frags(const Lds& L, bool fast, int I, int J, const uint4 (&in)[4],
-                                           uint4 (&out)[4], int q4) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    out[s] = fast ? in[s] : scale8(in[s], pair_of(L, I, J, 32 * s + 4 * q4), pair_of(L, I, J, 32 * s + 16 + 4 * q4));
-}
-__device__ __forceinline__ f32x4 mma4(const uint4 (&ra)[4], const uint4 (&cb)[4]) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
-  return acc;
-}
-// A(I, J) = diag(b) (K^ K_^T)(I, J) (the operands carry 1 / |k|): below the diagonal -> at
-// (negated, column-major: a lane's four rows are one 8-byte write), on it (strictly lower
-// part) -> adiag in fp32
-__device__ __forceinline__ void epi_a(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
-  const int j = SBT * J + l16;
-  const float4 b4 = ldf4(&L.beta[SBT * I + 4 * q4]);
-  const float rowf[4] = {b4.x, b4.y, b4.z, b4.w};
-  if (I == J) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? rowf[r] * acc[r] : 0.f;
-  } else {
-    *reinterpret_cast<uint2*>(&L.at[tr(j, SBT * I + 4 * q4)]) = pack4(
-        make_float4(-rowf[0] * acc[0], -rowf[1] * acc[1], -rowf[2] * acc[2], -rowf[3] * acc[3]));
-  }
-}
-// Aqk(I, J) = (Q^ K_^T)(I, J) (the operands carry 1 / |q| and 1 / |k|), lower triangle
-// including the diagonal, column-major
-__device__ __forceinline__ void epi_q(Lds& L, int I, int J, f32x4 acc, int l16, int q4) {
-  const int j = SBT * J + l16;
-  float v[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const bool keep = I > J || 4 * q4 + r >= l16;
-    v[r] = keep ? acc[r] : 0.f;
-  }
-  *reinterpret_cast<uint2*>(&L.aqk[tr(j, SBT * I + 4 * q4)]) = pack4(make_float4(v[0], v[1], v[2], v[3]));
-}
-// T_II = (I + A_II)^{-1}: lane j of a 16-lane group forms column j of T_II by forward
-// substitution, x_i = [i = j] - sum_{k < i} A_II(i, k) x_k, reading the rows of A_II
-// (written by this wave) as broadcasts; the column goes to at as four 8-byte writes.
-__device__ __forceinline__ void invert_diag(Lds& L, int I, int jj, bool write) {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  float x[SBT];
-#pragma unroll
-  for (int i = 0; i < SBT; ++i) {
-    float acc0 = i == jj ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-    for (int k4 = 0; k4 < (i + 3) / 4; ++k4) {
-      const float4 a4 = ldf4(&L.adiag[272 * I + 16 * i + 4 * k4]);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = 4 * k4 + e;
-        if (k < i) {
-          if (e & 1) acc1 -= av[e] * x[k];
-          else acc0 -= av[e] * x[k];
-        }
-      }
-    }
-    x[i] = acc0 + acc1;
-  }
-  if (write) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *reinterpret_cast<uint2*>(&L.at[tr(SBT * I + jj, SBT * I + 4 * m)]) =
-          make_uint2(pack_bf16x2(x[4 * m], x[4 * m + 1]), pack_bf16x2(x[4 * m + 2], x[4 * m + 3]));
-  }
-}
-// the four diagonal blocks at once, lane = 16 I + j
-__device__ __forceinline__ void invert_diag4(Lds& L, int lane) { invert_diag(L, lane >> 4, lane & 15, true); }
-// mma16 A fragments of at (transposed reads): block (I, J), J <= I, at I (I + 1) / 2 + J
-__device__ __forceinline__ void load_t_frags(const Lds& L, uint2 (&af)[10], int l16, int q4) {
-#pragma unroll
-  for (int I = 0; I < 4; ++I)
-#pragma unroll
-    for (int J = 0; J <= I; ++J)
-      af[I * (I + 1) / 2 + J] = ld_tr(&L.at[tr(SBT * J + 4 * q4 + (l16 >> 2), SBT * I + 4 * (l16 & 3))]);
-}
-// X = (I + A)^{-1} Y by block forward substitution, Y and X in the D layout
-__device__ __forceinline__ void block_solve(const uint2 (&af)[10], const f32x4 (&y0)[4], f32x4 (&X)[4]) {
-  uint2 Xb[4];
-#pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    f32x4 y = y0[I];
-#pragma unroll
-    for (int J = 0; J < I; ++J) y = mma16(af[I * (I + 1) / 2 + J], Xb[J], y);
-    X[I] = mma16(af[I * (I + 1) / 2 + I], pack4(y), f32x4{0.f, 0.f, 0.f, 0.f});
-    Xb[I] = pack4(X[I]);
-  }
-}
-// W = (I + A)^{-1} diag(b) K^ (K^ carries 1 / |k|) for channels 16 t .. 16 t + 15, negated and written
-// over the same kr channels (read transposed first; only this wave touches them)
-__device__ __forceinline__ void w_tile(Lds& L, bool fast, int t, const uint2 (&af)[10], int l16, int q4) {
-  const int tpos = 32 * (t >> 1) + 4 * (t & 1);      // cpos(16 t)
-  f32x4 y[4];
-#pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    // lane (l16, q4) receives channel 16 t + l16 of tokens 16 I + 4 q4 + 0..3
-    const float4 kv = unpack4(ld_tr(&L.kr[rk(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
-    float sc = 1.f;
-    if (!fast) sc = pick(em_of(L, I, 16 * t + (l16 & ~3)), l16 & 3);
-    const float4 kr4 = ldf4(&L.beta[SBT * I + 4 * q4]);
-    y[I][0] = kv.x * kr4.x * sc; y[I][1] = kv.y * kr4.y * sc;
-    y[I][2] = kv.z * kr4.z * sc; y[I][3] = kv.w * kr4.w * sc;
-  }
-  f32x4 X[4];
-  block_solve(af, y, X);
-  const int wcol = tpos + 8 * (l16 >> 2) + (l16 & 3);   // cpos(16 t + l16)
-#pragma unroll
-  for (int I = 0; I < 4; ++I)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.kr[rk(SBT * I + 4 * q4 + r, wcol)] = f2bf(-X[I][r]);
-}
-// v of channels col0 .. col0 + 31 (vx: lane = tokens 4 (lane >> 2) + j, channels
-// col0 + 8 (lane & 3) ..) -> the same channels of qw, which only this wave uses now
-__device__ __forceinline__ void stage_v(Lds& L, int col0, const uint4 (&vx)[4], int lane) {
-  const int vp = col0 + 16 * (lane & 1) + 4 * ((lane >> 1) & 1);   // cpos(col0 + 8 (lane & 3))
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 4 * (lane >> 2) + j;
-    *reinterpret_cast<uint2*>(&L.qw[rm(row, vp)]) = make_uint2(vx[j].x, vx[j].y);
-    *reinterpret_cast<uint2*>(&L.qw[rm(row, vp + 8)]) = make_uint2(vx[j].z, vx[j].w);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-}
-// U~ = (I + A)^{-1} diag(b) V for the state columns col0 .. col0 + 31 (staged in qw)
-__device__ __forceinline__ void u_tiles(const Lds& L, int col0, const uint2 (&af)[10], f32x4 (&Ut)[4][2], int l16,
-                                        int q4) {
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int t = col0 / 16 + ct;
-    const int tpos = 32 * (t >> 1) + 4 * (t & 1);      // cpos(16 t)
-    f32x4 y[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const float4 vv = unpack4(ld_tr(&L.qw[rm(SBT * I + 4 * q4 + (l16 >> 2), tpos + 8 * (l16 & 3))]));
-      const float4 br = ldf4(&L.beta[SBT * I + 4 * q4]);
-      y[I][0] = vv.x * br.x; y[I][1] = vv.y * br.y;
-      y[I][2] = vv.z * br.z; y[I][3] = vv.w * br.w;
-    }
-    f32x4 X[4];
-    block_solve(af, y, X);
-#pragma unroll
-    for (int I = 0; I < 4; ++I) Ut[I][ct] = X[I];
-  }
-}
-// state as bf16 B operand: slots 0-3 rows 32 s + 4 q4 + r, 4-7 rows 32 s + 16 + 4 q4 + r
-__device__ __forceinline__ void pack_state(const f32x4 (&S)[8][2], uint4 (&Sf)[4][2]) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) Sf[s][ct] = pack8(S[2 * s][ct], S[2 * s + 1][ct]);
-}
-// U += (-W) S (-W in kr)
-__device__ __forceinline__ void minus_ws(const Lds& L, const uint4 (&Sf)[4][2], f32x4 (&U)[4][2], int l16, int q4) {
-#pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    uint4 wf[4];
-    tile_frags(L.kr, I, wf, l16, q4);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) U[I][ct] = mma32(wf[s], Sf[s][ct], U[I][ct]);
-  }
-}
-// S <- Diag(e^{g_n}) S + K~^T U, K~ = (K / |k|) e^{g_n - g} read transposed from kc
-__device__ __forceinline__ void update_state(const Lds& L, bool fast, f32x4 (&S)[8][2], const f32x4 (&U)[4][2],
-                                             int l16, int q4) {
-  uint4 Upf[2][2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) Upf[s][ct] = pack8(U[2 * s][ct], U[2 * s + 1][ct]);
-  // A operand K~^T: lane (l16, q4) = channel 16 rt + l16, tokens 32 s + 4 q4 + 0..3 and
-  // 32 s + 16 + 4 q4 + 0..3
-  const int kbase = rk(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
-#pragma unroll
-  for (int rt = 0; rt < 8; ++rt) {
-    const int cp = 32 * (rt >> 1) + 4 * (rt & 1);   // cpos(16 rt)
-    uint4 kt[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      kt[s] = cat(ld_tr(&L.kc[kbase + rk(32 * s, cp)]), ld_tr(&L.kc[kbase + rk(32 * s + 16, cp)]));
-    const float4 eg = ldf4(&L.egn[16 * rt + 4 * q4]);
-    if (fast) {   // K~ = K_ e^{g_n}: the factor is a row scaling of the product
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f32x4 acc = S[rt][ct];
-        acc = mma32(kt[0], Upf[0][ct], acc);
-        acc = mma32(kt[1], Upf[1][ct], acc);
-        acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
-        S[rt][ct] = acc;
-      }
-    } else {      // blocked: K~ = K_ e^{g_n - m_I} for the tokens of block I
-      const int cl = 16 * rt + (l16 & ~3), u = l16 & 3;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const float f0 = pick(enm_of(L, 2 * s, cl), u), f1 = pick(enm_of(L, 2 * s + 1, cl), u);
-        kt[s] = scale8(kt[s], make_float4(f0, f0, f0, f0), make_float4(f1, f1, f1, f1));
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f32x4 acc = S[rt][ct];
-        acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
-        acc = mma32(kt[0], Upf[0][ct], acc);
-        acc = mma32(kt[1], Upf[1][ct], acc);
-        S[rt][ct] = acc;
-      }
-    }
-  }
-}
 // the 32 state columns of this wave -> m ([D][D] fp32); svo = lane part of the offset
 __device__ __forceinline__ void store_state(const f32x4 (&S)[8][2], float* m, int svo) {
   float* dst = m + svo;
@@ -601,8 +332,6 @@ __device__ __forceinline__ int mfrag_off(int rt, int s, int lane) { return ((rt 
 // read, so that every global store is a 16-byte piece.
 constexpr int kMsP = 40;                            // scratch row pitch (elements)
 constexpr int kMsWave = 2 * 32 * kMsP;              // scratch elements per wave
-static_assert(offsetof(Lds, kc) == offsetof(Lds, kr) + sizeof(Lds::kr) && 4 * kMsWave <= 2 * CT * RKS,
-              "the four M waves' scratch lies in kr and kc");
 __device__ __forceinline__ void store_mfrag(const f32x4 (&S)[8][2], uint4* m, int cb, int lane, uint16_t* scr) {
   uint16_t* hiB = scr;
   uint16_t* loB = scr + 32 * kMsP;
@@ -628,61 +357,671 @@ __device__ __forceinline__ void store_mfrag(const f32x4 (&S)[8][2], uint4* m, in
   }
 }
 
-// v of the state columns col0 .. col0 + 31 of the chunk: lane = tokens 4 (lane >> 2) + j,
-// channels col0 + 8 (lane & 3) .. + 7; tokens past the end read as zero
-__device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t row, int64_t h, int n, int col0, int lane,
-                                       uint4 (&vx)[4]) {
-  const int st2 = (int)a.stride * 2;
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + row * a.stride + h * D), 0, n * st2, kRsrcW3);
-  const int vo = (4 * (lane >> 2)) * st2 + 2 * (col0 + 8 * (lane & 3));
+// ---- LDS of the pipelined passes ------------------------------------------------------
+// A stage holds what the producers form for one chunk and the consumers use one tick later;
+// two stages alternate by chunk parity. Arrays are flat with padded rows (the padding folds
+// into instruction offsets):
+//   kr, kc: [CT][D] row-major, row stride D + 16 elements (288 bytes)
+//   qw:     [CT][D] row-major, row stride D + 8 elements (272 bytes)
+//   at, aqk: [CT][CT] column-major, stride CT + 4 elements
+struct PcStage {
+  uint16_t kr[CT * RKS];  // K^ = k e^{g} / |k| (fast) or k e^{g - m_I} / |k| (blocked)
+  uint16_t kc[CT * RKS];  // K_ = k e^{-g} / |k| (fast) or k e^{m_I - g} / |k| (blocked)
+  float beta[CT];
+  float egn[D];           // e^{g_n}: decay of each key channel over the whole chunk
+  float pb[NSB][D];       // per block and channel: product of alpha over block tokens 0..7
+  float pf[NSB][D];       //                        ... over block tokens 8..15
+  int fast;               // the chunk-start factorisation holds (block-wide vote)
+  int pad[3];
+};
+struct PcLdsOut {         // output pass
+  PcStage st[2];
+  uint16_t qw[2][CT * RMS];   // Q^ = q e^{g} / |q| (fast) or q e^{g - m_I} / |q| (blocked), per stage;
+                              // once a stage's Q^ is used, its qw holds v of the next chunk
+  uint16_t at[CT * TRS];      // at[tr(j, i)] = -A(i, j) below the diagonal blocks, T_II on them
+  uint16_t aqk[CT * TRS];     // aqk[tr(j, i)] = Aqk(i, j), lower triangle with the diagonal
+  float adiag[NSB * 272];     // strictly lower A_II in fp32: A_II(i, k) at 272 I + 16 i + k
+  float rk[CT];               // 1 / |k_t| (1 without normalisation)
+  float rq[CT];
+  float rowss[CT * 4];        // gated: per token, each consumer wave's part of the sum of squares
+};
+struct PcLdsSum {         // summary pass
+  PcStage st[2];
+  uint16_t vs[CT * RMS];      // v of the consumers' next chunk, row-major (stride RMS)
+  uint16_t at[CT * TRS];
+  float adiag[NSB * 272];
+  float rk[CT];
+  float rq[CT];
+};
+static_assert(sizeof(PcLdsOut) <= 160 * 1024 && sizeof(PcLdsSum) <= 160 * 1024, "one block per CU");
+constexpr int kPcThreads = 512;   // 4 producer and 4 consumer waves
+static_assert(4 * kMsWave * sizeof(uint16_t) <= sizeof(PcLdsSum), "the four M waves' scratch lies in the summary LDS");
+
+// Decay factors of the blocked factorisation for channels c..c+3 (from a stage's pb, pf):
+//   em(I)     = e^{m_I}         product of alpha from the chunk start to block I's token 7
+//   enm(I)    = e^{g_n - m_I}   ... after block I's token 7 to the chunk end
+//   pair(I,J) = e^{m_I - m_J}   ... after block J's token 7 to block I's token 7
+__device__ __forceinline__ float4 ldf4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 em_of(const PcStage& st, int I, int c) {
+  float4 r = ldf4(&st.pb[I][c]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, j * st2, 0);
-    vx[j] = make_uint4(v4[0], v4[1], v4[2], v4[3]);
+  for (int J = 0; J < NSB; ++J)
+    if (J < I) r = mul4(r, mul4(ldf4(&st.pb[J][c]), ldf4(&st.pf[J][c])));
+  return r;
+}
+__device__ __forceinline__ float4 enm_of(const PcStage& st, int I, int c) {
+  float4 r = ldf4(&st.pf[I][c]);
+#pragma unroll
+  for (int J = 0; J < NSB; ++J)
+    if (J > I) r = mul4(r, mul4(ldf4(&st.pb[J][c]), ldf4(&st.pf[J][c])));
+  return r;
+}
+__device__ __forceinline__ float4 pair_of(const PcStage& st, int I, int J, int c) {
+  float4 r = mul4(ldf4(&st.pf[J][c]), ldf4(&st.pb[I][c]));
+#pragma unroll
+  for (int K = 0; K < NSB; ++K)
+    if (K > J && K < I) r = mul4(r, mul4(ldf4(&st.pb[K][c]), ldf4(&st.pf[K][c])));
+  return r;
+}
+
+// ---- MFMA fragment pieces ------------------------------------------------------------
+// Fragment conventions (16x16x32 MFMA): lane = 16 q4 + l16; a row fragment of block `blk`
+// holds row 16 blk + l16, positions 32 s + 8 q4 .. + 7 for s = 0..3 (channels 32 s + 4 q4 ..
+// + 3 and 32 s + 16 + 4 q4 .. + 3 in the cpos order). The A and B operand layouts of this
+// instruction are mirror images, so one fragment serves a matrix as A or its transpose as B.
+template <int STRIDE = RKS>
+__device__ __forceinline__ void tile_frags(const uint16_t* arr, int blk, uint4 (&f)[4], int l16, int q4) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f[s] = ld128(arr, (SBT * blk + l16) * STRIDE + 32 * s + 8 * q4);
+}
+// column-operand fragments of block J scaled by e^{m_I - m_J} (blocked factorisation)
+__device__ __forceinline__ void pair_frags(const PcStage& st, bool fast, int I, int J, const uint4 (&in)[4],
+                                           uint4 (&out)[4], int q4) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    out[s] = fast ? in[s] : scale8(in[s], pair_of(st, I, J, 32 * s + 4 * q4), pair_of(st, I, J, 32 * s + 16 + 4 * q4));
+}
+__device__ __forceinline__ f32x4 mma4(const uint4 (&ra)[4], const uint4 (&cb)[4]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
+  return acc;
+}
+// A(I, J) = diag(b) (K^ K_^T)(I, J) (the operands carry 1 / |k|): below the diagonal -> at
+// (negated, column-major: a lane's four rows are one 8-byte write), on it (strictly lower
+// part) -> adiag in fp32
+__device__ __forceinline__ void epi_a(uint16_t* at, float* adiag, const float* beta, int I, int J, f32x4 acc, int l16,
+                                      int q4) {
+  const int j = SBT * J + l16;
+  const float4 b4 = ldf4(&beta[SBT * I + 4 * q4]);
+  const float rowf[4] = {b4.x, b4.y, b4.z, b4.w};
+  if (I == J) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? rowf[r] * acc[r] : 0.f;
+  } else {
+    *reinterpret_cast<uint2*>(&at[tr(j, SBT * I + 4 * q4)]) =
+        pack4(make_float4(-rowf[0] * acc[0], -rowf[1] * acc[1], -rowf[2] * acc[2], -rowf[3] * acc[3]));
+  }
+}
+// Aqk(I, J) = (Q^ K_^T)(I, J) (the operands carry 1 / |q| and 1 / |k|), lower triangle
+// including the diagonal, column-major
+__device__ __forceinline__ void epi_q(uint16_t* aqk, int I, int J, f32x4 acc, int l16, int q4) {
+  const int j = SBT * J + l16;
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = (I > J || 4 * q4 + r >= l16) ? acc[r] : 0.f;
+  *reinterpret_cast<uint2*>(&aqk[tr(j, SBT * I + 4 * q4)]) = pack4(make_float4(v[0], v[1], v[2], v[3]));
+}
+// T_II = (I + A_II)^{-1}: lane j of a 16-lane group forms column j of T_II by forward
+// substitution, x_i = [i = j] - sum_{k < i} A_II(i, k) x_k, reading the rows of A_II
+// (written by this wave) as broadcasts; the column goes to at as four 8-byte writes.
+__device__ __forceinline__ void invert_diag(const float* adiag, uint16_t* at, int I, int jj, bool write) {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  float x[SBT];
+#pragma unroll
+  for (int i = 0; i < SBT; ++i) {
+    float acc0 = i == jj ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int k4 = 0; k4 < (i + 3) / 4; ++k4) {
+      const float4 a4 = ldf4(&adiag[272 * I + 16 * i + 4 * k4]);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * k4 + e;
+        if (k < i) {
+          if (e & 1) acc1 -= av[e] * x[k];
+          else acc0 -= av[e] * x[k];
+        }
+      }
+    }
+    x[i] = acc0 + acc1;
+  }
+  if (write) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<uint2*>(&at[tr(SBT * I + jj, SBT * I + 4 * m)]) =
+          make_uint2(pack_bf16x2(x[4 * m], x[4 * m + 1]), pack_bf16x2(x[4 * m + 2], x[4 * m + 3]));
+  }
+}
+// mma16 A fragments of at (transposed reads): block (I, J), J <= I, at I (I + 1) / 2 + J
+__device__ __forceinline__ void load_t_frags(const uint16_t* at, uint2 (&af)[10], int l16, int q4) {
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J)
+      af[I * (I + 1) / 2 + J] = ld_tr(&at[tr(SBT * J + 4 * q4 + (l16 >> 2), SBT * I + 4 * (l16 & 3))]);
+}
+// X = (I + A)^{-1} Y by block forward substitution, Y and X in the D layout
+__device__ __forceinline__ void block_solve(const uint2 (&af)[10], const f32x4 (&y0)[4], f32x4 (&X)[4]) {
+  uint2 Xb[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    f32x4 y = y0[I];
+#pragma unroll
+    for (int J = 0; J < I; ++J) y = mma16(af[I * (I + 1) / 2 + J], Xb[J], y);
+    X[I] = mma16(af[I * (I + 1) / 2 + I], pack4(y), f32x4{0.f, 0.f, 0.f, 0.f});
+    Xb[I] = pack4(X[I]);
   }
 }
 
-// Output pass over the chunks of one segment of one (batch, head): 4 waves, wave w
-// owns state columns 32 w .. 32 w + 31; writes o, and S_final from the last segment.
+// ---- producer waves ------------------------------------------------------------------
+// Producer wave w handles decay block w (tokens 16 w .. 16 w + 15): half-wave hf = tokens
+// 8 hf .. 8 hf + 7 of the block, lane cg = 32-lane index = channels 4 cg .. 4 cg + 3.
+struct PLoad {
+  uint2 k[8], q[8], a[8];   // tokens tk0 .. tk0 + 7, channels c0 .. c0 + 3
+  uint16_t bt;              // beta of token `lane` (wave 0)
+};
+// Buffer loads of chunk c: block-uniform base and bounds (the chunk's first n tokens); reads
+// past the bound return zero, which is k = q = beta = 0 for tokens past the end (alpha is set
+// to 1 for them when it is used).
+template <bool HASQ>
+__device__ __forceinline__ void p_issue(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c, int wave,
+                                        int lane, PLoad& R) {
+  const int hf = lane >> 5, c0 = 4 * (lane & 31);
+  const int64_t t0 = c * CT;
+  const int n = (int)min<int64_t>(CT, sv.T - t0);
+  const int64_t row0 = sv.row0 + t0;
+  const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
+  const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
+  const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
+  const int vk = (8 * hf) * st2 + 2 * c0, va = (8 * hf) * sa2 + 2 * c0;
+  const int tb = SBT * wave;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    R.k[i] = ld_buf64(rk_, vk, (tb + i) * st2);
+    R.a[i] = ld_buf64(ra_, va, (tb + i) * sa2);
+  }
+  if (HASQ) {
+    const auto rq_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) R.q[i] = ld_buf64(rq_, vk, (tb + i) * st2);
+  }
+  if (wave == 0) {
+    const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
+    R.bt = __builtin_amdgcn_raw_buffer_load_b16(rb_, lane * (int)a.H * 2, 0, 0);
+  }
+}
+
+// Phase 1: beta, per-token norms, block decay products of chunk c (n valid tokens) into stage st.
+template <bool HASQ>
+__device__ __forceinline__ void p_phase1(const ChunkArgs& a, PcStage& st, float* rkn, float* rqn, const PLoad& R, int n,
+                                         int wave, int lane, float4 (&al)[8]) {
+  const int hf = lane >> 5, cg = lane & 31, c0 = 4 * cg;
+  const int tk0 = SBT * wave + 8 * hf;
+  if (wave == 0) st.beta[lane] = bf2f(R.bt);
+  if (a.l2norm) {
+    float ss[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ss[i] = dot4(R.k[i]);
+      ss[i + 8] = HASQ ? dot4(R.q[i]) : 0.f;
+    }
+    const float tot = half_sum16(ss, lane);
+    if ((lane & 1) == 0) {
+      const int vv = (lane >> 1) & 15;          // 0..7: k of token vv; 8..15: q of token vv - 8
+      const float rn = __builtin_amdgcn_rsqf(tot + kL2Eps);
+      if (vv < 8) rkn[tk0 + vv] = rn;
+      else if (HASQ) rqn[tk0 + vv - 8] = rn;
+    }
+  } else if (cg < 8) {
+    rkn[tk0 + cg] = 1.f;
+    rqn[tk0 + cg] = 1.f;
+  }
+  const uint32_t one2 = 0x3F803F80u;   // alpha = 1 past the end
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool in = tk0 + i < n;
+    al[i] = unpack4(make_uint2(in ? clamp_alpha2(R.a[i].x) : one2, in ? clamp_alpha2(R.a[i].y) : one2));
+  }
+  float4 hp = al[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) hp = mul4(hp, al[i]);
+  *reinterpret_cast<float4*>(hf ? &st.pf[wave][c0] : &st.pb[wave][c0]) = hp;
+}
+
+// Phase 2: decay factors and the MFMA operands K^, K_ (and Q^) of the chunk into stage st.
+// Returns the factorisation vote (the same in every wave: each holds all 128 channels).
+template <bool HASQ>
+__device__ __forceinline__ bool p_phase2(PcStage& st, uint16_t* qw, const float* rkn, const float* rqn, const PLoad& R,
+                                         const float4 (&al)[8], int wave, int lane) {
+  const int hf = lane >> 5, cg = lane & 31, c0 = 4 * cg, p0 = cpos(c0);
+  const int tk0 = SBT * wave + 8 * hf;
+  // per channel: before = decay over the blocks before this one, after = over the blocks after
+  // it; the lane's half adds its block's other half on one side
+  float4 full[NSB], h0w = make_float4(1.f, 1.f, 1.f, 1.f), h1w = h0w;
+#pragma unroll
+  for (int J = 0; J < NSB; ++J) {
+    const float4 h0 = ldf4(&st.pb[J][c0]), h1 = ldf4(&st.pf[J][c0]);
+    full[J] = mul4(h0, h1);
+    if (J == wave) { h0w = h0; h1w = h1; }
+  }
+  float4 egn4 = full[0], before = make_float4(1.f, 1.f, 1.f, 1.f), after = before;
+#pragma unroll
+  for (int J = 1; J < NSB; ++J) egn4 = mul4(egn4, full[J]);
+#pragma unroll
+  for (int J = 0; J < NSB; ++J) {
+    if (J < wave) before = mul4(before, full[J]);
+    if (J > wave) after = mul4(after, full[J]);
+  }
+  const bool fast = __all(fminf(fminf(egn4.x, egn4.y), fminf(egn4.z, egn4.w)) >= kFastMin) != 0;
+  if (wave == 0 && hf == 0) *reinterpret_cast<float4*>(&st.egn[c0]) = egn4;
+  if (wave == 0 && lane == 0) st.fast = fast ? 1 : 0;
+  // 1 / |k| and 1 / |q| of the lane's tokens go into the operands, so that no product
+  // downstream needs a norm scaling
+  const float4 rk0 = ldf4(&rkn[tk0]), rk1 = ldf4(&rkn[tk0 + 4]);
+  float rkt[8] = {rk0.x, rk0.y, rk0.z, rk0.w, rk1.x, rk1.y, rk1.z, rk1.w};
+  float rqt[8];
+  if (HASQ) {
+    const float4 rq0 = ldf4(&rqn[tk0]), rq1 = ldf4(&rqn[tk0 + 4]);
+    rqt[0] = rq0.x; rqt[1] = rq0.y; rqt[2] = rq0.z; rqt[3] = rq0.w;
+    rqt[4] = rq1.x; rqt[5] = rq1.y; rqt[6] = rq1.z; rqt[7] = rq1.w;
+  }
+  auto put = [&](int i, float4 fr, float4 fc) {
+    const int tk = tk0 + i;
+    const float4 ks = mul4(unpack4(R.k[i]), make_float4(rkt[i], rkt[i], rkt[i], rkt[i]));
+    *reinterpret_cast<uint2*>(&st.kr[rk(tk, p0)]) = pack4(mul4(ks, fr));
+    *reinterpret_cast<uint2*>(&st.kc[rk(tk, p0)]) = pack4(mul4(ks, fc));
+    if (HASQ) {
+      const float4 qs = mul4(unpack4(R.q[i]), make_float4(rqt[i], rqt[i], rqt[i], rqt[i]));
+      *reinterpret_cast<uint2*>(&qw[rm(tk, p0)]) = pack4(mul4(qs, fr));
+    }
+  };
+  if (fast) {
+    // e^{g_t} as a prefix product from the chunk start and e^{g_n - g_t} / e^{g_n} as a suffix
+    // product towards the chunk end: no per-element reciprocal
+    float4 fw = hf ? mul4(before, h0w) : before;
+    float4 bw = mul4(hf ? after : mul4(after, h1w), rcp4(egn4));
+    float4 fr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      fw = mul4(fw, al[i]);
+      fr[i] = fw;
+    }
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      put(i, fr[i], bw);
+      if (i > 0) bw = mul4(bw, al[i]);
+    }
+  } else {
+    // blocked: reference m_I = g at the block's token 7; half 1 runs forward (e^{g - m_I} =
+    // product over tokens 8..t), half 0 backward (e^{m_I - g} = product over tokens t+1..7)
+    if (hf == 1) {
+      float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        run = mul4(run, al[i]);
+        put(i, run, rcp4(run));
+      }
+    } else {
+      float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        put(i, rcp4(run), run);
+        run = mul4(run, al[i]);
+      }
+    }
+  }
+  return fast;
+}
+
+// Phase 3 of the output pass: the A and Aqk blocks of the chunk and the diagonal inverses.
+//   wave 0: the four diagonal A blocks and their inverses (the chunk's longest chain);
+//   wave 1: Aqk00 A10 Aqk10 A20 Aqk20 A30;  wave 2: Aqk11 A21 Aqk21 A31 Aqk31;
+//   wave 3: Aqk22 A32 Aqk32 Aqk33 Aqk30
+__device__ __forceinline__ void p_phase3_out(const PcStage& st, const uint16_t* qw, uint16_t* at, uint16_t* aqk,
+                                             float* adiag, bool fast, int wave, int lane) {
+  const int l16 = lane & 15, q4 = lane >> 4;
+  uint4 cA[4], cB[4], rA[4], sc[4];
+  if (wave == 0) {
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int I = 0; I < NSB; ++I) {
+      tile_frags(st.kc, I, cA, l16, q4);
+      tile_frags(st.kr, I, rA, l16, q4);
+      epi_a(at, adiag, st.beta, I, I, mma4(rA, cA), l16, q4);
+    }
+    invert_diag(adiag, at, lane >> 4, lane & 15, true);
+    __builtin_amdgcn_s_setprio(0);
+  } else if (wave == 1) {
+    tile_frags(st.kc, 0, cA, l16, q4);
+    tile_frags<RMS>(qw, 0, rA, l16, q4);
+    epi_q(aqk, 0, 0, mma4(rA, cA), l16, q4);
+#pragma unroll
+    for (int I = 1; I < NSB; ++I) {
+      pair_frags(st, fast, I, 0, cA, sc, q4);
+      tile_frags(st.kr, I, rA, l16, q4);
+      epi_a(at, adiag, st.beta, I, 0, mma4(rA, sc), l16, q4);
+      if (I < 3) {
+        tile_frags<RMS>(qw, I, rA, l16, q4);
+        epi_q(aqk, I, 0, mma4(rA, sc), l16, q4);
+      }
+    }
+  } else if (wave == 2) {
+    tile_frags(st.kc, 1, cA, l16, q4);
+    tile_frags<RMS>(qw, 1, rA, l16, q4);
+    epi_q(aqk, 1, 1, mma4(rA, cA), l16, q4);
+#pragma unroll
+    for (int I = 2; I < NSB; ++I) {
+      pair_frags(st, fast, I, 1, cA, sc, q4);
+      tile_frags(st.kr, I, rA, l16, q4);
+      epi_a(at, adiag, st.beta, I, 1, mma4(rA, sc), l16, q4);
+      tile_frags<RMS>(qw, I, rA, l16, q4);
+      epi_q(aqk, I, 1, mma4(rA, sc), l16, q4);
+    }
+  } else {
+    tile_frags(st.kc, 2, cA, l16, q4);
+    tile_frags<RMS>(qw, 2, rA, l16, q4);
+    epi_q(aqk, 2, 2, mma4(rA, cA), l16, q4);
+    pair_frags(st, fast, 3, 2, cA, sc, q4);
+    tile_frags(st.kr, 3, rA, l16, q4);
+    epi_a(at, adiag, st.beta, 3, 2, mma4(rA, sc), l16, q4);
+    tile_frags<RMS>(qw, 3, rA, l16, q4);
+    epi_q(aqk, 3, 2, mma4(rA, sc), l16, q4);
+    tile_frags(st.kc, 3, cB, l16, q4);
+    epi_q(aqk, 3, 3, mma4(rA, cB), l16, q4);
+    tile_frags(st.kc, 0, cB, l16, q4);
+    pair_frags(st, fast, 3, 0, cB, sc, q4);
+    epi_q(aqk, 3, 0, mma4(rA, sc), l16, q4);
+  }
+}
+
+// Phase 3 of the summary pass: the A blocks; wave w forms diagonal block w and its inverse (all
+// four lane groups compute it, the first writes it) and the blocks below the diagonal
+// (wave 0: A10 A32, wave 1: A20, wave 2: A30 A21, wave 3: A31).
+__device__ __forceinline__ void p_phase3_sum(const PcStage& st, uint16_t* at, float* adiag, bool fast, int wave,
+                                             int lane) {
+  const int l16 = lane & 15, q4 = lane >> 4;
+  uint4 cA[4], rA[4], sc[4];
+  tile_frags(st.kc, wave, cA, l16, q4);
+  tile_frags(st.kr, wave, rA, l16, q4);
+  __builtin_amdgcn_s_setprio(3);
+  epi_a(at, adiag, st.beta, wave, wave, mma4(rA, cA), l16, q4);
+  invert_diag(adiag, at, wave, l16, q4 == 0);
+  __builtin_amdgcn_s_setprio(0);
+  auto below = [&](int I, int J) {
+    tile_frags(st.kc, J, cA, l16, q4);
+    pair_frags(st, fast, I, J, cA, sc, q4);
+    tile_frags(st.kr, I, rA, l16, q4);
+    epi_a(at, adiag, st.beta, I, J, mma4(rA, sc), l16, q4);
+  };
+  if (wave == 0) {
+    below(1, 0);
+    below(3, 2);
+  } else if (wave == 1) {
+    below(2, 0);
+  } else if (wave == 2) {
+    below(3, 0);
+    below(2, 1);
+  } else {
+    below(3, 1);
+  }
+}
+
+// ---- consumer waves ------------------------------------------------------------------
+// Consumer wave j owns state columns 32 j .. 32 j + 31 in registers for the whole segment:
+// X[rt][ct] holds rows 16 rt + 4 q4 + r, columns 32 j + 16 ct + l16 (the MFMA D layout).
+
+// v of chunk c, rows 16 cw .. 16 cw + 15, loaded whole: half-wave hf takes row 16 cw + 2 i + hf,
+// lane channels 4 (lane & 31) .. + 3 (one 256-byte token row per half-wave and load; tokens past
+// the end read 0). The consumers' MFMA layout would touch 16 token rows per load; instead the
+// rows go through LDS (c_stage_v) and come back in that layout with the transposing read.
+__device__ __forceinline__ void c_issue_v(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c, int cw,
+                                          int lane, uint2 (&vr)[8]) {
+  const int64_t t0 = c * CT;
+  const int n = (int)min<int64_t>(CT, sv.T - t0);
+  const int st2 = (int)a.stride * 2;
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (sv.row0 + t0) * a.stride + h * D), 0, n * st2,
+                                                    kRsrcW3);
+  const int vo = (SBT * cw + (lane >> 5)) * st2 + 8 * (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vr[i] = ld_buf64(rv, vo, 2 * i * st2);
+}
+// the rows of c_issue_v -> vbuf ([CT][D], row stride RMS, natural channel order)
+__device__ __forceinline__ void c_stage_v(uint16_t* vbuf, const uint2 (&vr)[8], int cw, int lane) {
+  const int r0 = SBT * cw + (lane >> 5), c0 = 4 * (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(&vbuf[rm(r0 + 2 * i, c0)]) = vr[i];
+}
+
+// U = (I + A)^{-1} diag(beta) (V - K^ X) for the wave's 32 columns (V = 0 without vbuf: the
+// transition's columns). V comes from its LDS staging in the D layout through the transposing
+// read; K^ X accumulates on top with -X as the B operand, one k slot of -X packed at a time.
+__device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, const uint16_t* vbuf, bool fast,
+                                        const f32x4 (&X)[8][2], int col0, f32x4 (&U)[4][2], int l16, int q4) {
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if (vbuf != nullptr) {
+        // lane (l16, q4) receives rows 16 I + 4 q4 + 0..3 of column col0 + 16 ct + l16
+        const float4 vv = unpack4(ld_tr(&vbuf[rm(SBT * I + 4 * q4 + (l16 >> 2), col0 + 16 * ct + 4 * (l16 & 3))]));
+        acc[I][ct] = f32x4{vv.x, vv.y, vv.z, vv.w};
+      } else {
+        acc[I][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 xs[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) xs[ct] = pack8(-X[2 * s][ct], -X[2 * s + 1][ct]);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      uint4 kf = ld128(st.kr, (SBT * I + l16) * RKS + 32 * s + 8 * q4);
+      if (!fast) kf = scale8(kf, em_of(st, I, 32 * s + 4 * q4), em_of(st, I, 32 * s + 16 + 4 * q4));
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) acc[I][ct] = mma32(kf, xs[ct], acc[I][ct]);
+    }
+  }
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    const float4 b4 = ldf4(&st.beta[SBT * I + 4 * q4]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      acc[I][ct][0] *= b4.x; acc[I][ct][1] *= b4.y;
+      acc[I][ct][2] *= b4.z; acc[I][ct][3] *= b4.w;
+    }
+  }
+  uint2 af[10];
+  load_t_frags(at, af, l16, q4);
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const f32x4 y0[4] = {acc[0][ct], acc[1][ct], acc[2][ct], acc[3][ct]};
+    f32x4 Xo[4];
+    block_solve(af, y0, Xo);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) U[I][ct] = Xo[I];
+  }
+}
+
+// X <- Diag(e^{g_n}) X + K~^T U, K~ = (K / |k|) e^{g_n - g} read transposed from kc
+__device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X)[8][2], const f32x4 (&U)[4][2],
+                                         int l16, int q4) {
+  uint4 Upf[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) Upf[s][ct] = pack8(U[2 * s][ct], U[2 * s + 1][ct]);
+  // A operand K~^T: lane (l16, q4) = channel 16 rt + l16, tokens 32 s + 4 q4 + 0..3 and
+  // 32 s + 16 + 4 q4 + 0..3
+  const int kbase = rk(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt) {
+    const int cp = 32 * (rt >> 1) + 4 * (rt & 1);   // cpos(16 rt)
+    uint4 kt[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      kt[s] = cat(ld_tr(&st.kc[kbase + rk(32 * s, cp)]), ld_tr(&st.kc[kbase + rk(32 * s + 16, cp)]));
+    const float4 eg = ldf4(&st.egn[16 * rt + 4 * q4]);
+    if (fast) {   // K~ = K_ e^{g_n}: the factor is a row scaling of the product
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f32x4 acc = X[rt][ct];
+        acc = mma32(kt[0], Upf[0][ct], acc);
+        acc = mma32(kt[1], Upf[1][ct], acc);
+        acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
+        X[rt][ct] = acc;
+      }
+    } else {      // blocked: K~ = K_ e^{g_n - m_I} for the tokens of block I
+      const int cl = 16 * rt + (l16 & ~3), u = l16 & 3;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const float f0 = pick(enm_of(st, 2 * s, cl), u), f1 = pick(enm_of(st, 2 * s + 1, cl), u);
+        kt[s] = scale8(kt[s], make_float4(f0, f0, f0, f0), make_float4(f1, f1, f1, f1));
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f32x4 acc = X[rt][ct];
+        acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
+        acc = mma32(kt[0], Upf[0][ct], acc);
+        acc = mma32(kt[1], Upf[1][ct], acc);
+        X[rt][ct] = acc;
+      }
+    }
+  }
+}
+
+// The output of the chunk, transposed: O^T = S^T Q^T + U^T Aqk^T. With the mirror-image
+// operand layouts the packed state serves as the A operand of S^T and the Q^ row fragments
+// as the B operand of Q^T, and likewise U and Aqk; the result's D layout gives lane
+// (l16, q4) of OT[ct][I] token 16 I + l16 at channels col0 + 16 ct + 4 q4 .. + 3, which go
+// out as one 8-byte store.
+__device__ __forceinline__ void c_output(const PcStage& st, const uint16_t* qw, const uint16_t* aqk, bool fast,
+                                         const f32x4 (&S)[8][2], const f32x4 (&U)[4][2], f32x4 (&OT)[2][4], int l16,
+                                         int q4) {
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) OT[ct][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 xs[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) xs[ct] = pack8(S[2 * s][ct], S[2 * s + 1][ct]);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      uint4 qf = ld128(qw, (SBT * I + l16) * RMS + 32 * s + 8 * q4);
+      if (!fast) qf = scale8(qf, em_of(st, I, 32 * s + 4 * q4), em_of(st, I, 32 * s + 16 + 4 * q4));
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) OT[ct][I] = mma32(xs[ct], qf, OT[ct][I]);
+    }
+  }
+  uint4 Uf[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) Uf[s][ct] = pack8(U[2 * s][ct], U[2 * s + 1][ct]);
+  // Aqk rows 16 I + l16 at tokens 32 s + 4 q4 + 0..3 and 32 s + 16 + 4 q4 + 0..3 (blocks above
+  // the diagonal read as zeros)
+  auto qfrag = [&](int I, int s) {
+    const int base = tr(32 * s + 4 * q4 + (l16 >> 2), SBT * I + 4 * (l16 & 3));
+    return cat(ld_tr(&aqk[base]), ld_tr(&aqk[base + tr(16, 0)]));
+  };
+  const uint4 qa0 = qfrag(0, 0), qa1 = qfrag(1, 0), qa2 = qfrag(2, 0), qa3 = qfrag(2, 1), qa4 = qfrag(3, 0),
+              qa5 = qfrag(3, 1);
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    OT[ct][0] = mma32(Uf[0][ct], qa0, OT[ct][0]);
+    OT[ct][1] = mma32(Uf[0][ct], qa1, OT[ct][1]);
+    OT[ct][2] = mma32(Uf[0][ct], qa2, OT[ct][2]);
+    OT[ct][2] = mma32(Uf[1][ct], qa3, OT[ct][2]);
+    OT[ct][3] = mma32(Uf[0][ct], qa4, OT[ct][3]);
+    OT[ct][3] = mma32(Uf[1][ct], qa5, OT[ct][3]);
+  }
+}
+
+// OT (one token per lane, 4 channels) rounded to bf16 -> the stage's kr, used as o staging:
+// row 16 I + l16, channels col0 + 16 ct + 4 q4 .. + 3 in natural order (row stride RKS)
+__device__ __forceinline__ void c_stage_o(uint16_t* ob, const f32x4 (&OT)[2][4], int col0, int l16, int q4) {
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      *reinterpret_cast<uint2*>(&ob[rk(SBT * I + l16, col0 + 16 * ct + 4 * q4)]) = pack4(OT[ct][I]);
+}
+// staged rows 16 cw .. 16 cw + 15 of chunk c -> o: each lane 16 bytes, a 16-lane group one whole
+// 256-byte token row; rows past the chunk's n tokens fall outside the buffer bound and are dropped
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void c_store_rows(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c,
+                                             const uint16_t* ob, int cw, int lane) {
+  const int64_t t0 = c * CT;
+  const int n = (int)min<int64_t>(CT, sv.T - t0);
+  const int so2 = (int)(a.H * D) * 2;
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((sv.row0 + t0) * a.H + h) * D), 0, n * so2,
+                                                    kRsrcW3);
+  const int r0 = SBT * cw + (lane >> 4), cc8 = 8 * (lane & 15);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 u = ld128(ob, rk(r0 + 4 * j, cc8));
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{u.x, u.y, u.z, u.w}, ro, (r0 + 4 * j) * so2 + 2 * cc8, 0, 0);
+  }
+}
+
+// the gate of the chunk in the layout of OT: gx[ct][I] = 4 bf16 of token 16 I + l16, channels
+// col0 + 16 ct + 4 q4 .. + 3
+__device__ __forceinline__ void c_issue_gate(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c, int col0,
+                                             int lane, uint2 (&gx)[2][4]) {
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int64_t t0 = c * CT;
+  const int n = (int)min<int64_t>(CT, sv.T - t0);
+  const int sg2 = (int)a.gate_stride * 2;
+  const auto rg = __builtin_amdgcn_make_buffer_rsrc((void*)(a.gate + (sv.row0 + t0) * a.gate_stride + h * D), 0,
+                                                    n * sg2, kRsrcW3);
+  const int go = l16 * sg2 + 2 * (col0 + 4 * q4);
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) gx[ct][I] = ld_buf64(rg, go + 32 * ct, SBT * I * sg2);
+}
+
+// ---- output pass ---------------------------------------------------------------------
+// One block per (sequence, head, output segment) and CU: waves 0-3 produce, waves 4-7 consume
+// (wave 4 + j owns state columns 32 j ..). Per tick t, producers work on chunk c_begin + t and
+// consumers on the chunk before it:
+//   phase 1  P: loads of c arrive; norms, block products      C: U = T diag(b) (V - K^ S)
+//   phase 2  P: K^, K_, Q^ of c; loads of c + 1 issued         C: O^T = S^T Q^T + U^T Aqk^T
+//   phase 3  P: A, Aqk of c, diagonal inverses (at, aqk)       C: S update; gated: norm, gate
+// with one block barrier after each phase. at and aqk have one copy: consumers read them in
+// phases 1 and 2 and producers overwrite them in phase 3; the other per-chunk arrays
+// alternate between two stages. The two roles run separate loops with the same number of
+// ticks and barriers, so that neither role's registers are held through the other's code.
 //
-// Per chunk, phases and the barriers after them:
-//   loads; E1: norms and block decay products              | B
-//   E2/E3: decay factors, operands kr kc qw                 | C
-//   M1T: A / Aqk tiles, diagonal inverses, Q^ S; v loads    | D
-//   X: block substitution for W (into kr) and U~            | E
-//   S: U = U~ - W S, O += Aqk U, state update, o store      | F
-//
-// Two factorisations of the pairwise decay e^{g_i - g_j} are used:
-//  * fast: one reference at the chunk start (K^ = K e^{g}, K_ = K e^{-g}, formed from
-//    prefix and suffix products of alpha); valid
-//    while every channel decays by less than e^{-80} over the chunk, chosen per
-//    chunk by a block-wide vote;
-//  * blocked: references at token 7 of each 16-token block, with the factors
-//    e^{m_I - m_J}, e^{m_I}, e^{g_n - m_I} applied to fragments as they are
-//    read; accurate for every alpha once alpha is raised to e^{-7.5} (kAlphaMin2).
-//
-// GATED adds the rest of Eq. 15 short of W_o to the output: o <- Sigmoid(gate) *
-// o / sqrt(mean over the head's channels of o^2 + eps) * w. Each wave holds 32 of the
-// 128 channels of the fp32 output; their per-row sums of squares meet in LDS (adiag)
-// behind the chunk's last barrier (F). The output of chunk c is then normalised,
-// staged in fp32 over kr and kc (free until the next chunk's operands are formed,
-// barrier B) and stored with the gate applied, rounded once, while the loads of chunk
-// c + 1 are in flight; the last chunk's after the loop.
-constexpr int kStP = 36;   // fp32 output staging pitch (floats per row)
-static_assert(offsetof(Lds, kc) == offsetof(Lds, kr) + sizeof(Lds::kr) &&
-                  4 * CT * kStP * sizeof(float) <= sizeof(Lds::kr) + sizeof(Lds::kc) &&
-                  4 * CT * sizeof(float) <= sizeof(Lds::adiag),
-              "gated output staging in kr and kc, row partial sums in adiag");
+// GATED adds the rest of Eq. 15 short of W_o to the output: o <- Sigmoid(gate) * o / sqrt(mean
+// over the head's channels of o^2 + eps) * w. Each consumer wave sums its 32 channels' squares
+// per token in phase 2 (rowss); phase 3 reads the four parts and writes o once.
 template <bool GATED>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_out_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  Lds& L = *reinterpret_cast<Lds*>(lds_raw);
+  PcLdsOut& L = *reinterpret_cast<PcLdsOut*>(lds_raw);
 
   const uint32_t lid = (a.xcd_ranges && a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid)
                                                          : blockIdx.x;
   if (lid >= (uint32_t)a.nblk) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int cw = wave & 3, col0 = 32 * cw;
   const int l16 = lane & 15, q4 = lane >> 4;
   const SeqDesc& rd = a.run[run_of<0>(a, lid)];
   const int32_t local = (int32_t)lid - rd.out0;
@@ -693,470 +1032,146 @@ __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   const int64_t NC = (sv.T + CT - 1) / CT;
   const int64_t c_begin = (int64_t)p * a.Lo;
   const int64_t c_end = min<int64_t>(NC, c_begin + a.Lo);
+  const int64_t nch = c_end - c_begin;
 
-  // ---- state: rows 16 rt + 4 q4 + r, columns col0 + 16 ct + l16 -----------------
-  const int col0 = 32 * wave;
-  const int svo = (4 * q4) * D + col0 + l16;   // lane part of a state element's offset
-  f32x4 S[8][2];
-  if (sv.P > 1) {
-    if (p % kSub == 0) {   // a chain start (tile-major)
-      const float* src = sv.ws + (2 * sv.E + p) * D * D;
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) S[rt][ct] = load_tile4(src, wave, rt, ct, lane);
-    }
-  } else {                 // S0 ([D][D] row-major) or zero
-    const float* src = a.S0 ? a.S0 + sv.sidx * D * D : nullptr;
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[rt][ct][r] = src ? src[svo + (16 * rt + r) * D + 16 * ct] : 0.f;
-  }
-  if (sv.P > 1 && p % kSub != 0) {
-    // a start inside a summary segment: S_start(p) = M_e S_start(p - p % kSub) + S_e with
-    // e = p - 1, in fp32-accurate MFMA (bf16 high and low parts, three products)
-    const int e = p - 1;
-    const float* Mp = sv.ws + (sv.E + e) * D * D;
-    const float* Sp = sv.ws + e * D * D;
-    const float* base = sv.ws + (2 * sv.E + p - p % kSub) * D * D;
-    uint4 bH[4][2], bL[4][2];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const f32x4 v0 = load_tile4(base, wave, 2 * s, ct, lane), v1 = load_tile4(base, wave, 2 * s + 1, ct, lane);
-        uint2 l0, l1;
-        const uint2 h0 = pack_split(make_float4(v0[0], v0[1], v0[2], v0[3]), l0);
-        const uint2 h1 = pack_split(make_float4(v1[0], v1[1], v1[2], v1[3]), l1);
-        bH[s][ct] = cat(h0, h1);
-        bL[s][ct] = cat(l0, l1);
-      }
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      uint4 aH[4], aL[4];
-      const uint4* Mf = reinterpret_cast<const uint4*>(Mp);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        aH[s] = Mf[mfrag_off(rt, s, lane)];
-        aL[s] = Mf[mfrag_off(rt, s, lane) + 1];
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f32x4 acc0 = load_tile4(Sp, wave, rt, ct, lane), acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          acc1 = mma32(aL[s], bH[s][ct], acc1);
-          acc2 = mma32(aH[s], bL[s][ct], acc2);
-          acc0 = mma32(aH[s], bH[s][ct], acc0);
-        }
-        S[rt][ct] = acc0 + (acc1 + acc2);
-      }
-    }
-  }
-  // the Aqk blocks (0,1) and (2,3) above the diagonal are read as zeros
-  for (int e = tid; e < 2 * SBT * SBT; e += NTHR) {
+  // the Aqk blocks (0,1) and (2,3) above the diagonal are read as zeros (ordered before their
+  // first read by the barriers of tick 0)
+  for (int e = tid; e < 2 * SBT * SBT; e += kPcThreads) {
     const int I = (e >> 8) * 2, i = (e >> 4) & 15, j = e & 15;
     L.aqk[tr(SBT * (I + 1) + j, SBT * I + i)] = 0;
   }
 
-  const uint2 kOnes = make_uint2(0x3F803F80u, 0x3F803F80u);   // alpha = 1 past the end
-  // GATED: the previous chunk's fp32 output (D layout) and its gate (rows 4 (lane >> 2) + j,
-  // channels col0 + 8 (lane & 3) .. + 7), carried into the next chunk step
-  f32x4 Og[4][2];
-  uint4 gx[4];
-  auto gate_epilogue = [&](int64_t cp) {
-    int lane_e = lane;
-    asm volatile("" : "+v"(lane_e));
-    const int e16 = lane_e & 15, e4 = lane_e >> 4;
-    const int64_t tp = cp * CT;
-    const int np = (int)min<int64_t>(CT, sv.T - tp);
-    const int oc = 8 * (lane_e & 3);
-    float4 w0 = make_float4(1.f, 1.f, 1.f, 1.f), w1 = w0;   // gain of the lane's output channels
-    if (a.norm_w != nullptr) {
-      w0 = ldf4(a.norm_w + col0 + oc);
-      w1 = ldf4(a.norm_w + col0 + oc + 4);
-    }
-    float* st = reinterpret_cast<float*>(L.kr) + wave * CT * kStP;
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) st[(16 * I + 4 * e4 + r) * kStP + 16 * ct + e16] = Og[I][ct][r];
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    // rows -> o, scaled by 1 / rms and the gain, with the gate; 16 bytes per lane; rows
-    // past the end are dropped
-    const int so2 = (int)(a.H * D) * 2;
-    const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((sv.row0 + tp) * a.H + h) * D), 0, np * so2,
-                                                      kRsrcW3);
-    auto sig = [](float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); };
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 4 * (lane_e >> 2) + j;
-      const float4 p4 = ldf4(&L.adiag[row * 4]);
-      const float rinv = __builtin_amdgcn_rsqf((p4.x + p4.y + p4.z + p4.w) * (1.f / D) + a.norm_eps);
-      const float4 y0 = mul4(ldf4(&st[row * kStP + oc]), w0), y1 = mul4(ldf4(&st[row * kStP + oc + 4]), w1);
-      const float4 g0 = unpack4(make_uint2(gx[j].x, gx[j].y)), g1 = unpack4(make_uint2(gx[j].z, gx[j].w));
-      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-      const u32x4_t w4 = {pack_bf16x2(y0.x * rinv * sig(g0.x), y0.y * rinv * sig(g0.y)),
-                          pack_bf16x2(y0.z * rinv * sig(g0.z), y0.w * rinv * sig(g0.w)),
-                          pack_bf16x2(y1.x * rinv * sig(g1.x), y1.y * rinv * sig(g1.y)),
-                          pack_bf16x2(y1.z * rinv * sig(g1.z), y1.w * rinv * sig(g1.w))};
-      __builtin_amdgcn_raw_buffer_store_b128(w4, ro, row * so2 + 2 * (col0 + oc), 0, 0);
-    }
-  };
-
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    // Lane-derived addresses are recomputed every chunk (cheap) rather than kept live
-    // across the loop: the lane id passes through an empty asm so that they cannot be
-    // hoisted out of it.
-    int lane_c = lane;
-    asm volatile("" : "+v"(lane_c));
-    const int l16 = lane_c & 15, q4 = lane_c >> 4;
-    // elementwise mapping: wave = decay block; half-wave hf = tokens 8 hf .. 8 hf + 7
-    // of the block; lane cg = channels 4 cg .. 4 cg + 3
-    const int hf = lane_c >> 5, cg = lane_c & 31, c0 = 4 * cg, p0 = cpos(c0);
-    const int tk0 = SBT * wave + 8 * hf;
-    const int64_t t0 = c * CT;
-    const int n = (int)min<int64_t>(CT, sv.T - t0);
-
-    // ---- loads ----------------------------------------------------------------------
-    // Buffer loads: block-uniform base and bounds (the chunk's first n tokens), byte
-    // offsets split into a lane part and a uniform part. Reads past the bound return
-    // zero, which is k = q = v = beta = 0 for tokens past the end; alpha is set to 1.
-    uint2 kx[8], qx[8], ax[8];
-    float bt;
-    {
-      const int64_t row0 = sv.row0 + t0;
-      const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
-      const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
-      const auto rq_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
-      const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
-      const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
-      const int vk = (8 * hf) * st2 + 2 * c0, va = (8 * hf) * sa2 + 2 * c0;
-      const int tb = SBT * wave;   // first token of this wave's block
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        kx[i] = ld_buf64(rk_, vk, (tb + i) * st2);
-        qx[i] = ld_buf64(rq_, vk, (tb + i) * st2);
-        const uint2 av = ld_buf64(ra_, va, (tb + i) * sa2);
-        ax[i] = tk0 + i < n ? av : kOnes;
+  if (wave < 4) {
+    // ---------------- producers ----------------
+    PLoad R;
+    float4 al[8];
+    bool fast = true;
+    if (nch > 0) p_issue<true>(a, sv, h, c_begin, wave, lane, R);
+    for (int64_t t = 0; t <= nch; ++t) {
+      const int64_t cp = c_begin + t;
+      PcStage& sp = L.st[cp & 1];
+      if (t < nch) p_phase1<true>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
+      lds_barrier();
+      if (t < nch) {
+        fast = p_phase2<true>(sp, L.qw[cp & 1], L.rk, L.rq, R, al, wave, lane);
+        if (t + 1 < nch) p_issue<true>(a, sv, h, cp + 1, wave, lane, R);
       }
-      bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb_, tid * (int)a.H * 2, 0, 0));
+      lds_barrier();
+      if (t < nch) p_phase3_out(sp, L.qw[cp & 1], L.at, L.aqk, L.adiag, fast, wave, lane);
+      lds_barrier();
     }
-    if (GATED && c > c_begin) gate_epilogue(c - 1);   // the previous chunk's output, while the loads fly
-
-    // ---- E1: norms, block decay products -------------------------------------------
-    if (tid < CT) L.beta[tid] = bt;
-    if (a.l2norm) {
-      float ss[16];
+  } else {
+    // ---------------- consumers ----------------
+    f32x4 S[8][2];
+    if (sv.P > 1) {   // the segment's start state, chained by the combine pass (tile-major)
+      const float* src = sv.ws + (2 * sv.E + p) * D * D;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ss[i] = dot4(kx[i]);
-        ss[i + 8] = dot4(qx[i]);
-      }
-      const float tot = half_sum16(ss, lane_c);
-      if ((lane_c & 1) == 0) {
-        const int vv = (lane_c >> 1) & 15;          // 0..7: k of token vv; 8..15: q of token vv - 8
-        const float rn = __builtin_amdgcn_rsqf(tot + kL2Eps);
-        if (vv < 8) L.rk[tk0 + vv] = rn; else L.rq[tk0 + vv - 8] = rn;
-      }
-    } else if (cg < 8) {
-      L.rk[tk0 + cg] = 1.f;
-      L.rq[tk0 + cg] = 1.f;
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) S[rt][ct] = load_tile4(src, cw, rt, ct, lane);
+    } else {          // S0 ([D][D] row-major) or zero
+      const float* src = a.S0 ? a.S0 + sv.sidx * D * D : nullptr;
+      const int svo = (4 * q4) * D + col0 + l16;
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[rt][ct][r] = src ? src[svo + (16 * rt + r) * D + 16 * ct] : 0.f;
     }
-    float4 al[8];   // alpha of the lane's tokens
-#pragma unroll
-    for (int i = 0; i < 8; ++i) al[i] = unpack4(make_uint2(clamp_alpha2(ax[i].x), clamp_alpha2(ax[i].y)));
-    {
-      float4 hp = al[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) hp = mul4(hp, al[i]);
-      *reinterpret_cast<float4*>(hf ? &L.pf[wave][c0] : &L.pb[wave][c0]) = hp;
-    }
-    lds_barrier();   // B
-
-    // ---- E2 / E3: decay factors and MFMA operands --------------------------------------
-    bool fast;
-    {
-      // per channel: before = decay over the blocks before this one, after = over the
-      // blocks after it; the lane's half adds its block's other half on one side
-      float4 full[NSB], h0w = make_float4(1.f, 1.f, 1.f, 1.f), h1w = h0w;
-#pragma unroll
-      for (int J = 0; J < NSB; ++J) {
-        const float4 h0 = ldf4(&L.pb[J][c0]), h1 = ldf4(&L.pf[J][c0]);
-        full[J] = mul4(h0, h1);
-        if (J == wave) { h0w = h0; h1w = h1; }
-      }
-      float4 egn4 = full[0], before = make_float4(1.f, 1.f, 1.f, 1.f), after = before;
-#pragma unroll
-      for (int J = 1; J < NSB; ++J) egn4 = mul4(egn4, full[J]);
-#pragma unroll
-      for (int J = 0; J < NSB; ++J) {
-        if (J < wave) before = mul4(before, full[J]);
-        if (J > wave) after = mul4(after, full[J]);
-      }
-      // every wave holds all 128 channels, so every wave reaches the same vote
-      fast = __all(fminf(fminf(egn4.x, egn4.y), fminf(egn4.z, egn4.w)) >= kFastMin) != 0;
-      if (wave == 0 && hf == 0) *reinterpret_cast<float4*>(&L.egn[c0]) = egn4;
-      // 1 / |k| and 1 / |q| of the lane's tokens (from E1) go into the operands, so that
-      // no product downstream needs a norm scaling
-      const float4 rk0 = ldf4(&L.rk[tk0]), rk1 = ldf4(&L.rk[tk0 + 4]);
-      const float4 rq0 = ldf4(&L.rq[tk0]), rq1 = ldf4(&L.rq[tk0 + 4]);
-      const float rkt[8] = {rk0.x, rk0.y, rk0.z, rk0.w, rk1.x, rk1.y, rk1.z, rk1.w};
-      const float rqt[8] = {rq0.x, rq0.y, rq0.z, rq0.w, rq1.x, rq1.y, rq1.z, rq1.w};
-      auto put = [&](int i, float4 fr, float4 fc) {
-        const int tk = tk0 + i;
-        const float4 ks = mul4(unpack4(kx[i]), make_float4(rkt[i], rkt[i], rkt[i], rkt[i]));
-        const float4 qs = mul4(unpack4(qx[i]), make_float4(rqt[i], rqt[i], rqt[i], rqt[i]));
-        *reinterpret_cast<uint2*>(&L.kr[rk(tk, p0)]) = pack4(mul4(ks, fr));
-        *reinterpret_cast<uint2*>(&L.kc[rk(tk, p0)]) = pack4(mul4(ks, fc));
-        *reinterpret_cast<uint2*>(&L.qw[rm(tk, p0)]) = pack4(mul4(qs, fr));
-      };
-      if (fast) {
-        // e^{g_t} as a prefix product from the chunk start and e^{g_n - g_t} / e^{g_n} as a
-        // suffix product towards the chunk end: no per-element reciprocal, and the same
-        // instruction stream in both half-waves
-        const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
-        float4 fw = hf ? mul4(before, h0w) : before;
-        float4 bw = mul4(hf ? after : mul4(after, h1w), rcp4(egn4));
-        float4 fr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          fw = mul4(fw, al[i]);
-          fr[i] = fw;
-        }
-#pragma unroll
-        for (int i = 7; i >= 0; --i) {
-          put(i, fr[i], bw);
-          if (i > 0) bw = mul4(bw, al[i]);
-        }
-        (void)one4;
-      } else {
-        // blocked: reference m_I = g at the block's token 7; half 1 runs forward
-        // (e^{g - m_I} = product over tokens 8..t), half 0 backward (e^{m_I - g} =
-        // product over tokens t+1..7)
-        if (hf == 1) {
-          float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            run = mul4(run, al[i]);
-            put(i, run, rcp4(run));
-          }
-        } else {
-          float4 run = make_float4(1.f, 1.f, 1.f, 1.f);
-#pragma unroll
-          for (int i = 7; i >= 0; --i) {
-            put(i, rcp4(run), run);
-            run = mul4(run, al[i]);
-          }
-        }
-      }
-    }
-    lds_barrier();   // C
-
-    // ---- M1T: A and Aqk blocks, diagonal inverses, Q^ S ---------------------------------
-    f32x4 O[4][2];
-    uint4 vx[4];
-    {
-      uint4 cA[4], cB[4], rA[4], sc[4];
-      // wave 0: the four diagonal A blocks and their inverses;
-      // wave 1: Aqk00 A10 Aqk10 A20 Aqk20 A30;  wave 2: Aqk11 A21 Aqk21 A31 Aqk31;
-      // wave 3: Aqk22 A32 Aqk32 Aqk33 Aqk30
-      if (wave == 0) {
-        __builtin_amdgcn_s_setprio(3);   // the chunk's critical path
-#pragma unroll
-        for (int I = 0; I < NSB; ++I) {
-          tile_frags(L.kc, I, cA, l16, q4);
-          tile_frags(L.kr, I, rA, l16, q4);
-          epi_a(L, I, I, mma4(rA, cA), l16, q4);
-        }
-        invert_diag4(L, lane_c);
-        __builtin_amdgcn_s_setprio(0);
-      } else if (wave == 1) {
-        tile_frags(L.kc, 0, cA, l16, q4);
-        tile_frags<RMS>(L.qw, 0, rA, l16, q4); epi_q(L, 0, 0, mma4(rA, cA), l16, q4);
-#pragma unroll
-        for (int I = 1; I < NSB; ++I) {
-          pair_frags(L, fast, I, 0, cA, sc, q4);
-          tile_frags(L.kr, I, rA, l16, q4); epi_a(L, I, 0, mma4(rA, sc), l16, q4);
-          if (I < 3) { tile_frags<RMS>(L.qw, I, rA, l16, q4); epi_q(L, I, 0, mma4(rA, sc), l16, q4); }
-        }
-      } else if (wave == 2) {
-        tile_frags(L.kc, 1, cA, l16, q4);
-        tile_frags<RMS>(L.qw, 1, rA, l16, q4); epi_q(L, 1, 1, mma4(rA, cA), l16, q4);
-#pragma unroll
-        for (int I = 2; I < NSB; ++I) {
-          pair_frags(L, fast, I, 1, cA, sc, q4);
-          tile_frags(L.kr, I, rA, l16, q4); epi_a(L, I, 1, mma4(rA, sc), l16, q4);
-          tile_frags<RMS>(L.qw, I, rA, l16, q4); epi_q(L, I, 1, mma4(rA, sc), l16, q4);
-        }
-      } else {
-        tile_frags(L.kc, 2, cA, l16, q4);
-        tile_frags<RMS>(L.qw, 2, rA, l16, q4); epi_q(L, 2, 2, mma4(rA, cA), l16, q4);
-        pair_frags(L, fast, 3, 2, cA, sc, q4);
-        tile_frags(L.kr, 3, rA, l16, q4); epi_a(L, 3, 2, mma4(rA, sc), l16, q4);
-        tile_frags<RMS>(L.qw, 3, rA, l16, q4); epi_q(L, 3, 2, mma4(rA, sc), l16, q4);
-        tile_frags(L.kc, 3, cB, l16, q4); epi_q(L, 3, 3, mma4(rA, cB), l16, q4);
-        tile_frags(L.kc, 0, cB, l16, q4); pair_frags(L, fast, 3, 0, cB, sc, q4);
-        epi_q(L, 3, 0, mma4(rA, sc), l16, q4);
-      }
-      // O = Q^ S (Q^ carries 1 / |q|); the blocked factorisation scales Q^'s channels by e^{m_I}
-      uint4 Sf[4][2];
-      pack_state(S, Sf);
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        uint4 qf[4];
-        tile_frags<RMS>(L.qw, I, qf, l16, q4);
-        if (!fast) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            qf[s] = scale8(qf[s], em_of(L, I, 32 * s + 4 * q4), em_of(L, I, 32 * s + 16 + 4 * q4));
-        }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mma32(qf[s], Sf[s][ct], acc);
-          O[I][ct] = acc;
-        }
-      }
-      load_v(a, sv.row0 + t0, h, n, col0, lane_c, vx);
-    }
-    lds_barrier();   // D
-
-    // ---- X: block substitution X = (I + A)^{-1} diag(sigma) R --------------------------
-    // right-hand sides: K^ channel tiles 2 wave, 2 wave + 1 (W, negated, into kr) and
-    // this wave's v columns (U~, kept in registers)
-    f32x4 Ut[4][2];
-    {
-      stage_v(L, col0, vx, lane_c);   // first: v (loaded during M1T) leaves the registers
-      uint2 af[10];
-      load_t_frags(L, af, l16, q4);
-      w_tile(L, fast, 2 * wave, af, l16, q4);
-      w_tile(L, fast, 2 * wave + 1, af, l16, q4);
-      u_tiles(L, col0, af, Ut, l16, q4);
-    }
-    lds_barrier();   // E
-
-    // ---- S: U = U~ - W S;  O += Aqk U;  S <- Diag(e^{g_n}) S + K~^T diag(1/|k|) U ----------
-    {
-      uint4 Sf[4][2];
-      pack_state(S, Sf);
-      minus_ws(L, Sf, Ut, l16, q4);
-    }
-    {
-      uint4 Uf[2][2], qa[6];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Uf[s][ct] = pack8(Ut[2 * s][ct], Ut[2 * s + 1][ct]);
-      // A operand rows 16 I + l16, tokens 32 s + 4 q4 + 0..3 and 32 s + 16 + 4 q4 + 0..3
-      auto qfrag = [&](int I, int s) {
-        const int base = tr(32 * s + 4 * q4 + (l16 >> 2), SBT * I + 4 * (l16 & 3));
-        return cat(ld_tr(&L.aqk[base]), ld_tr(&L.aqk[base + tr(16, 0)]));
-      };
-      qa[0] = qfrag(0, 0);
-      qa[1] = qfrag(1, 0);
-      qa[2] = qfrag(2, 0);
-      qa[3] = qfrag(2, 1);
-      qa[4] = qfrag(3, 0);
-      qa[5] = qfrag(3, 1);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        O[0][ct] = mma32(qa[0], Uf[0][ct], O[0][ct]);
-        O[1][ct] = mma32(qa[1], Uf[0][ct], O[1][ct]);
-        O[2][ct] = mma32(qa[2], Uf[0][ct], O[2][ct]);
-        O[2][ct] = mma32(qa[3], Uf[1][ct], O[2][ct]);
-        O[3][ct] = mma32(qa[4], Uf[0][ct], O[3][ct]);
-        O[3][ct] = mma32(qa[5], Uf[1][ct], O[3][ct]);
-      }
-      if (!GATED) {
-        // output tile -> this wave's channels of qw (natural order; v is consumed)
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) L.qw[rm(SBT * I + 4 * q4 + r, col0 + 16 * ct + l16)] = f2bf(O[I][ct][r]);
-      }
-    }
+    float4 gw[2];   // gated: the norm gain of the lane's channels col0 + 16 ct + 4 q4 .. + 3
     if (GATED) {
-      const int sg2 = (int)a.gate_stride * 2;
-      const auto rg = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.gate + (sv.row0 + t0) * a.gate_stride + h * D), 0, n * sg2, kRsrcW3);
-      const int gc = col0 + 8 * (lane_c & 3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const auto g4 = __builtin_amdgcn_raw_buffer_load_b128(rg, (4 * (lane_c >> 2) + j) * sg2 + 2 * gc, 0, 0);
-        gx[j] = make_uint4(g4[0], g4[1], g4[2], g4[3]);
-      }
-      // this wave's part of each row's sum of squares: lane l16 of a DPP row ends with row
-      // 16 (l16 >> 2) + 4 q4 + (l16 & 3); adiag is free after the inverses
-      float ss[16];
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ss[4 * I + r] = O[I][0][r] * O[I][0][r] + O[I][1][r] * O[I][1][r];
-      const float part = row_sum16(ss, l16);
-      L.adiag[(16 * (l16 >> 2) + 4 * q4 + (l16 & 3)) * 4 + wave] = part;
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Og[I][ct] = O[I][ct];
+      for (int ct = 0; ct < 2; ++ct)
+        gw[ct] = a.norm_w != nullptr ? ldf4(a.norm_w + col0 + 16 * ct + 4 * q4) : make_float4(1.f, 1.f, 1.f, 1.f);
     }
-    update_state(L, fast, S, Ut, l16, q4);
-    if (!GATED) {
-      // staged output rows -> o, 16 bytes per lane; rows past the end fall outside the
-      // buffer bound and are dropped
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      const int so2 = (int)(a.H * D) * 2;
-      const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((sv.row0 + t0) * a.H + h) * D), 0, n * so2,
-                                                        kRsrcW3);
-      const int oc = col0 + 8 * (lane_c & 3);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 4 * (lane_c >> 2) + j;
-        const uint4 u = *reinterpret_cast<const uint4*>(&L.qw[rm(row, oc)]);
-        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-        const u32x4_t w4 = {u.x, u.y, u.z, u.w};
-        __builtin_amdgcn_raw_buffer_store_b128(w4, ro, row * so2 + 2 * oc, 0, 0);
+    uint2 gx[2][4], vr[8];
+    f32x4 U[4][2], OT[2][4];
+    for (int64_t t = 0; t <= nch; ++t) {
+      const int64_t cc = c_begin + t - 1;
+      const PcStage& sc = L.st[cc & 1];
+      // the stage's vote, read from LDS: made wave-uniform so that the factorisation choice stays a
+      // branch (a value the compiler takes as divergent would run both paths)
+      const bool cf = t > 0 && __builtin_amdgcn_readfirstlane(sc.fast) != 0;
+      // ---- phase 1: gated, the previous chunk's staged rows go out; U of this chunk
+      if (GATED && t > 1) c_store_rows(a, sv, h, cc - 1, L.st[(cc - 1) & 1].kr, cw, lane);
+      if (t > 0) {
+        if (GATED) c_issue_gate(a, sv, h, cc, col0, lane, gx);
+        c_solve(sc, L.at, L.qw[(cc + 1) & 1], cf, S, col0, U, l16, q4);
       }
+      if (t < nch) c_issue_v(a, sv, h, cc + 1, cw, lane, vr);   // staged in phase 3
+      lds_barrier();
+      // ---- phase 2: the output
+      if (t > 0) {
+        c_output(sc, L.qw[cc & 1], L.aqk, cf, S, U, OT, l16, q4);
+        if (!GATED) {
+          c_stage_o(L.st[cc & 1].kr, OT, col0, l16, q4);   // K^ of this chunk is used up
+        } else {
+          // this wave's part of each token's sum of squares: over the lane's 8 channels, then
+          // over the four lane groups that hold the same token
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            float v = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v += OT[ct][I][r] * OT[ct][I][r];
+            v = halve32(v, v);
+            v = halve16(v, v);
+            if (q4 == 0) L.rowss[(SBT * I + l16) * 4 + cw] = v;
+          }
+        }
+      }
+      lds_barrier();
+      // ---- phase 3: the state update; the output rows go out (gated: normalised, staged)
+      if (t > 0) {
+        if (!GATED) c_store_rows(a, sv, h, cc, L.st[cc & 1].kr, cw, lane);
+        c_update(sc, cf, S, U, l16, q4);
+        if (GATED) {
+          auto sig = [](float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); };
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            const float4 p4 = ldf4(&L.rowss[(SBT * I + l16) * 4]);
+            const float rinv = __builtin_amdgcn_rsqf((p4.x + p4.y + p4.z + p4.w) * (1.f / D) + a.norm_eps);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              const float4 g = unpack4(gx[ct][I]);
+              const float4 w = gw[ct];
+              OT[ct][I][0] *= rinv * w.x * sig(g.x);
+              OT[ct][I][1] *= rinv * w.y * sig(g.y);
+              OT[ct][I][2] *= rinv * w.z * sig(g.z);
+              OT[ct][I][3] *= rinv * w.w * sig(g.w);
+            }
+          }
+          c_stage_o(L.st[cc & 1].kr, OT, col0, l16, q4);   // stored in the next tick's phase 1
+        }
+      }
+      // v of the next chunk into this chunk's qw (its Q^ was used in phase 2): read in the next
+      // tick's phase 1, before the producers' Q^ of the chunk after goes there
+      if (t < nch) c_stage_v(L.qw[cc & 1], vr, cw, lane);
+      lds_barrier();
     }
-    lds_barrier();   // F
+    if (GATED && nch > 0) c_store_rows(a, sv, h, c_end - 1, L.st[(c_end - 1) & 1].kr, cw, lane);
+    if (a.S_final != nullptr && p == sv.P - 1) store_state(S, a.S_final + sv.sidx * D * D, (4 * q4) * D + col0 + l16);
   }
-  if (GATED && c_end > c_begin) gate_epilogue(c_end - 1);
-
-  if (a.S_final != nullptr && p == sv.P - 1) store_state(S, a.S_final + sv.sidx * D * D, svo);
 }
 
-// Summary pass: one block of 8 waves per (batch, head, summary segment). Waves 0-3 run
-// S from 0 (state columns 32 w ..), waves 4-7 the transition M from I (columns
-// 32 (w - 4) ..); the chunk operands, A, T and W are formed once for both. The state
-// is written at every output-segment boundary (every Lo chunks).
-//
-// Per chunk, phases and the barriers after them:
-//   loads; E1: partial norms, block decay products            | B
-//   E2/E3: norms, decay factors, operands kr kc; v loads       | C
-//   M1T: A blocks, diagonal inverses                           | D
-//   X: W (channel tile w, into kr); U~ (waves 0-3)             | E
-//   S: U = U~ - W S (or -W M), state update                    | F
-__global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) void kda_sum_kernel(ChunkArgs a) {
+// ---- summary pass --------------------------------------------------------------------
+// One block per (sequence, head, summary segment): waves 0-3 produce as in the output pass
+// (no q), waves 4-7 consume; wave 4 + j runs both the state S from 0 and the transition M from I
+// on columns 32 j .. 32 j + 31 (phase 1: S, phase 2: M; phase 3 idle while the producers form
+// A and the inverses). At the segment end S goes to the workspace tile-major and M as split
+// bf16 A fragments.
+__global__ __launch_bounds__(kPcThreads) void kda_sum_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  Lds& L = *reinterpret_cast<Lds*>(lds_raw);
-  float (&nk)[2][CT] = *reinterpret_cast<float(*)[2][CT]>(lds_raw + sizeof(Lds));   // partial |k|^2
+  PcLdsSum& L = *reinterpret_cast<PcLdsSum*>(lds_raw);
 
   const uint32_t lid = (a.xcd_ranges && a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid)
                                                          : blockIdx.x;
   if (lid >= (uint32_t)a.nblk) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
-  const bool mkind = wave >= 4;
+  const int cw = wave & 3, col0 = 32 * cw;
   const int l16 = lane & 15, q4 = lane >> 4;
   const SeqDesc& rd = a.run[run_of<1>(a, lid)];
   const int32_t local = (int32_t)lid - rd.sum0;
@@ -1165,261 +1180,72 @@ __global__ __launch_bounds__(2 * NTHR) __attribute__((amdgpu_waves_per_eu(2))) v
   const SeqView sv = seq_view(a, rd, bhl);
   const int64_t h = uni(bhl % (int32_t)a.H);
   const int64_t NC = (sv.T + CT - 1) / CT;
-  const int64_t Ls = (int64_t)kSub * a.Lo;            // chunks per summary segment
-  const int64_t c_stop = (int64_t)(sv.P - 1) * a.Lo;  // the last output segment needs no summary
-  const int64_t c_begin = (int64_t)p * Ls;
-  const int64_t c_end = min<int64_t>(min<int64_t>(NC, c_begin + Ls), c_stop);
+  const int64_t c_begin = (int64_t)p * a.Lo;
+  const int64_t c_end = min<int64_t>(NC, c_begin + a.Lo);   // summary segments are output segments 0 .. P - 2
+  const int64_t nch = c_end - c_begin;
 
-  const int col0 = 32 * (wave & 3);
-  f32x4 S[8][2];
-#pragma unroll
-  for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * rt + 4 * q4 + r, col = col0 + 16 * ct + l16;
-        S[rt][ct][r] = (mkind && row == col) ? 1.f : 0.f;
+  if (wave < 4) {
+    // ---------------- producers ----------------
+    PLoad R;
+    float4 al[8];
+    bool fast = true;
+    if (nch > 0) p_issue<false>(a, sv, h, c_begin, wave, lane, R);
+    for (int64_t t = 0; t <= nch; ++t) {
+      const int64_t cp = c_begin + t;
+      PcStage& sp = L.st[cp & 1];
+      if (t < nch) p_phase1<false>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
+      lds_barrier();
+      if (t < nch) {
+        fast = p_phase2<false>(sp, nullptr, L.rk, L.rq, R, al, wave, lane);
+        if (t + 1 < nch) p_issue<false>(a, sv, h, cp + 1, wave, lane, R);
       }
-
-  const uint32_t kOne = 0x3F803F80u;   // alpha = 1 past the end
-  // Raw inputs of one chunk for this lane: k and alpha of tokens tk0 .. tk0 + 7 at
-  // channels c0, c0 + 1, beta of token (tid & 63).
-  // Buffer loads bounded by the chunk's valid tokens (zero past the end). The next
-  // chunk's loads are issued during the state update of the current one.
-  struct Raw {
-    uint32_t k[8], a[8];
-    uint16_t bt;
-  };
-  auto issue = [&](int64_t c, Raw& R, int lane_c) {
-    const int I = wave & 3, hc = wave >> 2;
-    const int hf = lane_c >> 5, c0 = 64 * hc + 2 * (lane_c & 31);
-    const int64_t t0 = c * CT;
-    const int n = (int)min<int64_t>(CT, sv.T - t0);
-    const int64_t row0 = sv.row0 + t0;
-    const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
-    const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
-    const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
-    const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
-    const int vk = (8 * hf) * st2 + 2 * c0, va = (8 * hf) * sa2 + 2 * c0;
-    const int tb = SBT * I;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      R.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk_, vk, (tb + i) * st2, 0);
-      R.a[i] = __builtin_amdgcn_raw_buffer_load_b32(ra_, va, (tb + i) * sa2, 0);
+      lds_barrier();
+      if (t < nch) p_phase3_sum(sp, L.at, L.adiag, fast, wave, lane);
+      lds_barrier();
     }
-    R.bt = __builtin_amdgcn_raw_buffer_load_b16(rb_, (lane_c & 63) * (int)a.H * 2, 0, 0);
-  };
-  Raw nxt;
-  if (c_begin < c_end) issue(c_begin, nxt, lane);
-  int to_boundary = a.Lo;    // chunks left to the next output-segment boundary
-  int e_next = p * kSub;     // its workspace entry
-
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    int lane_c = lane;
-    asm volatile("" : "+v"(lane_c));
-    const int l16 = lane_c & 15, q4 = lane_c >> 4;
-    // elementwise mapping: wave -> decay block I = wave & 3 and channel half hc;
-    // half-wave hf = tokens 8 hf .. 8 hf + 7 of the block; lane cg = channels c0, c0 + 1
-    const int I = wave & 3, hc = wave >> 2;
-    const int hf = lane_c >> 5, cg = lane_c & 31, c0 = 64 * hc + 2 * cg, p0 = cpos(c0);
-    const int tk0 = SBT * I + 8 * hf;
-    const int64_t t0 = c * CT;
-    const int n = (int)min<int64_t>(CT, sv.T - t0);
-
-    const Raw cur = nxt;
-    uint32_t kx[8], ax[8];
+    lds_barrier();   // (the consumers' scratch below)
+  } else {
+    // ---------------- consumers ----------------
+    f32x4 S[8][2], M[8][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      kx[i] = cur.k[i];
-      ax[i] = tk0 + i < n ? cur.a[i] : kOne;
-    }
-    const float bt = bf2f(cur.bt);
-
-    // ---- E1: partial norms, block decay products ---------------------------------------
-    if (tid < CT) L.beta[tid] = bt;
-    if (a.l2norm) {
-      float ss[16];
+    for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ss[i] = sq2(kx[i], 0.f);
-        ss[i + 8] = 0.f;
-      }
-      const float tot = half_sum16(ss, lane_c);
-      const int vv = (lane_c >> 1) & 15;
-      if ((lane_c & 1) == 0 && vv < 8) nk[hc][tk0 + vv] = tot;
-    }
-    float2 al[8];   // alpha of the lane's tokens
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t ac = clamp_alpha2(ax[i]);
-      al[i] = make_float2(bf_lo(ac), bf_hi(ac));
-    }
-    {
-      float2 hp = al[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) { hp.x *= al[i].x; hp.y *= al[i].y; }
-      *reinterpret_cast<float2*>(hf ? &L.pf[I][c0] : &L.pb[I][c0]) = hp;
-    }
-    lds_barrier();   // B
-
-    // ---- E2 / E3: norms, decay factors, MFMA operands ---------------------------------
-    bool fast;
-    {
-      float2 full[NSB];
-      float2 h0w = make_float2(1.f, 1.f), h1w = h0w, eo = h0w;
-#pragma unroll
-      for (int J = 0; J < NSB; ++J) {
-        const float2 h0 = *reinterpret_cast<const float2*>(&L.pb[J][c0]);
-        const float2 h1 = *reinterpret_cast<const float2*>(&L.pf[J][c0]);
-        full[J] = make_float2(h0.x * h1.x, h0.y * h1.y);
-        if (J == I) { h0w = h0; h1w = h1; }
-        // the other channel half, formed the same way, so that every wave votes alike
-        const float2 h0o = *reinterpret_cast<const float2*>(&L.pb[J][c0 ^ 64]);
-        const float2 h1o = *reinterpret_cast<const float2*>(&L.pf[J][c0 ^ 64]);
-        const float2 fo = make_float2(h0o.x * h1o.x, h0o.y * h1o.y);
-        eo = J == 0 ? fo : make_float2(eo.x * fo.x, eo.y * fo.y);
-      }
-      float2 egn2 = full[0], before = make_float2(1.f, 1.f), after = before;
-#pragma unroll
-      for (int J = 1; J < NSB; ++J) { egn2.x *= full[J].x; egn2.y *= full[J].y; }
-#pragma unroll
-      for (int J = 0; J < NSB; ++J) {
-        if (J < I) { before.x *= full[J].x; before.y *= full[J].y; }
-        if (J > I) { after.x *= full[J].x; after.y *= full[J].y; }
-      }
-      fast = __all(fminf(fminf(egn2.x, egn2.y), fminf(eo.x, eo.y)) >= kFastMin) != 0;
-      if (I == 0 && hf == 0) *reinterpret_cast<float2*>(&L.egn[c0]) = egn2;
-      // 1 / |k| of the lane's tokens from the two channel halves' partial sums (E1),
-      // folded into the operands
-      float rkt[8];
-      if (a.l2norm) {
-        const float4 a0 = ldf4(&nk[0][tk0]), a1 = ldf4(&nk[0][tk0 + 4]);
-        const float4 b0 = ldf4(&nk[1][tk0]), b1 = ldf4(&nk[1][tk0 + 4]);
-        const float ss[8] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w,
-                             a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rkt[i] = __builtin_amdgcn_rsqf(ss[i] + kL2Eps);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rkt[i] = 1.f;
-      }
-      auto put = [&](int i, float fr0, float fr1, float fc0, float fc1) {
-        const int tk = tk0 + i;
-        const float k0 = bf_lo(kx[i]) * rkt[i], k1 = bf_hi(kx[i]) * rkt[i];
-        *reinterpret_cast<uint32_t*>(&L.kr[rk(tk, p0)]) = pack_bf16x2(k0 * fr0, k1 * fr1);
-        *reinterpret_cast<uint32_t*>(&L.kc[rk(tk, p0)]) = pack_bf16x2(k0 * fc0, k1 * fc1);
-      };
-      if (fast) {
-        // prefix products e^{g_t}, suffix products e^{g_n - g_t} / e^{g_n}
-        float f0 = before.x * (hf ? h0w.x : 1.f), f1 = before.y * (hf ? h0w.y : 1.f);
-        float b0 = (after.x * (hf ? 1.f : h1w.x)) * __builtin_amdgcn_rcpf(egn2.x);
-        float b1 = (after.y * (hf ? 1.f : h1w.y)) * __builtin_amdgcn_rcpf(egn2.y);
-        float fr0[8], fr1[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          f0 *= al[i].x; f1 *= al[i].y;
-          fr0[i] = f0; fr1[i] = f1;
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rt + 4 * q4 + r, col = col0 + 16 * ct + l16;
+          S[rt][ct][r] = 0.f;
+          M[rt][ct][r] = row == col ? 1.f : 0.f;
         }
-#pragma unroll
-        for (int i = 7; i >= 0; --i) {
-          put(i, fr0[i], fr1[i], b0, b1);
-          if (i > 0) { b0 *= al[i].x; b1 *= al[i].y; }
-        }
-      } else {
-        // blocked: reference m_I = g at the block's token 7
-        float r0 = 1.f, r1 = 1.f;
-        if (hf == 1) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            r0 *= al[i].x; r1 *= al[i].y;
-            put(i, r0, r1, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1));
-          }
-        } else {
-#pragma unroll
-          for (int i = 7; i >= 0; --i) {
-            put(i, __builtin_amdgcn_rcpf(r0), __builtin_amdgcn_rcpf(r1), r0, r1);
-            r0 *= al[i].x; r1 *= al[i].y;
-          }
-        }
+    uint2 vr[8];
+    for (int64_t t = 0; t <= nch; ++t) {
+      const int64_t cc = c_begin + t - 1;
+      const PcStage& sc = L.st[cc & 1];
+      // the stage's vote, read from LDS: made wave-uniform so that the factorisation choice stays a
+      // branch (a value the compiler takes as divergent would run both paths)
+      const bool cf = t > 0 && __builtin_amdgcn_readfirstlane(sc.fast) != 0;
+      if (t > 0) {
+        f32x4 U[4][2];
+        c_solve(sc, L.at, L.vs, cf, S, col0, U, l16, q4);
+        c_update(sc, cf, S, U, l16, q4);
       }
-    }
-    uint4 vx[4];
-    if (!mkind) load_v(a, sv.row0 + t0, h, n, col0, lane_c, vx);
-    lds_barrier();   // C
-
-    // ---- M1T: A blocks, diagonal inverses ------------------------------------------------
-    {
-      uint4 cA[4], rA[4], sc[4];
-      // waves 4-7: diagonal block I = wave - 4 and its inverse; waves 0-3: the blocks below
-      // the diagonal (wave 0: A10 A32, wave 1: A20, wave 2: A30 A21, wave 3: A31)
-      if (wave >= 4) {
-        const int I = wave - 4;
-        tile_frags(L.kc, I, cA, l16, q4);
-        tile_frags(L.kr, I, rA, l16, q4);
-        __builtin_amdgcn_s_setprio(3);
-        epi_a(L, I, I, mma4(rA, cA), l16, q4);
-        invert_diag(L, I, l16, q4 == 0);
-        __builtin_amdgcn_s_setprio(0);
-      } else {
-        auto below = [&](int I, int J) {
-          tile_frags(L.kc, J, cA, l16, q4);
-          pair_frags(L, fast, I, J, cA, sc, q4);
-          tile_frags(L.kr, I, rA, l16, q4);
-          epi_a(L, I, J, mma4(rA, sc), l16, q4);
-        };
-        if (wave == 0) {
-          below(1, 0);
-          below(3, 2);
-        } else if (wave == 1) {
-          below(2, 0);
-        } else if (wave == 2) {
-          below(3, 0);
-          below(2, 1);
-        } else {
-          below(3, 1);
-        }
+      if (t < nch) c_issue_v(a, sv, h, cc + 1, cw, lane, vr);   // staged in phase 3
+      lds_barrier();
+      if (t > 0) {
+        f32x4 U[4][2];
+        c_solve(sc, L.at, nullptr, cf, M, col0, U, l16, q4);
+        c_update(sc, cf, M, U, l16, q4);
       }
+      lds_barrier();
+      if (t < nch) c_stage_v(L.vs, vr, cw, lane);   // read in the next tick's phase 1
+      lds_barrier();
     }
-    lds_barrier();   // D
-
-    // ---- X: W channel tile w (into kr); U~ for the S columns ----------------------------
-    f32x4 Ut[4][2];
-    {
-      uint2 af[10];
-      load_t_frags(L, af, l16, q4);
-      w_tile(L, fast, wave, af, l16, q4);
-      if (!mkind) {
-        stage_v(L, col0, vx, lane_c);
-        u_tiles(L, col0, af, Ut, l16, q4);
-      } else {
-#pragma unroll
-        for (int I2 = 0; I2 < 4; ++I2)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) Ut[I2][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    lds_barrier();   // E
-
-    // ---- S: U = U~ - W S (M: U = -W M), state update ------------------------------------
-    if (c + 1 < c_end) issue(c + 1, nxt, lane_c);
-    {
-      uint4 Sf[4][2];
-      pack_state(S, Sf);
-      minus_ws(L, Sf, Ut, l16, q4);
-    }
-    update_state(L, fast, S, Ut, l16, q4);
-    lds_barrier();   // F
-
-    if (--to_boundary == 0) {
-      to_boundary = a.Lo;
-      const int e = e_next++;   // the entry of this output-segment boundary
-      // M: the chunk's kr and kc are free until the next chunk's barrier B
-      if (mkind)
-        store_mfrag(S, reinterpret_cast<uint4*>(sv.ws + (sv.E + e) * D * D), wave & 3, lane_c,
-                    L.kr + (wave - 4) * kMsWave);
-      else
-        store_tiles(S, sv.ws + e * D * D, wave & 3, lane_c);
+    lds_barrier();   // every wave is past its last LDS read: the stages are scratch now
+    if (nch > 0) {
+      // the segment's state and transition (entry e = p); M through this wave's LDS scratch
+      store_tiles(S, sv.ws + p * D * D, cw, lane);
+      store_mfrag(M, reinterpret_cast<uint4*>(sv.ws + (sv.E + p) * D * D), cw, lane,
+                  reinterpret_cast<uint16_t*>(lds_raw) + cw * kMsWave);
     }
   }
 }
@@ -1531,11 +1357,11 @@ struct Plan {
 };
 
 // Estimated time of the two passes for a segment length Lo, in chunk steps of an output block
-// (two per CU, about kTargetBlocks at once): the longest block or the total work spread over
-// the chip, whichever is larger; a summary block (one per CU, about 0.55 of an output block's
-// time per chunk) covers up to kSub * Lo chunks. For a batch of equal sequences the smallest
-// Lo that gives about kTargetBlocks output blocks is always best; for packed samples of mixed
-// lengths a shorter Lo can spread the few long samples' summaries over more blocks.
+// (one per CU, about kTargetBlocks at once): the longest block or the total work spread over
+// the chip, whichever is larger; a summary block (also one per CU) moves about 0.6 of an output
+// block's bytes per chunk and covers up to kSub * Lo chunks. For a batch of equal sequences the
+// smallest Lo that gives about kTargetBlocks output blocks is always best; for packed samples
+// of mixed lengths a shorter Lo can spread the few long samples' summaries over more blocks.
 double plan_cost(const KdaRun* runs, int64_t nruns, int64_t H, int64_t Lo) {
   double w_out = 0, w_sum = 0, max_out = 0, max_sum = 0;
   for (int64_t r = 0; r < nruns; ++r) {
@@ -1548,7 +1374,7 @@ double plan_cost(const KdaRun* runs, int64_t nruns, int64_t H, int64_t Lo) {
       max_sum = std::max(max_sum, (double)std::min((P - 1) * Lo, (int64_t)kSub * Lo));
     }
   }
-  return std::max(max_out, w_out / kTargetBlocks) + 0.55 * std::max(max_sum, w_sum / (kTargetBlocks / 2));
+  return std::max(max_out, w_out / kTargetBlocks) + 0.6 * std::max(max_sum, w_sum / kTargetBlocks);
 }
 
 Plan make_plan(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
@@ -1662,7 +1488,7 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
   a.Lo = pl.Lo;
   a.l2norm = x.l2norm ? 1 : 0;
   a.xcd_ranges = pl.desc.size() == 1 ? 1 : 0;   // blocks of unequal length: the hardware's round robin
-  const size_t lds = sizeof(Lds), lds_sum = sizeof(Lds) + 2 * CT * sizeof(float);
+  const size_t lds = sizeof(PcLdsOut), lds_sum = sizeof(PcLdsSum);
   int dev = 0;
   hipError_t de = hipGetDevice(&dev);
   if (de != hipSuccess) return de;
@@ -1702,7 +1528,7 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
       ChunkArgs s = a;
       s.nblk = (int)sum0;
       s.grid = round8(sum0);
-      hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(2 * NTHR), lds_sum, stream, s);
+      hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(kPcThreads), lds_sum, stream, s);
       hipError_t e = hipGetLastError();
       if (e == hipSuccess) e = mark_after(marks, "kda_sum_kernel", stream);
       if (e != hipSuccess) return e;
@@ -1717,9 +1543,9 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
     a.nblk = (int)out0;
     a.grid = round8(out0);
     if (fuse_gate)
-      hipLaunchKernelGGL(kda_out_kernel<true>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
+      hipLaunchKernelGGL(kda_out_kernel<true>, dim3((unsigned)a.grid), dim3(kPcThreads), lds, stream, a);
     else
-      hipLaunchKernelGGL(kda_out_kernel<false>, dim3((unsigned)a.grid), dim3(NTHR), lds, stream, a);
+      hipLaunchKernelGGL(kda_out_kernel<false>, dim3((unsigned)a.grid), dim3(kPcThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark_after(marks, fuse_gate ? "kda_out_gated_kernel" : "kda_out_kernel", stream);
     if (e != hipSuccess) return e;
