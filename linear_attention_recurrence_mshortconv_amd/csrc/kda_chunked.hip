@@ -365,7 +365,8 @@ __device__ __forceinline__ void store_mfrag(const f32x4 (&S)[8][2], uint4* m, in
 //   qw:     [CT][D] row-major, row stride D + 8 elements (272 bytes)
 //   at, aqk: [CT][CT] column-major, stride CT + 4 elements
 struct PcStage {
-  uint16_t kr[CT * RKS];  // K^ = k e^{g} / |k| (fast) or k e^{g - m_I} / |k| (blocked)
+  uint16_t kr[CT * RKS];  // -K^, K^ = k e^{g} / |k| (fast) or k e^{g - m_I} / |k| (blocked), negated so that
+                          // the consumers' K^ S products accumulate V - K^ S directly
   uint16_t kc[CT * RKS];  // K_ = k e^{-g} / |k| (fast) or k e^{m_I - g} / |k| (blocked)
   float beta[CT];
   float egn[D];           // e^{g_n}: decay of each key channel over the whole chunk
@@ -447,9 +448,9 @@ __device__ __forceinline__ f32x4 mma4(const uint4 (&ra)[4], const uint4 (&cb)[4]
   for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
   return acc;
 }
-// A(I, J) = diag(b) (K^ K_^T)(I, J) (the operands carry 1 / |k|): below the diagonal -> at
-// (negated, column-major: a lane's four rows are one 8-byte write), on it (strictly lower
-// part) -> adiag in fp32
+// A(I, J) = diag(b) (K^ K_^T)(I, J) from acc = ((-K^) K_^T)(I, J) (the operands carry 1 / |k|):
+// below the diagonal -> at (negated, column-major: a lane's four rows are one 8-byte write), on
+// it (strictly lower part) -> adiag in fp32
 __device__ __forceinline__ void epi_a(uint16_t* at, float* adiag, const float* beta, int I, int J, f32x4 acc, int l16,
                                       int q4) {
   const int j = SBT * J + l16;
@@ -457,10 +458,10 @@ __device__ __forceinline__ void epi_a(uint16_t* at, float* adiag, const float* b
   const float rowf[4] = {b4.x, b4.y, b4.z, b4.w};
   if (I == J) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? rowf[r] * acc[r] : 0.f;
+    for (int r = 0; r < 4; ++r) adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? -rowf[r] * acc[r] : 0.f;
   } else {
     *reinterpret_cast<uint2*>(&at[tr(j, SBT * I + 4 * q4)]) =
-        pack4(make_float4(-rowf[0] * acc[0], -rowf[1] * acc[1], -rowf[2] * acc[2], -rowf[3] * acc[3]));
+        pack4(make_float4(rowf[0] * acc[0], rowf[1] * acc[1], rowf[2] * acc[2], rowf[3] * acc[3]));
   }
 }
 // Aqk(I, J) = (Q^ K_^T)(I, J) (the operands carry 1 / |q| and 1 / |k|), lower triangle
@@ -535,31 +536,43 @@ struct PLoad {
 // Buffer loads of chunk c: block-uniform base and bounds (the chunk's first n tokens); reads
 // past the bound return zero, which is k = q = beta = 0 for tokens past the end (alpha is set
 // to 1 for them when it is used).
-template <bool HASQ>
-__device__ __forceinline__ void p_issue(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c, int wave,
-                                        int lane, PLoad& R) {
+// alpha and beta of chunk c (needed first, in phase 1; issued as soon as phase 1 has used the
+// previous chunk's)
+__device__ __forceinline__ void p_issue_a(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c, int wave,
+                                          int lane, PLoad& R) {
   const int hf = lane >> 5, c0 = 4 * (lane & 31);
   const int64_t t0 = c * CT;
   const int n = (int)min<int64_t>(CT, sv.T - t0);
   const int64_t row0 = sv.row0 + t0;
-  const int st2 = (int)a.stride * 2, sa2 = (int)(a.H * D) * 2;
-  const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
+  const int sa2 = (int)(a.H * D) * 2;
   const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
-  const int vk = (8 * hf) * st2 + 2 * c0, va = (8 * hf) * sa2 + 2 * c0;
+  const int va = (8 * hf) * sa2 + 2 * c0;
   const int tb = SBT * wave;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    R.k[i] = ld_buf64(rk_, vk, (tb + i) * st2);
-    R.a[i] = ld_buf64(ra_, va, (tb + i) * sa2);
+  for (int i = 0; i < 8; ++i) R.a[i] = ld_buf64(ra_, va, (tb + i) * sa2);
+  if (wave == 0) {
+    const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
+    R.bt = __builtin_amdgcn_raw_buffer_load_b16(rb_, lane * (int)a.H * 2, 0, 0);
   }
+}
+// k (and q) of chunk c (issued once phase 2 has used the previous chunk's)
+template <bool HASQ>
+__device__ __forceinline__ void p_issue_kq(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c, int wave,
+                                           int lane, PLoad& R) {
+  const int hf = lane >> 5, c0 = 4 * (lane & 31);
+  const int64_t t0 = c * CT;
+  const int n = (int)min<int64_t>(CT, sv.T - t0);
+  const int64_t row0 = sv.row0 + t0;
+  const int st2 = (int)a.stride * 2;
+  const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
+  const int vk = (8 * hf) * st2 + 2 * c0;
+  const int tb = SBT * wave;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) R.k[i] = ld_buf64(rk_, vk, (tb + i) * st2);
   if (HASQ) {
     const auto rq_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
 #pragma unroll
     for (int i = 0; i < 8; ++i) R.q[i] = ld_buf64(rq_, vk, (tb + i) * st2);
-  }
-  if (wave == 0) {
-    const auto rb_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.beta + row0 * a.H + h), 0, n * (int)a.H * 2, kRsrcW3);
-    R.bt = __builtin_amdgcn_raw_buffer_load_b16(rb_, lane * (int)a.H * 2, 0, 0);
   }
 }
 
@@ -640,7 +653,7 @@ __device__ __forceinline__ bool p_phase2(PcStage& st, uint16_t* qw, const float*
   auto put = [&](int i, float4 fr, float4 fc) {
     const int tk = tk0 + i;
     const float4 ks = mul4(unpack4(R.k[i]), make_float4(rkt[i], rkt[i], rkt[i], rkt[i]));
-    *reinterpret_cast<uint2*>(&st.kr[rk(tk, p0)]) = pack4(mul4(ks, fr));
+    *reinterpret_cast<uint2*>(&st.kr[rk(tk, p0)]) = pack4(mul4(ks, make_float4(-fr.x, -fr.y, -fr.z, -fr.w)));
     *reinterpret_cast<uint2*>(&st.kc[rk(tk, p0)]) = pack4(mul4(ks, fc));
     if (HASQ) {
       const float4 qs = mul4(unpack4(R.q[i]), make_float4(rqt[i], rqt[i], rqt[i], rqt[i]));
@@ -786,34 +799,37 @@ __device__ __forceinline__ void p_phase3_sum(const PcStage& st, uint16_t* at, fl
 // lane channels 4 (lane & 31) .. + 3 (one 256-byte token row per half-wave and load; tokens past
 // the end read 0). The consumers' MFMA layout would touch 16 token rows per load; instead the
 // rows go through LDS (c_stage_v) and come back in that layout with the transposing read.
+template <int ROWS>   // rows per consumer wave: cw takes rows ROWS cw .. ROWS cw + ROWS - 1
 __device__ __forceinline__ void c_issue_v(const ChunkArgs& a, const SeqView& sv, int64_t h, int64_t c, int cw,
-                                          int lane, uint2 (&vr)[8]) {
+                                          int lane, uint2 (&vr)[ROWS / 2]) {
   const int64_t t0 = c * CT;
   const int n = (int)min<int64_t>(CT, sv.T - t0);
   const int st2 = (int)a.stride * 2;
   const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (sv.row0 + t0) * a.stride + h * D), 0, n * st2,
                                                     kRsrcW3);
-  const int vo = (SBT * cw + (lane >> 5)) * st2 + 8 * (lane & 31);
+  const int vo = (ROWS * cw + (lane >> 5)) * st2 + 8 * (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) vr[i] = ld_buf64(rv, vo, 2 * i * st2);
+  for (int i = 0; i < ROWS / 2; ++i) vr[i] = ld_buf64(rv, vo, 2 * i * st2);
 }
 // the rows of c_issue_v -> vbuf ([CT][D], row stride RMS, natural channel order)
-__device__ __forceinline__ void c_stage_v(uint16_t* vbuf, const uint2 (&vr)[8], int cw, int lane) {
-  const int r0 = SBT * cw + (lane >> 5), c0 = 4 * (lane & 31);
+template <int ROWS>
+__device__ __forceinline__ void c_stage_v(uint16_t* vbuf, const uint2 (&vr)[ROWS / 2], int cw, int lane) {
+  const int r0 = ROWS * cw + (lane >> 5), c0 = 4 * (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint2*>(&vbuf[rm(r0 + 2 * i, c0)]) = vr[i];
+  for (int i = 0; i < ROWS / 2; ++i) *reinterpret_cast<uint2*>(&vbuf[rm(r0 + 2 * i, c0)]) = vr[i];
 }
 
 // U = (I + A)^{-1} diag(beta) (V - K^ X) for the wave's 32 columns (V = 0 without vbuf: the
 // transition's columns). V comes from its LDS staging in the D layout through the transposing
-// read; K^ X accumulates on top with -X as the B operand, one k slot of -X packed at a time.
+// read; (-K^) X accumulates on top (kr holds -K^), one k slot of X packed at a time.
+template <int NCT>   // column tiles of 16 (col0 + 16 ct)
 __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, const uint16_t* vbuf, bool fast,
-                                        const f32x4 (&X)[8][2], int col0, f32x4 (&U)[4][2], int l16, int q4) {
-  f32x4 acc[4][2];
+                                        const f32x4 (&X)[8][NCT], int col0, f32x4 (&U)[4][NCT], int l16, int q4) {
+  f32x4 acc[4][NCT];
 #pragma unroll
   for (int I = 0; I < 4; ++I)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       if (vbuf != nullptr) {
         // lane (l16, q4) receives rows 16 I + 4 q4 + 0..3 of column col0 + 16 ct + l16
         const float4 vv = unpack4(ld_tr(&vbuf[rm(SBT * I + 4 * q4 + (l16 >> 2), col0 + 16 * ct + 4 * (l16 & 3))]));
@@ -824,22 +840,22 @@ __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, c
     }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    uint4 xs[2];
+    uint4 xs[NCT];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) xs[ct] = pack8(-X[2 * s][ct], -X[2 * s + 1][ct]);
+    for (int ct = 0; ct < NCT; ++ct) xs[ct] = pack8(X[2 * s][ct], X[2 * s + 1][ct]);
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       uint4 kf = ld128(st.kr, (SBT * I + l16) * RKS + 32 * s + 8 * q4);
       if (!fast) kf = scale8(kf, em_of(st, I, 32 * s + 4 * q4), em_of(st, I, 32 * s + 16 + 4 * q4));
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) acc[I][ct] = mma32(kf, xs[ct], acc[I][ct]);
+      for (int ct = 0; ct < NCT; ++ct) acc[I][ct] = mma32(kf, xs[ct], acc[I][ct]);
     }
   }
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
     const float4 b4 = ldf4(&st.beta[SBT * I + 4 * q4]);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
       acc[I][ct][0] *= b4.x; acc[I][ct][1] *= b4.y;
       acc[I][ct][2] *= b4.z; acc[I][ct][3] *= b4.w;
     }
@@ -847,7 +863,7 @@ __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, c
   uint2 af[10];
   load_t_frags(at, af, l16, q4);
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < NCT; ++ct) {
     const f32x4 y0[4] = {acc[0][ct], acc[1][ct], acc[2][ct], acc[3][ct]};
     f32x4 Xo[4];
     block_solve(af, y0, Xo);
@@ -857,13 +873,14 @@ __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, c
 }
 
 // X <- Diag(e^{g_n}) X + K~^T U, K~ = (K / |k|) e^{g_n - g} read transposed from kc
-__device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X)[8][2], const f32x4 (&U)[4][2],
+template <int NCT>
+__device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X)[8][NCT], const f32x4 (&U)[4][NCT],
                                          int l16, int q4) {
-  uint4 Upf[2][2];
+  uint4 Upf[2][NCT];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) Upf[s][ct] = pack8(U[2 * s][ct], U[2 * s + 1][ct]);
+    for (int ct = 0; ct < NCT; ++ct) Upf[s][ct] = pack8(U[2 * s][ct], U[2 * s + 1][ct]);
   // A operand K~^T: lane (l16, q4) = channel 16 rt + l16, tokens 32 s + 4 q4 + 0..3 and
   // 32 s + 16 + 4 q4 + 0..3
   const int kbase = rk(4 * q4 + (l16 >> 2), 8 * (l16 & 3));
@@ -877,7 +894,7 @@ __device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X
     const float4 eg = ldf4(&st.egn[16 * rt + 4 * q4]);
     if (fast) {   // K~ = K_ e^{g_n}: the factor is a row scaling of the product
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = X[rt][ct];
         acc = mma32(kt[0], Upf[0][ct], acc);
         acc = mma32(kt[1], Upf[1][ct], acc);
@@ -892,7 +909,7 @@ __device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X
         kt[s] = scale8(kt[s], make_float4(f0, f0, f0, f0), make_float4(f1, f1, f1, f1));
       }
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = X[rt][ct];
         acc[0] *= eg.x; acc[1] *= eg.y; acc[2] *= eg.z; acc[3] *= eg.w;
         acc = mma32(kt[0], Upf[0][ct], acc);
@@ -1043,18 +1060,26 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
 
   if (wave < 4) {
     // ---------------- producers ----------------
+    // the next chunk's alpha and beta go out once phase 1 has used this chunk's, its k and q once
+    // phase 2 has
     PLoad R;
     float4 al[8];
     bool fast = true;
-    if (nch > 0) p_issue<true>(a, sv, h, c_begin, wave, lane, R);
+    if (nch > 0) {
+      p_issue_a(a, sv, h, c_begin, wave, lane, R);
+      p_issue_kq<true>(a, sv, h, c_begin, wave, lane, R);
+    }
     for (int64_t t = 0; t <= nch; ++t) {
       const int64_t cp = c_begin + t;
       PcStage& sp = L.st[cp & 1];
-      if (t < nch) p_phase1<true>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
+      if (t < nch) {
+        p_phase1<true>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
+        if (t + 1 < nch) p_issue_a(a, sv, h, cp + 1, wave, lane, R);
+      }
       lds_barrier();
       if (t < nch) {
         fast = p_phase2<true>(sp, L.qw[cp & 1], L.rk, L.rq, R, al, wave, lane);
-        if (t + 1 < nch) p_issue<true>(a, sv, h, cp + 1, wave, lane, R);
+        if (t + 1 < nch) p_issue_kq<true>(a, sv, h, cp + 1, wave, lane, R);
       }
       lds_barrier();
       if (t < nch) p_phase3_out(sp, L.qw[cp & 1], L.at, L.aqk, L.adiag, fast, wave, lane);
@@ -1097,9 +1122,9 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       if (GATED && t > 1) c_store_rows(a, sv, h, cc - 1, L.st[(cc - 1) & 1].kr, cw, lane);
       if (t > 0) {
         if (GATED) c_issue_gate(a, sv, h, cc, col0, lane, gx);
-        c_solve(sc, L.at, L.qw[(cc + 1) & 1], cf, S, col0, U, l16, q4);
+        c_solve<2>(sc, L.at, L.qw[(cc + 1) & 1], cf, S, col0, U, l16, q4);
       }
-      if (t < nch) c_issue_v(a, sv, h, cc + 1, cw, lane, vr);   // staged in phase 3
+      if (t < nch) c_issue_v<16>(a, sv, h, cc + 1, cw, lane, vr);   // staged in phase 3
       lds_barrier();
       // ---- phase 2: the output
       if (t > 0) {
@@ -1126,7 +1151,7 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       // ---- phase 3: the state update; the output rows go out (gated: normalised, staged)
       if (t > 0) {
         if (!GATED) c_store_rows(a, sv, h, cc, L.st[cc & 1].kr, cw, lane);
-        c_update(sc, cf, S, U, l16, q4);
+        c_update<2>(sc, cf, S, U, l16, q4);
         if (GATED) {
           auto sig = [](float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); };
 #pragma unroll
@@ -1148,7 +1173,7 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       }
       // v of the next chunk into this chunk's qw (its Q^ was used in phase 2): read in the next
       // tick's phase 1, before the producers' Q^ of the chunk after goes there
-      if (t < nch) c_stage_v(L.qw[cc & 1], vr, cw, lane);
+      if (t < nch) c_stage_v<16>(L.qw[cc & 1], vr, cw, lane);
       lds_barrier();
     }
     if (GATED && nch > 0) c_store_rows(a, sv, h, c_end - 1, L.st[(c_end - 1) & 1].kr, cw, lane);
@@ -1157,12 +1182,15 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
 }
 
 // ---- summary pass --------------------------------------------------------------------
-// One block per (sequence, head, summary segment): waves 0-3 produce as in the output pass
-// (no q), waves 4-7 consume; wave 4 + j runs both the state S from 0 and the transition M from I
-// on columns 32 j .. 32 j + 31 (phase 1: S, phase 2: M; phase 3 idle while the producers form
-// A and the inverses). At the segment end S goes to the workspace tile-major and M as split
-// bf16 A fragments.
-__global__ __launch_bounds__(kPcThreads) void kda_sum_kernel(ChunkArgs a) {
+// One block of 12 waves per (sequence, head, summary segment): waves 0-3 produce as in the output
+// pass (no q); waves 4-11 consume, wave 4 + j holding columns 16 j .. 16 j + 15 both of the state
+// S (from 0) and of the transition M (from I). Phase 1 solves for U of the S tile and updates it,
+// phase 2 solves for U of the M tile, phase 3 updates M (the stage's kc and egn stay until the
+// next tick) and stages the next chunk's v, so that each SIMD's two consumer waves interleave
+// their chains with the producer's work. At the segment end S goes to the workspace tile-major and M, through
+// LDS, as split bf16 A fragments.
+constexpr int kPcSumThreads = 768;
+__global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   PcLdsSum& L = *reinterpret_cast<PcLdsSum*>(lds_raw);
 
@@ -1171,7 +1199,6 @@ __global__ __launch_bounds__(kPcThreads) void kda_sum_kernel(ChunkArgs a) {
   if (lid >= (uint32_t)a.nblk) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
-  const int cw = wave & 3, col0 = 32 * cw;
   const int l16 = lane & 15, q4 = lane >> 4;
   const SeqDesc& rd = a.run[run_of<1>(a, lid)];
   const int32_t local = (int32_t)lid - rd.sum0;
@@ -1183,41 +1210,52 @@ __global__ __launch_bounds__(kPcThreads) void kda_sum_kernel(ChunkArgs a) {
   const int64_t c_begin = (int64_t)p * a.Lo;
   const int64_t c_end = min<int64_t>(NC, c_begin + a.Lo);   // summary segments are output segments 0 .. P - 2
   const int64_t nch = c_end - c_begin;
+  // M staging for the fragment store at the end: bf16 high and low parts, [D][D + 8] each
+  constexpr int kMP = D + 8;
+  uint16_t* mhi = reinterpret_cast<uint16_t*>(lds_raw);
+  uint16_t* mlo = mhi + D * kMP;
+  static_assert(2 * D * kMP * sizeof(uint16_t) <= sizeof(PcLdsSum), "M staging fits the summary LDS");
 
   if (wave < 4) {
     // ---------------- producers ----------------
-    PLoad R;
+    PLoad R;   // loads issued as in the output pass
     float4 al[8];
     bool fast = true;
-    if (nch > 0) p_issue<false>(a, sv, h, c_begin, wave, lane, R);
+    if (nch > 0) {
+      p_issue_a(a, sv, h, c_begin, wave, lane, R);
+      p_issue_kq<false>(a, sv, h, c_begin, wave, lane, R);
+    }
     for (int64_t t = 0; t <= nch; ++t) {
       const int64_t cp = c_begin + t;
       PcStage& sp = L.st[cp & 1];
-      if (t < nch) p_phase1<false>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
+      if (t < nch) {
+        p_phase1<false>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
+        if (t + 1 < nch) p_issue_a(a, sv, h, cp + 1, wave, lane, R);
+      }
       lds_barrier();
       if (t < nch) {
         fast = p_phase2<false>(sp, nullptr, L.rk, L.rq, R, al, wave, lane);
-        if (t + 1 < nch) p_issue<false>(a, sv, h, cp + 1, wave, lane, R);
+        if (t + 1 < nch) p_issue_kq<false>(a, sv, h, cp + 1, wave, lane, R);
       }
       lds_barrier();
       if (t < nch) p_phase3_sum(sp, L.at, L.adiag, fast, wave, lane);
       lds_barrier();
     }
-    lds_barrier();   // (the consumers' scratch below)
+    lds_barrier();   // (the consumers' M staging below)
+    lds_barrier();
   } else {
     // ---------------- consumers ----------------
-    f32x4 S[8][2], M[8][2];
+    const int j = wave - 4, col0 = 16 * j;
+    f32x4 S[8][1], M[8][1];
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + 4 * q4 + r, col = col0 + 16 * ct + l16;
-          S[rt][ct][r] = 0.f;
-          M[rt][ct][r] = row == col ? 1.f : 0.f;
-        }
-    uint2 vr[8];
+      for (int r = 0; r < 4; ++r) {
+        S[rt][0][r] = 0.f;
+        M[rt][0][r] = 16 * rt + 4 * q4 + r == col0 + l16 ? 1.f : 0.f;
+      }
+    uint2 vr[4];
+    f32x4 UM[4][1];
     for (int64_t t = 0; t <= nch; ++t) {
       const int64_t cc = c_begin + t - 1;
       const PcStage& sc = L.st[cc & 1];
@@ -1225,27 +1263,52 @@ __global__ __launch_bounds__(kPcThreads) void kda_sum_kernel(ChunkArgs a) {
       // branch (a value the compiler takes as divergent would run both paths)
       const bool cf = t > 0 && __builtin_amdgcn_readfirstlane(sc.fast) != 0;
       if (t > 0) {
-        f32x4 U[4][2];
-        c_solve(sc, L.at, L.vs, cf, S, col0, U, l16, q4);
-        c_update(sc, cf, S, U, l16, q4);
-      }
-      if (t < nch) c_issue_v(a, sv, h, cc + 1, cw, lane, vr);   // staged in phase 3
-      lds_barrier();
-      if (t > 0) {
-        f32x4 U[4][2];
-        c_solve(sc, L.at, nullptr, cf, M, col0, U, l16, q4);
-        c_update(sc, cf, M, U, l16, q4);
+        f32x4 US[4][1];
+        c_solve<1>(sc, L.at, L.vs, cf, S, col0, US, l16, q4);
+        c_update<1>(sc, cf, S, US, l16, q4);
       }
       lds_barrier();
-      if (t < nch) c_stage_v(L.vs, vr, cw, lane);   // read in the next tick's phase 1
+      if (t > 0) c_solve<1>(sc, L.at, nullptr, cf, M, col0, UM, l16, q4);
+      if (t < nch) c_issue_v<8>(a, sv, h, cc + 1, j, lane, vr);   // staged in phase 3
+      lds_barrier();
+      if (t > 0) c_update<1>(sc, cf, M, UM, l16, q4);   // kc and egn of the stage stay until the next tick
+      if (t < nch) c_stage_v<8>(L.vs, vr, j, lane);     // read in the next tick's phase 1
       lds_barrier();
     }
-    lds_barrier();   // every wave is past its last LDS read: the stages are scratch now
+    lds_barrier();   // every wave is past its last LDS read: the LDS is scratch now
     if (nch > 0) {
-      // the segment's state and transition (entry e = p); M through this wave's LDS scratch
-      store_tiles(S, sv.ws + p * D * D, cw, lane);
-      store_mfrag(M, reinterpret_cast<uint4*>(sv.ws + (sv.E + p) * D * D), cw, lane,
-                  reinterpret_cast<uint16_t*>(lds_raw) + cw * kMsWave);
+      // S: the tile (rows, columns 16 j ..) goes out tile-major
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+        *reinterpret_cast<f32x4*>(sv.ws + p * D * D + tile_off(j >> 1, rt, j & 1, lane)) = S[rt][0];
+      // M: split into bf16 high and low parts, staged row-major
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = M[rt][0][r];
+          const uint16_t hb = f2bf(x);
+          const int o = (16 * rt + 4 * q4 + r) * kMP + col0 + l16;
+          mhi[o] = hb;
+          mlo[o] = f2bf(x - bf2f(hb));
+        }
+    }
+    lds_barrier();
+    if (nch > 0) {
+      // M as A fragments: wave j forms row tile j of every k slot (row 16 j + l16, columns
+      // 32 s + 4 q4 .. + 3 and 32 s + 16 + 4 q4 .. + 3, the high part then the low part)
+      uint4* m = reinterpret_cast<uint4*>(sv.ws + (sv.E + p) * D * D);
+      const int row = (SBT * j + l16) * kMP;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int c0 = 32 * s4 + 4 * q4;
+        const uint2 h0 = *reinterpret_cast<const uint2*>(&mhi[row + c0]);
+        const uint2 h1 = *reinterpret_cast<const uint2*>(&mhi[row + c0 + 16]);
+        const uint2 l0 = *reinterpret_cast<const uint2*>(&mlo[row + c0]);
+        const uint2 l1 = *reinterpret_cast<const uint2*>(&mlo[row + c0 + 16]);
+        m[mfrag_off(j, s4, lane)] = cat(h0, h1);
+        m[mfrag_off(j, s4, lane) + 1] = cat(l0, l1);
+      }
     }
   }
 }
@@ -1528,7 +1591,7 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
       ChunkArgs s = a;
       s.nblk = (int)sum0;
       s.grid = round8(sum0);
-      hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(kPcThreads), lds_sum, stream, s);
+      hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(kPcSumThreads), lds_sum, stream, s);
       hipError_t e = hipGetLastError();
       if (e == hipSuccess) e = mark_after(marks, "kda_sum_kernel", stream);
       if (e != hipSuccess) return e;
