@@ -31,6 +31,16 @@ def assert_close(got, want, dtype: str, what: str = ""):
     return r
 
 
+def assert_rel_l2(got, want, dtype: str, what: str = ""):
+    """The rel-L2 part of assert_close only, for outputs whose every element is already held
+    to an error bound of its own (a max-abs figure does not scale with the output's size:
+    one bf16 rounding of a value above 16 may move it by more than 5e-2)."""
+    r = rel_l2(got, want)
+    tol = TOL_F32_REL_L2 if dtype == "f32" else TOL_BF16_REL_L2
+    assert r <= tol, f"{what}: rel-L2 {r:.3e} > {tol}"
+    return r
+
+
 def to_device(a: np.ndarray, dtype: str, device="cuda"):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))

@@ -201,11 +201,12 @@ def test_kda_chunked_split_invariance(chm):
 @pytest.mark.parametrize("wi", [1, 2, 3, 4])
 def test_pipeline_full_workload_sampled_heads(chm, wi):
     """conv then chunked KDA at full size in the bench's launch configuration;
-    the oracle recomputes whole heads (every token) for a sample of heads."""
+    the oracle recomputes whole heads (every token) for the first, a middle and the last head
+    (the first and last at the 255K-token video)."""
     import torch
     w = wl.WORKLOADS[wi]
     inp = wl.make_inputs(w)
-    heads = [0] if wi == 4 else [0, w.H - 1]
+    heads = [0, w.H - 1] if wi == 4 else [0, w.H // 2 - 1, w.H - 1]
     x_dev = to_device(inp["x"], "bf16")
     y = chm.mshortconv_fwd(x_dev, torch.from_numpy(inp["w_text"]), torch.from_numpy(inp["w_vis"]), inp["segments"])
     del x_dev
@@ -223,6 +224,24 @@ def test_pipeline_full_workload_sampled_heads(chm, wi):
                            inp["alpha"][:, :, heads], inp["beta"][:, :, heads], S0)
     assert_close(o_got, o_ref, "bf16", f"{w.name} o")
     assert_close(S_got, S_ref, "bf16", f"{w.name} S_final")
+
+
+def test_kda_chunked_matches_token_by_token(chm):
+    """The chunk-size invariance of the method on the GPU: the chunked MFMA path (64-token chunks, the
+    sequence cut into segments) and the token-by-token kernel (one token per step, fp32) on the same
+    bf16 inputs give the same o and S_final within the bf16 tolerance, and each is within it of the
+    oracle."""
+    rng = np.random.default_rng(21)
+    B, T, H, d = 2, 64 * 23 + 37, 4, 128
+    q, k, v, alpha, beta, S0 = _small_case(rng, B, T, H, d, s0=True)
+    o1, S1 = _gpu_kda(chm, q, k, v, alpha, beta, S0)
+    o2, S2 = _gpu_kda(chm, q, k, v, alpha, beta, S0, sequential=True)
+    assert_close(to_host(o1), to_host(o2), "bf16", "o chunked vs token-by-token")
+    assert_close(to_host(S1), to_host(S2), "bf16", "S_final chunked vs token-by-token")
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    for o, S, name in ((o1, S1, "chunked"), (o2, S2, "token-by-token")):
+        assert_close(to_host(o), o_ref, "bf16", f"{name} o")
+        assert_close(to_host(S), S_ref, "bf16", f"{name} S_final")
 
 
 def test_timed_variants_match_untimed(chm):
