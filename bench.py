@@ -25,8 +25,8 @@ image_1024, video_5s, video_30s) are measured the same way with --workload.
 chimera_kda_bwd (writing dq, dk, dv straight into one fused q|k|v gradient) and
 chimera_mshortconv_bwd on it, against a synthetic dL/do; each call is bracketed
 by HIP events on the stream. --fused times chimera_kda_fwd_conv (the conv computed
-inside the token-by-token recurrence, q|k|v never stored) beside the same step as
-two calls on the same recurrence kernel.
+in the recurrence's load stage, q|k|v never stored; the chunked kernels for bf16
+d = 128) beside the product's two calls (the conv, then the recurrence).
 
 Two helper modes turn rocprofv3 output into the summaries kept with the code:
   python bench.py --summarize-stats <kernel_stats.csv>
@@ -145,8 +145,8 @@ def _args():
     ap.add_argument("--backward", action="store_true",
                     help="a training step: forward, then the KDA and conv backward (gradients of a synthetic dL/do)")
     ap.add_argument("--fused", action="store_true",
-                    help="the conv fused into the token-by-token recurrence (chimera_kda_fwd_conv), against the "
-                         "two calls on the same recurrence kernel")
+                    help="the conv fused into the recurrence's load stage (chimera_kda_fwd_conv), against the "
+                         "two calls (conv, then the recurrence)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=20736,
                     help="tokens per sequence in the oracle's timed sample (text + whole grid rows/frames)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
@@ -509,9 +509,10 @@ def bench_backward(args, w):
 
 
 def bench_fused(args, w):
-    """The fused conv + recurrence (one kernel, q|k|v never stored) on the workload, timed with HIP
-    events around each call on the stream; beside it the same step as two calls (conv, then the
-    token-by-token recurrence on the stored q|k|v)."""
+    """The fused conv + recurrence (chimera_kda_fwd_conv: q|k|v computed in the recurrence's load
+    stage, never stored) on the workload, timed with HIP events on the stream, each kernel marked;
+    beside it the product's two calls (the conv, then the recurrence on the stored q|k|v) on the
+    same inputs."""
     import torch
     import workloads as wl
     import linear_attention_recurrence_mshortconv_amd as chm
@@ -526,36 +527,55 @@ def bench_fused(args, w):
     S0 = None if inp["S0"] is None else torch.from_numpy(inp["S0"]).to(dev)
     wt, wv = torch.from_numpy(inp["w_text"]).to(dev), torch.from_numpy(inp["w_vis"]).to(dev)
     segs = w.segments
-    y = torch.empty_like(x)
-    q, k, v = chm.split_qkv(y, H, d)
     o = torch.empty(B, T, H, d, dtype=tdt, device=dev)
     s_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    dt = chm.BF16 if w.dtype == "bf16" else chm.F32
+    need_f = chm.kda_conv_workspace_size(segs, B, T, H, d, d, dt, chm.KDA_L2NORM_QK)
+    ws_f = torch.empty(max(need_f, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def fused():
-        chm.kda_fwd_conv(x, wt, wv, segs, alpha, beta, S0, H=H, dk=d, dv=d, out=o, state_out=s_final)
+    def fused(m=None):
+        chm.kda_fwd_conv(x, wt, wv, segs, alpha, beta, S0, H=H, dk=d, dv=d, out=o, state_out=s_final,
+                         workspace=ws_f, marks=m)
 
-    def two_calls():
-        chm.mshortconv_fwd(x, wt, wv, segs, out=y)
-        chm.kda_fwd(q, k, v, alpha, beta, S0, sequential=True, out=o, state_out=s_final)
-
-    def timed(fn):
+    def timed(fn, cap):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for e0, e1 in evs:
-            e0.record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
             fn()
-            e1.record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        return sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+        ms = e0.elapsed_time(e1) / args.steps
+        marks = [chm.Marks(cap) for _ in range(args.steps)]
+        for m in marks:
+            fn(m)
+        torch.cuda.synchronize()
+        per = {}
+        for m in marks:
+            for name, t in m.kernels():
+                per.setdefault(name, []).append(t)
+        return ms, {n: sum(v) / len(v) for n, v in per.items()}
 
-    ms_fused = timed(fused)
-    ms_two = timed(two_calls)
+    ms_fused, k_fused = timed(fused, 6)
+    peak_fused = int(torch.cuda.max_memory_allocated(dev))
+    y = torch.empty_like(x)
+    q, k, v = chm.split_qkv(y, H, d)
+    need_k = chm.kda_workspace_size(B, T, H, d, d, dt, chm.KDA_L2NORM_QK)
+    ws_k = torch.empty(max(need_k, 1), dtype=torch.uint8, device=dev)
+
+    def two_calls(m=None):
+        chm.mshortconv_fwd(x, wt, wv, segs, out=y)
+        chm.kda_fwd(q, k, v, alpha, beta, S0, out=o, state_out=s_final, workspace=ws_k, marks=m)
+
+    ms_two, k_two = timed(two_calls, 5)
     e = 2 if w.dtype == "bf16" else 4
-    # minimal traffic per token-head: x's q|k|v channels, alpha, beta in; o out
-    fused_bytes = B * T * H * (5 * d + 1) * e
+    # minimal traffic per token-head: x's q|k|v channels, alpha, beta in; o out (plus S_final)
+    fused_bytes = B * T * H * (5 * d + 1) * e + B * H * d * d * 4 * (2 if S0 is not None else 1)
+    chunked = "kda_out_conv_kernel" in k_fused
+    call_ms = sum(k_fused.values()) if chunked else ms_fused
     out = {
         "metric": "KDA+mShortConv fused fwd tokens/sec/GPU",
         "value": B * T / (ms_fused * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -563,14 +583,19 @@ def bench_fused(args, w):
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": f"synthetic (seeded; {w.dtype} x, alpha, beta; fp32 conv weights; fp32 state)",
         "config": {"workload": f"{w.name}: {T} tokens per sequence, B={B}, H={H}, d={d}; the conv computed in the "
-                               f"token-by-token recurrence's load stage (q|k|v never stored)",
-                   "tokens_per_step": B * T, "ms_two_calls_same_recurrence": ms_two,
-                   "two_calls_tokens_per_s": B * T / (ms_two * 1e-3)},
-        "roofline": {"bound": "hbm", "kernel": "kda_seq_kernel (fused conv)", "achieved":
-                     fused_bytes / (ms_fused * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": fused_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                     "ms_per_launch": ms_fused, "algorithmic_bytes_per_launch": fused_bytes,
-                     "recipe": f"x's q|k|v channels, alpha, beta in and o out: {(5 * d + 1) * e} B per token-head"},
+                               f"{'chunked' if chunked else 'token-by-token'} recurrence's load stage (q|k|v never "
+                               f"stored)",
+                   "tokens_per_step": B * T, "kernels_ms": k_fused, "ms_two_calls": ms_two,
+                   "two_calls_kernels_ms": k_two, "two_calls_tokens_per_s": B * T / (ms_two * 1e-3),
+                   "fused_over_two_calls": ms_two / ms_fused,
+                   "memory": {"peak_allocated_bytes_fused": peak_fused, "workspace_bytes_fused": int(need_f),
+                              "conv_output_bytes_two_calls": int(y.numel() * y.element_size())}},
+        "roofline": {"bound": "hbm", "kernel": "fused call (" + " + ".join(k_fused) + ")", "achieved":
+                     fused_bytes / (call_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": fused_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "ms_per_launch": call_ms, "algorithmic_bytes_per_launch": fused_bytes,
+                     "recipe": f"x's q|k|v channels, alpha, beta in and o out: {(5 * d + 1) * e} B per token-head, "
+                               f"+ S_final; ms_per_launch is the sum of the call's kernels' average durations"},
         "cpu_baseline": None if args.no_cpu_baseline else _cpu_baseline(inp, w, args.cpu_sample_tokens),
     }
     print(json.dumps(out), flush=True)

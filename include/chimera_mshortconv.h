@@ -224,26 +224,39 @@ chimera_status chimera_kda_fwd_noalloc(const void* q, const void* k, const void*
  * chimera_kda_fwd_conv -- mShortConv and KDA in one pass (Chimera page 1, section 3.4:
  * the conv on packed storage fused with the recurrence; Eq. 13 then Eq. 14): q, k and v of
  * every token are computed from x in the recurrence's load stage, rounded to dt as
- * chimera_mshortconv_fwd would store them, and never written to memory. The result equals
- * chimera_mshortconv_fwd followed by chimera_kda_fwd with CHIMERA_KDA_SEQUENTIAL on the
- * views q, k, v = y[..., 0:H*dk], y[..., H*dk:2*H*dk], y[..., 2*H*dk:] (up to the order of
- * the conv's fp32 sums).
+ * chimera_mshortconv_fwd would store them, and never written to memory.
  *
  *   x         device [B][T][C], dt, C = H * (2 * dk + dv): the q, k, v channels in that
  *             order, head-major inside each
- *   w_text, w_vis, segs, nseg   as for chimera_mshortconv_fwd (nseg <= 32 here)
+ *   w_text, w_vis, segs, nseg   as for chimera_mshortconv_fwd (nseg <= 32 here); every
+ *             sequence of the batch has the layout segs
  *   alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt   as for chimera_kda_fwd
- *   flags     CHIMERA_KDA_L2NORM_QK (CHIMERA_KDA_SEQUENTIAL is accepted and implied)
+ *   flags     CHIMERA_KDA_L2NORM_QK, CHIMERA_KDA_SEQUENTIAL, CHIMERA_KDA_NO_SPLIT
+ *   workspace device, at least chimera_kda_conv_workspace_size(...) bytes, owned by the
+ *             caller (may be NULL when that size is 0)
  *
- * Runs on the token-by-token fp32 kernel (dk <= 128, else CHIMERA_ERR_UNSUPPORTED; more
- * than 32 segments likewise); the chunked MFMA path keeps the two calls. No workspace; o
- * must not alias x. Asynchronous on `stream`.
+ * Two paths, chosen as for chimera_kda_fwd:
+ *   - bf16 with dk = dv = 128 (and a layout whose farthest tap, 2 frames + 1 row + 1 token
+ *     back for video, keeps a chunk's window of x below 2 GiB): the chunked MFMA kernels with
+ *     the conv in their load stage. The conv sums its taps in the order of the conv kernels
+ *     and rounds once, so q, k and v equal chimera_mshortconv_fwd's output bit for bit and
+ *     the result equals chimera_mshortconv_fwd followed by chimera_kda_fwd (same flags) on
+ *     the views q, k, v = y[..., 0:H*dk], y[..., H*dk:2*H*dk], y[..., 2*H*dk:] (alpha clamped
+ *     as there).
+ *   - otherwise, and with CHIMERA_KDA_SEQUENTIAL: the token-by-token fp32 kernel (dk <= 128,
+ *     else CHIMERA_ERR_UNSUPPORTED), equal to the two calls with CHIMERA_KDA_SEQUENTIAL up to
+ *     the order of the conv's fp32 sums; no workspace.
+ * More than 32 segments: CHIMERA_ERR_UNSUPPORTED. A workspace below the size:
+ * CHIMERA_ERR_WORKSPACE before any launch. o must not alias x. Asynchronous on `stream`.
  */
+size_t chimera_kda_conv_workspace_size(const chimera_segment* segs, int32_t nseg, int64_t B, int64_t T,
+                                       int64_t H, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags);
 chimera_status chimera_kda_fwd_conv(const void* x, const float* w_text, const float* w_vis,
                                     const chimera_segment* segs, int32_t nseg, const void* alpha,
                                     const void* beta, const float* S0, void* o, float* S_final,
                                     int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                                    chimera_dtype dt, uint32_t flags, hipStream_t stream);
+                                    chimera_dtype dt, uint32_t flags, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Per-kernel timing variants. Each runs exactly the launches of the call it is
@@ -259,13 +272,15 @@ chimera_status chimera_kda_fwd_conv(const void* x, const float* w_text, const fl
  *             timing enabled (hipEventCreate), owned by the caller
  *   names     host array of `capacity` pointers, written
  *   capacity  at least nseg + 1 for the conv, CHIMERA_KDA_MAX_KERNELS + 1 for
- *             KDA; otherwise CHIMERA_ERR_SHAPE before any launch
+ *             KDA, CHIMERA_KDA_CONV_MAX_KERNELS + 1 for the fused conv + KDA;
+ *             otherwise CHIMERA_ERR_SHAPE before any launch
  *
  * Errors as for the untimed call; a failed event record is CHIMERA_ERR_HIP.
  * The marks serve measurement: they add a few microseconds of event overhead
  * per kernel.
  */
 #define CHIMERA_KDA_MAX_KERNELS 3
+#define CHIMERA_KDA_CONV_MAX_KERNELS 4   /* chimera_kda_fwd_conv_timed: capacity at least this + 1 */
 chimera_status chimera_mshortconv_fwd_timed(const void* x, void* y, int64_t B, int64_t T, int64_t C,
                                             chimera_dtype dt, const float* w_text, const float* w_vis,
                                             const chimera_segment* segs, int32_t nseg, hipStream_t stream,
@@ -276,6 +291,13 @@ chimera_status chimera_kda_fwd_timed(const void* q, const void* k, const void* v
                                      int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
                                      uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream,
                                      hipEvent_t* marks, const char** names, int32_t capacity, int32_t* used);
+chimera_status chimera_kda_fwd_conv_timed(const void* x, const float* w_text, const float* w_vis,
+                                          const chimera_segment* segs, int32_t nseg, const void* alpha,
+                                          const void* beta, const float* S0, void* o, float* S_final, int64_t B,
+                                          int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                                          uint32_t flags, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream, hipEvent_t* marks, const char** names,
+                                          int32_t capacity, int32_t* used);
 
 /*
  * chimera_kda_fwd_gated -- chimera_kda_fwd followed by the output gate and norm of

@@ -98,7 +98,11 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_int, vp]
     L.chimera_kda_fwd_conv.restype = ctypes.c_int
     L.chimera_kda_fwd_conv.argtypes = [vp, vp, vp, seg_p, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
-                                       ctypes.c_int, u32, vp]
+                                       ctypes.c_int, u32, vp, sz, vp]
+    L.chimera_kda_fwd_conv_timed.restype = ctypes.c_int
+    L.chimera_kda_fwd_conv_timed.argtypes = L.chimera_kda_fwd_conv.argtypes + [pp, cp, i32, ctypes.POINTER(i32)]
+    L.chimera_kda_conv_workspace_size.restype = sz
+    L.chimera_kda_conv_workspace_size.argtypes = [seg_p, i32, i64, i64, i64, i64, i64, ctypes.c_int, u32]
     L.chimera_kda_fwd_noalloc.restype = ctypes.c_int
     L.chimera_kda_fwd_noalloc.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                           ctypes.c_int, u32, vp]
@@ -523,10 +527,18 @@ def mshortconv_bwd(x, dy, w_text, w_vis, segments: Sequence, dx=None):
     return dx, dwt, dwv
 
 
+def kda_conv_workspace_size(segments: Sequence, B: int, T: int, H: int, dk: int, dv: int, dtype_code: int,
+                            flags: int) -> int:
+    arr = segment_array(segments)
+    return int(lib().chimera_kda_conv_workspace_size(arr, len(segments), B, T, H, dk, dv, dtype_code, flags))
+
+
 def kda_fwd_conv(x, w_text, w_vis, segments: Sequence, alpha, beta, S0=None, *, H: int, dk: int, dv: int,
-                 l2norm: bool = True, out=None, state_out=None, want_state: bool = True):
-    """mShortConv and KDA in one pass (chimera_kda_fwd_conv): x [B, T, H*(2 dk + dv)] holds the
-    pre-conv q|k|v channels; returns (o [B, T, H, dv], S_final or None)."""
+                 l2norm: bool = True, sequential: bool = False, no_split: bool = False, out=None,
+                 state_out=None, want_state: bool = True, workspace=None, marks: Optional[Marks] = None):
+    """mShortConv and KDA in one pass (chimera_kda_fwd_conv; chimera_kda_fwd_conv_timed with
+    `marks`): x [B, T, H*(2 dk + dv)] holds the pre-conv q|k|v channels; returns
+    (o [B, T, H, dv], S_final or None)."""
     import torch
     _need(x.dim() == 3, "x must be [B, T, C]")
     B, T, C = x.shape
@@ -541,13 +553,23 @@ def kda_fwd_conv(x, w_text, w_vis, segments: Sequence, alpha, beta, S0=None, *, 
     w_text, w_vis = _conv_weights(w_text, w_vis, C, dev)
     _on_gpu(x, "x")
     dt = _dtype_code(x)
+    flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0) | (KDA_NO_SPLIT if no_split else 0)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=x.dtype, device=x.device)
     Sf = state_out if state_out is not None else (
         torch.empty((B, H, dk, dv), dtype=torch.float32, device=x.device) if want_state else None)
     arr = segment_array(segments)
-    _check("chimera_kda_fwd_conv", lib().chimera_kda_fwd_conv(
-        _ptr(x), _ptr(w_text), _ptr(w_vis), arr, len(segments), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(Sf),
-        B, T, H, dk, dv, dt, KDA_L2NORM_QK if l2norm else 0, _stream(x)))
+    need = int(lib().chimera_kda_conv_workspace_size(arr, len(segments), B, T, H, dk, dv, dt, flags))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(x), _ptr(w_text), _ptr(w_vis), arr, len(segments), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o),
+            _ptr(Sf), B, T, H, dk, dv, dt, flags, _ptr(workspace), wbytes, _stream(x))
+    if marks is None:
+        _check("chimera_kda_fwd_conv", lib().chimera_kda_fwd_conv(*args))
+    else:
+        _check("chimera_kda_fwd_conv_timed",
+               lib().chimera_kda_fwd_conv_timed(*args, marks.handles, marks.names, marks.capacity,
+                                                ctypes.byref(marks.used)))
     return o, Sf
 
 

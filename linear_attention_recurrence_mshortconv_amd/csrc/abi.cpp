@@ -292,41 +292,111 @@ static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64
   return CHIMERA_OK;
 }
 
-chimera_status chimera_kda_fwd_conv(const void* x, const float* w_text, const float* w_vis,
-                                    const chimera_segment* segs, int32_t nseg, const void* alpha, const void* beta,
-                                    const float* S0, void* o, float* S_final, int64_t B, int64_t T, int64_t H,
-                                    int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, hipStream_t stream) {
+// The fused conv + recurrence: argument checks, then the chunked kernels with the conv in their
+// load stage (bf16, dk = dv = 128, the window a chunk's taps reach within 32-bit offsets, unless
+// CHIMERA_KDA_SEQUENTIAL), else the token-by-token kernel. need = the chunked path's workspace
+// bytes (0 for the token-by-token kernel).
+struct ConvCall {
+  chm::ConvSrc cs;
+  chm::KdaArgs a;
+  bool chunked = false;
+  size_t need = 0;
+};
+static chimera_status conv_call(const void* x, const float* w_text, const float* w_vis, const chimera_segment* segs,
+                                int32_t nseg, const void* alpha, const void* beta, const float* S0, void* o,
+                                float* S_final, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                chimera_dtype dt, uint32_t flags, bool check_ptrs, ConvCall& c) {
   if (dt != CHIMERA_F32 && dt != CHIMERA_BF16) return CHIMERA_ERR_DTYPE;
   if (!kda_sizes_ok(B, T, H, dk, dv)) return CHIMERA_ERR_SHAPE;
   if (dk > 128) return CHIMERA_ERR_UNSUPPORTED;
-  if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL)) return CHIMERA_ERR_UNSUPPORTED;
+  if (flags & ~(CHIMERA_KDA_L2NORM_QK | CHIMERA_KDA_SEQUENTIAL | CHIMERA_KDA_NO_SPLIT)) return CHIMERA_ERR_UNSUPPORTED;
   bool any_text, any_vis;
   const chimera_status st = check_segments(segs, nseg, T, &any_text, &any_vis);
   if (st != CHIMERA_OK) return st;
   if (nseg > chm::kMaxFusedSegs) return CHIMERA_ERR_UNSUPPORTED;
-  if (B == 0 || H == 0) return CHIMERA_OK;
-  if (T > 0) {
+  if (check_ptrs && B > 0 && H > 0 && T > 0) {
     if (x == nullptr || alpha == nullptr || beta == nullptr || o == nullptr) return CHIMERA_ERR_NULL;
     if ((any_text && w_text == nullptr) || (any_vis && w_vis == nullptr)) return CHIMERA_ERR_NULL;
     if (x == o) return CHIMERA_ERR_UNSUPPORTED;
   }
-  chm::ConvSrc cs;
-  cs.x = x;
-  cs.C = H * (2 * dk + dv);
-  cs.w_text = w_text;
-  cs.w_vis = w_vis;
-  cs.nseg = nseg;
-  for (int32_t i = 0; i < nseg; ++i) cs.seg[i] = to_seg(segs[i]);
-  chm::KdaArgs a;
+  c.cs.x = x;
+  c.cs.C = H * (2 * dk + dv);
+  c.cs.w_text = w_text;
+  c.cs.w_vis = w_vis;
+  c.cs.nseg = nseg;
+  for (int32_t i = 0; i < nseg; ++i) c.cs.seg[i] = to_seg(segs[i]);
+  chm::KdaArgs& a = c.a;
   a.q = a.k = a.v = nullptr;
-  a.qkv_stride = cs.C;
+  a.qkv_stride = c.cs.C;
   a.alpha = alpha; a.beta = beta;
   a.S0 = S0; a.o = o; a.S_final = S_final;
   a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
   a.bf16 = dt == CHIMERA_BF16;
   a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
-  a.conv = &cs;
-  return hip_status(chm::launch_kda_sequential(a, stream));
+  a.conv = &c.cs;
+  c.chunked = !(flags & CHIMERA_KDA_SEQUENTIAL) && B * T * H > 0 && chm::kda_chunked_supported(a) &&
+              chm::kda_chunked_conv_supported(a);
+  if (c.chunked) {
+    const chm::KdaRun run{0, T, B, 0};
+    const bool no_split = (flags & CHIMERA_KDA_NO_SPLIT) != 0;
+    if (!chm::kda_chunked_plan_ok(&run, 1, H, no_split)) return CHIMERA_ERR_SHAPE;
+    c.need = chm::kda_chunked_workspace(&run, 1, H, no_split, &c.cs);
+  }
+  return CHIMERA_OK;
+}
+
+size_t chimera_kda_conv_workspace_size(const chimera_segment* segs, int32_t nseg, int64_t B, int64_t T, int64_t H,
+                                       int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags) {
+  ConvCall c;
+  if (conv_call(nullptr, nullptr, nullptr, segs, nseg, nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H, dk, dv,
+                dt, flags, false, c) != CHIMERA_OK)
+    return 0;
+  return c.need;
+}
+
+static chimera_status kda_fwd_conv(const void* x, const float* w_text, const float* w_vis,
+                                   const chimera_segment* segs, int32_t nseg, const void* alpha, const void* beta,
+                                   const float* S0, void* o, float* S_final, int64_t B, int64_t T, int64_t H,
+                                   int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, chm::Marks* marks) {
+  ConvCall c;
+  const chimera_status st = conv_call(x, w_text, w_vis, segs, nseg, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt,
+                                      flags, true, c);
+  if (st != CHIMERA_OK) return st;
+  if (B == 0 || H == 0) return CHIMERA_OK;
+  if (c.chunked && (workspace == nullptr || workspace_bytes < c.need)) return CHIMERA_ERR_WORKSPACE;
+  if (marks != nullptr && chm::mark_begin(marks, stream) != hipSuccess) return CHIMERA_ERR_HIP;
+  if (c.chunked) {
+    const chm::KdaRun run{0, T, B, 0};
+    return hip_status(chm::launch_kda_chunked(c.a, &run, 1, (flags & CHIMERA_KDA_NO_SPLIT) != 0, workspace, stream,
+                                              marks));
+  }
+  return hip_status(chm::launch_kda_sequential(c.a, stream, marks));
+}
+
+chimera_status chimera_kda_fwd_conv(const void* x, const float* w_text, const float* w_vis,
+                                    const chimera_segment* segs, int32_t nseg, const void* alpha, const void* beta,
+                                    const float* S0, void* o, float* S_final, int64_t B, int64_t T, int64_t H,
+                                    int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  return kda_fwd_conv(x, w_text, w_vis, segs, nseg, alpha, beta, S0, o, S_final, B, T, H, dk, dv, dt, flags,
+                      workspace, workspace_bytes, stream, nullptr);
+}
+
+chimera_status chimera_kda_fwd_conv_timed(const void* x, const float* w_text, const float* w_vis,
+                                          const chimera_segment* segs, int32_t nseg, const void* alpha,
+                                          const void* beta, const float* S0, void* o, float* S_final, int64_t B,
+                                          int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                                          uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                          hipEvent_t* marks, const char** names, int32_t capacity, int32_t* used) {
+  if (marks == nullptr || names == nullptr || used == nullptr) return CHIMERA_ERR_NULL;
+  *used = 0;
+  if (capacity < CHIMERA_KDA_CONV_MAX_KERNELS + 1) return CHIMERA_ERR_SHAPE;
+  chm::Marks m{marks, names, capacity, 0};
+  const chimera_status st = kda_fwd_conv(x, w_text, w_vis, segs, nseg, alpha, beta, S0, o, S_final, B, T, H, dk, dv,
+                                         dt, flags, workspace, workspace_bytes, stream, &m);
+  *used = m.n;
+  return st;
 }
 
 chimera_status chimera_kda_fwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,

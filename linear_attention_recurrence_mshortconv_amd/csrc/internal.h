@@ -51,7 +51,7 @@ hipError_t launch_conv_rows_adjoint(const void* dy, void* dx, const float* w_vis
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream);
 
 // ---- KDA ----------------------------------------------------------------------
-// Conv source of the fused conv + recurrence (token-by-token kernel): q|k|v of every token
+// Conv source of the fused conv + recurrence: q|k|v of every token
 // are computed from x [B][T][C] (C = H (2 dk + dv); the q, k and v channels in that order)
 // by the mShortConv of the segment layout, rounded to the storage type as the conv call
 // would store them, and never written out.
@@ -84,7 +84,8 @@ struct KdaArgs {
   int64_t gate_stride = 0;
   const float* norm_w = nullptr;  // [dv] or null (ones)
   float norm_eps = 0.f;
-  // Fused conv (token-by-token kernel only): q, k, v are ignored and computed from conv->x.
+  // Fused conv: q, k, v are ignored and computed from conv->x (the token-by-token kernel, or
+  // the chunked kernels when kda_chunked_conv_supported).
   const ConvSrc* conv = nullptr;
 };
 
@@ -143,8 +144,13 @@ struct KdaRun {
   int64_t start, len, count, sidx0;
 };
 bool kda_chunked_supported(const KdaArgs& a);
+// With a.conv: the fused conv in the chunked kernels' load stage (bf16 x, one run, the window
+// of x that a chunk's taps reach addressable with 32-bit offsets).
+bool kda_chunked_conv_supported(const KdaArgs& a);
 bool kda_chunked_plan_ok(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split);   // grid sizes fit
-size_t kda_chunked_workspace(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split);
+// bytes; with conv, the transposed weights and the segment table after the states
+size_t kda_chunked_workspace(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split,
+                             const ConvSrc* conv = nullptr);
 hipError_t launch_kda_chunked(const KdaArgs& a, const KdaRun* runs, int64_t nruns, bool no_split, void* workspace,
                               hipStream_t stream, Marks* marks = nullptr);
 

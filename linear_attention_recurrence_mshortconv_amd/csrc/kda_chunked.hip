@@ -37,6 +37,8 @@
 #include <cstddef>
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
+#include <utility>
 #include <vector>
 
 #include "dtypes.h"
@@ -179,6 +181,15 @@ struct ChunkArgs {
   int l2norm;
   int nruns;
   int xcd_ranges;         // give each XCD a contiguous range of logical blocks (one run only)
+  // fused conv (the CONV kernels only): q, k, v computed from x [rows][xC] bf16 (the q, k and v
+  // channel blocks, head-major inside each) with the weights wT [31][xC] fp32 and the segments
+  // of every sequence; conv_back = the farthest any tap reaches back (tokens)
+  const uint16_t* x;
+  int64_t xC;
+  const float* wT;
+  const Seg* conv_seg;
+  int64_t conv_back;
+  int conv_nseg;
   SeqDesc run[kMaxRuns];
 };
 
@@ -398,6 +409,140 @@ static_assert(sizeof(PcLdsOut) <= 160 * 1024 && sizeof(PcLdsSum) <= 160 * 1024, 
 constexpr int kPcThreads = 512;   // 4 producer and 4 consumer waves
 static_assert(4 * kMsWave * sizeof(uint16_t) <= sizeof(PcLdsSum), "the four M waves' scratch lies in the summary LDS");
 
+// ---- fused conv in the load stage ------------------------------------------------------
+// Chimera page 1, section 3.4: mShortConv on packed storage, each segment convolved on its own
+// (Eq. 13; neighbours by Eq. 12, zero outside the segment, causal in time). The CONV kernels
+// compute q, k and v of a chunk from x as they load it: producers k (and q), consumers v. Per
+// token and tap slot (slots 0-3: the text taps; slots 4-30: visual tap (kt, kh, kw) at
+// 4 + 9 kt + 3 kh + kw), the producers tabulate the byte offset of the source token's x row
+// inside the chunk's window of x (the rows from conv_back tokens before the chunk on), or an
+// offset past the window for zero padding. Each lane then sums its tokens' taps slot by slot
+// with fmaf from zero, the slots in increasing order, which is the tap order of the conv
+// kernels, and rounds once to bf16: q, k and v are what the conv call stores, bit for bit.
+constexpr int kConvSlots = 31;
+constexpr uint32_t kOffPad = 0x7FFFFFF0u;   // window offsets stay below this; padding reads past it
+struct ConvLds {
+  uint32_t nb[2][CT][32];   // per chunk parity: [token][slot] window byte offset of the source row
+  Seg seg[kMaxFusedSegs];   // the segments of a sequence
+  uint32_t gmask[2];        // per chunk parity: the slot groups its tokens use (bit 0: text taps;
+                            // bit 1 + 3 kt + kh: visual taps (kt, kh, 0..2))
+  uint32_t pad[2];
+};
+static_assert(sizeof(PcLdsOut) + sizeof(ConvLds) <= 160 * 1024, "the conv tables fit beside the output pass");
+
+// x rows of the window of chunk c: from max(0, c CT - conv_back) to the sequence end
+__device__ __forceinline__ int64_t conv_window_start(const ChunkArgs& a, int64_t c) {
+  return max<int64_t>(0, c * CT - a.conv_back);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t conv_window(const ChunkArgs& a, int64_t row0, int64_t T, int64_t c) {
+  const int64_t wb = conv_window_start(a, c);
+  const int64_t bytes = (T - wb) * a.xC * 2;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(a.x + (row0 + wb) * a.xC), 0,
+                                           (int)min<int64_t>(bytes, (int64_t)kOffPad), kRsrcW3);
+}
+// The table of chunk c (n valid tokens) by the 256 producer threads (ptid): token ptid / 4,
+// slots ptid % 4 + 4 m. Thread 0 also forms the chunk's slot-group mask.
+__device__ __forceinline__ void conv_fill(const ChunkArgs& a, int64_t T, ConvLds& CL, int64_t c, int ptid) {
+  const int i = ptid >> 2, part = ptid & 3;
+  const int64_t t0 = c * CT, p = t0 + i;
+  const int64_t wb = conv_window_start(a, c);
+  const uint32_t C2 = (uint32_t)a.xC * 2;
+  uint32_t* row = CL.nb[c & 1][i];
+  const int nseg = a.conv_nseg;
+  if (p < T) {
+    int lo = 0, hi = nseg - 1;   // the segment holding p: the last one starting at or before it
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (CL.seg[mid].start <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    const Seg sg = CL.seg[lo];
+    const bool text = sg.kind == SEG_TEXT;
+    // grid point of p (Eq. 12), 32-bit: positions inside a sequence stay below 2^31
+    const uint32_t local = (uint32_t)(p - sg.start), W = (uint32_t)max(sg.width, 1);
+    const uint32_t HW = (uint32_t)max(sg.height, 1) * W;
+    const uint32_t f = text ? 0u : local / HW, rem = text ? 0u : local - f * HW;
+    const uint32_t hh = rem / W, ww = rem - hh * W;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int slot = part + 4 * m;
+      int64_t src = -1;
+      if (slot < kTextTaps) {
+        if (text) src = text_tap_source(sg, p, slot);
+      } else if (slot < kConvSlots && !text) {
+        const int tap = slot - kTextTaps;
+        src = vis_tap_source(sg, f, hh, ww, tap / 9, (tap / 3) % 3, tap % 3);
+      }
+      row[slot] = src >= 0 ? (uint32_t)(src - wb) * C2 : kOffPad;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) row[part + 4 * m] = kOffPad;   // tokens past the end: q = k = v = 0
+  }
+  if (ptid == 0) {
+    const int64_t t1 = min<int64_t>(T, t0 + CT);
+    uint32_t gm = 0;
+    for (int k = 0; k < nseg; ++k) {
+      const Seg& g = CL.seg[k];
+      if (g.start < t1 && g.start + g.length > t0)
+        gm |= g.kind == SEG_TEXT ? 1u : g.frames >= 3 ? 0x3FEu : g.frames == 2 ? 0x3F0u : 0x380u;
+    }
+    CL.gmask[c & 1] = gm;
+  }
+}
+// NTEN tensors (channel ch[e] + 0..3 of the x rows) of NT tokens (table rows tok[i]) of a chunk,
+// summed over the slots of the groups in gm, rounded to bf16 into out[e][i].
+template <int NT, int NTEN>
+__device__ __forceinline__ void conv_tokens(__amdgpu_buffer_rsrc_t rx, const float* wT, int64_t C,
+                                            const uint32_t (*nb)[32], const int (&tok)[NT], const int (&ch)[NTEN],
+                                            uint32_t gm, uint2 (&out)[NTEN][NT]) {
+  float acc[NTEN][NT][4];
+#pragma unroll
+  for (int e = 0; e < NTEN; ++e)
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[e][i][r] = 0.f;
+  // one group of NS slots from s0 on: every load first, then the multiply-adds in slot order
+  auto group = [&](auto nsc, int s0) {
+    constexpr int NS = decltype(nsc)::value;
+    float4 w[NTEN][NS];
+    uint2 xv[NTEN][NS][NT];
+#pragma unroll
+    for (int e = 0; e < NTEN; ++e)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) w[e][s] = *reinterpret_cast<const float4*>(wT + (s0 + s) * C + ch[e]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const uint32_t off = nb[tok[i]][s0 + s];
+#pragma unroll
+        for (int e = 0; e < NTEN; ++e) xv[e][s][i] = ld_buf64(rx, (int)(off + 2u * (uint32_t)ch[e]), 0);
+      }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < NTEN; ++e)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const float4 xf = unpack4(xv[e][s][i]);
+          acc[e][i][0] = fmaf(w[e][s].x, xf.x, acc[e][i][0]);
+          acc[e][i][1] = fmaf(w[e][s].y, xf.y, acc[e][i][1]);
+          acc[e][i][2] = fmaf(w[e][s].z, xf.z, acc[e][i][2]);
+          acc[e][i][3] = fmaf(w[e][s].w, xf.w, acc[e][i][3]);
+        }
+  };
+  if (gm & 1u) group(std::integral_constant<int, kTextTaps>{}, 0);
+  for (int g = 1; g < 10; ++g)
+    if ((gm >> g) & 1u) group(std::integral_constant<int, 3>{}, kTextTaps + 3 * (g - 1));
+#pragma unroll
+  for (int e = 0; e < NTEN; ++e)
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      out[e][i] = make_uint2(pack_bf16x2(acc[e][i][0], acc[e][i][1]), pack_bf16x2(acc[e][i][2], acc[e][i][3]));
+}
+
 // Decay factors of the blocked factorisation for channels c..c+3 (from a stage's pb, pf):
 //   em(I)     = e^{m_I}         product of alpha from the chunk start to block I's token 7
 //   enm(I)    = e^{g_n - m_I}   ... after block I's token 7 to the chunk end
@@ -573,6 +718,34 @@ __device__ __forceinline__ void p_issue_kq(const ChunkArgs& a, const SeqView& sv
     const auto rq_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
 #pragma unroll
     for (int i = 0; i < 8; ++i) R.q[i] = ld_buf64(rq_, vk, (tb + i) * st2);
+  }
+}
+
+// CONV: k (and q) of chunk c by the conv of x in the layout of p_issue_kq (the chunk's table
+// ready in CL)
+template <bool HASQ>
+__device__ __forceinline__ void p_conv_kq(const ChunkArgs& a, const SeqView& sv, const ConvLds& CL, int64_t h,
+                                          int64_t c, int wave, int lane, PLoad& R) {
+  const int hf = lane >> 5, c0 = 4 * (lane & 31);
+  int tok[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tok[i] = SBT * wave + 8 * hf + i;
+  const auto rx = conv_window(a, sv.row0, sv.T, c);
+  const uint32_t gm = __builtin_amdgcn_readfirstlane(CL.gmask[c & 1]);
+  const int kch = (int)((a.H + h) * D) + c0;
+  {
+    const int ch[1] = {kch};
+    uint2 out[1][8];
+    conv_tokens<8, 1>(rx, a.wT, a.xC, CL.nb[c & 1], tok, ch, gm, out);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) R.k[i] = out[0][i];
+  }
+  if (HASQ) {
+    const int ch[1] = {(int)(h * D) + c0};
+    uint2 out[1][8];
+    conv_tokens<8, 1>(rx, a.wT, a.xC, CL.nb[c & 1], tok, ch, gm, out);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) R.q[i] = out[0][i];
   }
 }
 
@@ -819,6 +992,22 @@ __device__ __forceinline__ void c_stage_v(uint16_t* vbuf, const uint2 (&vr)[ROWS
   for (int i = 0; i < ROWS / 2; ++i) *reinterpret_cast<uint2*>(&vbuf[rm(r0 + 2 * i, c0)]) = vr[i];
 }
 
+// CONV: the rows of c_issue_v computed by the conv of x (the chunk's table ready in CL)
+template <int ROWS>
+__device__ __forceinline__ void c_conv_v(const ChunkArgs& a, const SeqView& sv, const ConvLds& CL, int64_t h,
+                                         int64_t c, int cw, int lane, uint2 (&vr)[ROWS / 2]) {
+  int tok[ROWS / 2];
+#pragma unroll
+  for (int i = 0; i < ROWS / 2; ++i) tok[i] = ROWS * cw + 2 * i + (lane >> 5);
+  const auto rx = conv_window(a, sv.row0, sv.T, c);
+  const uint32_t gm = __builtin_amdgcn_readfirstlane(CL.gmask[c & 1]);
+  const int ch[1] = {(int)((2 * a.H + h) * D) + 4 * (lane & 31)};
+  uint2 out[1][ROWS / 2];
+  conv_tokens<ROWS / 2, 1>(rx, a.wT, a.xC, CL.nb[c & 1], tok, ch, gm, out);
+#pragma unroll
+  for (int i = 0; i < ROWS / 2; ++i) vr[i] = out[0][i];
+}
+
 // U = (I + A)^{-1} diag(beta) (V - K^ X) for the wave's 32 columns (V = 0 without vbuf: the
 // transition's columns). V comes from its LDS staging in the D layout through the transposing
 // read; (-K^) X accumulates on top (kr holds -K^), one k slot of X packed at a time.
@@ -1028,10 +1217,11 @@ __device__ __forceinline__ void c_issue_gate(const ChunkArgs& a, const SeqView& 
 // GATED adds the rest of Eq. 15 short of W_o to the output: o <- Sigmoid(gate) * o / sqrt(mean
 // over the head's channels of o^2 + eps) * w. Each consumer wave sums its 32 channels' squares
 // per token in phase 2 (rowss); phase 3 reads the four parts and writes o once.
-template <bool GATED>
+template <bool GATED, bool CONV>
 __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   PcLdsOut& L = *reinterpret_cast<PcLdsOut*>(lds_raw);
+  ConvLds& CL = *reinterpret_cast<ConvLds*>(lds_raw + sizeof(PcLdsOut));   // CONV only
 
   const uint32_t lid = (a.xcd_ranges && a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid)
                                                          : blockIdx.x;
@@ -1065,21 +1255,34 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
     PLoad R;
     float4 al[8];
     bool fast = true;
+    if (CONV) {   // the segment table, then the first chunk's tap table (both roles wait for each)
+      for (int i = tid; i < a.conv_nseg; i += 256) CL.seg[i] = a.conv_seg[i];
+      lds_barrier();
+      if (nch > 0) conv_fill(a, sv.T, CL, c_begin, tid);
+      lds_barrier();
+    }
     if (nch > 0) {
       p_issue_a(a, sv, h, c_begin, wave, lane, R);
-      p_issue_kq<true>(a, sv, h, c_begin, wave, lane, R);
+      if (CONV) p_conv_kq<true>(a, sv, CL, h, c_begin, wave, lane, R);
+      else p_issue_kq<true>(a, sv, h, c_begin, wave, lane, R);
     }
     for (int64_t t = 0; t <= nch; ++t) {
       const int64_t cp = c_begin + t;
       PcStage& sp = L.st[cp & 1];
       if (t < nch) {
         p_phase1<true>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
-        if (t + 1 < nch) p_issue_a(a, sv, h, cp + 1, wave, lane, R);
+        if (t + 1 < nch) {
+          p_issue_a(a, sv, h, cp + 1, wave, lane, R);
+          if (CONV) conv_fill(a, sv.T, CL, cp + 1, tid);   // read from phase 2 on
+        }
       }
       lds_barrier();
       if (t < nch) {
         fast = p_phase2<true>(sp, L.qw[cp & 1], L.rk, L.rq, R, al, wave, lane);
-        if (t + 1 < nch) p_issue_kq<true>(a, sv, h, cp + 1, wave, lane, R);
+        if (t + 1 < nch) {
+          if (CONV) p_conv_kq<true>(a, sv, CL, h, cp + 1, wave, lane, R);
+          else p_issue_kq<true>(a, sv, h, cp + 1, wave, lane, R);
+        }
       }
       lds_barrier();
       if (t < nch) p_phase3_out(sp, L.qw[cp & 1], L.at, L.aqk, L.adiag, fast, wave, lane);
@@ -1112,6 +1315,10 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
     }
     uint2 gx[2][4], vr[8];
     f32x4 U[4][2], OT[2][4];
+    if (CONV) {   // (the producers' segment and first tap tables)
+      lds_barrier();
+      lds_barrier();
+    }
     for (int64_t t = 0; t <= nch; ++t) {
       const int64_t cc = c_begin + t - 1;
       const PcStage& sc = L.st[cc & 1];
@@ -1124,7 +1331,10 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
         if (GATED) c_issue_gate(a, sv, h, cc, col0, lane, gx);
         c_solve<2>(sc, L.at, L.qw[(cc + 1) & 1], cf, S, col0, U, l16, q4);
       }
-      if (t < nch) c_issue_v<16>(a, sv, h, cc + 1, cw, lane, vr);   // staged in phase 3
+      if (t < nch) {   // staged in phase 3
+        if (CONV) c_conv_v<16>(a, sv, CL, h, cc + 1, cw, lane, vr);
+        else c_issue_v<16>(a, sv, h, cc + 1, cw, lane, vr);
+      }
       lds_barrier();
       // ---- phase 2: the output
       if (t > 0) {
@@ -1190,9 +1400,11 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
 // their chains with the producer's work. At the segment end S goes to the workspace tile-major and M, through
 // LDS, as split bf16 A fragments.
 constexpr int kPcSumThreads = 768;
+template <bool CONV>
 __global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   PcLdsSum& L = *reinterpret_cast<PcLdsSum*>(lds_raw);
+  ConvLds& CL = *reinterpret_cast<ConvLds*>(lds_raw + sizeof(PcLdsSum));   // CONV only
 
   const uint32_t lid = (a.xcd_ranges && a.grid % 8 == 0) ? xcd_contiguous_id(blockIdx.x, (uint32_t)a.grid)
                                                          : blockIdx.x;
@@ -1221,21 +1433,34 @@ __global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
     PLoad R;   // loads issued as in the output pass
     float4 al[8];
     bool fast = true;
+    if (CONV) {   // the segment table, then the first chunk's tap table (both roles wait for each)
+      for (int i = tid; i < a.conv_nseg; i += 256) CL.seg[i] = a.conv_seg[i];
+      lds_barrier();
+      if (nch > 0) conv_fill(a, sv.T, CL, c_begin, tid);
+      lds_barrier();
+    }
     if (nch > 0) {
       p_issue_a(a, sv, h, c_begin, wave, lane, R);
-      p_issue_kq<false>(a, sv, h, c_begin, wave, lane, R);
+      if (CONV) p_conv_kq<false>(a, sv, CL, h, c_begin, wave, lane, R);
+      else p_issue_kq<false>(a, sv, h, c_begin, wave, lane, R);
     }
     for (int64_t t = 0; t <= nch; ++t) {
       const int64_t cp = c_begin + t;
       PcStage& sp = L.st[cp & 1];
       if (t < nch) {
         p_phase1<false>(a, sp, L.rk, L.rq, R, (int)min<int64_t>(CT, sv.T - cp * CT), wave, lane, al);
-        if (t + 1 < nch) p_issue_a(a, sv, h, cp + 1, wave, lane, R);
+        if (t + 1 < nch) {
+          p_issue_a(a, sv, h, cp + 1, wave, lane, R);
+          if (CONV) conv_fill(a, sv.T, CL, cp + 1, tid);   // read from phase 2 on
+        }
       }
       lds_barrier();
       if (t < nch) {
         fast = p_phase2<false>(sp, nullptr, L.rk, L.rq, R, al, wave, lane);
-        if (t + 1 < nch) p_issue_kq<false>(a, sv, h, cp + 1, wave, lane, R);
+        if (t + 1 < nch) {
+          if (CONV) p_conv_kq<false>(a, sv, CL, h, cp + 1, wave, lane, R);
+          else p_issue_kq<false>(a, sv, h, cp + 1, wave, lane, R);
+        }
       }
       lds_barrier();
       if (t < nch) p_phase3_sum(sp, L.at, L.adiag, fast, wave, lane);
@@ -1256,6 +1481,10 @@ __global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
       }
     uint2 vr[4];
     f32x4 UM[4][1];
+    if (CONV) {   // (the producers' segment and first tap tables)
+      lds_barrier();
+      lds_barrier();
+    }
     for (int64_t t = 0; t <= nch; ++t) {
       const int64_t cc = c_begin + t - 1;
       const PcStage& sc = L.st[cc & 1];
@@ -1269,7 +1498,10 @@ __global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
       }
       lds_barrier();
       if (t > 0) c_solve<1>(sc, L.at, nullptr, cf, M, col0, UM, l16, q4);
-      if (t < nch) c_issue_v<8>(a, sv, h, cc + 1, j, lane, vr);   // staged in phase 3
+      if (t < nch) {   // staged in phase 3
+        if (CONV) c_conv_v<8>(a, sv, CL, h, cc + 1, j, lane, vr);
+        else c_issue_v<8>(a, sv, h, cc + 1, j, lane, vr);
+      }
       lds_barrier();
       if (t > 0) c_update<1>(sc, cf, M, UM, l16, q4);   // kc and egn of the stage stay until the next tick
       if (t < nch) c_stage_v<8>(L.vs, vr, j, lane);     // read in the next tick's phase 1
@@ -1501,7 +1733,44 @@ SetBlocks set_blocks(const Plan& pl, size_t r0, size_t r1, int64_t H) {
   return b;
 }
 
+// The fused conv's weights transposed to wT [31][C] (the text taps, then the visual taps; a
+// missing weight array reads as zeros) and the segment table, into the workspace.
+__global__ __launch_bounds__(256) void conv_prep_kernel(ConvSrc cs, float* wT, Seg* seg) {
+  const int64_t n = (int64_t)kConvSlots * cs.C;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int slot = (int)(e / cs.C);
+    const int64_t c = e - slot * cs.C;
+    wT[e] = slot < kTextTaps ? (cs.w_text != nullptr ? cs.w_text[c * kTextTaps + slot] : 0.f)
+                             : (cs.w_vis != nullptr ? cs.w_vis[c * kVisTaps + slot - kTextTaps] : 0.f);
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < cs.nseg) seg[threadIdx.x] = cs.seg[threadIdx.x];
+}
+
+// how far back any tap of the layout reaches (tokens)
+int64_t conv_reach_back(const ConvSrc& cs) {
+  int64_t back = 0;
+  for (int i = 0; i < cs.nseg; ++i) {
+    const Seg& g = cs.seg[i];
+    const int64_t b = g.kind == SEG_TEXT ? kTextTaps - 1
+                                         : std::min<int64_t>(std::max(g.frames - 1, 0), 2) * g.height * g.width +
+                                               g.width + 1;
+    back = std::max(back, b);
+  }
+  return back;
+}
+size_t conv_wT_bytes(int64_t C) { return ((size_t)kConvSlots * C * sizeof(float) + 255) / 256 * 256; }
+
 }  // namespace
+
+bool kda_chunked_conv_supported(const KdaArgs& a) {
+  if (a.conv == nullptr || !a.bf16 || a.dk != D || a.dv != D) return false;
+  const ConvSrc& cs = *a.conv;
+  if (cs.C != a.H * 3 * D || cs.nseg < 1 || cs.nseg > kMaxFusedSegs) return false;
+  if ((reinterpret_cast<uintptr_t>(cs.x) & 7) != 0) return false;
+  // every offset into a chunk's window stays below the padding offset
+  const int64_t back = conv_reach_back(cs);
+  return (double)(CT + 1 + 2 * back) * (double)cs.C * 2.0 < (double)kOffPad;
+}
 
 bool kda_chunked_supported(const KdaArgs& a) {
   // 8-byte loads of q, k and alpha: token stride a multiple of 4 elements, 8-byte aligned bases
@@ -1520,8 +1789,9 @@ bool kda_chunked_plan_ok(const KdaRun* runs, int64_t nruns, int64_t H, bool no_s
   return true;
 }
 
-size_t kda_chunked_workspace(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
-  return (size_t)make_plan(runs, nruns, H, no_split).ws_mats * D * D * sizeof(float);
+size_t kda_chunked_workspace(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split, const ConvSrc* conv) {
+  const size_t states = (size_t)make_plan(runs, nruns, H, no_split).ws_mats * D * D * sizeof(float);
+  return conv == nullptr ? states : states + conv_wT_bytes(conv->C) + (size_t)conv->nseg * sizeof(Seg);
 }
 
 hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nruns, bool no_split, void* workspace,
@@ -1551,7 +1821,32 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
   a.Lo = pl.Lo;
   a.l2norm = x.l2norm ? 1 : 0;
   a.xcd_ranges = pl.desc.size() == 1 ? 1 : 0;   // blocks of unequal length: the hardware's round robin
-  const size_t lds = sizeof(PcLdsOut), lds_sum = sizeof(PcLdsSum);
+  const bool conv = x.conv != nullptr;
+  a.x = nullptr;
+  a.xC = 0;
+  a.wT = nullptr;
+  a.conv_seg = nullptr;
+  a.conv_back = 0;
+  a.conv_nseg = 0;
+  if (conv) {
+    if (!kda_chunked_conv_supported(x) || nruns != 1) return hipErrorInvalidValue;
+    float* wT = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_mats * D * D * sizeof(float));
+    Seg* segs = reinterpret_cast<Seg*>(reinterpret_cast<char*>(wT) + conv_wT_bytes(x.conv->C));
+    const int64_t n = (int64_t)kConvSlots * x.conv->C;
+    const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(conv_prep_kernel, dim3(blocks), dim3(256), 0, stream, *x.conv, wT, segs);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark_after(marks, "conv_prep_kernel", stream);
+    if (e != hipSuccess) return e;
+    a.x = static_cast<const uint16_t*>(x.conv->x);
+    a.xC = x.conv->C;
+    a.wT = wT;
+    a.conv_seg = segs;
+    a.conv_back = conv_reach_back(*x.conv);
+    a.conv_nseg = x.conv->nseg;
+  }
+  const size_t lds = sizeof(PcLdsOut) + (conv ? sizeof(ConvLds) : 0);
+  const size_t lds_sum = sizeof(PcLdsSum) + (conv ? sizeof(ConvLds) : 0);
   int dev = 0;
   hipError_t de = hipGetDevice(&dev);
   if (de != hipSuccess) return de;
@@ -1559,15 +1854,17 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
   // at once on one device race on nothing (setting it twice is harmless).
   static std::atomic<bool> attr_done[64];
   if (dev < 0 || dev >= 64 || !attr_done[dev].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_out_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_out_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda_sum_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds_sum);
-    if (e != hipSuccess) return e;
+    const int lo = (int)sizeof(PcLdsOut), ls = (int)sizeof(PcLdsSum), lc = (int)sizeof(ConvLds);
+    const std::pair<const void*, int> fns[] = {
+        {reinterpret_cast<const void*>(&kda_out_kernel<false, false>), lo},
+        {reinterpret_cast<const void*>(&kda_out_kernel<true, false>), lo},
+        {reinterpret_cast<const void*>(&kda_out_kernel<false, true>), lo + lc},
+        {reinterpret_cast<const void*>(&kda_sum_kernel<false>), ls},
+        {reinterpret_cast<const void*>(&kda_sum_kernel<true>), ls + lc}};
+    for (const auto& f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, f.second);
+      if (e != hipSuccess) return e;
+    }
     if (dev >= 0 && dev < 64) attr_done[dev].store(true, std::memory_order_release);
   }
   auto round8 = [](int64_t n) { return (int)((n + 7) / 8 * 8); };
@@ -1591,9 +1888,10 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
       ChunkArgs s = a;
       s.nblk = (int)sum0;
       s.grid = round8(sum0);
-      hipLaunchKernelGGL(kda_sum_kernel, dim3((unsigned)s.grid), dim3(kPcSumThreads), lds_sum, stream, s);
+      if (conv) hipLaunchKernelGGL(kda_sum_kernel<true>, dim3((unsigned)s.grid), dim3(kPcSumThreads), lds_sum, stream, s);
+      else hipLaunchKernelGGL(kda_sum_kernel<false>, dim3((unsigned)s.grid), dim3(kPcSumThreads), lds_sum, stream, s);
       hipError_t e = hipGetLastError();
-      if (e == hipSuccess) e = mark_after(marks, "kda_sum_kernel", stream);
+      if (e == hipSuccess) e = mark_after(marks, conv ? "kda_sum_conv_kernel" : "kda_sum_kernel", stream);
       if (e != hipSuccess) return e;
       s.nblk = (int)comb0;
       s.grid = (int)comb0;
@@ -1605,12 +1903,15 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
     if (out0 == 0) continue;
     a.nblk = (int)out0;
     a.grid = round8(out0);
-    if (fuse_gate)
-      hipLaunchKernelGGL(kda_out_kernel<true>, dim3((unsigned)a.grid), dim3(kPcThreads), lds, stream, a);
+    if (conv)
+      hipLaunchKernelGGL((kda_out_kernel<false, true>), dim3((unsigned)a.grid), dim3(kPcThreads), lds, stream, a);
+    else if (fuse_gate)
+      hipLaunchKernelGGL((kda_out_kernel<true, false>), dim3((unsigned)a.grid), dim3(kPcThreads), lds, stream, a);
     else
-      hipLaunchKernelGGL(kda_out_kernel<false>, dim3((unsigned)a.grid), dim3(kPcThreads), lds, stream, a);
+      hipLaunchKernelGGL((kda_out_kernel<false, false>), dim3((unsigned)a.grid), dim3(kPcThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess) e = mark_after(marks, fuse_gate ? "kda_out_gated_kernel" : "kda_out_kernel", stream);
+    if (e == hipSuccess)
+      e = mark_after(marks, conv ? "kda_out_conv_kernel" : fuse_gate ? "kda_out_gated_kernel" : "kda_out_kernel", stream);
     if (e != hipSuccess) return e;
   }
   return gated && !fuse_gate ? launch_kda_gate_norm(x, stream, marks) : hipSuccess;

@@ -255,16 +255,43 @@ def test_fused_conv_argument_errors():
         a.update(kw)
         n = len(segs) if nseg is None else nseg
         return L.chimera_kda_fwd_conv(a["x"], a["wt"], a["wv"], segs, n, a["al"], a["be"], a["S0"], a["o"], a["Sf"],
-                                      a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["flags"], None)
+                                      a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], a["flags"],
+                                      a.get("ws"), a.get("wsb", 0), None)
     assert call(dt=7) == 3
     assert call(dk=256) == 5                                            # the conv weights of dk > 128 do not fit
-    assert call(flags=4) == 5                                           # no chunked options
+    assert call(flags=8) == 5                                           # an unknown flag
     assert call(T=9) == 4                                               # segments must tile [0, T)
     assert call(segs=many, T=33) == 5                                   # more than 32 segments
     assert call(x=None) == 1 and call(o=None) == 1 and call(al=None) == 1
     assert call(wt=None) == 1 and call(segs=img, wv=None) == 1          # the weights the layout uses
     assert call(x=6) == 5                                               # o aliasing x
     assert call(B=0) == 0
+    # bf16 with dk = dv = 128 (x and alpha 8-byte aligned) runs the chunked kernels, which need the workspace
+    need = int(L.chimera_kda_conv_workspace_size(img, 1, 1, 8, 2, 128, 128, 1, 1))
+    assert need > 0
+    big = dict(segs=img, dk=128, dv=128, x=8, o=16, al=32)
+    assert call(**big) == 6
+    assert call(**big, ws=16, wsb=need - 1) == 6
+    assert call(**dict(big, x=None), ws=16, wsb=need) == 1                # argument checks come first
+
+
+def test_fused_conv_workspace_size_rules():
+    """The fused call's workspace: the chunked path's states plus the transposed weights and
+    the segment table; zero on the token-by-token kernel."""
+    L = chm.lib()
+    img = chm.segment_array([dict(kind=0, start=0, length=256), dict(kind=1, start=256, length=65536, frames=1,
+                                                                      height=256, width=256)])
+    size = lambda *a: int(L.chimera_kda_conv_workspace_size(img, 2, *a))
+    T, H, d = 65792, 16, 128
+    full = size(1, T, H, d, d, 1, 1)
+    states = chm.kda_workspace_size(1, T, H, d, d, chm.BF16, chm.KDA_L2NORM_QK)
+    assert full == states + (31 * 3 * H * d * 4 + 255) // 256 * 256 + 2 * 32
+    assert size(1, T, H, d, d, 1, 1 | 2) == 0                             # CHIMERA_KDA_SEQUENTIAL
+    assert size(1, T, H, d, d, 0, 1) == 0                                 # fp32: token by token
+    assert size(1, T, H, 64, 64, 1, 1) == 0                               # d = 64: token by token
+    assert size(1, T + 1, H, d, d, 1, 1) == 0                             # segments that do not tile T
+    no_split = size(1, T, H, d, d, 1, 1 | 4)
+    assert no_split == (31 * 3 * H * d * 4 + 255) // 256 * 256 + 2 * 32   # one segment: no states
 
 
 def test_workspace_size_rules():
@@ -291,6 +318,10 @@ def test_timed_variants_check_their_marks_first():
                                                    None, 0, None, ev_, names, cap, ctypes.byref(used))
     assert kda(None, 8) == 1
     assert kda(ev, 3) == 2                                                 # needs 3 kernels + 1
+    fused = lambda ev_, cap: L.chimera_kda_fwd_conv_timed(1, 2, 3, arr, 2, 4, 5, None, 6, None, 1, 8, 2, 128, 128, 1,
+                                                          1, None, 0, None, ev_, names, cap, ctypes.byref(used))
+    assert fused(None, 8) == 1
+    assert fused(ev, 4) == 2                                               # needs 4 kernels + 1
     used.value = 9
     assert L.chimera_kda_fwd_timed(1, 2, 3, 256, 4, 5, None, 6, None, 0, 8, 2, 128, 128, 1, 1, None, 0, None, ev,
                                    names, 4, ctypes.byref(used)) == 0 and used.value == 0   # B = 0: nothing launched
