@@ -1008,10 +1008,11 @@ __device__ __forceinline__ void c_conv_v(const ChunkArgs& a, const SeqView& sv, 
   for (int i = 0; i < ROWS / 2; ++i) vr[i] = out[0][i];
 }
 
-// U = (I + A)^{-1} diag(beta) (V - K^ X) for the wave's 32 columns (V = 0 without vbuf: the
-// transition's columns). V comes from its LDS staging in the D layout through the transposing
-// read; (-K^) X accumulates on top (kr holds -K^), one k slot of X packed at a time.
-template <int NCT>   // column tiles of 16 (col0 + 16 ct)
+// U = (I + A)^{-1} diag(beta) (V - K^ X) for the wave's column tiles: the first VCT tiles take V
+// (columns col0 + 16 ct of v), the others V = 0 (the transition's columns). V comes from its LDS
+// staging in the D layout through the transposing read; (-K^) X accumulates on top (kr holds
+// -K^), one k slot of X packed at a time.
+template <int NCT, int VCT = NCT>   // column tiles of 16 (col0 + 16 ct)
 __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, const uint16_t* vbuf, bool fast,
                                         const f32x4 (&X)[8][NCT], int col0, f32x4 (&U)[4][NCT], int l16, int q4) {
   f32x4 acc[4][NCT];
@@ -1019,7 +1020,7 @@ __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, c
   for (int I = 0; I < 4; ++I)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      if (vbuf != nullptr) {
+      if (vbuf != nullptr && ct < VCT) {
         // lane (l16, q4) receives rows 16 I + 4 q4 + 0..3 of column col0 + 16 ct + l16
         const float4 vv = unpack4(ld_tr(&vbuf[rm(SBT * I + 4 * q4 + (l16 >> 2), col0 + 16 * ct + 4 * (l16 & 3))]));
         acc[I][ct] = f32x4{vv.x, vv.y, vv.z, vv.w};
@@ -1471,16 +1472,17 @@ __global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
   } else {
     // ---------------- consumers ----------------
     const int j = wave - 4, col0 = 16 * j;
-    f32x4 S[8][1], M[8][1];
+    // X[rt][0]: the state S (from 0), X[rt][1]: the transition M (from I), both columns 16 j ..
+    f32x4 X[8][2];
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        S[rt][0][r] = 0.f;
-        M[rt][0][r] = 16 * rt + 4 * q4 + r == col0 + l16 ? 1.f : 0.f;
+        X[rt][0][r] = 0.f;
+        X[rt][1][r] = 16 * rt + 4 * q4 + r == col0 + l16 ? 1.f : 0.f;
       }
     uint2 vr[4];
-    f32x4 UM[4][1];
+    f32x4 U[4][2];
     if (CONV) {   // (the producers' segment and first tap tables)
       lds_barrier();
       lds_barrier();
@@ -1491,20 +1493,18 @@ __global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
       // the stage's vote, read from LDS: made wave-uniform so that the factorisation choice stays a
       // branch (a value the compiler takes as divergent would run both paths)
       const bool cf = t > 0 && __builtin_amdgcn_readfirstlane(sc.fast) != 0;
-      if (t > 0) {
-        f32x4 US[4][1];
-        c_solve<1>(sc, L.at, L.vs, cf, S, col0, US, l16, q4);
-        c_update<1>(sc, cf, S, US, l16, q4);
-      }
+      // phase 1 (the producers' lightest): U of the S and M tiles in one pass over K^ and T
+      if (t > 0) c_solve<2, 1>(sc, L.at, L.vs, cf, X, col0, U, l16, q4);
       lds_barrier();
-      if (t > 0) c_solve<1>(sc, L.at, nullptr, cf, M, col0, UM, l16, q4);
-      if (t < nch) {   // staged in phase 3
+      // phase 2: v of the next chunk into vs (read in the next tick's phase 1; this tick's reads are done)
+      if (t < nch) {
         if (CONV) c_conv_v<8>(a, sv, CL, h, cc + 1, j, lane, vr);
         else c_issue_v<8>(a, sv, h, cc + 1, j, lane, vr);
+        c_stage_v<8>(L.vs, vr, j, lane);
       }
       lds_barrier();
-      if (t > 0) c_update<1>(sc, cf, M, UM, l16, q4);   // kc and egn of the stage stay until the next tick
-      if (t < nch) c_stage_v<8>(L.vs, vr, j, lane);     // read in the next tick's phase 1
+      // phase 3 (the producers' heaviest): both updates (kc and egn of the stage stay until the next tick)
+      if (t > 0) c_update<2>(sc, cf, X, U, l16, q4);
       lds_barrier();
     }
     lds_barrier();   // every wave is past its last LDS read: the LDS is scratch now
@@ -1512,13 +1512,13 @@ __global__ __launch_bounds__(kPcSumThreads) void kda_sum_kernel(ChunkArgs a) {
       // S: the tile (rows, columns 16 j ..) goes out tile-major
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
-        *reinterpret_cast<f32x4*>(sv.ws + p * D * D + tile_off(j >> 1, rt, j & 1, lane)) = S[rt][0];
+        *reinterpret_cast<f32x4*>(sv.ws + p * D * D + tile_off(j >> 1, rt, j & 1, lane)) = X[rt][0];
       // M: split into bf16 high and low parts, staged row-major
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float x = M[rt][0][r];
+          const float x = X[rt][1][r];
           const uint16_t hb = f2bf(x);
           const int o = (16 * rt + 4 * q4 + r) * kMP + col0 + l16;
           mhi[o] = hb;
