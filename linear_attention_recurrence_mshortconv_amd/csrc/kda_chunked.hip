@@ -390,7 +390,8 @@ struct PcLdsOut {         // output pass
   PcStage st[2];
   uint16_t qw[2][CT * RMS];   // Q^ = q e^{g} / |q| (fast) or q e^{g - m_I} / |q| (blocked), per stage;
                               // once a stage's Q^ is used, its qw holds v of the next chunk
-  uint16_t at[CT * TRS];      // at[tr(j, i)] = -A(i, j) below the diagonal blocks, T_II on them
+  uint16_t at[CT * TRS];      // at[tr(j, i)] = -(K^ K_^T)(i, j) (no b) below the diagonal blocks,
+                              // T_II diag(b_I) on them
   uint16_t aqk[CT * TRS];     // aqk[tr(j, i)] = Aqk(i, j), lower triangle with the diagonal
   float adiag[NSB * 272];     // strictly lower A_II in fp32: A_II(i, k) at 272 I + 16 i + k
   float rk[CT];               // 1 / |k_t| (1 without normalisation)
@@ -593,20 +594,22 @@ __device__ __forceinline__ f32x4 mma4(const uint4 (&ra)[4], const uint4 (&cb)[4]
   for (int s = 0; s < 4; ++s) acc = mma32(ra[s], cb[s], acc);
   return acc;
 }
-// A(I, J) = diag(b) (K^ K_^T)(I, J) from acc = ((-K^) K_^T)(I, J) (the operands carry 1 / |k|):
-// below the diagonal -> at (negated, column-major: a lane's four rows are one 8-byte write), on
-// it (strictly lower part) -> adiag in fp32
+// From acc = ((-K^) K_^T)(I, J) (the operands carry 1 / |k|), with A = diag(b) K^ K_^T strictly
+// lower: below the diagonal blocks -A'(I, J) = acc without the row factor b -> at (column-major: a
+// lane's four rows are one 8-byte write); on the diagonal A_II = diag(b) (K^ K_^T)(I, I) (strictly
+// lower part) -> adiag in fp32. The b of each block row goes into T'_II = T_II diag(b_I) instead
+// (invert_diag), so that (I + A) U = diag(b) Z is solved block by block as
+// U_I = T'_II (Z_I - sum_{J < I} A'(I, J) U_J) with no row scaling of Z.
 __device__ __forceinline__ void epi_a(uint16_t* at, float* adiag, const float* beta, int I, int J, f32x4 acc, int l16,
                                       int q4) {
   const int j = SBT * J + l16;
-  const float4 b4 = ldf4(&beta[SBT * I + 4 * q4]);
-  const float rowf[4] = {b4.x, b4.y, b4.z, b4.w};
   if (I == J) {
+    const float4 b4 = ldf4(&beta[SBT * I + 4 * q4]);
+    const float rowf[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) adiag[272 * I + 16 * (4 * q4 + r) + l16] = 4 * q4 + r > l16 ? -rowf[r] * acc[r] : 0.f;
   } else {
-    *reinterpret_cast<uint2*>(&at[tr(j, SBT * I + 4 * q4)]) =
-        pack4(make_float4(rowf[0] * acc[0], rowf[1] * acc[1], rowf[2] * acc[2], rowf[3] * acc[3]));
+    *reinterpret_cast<uint2*>(&at[tr(j, SBT * I + 4 * q4)]) = pack4(acc);
   }
 }
 // Aqk(I, J) = (Q^ K_^T)(I, J) (the operands carry 1 / |q| and 1 / |k|), lower triangle
@@ -618,10 +621,12 @@ __device__ __forceinline__ void epi_q(uint16_t* aqk, int I, int J, f32x4 acc, in
   for (int r = 0; r < 4; ++r) v[r] = (I > J || 4 * q4 + r >= l16) ? acc[r] : 0.f;
   *reinterpret_cast<uint2*>(&aqk[tr(j, SBT * I + 4 * q4)]) = pack4(make_float4(v[0], v[1], v[2], v[3]));
 }
-// T_II = (I + A_II)^{-1}: lane j of a 16-lane group forms column j of T_II by forward
+// T'_II = (I + A_II)^{-1} diag(b_I): lane j of a 16-lane group forms column j of T_II by forward
 // substitution, x_i = [i = j] - sum_{k < i} A_II(i, k) x_k, reading the rows of A_II
-// (written by this wave) as broadcasts; the column goes to at as four 8-byte writes.
-__device__ __forceinline__ void invert_diag(const float* adiag, uint16_t* at, int I, int jj, bool write) {
+// (written by this wave) as broadcasts; the column, times b of token 16 I + j, goes to at as
+// four 8-byte writes.
+__device__ __forceinline__ void invert_diag(const float* adiag, const float* beta, uint16_t* at, int I, int jj,
+                                            bool write) {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   float x[SBT];
@@ -644,10 +649,11 @@ __device__ __forceinline__ void invert_diag(const float* adiag, uint16_t* at, in
     x[i] = acc0 + acc1;
   }
   if (write) {
+    const float bj = beta[SBT * I + jj];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       *reinterpret_cast<uint2*>(&at[tr(SBT * I + jj, SBT * I + 4 * m)]) =
-          make_uint2(pack_bf16x2(x[4 * m], x[4 * m + 1]), pack_bf16x2(x[4 * m + 2], x[4 * m + 3]));
+          make_uint2(pack_bf16x2(bj * x[4 * m], bj * x[4 * m + 1]), pack_bf16x2(bj * x[4 * m + 2], bj * x[4 * m + 3]));
   }
 }
 // mma16 A fragments of at (transposed reads): block (I, J), J <= I, at I (I + 1) / 2 + J
@@ -658,7 +664,8 @@ __device__ __forceinline__ void load_t_frags(const uint16_t* at, uint2 (&af)[10]
     for (int J = 0; J <= I; ++J)
       af[I * (I + 1) / 2 + J] = ld_tr(&at[tr(SBT * J + 4 * q4 + (l16 >> 2), SBT * I + 4 * (l16 & 3))]);
 }
-// X = (I + A)^{-1} Y by block forward substitution, Y and X in the D layout
+// X = (I + A)^{-1} diag(b) Z by block forward substitution, X_I = T'_II (Z_I - sum_{J < I} A'(I, J) X_J)
+// (af: -A' below the diagonal, T' on it), Z and X in the D layout
 __device__ __forceinline__ void block_solve(const uint2 (&af)[10], const f32x4 (&y0)[4], f32x4 (&X)[4]) {
   uint2 Xb[4];
 #pragma unroll
@@ -887,7 +894,7 @@ __device__ __forceinline__ void p_phase3_out(const PcStage& st, const uint16_t* 
       tile_frags(st.kr, I, rA, l16, q4);
       epi_a(at, adiag, st.beta, I, I, mma4(rA, cA), l16, q4);
     }
-    invert_diag(adiag, at, lane >> 4, lane & 15, true);
+    invert_diag(adiag, st.beta, at, lane >> 4, lane & 15, true);
     __builtin_amdgcn_s_setprio(0);
   } else if (wave == 1) {
     tile_frags(st.kc, 0, cA, l16, q4);
@@ -943,7 +950,7 @@ __device__ __forceinline__ void p_phase3_sum(const PcStage& st, uint16_t* at, fl
   tile_frags(st.kr, wave, rA, l16, q4);
   __builtin_amdgcn_s_setprio(3);
   epi_a(at, adiag, st.beta, wave, wave, mma4(rA, cA), l16, q4);
-  invert_diag(adiag, at, wave, l16, q4 == 0);
+  invert_diag(adiag, st.beta, at, wave, l16, q4 == 0);
   __builtin_amdgcn_s_setprio(0);
   auto below = [&](int I, int J) {
     tile_frags(st.kc, J, cA, l16, q4);
@@ -1008,7 +1015,8 @@ __device__ __forceinline__ void c_conv_v(const ChunkArgs& a, const SeqView& sv, 
   for (int i = 0; i < ROWS / 2; ++i) vr[i] = out[0][i];
 }
 
-// U = (I + A)^{-1} diag(beta) (V - K^ X) for the wave's column tiles: the first VCT tiles take V
+// U = (I + A)^{-1} diag(beta) (V - K^ X) for the wave's column tiles (the block solve with T' and
+// A', which carry diag(beta)): the first VCT tiles take V
 // (columns col0 + 16 ct of v), the others V = 0 (the transition's columns). V comes from its LDS
 // staging in the D layout through the transposing read; (-K^) X accumulates on top (kr holds
 // -K^), one k slot of X packed at a time.
@@ -1041,16 +1049,7 @@ __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, c
       for (int ct = 0; ct < NCT; ++ct) acc[I][ct] = mma32(kf, xs[ct], acc[I][ct]);
     }
   }
-#pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    const float4 b4 = ldf4(&st.beta[SBT * I + 4 * q4]);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      acc[I][ct][0] *= b4.x; acc[I][ct][1] *= b4.y;
-      acc[I][ct][2] *= b4.z; acc[I][ct][3] *= b4.w;
-    }
-  }
-  uint2 af[10];
+  uint2 af[10];   // T' on the diagonal blocks carries diag(b)
   load_t_frags(at, af, l16, q4);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
