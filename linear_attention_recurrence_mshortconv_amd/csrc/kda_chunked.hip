@@ -1020,9 +1020,11 @@ __device__ __forceinline__ void c_conv_v(const ChunkArgs& a, const SeqView& sv, 
 // (columns col0 + 16 ct of v), the others V = 0 (the transition's columns). V comes from its LDS
 // staging in the D layout through the transposing read; (-K^) X accumulates on top (kr holds
 // -K^), one k slot of X packed at a time.
-template <int NCT, int VCT = NCT>   // column tiles of 16 (col0 + 16 ct)
-__device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, const uint16_t* vbuf, bool fast,
-                                        const f32x4 (&X)[8][NCT], int col0, f32x4 (&U)[4][NCT], int l16, int q4) {
+// MODE: 0 the factorisation chosen per fragment from `fast`; 1 fast; 2 blocked
+template <int NCT, int VCT, int MODE>   // column tiles of 16 (col0 + 16 ct)
+__device__ __forceinline__ void c_solve_f(const PcStage& st, const uint16_t* at, const uint16_t* vbuf, bool fast,
+                                          const f32x4 (&X)[8][NCT], int col0, f32x4 (&U)[4][NCT], int l16, int q4) {
+  const bool blocked = MODE == 0 ? !fast : MODE == 2;
   f32x4 acc[4][NCT];
 #pragma unroll
   for (int I = 0; I < 4; ++I)
@@ -1044,7 +1046,7 @@ __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, c
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       uint4 kf = ld128(st.kr, (SBT * I + l16) * RKS + 32 * s + 8 * q4);
-      if (!fast) kf = scale8(kf, em_of(st, I, 32 * s + 4 * q4), em_of(st, I, 32 * s + 16 + 4 * q4));
+      if (blocked) kf = scale8(kf, em_of(st, I, 32 * s + 4 * q4), em_of(st, I, 32 * s + 16 + 4 * q4));
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) acc[I][ct] = mma32(kf, xs[ct], acc[I][ct]);
     }
@@ -1060,11 +1062,21 @@ __device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, c
     for (int I = 0; I < 4; ++I) U[I][ct] = Xo[I];
   }
 }
+// SPLIT: each factorisation compiled on its own, so that the fast path is straight-line code whose
+// LDS loads the compiler can move ahead of the MFMAs (where the registers allow it)
+template <int NCT, int VCT = NCT, bool SPLIT = false>
+__device__ __forceinline__ void c_solve(const PcStage& st, const uint16_t* at, const uint16_t* vbuf, bool fast,
+                                        const f32x4 (&X)[8][NCT], int col0, f32x4 (&U)[4][NCT], int l16, int q4) {
+  if (!SPLIT) c_solve_f<NCT, VCT, 0>(st, at, vbuf, fast, X, col0, U, l16, q4);
+  else if (fast) c_solve_f<NCT, VCT, 1>(st, at, vbuf, fast, X, col0, U, l16, q4);
+  else c_solve_f<NCT, VCT, 2>(st, at, vbuf, fast, X, col0, U, l16, q4);
+}
 
 // X <- Diag(e^{g_n}) X + K~^T U, K~ = (K / |k|) e^{g_n - g} read transposed from kc
-template <int NCT>
-__device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X)[8][NCT], const f32x4 (&U)[4][NCT],
-                                         int l16, int q4) {
+template <int NCT, int MODE>   // MODE as for c_solve_f
+__device__ __forceinline__ void c_update_f(const PcStage& st, bool fast_rt, f32x4 (&X)[8][NCT],
+                                           const f32x4 (&U)[4][NCT], int l16, int q4) {
+  const bool fast = MODE == 0 ? fast_rt : MODE == 1;
   uint4 Upf[2][NCT];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -1108,15 +1120,24 @@ __device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X
     }
   }
 }
+template <int NCT, bool SPLIT = false>
+__device__ __forceinline__ void c_update(const PcStage& st, bool fast, f32x4 (&X)[8][NCT], const f32x4 (&U)[4][NCT],
+                                         int l16, int q4) {
+  if (!SPLIT) c_update_f<NCT, 0>(st, fast, X, U, l16, q4);
+  else if (fast) c_update_f<NCT, 1>(st, fast, X, U, l16, q4);
+  else c_update_f<NCT, 2>(st, fast, X, U, l16, q4);
+}
 
 // The output of the chunk, transposed: O^T = S^T Q^T + U^T Aqk^T. With the mirror-image
 // operand layouts the packed state serves as the A operand of S^T and the Q^ row fragments
 // as the B operand of Q^T, and likewise U and Aqk; the result's D layout gives lane
 // (l16, q4) of OT[ct][I] token 16 I + l16 at channels col0 + 16 ct + 4 q4 .. + 3, which go
 // out as one 8-byte store.
-__device__ __forceinline__ void c_output(const PcStage& st, const uint16_t* qw, const uint16_t* aqk, bool fast,
-                                         const f32x4 (&S)[8][2], const f32x4 (&U)[4][2], f32x4 (&OT)[2][4], int l16,
-                                         int q4) {
+template <int MODE>   // MODE as for c_solve_f
+__device__ __forceinline__ void c_output_f(const PcStage& st, const uint16_t* qw, const uint16_t* aqk, bool fast,
+                                           const f32x4 (&S)[8][2], const f32x4 (&U)[4][2], f32x4 (&OT)[2][4], int l16,
+                                           int q4) {
+  const bool blocked = MODE == 0 ? !fast : MODE == 2;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -1129,7 +1150,7 @@ __device__ __forceinline__ void c_output(const PcStage& st, const uint16_t* qw, 
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       uint4 qf = ld128(qw, (SBT * I + l16) * RMS + 32 * s + 8 * q4);
-      if (!fast) qf = scale8(qf, em_of(st, I, 32 * s + 4 * q4), em_of(st, I, 32 * s + 16 + 4 * q4));
+      if (blocked) qf = scale8(qf, em_of(st, I, 32 * s + 4 * q4), em_of(st, I, 32 * s + 16 + 4 * q4));
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) OT[ct][I] = mma32(xs[ct], qf, OT[ct][I]);
     }
@@ -1156,6 +1177,14 @@ __device__ __forceinline__ void c_output(const PcStage& st, const uint16_t* qw, 
     OT[ct][3] = mma32(Uf[0][ct], qa4, OT[ct][3]);
     OT[ct][3] = mma32(Uf[1][ct], qa5, OT[ct][3]);
   }
+}
+template <bool SPLIT = false>
+__device__ __forceinline__ void c_output(const PcStage& st, const uint16_t* qw, const uint16_t* aqk, bool fast,
+                                         const f32x4 (&S)[8][2], const f32x4 (&U)[4][2], f32x4 (&OT)[2][4], int l16,
+                                         int q4) {
+  if (!SPLIT) c_output_f<0>(st, qw, aqk, fast, S, U, OT, l16, q4);
+  else if (fast) c_output_f<1>(st, qw, aqk, fast, S, U, OT, l16, q4);
+  else c_output_f<2>(st, qw, aqk, fast, S, U, OT, l16, q4);
 }
 
 // OT (one token per lane, 4 channels) rounded to bf16 -> the stage's kr, used as o staging:
@@ -1329,7 +1358,7 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       if (GATED && t > 1) c_store_rows(a, sv, h, cc - 1, L.st[(cc - 1) & 1].kr, cw, lane);
       if (t > 0) {
         if (GATED) c_issue_gate(a, sv, h, cc, col0, lane, gx);
-        c_solve<2>(sc, L.at, L.qw[(cc + 1) & 1], cf, S, col0, U, l16, q4);
+        c_solve<2, 2, !GATED && !CONV>(sc, L.at, L.qw[(cc + 1) & 1], cf, S, col0, U, l16, q4);
       }
       if (t < nch) {   // staged in phase 3
         if (CONV) c_conv_v<16>(a, sv, CL, h, cc + 1, cw, lane, vr);
@@ -1338,7 +1367,7 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       lds_barrier();
       // ---- phase 2: the output
       if (t > 0) {
-        c_output(sc, L.qw[cc & 1], L.aqk, cf, S, U, OT, l16, q4);
+        c_output<!GATED && !CONV>(sc, L.qw[cc & 1], L.aqk, cf, S, U, OT, l16, q4);
         if (!GATED) {
           c_stage_o(L.st[cc & 1].kr, OT, col0, l16, q4);   // K^ of this chunk is used up
         } else {
@@ -1361,7 +1390,7 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       // ---- phase 3: the state update; the output rows go out (gated: normalised, staged)
       if (t > 0) {
         if (!GATED) c_store_rows(a, sv, h, cc, L.st[cc & 1].kr, cw, lane);
-        c_update<2>(sc, cf, S, U, l16, q4);
+        c_update<2, !GATED && !CONV>(sc, cf, S, U, l16, q4);
         if (GATED) {
           auto sig = [](float g) { return __builtin_amdgcn_rcpf(1.f + __expf(-g)); };
 #pragma unroll
