@@ -187,6 +187,27 @@ def test_kda_chunked_degenerate_decay(chm, no_split):
     assert_close(to_host(Sf), S_ref, "bf16", "S degenerate decay")
 
 
+@pytest.mark.parametrize("no_split", [False, True])
+def test_kda_chunked_mixed_decay_rates(chm, no_split):
+    """Per-channel decay rates from e^-0.01 to e^-0.45 per token (within a chunk some channels fall
+    below e^-25 while others barely move), every fifth chunk with log alpha = -1 (the blocked
+    factorisation), and a chunk with alpha = 1, in one sequence; against the oracle."""
+    rng = np.random.default_rng(41)
+    B, T, H, d = 2, 64 * 21 + 30, 2, 128
+    q, k, v, _, beta, S0 = _small_case(rng, B, T, H, d, s0=True)
+    rate = np.exp(rng.uniform(np.log(0.01), np.log(0.45), (1, 1, H, d))).astype(np.float32)
+    la = -rate * (0.5 + rng.random((B, T, H, d), dtype=np.float32))
+    for c in range(4, T // 64, 5):
+        la[:, 64 * c:64 * (c + 1)] = -1.0
+    la[:, 64 * 7:64 * 8] = 0.0
+    alpha = wl.round_to_bf16(np.exp(la).astype(np.float32))
+    o, Sf = _gpu_kda(chm, q, k, v, alpha, beta, S0, no_split=no_split)
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    assert np.isfinite(to_host(o)).all() and np.isfinite(to_host(Sf)).all()
+    assert_close(to_host(o), o_ref, "bf16", "o mixed rates")
+    assert_close(to_host(Sf), S_ref, "bf16", "S mixed rates")
+
+
 def test_kda_chunked_split_invariance(chm):
     """Segmenting the sequence (three passes) and not segmenting it agree closely."""
     rng = np.random.default_rng(8)
