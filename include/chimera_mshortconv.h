@@ -176,8 +176,12 @@ size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, i
  *           NULL when that size is 0; contents on entry do not matter
  *
  * Supported: dk, dv in 1..256 for the token-by-token kernel (fp32 and bf16);
- * the chunked MFMA kernel runs for bf16 with dk = dv = 128. alpha < 0 is
- * undefined.
+ * the chunked MFMA kernel runs for bf16 with dk and dv multiples of 8 up to 128
+ * (qkv_stride a multiple of 4, q, k and alpha 8-byte aligned). It works at 128
+ * channels: smaller heads are zero-padded inside the kernels (their extra k, q,
+ * v channels read as 0 and alpha as 1, and only the real channels of o and
+ * S_final are written), so a head costs the same at any size up to 128. alpha < 0
+ * is undefined.
  *
  * Small alpha on the chunked kernel: it factors the decay inside 16-token
  * blocks and raises every alpha below e^-7.5 (about 5.5e-4) to e^-7.5 as it

@@ -175,6 +175,7 @@ struct ChunkArgs {
   const float* norm_w;    // [D] or null
   float norm_eps;
   int64_t H;
+  int dk, dv;             // head sizes (multiples of 8 up to D; the kernels run at D, zero-padded)
   int Lo;                 // chunks per output segment
   int nblk;               // logical blocks of this pass
   int grid;               // launched blocks
@@ -289,6 +290,10 @@ __device__ __forceinline__ float row_sum16(const float (&a)[16], int l16) {
 
 // third descriptor word of a raw buffer resource on gfx9
 constexpr int kRsrcW3 = 0x00020000;
+// A buffer offset past every bound (2^31 as the unsigned offset the hardware sees): channels beyond
+// a head's dk / dv read zero and are not stored. Bounds stay at or below 2^31 bytes (64 token rows
+// of at most 2^25 bytes), and offset plus any token row offset stays below 2^32.
+constexpr int kOffOut = INT32_MIN;
 __device__ __forceinline__ uint2 ld_buf64(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   return make_uint2(v[0], v[1]);
@@ -305,14 +310,19 @@ __device__ __forceinline__ uint2 ld_tr(const uint16_t* p) {
 }
 
 // the 32 state columns of this wave -> m ([D][D] fp32); svo = lane part of the offset
-__device__ __forceinline__ void store_state(const f32x4 (&S)[8][2], float* m, int svo) {
-  float* dst = m + svo;
+// the state's rows < dk of its columns < dv (lane rows 16 rt + 4 q4 + r, columns col0 + 16 ct + l16) ->
+// m ([dk][dv] fp32)
+__device__ __forceinline__ void store_state(const f32x4 (&S)[8][2], float* m, int dk, int dv, int col0, int l16,
+                                            int q4) {
 #pragma unroll
   for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * rt + r) * D + 16 * ct] = S[rt][ct][r];
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * q4 + r, col = col0 + 16 * ct + l16;
+        if (row < dk && col < dv) m[row * dv + col] = S[rt][ct][r];
+      }
 }
 // Workspace matrices ([D][D] fp32 states and transitions) are kept tile-major: the
 // 16 x 16 tile (rt, column block cb, ct) is 256 contiguous floats, lane l = 16 q4 + l16
@@ -696,9 +706,9 @@ __device__ __forceinline__ void p_issue_a(const ChunkArgs& a, const SeqView& sv,
   const int64_t t0 = c * CT;
   const int n = (int)min<int64_t>(CT, sv.T - t0);
   const int64_t row0 = sv.row0 + t0;
-  const int sa2 = (int)(a.H * D) * 2;
-  const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * D), 0, n * sa2, kRsrcW3);
-  const int va = (8 * hf) * sa2 + 2 * c0;
+  const int sa2 = (int)(a.H * a.dk) * 2;
+  const auto ra_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.alpha + (row0 * a.H + h) * a.dk), 0, n * sa2, kRsrcW3);
+  const int va = c0 < a.dk ? (8 * hf) * sa2 + 2 * c0 : kOffOut;   // padded channels: alpha = 1 (p_phase1)
   const int tb = SBT * wave;
 #pragma unroll
   for (int i = 0; i < 8; ++i) R.a[i] = ld_buf64(ra_, va, (tb + i) * sa2);
@@ -716,13 +726,13 @@ __device__ __forceinline__ void p_issue_kq(const ChunkArgs& a, const SeqView& sv
   const int n = (int)min<int64_t>(CT, sv.T - t0);
   const int64_t row0 = sv.row0 + t0;
   const int st2 = (int)a.stride * 2;
-  const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
-  const int vk = (8 * hf) * st2 + 2 * c0;
+  const auto rk_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + row0 * a.stride + h * a.dk), 0, n * st2, kRsrcW3);
+  const int vk = c0 < a.dk ? (8 * hf) * st2 + 2 * c0 : kOffOut;   // padded channels: k = q = 0
   const int tb = SBT * wave;
 #pragma unroll
   for (int i = 0; i < 8; ++i) R.k[i] = ld_buf64(rk_, vk, (tb + i) * st2);
   if (HASQ) {
-    const auto rq_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + row0 * a.stride + h * D), 0, n * st2, kRsrcW3);
+    const auto rq_ = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + row0 * a.stride + h * a.dk), 0, n * st2, kRsrcW3);
 #pragma unroll
     for (int i = 0; i < 8; ++i) R.q[i] = ld_buf64(rq_, vk, (tb + i) * st2);
   }
@@ -785,7 +795,8 @@ __device__ __forceinline__ void p_phase1(const ChunkArgs& a, PcStage& st, float*
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const bool in = tk0 + i < n;
-    al[i] = unpack4(make_uint2(in ? clamp_alpha2(R.a[i].x) : one2, in ? clamp_alpha2(R.a[i].y) : one2));
+    const bool use = in && c0 < a.dk;
+    al[i] = unpack4(make_uint2(use ? clamp_alpha2(R.a[i].x) : one2, use ? clamp_alpha2(R.a[i].y) : one2));
   }
   float4 hp = al[0];
 #pragma unroll
@@ -985,9 +996,9 @@ __device__ __forceinline__ void c_issue_v(const ChunkArgs& a, const SeqView& sv,
   const int64_t t0 = c * CT;
   const int n = (int)min<int64_t>(CT, sv.T - t0);
   const int st2 = (int)a.stride * 2;
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (sv.row0 + t0) * a.stride + h * D), 0, n * st2,
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + (sv.row0 + t0) * a.stride + h * a.dv), 0, n * st2,
                                                     kRsrcW3);
-  const int vo = (ROWS * cw + (lane >> 5)) * st2 + 8 * (lane & 31);
+  const int vo = 4 * (lane & 31) < a.dv ? (ROWS * cw + (lane >> 5)) * st2 + 8 * (lane & 31) : kOffOut;
 #pragma unroll
   for (int i = 0; i < ROWS / 2; ++i) vr[i] = ld_buf64(rv, vo, 2 * i * st2);
 }
@@ -1203,14 +1214,15 @@ __device__ __forceinline__ void c_store_rows(const ChunkArgs& a, const SeqView& 
                                              const uint16_t* ob, int cw, int lane) {
   const int64_t t0 = c * CT;
   const int n = (int)min<int64_t>(CT, sv.T - t0);
-  const int so2 = (int)(a.H * D) * 2;
-  const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((sv.row0 + t0) * a.H + h) * D), 0, n * so2,
+  const int so2 = (int)(a.H * a.dv) * 2;
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc((void*)(a.o + ((sv.row0 + t0) * a.H + h) * a.dv), 0, n * so2,
                                                     kRsrcW3);
   const int r0 = SBT * cw + (lane >> 4), cc8 = 8 * (lane & 15);
+  const int oc = cc8 < a.dv ? 2 * cc8 : kOffOut;   // padded channels are not stored
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint4 u = ld128(ob, rk(r0 + 4 * j, cc8));
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{u.x, u.y, u.z, u.w}, ro, (r0 + 4 * j) * so2 + 2 * cc8, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{u.x, u.y, u.z, u.w}, ro, (r0 + 4 * j) * so2 + oc, 0, 0);
   }
 }
 
@@ -1326,15 +1338,17 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) S[rt][ct] = load_tile4(src, cw, rt, ct, lane);
-    } else {          // S0 ([D][D] row-major) or zero
-      const float* src = a.S0 ? a.S0 + sv.sidx * D * D : nullptr;
-      const int svo = (4 * q4) * D + col0 + l16;
+    } else {          // S0 ([dk][dv] row-major, zero-padded to D x D) or zero
+      const float* src = a.S0 ? a.S0 + sv.sidx * a.dk * a.dv : nullptr;
 #pragma unroll
       for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) S[rt][ct][r] = src ? src[svo + (16 * rt + r) * D + 16 * ct] : 0.f;
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rt + 4 * q4 + r, col = col0 + 16 * ct + l16;
+            S[rt][ct][r] = src != nullptr && row < a.dk && col < a.dv ? src[row * a.dv + col] : 0.f;
+          }
     }
     float4 gw[2];   // gated: the norm gain of the lane's channels col0 + 16 ct + 4 q4 .. + 3
     if (GATED) {
@@ -1416,7 +1430,8 @@ __global__ __launch_bounds__(kPcThreads) void kda_out_kernel(ChunkArgs a) {
       lds_barrier();
     }
     if (GATED && nch > 0) c_store_rows(a, sv, h, c_end - 1, L.st[(c_end - 1) & 1].kr, cw, lane);
-    if (a.S_final != nullptr && p == sv.P - 1) store_state(S, a.S_final + sv.sidx * D * D, (4 * q4) * D + col0 + l16);
+    if (a.S_final != nullptr && p == sv.P - 1)
+      store_state(S, a.S_final + sv.sidx * a.dk * a.dv, a.dk, a.dv, col0, l16, q4);
   }
 }
 
@@ -1601,7 +1616,7 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(ChunkArgs a) {
   const float* WS = sv.ws;                  // [E] summary states
   const float* WM = sv.ws + sv.E * D * D;   // [E] transitions
   float* Sst = sv.ws + 2 * sv.E * D * D;    // [P] start states
-  const float* S0 = a.S0 ? a.S0 + sv.sidx * D * D : nullptr;
+  const float* S0 = a.S0 ? a.S0 + sv.sidx * a.dk * a.dv : nullptr;   // [dk][dv], zero-padded to D x D
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = 16 * slice + l16;
@@ -1609,7 +1624,7 @@ __global__ __launch_bounds__(CB_T) void kda_combine_kernel(ChunkArgs a) {
 
   f32x4 cur;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) cur[r] = S0 ? S0[(row0 + r) * D + col] : 0.f;
+  for (int r = 0; r < 4; ++r) cur[r] = S0 != nullptr && row0 + r < a.dk && col < a.dv ? S0[(row0 + r) * a.dv + col] : 0.f;
   auto store = [&](int po, const f32x4& v) {   // tile-major
     *reinterpret_cast<f32x4*>(Sst + po * D * D + tile_off(slice >> 1, wave, slice & 1, lane)) = v;
   };
@@ -1804,8 +1819,10 @@ bool kda_chunked_supported(const KdaArgs& a) {
   // 8-byte loads of q, k and alpha: token stride a multiple of 4 elements, 8-byte aligned bases
   const uintptr_t al = reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k) |
                        reinterpret_cast<uintptr_t>(a.alpha);
-  return a.bf16 && a.dk == D && a.dv == D && a.qkv_stride % 4 == 0 && a.qkv_stride <= (int64_t(1) << 24) &&
-         (al & 7) == 0;
+  // head sizes up to D in steps of 8: the kernels run at D with the extra channels zero (k, q, v)
+  // or one (alpha), and store only the real ones
+  return a.bf16 && a.dk >= 8 && a.dk <= D && a.dk % 8 == 0 && a.dv >= 8 && a.dv <= D && a.dv % 8 == 0 &&
+         a.qkv_stride % 4 == 0 && a.qkv_stride <= (int64_t(1) << 24) && (al & 7) == 0;
 }
 
 bool kda_chunked_plan_ok(const KdaRun* runs, int64_t nruns, int64_t H, bool no_split) {
@@ -1839,13 +1856,15 @@ hipError_t launch_kda_chunked(const KdaArgs& x, const KdaRun* runs, int64_t nrun
   // the gate is fused into the output pass when its rows and the gain are read as 16-byte
   // pieces; otherwise the separate in-place gate/norm pass runs after it
   const bool gated = x.gate != nullptr;
-  const bool fuse_gate = gated && x.gate_stride % 8 == 0 && (reinterpret_cast<uintptr_t>(x.gate) & 15) == 0 &&
+  const bool fuse_gate = gated && x.dv == D && x.gate_stride % 8 == 0 && (reinterpret_cast<uintptr_t>(x.gate) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(x.norm_w) & 15) == 0 && x.gate_stride <= (int64_t(1) << 24);
   a.gate = static_cast<const uint16_t*>(x.gate);
   a.gate_stride = x.gate_stride;
   a.norm_w = x.norm_w;
   a.norm_eps = x.norm_eps;
   a.H = x.H;
+  a.dk = (int)x.dk;
+  a.dv = (int)x.dv;
   a.Lo = pl.Lo;
   a.l2norm = x.l2norm ? 1 : 0;
   a.xcd_ranges = pl.desc.size() == 1 ? 1 : 0;   // blocks of unequal length: the hardware's round robin

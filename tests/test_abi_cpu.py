@@ -288,7 +288,7 @@ def test_fused_conv_workspace_size_rules():
     assert full == states + (31 * 3 * H * d * 4 + 255) // 256 * 256 + 2 * 32
     assert size(1, T, H, d, d, 1, 1 | 2) == 0                             # CHIMERA_KDA_SEQUENTIAL
     assert size(1, T, H, d, d, 0, 1) == 0                                 # fp32: token by token
-    assert size(1, T, H, 64, 64, 1, 1) == 0                               # d = 64: token by token
+    assert size(1, T, H, 64, 64, 1, 1) == 0                               # d = 64: the conv is fused only at 128
     assert size(1, T + 1, H, d, d, 1, 1) == 0                             # segments that do not tile T
     no_split = size(1, T, H, d, d, 1, 1 | 4)
     assert no_split == (31 * 3 * H * d * 4 + 255) // 256 * 256 + 2 * 32   # one segment: no states
@@ -297,6 +297,11 @@ def test_fused_conv_workspace_size_rules():
 def test_workspace_size_rules():
     n = chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_L2NORM_QK)
     assert n >= 0
+    # bf16 heads up to 128 in steps of 8 run the chunked kernels at 128 channels: the same states
+    for dk, dv in ((64, 64), (32, 32), (8, 128), (128, 96)):
+        assert chm.kda_workspace_size(1, 65792, 16, dk, dv, chm.BF16, chm.KDA_L2NORM_QK) == n
+    for dk, dv in ((60, 64), (64, 132), (256, 256)):                      # token by token
+        assert chm.kda_workspace_size(1, 65792, 16, dk, dv, chm.BF16, chm.KDA_L2NORM_QK) == 0
     assert chm.kda_workspace_size(1, 256, 2, 32, 32, chm.F32, 0) == 0            # sequential path
     assert chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_SEQUENTIAL) == 0
     assert chm.kda_workspace_size(1, 10, 1, 0, 128, chm.BF16, 0) == 0            # invalid sizes

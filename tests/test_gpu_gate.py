@@ -64,6 +64,25 @@ def test_gated_chunked(chm, T, no_split, fused):
     assert_close(to_host(Sf), S_ref, "bf16", f"S_final T={T}")
 
 
+def test_gated_head_size_64(chm):
+    """64-channel heads: the chunked kernels, then the separate gate and norm pass (the fused one
+    takes 128-channel heads); the norm runs over each head's 64 channels."""
+    import torch
+    rng = np.random.default_rng(99)
+    B, T, H, d = 2, 300, 3, 64
+    q, k, v, alpha, beta, S0, gate, w = _bf16_case(rng, B, T, H, d)
+    dev = lambda a: to_device(a, "bf16")
+    marks = chm.Marks(8)
+    o, Sf = chm.kda_fwd(dev(q), dev(k), dev(v), dev(alpha), dev(beta), torch.from_numpy(S0).cuda(),
+                        gate=dev(gate), norm_weight=torch.from_numpy(w).cuda(), norm_eps=EPS, marks=marks)
+    torch.cuda.synchronize()
+    names = [n for n, _ in marks.kernels()]
+    assert "kda_out_kernel" in names and "kda_gate_norm_kernel" in names, names
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    assert_close(to_host(o), gated_rmsnorm_ref(o_ref, gate, w, EPS), "bf16", "gated o d=64")
+    assert_close(to_host(Sf), S_ref, "bf16", "S_final d=64")
+
+
 def test_gated_tiny_fp32_pipeline(chm):
     """The fp32 text workload end to end with the gate (token-by-token kernel, then the
     gate/norm pass)."""

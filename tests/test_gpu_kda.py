@@ -208,6 +208,38 @@ def test_kda_chunked_mixed_decay_rates(chm, no_split):
     assert_close(to_host(Sf), S_ref, "bf16", "S mixed rates")
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (32, 32), (64, 128), (128, 96), (8, 16)])
+@pytest.mark.parametrize("no_split", [False, True])
+def test_kda_chunked_head_sizes(chm, dk, dv, no_split):
+    """bf16 heads below 128 channels on the chunked kernels (zero-padded inside them to 128):
+    q, k, v as views into one fused tensor, several chunks and a ragged tail, S0; every head
+    against the oracle, and the kernel names show the chunked path ran."""
+    import torch
+    rng = np.random.default_rng(dk * 1000 + dv)
+    B, T, H = 2, 64 * 5 + 23, 3
+    C = H * (2 * dk + dv)
+    x = wl.round_to_bf16(rng.standard_normal((B, T, C)).astype(np.float32))
+    q = x[:, :, :H * dk].reshape(B, T, H, dk)
+    k = x[:, :, H * dk:2 * H * dk].reshape(B, T, H, dk)
+    v = x[:, :, 2 * H * dk:].reshape(B, T, H, dv)
+    la = -0.05 * np.logaddexp(0, rng.standard_normal((B, T, H, dk))).astype(np.float32)
+    alpha = wl.round_to_bf16(np.exp(la).astype(np.float32))
+    beta = wl.round_to_bf16((1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32))
+    S0 = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    xd = to_device(x, "bf16")
+    qd = xd[:, :, :H * dk].view(B, T, H, dk)
+    kd = xd[:, :, H * dk:2 * H * dk].view(B, T, H, dk)
+    vd = xd[:, :, 2 * H * dk:].view(B, T, H, dv)
+    marks = chm.Marks(8)
+    o, Sf = chm.kda_fwd(qd, kd, vd, to_device(alpha, "bf16"), to_device(beta, "bf16"), torch.from_numpy(S0).cuda(),
+                        no_split=no_split, marks=marks)
+    torch.cuda.synchronize()
+    assert "kda_out_kernel" in [n for n, _ in marks.kernels()]
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    assert_close(to_host(o), o_ref, "bf16", f"o dk={dk} dv={dv}")
+    assert_close(to_host(Sf), S_ref, "bf16", f"S_final dk={dk} dv={dv}")
+
+
 def test_kda_chunked_split_invariance(chm):
     """Segmenting the sequence (three passes) and not segmenting it agree closely."""
     rng = np.random.default_rng(8)

@@ -50,6 +50,18 @@ def test_varlen_mixed_lengths(chm, no_split):
     assert np.array_equal(to_host(Sf)[3], S0[3].astype(np.float64))    # the empty sample keeps its S0
 
 
+def test_varlen_head_size_64(chm):
+    """Packed samples with 64-channel heads on the chunked kernels (zero-padded inside them)."""
+    rng = np.random.default_rng(72)
+    cu = [0, 70, 70, 333, 400]
+    H, d = 3, 64
+    q, k, v, alpha, beta, S0 = _case(rng, cu[-1], H, d, len(cu) - 1)
+    o, Sf = _run(chm, q, k, v, alpha, beta, S0, cu)
+    o_ref, S_ref = kda_varlen_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, cu, S0)
+    assert_close(to_host(o), o_ref, "bf16", "o d=64")
+    assert_close(to_host(Sf), S_ref, "bf16", "S_final d=64")
+
+
 def test_varlen_equal_samples_match_the_batched_call(chm):
     """Three samples of equal length in one row launch exactly as a batch of three."""
     import torch
