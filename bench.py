@@ -36,6 +36,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import hashlib
 import json
 import os
@@ -147,6 +148,10 @@ def _args():
     ap.add_argument("--fused", action="store_true",
                     help="the conv fused into the recurrence's load stage (chimera_kda_fwd_conv), against the "
                          "two calls (conv, then the recurrence)")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="run the workload with heads of this size at the same width (H * d kept)")
+    ap.add_argument("--sequential", action="store_true",
+                    help="the KDA call on the token-by-token kernel (CHIMERA_KDA_SEQUENTIAL)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=20736,
                     help="tokens per sequence in the oracle's timed sample (text + whole grid rows/frames)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
@@ -634,6 +639,10 @@ def main():
     chm.lib()
     by_name = {w.name: w for w in wl.WORKLOADS}
     w = by_name[args.workload] if args.workload in by_name else wl.WORKLOADS[int(args.workload)]
+    if args.head_dim:
+        if (w.H * w.d) % args.head_dim:
+            sys.exit(f"--head-dim {args.head_dim} does not divide the width {w.H * w.d}")
+        w = dataclasses.replace(w, H=w.H * w.d // args.head_dim, d=args.head_dim)
     if args.backward:
         bench_backward(args, w)
         return
@@ -659,8 +668,9 @@ def main():
     nseq = len(w.samples) - 1 if w.samples else B
     s_final = torch.empty(nseq if w.samples else B, H, d, d, dtype=torch.float32, device=dev)
     dcode = chm.BF16 if w.dtype == "bf16" else chm.F32
-    need = (chm.kda_varlen_workspace_size(w.samples, H, d, d, dcode, chm.KDA_L2NORM_QK) if w.samples else
-            chm.kda_workspace_size(B, T, H, d, d, dcode, chm.KDA_L2NORM_QK))
+    kflags = chm.KDA_L2NORM_QK | (chm.KDA_SEQUENTIAL if args.sequential else 0)
+    need = (chm.kda_varlen_workspace_size(w.samples, H, d, d, dcode, kflags) if w.samples else
+            chm.kda_workspace_size(B, T, H, d, d, dcode, kflags))
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     gate_np = wl.make_gate(w) if args.gated else None
     gkw = {}
@@ -670,10 +680,12 @@ def main():
     def step(mc=None, mk=None):
         chm.mshortconv_fwd(x, wt, wv, segs, out=y, marks=mc)
         if w.samples:
-            chm.kda_fwd_varlen(q[0], k[0], v[0], alpha[0], beta[0], w.samples, None, workspace=ws, out=o[0],
+            chm.kda_fwd_varlen(q[0], k[0], v[0], alpha[0], beta[0], w.samples, None, sequential=args.sequential,
+                               workspace=ws, out=o[0],
                                marks=mk, state_out=s_final, **gkw)
         else:
-            chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, marks=mk, state_out=s_final, **gkw)
+            chm.kda_fwd(q, k, v, alpha, beta, S0, sequential=args.sequential, workspace=ws, out=o, marks=mk,
+                        state_out=s_final, **gkw)
 
     if args.profile_once:
         ref_src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device=dev)   # 1 GiB
@@ -732,7 +744,7 @@ def main():
     # HBM bytes the counters measured for the KDA call: every KDA kernel's stored figure, when all of them
     # are current for this source
     traffic = None
-    if w.name == wl.WORKLOADS[WORKLOAD_INDEX].name and not args.gated:
+    if w.name == wl.WORKLOADS[WORKLOAD_INDEX].name and not (args.gated or args.head_dim or args.sequential):
         parts = [stored_traffic(n) for n in kda_names]
         traffic = sum(parts) if parts and all(t is not None for t in parts) else None
     t_roof = (conv_bytes + kda_bytes) / (HBM_PEAK_GBS * 1e9)
@@ -760,7 +772,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": f"synthetic (seeded; {w.dtype} q|k|v, alpha, beta; fp32 conv weights; fp32 state)",
         "config": {"workload": f"{w.name}: {layout} = {T} tokens per sequence, B={B}, H={H}, d_k=d_v={d}, "
-                               f"chunk 64, conv 4-tap text / 3x3 image / 3x3x3 video, q/k L2-normalised, "
+                               + ("KDA on the token-by-token kernel, " if args.sequential else "chunk 64, ")
+                               + "conv 4-tap text / 3x3 image / 3x3x3 video, q/k L2-normalised, "
                                f"o and S_final written" + (", S0 given" if S0 is not None else "")
                                + (", output gate and per-head RMSNorm of Eq. 15 fused" if args.gated else ""),
                    "tokens_per_step": tokens,
