@@ -407,15 +407,22 @@ chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const 
  *   dalpha    device [B][T][H][dk], written, dtype dt
  *   dbeta     device [B][T][H], written, dtype dt
  *   dS0       device fp32 [B][H][dk][dv], written, or NULL
- *   workspace at least chimera_kda_bwd_workspace_size(...) bytes: the state before every
- *             16th token (from forward passes inside the call), per-slice partial sums, and
- *             per-segment states when the sequences are cut into segments
+ *   workspace at least chimera_kda_bwd_workspace_size(...) bytes (same flags)
  *
- * dk <= 128 (CHIMERA_ERR_UNSUPPORTED above). The recurrence runs token by token in fp32
- * (a checkpointed reverse pass); long sequences are cut into segments that run at once,
- * joined through each segment's transition product (the cut depends only on B, T, H and
- * dv); the flags that choose forward kernels are ignored. Asynchronous on `stream`; the
- * outputs must not alias the inputs.
+ * dk <= 128 (CHIMERA_ERR_UNSUPPORTED above). Long sequences are cut into segments that run
+ * at once, joined through each segment's transition product (the cut depends only on B, T,
+ * H, dk, dv, the dtype and the flags). Two paths:
+ *   - bf16 with dk = dv = 128 and T > 0, unless CHIMERA_KDA_SEQUENTIAL: the chunked form on
+ *     MFMA (16-token chunks; the reverse of the chunk step of Eq. 14 per chunk, the states
+ *     at chunk starts recomputed from forward passes inside the call and kept in the
+ *     workspace as bf16, B H ceil(T/16) 32 KiB, plus six fp32 d x d matrices per segment).
+ *     q, k, v, alpha and dout must be 8-byte aligned with qkv_stride a multiple of 4, else
+ *     CHIMERA_ERR_UNSUPPORTED before any launch. Like the chunked forward, it raises alpha
+ *     below e^-7.5 to e^-7.5 (dalpha is then the gradient at the raised value);
+ *   - otherwise token by token in fp32 (a checkpointed reverse pass: the fp32 state before
+ *     every 16th token and per-slice partial sums in the workspace).
+ * CHIMERA_KDA_NO_SPLIT is ignored. Asynchronous on `stream`; the outputs must not alias the
+ * inputs.
  */
 size_t chimera_kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
                                       uint32_t flags);
@@ -453,7 +460,8 @@ chimera_status chimera_gate_norm_bwd(const void* o, const void* gate, int64_t ga
  * and dS0 ([nseq][H][dk][dv] each; S0 and dS_final may be NULL for zero). Each run of
  * consecutive samples of equal length is one batched backward on views of the packed
  * tensors; the runs share the workspace (chimera_kda_bwd_varlen_workspace_size: the
- * largest run's need). An empty sample gives dS0 = dS_final.
+ * largest run's need). An empty sample gives dS0 = dS_final. Paths, flags and layout rules
+ * as for chimera_kda_bwd (a misaligned layout is refused before the first run launches).
  */
 size_t chimera_kda_bwd_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
                                              int64_t dv, chimera_dtype dt, uint32_t flags);

@@ -397,10 +397,12 @@ def kda_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, l2norm: bool = 
     return o, Sf
 
 
-def kda_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, l2norm: bool = True, grads=None, workspace=None):
+def kda_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, l2norm: bool = True, grads=None, workspace=None,
+            sequential: bool = False):
     """Gradients of kda_fwd (chimera_kda_bwd). Inputs as for kda_fwd; dout [B, T, H, dv]
     (input dtype), dS_final fp32 [B, H, dk, dv] or None. `grads` = (dq, dk, dv) tensors with
     the layout of q, k, v (views into one fused gradient are accepted), else fresh tensors.
+    sequential: the token-by-token kernels also for bf16 heads of 128 (CHIMERA_KDA_SEQUENTIAL).
     Returns dict dq, dk, dv, dalpha, dbeta, dS0."""
     import torch
     B, T, H, dk = k.shape
@@ -427,19 +429,20 @@ def kda_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, l2norm: bool = Tru
     dalpha = torch.empty_like(alpha)
     dbeta = torch.empty_like(beta)
     dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=k.device)
-    need = int(lib().chimera_kda_bwd_workspace_size(B, T, H, dk, dv, dt, KDA_L2NORM_QK if l2norm else 0))
+    flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0)
+    need = int(lib().chimera_kda_bwd_workspace_size(B, T, H, dk, dv, dt, flags))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("chimera_kda_bwd", lib().chimera_kda_bwd(
         _ptr(q), _ptr(k), _ptr(v), stride, _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dout), _ptr(dS_final),
         _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dalpha), _ptr(dbeta), _ptr(dS0), B, T, H, dk, dv, dt,
-        KDA_L2NORM_QK if l2norm else 0, _ptr(workspace), wbytes, _stream(k)))
+        flags, _ptr(workspace), wbytes, _stream(k)))
     return {"dq": dq, "dk": dkk, "dv": dvv, "dalpha": dalpha, "dbeta": dbeta, "dS0": dS0}
 
 
 def kda_bwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0, dout, dS_final=None, *, l2norm: bool = True, grads=None,
-                   workspace=None):
+                   workspace=None, sequential: bool = False):
     """Gradients of kda_fwd_varlen without a gate (chimera_kda_bwd_varlen): q, k, v [T, H, d] (views
     into one packed row), cu_seqlens the sample offsets; S0, dS_final, and the returned dS0 are
     [nseq, H, dk, dv] fp32. Returns dict dq, dk, dv, dalpha, dbeta, dS0."""
@@ -472,7 +475,7 @@ def kda_bwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0, dout, dS_final=None, *,
     dalpha = torch.empty_like(alpha)
     dbeta = torch.empty_like(beta)
     dS0 = torch.empty((nseq, H, dk, dv), dtype=torch.float32, device=k.device)
-    flags = KDA_L2NORM_QK if l2norm else 0
+    flags = (KDA_L2NORM_QK if l2norm else 0) | (KDA_SEQUENTIAL if sequential else 0)
     need = int(lib().chimera_kda_bwd_varlen_workspace_size(cu.ctypes.data, nseq, H, dk, dv, dt, flags))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libchimera_mshortconv.so")
 SOURCES = ["abi.cpp", "mshortconv.hip", "kda_sequential.hip", "kda_chunked.hip", "kda_backward.hip",
-           "noalloc.hip"]
+           "kda_bwd_chunked.hip", "noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",

@@ -492,11 +492,26 @@ chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const 
   return st;
 }
 
+// The backward runs on the chunked MFMA kernels for bf16 heads of 128 (unless
+// CHIMERA_KDA_SEQUENTIAL), on the token-by-token kernels otherwise.
+static bool bwd_chunked(int64_t T, int64_t dk, int64_t dv, chimera_dtype dt, uint32_t flags) {
+  return T > 0 && (flags & CHIMERA_KDA_SEQUENTIAL) == 0 && chm::kda_bwd_chunked_shape(dk, dv, dt == CHIMERA_BF16);
+}
+static size_t bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
+                            uint32_t flags) {
+  return bwd_chunked(T, dk, dv, dt, flags) ? chm::kda_bwd_chunked_workspace(B, T, H)
+                                           : chm::kda_bwd_workspace(B, T, H, dk, dv);
+}
+static hipError_t bwd_launch(const chm::KdaArgs& a, const chm::KdaGrads& g, chimera_dtype dt, uint32_t flags,
+                             void* workspace, hipStream_t stream) {
+  return bwd_chunked(a.T, a.dk, a.dv, dt, flags) ? chm::launch_kda_backward_chunked(a, g, workspace, stream)
+                                                 : chm::launch_kda_backward(a, g, workspace, stream);
+}
+
 size_t chimera_kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
                                       uint32_t flags) {
-  (void)flags;
   if (!kda_sizes_ok(B, T, H, dk, dv) || dk > 128 || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
-  return chm::kda_bwd_workspace(B, T, H, dk, dv);
+  return bwd_workspace(B, T, H, dk, dv, dt, flags);
 }
 
 chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int64_t qkv_stride, const void* alpha,
@@ -515,7 +530,7 @@ chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int6
       return CHIMERA_ERR_NULL;
     if (qkv_stride < H * dk || qkv_stride < H * dv) return CHIMERA_ERR_SHAPE;
   }
-  const size_t need = chm::kda_bwd_workspace(B, T, H, dk, dv);
+  const size_t need = bwd_workspace(B, T, H, dk, dv, dt, flags);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
   chm::KdaArgs a{};
   a.q = q; a.k = k; a.v = v; a.qkv_stride = qkv_stride; a.alpha = alpha; a.beta = beta;
@@ -524,7 +539,8 @@ chimera_status chimera_kda_bwd(const void* q, const void* k, const void* v, int6
   a.bf16 = dt == CHIMERA_BF16;
   a.l2norm = (flags & CHIMERA_KDA_L2NORM_QK) != 0;
   const chm::KdaGrads g{dout, dS_final, dq, dk_out, dv_out, dalpha, dbeta, dS0};
-  return hip_status(chm::launch_kda_backward(a, g, workspace, stream));
+  if (bwd_chunked(T, dk, dv, dt, flags) && !chm::kda_bwd_chunked_layout_ok(a, g)) return CHIMERA_ERR_UNSUPPORTED;
+  return hip_status(bwd_launch(a, g, dt, flags, workspace, stream));
 }
 
 chimera_status chimera_gate_norm_bwd(const void* o, const void* gate, int64_t gate_stride, const float* norm_weight,
@@ -553,7 +569,7 @@ size_t chimera_kda_bwd_varlen_workspace_size(const int64_t* cu_seqlens, int32_t 
   if (!kda_sizes_ok(1, cu_seqlens[nseq], H, dk, dv)) return 0;
   size_t need = 0;
   for (const chm::KdaRun& r : varlen_runs(cu_seqlens, nseq))
-    need = std::max(need, chm::kda_bwd_workspace(r.count, r.len, H, dk, dv));
+    need = std::max(need, bwd_workspace(r.count, r.len, H, dk, dv, dt, flags));
   return need;
 }
 
@@ -579,8 +595,15 @@ chimera_status chimera_kda_bwd_varlen(const void* q, const void* k, const void* 
   }
   const std::vector<chm::KdaRun> runs = varlen_runs(cu_seqlens, nseq);
   size_t need = 0;
-  for (const chm::KdaRun& r : runs) need = std::max(need, chm::kda_bwd_workspace(r.count, r.len, H, dk, dv));
+  for (const chm::KdaRun& r : runs) need = std::max(need, bwd_workspace(r.count, r.len, H, dk, dv, dt, flags));
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
+  if (rows > 0 && bwd_chunked(rows, dk, dv, dt, flags)) {
+    // a run's views start a whole number of rows in, which keeps the base pointers' alignment
+    chm::KdaArgs a{};
+    a.q = q; a.k = k; a.v = v; a.qkv_stride = qkv_stride; a.alpha = alpha;
+    const chm::KdaGrads g{dout, dS_final, dq, dk_out, dv_out, dalpha, dbeta, dS0};
+    if (!chm::kda_bwd_chunked_layout_ok(a, g)) return CHIMERA_ERR_UNSUPPORTED;
+  }
   // each run of equal lengths is a batch on views of the packed tensors; the runs share the workspace
   const int64_t e = dt == CHIMERA_BF16 ? 2 : 4;
   auto at = [&](const void* p, int64_t elems) {
@@ -602,7 +625,7 @@ chimera_status chimera_kda_bwd_varlen(const void* q, const void* k, const void* 
                           mut(dq, r.start * qkv_stride), mut(dk_out, r.start * qkv_stride),
                           mut(dv_out, r.start * qkv_stride), mut(dalpha, r.start * H * dk), mut(dbeta, r.start * H),
                           dS0 == nullptr ? nullptr : dS0 + r.sidx0 * state};
-    const hipError_t he = chm::launch_kda_backward(a, g, workspace, stream);
+    const hipError_t he = bwd_launch(a, g, dt, flags, workspace, stream);
     if (he != hipSuccess) return CHIMERA_ERR_HIP;
   }
   return CHIMERA_OK;

@@ -126,6 +126,20 @@ struct KdaGrads {
 size_t kda_bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
 hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* workspace, hipStream_t stream,
                                Marks* marks = nullptr);
+// The same gradients on MFMA (bf16, dk = dv = 128; the inputs and dout 8-byte aligned with a
+// token stride that is a multiple of 4): 16-token chunks, each sequence cut into segments
+// joined by fp32 chains; the workspace holds the bf16 state before every chunk.
+bool kda_bwd_chunked_shape(int64_t dk, int64_t dv, bool bf16);
+bool kda_bwd_chunked_layout_ok(const KdaArgs& a, const KdaGrads& g);
+size_t kda_bwd_chunked_workspace(int64_t B, int64_t T, int64_t H);
+hipError_t launch_kda_backward_chunked(const KdaArgs& a, const KdaGrads& g, void* workspace, hipStream_t stream,
+                                       Marks* marks = nullptr);
+// The segment chains of the backward passes for BH (sequence, head) pairs of nseg segments each,
+// M [BH][nseg][dk][dk], X, Y [BH][nseg][dk][dv], init [BH][dk][dv] or null (fp32, row-major):
+// forward (back false) Y_0 = init, Y_p = M_{p-1} Y_{p-1} + X_{p-1}; backward (back true)
+// Y_{nseg-1} = init, Y_p = M_{p+1}^T Y_{p+1} + X_{p+1}.
+hipError_t launch_kda_chain(bool back, const float* M, const float* X, const float* init, float* Y, int64_t BH,
+                            int nseg, int dk, int dv, hipStream_t stream);
 // Backward of the gate and norm: do [rows][dv] and dgate (gate layout) in the dtype, dnorm_w [dv]
 // fp32 written (summed over rows) when not null; rows = B * T * H.
 hipError_t launch_gate_norm_backward(const void* o, const void* gate, int64_t gate_stride, const float* norm_w,

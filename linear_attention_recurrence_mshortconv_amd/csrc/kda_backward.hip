@@ -811,6 +811,19 @@ hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* worksp
                 : launch_bwd_t<float>(a, g, G_end, c.len, c.nseg, ckpt, part, stream, marks);
 }
 
+hipError_t launch_kda_chain(bool back, const float* M, const float* X, const float* init, float* Y, int64_t BH,
+                            int nseg, int dk, int dv, hipStream_t stream) {
+  const int64_t chains = BH * ((dv + 15) / 16);
+  if (chains == 0) return hipSuccess;
+  if (chains > 0x7fffffff || dk > 128) return hipErrorInvalidValue;
+  if (back)
+    hipLaunchKernelGGL(kda_chain_kernel<true>, dim3((unsigned)chains), dim3(256), 0, stream, M, X, init, Y, nseg, dk, dv);
+  else
+    hipLaunchKernelGGL(kda_chain_kernel<false>, dim3((unsigned)chains), dim3(256), 0, stream, M, X, init, Y, nseg, dk,
+                       dv);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_norm_backward(const void* o, const void* gate, int64_t gate_stride, const float* norm_w,
                                      float eps, const void* dy, void* dout, void* dgate, float* dnorm_w, int64_t rows,
                                      int64_t H, int64_t dv, bool bf16, hipStream_t stream) {

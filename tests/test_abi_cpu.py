@@ -209,8 +209,20 @@ def test_backward_argument_errors():
     assert call(stride=100) == 2
     assert call() == 6                                                  # workspace missing
     assert call(B=0) == 0
+    # bf16 heads of 128 run the chunked backward: the bf16 state before every 16-token chunk, plus
+    # six fp32 matrices per segment (here 5 segments of 272 tokens per head)
     n = int(L.chimera_kda_bwd_workspace_size(1, 64 * 20 + 3, 16, 128, 128, 1, 1))
-    assert n >= 4 * (16 * 81 * 128 * 128 + 8 * 1283 * 16 * (3 * 128 + 1))   # checkpoints + slice partials
+    assert n == 2 * 16 * 81 * 128 * 128 + 4 * 6 * 16 * 5 * 128 * 128
+    # the token-by-token backward (CHIMERA_KDA_SEQUENTIAL, or fp32): fp32 checkpoints + slice partials
+    for dt, fl in ((1, 3), (0, 1)):
+        n = int(L.chimera_kda_bwd_workspace_size(1, 64 * 20 + 3, 16, 128, 128, dt, fl))
+        assert n >= 4 * (16 * 81 * 128 * 128 + 8 * 1283 * 16 * (3 * 128 + 1))
+    # the chunked backward reads q, k, v, alpha and dout as 8-byte pieces: other layouts are refused
+    small = int(L.chimera_kda_bwd_workspace_size(1, 8, 2, 128, 128, 1, 1))
+    big = np.zeros(small + 256, dtype=np.uint8)
+    wsp = (big.ctypes.data + 255) // 256 * 256
+    assert call(ws=wsp, wsb=small) == 5                                 # q = 1: misaligned
+    assert call(ws=wsp, wsb=small, stride=258, q=8, k=16, v=24, a=32, do=40) == 5   # stride % 4
     arr = chm.segment_array([dict(kind=0, start=0, length=4)])
     cb = lambda **kw: L.chimera_mshortconv_bwd(kw.get("x", 1), kw.get("dy", 2), kw.get("dx", 3), kw.get("dwt", 4),
                                                kw.get("dwv", 5), 1, 4, kw.get("C", 8), 1, 6, 7, arr, 1, None)

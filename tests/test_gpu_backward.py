@@ -93,6 +93,37 @@ def test_kda_bwd_bf16_d128(chm, T):
         _close_bf16(got[n], ref[n], f"{n} T={T}")
 
 
+@pytest.mark.parametrize("B,T,H,l2norm,init,decay", [
+    (1, 1000, 2, True, True, 0.3),     # three segments of 336, 336 and 328 tokens; a ragged last chunk
+    (2, 77, 3, True, False, 0.3),      # one segment with a ragged chunk, two batch items, no S0 / dS_final
+    (1, 16, 1, False, True, 0.3),      # exactly one chunk, no normalisation
+    (1, 600, 1, True, True, 3.0),      # strong decay (alpha down to about e^-8 within a chunk), 2 segments
+])
+def test_kda_bwd_chunked_bf16(chm, B, T, H, l2norm, init, decay):
+    """The chunked MFMA backward (bf16, d = 128; 16-token chunks, segments joined by chains) against
+    the fp64 autograd oracle, and the token-by-token backward (CHIMERA_KDA_SEQUENTIAL) on the same
+    inputs against it too."""
+    import torch
+    rng = np.random.default_rng(300 + T + H)
+    q, k, v, alpha, beta, S0, do, dS = _case(rng, B, T, H, 128, 128, "bf16")
+    alpha = wl.round_to_bf16(np.exp(-decay * np.logaddexp(0, rng.standard_normal(alpha.shape))).astype(np.float32))
+    # raised to the chunked kernels' floor (bf16 0x3A11, about e^-7.5), so that their clamp changes nothing
+    alpha = np.maximum(alpha, np.array([0x3A110000], dtype=np.uint32).view(np.float32)[0])
+    if not l2norm:   # unit-norm scale without the normalisation, so that the recurrence stays bounded
+        q, k = wl.round_to_bf16(q / np.float32(np.sqrt(128))), wl.round_to_bf16(k / np.float32(np.sqrt(128)))
+    if not init:
+        S0 = dS = None
+    dev = lambda a: to_device(a, "bf16")
+    opt = lambda a: None if a is None else torch.from_numpy(a).cuda()
+    ref = kda_backward_ref(q, k, v, alpha, beta, S0, do, dS, l2norm=l2norm)
+    for seq in (False, True):
+        g = chm.kda_bwd(dev(q), dev(k), dev(v), dev(alpha), dev(beta), opt(S0), dev(do), opt(dS), l2norm=l2norm,
+                        sequential=seq)
+        got = {n: to_host(t) for n, t in g.items()}
+        for n in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+            _close_bf16(got[n], ref[n], f"{n} (sequential={seq})")
+
+
 def test_kda_bwd_fp32_segments(chm):
     """fp32, T = 700 on two 32-wide heads: the sequence is cut into segments of 80 tokens (the
     last 60) whose reverse passes run at once, joined by the chains of transition products;
