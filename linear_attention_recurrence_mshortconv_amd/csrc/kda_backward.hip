@@ -33,6 +33,7 @@
 // adjoint gather: p is s moved back by the tap's offset, inside the same segment; for an
 // image grid, the same 3x3 conv with the taps mirrored in both directions) and
 // dw[c, tap] = sum_p x[src(p, tap), c] dy[p, c] (summed over tokens and batch items).
+#include <atomic>
 #include <vector>
 
 #include "dtypes.h"
@@ -290,13 +291,18 @@ __global__ __launch_bounds__(256) void kda_bwd_local_kernel(
 // term) and a term X_p per segment:
 //   forward (BACK false): Y_0 = init, Y_p = M_{p-1} Y_{p-1} + X_{p-1}: the state at each segment's start;
 //   backward (BACK true): Y_{P-1} = init, Y_p = M_{p+1}^T Y_{p+1} + X_{p+1}: dL/dS at each segment's end.
-// init may be null (zero). dk <= 128.
-template <bool BACK>
+// init may be null (zero). dk <= 128. Each step's matrix goes to LDS whole (mt[j][r] = the factor
+// of entry j in row r of the product), and the next step's is loaded into registers meanwhile, so
+// a step waits for one load only at the start of the chain.
+constexpr int kChainPitch = 132;   // mt rows: 16-byte aligned, 4 banks apart
+constexpr int kChainLds = (128 * kChainPitch + 128 * 16) * (int)sizeof(float);
+template <bool BACK, bool FULL>   // FULL: dk = 128 (16-byte loads of M)
 __global__ __launch_bounds__(256) void kda_chain_kernel(const float* __restrict__ M, const float* __restrict__ X,
                                                         const float* __restrict__ init, float* __restrict__ Y,
                                                         int nseg, int dk, int dv) {
-  __shared__ float cur[128][16];
-  __shared__ float mt[16][129];
+  extern __shared__ float chain_lds[];
+  float (*mt)[kChainPitch] = reinterpret_cast<float (*)[kChainPitch]>(chain_lds);
+  float (*cur)[16] = reinterpret_cast<float (*)[16]>(chain_lds + 128 * kChainPitch);
   const int n_vs = (dv + 15) / 16;
   const int vs = blockIdx.x % n_vs;
   const int64_t bh = blockIdx.x / n_vs;
@@ -304,51 +310,137 @@ __global__ __launch_bounds__(256) void kda_chain_kernel(const float* __restrict_
   const int col = vs * 16 + colid;
   const bool col_ok = col < dv;
   auto yat = [&](int p, int row) { return ((bh * nseg + p) * dk + row) * dv + col; };
+  // M entries e = 4 (tid + 256 m) + u (FULL) or tid + 256 m (row e / dk, column e % dk)
+  const int nm = dk * dk;
+  constexpr int NP = FULL ? 16 : 64;
+  float4 pre4[FULL ? NP : 1];
+  float pre[FULL ? 1 : NP];
+  float xv[8];
+  auto load = [&](int src) {   // M and X of segment src
+    const float* Mp = M + (bh * nseg + src) * (int64_t)nm;
+    if constexpr (FULL) {
+#pragma unroll
+      for (int m = 0; m < NP; ++m) pre4[m] = reinterpret_cast<const float4*>(Mp)[tid + 256 * m];
+    } else {
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const int e = tid + 256 * m;
+        pre[m] = e < nm ? Mp[e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * rt + i;
+      xv[i] = col_ok && row < dk ? X[yat(src, row)] : 0.f;
+    }
+  };
+  auto put = [&](int i, int j, float x) {   // M[i][j]
+    if (BACK) mt[i][j] = x;                 // row j of M^T takes M[i][j] at entry i
+    else mt[j][i] = x;                      // row i of M takes M[i][j] at entry j
+  };
+  auto stage = [&]() {
+    if constexpr (FULL) {
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const int e = 4 * (tid + 256 * m), i = e >> 7, j = e & 127;
+        put(i, j, pre4[m].x);
+        put(i, j + 1, pre4[m].y);
+        put(i, j + 2, pre4[m].z);
+        put(i, j + 3, pre4[m].w);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const int e = tid + 256 * m;
+        if (e < nm) put(e / dk, e % dk, pre[m]);
+      }
+    }
+  };
   {
     const int p0 = BACK ? nseg - 1 : 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = rt + 16 * i;
+      const int row = 8 * rt + i;
       const bool ok = col_ok && row < dk;
       const float val = (ok && init != nullptr) ? init[(bh * dk + row) * dv + col] : 0.f;
       cur[row][colid] = val;
       if (ok) Y[yat(p0, row)] = val;
     }
   }
+  if (nseg > 1) load(BACK ? nseg - 1 : 0);
   for (int step = 1; step < nseg; ++step) {
     const int p = BACK ? nseg - 1 - step : step;   // the entry formed
     const int src = BACK ? p + 1 : p - 1;          // the segment whose M and X form it
-    const float* Mp = M + (bh * nseg + src) * dk * dk;
+    lds_barrier();   // the previous step's reads of mt are done (the next matrix's loads stay in flight)
+    stage();
+    float xs[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs[i] = xv[i];
+    lds_barrier();
+    if (step + 1 < nseg) load(BACK ? src - 1 : src + 1);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j0 = 0; j0 < dk; j0 += 16) {
-      __syncthreads();   // cur is written, the previous tile is read
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int e = tid + 256 * m;
-        const int jj = BACK ? e >> 7 : e & 15, r = BACK ? e & 127 : e >> 4;
-        const bool ok = j0 + jj < dk && r < dk;
-        mt[jj][r] = !ok ? 0.f : BACK ? Mp[(j0 + jj) * dk + r] : Mp[r * dk + j0 + jj];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const float cj = cur[j0 + jj][colid];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(mt[jj][rt + 16 * i], cj, acc[i]);
-      }
+    // thread rows 8 rt .. 8 rt + 7: two 16-byte reads of mt per entry j
+#pragma unroll 4
+    for (int j = 0; j < dk; ++j) {
+      const float cj = cur[j][colid];
+      const float4 m0 = *reinterpret_cast<const float4*>(&mt[j][8 * rt]);
+      const float4 m1 = *reinterpret_cast<const float4*>(&mt[j][8 * rt + 4]);
+      acc[0] = fmaf(m0.x, cj, acc[0]);
+      acc[1] = fmaf(m0.y, cj, acc[1]);
+      acc[2] = fmaf(m0.z, cj, acc[2]);
+      acc[3] = fmaf(m0.w, cj, acc[3]);
+      acc[4] = fmaf(m1.x, cj, acc[4]);
+      acc[5] = fmaf(m1.y, cj, acc[5]);
+      acc[6] = fmaf(m1.z, cj, acc[6]);
+      acc[7] = fmaf(m1.w, cj, acc[7]);
     }
-    __syncthreads();   // every read of cur is done
+    lds_barrier();   // every read of cur is done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = rt + 16 * i;
+      const int row = 8 * rt + i;
       const bool ok = col_ok && row < dk;
-      const float val = ok ? acc[i] + X[yat(src, row)] : 0.f;
+      const float val = ok ? acc[i] + xs[i] : 0.f;
       cur[row][colid] = val;
       if (ok) Y[yat(p, row)] = val;
     }
   }
+}
+
+// The chain kernels' LDS (above 64 KB) is allowed once per device; the flag is atomic so that
+// host threads calling at once race on nothing (setting it twice is harmless).
+hipError_t chain_attr() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::atomic<bool> done[64];
+  if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const void* fns[] = {reinterpret_cast<const void*>(&kda_chain_kernel<false, false>),
+                       reinterpret_cast<const void*>(&kda_chain_kernel<true, false>),
+                       reinterpret_cast<const void*>(&kda_chain_kernel<false, true>),
+                       reinterpret_cast<const void*>(&kda_chain_kernel<true, true>)};
+  for (const void* f : fns) {
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kChainLds);
+    if (e != hipSuccess) return e;
+  }
+  if (dev >= 0 && dev < 64) done[dev].store(true, std::memory_order_release);
+  return hipSuccess;
+}
+// one chain launch (see kda_chain_kernel)
+hipError_t chain_launch(bool back, const float* M, const float* X, const float* init, float* Y, int64_t chains,
+                        int nseg, int dk, int dv, hipStream_t stream) {
+  const hipError_t e = chain_attr();
+  if (e != hipSuccess) return e;
+  const dim3 g((unsigned)chains), t(256);
+  if (dk == 128) {
+    if (back) hipLaunchKernelGGL((kda_chain_kernel<true, true>), g, t, kChainLds, stream, M, X, init, Y, nseg, dk, dv);
+    else hipLaunchKernelGGL((kda_chain_kernel<false, true>), g, t, kChainLds, stream, M, X, init, Y, nseg, dk, dv);
+  } else {
+    if (back) hipLaunchKernelGGL((kda_chain_kernel<true, false>), g, t, kChainLds, stream, M, X, init, Y, nseg, dk, dv);
+    else hipLaunchKernelGGL((kda_chain_kernel<false, false>), g, t, kChainLds, stream, M, X, init, Y, nseg, dk, dv);
+  }
+  return hipGetLastError();
 }
 
 // Adds the slices' partials of one (token, head) row and applies the L2 normalisation's
@@ -565,6 +657,166 @@ __global__ __launch_bounds__(256) void conv_bwd_dw_kernel(const T* __restrict__ 
     for (int i = 0; i < 4; ++i) atomicAdd(dw + (c0 + i) * NW + TAP0 + t, acc[t][i]);
 }
 
+// dw of a grid segment. A wave owns 64 x CPT channels and a range of tokens, and walks it along
+// the grid rows keeping the 3 x 3 (x frames) window of x around the current token in registers:
+// per token it loads the window's new column only (3 or 9 rows instead of 9 or 27 taps), four
+// tokens' loads at a time. Each window row is a buffer descriptor over one grid row of x (empty
+// for rows outside the grid), addressed by the column through the wave-uniform offset, so
+// columns past the edge read zero with no branch or select. The block's four waves walk four
+// consecutive ranges of the same channels and add their sums in LDS before one atomic per value.
+// Frames: one (an image: dw_vis taps 18..26) or three (video: all 27).
+template <typename T, int CPT>
+__device__ __forceinline__ void ld_cpt(__amdgpu_buffer_rsrc_t r, int voff, int soff, float (&o)[CPT]) {
+  if constexpr (sizeof(T) == 2 && CPT == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    o[0] = bf_lo(v[0]); o[1] = bf_hi(v[0]); o[2] = bf_lo(v[1]); o[3] = bf_hi(v[1]);
+  } else if constexpr (sizeof(T) == 2) {
+    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    o[0] = bf_lo(v); o[1] = bf_hi(v);
+  } else if constexpr (CPT == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    o[0] = __uint_as_float(v[0]); o[1] = __uint_as_float(v[1]); o[2] = __uint_as_float(v[2]); o[3] = __uint_as_float(v[3]);
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    o[0] = __uint_as_float(v[0]); o[1] = __uint_as_float(v[1]);
+  }
+}
+constexpr int kDwWaves = 4;
+template <typename T, int KIND, int CPT>
+__global__ __launch_bounds__(64 * kDwWaves) void conv_bwd_dw_grid_kernel(const T* __restrict__ x,
+                                                                         const T* __restrict__ dy,
+                                                                         float* __restrict__ dw, int64_t Ttot, int64_t C,
+                                                                         Seg seg, int64_t tokens_per_range) {
+  constexpr int KT = KIND == SEG_IMAGE ? 1 : 3;
+  constexpr int TAP0 = KIND == SEG_IMAGE ? 18 : 0;
+  constexpr int NV = KT * 9 * CPT;
+  constexpr int U = 4;   // tokens whose loads are issued together
+  __shared__ float red[kDwWaves - 1][NV][64];
+  // the wave index through readfirstlane: everything the buffer descriptors are built from is then
+  // visibly wave-uniform (a descriptor in vector registers would loop over lanes at every load)
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t cg = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t p0 = ((int64_t)blockIdx.y * kDwWaves + w) * tokens_per_range;
+  const int64_t b = blockIdx.z;
+  const bool cok = cg < C / CPT;
+  const int64_t c0 = cok ? cg * CPT : 0;
+  const int voff = (int)(c0 * (int64_t)sizeof(T));
+  const int rowb = (int)(seg.width * C * (int64_t)sizeof(T));   // bytes per grid row (below 2^31: checked by the host)
+  const int colb = (int)(C * (int64_t)sizeof(T));
+  const T* xb = x + b * Ttot * C;
+  const T* dyb = dy + b * Ttot * C;
+  const int H = seg.height, W = seg.width;
+  const int64_t hw = (int64_t)H * W;
+  float acc[KT][3][3][CPT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) acc[kt][kh][kw][i] = 0.f;
+  if (p0 < seg.length) {   // wave-uniform
+    const int64_t p1 = min<int64_t>(seg.length, p0 + tokens_per_range);
+    int f = (int)(p0 / hw), hh = (int)((p0 / W) % H), ww = (int)(p0 % W);
+    float win[KT][3][3][CPT];
+    int64_t local = p0;
+    while (local < p1) {
+      const int run = (int)min<int64_t>(W - ww, p1 - local);   // tokens left on this grid row
+      __amdgpu_buffer_rsrc_t xr[KT][3];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+          const int ff = f + kt - (KT - 1), h2 = hh + kh - 1;
+          const bool rok = ff >= 0 && h2 >= 0 && h2 < H;
+          xr[kt][kh] = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(xb + (rok ? seg.start + (int64_t)ff * hw + (int64_t)h2 * W : 0) * C), 0, rok ? rowb : 0,
+              0x00020000);
+          if (ww > 0) ld_cpt<T, CPT>(xr[kt][kh], voff, (ww - 1) * colb, win[kt][kh][0]);
+          else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) win[kt][kh][0][i] = 0.f;
+          }
+          ld_cpt<T, CPT>(xr[kt][kh], voff, ww * colb, win[kt][kh][1]);
+        }
+      const auto dr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(dyb + (seg.start + (int64_t)f * hw + (int64_t)hh * W) * C), 0, rowb, 0x00020000);
+      for (int r = 0; r < run; r += U) {
+        float col[U][KT][3][CPT], g[U][CPT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int kh = 0; kh < 3; ++kh) ld_cpt<T, CPT>(xr[kt][kh], voff, (ww + r + u + 1) * colb, col[u][kt][kh]);
+          ld_cpt<T, CPT>(dr, voff, (ww + r + u) * colb, g[u]);
+          if (r + u >= run) {   // past the range's end on this row: adds nothing (wave-uniform)
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) g[u][i] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int kh = 0; kh < 3; ++kh) {
+#pragma unroll
+              for (int i = 0; i < CPT; ++i) win[kt][kh][2][i] = col[u][kt][kh][i];
+#pragma unroll
+              for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+                for (int i = 0; i < CPT; ++i)
+                  acc[kt][kh][kw][i] = fmaf(win[kt][kh][kw][i], g[u][i], acc[kt][kh][kw][i]);
+#pragma unroll
+              for (int i = 0; i < CPT; ++i) {
+                win[kt][kh][0][i] = win[kt][kh][1][i];
+                win[kt][kh][1][i] = win[kt][kh][2][i];
+              }
+            }
+      }
+      local += run;
+      ww += run;
+      if (ww == W) {
+        ww = 0;
+        if (++hh == H) {
+          hh = 0;
+          ++f;
+        }
+      }
+    }
+  }
+  // the four waves' sums, then one atomic per value
+  if (w > 0) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) red[w - 1][((kt * 3 + kh) * 3 + kw) * CPT + i][lane] = acc[kt][kh][kw][i];
+  }
+  __syncthreads();
+  if (w == 0 && cok) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) {
+            const int v = ((kt * 3 + kh) * 3 + kw) * CPT + i;
+            float t = acc[kt][kh][kw][i];
+#pragma unroll
+            for (int ww2 = 0; ww2 < kDwWaves - 1; ++ww2) t += red[ww2][v][lane];
+            atomicAdd(dw + (c0 + i) * kVisTaps + TAP0 + 9 * kt + 3 * kh + kw, t);
+          }
+  }
+}
+
 // Backward of Eq. 15's gate and norm (page 1, section 3.3), y = Sigmoid(g) * o r * w per
 // (token, head) row of dv channels, r = 1 / sqrt(mean(o^2) + eps): with n = o r, s = Sigmoid(g)
 // and dn = dy s w,
@@ -667,16 +919,30 @@ hipError_t conv_bwd_t(const void* x, const void* dy, void* dx, float* dw_text, f
     }
     // dw: about 512 token ranges per segment and batch item
     const int64_t per = std::max<int64_t>(16, (sg.length + 511) / 512);
-    const dim3 gw((unsigned)((C / 4 + 255) / 256), (unsigned)((sg.length + per - 1) / per), (unsigned)B);
-    if (sg.kind == SEG_TEXT)
-      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_TEXT>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
-                         static_cast<const T*>(dy), dw_text, Ttot, C, sg, per);
-    else if (sg.frames == 1)
-      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_IMAGE>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
-                         static_cast<const T*>(dy), dw_vis, Ttot, C, sg, per);
-    else
-      hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_VIDEO>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
-                         static_cast<const T*>(dy), dw_vis, Ttot, C, sg, per);
+    const int64_t ranges = (sg.length + per - 1) / per;
+    const bool grid_rows = (int64_t)sg.width * C * (int64_t)sizeof(T) < (int64_t(1) << 31);
+    if (sg.kind == SEG_TEXT || !grid_rows) {
+      const dim3 gw((unsigned)((C / 4 + 255) / 256), (unsigned)ranges, (unsigned)B);
+      if (sg.kind == SEG_TEXT)
+        hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_TEXT>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
+                           static_cast<const T*>(dy), dw_text, Ttot, C, sg, per);
+      else if (sg.frames == 1)
+        hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_IMAGE>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
+                           static_cast<const T*>(dy), dw_vis, Ttot, C, sg, per);
+      else
+        hipLaunchKernelGGL((conv_bwd_dw_kernel<T, SEG_VIDEO>), gw, dim3(256), 0, stream, static_cast<const T*>(x),
+                           static_cast<const T*>(dy), dw_vis, Ttot, C, sg, per);
+    } else {
+      const unsigned ry = (unsigned)((ranges + kDwWaves - 1) / kDwWaves);
+      if (sg.frames == 1)
+        hipLaunchKernelGGL((conv_bwd_dw_grid_kernel<T, SEG_IMAGE, 4>), dim3((unsigned)((C / 4 + 63) / 64), ry, (unsigned)B),
+                           dim3(64 * kDwWaves), 0, stream, static_cast<const T*>(x), static_cast<const T*>(dy), dw_vis,
+                           Ttot, C, sg, per);
+      else
+        hipLaunchKernelGGL((conv_bwd_dw_grid_kernel<T, SEG_VIDEO, 2>), dim3((unsigned)((C / 2 + 63) / 64), ry, (unsigned)B),
+                           dim3(64 * kDwWaves), 0, stream, static_cast<const T*>(x), static_cast<const T*>(dy), dw_vis,
+                           Ttot, C, sg, per);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -783,9 +1049,7 @@ hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* worksp
     sm.identity = 1;
     e = launch_kda_sequential(fm, stream, marks, nullptr, &sm);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_chain_kernel<false>, dim3((unsigned)chains), dim3(256), 0, stream, Mw, Lw, a.S0, Sst,
-                       c.nseg, (int)a.dk, (int)a.dv);
-    e = hipGetLastError();
+    e = chain_launch(false, Mw, Lw, a.S0, Sst, chains, c.nseg, (int)a.dk, (int)a.dv, stream);
     if (e != hipSuccess) return e;
     SeqSegs sc;
     sc.len = c.len;
@@ -797,9 +1061,7 @@ hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* worksp
                : launch_local_t<float>(a, g, Ew, c.len, c.nseg, stream);
     if (e == hipSuccess) e = mark_after(marks, "kda_bwd_local_kernel", stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kda_chain_kernel<true>, dim3((unsigned)chains), dim3(256), 0, stream, Mw, Ew, g.dS_final, Gend,
-                       c.nseg, (int)a.dk, (int)a.dv);
-    e = hipGetLastError();
+    e = chain_launch(true, Mw, Ew, g.dS_final, Gend, chains, c.nseg, (int)a.dk, (int)a.dv, stream);
     if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
     if (e != hipSuccess) return e;
     G_end = Gend;
@@ -816,12 +1078,7 @@ hipError_t launch_kda_chain(bool back, const float* M, const float* X, const flo
   const int64_t chains = BH * ((dv + 15) / 16);
   if (chains == 0) return hipSuccess;
   if (chains > 0x7fffffff || dk > 128) return hipErrorInvalidValue;
-  if (back)
-    hipLaunchKernelGGL(kda_chain_kernel<true>, dim3((unsigned)chains), dim3(256), 0, stream, M, X, init, Y, nseg, dk, dv);
-  else
-    hipLaunchKernelGGL(kda_chain_kernel<false>, dim3((unsigned)chains), dim3(256), 0, stream, M, X, init, Y, nseg, dk,
-                       dv);
-  return hipGetLastError();
+  return chain_launch(back, M, X, init, Y, chains, nseg, dk, dv, stream);
 }
 
 hipError_t launch_gate_norm_backward(const void* o, const void* gate, int64_t gate_stride, const float* norm_w,

@@ -61,6 +61,7 @@ constexpr int OP = D + 8;               // [BC][OP] bf16 operand rows (channels 
 constexpr int SP = D + 8;               // [D][SP] bf16 transposed state copies
 constexpr int TP = BC + 4;              // [BC][TP] bf16 16 x 16 matrices
 constexpr float kL2Eps = 1e-6f;
+constexpr int kWaitVm0 = 0x0F70;        // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone)
 constexpr int kTargetBlocks = 256;      // one block per CU
 constexpr int64_t kMinSeg = 256;        // tokens per segment at least
 
@@ -86,6 +87,7 @@ struct BwdArgs {
   const float* Sin;        // start states: [bh][nseg][D][D] (nseg > 1) or S0 [bh][D][D]; null = zero
   float* Sout;             // summary end states [bh][nseg][D][D]: L (blocks < BHP), M (blocks >= BHP)
   uint4* ckpt;             // [bh][ceil(T / BC)][8 waves][4][64 lanes] bf16 fragments
+  uint2* tfrag;            // [bh][ceil(T / BC)][2][64 lanes]: each chunk's T and T^T mma16 A fragments
   // gradient passes
   const float* Gin;        // dS at segment ends: [bh][nseg][D][D] or dS_final [bh][D][D]; null = zero
   float* Eout;             // local pass: dS at each segment's start [bh][nseg][D][D]
@@ -110,9 +112,12 @@ __device__ __forceinline__ float rowsum(float x) {
 __device__ __forceinline__ uint4 opfrag(const uint16_t* arr, int s, int l16, int q4) {
   return ld128(arr, l16 * OP + 32 * s + 8 * q4);
 }
-// A fragment of X^T (rows = channels 16 rt .. 16 rt + 15, k = tokens 4 q4 .. + 3) for mma16
-__device__ __forceinline__ uint2 opT16(const uint16_t* arr, int rt, int l16, int q4) {
-  return ld_tr(&arr[(4 * q4 + (l16 >> 2)) * OP + cpos(16 * rt + 4 * (l16 & 3))]);
+// A fragment of X^T (rows = channels 16 rt .. 16 rt + 15, k = tokens 4 q4 .. + 3) for mma16:
+// the transposing read at token 4 q4 + l16 / 4, position cpos(16 rt + 4 (l16 % 4)) =
+// 32 (rt / 2) + 4 (rt % 2) + 8 (l16 % 4), written as the lane's base plus a constant
+__device__ __forceinline__ int opT_base(int l16, int q4) { return (4 * q4 + (l16 >> 2)) * OP + 8 * (l16 & 3); }
+__device__ __forceinline__ uint2 opT16(const uint16_t* arr, int rt, int base) {
+  return ld_tr(&arr[base + 32 * (rt >> 1) + 4 * (rt & 1)]);
 }
 // B fragment (k = tokens 4 q4 .. + 3, n = channel or v at row position p0 + l16) for mma16
 __device__ __forceinline__ uint2 posB16(const uint16_t* arr, int p0, int l16, int q4) {
@@ -177,33 +182,97 @@ __device__ __forceinline__ void factors_q(const float (&a)[BC], Fac4& f) {
     }
   }
 }
-// tq wave-uniform
-__device__ __forceinline__ Fac4 factors4(const float* al, int tq, int c) {
+// Operands of tokens 4 TQ .. 4 TQ + 3 of channel c into the operand arrays (bf16, channels at
+// cpos): -K^, K_, Kr, Kc and (with q) Q^, Qr; with fac also the fp32 factors e^{g}, e^{g_n - g},
+// e^{g - m} ([BC][D]); e^{g_n} of the channel when TQ = 0.
+struct OpOut {
+  uint16_t *kn, *kb, *kr, *kc, *qh, *qr;
+  float *fg, *fb, *ff, *gn;
+};
+// Operand sets: kOpState (-K^, K_), kOpLocal (also Kc, Q^, Qr), kOpAll (also Kr)
+constexpr int kOpState = 0, kOpLocal = 1, kOpAll = 2;
+template <int TQ, int OPS, bool FAC>
+__device__ __forceinline__ void form_ops_q(const uint16_t* al, const uint16_t* kraw, const uint16_t* qraw, const float* rk,
+                                           const float* rq, const OpOut& o, int c) {
   float a[BC];
 #pragma unroll
-  for (int s = 0; s < BC; ++s) a[s] = al[s * D + c];
+  for (int s = 0; s < BC; ++s) a[s] = bf2f(al[s * D + c]);
   Fac4 f;
-  switch (__builtin_amdgcn_readfirstlane(tq)) {
-    case 0: factors_q<0>(a, f); break;
-    case 1: factors_q<1>(a, f); break;
-    case 2: factors_q<2>(a, f); break;
-    default: factors_q<3>(a, f); break;
+  factors_q<TQ>(a, f);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 4 * TQ + j, x = t * OP + cpos(c), e = t * D + c;
+    const float kn = bf2f(kraw[e]) * rk[t];
+    o.kn[x] = f2bf(-kn * f.g[j]);
+    o.kb[x] = f2bf(kn * f.bar[j]);
+    if (OPS == kOpAll) o.kr[x] = f2bf(kn * f.fw[j]);
+    if (OPS != kOpState) {
+      o.kc[x] = f2bf(kn * f.bw[j]);
+      const float qn = bf2f(qraw[e]) * rq[t];
+      o.qh[x] = f2bf(qn * f.g[j]);
+      o.qr[x] = f2bf(qn * f.fw[j]);
+    }
+    if (FAC) {
+      o.fg[e] = f.g[j];
+      o.fb[e] = f.bar[j];
+      o.ff[e] = f.fw[j];
+    }
   }
-  return f;
+  if (TQ == 0) o.gn[c] = f.gn;
+}
+// thread = channel c of tokens 4 tq .. + 3 (tq wave-uniform)
+template <int OPS, bool FAC>
+__device__ __forceinline__ void form_ops(const uint16_t* al, const uint16_t* kraw, const uint16_t* qraw, const float* rk,
+                                         const float* rq, const OpOut& o, int tq, int c) {
+  switch (__builtin_amdgcn_readfirstlane(tq)) {
+    case 0: form_ops_q<0, OPS, FAC>(al, kraw, qraw, rk, rq, o, c); break;
+    case 1: form_ops_q<1, OPS, FAC>(al, kraw, qraw, rk, rq, o, c); break;
+    case 2: form_ops_q<2, OPS, FAC>(al, kraw, qraw, rk, rq, o, c); break;
+    default: form_ops_q<3, OPS, FAC>(al, kraw, qraw, rk, rq, o, c); break;
+  }
 }
 
 // Loads of one chunk's token tt, channels 4 cg .. + 3 (tokens past n read q = k = v = dout = 0,
 // alpha = 1, beta = 0)
 struct RowLoad {
   uint2 q, k, a, v, d;
+  uint16_t beta;   // of token `tid` (threads below 16), as loaded: converted where it is used, so
+                   // that no wait for the load lands inside the branch that issues it
 };
-__device__ __forceinline__ float4 alpha4(uint2 a) { return unpack4(make_uint2(clamp_alpha2(a.x), clamp_alpha2(a.y))); }
+// Buffer descriptors over one chunk's rows: reads past `bytes` return zero and writes there are
+// dropped, so no load or store of a chunk sits in a branch (a wait for one that might not have
+// been issued would otherwise have to wait for everything).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcW3);
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_buf64(__amdgpu_buffer_rsrc_t r, int voff, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, voff, 0, 0);
+}
+// Row loads of the chunk at t0 (n tokens): token tt, channels c0 .. c0 + 3; beta of token tid
+template <bool Q, bool V, bool DO>
+__device__ __forceinline__ void load_rows(const BwdArgs& a, int64_t b, int64_t h, int64_t t0, int n, int tt, int c0,
+                                          int tid, RowLoad& r) {
+  const int64_t row0 = b * a.T + t0;
+  const int st2 = (int)a.stride * 2, sa2 = (int)a.H * D * 2;
+  const int vq = tt * st2 + 2 * c0, va = tt * sa2 + 2 * c0;
+  r.k = ld_buf64(rsrc(a.k + row0 * a.stride + h * D, n * st2), vq, 0);
+  r.q = Q ? ld_buf64(rsrc(a.q + row0 * a.stride + h * D, n * st2), vq, 0) : make_uint2(0, 0);
+  r.v = V ? ld_buf64(rsrc(a.v + row0 * a.stride + h * D, n * st2), vq, 0) : make_uint2(0, 0);
+  r.a = ld_buf64(rsrc(a.alpha + (row0 * a.H + h) * D, n * sa2), va, 0);   // 0 past n: made 1 where used
+  r.d = DO ? ld_buf64(rsrc(a.dout + (row0 * a.H + h) * D, n * sa2), va, 0) : make_uint2(0, 0);
+  r.beta = __builtin_amdgcn_raw_buffer_load_b16(rsrc(a.beta + row0 * a.H + h, n * (int)a.H * 2),
+                                                (tid & (BC - 1)) * (int)a.H * 2 + (tid < BC ? 0 : n * (int)a.H * 2), 0, 0);
+}
+__device__ __forceinline__ uint2 alpha2(uint2 a) { return make_uint2(clamp_alpha2(a.x), clamp_alpha2(a.y)); }
+constexpr uint2 ones2 = {0x3F803F80u, 0x3F803F80u};
 
 // The inversion T = (I + diag(b) A)^{-1} from adiag = -b_r A_ri (i < r): lane j of the first
 // 16 forms column j by forward substitution and writes it to tcm (column-major).
 __device__ __forceinline__ void invert16(const float* adiag, uint16_t* tcm, int lane) {
   if (lane >= 16) return;
-  const int j = lane;
+  int j = lane;
+  asm volatile("" : "+v"(j));   // formed here: 16 hoisted (i == j) selects would stay live across the chunk loop
   float x[BC];
 #pragma unroll
   for (int i = 0; i < BC; ++i) {
@@ -228,21 +297,142 @@ __device__ __forceinline__ void invert16(const float* adiag, uint16_t* tcm, int 
     *reinterpret_cast<uint2*>(&tcm[j * TP + 4 * m]) = pack4(make_float4(x[4 * m], x[4 * m + 1], x[4 * m + 2], x[4 * m + 3]));
 }
 
+// ---- the chunk factorisation pass ---------------------------------------------------------
+// T = (I + diag(b) A)^{-1}, A = strict_lower(Kr Kc^T), of every chunk once, for all the passes
+// after it: one wave per chunk forms Kr, Kc (channels of the pair 2 l, 2 l + 1 per lane over the
+// 16 tokens), A on MFMA, and T by forward substitution, and stores the two mma16 A fragments
+// the passes use, of T (U = T diag(b) R) and of T^T (Y = T^T dU): [bh][chunk][2][64 lanes] x 8 bytes.
+struct TfacLds {          // per wave
+  uint16_t kr[BC * OP];
+  uint16_t kc[BC * OP];
+  uint16_t kraw[BC * D];
+  uint16_t al[BC * D];
+  uint16_t tcm[BC * TP];  // T column-major
+  float adiag[BC * BC];   // -b_r A_ri (i < r)
+  float rk[BC];
+  float beta[BC];
+};
+constexpr int kTfacWaves = 4;
+__global__ __launch_bounds__(64 * kTfacWaves) void kda_bwd_tfac_kernel(BwdArgs a, int64_t total) {
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, q4 = lane >> 4;
+  TfacLds& L = reinterpret_cast<TfacLds*>(smem)[w];
+  const int64_t gc = (int64_t)blockIdx.x * kTfacWaves + w;   // chunk of all sequences and heads
+  if (gc >= total) return;                                   // (no block barriers below)
+  const int64_t nck = (a.T + BC - 1) / BC;
+  const int64_t bh = gc / nck, c = gc % nck;
+  const int64_t b = bh / a.H, h = bh % a.H, t0 = c * BC, row0 = b * a.T + t0;
+  const int n = (int)min<int64_t>(BC, a.T - t0);
+  // loads: lane = token tq, channels 32 cq .. + 31
+  const int tq = lane >> 2, cq = lane & 3;
+  const int st2 = (int)a.stride * 2, sa2 = (int)a.H * D * 2;
+  const auto rk_ = rsrc(a.k + row0 * a.stride + h * D, n * st2);
+  const auto ra_ = rsrc(a.alpha + (row0 * a.H + h) * D, n * sa2);
+  uint4 kv[4], av[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto k4 = __builtin_amdgcn_raw_buffer_load_b128(rk_, tq * st2 + 64 * cq + 16 * j, 0, 0);
+    const auto a4 = __builtin_amdgcn_raw_buffer_load_b128(ra_, tq * sa2 + 64 * cq + 16 * j, 0, 0);
+    kv[j] = make_uint4(k4[0], k4[1], k4[2], k4[3]);
+    av[j] = make_uint4(a4[0], a4[1], a4[2], a4[3]);
+  }
+  const uint16_t braw = __builtin_amdgcn_raw_buffer_load_b16(rsrc(a.beta + row0 * a.H + h, n * (int)a.H * 2),
+                                                             (lane & (BC - 1)) * (int)a.H * 2 + (lane < BC ? 0 : n * (int)a.H * 2), 0, 0);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ss = sq2(kv[j].w, sq2(kv[j].z, sq2(kv[j].y, sq2(kv[j].x, ss))));
+  ss += lane_xor1(ss);
+  ss += lane_xor2(ss);
+  const bool in = tq < n;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint4*>(&L.kraw[tq * D + 32 * cq + 8 * j]) = kv[j];
+    *reinterpret_cast<uint4*>(&L.al[tq * D + 32 * cq + 8 * j]) =
+        in ? make_uint4(clamp_alpha2(av[j].x), clamp_alpha2(av[j].y), clamp_alpha2(av[j].z), clamp_alpha2(av[j].w))
+           : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+  }
+  if (cq == 0) L.rk[tq] = a.l2norm ? __builtin_amdgcn_rsqf(ss + kL2Eps) : 1.f;
+  if (lane < BC) L.beta[lane] = bf2f(braw);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  // Kr = k e^{g - m} / |k|, Kc = k e^{m - g} / |k| (m = g_7) for channels 2 lane, 2 lane + 1
+  {
+    float a0[BC], a1[BC];
+#pragma unroll
+    for (int t = 0; t < BC; ++t) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(&L.al[t * D + 2 * lane]);
+      a0[t] = bf_lo(u);
+      a1[t] = bf_hi(u);
+    }
+    float f0[BC], f1[BC];   // e^{m - g_t} for t <= 7, e^{g_t - m} for t >= 8
+    float r0 = 1.f, r1 = 1.f;
+#pragma unroll
+    for (int t = 7; t >= 0; --t) {
+      f0[t] = r0;
+      f1[t] = r1;
+      r0 *= a0[t];
+      r1 *= a1[t];
+    }
+    r0 = r1 = 1.f;
+#pragma unroll
+    for (int t = 8; t < BC; ++t) {
+      r0 *= a0[t];
+      r1 *= a1[t];
+      f0[t] = r0;
+      f1[t] = r1;
+    }
+    const int x = cpos(2 * lane);
+#pragma unroll
+    for (int t = 0; t < BC; ++t) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(&L.kraw[t * D + 2 * lane]);
+      const float rk = L.rk[t], k0 = bf_lo(u) * rk, k1 = bf_hi(u) * rk;
+      const float i0 = __builtin_amdgcn_rcpf(f0[t]), i1 = __builtin_amdgcn_rcpf(f1[t]);
+      const bool lo = t <= 7;   // f holds e^{m - g} there, e^{g - m} after
+      *reinterpret_cast<uint32_t*>(&L.kr[t * OP + x]) = pack_bf16x2(k0 * (lo ? i0 : f0[t]), k1 * (lo ? i1 : f1[t]));
+      *reinterpret_cast<uint32_t*>(&L.kc[t * OP + x]) = pack_bf16x2(k0 * (lo ? f0[t] : i0), k1 * (lo ? f1[t] : i1));
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mma32(opfrag(L.kr, s, l16, q4), opfrag(L.kc, s, l16, q4), acc);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = 4 * q4 + r;
+    L.adiag[16 * rr + l16] = rr > l16 ? -L.beta[rr] * acc[r] : 0.f;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  invert16(L.adiag, L.tcm, lane);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  uint2* out = a.tfrag + gc * 2 * 64 + lane;
+  out[0] = ld_tr(&L.tcm[(4 * q4 + (l16 >> 2)) * TP + 4 * (l16 & 3)]);
+  out[64] = *reinterpret_cast<const uint2*>(&L.tcm[l16 * TP + 4 * q4]);
+}
+// the T (which = 0) or T^T (which = 1) fragment of chunk `c` of sequence-head bh
+__device__ __forceinline__ uint2 tfrag(const BwdArgs& a, int64_t bh, int64_t nck, int64_t c, int which, int lane) {
+  return a.tfrag[((bh * nck + c) * 2 + which) * 64 + lane];
+}
+
 // ---- forward state passes ----------------------------------------------------------------
 constexpr int kCkpt = 0, kSum = 1;
+// Two barriers per chunk: the arrays phase 1 writes alternate by chunk parity (phases 2 and 3
+// read them), the operands are written in phase 2 once every wave has passed the chunk
+// before's phases 3 and 4.
+struct FwdIn {
+  uint16_t vv[BC * OP];   // v (cpos order)
+  uint16_t kraw[BC * D];  // k as loaded (natural order)
+  uint16_t al[BC * D];    // alpha raised to the floor (natural order)
+  float beta[BC];
+  float rk[BC];
+};
 struct FwdLds {
   uint16_t kn[BC * OP];   // -K^
   uint16_t kb[BC * OP];   // K_
-  uint16_t kr[BC * OP];
-  uint16_t kc[BC * OP];
-  uint16_t vv[BC * OP];   // v (cpos order)
-  uint16_t tcm[BC * TP];  // T column-major
-  uint16_t kraw[BC * D];  // k as loaded (natural order)
-  float al[BC * D];
-  float adiag[BC * BC];
   float gn[D];
-  float beta[BC];
-  float rk[BC];
+  FwdIn in[2];
 };
 
 template <int MODE>
@@ -251,6 +441,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_fwd_kernel(BwdArgs a) {
   FwdLds& L = *reinterpret_cast<FwdLds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
   const int tt = tid >> 5, cg = tid & 31, c0 = 4 * cg;
+  const int tb = opT_base(l16, q4);
   const int64_t BHP = (int64_t)gridDim.x / (MODE == kSum ? 2 : 1);
   const int64_t bid = blockIdx.x;
   const bool mpart = MODE == kSum && bid >= BHP;   // transition product: from I with v = 0
@@ -274,84 +465,65 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_fwd_kernel(BwdArgs a) {
         S[rt][r] = src != nullptr ? src[row * D + col] : (mpart && row == col ? 1.f : 0.f);
       }
   }
-  const float4 ones = make_float4(1.f, 1.f, 1.f, 1.f);
-  for (int64_t t0 = t_beg; t0 < t_end; t0 += BC) {
+  // each chunk's rows and T fragment are loaded one chunk ahead
+  RowLoad rl;
+  auto load_chunk = [&](int64_t tc, uint2& tf) {
+    const int nn = (int)min<int64_t>(BC, t_end - tc);
+    if (mpart) load_rows<false, false, false>(a, b, h, tc, nn, tt, c0, tid, rl);
+    else load_rows<false, true, false>(a, b, h, tc, nn, tt, c0, tid, rl);
+    tf = tfrag(a, bh, nck, tc / BC, 0, lane);
+  };
+  uint2 tfn;
+  load_chunk(t_beg, tfn);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // as in the gradient kernel: the loop's counts decide its waits
+  int par = 0;
+  for (int64_t t0 = t_beg; t0 < t_end; t0 += BC, par ^= 1) {
     const int n = (int)min<int64_t>(BC, t_end - t0);
-    // phase 1: loads, norms; the chunk's start state out
+    FwdIn& I = L.in[par];
+    // phase 1: the chunk's rows into LDS, norms; the chunk's start state out
     if (MODE == kCkpt) {
       uint4* dst = a.ckpt + ((bh * nck + t0 / BC) * NWAVE + w) * 4 * 64 + lane;
 #pragma unroll
       for (int s = 0; s < 4; ++s) dst[s * 64] = sfrag(S, s);
     }
     const bool in = tt < n;
-    const int64_t row = b * a.T + t0 + tt;
-    uint2 kr = make_uint2(0, 0), ar = make_uint2(0x3F803F80u, 0x3F803F80u), vr = make_uint2(0, 0);
-    if (in) {
-      kr = *reinterpret_cast<const uint2*>(a.k + row * a.stride + h * D + c0);
-      ar = *reinterpret_cast<const uint2*>(a.alpha + (row * a.H + h) * D + c0);
-      if (!mpart) vr = *reinterpret_cast<const uint2*>(a.v + row * a.stride + h * D + c0);
-    }
-    if (tid < BC) L.beta[tid] = tid < n ? bf2f(a.beta[(b * a.T + t0 + tid) * a.H + h]) : 0.f;
-    float ss = dot4(kr);
+    if (tid < BC) I.beta[tid] = bf2f(rl.beta);
+    float ss = dot4(rl.k);
     ss = rowsum(ss);
     ss = halve16(ss, ss);
     const float rk = a.l2norm ? __builtin_amdgcn_rsqf(ss + kL2Eps) : 1.f;
-    *reinterpret_cast<float4*>(&L.al[tt * D + c0]) = in ? alpha4(ar) : ones;
-    *reinterpret_cast<uint2*>(&L.vv[tt * OP + cpos(c0)]) = vr;
-    *reinterpret_cast<uint2*>(&L.kraw[tt * D + c0]) = kr;
-    if (cg == 0) L.rk[tt] = rk;
+    *reinterpret_cast<uint2*>(&I.al[tt * D + c0]) = in ? alpha2(rl.a) : ones2;
+    *reinterpret_cast<uint2*>(&I.vv[tt * OP + cpos(c0)]) = rl.v;
+    *reinterpret_cast<uint2*>(&I.kraw[tt * D + c0]) = rl.k;
+    if (cg == 0) I.rk[tt] = rk;
+    const uint2 tf = tfn;
+    // the next chunk's (the last chunk's again after it: no load sits in a branch)
+    load_chunk(t0 + BC < t_end ? t0 + BC : t0, tfn);
     lds_barrier();
     // phase 2: decay factors and operands, thread = channel c of tokens 4 tq .. + 3
-    {
-      const int c = tid & (D - 1), tq = tid >> 7;
-      const Fac4 f = factors4(L.al, tq, c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 4 * tq + j, o = t * OP + cpos(c);
-        const float kn = bf2f(L.kraw[t * D + c]) * L.rk[t];
-        L.kn[o] = f2bf(-kn * f.g[j]);
-        L.kb[o] = f2bf(kn * f.bar[j]);
-        L.kr[o] = f2bf(kn * f.fw[j]);
-        L.kc[o] = f2bf(kn * f.bw[j]);
-      }
-      if (tq == 0) L.gn[c] = f.gn;
-    }
+    form_ops<kOpState, false>(I.al, I.kraw, nullptr, I.rk, nullptr,
+                              OpOut{L.kn, L.kb, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, L.gn},
+                              tid >> 7, tid & (D - 1));
     lds_barrier();
-    // phase 3: A and T (wave 0); R = V - K^ S and diag(b) R (every wave)
-    if (w == 0) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mma32(opfrag(L.kr, s, l16, q4), opfrag(L.kc, s, l16, q4), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = 4 * q4 + r;
-        L.adiag[16 * rr + l16] = rr > l16 ? -L.beta[rr] * acc[r] : 0.f;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      invert16(L.adiag, L.tcm, lane);
-    }
+    // phase 3: R = V - K^ S, diag(b) R; U = T diag(b) R; S <- Diag(e^{g_n}) S + K_^T U
     f32x4 R = {0.f, 0.f, 0.f, 0.f};
     if (!mpart) {
-      const float4 v4 = unpack4(colB16(L.vv, w, l16, q4));
+      const float4 v4 = unpack4(colB16(I.vv, w, l16, q4));
       R = f32x4{v4.x, v4.y, v4.z, v4.w};
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) R = mma32(opfrag(L.kn, s, l16, q4), sfrag(S, s), R);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) R[r] *= L.beta[4 * q4 + r];
-    lds_barrier();
-    // phase 4: U = T diag(b) R; S <- Diag(e^{g_n}) S + K_^T U
-    const f32x4 U = mma16(ld_tr(&L.tcm[(4 * q4 + (l16 >> 2)) * TP + 4 * (l16 & 3)]), pack4(R), f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int r = 0; r < 4; ++r) R[r] *= I.beta[4 * q4 + r];
+    const f32x4 U = mma16(tf, pack4(R), f32x4{0.f, 0.f, 0.f, 0.f});
     const uint2 Ub = pack4(U);
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt) {
       const float4 g4 = *reinterpret_cast<const float4*>(&L.gn[16 * rt + 4 * q4]);
       f32x4 x = S[rt];
       x[0] *= g4.x; x[1] *= g4.y; x[2] *= g4.z; x[3] *= g4.w;
-      S[rt] = mma16(opT16(L.kb, rt, l16, q4), Ub, x);
+      S[rt] = mma16(opT16(L.kb, rt, tb), Ub, x);
     }
-    // the next chunk's phase 1 writes al, vv and beta only, which phase 4 does not read
   }
   if (MODE == kSum) {
     float* dst = a.Sout + (mpart ? BHP : 0) * (int64_t)(D * D) + lb * (int64_t)(D * D);
@@ -363,55 +535,51 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_fwd_kernel(BwdArgs a) {
 }
 
 // ---- gradient passes ---------------------------------------------------------------------
-// Arrays with many per-lane access patterns first: LDS instruction offsets reach 64 KB from a
-// base register, and each pattern on an array beyond that needs a register of its own.
+// The arrays that the operand pass reads and writes at many constant offsets come first, within
+// the 64 KB that LDS instruction offsets reach from one base register (each access pattern on
+// an array beyond that needs a register of its own).
 struct GradLds {
+  uint16_t qraw[BC * D];  // q, k as loaded (natural order)
+  uint16_t kraw[BC * D];
+  uint16_t al[BC * D];    // alpha raised to the floor (natural order)
   uint16_t kn[BC * OP];   // -K^
   uint16_t kb[BC * OP];   // K_
   uint16_t kr[BC * OP];
   uint16_t kc[BC * OP];
   uint16_t qh[BC * OP];   // Q^
   uint16_t qr[BC * OP];
-  uint16_t dob[BC * OP];  // dout (v at cpos)
-  uint16_t uc[BC * OP];   // U (v at cpos); v of the chunk before U is formed
-  uint16_t yc[BC * OP];   // Y
-  uint16_t tcm[BC * TP];  // T column-major
-  uint16_t aqt[BC * TP];  // Aq^T row-major
-  uint16_t daq[BC * TP];  // dAq column-major
-  uint16_t dam[BC * TP];  // dA column-major
-  float adiag[BC * BC];   // -b_r A_ri (i < r)
-  float aw[BC * BC];      // A_ri (i < r)
-  float gn[D];
-  float dgn[NWAVE * D];   // per wave: sum over its v of S o dS' per channel
-  float beta[BC];
-  float rq[BC];
-  float rk[BC];
-  float dbp[NWAVE * BC];  // per wave: Y . R per token
-  float dba[BC];          // -rowsum(A o H)
-  uint16_t qraw[BC * D];  // q, k as loaded (natural order)
-  uint16_t kraw[BC * D];
-  float al[BC * D];       // clamped alpha (natural order)
   float fg[BC * D];       // e^{g}
   float fb[BC * D];       // e^{g_n - g}
   float ff[BC * D];       // e^{g - m}
                           // (fg, fb, ff hold dq^, dk^ and dalpha once the chain rule has run)
+  float rq[BC];
+  float rk[BC];
+  float beta[BC];
+  float gn[D];
+  uint16_t dob[BC * OP];  // dout (v at cpos)
+  uint16_t uc[BC * OP];   // U (v at cpos); v of the chunk before U is formed
+  uint16_t yc[BC * OP];   // Y
+  uint16_t aqt[BC * TP];  // Aq^T row-major
+  uint16_t daq[BC * TP];  // dAq column-major
+  uint16_t dam[BC * TP];  // dA column-major
+  float aw[BC * BC];      // A_ri (i < r)
+  float dgn[NWAVE * D];   // per wave: sum over its v of S o dS' per channel
+  float dbp[NWAVE * BC];  // per wave: Y . R per token
+  float dba[BC];          // -rowsum(A o H)
   uint16_t st[D * SP];    // S^T: [v][channel position]
   uint16_t dst[D * SP];   // dS'^T
 };
-struct LocalLds {         // the local pass: operands, dout, T and Aq^T
+struct LocalLds {         // the local pass: operands, dout and Aq^T
   uint16_t kn[BC * OP];
   uint16_t kb[BC * OP];
-  uint16_t kr[BC * OP];
   uint16_t kc[BC * OP];
   uint16_t qh[BC * OP];
   uint16_t qr[BC * OP];
   uint16_t dob[BC * OP];
-  uint16_t tcm[BC * TP];
   uint16_t aqt[BC * TP];
   uint16_t qraw[BC * D];
   uint16_t kraw[BC * D];
-  float al[BC * D];
-  float adiag[BC * BC];
+  uint16_t al[BC * D];
   float gn[D];
   float beta[BC];
   float rq[BC];
@@ -426,6 +594,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
   Lds& L = *reinterpret_cast<Lds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
   const int tt = tid >> 5, cg = tid & 31, c0 = 4 * cg;
+  const int tb = opT_base(l16, q4);
   const int64_t bid = blockIdx.x;
   const int p = (int)(bid % a.nseg);
   const int64_t bh = bid / a.nseg;
@@ -446,69 +615,62 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r)
         dS[rt][r] = src != nullptr ? src[(16 * rt + 4 * q4 + r) * D + 16 * w + l16] : 0.f;
   }
-  const float4 ones = make_float4(1.f, 1.f, 1.f, 1.f);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const int64_t first = (t_end - 1 - t_beg) / BC;   // the segment's last chunk (t_end > t_beg)
+  // each chunk's rows are loaded one chunk ahead, its state fragments once the chunk before
+  // it is past its phase 3
+  RowLoad rl;
+  uint4 Sf[4];
+  uint2 tfn = make_uint2(0, 0), ttfn;   // the chunk's T and T^T fragments
+  auto load_chunk_rows = [&](int64_t c) {
+    const int64_t c0t = t_beg + c * BC;
+    load_rows<true, !LOCAL, true>(a, b, h, c0t, (int)min<int64_t>(BC, t_end - c0t), tt, c0, tid, rl);
+    if (!LOCAL) tfn = tfrag(a, bh, nck, c0t / BC, 0, lane);
+    ttfn = tfrag(a, bh, nck, c0t / BC, 1, lane);
+  };
+  auto load_frags = [&](int64_t c) {
+    const uint4* src = a.ckpt + ((bh * nck + (t_beg + c * BC) / BC) * NWAVE + w) * 4 * 64 + lane;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Sf[s] = src[s * 64];
+  };
+  load_chunk_rows(first);
+  if (!LOCAL) load_frags(first);
+  // all of these in before the loop: at its head the loop's own counts then decide every wait
+  // (merged with this path's, a wait for a prefetched row would wait for everything)
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   for (int64_t ci = first; ci >= 0; --ci) {
     const int64_t t0 = t_beg + ci * BC;
     const int n = (int)min<int64_t>(BC, t_end - t0);
-    lds_barrier();   // the previous chunk's reads of the LDS are done
-    // phase 1: loads and norms
-    uint4 Sf[4];
-    if (!LOCAL) {
-      const uint4* src = a.ckpt + ((bh * nck + t0 / BC) * NWAVE + w) * 4 * 64 + lane;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Sf[s] = src[s * 64];
-    }
     const bool in = tt < n;
-    const int64_t row = b * a.T + t0 + tt;
-    uint2 qv = make_uint2(0, 0), kv = qv, av = make_uint2(0x3F803F80u, 0x3F803F80u), dv = qv, vv = qv;
-    if (in) {
-      qv = *reinterpret_cast<const uint2*>(a.q + row * a.stride + h * D + c0);
-      kv = *reinterpret_cast<const uint2*>(a.k + row * a.stride + h * D + c0);
-      av = *reinterpret_cast<const uint2*>(a.alpha + (row * a.H + h) * D + c0);
-      dv = *reinterpret_cast<const uint2*>(a.dout + (row * a.H + h) * D + c0);
-      if (!LOCAL) vv = *reinterpret_cast<const uint2*>(a.v + row * a.stride + h * D + c0);
-    }
-    if (tid < BC) L.beta[tid] = tid < n ? bf2f(a.beta[(b * a.T + t0 + tid) * a.H + h]) : 0.f;
-    float sq = rowsum(dot4(qv)), sk = rowsum(dot4(kv));
+    lds_barrier();   // the previous chunk's reads of the LDS are done
+    // phase 1: the chunk's rows into LDS, norms
+    if (tid < BC) L.beta[tid] = bf2f(rl.beta);
+    float sq = rowsum(dot4(rl.q)), sk = rowsum(dot4(rl.k));
     sq = halve16(sq, sq);
     sk = halve16(sk, sk);
     const float rq = a.l2norm ? __builtin_amdgcn_rsqf(sq + kL2Eps) : 1.f;
     const float rk = a.l2norm ? __builtin_amdgcn_rsqf(sk + kL2Eps) : 1.f;
-    *reinterpret_cast<float4*>(&L.al[tt * D + c0]) = in ? alpha4(av) : ones;
-    *reinterpret_cast<uint2*>(&L.dob[tt * OP + cpos(c0)]) = dv;
-    *reinterpret_cast<uint2*>(&L.qraw[tt * D + c0]) = qv;
-    *reinterpret_cast<uint2*>(&L.kraw[tt * D + c0]) = kv;
+    *reinterpret_cast<uint2*>(&L.al[tt * D + c0]) = in ? alpha2(rl.a) : ones2;
+    *reinterpret_cast<uint2*>(&L.dob[tt * OP + cpos(c0)]) = rl.d;
+    *reinterpret_cast<uint2*>(&L.qraw[tt * D + c0]) = rl.q;
+    *reinterpret_cast<uint2*>(&L.kraw[tt * D + c0]) = rl.k;
     if (cg == 0) {
       L.rq[tt] = rq;
       L.rk[tt] = rk;
     }
-    if constexpr (!LOCAL) *reinterpret_cast<uint2*>(&L.uc[tt * OP + cpos(c0)]) = vv;
+    if constexpr (!LOCAL) *reinterpret_cast<uint2*>(&L.uc[tt * OP + cpos(c0)]) = rl.v;
+    const uint2 tf = tfn, ttf = ttfn;
+    load_chunk_rows(ci > 0 ? ci - 1 : 0);   // (chunk 0's again after it: no load sits in a branch)
     lds_barrier();
     // phase 2: factors and operands (thread = channel c of tokens 4 tq .. + 3); the transposed
     // state copies and dS' o S per channel
-    {
-      const int c = tid & (D - 1), tq = tid >> 7;
-      const Fac4 f = factors4(L.al, tq, c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 4 * tq + j, o = t * OP + cpos(c), e = t * D + c;
-        const float kn = bf2f(L.kraw[e]) * L.rk[t], qn = bf2f(L.qraw[e]) * L.rq[t];
-        L.kn[o] = f2bf(-kn * f.g[j]);
-        L.kb[o] = f2bf(kn * f.bar[j]);
-        L.kr[o] = f2bf(kn * f.fw[j]);
-        L.kc[o] = f2bf(kn * f.bw[j]);
-        L.qh[o] = f2bf(qn * f.g[j]);
-        L.qr[o] = f2bf(qn * f.fw[j]);
-        if constexpr (!LOCAL) {
-          L.fg[e] = f.g[j];
-          L.fb[e] = f.bar[j];
-          L.ff[e] = f.fw[j];
-        }
-      }
-      if (tq == 0) L.gn[c] = f.gn;
-    }
+    if constexpr (LOCAL)
+      form_ops<kOpLocal, false>(L.al, L.kraw, L.qraw, L.rk, L.rq,
+                            OpOut{L.kn, L.kb, nullptr, L.kc, L.qh, L.qr, nullptr, nullptr, nullptr, L.gn}, tid >> 7,
+                            tid & (D - 1));
+    else
+      form_ops<kOpAll, true>(L.al, L.kraw, L.qraw, L.rk, L.rq,
+                           OpOut{L.kn, L.kb, L.kr, L.kc, L.qh, L.qr, L.fg, L.fb, L.ff, L.gn}, tid >> 7, tid & (D - 1));
     if constexpr (!LOCAL) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -536,20 +698,18 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
       L.dgn[w * D + 64 + rrow] = tb;
     }
     lds_barrier();
-    // phase 3: A, T (wave 0) and Aq (wave 1); dU = K_ dS' and R = V - K^ S (every wave)
-    if (w == 0) {
-      f32x4 acc = zero4;
+    // phase 3: A (wave 0, for db) and Aq (wave 1); dU = K_ dS' and R = V - K^ S (every wave)
+    if (!LOCAL && w == 0) {
+      if constexpr (!LOCAL) {
+        f32x4 acc = zero4;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mma32(opfrag(L.kr, s, l16, q4), opfrag(L.kc, s, l16, q4), acc);
+        for (int s = 0; s < 4; ++s) acc = mma32(opfrag(L.kr, s, l16, q4), opfrag(L.kc, s, l16, q4), acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = 4 * q4 + r;
-        L.adiag[16 * rr + l16] = rr > l16 ? -L.beta[rr] * acc[r] : 0.f;
-        if constexpr (!LOCAL) L.aw[16 * rr + l16] = rr > l16 ? acc[r] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int rr = 4 * q4 + r;
+          L.aw[16 * rr + l16] = rr > l16 ? acc[r] : 0.f;
+        }
       }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      invert16(L.adiag, L.tcm, lane);
     } else if (w == 1) {
       f32x4 acc = zero4;
 #pragma unroll
@@ -568,12 +728,13 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
       R = f32x4{v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) R = mma32(opfrag(L.kn, s, l16, q4), Sf[s], R);
+      load_frags(ci > 0 ? ci - 1 : 0);
     }
     lds_barrier();
     // phase 4: U, dU += Aq^T dout, Y = T^T dU, dR = diag(b) Y; dS <- Q^^T dout + e^{g_n} dS' - K^^T dR
     const uint2 dOB = colB16(L.dob, w, l16, q4);
     dU = mma16(*reinterpret_cast<const uint2*>(&L.aqt[l16 * TP + 4 * q4]), dOB, dU);
-    const f32x4 Y = mma16(*reinterpret_cast<const uint2*>(&L.tcm[l16 * TP + 4 * q4]), pack4(dU), zero4);
+    const f32x4 Y = mma16(ttf, pack4(dU), zero4);
     f32x4 dR;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dR[r] = L.beta[4 * q4 + r] * Y[r];
@@ -582,13 +743,14 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
       f32x4 bR;
 #pragma unroll
       for (int r = 0; r < 4; ++r) bR[r] = L.beta[4 * q4 + r] * R[r];
-      U = mma16(ld_tr(&L.tcm[(4 * q4 + (l16 >> 2)) * TP + 4 * (l16 & 3)]), pack4(bR), zero4);
+      U = mma16(tf, pack4(bR), zero4);
       // dv, and this wave's part of Y . R per token
+      const auto rdv = rsrc(a.dv + (b * a.T + t0) * a.stride + h * D, n * (int)a.stride * 2);
       float yr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * q4 + r;
-        if (t < n) a.dv[(b * a.T + t0 + t) * a.stride + h * D + 16 * w + l16] = f2bf(dR[r]);
+        __builtin_amdgcn_raw_buffer_store_b16(f2bf(dR[r]), rdv, t * (int)a.stride * 2 + 2 * (16 * w + l16), 0, 0);
         yr[r] = rowsum(Y[r] * R[r]);
         L.uc[t * OP + cpos(16 * w + l16)] = f2bf(U[r]);
         L.yc[t * OP + cpos(16 * w + l16)] = f2bf(Y[r]);
@@ -602,8 +764,8 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
         const float4 g4 = *reinterpret_cast<const float4*>(&L.gn[16 * rt + 4 * q4]);
         f32x4 x = dS[rt];
         x[0] *= g4.x; x[1] *= g4.y; x[2] *= g4.z; x[3] *= g4.w;
-        x = mma16(opT16(L.kn, rt, l16, q4), dRb, x);
-        dS[rt] = mma16(opT16(L.qh, rt, l16, q4), dOB, x);
+        x = mma16(opT16(L.kn, rt, tb), dRb, x);
+        dS[rt] = mma16(opT16(L.qh, rt, tb), dOB, x);
       }
     }
     if constexpr (LOCAL) continue;
@@ -659,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * q4 + r, e = t * D + ch, o = t * OP + pc;
         const float fg = L.fg[e], fb = L.fb[e], ff = L.ff[e], fw = __builtin_amdgcn_rcpf(ff);
-        al4[r] = L.al[e];
+        al4[r] = bf2f(L.al[e]);
         const float dKh = -L.beta[t] * dYS[r];
         dqn[r] = dQh[r] * fg + dQr[r] * ff;
         dkn[r] = dKh * fg + dKb[r] * fb + dKr[r] * ff + dKc[r] * fw;
@@ -702,32 +864,35 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
       lds_barrier();
       // phase 7 (thread = token tt, channels 4 cg .. + 3): the L2 normalisation's backward and
       // the stores
-      if (in) {
+      {
         const int e = tt * D + c0;
         float4 dq = *reinterpret_cast<const float4*>(&L.fg[e]);
         float4 dk = *reinterpret_cast<const float4*>(&L.fb[e]);
         const float4 da = *reinterpret_cast<const float4*>(&L.ff[e]);
         if (a.l2norm) {
-          const float4 qn = mul4(unpack4(qv), make_float4(rq, rq, rq, rq));
-          const float4 kn = mul4(unpack4(kv), make_float4(rk, rk, rk, rk));
+          const float rqt = L.rq[tt], rkt = L.rk[tt];
+          const float4 qn = mul4(unpack4(*reinterpret_cast<const uint2*>(&L.qraw[e])), make_float4(rqt, rqt, rqt, rqt));
+          const float4 kn = mul4(unpack4(*reinterpret_cast<const uint2*>(&L.kraw[e])), make_float4(rkt, rkt, rkt, rkt));
           float sq2 = rowsum(qn.x * dq.x + qn.y * dq.y + qn.z * dq.z + qn.w * dq.w);
           float sk2 = rowsum(kn.x * dk.x + kn.y * dk.y + kn.z * dk.z + kn.w * dk.w);
           sq2 = halve16(sq2, sq2);
           sk2 = halve16(sk2, sk2);
-          dq = make_float4(rq * (dq.x - qn.x * sq2), rq * (dq.y - qn.y * sq2), rq * (dq.z - qn.z * sq2),
-                           rq * (dq.w - qn.w * sq2));
-          dk = make_float4(rk * (dk.x - kn.x * sk2), rk * (dk.y - kn.y * sk2), rk * (dk.z - kn.z * sk2),
-                           rk * (dk.w - kn.w * sk2));
+          dq = make_float4(rqt * (dq.x - qn.x * sq2), rqt * (dq.y - qn.y * sq2), rqt * (dq.z - qn.z * sq2),
+                           rqt * (dq.w - qn.w * sq2));
+          dk = make_float4(rkt * (dk.x - kn.x * sk2), rkt * (dk.y - kn.y * sk2), rkt * (dk.z - kn.z * sk2),
+                           rkt * (dk.w - kn.w * sk2));
         }
-        *reinterpret_cast<uint2*>(a.dq + row * a.stride + h * D + c0) = pack4(dq);
-        *reinterpret_cast<uint2*>(a.dk + row * a.stride + h * D + c0) = pack4(dk);
-        *reinterpret_cast<uint2*>(a.dalpha + (row * a.H + h) * D + c0) = pack4(da);
-      }
-      if (tid < BC && tid < n) {
-        float db = L.dba[tid];
+        const int64_t row0 = b * a.T + t0;
+        const int st2 = (int)a.stride * 2, sa2 = (int)a.H * D * 2;
+        st_buf64(rsrc(a.dq + row0 * a.stride + h * D, n * st2), tt * st2 + 2 * c0, pack4(dq));
+        st_buf64(rsrc(a.dk + row0 * a.stride + h * D, n * st2), tt * st2 + 2 * c0, pack4(dk));
+        st_buf64(rsrc(a.dalpha + (row0 * a.H + h) * D, n * sa2), tt * sa2 + 2 * c0, pack4(da));
+        const int tb16 = tid & (BC - 1);
+        float db = L.dba[tb16];
 #pragma unroll
-        for (int ww = 0; ww < NWAVE; ++ww) db += L.dbp[ww * BC + tid];
-        a.dbeta[(b * a.T + t0 + tid) * a.H + h] = f2bf(db);
+        for (int ww = 0; ww < NWAVE; ++ww) db += L.dbp[ww * BC + tb16];
+        __builtin_amdgcn_raw_buffer_store_b16(f2bf(db), rsrc(a.dbeta + row0 * a.H + h, n * (int)a.H * 2),
+                                              tb16 * (int)a.H * 2 + (tid < BC ? 0 : n * (int)a.H * 2), 0, 0);
       }
     }
   }
@@ -769,13 +934,16 @@ bool kda_bwd_chunked_layout_ok(const KdaArgs& a, const KdaGrads& g) {
 
 size_t kda_bwd_chunked_workspace(int64_t B, int64_t T, int64_t H) {
   const Cut c = bwd_chunked_cut(B, T, H);
-  const size_t ck = (size_t)(B * H) * (size_t)((T + BC - 1) / BC) * D * D * sizeof(uint16_t);
+  const size_t nck = (size_t)((T + BC - 1) / BC);
+  const size_t ck = (size_t)(B * H) * nck * D * D * sizeof(uint16_t);
+  const size_t tf = (size_t)(B * H) * nck * 2 * 64 * sizeof(uint2);
   const size_t segs = c.nseg > 1 ? (size_t)(B * H) * c.nseg * 6 * D * D * sizeof(float) : 0;
-  return ck + segs;
+  return ck + tf + segs;
 }
 
-// Workspace: the bf16 chunk states, then (segments only) L and M of every segment (the
-// summary pass writes [L of all (bh, p)][M of all (bh, p)]), the start states, E and G.
+// Workspace: the bf16 chunk states, the chunks' T fragments, then (segments only) L and M of
+// every segment (the summary pass writes [L of all (bh, p)][M of all (bh, p)]), the start
+// states, E and G.
 hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void* workspace, hipStream_t stream,
                                        Marks* marks) {
   if (x.B * x.H == 0 || x.T == 0) return hipSuccess;
@@ -791,7 +959,8 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
         {reinterpret_cast<const void*>(&kda_bwd_fwd_kernel<kCkpt>), (int)sizeof(FwdLds)},
         {reinterpret_cast<const void*>(&kda_bwd_fwd_kernel<kSum>), (int)sizeof(FwdLds)},
         {reinterpret_cast<const void*>(&kda_bwd_grad_kernel<true>), (int)sizeof(LocalLds)},
-        {reinterpret_cast<const void*>(&kda_bwd_grad_kernel<false>), (int)sizeof(GradLds)}};
+        {reinterpret_cast<const void*>(&kda_bwd_grad_kernel<false>), (int)sizeof(GradLds)},
+        {reinterpret_cast<const void*>(&kda_bwd_tfac_kernel), (int)(kTfacWaves * sizeof(TfacLds))}};
     for (const auto& f : fns) {
       e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, f.second);
       if (e != hipSuccess) return e;
@@ -818,15 +987,26 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   a.dalpha = static_cast<uint16_t*>(g.dalpha);
   a.dbeta = static_cast<uint16_t*>(g.dbeta);
   a.dS0 = g.dS0;
-  const size_t ck = (size_t)BH * (size_t)((x.T + BC - 1) / BC) * D * D * sizeof(uint16_t);
+  const int64_t nck = (x.T + BC - 1) / BC;
+  const size_t ck = (size_t)BH * (size_t)nck * D * D * sizeof(uint16_t);
+  const size_t tfb = (size_t)BH * (size_t)nck * 2 * 64 * sizeof(uint2);
+  a.tfrag = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + ck);
   const int64_t mat = BH * c.nseg * (int64_t)(D * D);
-  float* Lw = reinterpret_cast<float*>(static_cast<char*>(workspace) + ck);
+  float* Lw = reinterpret_cast<float*>(static_cast<char*>(workspace) + ck + tfb);
   float* Mw = Lw + mat;
   float* Sst = Mw + mat;
   float* Ew = Sst + mat;
   float* Gw = Ew + mat;
   const dim3 thr(kThreads);
   const unsigned blocks = (unsigned)(BH * c.nseg);
+  {
+    const int64_t total = BH * nck;
+    hipLaunchKernelGGL(kda_bwd_tfac_kernel, dim3((unsigned)((total + kTfacWaves - 1) / kTfacWaves)),
+                       dim3(64 * kTfacWaves), kTfacWaves * sizeof(TfacLds), stream, a, total);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_tfac_kernel", stream);
+    if (e != hipSuccess) return e;
+  }
   if (c.nseg > 1) {
     BwdArgs s = a;
     s.Sout = Lw;

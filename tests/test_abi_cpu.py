@@ -209,10 +209,11 @@ def test_backward_argument_errors():
     assert call(stride=100) == 2
     assert call() == 6                                                  # workspace missing
     assert call(B=0) == 0
-    # bf16 heads of 128 run the chunked backward: the bf16 state before every 16-token chunk, plus
-    # six fp32 matrices per segment (here 5 segments of 272 tokens per head)
+    # bf16 heads of 128 run the chunked backward: the bf16 state before every 16-token chunk and
+    # 1 KiB of T fragments per chunk, plus six fp32 matrices per segment (here 5 segments of 272
+    # tokens per head)
     n = int(L.chimera_kda_bwd_workspace_size(1, 64 * 20 + 3, 16, 128, 128, 1, 1))
-    assert n == 2 * 16 * 81 * 128 * 128 + 4 * 6 * 16 * 5 * 128 * 128
+    assert n == 2 * 16 * 81 * 128 * 128 + 16 * 81 * 1024 + 4 * 6 * 16 * 5 * 128 * 128
     # the token-by-token backward (CHIMERA_KDA_SEQUENTIAL, or fp32): fp32 checkpoints + slice partials
     for dt, fl in ((1, 3), (0, 1)):
         n = int(L.chimera_kda_bwd_workspace_size(1, 64 * 20 + 3, 16, 128, 128, dt, fl))
