@@ -151,7 +151,7 @@ def _args():
     ap.add_argument("--head-dim", type=int, default=0,
                     help="run the workload with heads of this size at the same width (H * d kept)")
     ap.add_argument("--sequential", action="store_true",
-                    help="the KDA call on the token-by-token kernel (CHIMERA_KDA_SEQUENTIAL)")
+                    help="the KDA call (with --backward: the KDA backward) on the token-by-token kernels (CHIMERA_KDA_SEQUENTIAL)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=20736,
                     help="tokens per sequence in the oracle's timed sample (text + whole grid rows/frames)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="markdown table of a rocprofv3 kernel_stats.csv")
@@ -447,7 +447,8 @@ def bench_backward(args, w):
     dcode = chm.BF16 if w.dtype == "bf16" else chm.F32
     ws = torch.empty(max(chm.kda_workspace_size(B, T, H, d, d, dcode, chm.KDA_L2NORM_QK), 1), dtype=torch.uint8,
                      device=dev)
-    wsb = torch.empty(max(int(chm.lib().chimera_kda_bwd_workspace_size(B, T, H, d, d, dcode, chm.KDA_L2NORM_QK)), 1),
+    bflags = chm.KDA_L2NORM_QK | (chm.KDA_SEQUENTIAL if args.sequential else 0)
+    wsb = torch.empty(max(int(chm.lib().chimera_kda_bwd_workspace_size(B, T, H, d, d, dcode, bflags)), 1),
                       dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     calls = ["conv_fwd", "kda_fwd", "kda_bwd", "conv_bwd"]
@@ -459,7 +460,7 @@ def bench_backward(args, w):
         mark(1)
         chm.kda_fwd(q, k, v, alpha, beta, S0, workspace=ws, out=o, state_out=s_final)
         mark(2)
-        chm.kda_bwd(q, k, v, alpha, beta, S0, do, None, grads=(gq, gk, gv), workspace=wsb)
+        chm.kda_bwd(q, k, v, alpha, beta, S0, do, None, grads=(gq, gk, gv), workspace=wsb, sequential=args.sequential)
         mark(3)
         chm.mshortconv_bwd(x, dy, wt, wv, segs, dx=dx)
         mark(4)
@@ -480,6 +481,9 @@ def bench_backward(args, w):
     # dbeta out
     bwd_bytes = B * T * H * ((4 * d + 1 + d) * e + (4 * d + 1) * e)
     ms_bwd = per["kda_bwd"]
+    chunked_bwd = w.dtype == "bf16" and d == 128 and not args.sequential
+    bwd_desc = ("the chunked KDA backward (16-token chunks on MFMA)" if chunked_bwd
+                else "the checkpointed token-by-token KDA backward")
     out = {
         "metric": "KDA+mShortConv training step (fwd + bwd) tokens/sec/GPU",
         "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -487,9 +491,12 @@ def bench_backward(args, w):
         "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": f"synthetic (seeded; {w.dtype} inputs and dL/do; fp32 state)",
         "config": {"workload": f"{w.name}: {T} tokens per sequence, B={B}, H={H}, d={d}; forward (conv, chunked KDA), "
-                               f"then the checkpointed token-by-token KDA backward and the conv backward",
-                   "tokens_per_step": B * T, "calls_ms": per, "wall_s_timed": wall},
-        "roofline": {"bound": "hbm", "kernel": "kda_bwd (call: checkpoint forward, reverse pass, slice sums)",
+                               f"then {bwd_desc} and the conv backward",
+                   "tokens_per_step": B * T, "calls_ms": per, "wall_s_timed": wall,
+                   "kda_bwd_workspace_bytes": int(wsb.numel())},
+        "roofline": {"bound": "hbm",
+                     "kernel": ("kda_bwd (call: chunk factorisation, state passes, chains, gradient pass)" if chunked_bwd
+                                else "kda_bwd (call: checkpoint forward, reverse pass, slice sums)"),
                      "achieved": bwd_bytes / (ms_bwd * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": bwd_bytes / (ms_bwd * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
                      "ms_per_launch": ms_bwd, "algorithmic_bytes_per_launch": bwd_bytes,

@@ -563,7 +563,6 @@ struct GradLds {
   uint16_t daq[BC * TP];  // dAq column-major
   uint16_t dam[BC * TP];  // dA column-major
   float aw[BC * BC];      // A_ri (i < r)
-  float dgn[NWAVE * D];   // per wave: sum over its v of S o dS' per channel
   float dbp[NWAVE * BC];  // per wave: Y . R per token
   float dba[BC];          // -rowsum(A o H)
   uint16_t st[D * SP];    // S^T: [v][channel position]
@@ -677,25 +676,6 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
         *reinterpret_cast<uint4*>(&L.st[(16 * w + l16) * SP + 32 * s + 8 * q4]) = Sf[s];
         *reinterpret_cast<uint4*>(&L.dst[(16 * w + l16) * SP + 32 * s + 8 * q4]) = sfrag(dS, s);
       }
-      // sum over this wave's 16 columns of S o dS' for every row (channel)
-      float pa[16], pb[16];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float4 lo = unpack4(make_uint2(Sf[s].x, Sf[s].y)), hi = unpack4(make_uint2(Sf[s].z, Sf[s].w));
-        const float sv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rt = 2 * s + (e >> 2), r = e & 3;   // row 16 rt + 4 q4 + r
-          const float prod = sv[e] * dS[rt][r];
-          if (rt < 4) pa[4 * rt + r] = prod;
-          else pb[4 * (rt - 4) + r] = prod;
-        }
-      }
-      const float ta = row_sum16(pa, l16), tb = row_sum16(pb, l16);
-      // lane l16 holds the total of value l16: row 16 (l16 / 4) + 4 q4 + l16 % 4 (+ 64 for tb)
-      const int rrow = 16 * (l16 >> 2) + 4 * q4 + (l16 & 3);
-      L.dgn[w * D + rrow] = ta;
-      L.dgn[w * D + 64 + rrow] = tb;
     }
     lds_barrier();
     // phase 3: A (wave 0, for db) and Aq (wave 1); dU = K_ dS' and R = V - K^ S (every wave)
@@ -796,13 +776,16 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
         *reinterpret_cast<uint2*>(&L.dam[l16 * TP + 4 * q4]) = pack4(make_float4(m[0], m[1], m[2], m[3]));
         if (l16 == 0) *reinterpret_cast<float4*>(&L.dba[4 * q4]) = make_float4(-ah[0], -ah[1], -ah[2], -ah[3]);
       }
-      f32x4 dQh = zero4, dYS = zero4, dKb = zero4;
+      // (and S dS'^T over this wave's 16 channel positions, whose diagonal is sum_v S o dS' per channel:
+      // the transposed copies' fragments serve as A and as B operands alike)
+      f32x4 dQh = zero4, dYS = zero4, dKb = zero4, sds = zero4;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint4 sb = stB(L.st, s, w, l16, q4);
+        const uint4 sb = stB(L.st, s, w, l16, q4), db = stB(L.dst, s, w, l16, q4);
         dQh = mma32(opfrag(L.dob, s, l16, q4), sb, dQh);
         dYS = mma32(opfrag(L.yc, s, l16, q4), sb, dYS);
-        dKb = mma32(opfrag(L.uc, s, l16, q4), stB(L.dst, s, w, l16, q4), dKb);
+        dKb = mma32(opfrag(L.uc, s, l16, q4), db, dKb);
+        sds = mma32(sb, db, sds);
       }
       lds_barrier();
       // phase 6: dQr = dAq Kc, dKr = dA Kc, dKc = dAq^T Qr + dA^T Kr; the per-element chain rule
@@ -838,9 +821,9 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
                   kd3 = __shfl(ksum, (lane + 16) & 63);
       float after = (q4 < 3 ? gu1 : 0.f) + (q4 < 2 ? gu2 : 0.f) + (q4 < 1 ? gu3 : 0.f);
       float before = (q4 > 0 ? kd1 : 0.f) + (q4 > 1 ? kd2 : 0.f) + (q4 > 2 ? kd3 : 0.f);
-      float sdS = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NWAVE; ++ww) sdS += L.dgn[ww * D + ch];
+      // the diagonal element of position l16 sits in lane 16 (l16 / 4) + l16, element l16 % 4
+      const float dsel = (l16 & 3) == 0 ? sds[0] : (l16 & 3) == 1 ? sds[1] : (l16 & 3) == 2 ? sds[2] : sds[3];
+      const float sdS = __shfl(dsel, 16 * (l16 >> 2) + l16);
       const float whole = L.gn[ch] * sdS;
       float dla[4];
 #pragma unroll
