@@ -435,15 +435,13 @@ struct FwdLds {
   FwdIn in[2];
 };
 
+// block bid of a pass over BHP (sequence, head, segment) blocks (the summary pass has 2 BHP: L, then M)
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void kda_bwd_fwd_kernel(BwdArgs a) {
-  extern __shared__ __align__(16) char smem[];
+__device__ __forceinline__ void fwd_body(const BwdArgs& a, char* smem, int64_t bid, int64_t BHP) {
   FwdLds& L = *reinterpret_cast<FwdLds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
   const int tt = tid >> 5, cg = tid & 31, c0 = 4 * cg;
   const int tb = opT_base(l16, q4);
-  const int64_t BHP = (int64_t)gridDim.x / (MODE == kSum ? 2 : 1);
-  const int64_t bid = blockIdx.x;
   const bool mpart = MODE == kSum && bid >= BHP;   // transition product: from I with v = 0
   const int64_t lb = mpart ? bid - BHP : bid;
   const int p = (int)(lb % a.nseg);
@@ -585,16 +583,16 @@ struct LocalLds {         // the local pass: operands, dout and Aq^T
   float rk[BC];
 };
 static_assert(sizeof(GradLds) <= 160 * 1024, "one block per CU");
+constexpr size_t kCkptLocalLds = sizeof(FwdLds) > sizeof(LocalLds) ? sizeof(FwdLds) : sizeof(LocalLds);
+static_assert(2 * kCkptLocalLds <= 160 * 1024, "two blocks per CU");
 
 template <bool LOCAL>
-__global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
-  extern __shared__ __align__(16) char smem[];
+__device__ __forceinline__ void grad_body(const BwdArgs& a, char* smem, int64_t bid) {
   typedef typename std::conditional<LOCAL, LocalLds, GradLds>::type Lds;
   Lds& L = *reinterpret_cast<Lds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
   const int tt = tid >> 5, cg = tid & 31, c0 = 4 * cg;
   const int tb = opT_base(l16, q4);
-  const int64_t bid = blockIdx.x;
   const int p = (int)(bid % a.nseg);
   const int64_t bh = bid / a.nseg;
   const int64_t b = bh / a.H, h = bh % a.H;
@@ -890,6 +888,24 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
   }
 }
 
+// The passes. The checkpoint and local passes are independent of each other and run as one
+// launch (two blocks per CU: each pass's latency fills the other's gaps).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_sum_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  fwd_body<kSum>(a, smem, blockIdx.x, gridDim.x / 2);
+}
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_ckpt_local_kernel(
+    BwdArgs a, int local) {
+  extern __shared__ __align__(16) char smem[];
+  const int64_t n = local ? gridDim.x / 2 : gridDim.x;   // checkpoint blocks first
+  if ((int64_t)blockIdx.x < n) fwd_body<kCkpt>(a, smem, blockIdx.x, n);
+  else grad_body<true>(a, smem, blockIdx.x - n);
+}
+__global__ __launch_bounds__(kThreads) void kda_bwd_grad_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  grad_body<false>(a, smem, blockIdx.x);
+}
+
 struct Cut {
   int64_t len;
   int nseg;
@@ -939,10 +955,9 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   static std::atomic<bool> attr_done[64];
   if (dev < 0 || dev >= 64 || !attr_done[dev].load(std::memory_order_acquire)) {
     const std::pair<const void*, int> fns[] = {
-        {reinterpret_cast<const void*>(&kda_bwd_fwd_kernel<kCkpt>), (int)sizeof(FwdLds)},
-        {reinterpret_cast<const void*>(&kda_bwd_fwd_kernel<kSum>), (int)sizeof(FwdLds)},
-        {reinterpret_cast<const void*>(&kda_bwd_grad_kernel<true>), (int)sizeof(LocalLds)},
-        {reinterpret_cast<const void*>(&kda_bwd_grad_kernel<false>), (int)sizeof(GradLds)},
+        {reinterpret_cast<const void*>(&kda_bwd_sum_kernel), (int)sizeof(FwdLds)},
+        {reinterpret_cast<const void*>(&kda_bwd_ckpt_local_kernel), (int)kCkptLocalLds},
+        {reinterpret_cast<const void*>(&kda_bwd_grad_kernel), (int)sizeof(GradLds)},
         {reinterpret_cast<const void*>(&kda_bwd_tfac_kernel), (int)(kTfacWaves * sizeof(TfacLds))}};
     for (const auto& f : fns) {
       e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, f.second);
@@ -993,9 +1008,9 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   if (c.nseg > 1) {
     BwdArgs s = a;
     s.Sout = Lw;
-    hipLaunchKernelGGL(kda_bwd_fwd_kernel<kSum>, dim3(2 * blocks), thr, sizeof(FwdLds), stream, s);
+    hipLaunchKernelGGL(kda_bwd_sum_kernel, dim3(2 * blocks), thr, sizeof(FwdLds), stream, s);
     e = hipGetLastError();
-    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_fwd_kernel", stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_sum_kernel", stream);
     if (e == hipSuccess) e = launch_kda_chain(false, Mw, Lw, x.S0, Sst, BH, c.nseg, D, D, stream);
     if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
     if (e != hipSuccess) return e;
@@ -1003,24 +1018,25 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   } else {
     a.Sin = x.S0;
   }
-  hipLaunchKernelGGL(kda_bwd_fwd_kernel<kCkpt>, dim3(blocks), thr, sizeof(FwdLds), stream, a);
-  e = hipGetLastError();
-  if (e == hipSuccess) e = mark_after(marks, "kda_bwd_fwd_kernel", stream);
-  if (e != hipSuccess) return e;
-  if (c.nseg > 1) {
+  // the checkpoint pass, and with segments the local pass in the same launch
+  {
     BwdArgs l = a;
     l.Eout = Ew;
-    hipLaunchKernelGGL(kda_bwd_grad_kernel<true>, dim3(blocks), thr, sizeof(LocalLds), stream, l);
+    const int local = c.nseg > 1 ? 1 : 0;
+    hipLaunchKernelGGL(kda_bwd_ckpt_local_kernel, dim3(blocks * (1 + local)), thr, kCkptLocalLds, stream, l, local);
     e = hipGetLastError();
-    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_local_kernel", stream);
-    if (e == hipSuccess) e = launch_kda_chain(true, Mw, Ew, g.dS_final, Gw, BH, c.nseg, D, D, stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_ckpt_local_kernel", stream);
+    if (e != hipSuccess) return e;
+  }
+  if (c.nseg > 1) {
+    e = launch_kda_chain(true, Mw, Ew, g.dS_final, Gw, BH, c.nseg, D, D, stream);
     if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
     if (e != hipSuccess) return e;
     a.Gin = Gw;
   } else {
     a.Gin = g.dS_final;
   }
-  hipLaunchKernelGGL(kda_bwd_grad_kernel<false>, dim3(blocks), thr, sizeof(GradLds), stream, a);
+  hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3(blocks), thr, sizeof(GradLds), stream, a);
   e = hipGetLastError();
   return e != hipSuccess ? e : mark_after(marks, "kda_bwd_grad_kernel", stream);
 }
