@@ -47,6 +47,13 @@ bool conv_rows_adjoint_ok(const Seg& seg, int64_t C, bool bf16);
 hipError_t launch_conv_rows_adjoint(const void* dy, void* dx, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
                                     const Seg* segs, int n, hipStream_t stream, Marks* marks = nullptr);
 
+// The conv's adjoint on the tile kernel (mirrored spatial taps, frames walked from the last one back),
+// for the grid segments that conv_tile_adjoint_ok accepts (bf16, C a multiple of 64, a frame within
+// 32-bit buffer offsets).
+bool conv_tile_adjoint_ok(const Seg& seg, int64_t C, bool bf16);
+hipError_t launch_conv_tile_adjoint(const void* dy, void* dx, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
+                                    const Seg& seg, hipStream_t stream, Marks* marks = nullptr);
+
 // Device-side neighbour table [T][27] for one segment (the conv kernels' arithmetic).
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream);
 

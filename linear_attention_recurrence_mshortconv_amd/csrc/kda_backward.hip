@@ -910,7 +910,10 @@ hipError_t conv_bwd_t(const void* x, const void* dy, void* dx, float* dw_text, f
   for (int i = 0; i < nseg; ++i) {
     const Seg& sg = segs[i];
     if (sg.length == 0) continue;
-    if (!conv_rows_adjoint_ok(sg, C, bf16)) {
+    if (!conv_rows_adjoint_ok(sg, C, bf16) && conv_tile_adjoint_ok(sg, C, bf16)) {   // video grids
+      e = launch_conv_tile_adjoint(dy, dx, w_vis, B, Ttot, C, sg, stream, nullptr);
+      if (e != hipSuccess) return e;
+    } else if (!conv_rows_adjoint_ok(sg, C, bf16)) {   // text, fp32
       const dim3 gx((unsigned)((C / 8 + 63) / 64), (unsigned)((sg.length + 3) / 4), (unsigned)B);
       hipLaunchKernelGGL(conv_bwd_dx_kernel<T>, gx, dim3(256), 0, stream, static_cast<const T*>(dy),
                          static_cast<T*>(dx), w_text, w_vis, Ttot, C, sg);

@@ -146,7 +146,10 @@ __device__ __forceinline__ void pack(uint2& u, const float* v) {
   u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
 }
 
-template <int NF, int CPT, int TR, int TW>
+// FLIP: the adjoint (dx from dy): the 3x3 spatial taps mirrored and the frames walked from the
+// last one back (logical frame f is frame frames - 1 - f of the segment, for reads and writes),
+// which turns the causal time taps into the anti-causal ones the adjoint needs.
+template <int NF, int CPT, int TR, int TW, bool FLIP = false>
 __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
     const uint16_t* __restrict__ x, uint16_t* __restrict__ y, const float* __restrict__ w_vis, int64_t Ttot,
     int64_t C, Seg seg, int n_slab, int n_tw, int n_th, int n_fr, int frames_per_block, int n_logical) {
@@ -185,7 +188,8 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
           const int kt = 3 - NF + t;
-          wr[t][kh][kw][i] = w_vis[((int64_t)slab * 64 + g * CPT + i) * kVisTaps + kt * 9 + kh * 3 + kw];
+          const int th_ = FLIP ? 2 - kh : kh, tw_ = FLIP ? 2 - kw : kw;
+          wr[t][kh][kw][i] = w_vis[((int64_t)slab * 64 + g * CPT + i) * kVisTaps + kt * 9 + th_ * 3 + tw_];
         }
 
   const int f_begin = fr * frames_per_block;
@@ -199,9 +203,10 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
   // Staging of one frame's tile plus halo: every thread first loads its items
   // into registers (all loads in flight together), then stores them to LDS.
   V pre[NIT];
+  auto phys = [&](int ff) { return FLIP ? seg.frames - 1 - ff : ff; };   // the segment frame of logical frame ff
   auto fetch = [&](int ff) {
-    const auto xr = __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (int64_t)ff * seg.height * seg.width * C), 0,
-                                                      frame_bytes, kRsrcWord3);
+    const auto xr = __builtin_amdgcn_make_buffer_rsrc((void*)(xb + (int64_t)phys(ff) * seg.height * seg.width * C),
+                                                      0, frame_bytes, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < NIT; ++j) {
       const int it = tid + j * Cfg::kThreads;
@@ -258,8 +263,8 @@ __global__ __launch_bounds__(TW * (64 / CPT)) void conv_tile_kernel(
         }
       }
     }
-    const auto yr = __builtin_amdgcn_make_buffer_rsrc((void*)(yb + (int64_t)f * seg.height * seg.width * C), 0,
-                                                      frame_bytes, kRsrcWord3);
+    const auto yr = __builtin_amdgcn_make_buffer_rsrc((void*)(yb + (int64_t)phys(f) * seg.height * seg.width * C),
+                                                      0, frame_bytes, kRsrcWord3);
 #pragma unroll
     for (int rr = 0; rr < TR; ++rr) {
       V out;
@@ -523,7 +528,7 @@ int device_cus() {
 
 template <int NF, int CPT, int TR, int TW>
 hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
-                       const Seg& seg, hipStream_t stream, Marks* marks) {
+                       const Seg& seg, hipStream_t stream, Marks* marks, bool flip = false) {
   using Cfg = TileCfg<NF, CPT, TR, TW>;
   const int n_slab = (int)(C / 64);
   const int n_tw = (int)((seg.width + TW - 1) / TW);
@@ -544,10 +549,14 @@ hipError_t launch_tile(const uint16_t* x, uint16_t* y, const float* w_vis, int64
   if (n_logical <= 0) return hipSuccess;
   if (n_logical > (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int64_t grid = (n_logical + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_tile_kernel<NF, CPT, TR, TW>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, stream, x, y,
-                     w_vis, Ttot, C, seg, n_slab, n_tw, n_th, n_fr, fpb, (int)n_logical);
+  if (flip)
+    hipLaunchKernelGGL((conv_tile_kernel<NF, CPT, TR, TW, true>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, stream,
+                       x, y, w_vis, Ttot, C, seg, n_slab, n_tw, n_th, n_fr, fpb, (int)n_logical);
+  else
+    hipLaunchKernelGGL((conv_tile_kernel<NF, CPT, TR, TW>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, stream, x, y,
+                       w_vis, Ttot, C, seg, n_slab, n_tw, n_th, n_fr, fpb, (int)n_logical);
   const hipError_t e = hipGetLastError();
-  return e != hipSuccess ? e : mark_after(marks, "conv_tile_kernel", stream);
+  return e != hipSuccess ? e : mark_after(marks, flip ? "conv_tile_adjoint_kernel" : "conv_tile_kernel", stream);
 }
 
 // Byte span of one rows-kernel buffer: (rows_per_range + 2) grid rows; kept
@@ -724,6 +733,17 @@ hipError_t launch_conv_rows_adjoint(const void* dy, void* dx, const float* w_vis
   if (B == 0 || n == 0) return hipSuccess;
   return launch_rows_batch<4, 32, true>(static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dx), w_vis, B, Ttot,
                                         C, segs, n, stream, marks);
+}
+
+bool conv_tile_adjoint_ok(const Seg& seg, int64_t C, bool bf16) {
+  return bf16 && seg.kind != SEG_TEXT && C % 64 == 0 && (int64_t)seg.height * seg.width * C * 2 <= (int64_t)kOutside - 64;
+}
+
+hipError_t launch_conv_tile_adjoint(const void* dy, void* dx, const float* w_vis, int64_t B, int64_t Ttot, int64_t C,
+                                    const Seg& seg, hipStream_t stream, Marks* marks) {
+  if (B == 0 || seg.length == 0) return hipSuccess;
+  return launch_tile<3, 4, 4, 16>(static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dx), w_vis, B, Ttot, C, seg,
+                                  stream, marks, true);
 }
 
 hipError_t launch_index_device(const Seg& seg, int64_t T, int32_t* idx, hipStream_t stream) {

@@ -345,8 +345,8 @@ def test_conv_bwd_fp32_mixed_layout(chm):
 
 def test_conv_bwd_bf16_grids(chm):
     """bf16: image grids take the image conv's kernel with mirrored taps for dx (one launch for
-    both images), the video and the text the gather kernel; dx within one bf16 rounding of the
-    fp64 adjoint, dw within fp32 summation error."""
+    both images), the video the tile kernel's adjoint, the text the gather kernel; dx within one
+    bf16 rounding of the fp64 adjoint, dw within fp32 summation error."""
     import torch
     S = wl.Segment
     segs = (S(wl.TEXT, 0, 5), S(wl.IMAGE, 5, 20 * 33, 1, 20, 33), S(wl.VIDEO, 665, 2 * 5 * 6, 2, 5, 6),
@@ -363,6 +363,30 @@ def test_conv_bwd_bf16_grids(chm):
     np.testing.assert_allclose(to_host(dx), ref["dx"], rtol=2.0 ** -8, atol=1e-4)
     for got, want in ((dwt, ref["dw_text"]), (dwv, ref["dw_vis"])):
         np.testing.assert_allclose(to_host(got), want, rtol=1e-4, atol=1e-4 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("frames,height,width", [(11, 6, 19), (2, 9, 17), (3, 4, 4)])
+def test_conv_bwd_bf16_video_adjoint(chm, frames, height, width):
+    """bf16 video dx on the tile kernel's adjoint (mirrored spatial taps, frames walked from the
+    last one back): 11 frames make two frame ranges of a block (the second starts from staged
+    frames after it), grids that are not a multiple of the 4 x 16 tile, and a grid smaller than
+    one tile, against the fp64 adjoint (dy outside the segment, a text prefix and a trailing text,
+    must not leak in)."""
+    import torch
+    S = wl.Segment
+    n = frames * height * width
+    segs = (S(wl.TEXT, 0, 7), S(wl.VIDEO, 7, n, frames, height, width), S(wl.TEXT, 7 + n, 5))
+    T, C = 7 + n + 5, 192
+    rng = np.random.default_rng(frames * 100 + height * 10 + width)
+    x = wl.round_to_bf16(rng.standard_normal((1, T, C)).astype(np.float32))
+    dy = wl.round_to_bf16(rng.standard_normal((1, T, C)).astype(np.float32))
+    wt = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    wv = (0.5 * rng.standard_normal((C, 27))).astype(np.float32)
+    dx, dwt, dwv = chm.mshortconv_bwd(to_device(x, "bf16"), to_device(dy, "bf16"), torch.from_numpy(wt),
+                                      torch.from_numpy(wv), segs)
+    ref = conv_backward_ref(x, wt, wv, segs, dy)
+    np.testing.assert_allclose(to_host(dx), ref["dx"], rtol=2.0 ** -8, atol=1e-4)
+    np.testing.assert_allclose(to_host(dwv), ref["dw_vis"], rtol=1e-4, atol=1e-4 * np.abs(ref["dw_vis"]).max())
 
 
 def test_pipeline_backward_bf16(chm):
