@@ -415,7 +415,9 @@ chimera_status chimera_kda_fwd_varlen_timed(const void* q, const void* k, const 
  *   - bf16 with dk = dv = 128 and T > 0, unless CHIMERA_KDA_SEQUENTIAL: the chunked form on
  *     MFMA (16-token chunks; the reverse of the chunk step of Eq. 14 per chunk, the states
  *     at chunk starts recomputed from forward passes inside the call and kept in the
- *     workspace as bf16, B H ceil(T/16) 32 KiB, plus six fp32 d x d matrices per segment).
+ *     workspace as bf16, 32 KiB each: with segments, each segment's two halves run one
+ *     after the other and only one half's states are kept, about B H ceil(T/32) of them,
+ *     plus 13 fp32 d x d matrices per segment; one segment keeps all B H ceil(T/16)).
  *     q, k, v, alpha and dout must be 8-byte aligned with qkv_stride a multiple of 4, else
  *     CHIMERA_ERR_UNSUPPORTED before any launch. Like the chunked forward, it raises alpha
  *     below e^-7.5 to e^-7.5 (dalpha is then the gradient at the raised value);

@@ -83,14 +83,23 @@ struct BwdArgs {
   int64_t seg_len;         // tokens per segment (a multiple of BC)
   int nseg;
   int l2norm;
+  // Segments split in two parts (split = 1, with segments): the checkpoint and gradient passes run
+  // per part (part 1, the second, first), so the checkpoints of one part at a time are kept
+  int split;
+  int part;
+  int64_t hmax;            // split: checkpoint slots per segment (chunks of its longer part)
   // state passes
   const float* Sin;        // start states: [bh][nseg][D][D] (nseg > 1) or S0 [bh][D][D]; null = zero
+  int64_t sin_stride;      // matrices between consecutive (bh, segment) entries of Sin (segments)
+  float* Hout;             // split: the summary pass's state at each part boundary, L slots then M
+                           // slots, [2][bh][nseg][2 slots][D][D] (the first slot of each pair)
   float* Sout;             // summary end states [bh][nseg][D][D]: L (blocks < BHP), M (blocks >= BHP)
   uint4* ckpt;             // [bh][ceil(T / BC)][8 waves][4][64 lanes] bf16 fragments
   uint2* tfrag;            // [bh][ceil(T / BC)][2][64 lanes]: each chunk's T and T^T mma16 A fragments
   // gradient passes
   const float* Gin;        // dS at segment ends: [bh][nseg][D][D] or dS_final [bh][D][D]; null = zero
   float* Eout;             // local pass: dS at each segment's start [bh][nseg][D][D]
+  float* Gmid;             // split: dS at each part boundary [bh][nseg][D][D] (part 1 writes, part 0 reads)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -98,6 +107,20 @@ struct BwdArgs {
   uint16_t* dbeta;
   float* dS0;              // [bh][D][D] or null
 };
+
+// The token range of a segment that a split pass runs: part 0 its first ceil(nc / 2) chunks, part 1
+// the rest (empty for a one-chunk segment).
+__device__ __forceinline__ int64_t part_mid(int64_t t_beg, int64_t t_end) {
+  const int64_t nc = (t_end - t_beg + BC - 1) / BC;
+  return min<int64_t>(t_end, t_beg + (nc + 1) / 2 * BC);
+}
+// the checkpoint of the chunk at token t0: per (bh, chunk), or split per (bh, segment, chunk of the
+// part that starts at token tp)
+__device__ __forceinline__ uint4* ckpt_at(const BwdArgs& a, int64_t bh, int p, int64_t nck, int64_t tp,
+                                          int64_t t0) {
+  const int64_t slot = a.split ? (bh * a.nseg + p) * a.hmax + (t0 - tp) / BC : bh * nck + t0 / BC;
+  return a.ckpt + slot * NWAVE * 4 * 64;
+}
 
 // ---- small helpers ----------------------------------------------------------------------
 // sum over the 16 lanes of a DPP row, in every lane
@@ -447,14 +470,23 @@ __device__ __forceinline__ void fwd_body(const BwdArgs& a, char* smem, int64_t b
   const int p = (int)(lb % a.nseg);
   const int64_t bh = lb / a.nseg;
   const int64_t b = bh / a.H, h = bh % a.H;
-  const int64_t t_beg = (int64_t)p * a.seg_len;
-  const int64_t t_end = min<int64_t>(a.T, t_beg + a.seg_len);
+  const int64_t s_beg = (int64_t)p * a.seg_len;
+  const int64_t s_end = min<int64_t>(a.T, s_beg + a.seg_len);
+  const int64_t s_mid = part_mid(s_beg, s_end);
+  // split: one part of the segment (the summary pass's part 0 ends at the boundary's state, its part
+  // 1 starts there)
+  const int64_t t_beg = a.split && a.part == 1 ? s_mid : s_beg;
+  const int64_t t_end = a.split && a.part == 0 ? s_mid : s_end;
   const int64_t nck = (a.T + BC - 1) / BC;
+  // the summary pass's part-boundary state of this block (L or M, the first slot of its pair)
+  float* hslot = MODE == kSum && a.split ? a.Hout + ((mpart ? 2 * BHP : 0) + 2 * lb) * (int64_t)(D * D) : nullptr;
 
   f32x4 S[8];
   {
     const float* src = nullptr;
-    if (MODE == kCkpt && a.Sin != nullptr) src = a.Sin + (a.nseg > 1 ? (bh * a.nseg + p) : bh) * (int64_t)(D * D);
+    if (MODE == kCkpt && a.Sin != nullptr)
+      src = a.Sin + (a.nseg > 1 ? (bh * a.nseg + p) * a.sin_stride : bh) * (int64_t)(D * D);
+    if (MODE == kSum && a.split && a.part == 1) src = hslot;
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -462,6 +494,21 @@ __device__ __forceinline__ void fwd_body(const BwdArgs& a, char* smem, int64_t b
         const int row = 16 * rt + 4 * q4 + r, col = 16 * w + l16;
         S[rt][r] = src != nullptr ? src[row * D + col] : (mpart && row == col ? 1.f : 0.f);
       }
+  }
+  float* out = nullptr;   // the summary pass's state at the end of its range
+  if (MODE == kSum)
+    out = a.split && a.part == 0 ? hslot : a.Sout + (mpart ? BHP : 0) * (int64_t)(D * D) + lb * (int64_t)(D * D);
+  auto store_state = [&]() {
+    if (out != nullptr) {
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[(16 * rt + 4 * q4 + r) * D + 16 * w + l16] = S[rt][r];
+    }
+  };
+  if (t_end <= t_beg) {   // an empty part 1 (a one-chunk segment): the state passes through (block-uniform)
+    store_state();
+    return;
   }
   // each chunk's rows and T fragment are loaded one chunk ahead
   RowLoad rl;
@@ -480,7 +527,7 @@ __device__ __forceinline__ void fwd_body(const BwdArgs& a, char* smem, int64_t b
     FwdIn& I = L.in[par];
     // phase 1: the chunk's rows into LDS, norms; the chunk's start state out
     if (MODE == kCkpt) {
-      uint4* dst = a.ckpt + ((bh * nck + t0 / BC) * NWAVE + w) * 4 * 64 + lane;
+      uint4* dst = ckpt_at(a, bh, p, nck, t_beg, t0) + w * 4 * 64 + lane;
 #pragma unroll
       for (int s = 0; s < 4; ++s) dst[s * 64] = sfrag(S, s);
     }
@@ -523,13 +570,7 @@ __device__ __forceinline__ void fwd_body(const BwdArgs& a, char* smem, int64_t b
       S[rt] = mma16(opT16(L.kb, rt, tb), Ub, x);
     }
   }
-  if (MODE == kSum) {
-    float* dst = a.Sout + (mpart ? BHP : 0) * (int64_t)(D * D) + lb * (int64_t)(D * D);
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * rt + 4 * q4 + r) * D + 16 * w + l16] = S[rt][r];
-  }
+  store_state();
 }
 
 // ---- gradient passes ---------------------------------------------------------------------
@@ -596,8 +637,14 @@ __device__ __forceinline__ void grad_body(const BwdArgs& a, char* smem, int64_t 
   const int p = (int)(bid % a.nseg);
   const int64_t bh = bid / a.nseg;
   const int64_t b = bh / a.H, h = bh % a.H;
-  const int64_t t_beg = (int64_t)p * a.seg_len;
-  const int64_t t_end = min<int64_t>(a.T, t_beg + a.seg_len);
+  const int64_t s_beg = (int64_t)p * a.seg_len;
+  const int64_t s_end = min<int64_t>(a.T, s_beg + a.seg_len);
+  const int64_t s_mid = part_mid(s_beg, s_end);
+  // the local pass runs the whole segment, a split gradient pass one part of it (part 1 from dS at
+  // the segment end to the part boundary, part 0 from there to the segment start)
+  const bool split = !LOCAL && a.split;
+  const int64_t t_beg = split && a.part == 1 ? s_mid : s_beg;
+  const int64_t t_end = split && a.part == 0 ? s_mid : s_end;
   const int64_t nck = (a.T + BC - 1) / BC;
   const int pc = 16 * w + l16;    // this lane's channel position (per-channel gradients)
   const int ch = cinv(pc);        // ... and its channel
@@ -605,12 +652,30 @@ __device__ __forceinline__ void grad_body(const BwdArgs& a, char* smem, int64_t 
   f32x4 dS[8];
   {
     const float* src = nullptr;
-    if (!LOCAL && a.Gin != nullptr) src = a.Gin + (a.nseg > 1 ? (bh * a.nseg + p) : bh) * (int64_t)(D * D);
+    if (split && a.part == 0) src = a.Gmid + (bh * a.nseg + p) * (int64_t)(D * D);
+    else if (!LOCAL && a.Gin != nullptr) src = a.Gin + (a.nseg > 1 ? (bh * a.nseg + p) : bh) * (int64_t)(D * D);
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         dS[rt][r] = src != nullptr ? src[(16 * rt + 4 * q4 + r) * D + 16 * w + l16] : 0.f;
+  }
+  // where dS goes at the end: the local pass's segment start, a split part 1's boundary, or dS0
+  float* out = nullptr;
+  if (LOCAL) out = a.Eout + (bh * a.nseg + p) * (int64_t)(D * D);
+  else if (split && a.part == 1) out = a.Gmid + (bh * a.nseg + p) * (int64_t)(D * D);
+  else if (p == 0 && a.dS0 != nullptr) out = a.dS0 + bh * (int64_t)(D * D);
+  auto store_out = [&]() {
+    if (out != nullptr) {
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[(16 * rt + 4 * q4 + r) * D + 16 * w + l16] = dS[rt][r];
+    }
+  };
+  if (t_end <= t_beg) {   // an empty part 1 (a one-chunk segment): dS passes through (block-uniform)
+    store_out();
+    return;
   }
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const int64_t first = (t_end - 1 - t_beg) / BC;   // the segment's last chunk (t_end > t_beg)
@@ -626,7 +691,7 @@ __device__ __forceinline__ void grad_body(const BwdArgs& a, char* smem, int64_t 
     ttfn = tfrag(a, bh, nck, c0t / BC, 1, lane);
   };
   auto load_frags = [&](int64_t c) {
-    const uint4* src = a.ckpt + ((bh * nck + (t_beg + c * BC) / BC) * NWAVE + w) * 4 * 64 + lane;
+    const uint4* src = ckpt_at(a, bh, p, nck, t_beg, t_beg + c * BC) + w * 4 * 64 + lane;
 #pragma unroll
     for (int s = 0; s < 4; ++s) Sf[s] = src[s * 64];
   };
@@ -877,15 +942,7 @@ __device__ __forceinline__ void grad_body(const BwdArgs& a, char* smem, int64_t 
       }
     }
   }
-  float* out = nullptr;
-  if (LOCAL) out = a.Eout + (bh * a.nseg + p) * (int64_t)(D * D);
-  else if (p == 0 && a.dS0 != nullptr) out = a.dS0 + bh * (int64_t)(D * D);
-  if (out != nullptr) {
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) out[(16 * rt + 4 * q4 + r) * D + 16 * w + l16] = dS[rt][r];
-  }
+  store_out();
 }
 
 // The passes. The checkpoint and local passes are independent of each other and run as one
@@ -910,6 +967,9 @@ struct Cut {
   int64_t len;
   int nseg;
 };
+constexpr int kSegMats = 6 + 7;   // per (bh, segment): L, M, start, E, G, spare; 2 x 2 + 2 + 1 at the part boundary
+// checkpoint slots per segment of len tokens when split: the chunks of its longer (first) part
+int64_t part_slots(int64_t len) { return ((len + BC - 1) / BC + 1) / 2; }
 Cut bwd_chunked_cut(int64_t B, int64_t T, int64_t H) {
   const int64_t bh = std::max<int64_t>(1, B * H);
   int64_t P = (kTargetBlocks + bh - 1) / bh;
@@ -934,15 +994,18 @@ bool kda_bwd_chunked_layout_ok(const KdaArgs& a, const KdaGrads& g) {
 size_t kda_bwd_chunked_workspace(int64_t B, int64_t T, int64_t H) {
   const Cut c = bwd_chunked_cut(B, T, H);
   const size_t nck = (size_t)((T + BC - 1) / BC);
-  const size_t ck = (size_t)(B * H) * nck * D * D * sizeof(uint16_t);
+  const size_t slots = c.nseg > 1 ? (size_t)c.nseg * (size_t)part_slots(c.len) : nck;   // per (b, h)
+  const size_t ck = (size_t)(B * H) * slots * D * D * sizeof(uint16_t);
   const size_t tf = (size_t)(B * H) * nck * 2 * 64 * sizeof(uint2);
-  const size_t segs = c.nseg > 1 ? (size_t)(B * H) * c.nseg * 6 * D * D * sizeof(float) : 0;
+  const size_t segs = c.nseg > 1 ? (size_t)(B * H) * c.nseg * kSegMats * D * D * sizeof(float) : 0;
   return ck + tf + segs;
 }
 
-// Workspace: the bf16 chunk states, the chunks' T fragments, then (segments only) L and M of
-// every segment (the summary pass writes [L of all (bh, p)][M of all (bh, p)]), the start
-// states, E and G.
+// Workspace: the bf16 chunk states (with segments: of one part of every segment at a time), the
+// chunks' T fragments, then (segments only) per (bh, segment) fp32 D x D matrices: L and M of every
+// segment (the summary pass writes [L of all (bh, p)][M of all (bh, p)]), the start states, E, G
+// and a spare, then the part-boundary states of the summary pass (L, M: two slots each), the chain's
+// part-boundary starts (two slots) and dS at the part boundaries.
 hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void* workspace, hipStream_t stream,
                                        Marks* marks) {
   if (x.B * x.H == 0 || x.T == 0) return hipSuccess;
@@ -979,6 +1042,10 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   a.nseg = c.nseg;
   a.l2norm = x.l2norm ? 1 : 0;
   a.ckpt = static_cast<uint4*>(workspace);
+  a.split = c.nseg > 1 ? 1 : 0;
+  a.part = 0;
+  a.hmax = part_slots(c.len);
+  a.sin_stride = 1;
   a.dq = static_cast<uint16_t*>(g.dq);
   a.dk = static_cast<uint16_t*>(g.dk);
   a.dv = static_cast<uint16_t*>(g.dv);
@@ -986,7 +1053,8 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   a.dbeta = static_cast<uint16_t*>(g.dbeta);
   a.dS0 = g.dS0;
   const int64_t nck = (x.T + BC - 1) / BC;
-  const size_t ck = (size_t)BH * (size_t)nck * D * D * sizeof(uint16_t);
+  const size_t slots = a.split ? (size_t)c.nseg * (size_t)a.hmax : (size_t)nck;
+  const size_t ck = (size_t)BH * slots * D * D * sizeof(uint16_t);
   const size_t tfb = (size_t)BH * (size_t)nck * 2 * 64 * sizeof(uint2);
   a.tfrag = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + ck);
   const int64_t mat = BH * c.nseg * (int64_t)(D * D);
@@ -995,6 +1063,9 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   float* Sst = Mw + mat;
   float* Ew = Sst + mat;
   float* Gw = Ew + mat;
+  float* Hw = Lw + 6 * mat;   // part boundary: [L: 2 slots][M: 2 slots] per (bh, segment)
+  float* Yw = Hw + 4 * mat;   // the part-boundary starts (slot 1 of each pair)
+  float* Gm = Yw + 2 * mat;   // dS at the part boundaries
   const dim3 thr(kThreads);
   const unsigned blocks = (unsigned)(BH * c.nseg);
   {
@@ -1005,40 +1076,72 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
     if (e == hipSuccess) e = mark_after(marks, "kda_bwd_tfac_kernel", stream);
     if (e != hipSuccess) return e;
   }
-  if (c.nseg > 1) {
-    BwdArgs s = a;
-    s.Sout = Lw;
-    hipLaunchKernelGGL(kda_bwd_sum_kernel, dim3(2 * blocks), thr, sizeof(FwdLds), stream, s);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_sum_kernel", stream);
-    if (e == hipSuccess) e = launch_kda_chain(false, Mw, Lw, x.S0, Sst, BH, c.nseg, D, D, stream);
-    if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
-    if (e != hipSuccess) return e;
-    a.Sin = Sst;
-  } else {
+  if (c.nseg == 1) {   // one segment: the checkpoint pass, then the gradient pass
     a.Sin = x.S0;
-  }
-  // the checkpoint pass, and with segments the local pass in the same launch
-  {
-    BwdArgs l = a;
-    l.Eout = Ew;
-    const int local = c.nseg > 1 ? 1 : 0;
-    hipLaunchKernelGGL(kda_bwd_ckpt_local_kernel, dim3(blocks * (1 + local)), thr, kCkptLocalLds, stream, l, local);
+    a.Gin = g.dS_final;
+    hipLaunchKernelGGL(kda_bwd_ckpt_local_kernel, dim3(blocks), thr, kCkptLocalLds, stream, a, 0);
     e = hipGetLastError();
     if (e == hipSuccess) e = mark_after(marks, "kda_bwd_ckpt_local_kernel", stream);
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3(blocks), thr, sizeof(GradLds), stream, a);
+    e = hipGetLastError();
+    return e != hipSuccess ? e : mark_after(marks, "kda_bwd_grad_kernel", stream);
   }
-  if (c.nseg > 1) {
-    e = launch_kda_chain(true, Mw, Ew, g.dS_final, Gw, BH, c.nseg, D, D, stream);
+  // Segments, each split in two parts so that the checkpoints of one part at a time are kept: the
+  // summary pass in two launches (each segment's L and M at its part boundary, then at its end), the
+  // chain of segment starts,
+  // the part-boundary starts (S_mid = M_half S_start + L_half, a one-step chain per segment); part 1's
+  // checkpoints with the local pass in one launch, the chain of dL/dS at segment ends, part 1's
+  // gradients (down to dS at the part boundary), part 0's checkpoints, part 0's gradients.
+  {
+    BwdArgs s = a;
+    s.Sout = Lw;
+    s.Hout = Hw;
+    for (int part = 0; part < 2 && e == hipSuccess; ++part) {   // part 1 from part 0's boundary state
+      s.part = part;
+      hipLaunchKernelGGL(kda_bwd_sum_kernel, dim3(2 * blocks), thr, sizeof(FwdLds), stream, s);
+      e = hipGetLastError();
+      if (e == hipSuccess) e = mark_after(marks, "kda_bwd_sum_kernel", stream);
+    }
+    if (e == hipSuccess) e = launch_kda_chain(false, Mw, Lw, x.S0, Sst, BH, c.nseg, D, D, stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
+    if (e == hipSuccess) e = launch_kda_chain(false, Hw + 2 * mat, Hw, Sst, Yw, BH * c.nseg, 2, D, D, stream);
     if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
     if (e != hipSuccess) return e;
-    a.Gin = Gw;
-  } else {
-    a.Gin = g.dS_final;
   }
-  hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3(blocks), thr, sizeof(GradLds), stream, a);
-  e = hipGetLastError();
-  return e != hipSuccess ? e : mark_after(marks, "kda_bwd_grad_kernel", stream);
+  {
+    BwdArgs l = a;
+    l.part = 1;
+    l.Sin = Yw + D * D;
+    l.sin_stride = 2;
+    l.Eout = Ew;
+    hipLaunchKernelGGL(kda_bwd_ckpt_local_kernel, dim3(2 * blocks), thr, kCkptLocalLds, stream, l, 1);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_ckpt_local_kernel", stream);
+    if (e == hipSuccess) e = launch_kda_chain(true, Mw, Ew, g.dS_final, Gw, BH, c.nseg, D, D, stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
+    if (e != hipSuccess) return e;
+  }
+  a.Gin = Gw;
+  a.Gmid = Gm;
+  for (int part = 1; part >= 0; --part) {
+    if (part == 0) {
+      BwdArgs c0 = a;
+      c0.part = 0;
+      c0.Sin = Sst;
+      hipLaunchKernelGGL(kda_bwd_ckpt_local_kernel, dim3(blocks), thr, kCkptLocalLds, stream, c0, 0);
+      e = hipGetLastError();
+      if (e == hipSuccess) e = mark_after(marks, "kda_bwd_ckpt_local_kernel", stream);
+      if (e != hipSuccess) return e;
+    }
+    BwdArgs gp = a;
+    gp.part = part;
+    hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3(blocks), thr, sizeof(GradLds), stream, gp);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_grad_kernel", stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace chm

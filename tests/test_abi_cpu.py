@@ -209,11 +209,16 @@ def test_backward_argument_errors():
     assert call(stride=100) == 2
     assert call() == 6                                                  # workspace missing
     assert call(B=0) == 0
-    # bf16 heads of 128 run the chunked backward: the bf16 state before every 16-token chunk and
-    # 1 KiB of T fragments per chunk, plus six fp32 matrices per segment (here 5 segments of 272
-    # tokens per head)
+    # bf16 heads of 128 run the chunked backward: here 5 segments of 272 tokens (17 chunks of 16) per
+    # head, each split in two parts whose checkpoints are kept one part at a time: the bf16 state
+    # before each chunk of the longer part (9 slots per segment), 1 KiB of T fragments per chunk,
+    # and 13 fp32 matrices per segment (its L, M, start, E, G and a spare; at its part boundary L and
+    # M in two slots each, the start in two slots, dS)
     n = int(L.chimera_kda_bwd_workspace_size(1, 64 * 20 + 3, 16, 128, 128, 1, 1))
-    assert n == 2 * 16 * 81 * 128 * 128 + 16 * 81 * 1024 + 4 * 6 * 16 * 5 * 128 * 128
+    assert n == 2 * 16 * 5 * 9 * 128 * 128 + 16 * 81 * 1024 + 4 * 13 * 16 * 5 * 128 * 128
+    # one segment (sequences too short to cut): the state before every chunk, no per-segment matrices
+    n1 = int(L.chimera_kda_bwd_workspace_size(1, 200, 16, 128, 128, 1, 1))
+    assert n1 == 2 * 16 * 13 * 128 * 128 + 16 * 13 * 1024
     # the token-by-token backward (CHIMERA_KDA_SEQUENTIAL, or fp32): fp32 checkpoints + slice partials
     for dt, fl in ((1, 3), (0, 1)):
         n = int(L.chimera_kda_bwd_workspace_size(1, 64 * 20 + 3, 16, 128, 128, dt, fl))

@@ -95,14 +95,15 @@ def test_kda_bwd_bf16_d128(chm, T):
 
 @pytest.mark.parametrize("B,T,H,l2norm,init,decay", [
     (1, 1000, 2, True, True, 0.3),     # three segments of 336, 336 and 328 tokens; a ragged last chunk
+    (1, 4357, 1, True, True, 0.3),     # 17 segments of 272 tokens, the last of 5: its second part is empty
     (2, 77, 3, True, False, 0.3),      # one segment with a ragged chunk, two batch items, no S0 / dS_final
     (1, 16, 1, False, True, 0.3),      # exactly one chunk, no normalisation
     (1, 600, 1, True, True, 3.0),      # strong decay (alpha down to about e^-8 within a chunk), 2 segments
 ])
 def test_kda_bwd_chunked_bf16(chm, B, T, H, l2norm, init, decay):
-    """The chunked MFMA backward (bf16, d = 128; 16-token chunks, segments joined by chains) against
-    the fp64 autograd oracle, and the token-by-token backward (CHIMERA_KDA_SEQUENTIAL) on the same
-    inputs against it too."""
+    """The chunked MFMA backward (bf16, d = 128; 16-token chunks, segments joined by chains, each
+    segment's checkpoint and gradient passes run per half) against the fp64 autograd oracle, and the
+    token-by-token backward (CHIMERA_KDA_SEQUENTIAL) on the same inputs against it too."""
     import torch
     rng = np.random.default_rng(300 + T + H)
     q, k, v, alpha, beta, S0, do, dS = _case(rng, B, T, H, 128, 128, "bf16")
