@@ -945,6 +945,127 @@ __device__ __forceinline__ void grad_body(const BwdArgs& a, char* smem, int64_t 
   store_out();
 }
 
+// ---- chains of segment states on MFMA -------------------------------------------------------
+// Y_0 = init, Y_p = A_p Y_{p-1} + X_{p-1} over the segments of each (bh) (forward: A_p = M_{p-1};
+// BACK: from the last segment down, Y_p = M_{p+1}^T Y_{p+1} + X_{p+1}), fp32 d x d row-major
+// matrices [bh][nseg][D][D], init [bh][D][D] or null. As the forward pass's combine step: block
+// (bh, slice) owns columns 16 slice .. 16 slice + 15 of Y, wave w rows 16 w .. 16 w + 15 of them in
+// fp32 (MFMA D layout); each step exchanges the base through LDS split into bf16 high and low parts
+// and forms the product with three bf16 MFMAs per k slot (hi*hi + hi*lo + lo*hi, about 16
+// significant bits per product), the A fragments split from the fp32 M as they arrive. The next
+// step's M rows (M^T: columns) and X are loaded while a step computes.
+constexpr int kChThreads = 512;
+constexpr int kChP = D + 8;   // LDS pitch of the transposed base (bf16 elements)
+// v split into bf16 high parts (returned) and low parts v - hi (in lo), 8 values
+__device__ __forceinline__ uint4 split8(const float (&v)[8], uint4& lo) {
+  const uint2 h0 = pack4(make_float4(v[0], v[1], v[2], v[3])), h1 = pack4(make_float4(v[4], v[5], v[6], v[7]));
+  const float4 b0 = unpack4(h0), b1 = unpack4(h1);
+  const uint2 l0 = pack4(make_float4(v[0] - b0.x, v[1] - b0.y, v[2] - b0.z, v[3] - b0.w));
+  const uint2 l1 = pack4(make_float4(v[4] - b1.x, v[5] - b1.y, v[6] - b1.z, v[7] - b1.w));
+  lo = cat(l0, l1);
+  return cat(h0, h1);
+}
+template <bool BACK>
+__global__ __launch_bounds__(kChThreads) void kda_bwd_chain_kernel(const float* __restrict__ M,
+                                                                   const float* __restrict__ X,
+                                                                   const float* __restrict__ init,
+                                                                   float* __restrict__ Y, int nseg) {
+  __shared__ __align__(16) uint16_t bhi[2][16 * kChP];   // [column][cpos(row)] of the base, by step parity
+  __shared__ __align__(16) uint16_t blo[2][16 * kChP];
+  const int slice = blockIdx.x & 7;
+  const int64_t bh = blockIdx.x >> 3;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = 16 * slice + l16;
+  const int row0 = 16 * w + 4 * q4;   // D-layout rows of this lane: row0 .. row0 + 3
+  const int64_t off0 = bh * nseg * (int64_t)(D * D);   // this (bh)'s first matrix
+  auto at = [&](const float* base, int p) { return base + off0 + p * (int64_t)(D * D); };
+  auto at_w = [&](float* base, int p) { return base + off0 + p * (int64_t)(D * D); };
+  f32x4 cur;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cur[r] = init != nullptr ? init[(bh * D + row0 + r) * D + col] : 0.f;
+  auto put = [&](int p) {
+    float* y = at_w(Y, p);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[(row0 + r) * D + col] = cur[r];
+  };
+  put(BACK ? nseg - 1 : 0);
+  // the operands of step i (1 .. nseg - 1): A's 32 values of this lane (row 16 w + l16, k = the
+  // positions 32 s + 4 q4 .. + 3 and 32 s + 16 + 4 q4 .. + 3 of each slot s) and X's 4
+  struct Ops {
+    float a[4][8];
+    f32x4 x;
+  };
+  auto src_of = [&](int i) {   // the segment whose M and X form step i (clamped: no load in a branch)
+    const int ic = min(max(i, 1), max(nseg - 1, 1));
+    return min(BACK ? nseg - ic : ic - 1, nseg - 1);
+  };
+  auto fetch = [&](int i, Ops& o) {
+    const int src = src_of(i);
+    const float* m = at(M, src);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (!BACK) {
+        const float4 u = *reinterpret_cast<const float4*>(&m[(16 * w + l16) * D + 32 * s + 4 * q4]);
+        const float4 v = *reinterpret_cast<const float4*>(&m[(16 * w + l16) * D + 32 * s + 16 + 4 * q4]);
+        o.a[s][0] = u.x; o.a[s][1] = u.y; o.a[s][2] = u.z; o.a[s][3] = u.w;
+        o.a[s][4] = v.x; o.a[s][5] = v.y; o.a[s][6] = v.z; o.a[s][7] = v.w;
+      } else {
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          o.a[s][i2] = m[(32 * s + 4 * q4 + i2) * D + 16 * w + l16];
+          o.a[s][4 + i2] = m[(32 * s + 16 + 4 * q4 + i2) * D + 16 * w + l16];
+        }
+      }
+    }
+    const float* x = at(X, src);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o.x[r] = x[(row0 + r) * D + col];
+  };
+  Ops nxt;
+  fetch(1, nxt);
+  for (int i = 1; i < nseg; ++i) {
+    const Ops op = nxt;
+    fetch(i + 1, nxt);
+    const int buf = i & 1;
+    {   // the base's rows row0 .. row0 + 3 of column l16 -> LDS, transposed and split
+      uint2 lo;
+      const float4 c4 = make_float4(cur[0], cur[1], cur[2], cur[3]);
+      const uint2 hi = pack4(c4);
+      const float4 b = unpack4(hi);
+      lo = pack4(make_float4(c4.x - b.x, c4.y - b.y, c4.z - b.z, c4.w - b.w));
+      const int pos = cpos(row0);
+      *reinterpret_cast<uint2*>(&bhi[buf][l16 * kChP + pos]) = hi;
+      *reinterpret_cast<uint2*>(&blo[buf][l16 * kChP + pos]) = lo;
+    }
+    lds_barrier();
+    f32x4 acc0 = op.x, acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 bH = *reinterpret_cast<const uint4*>(&bhi[buf][l16 * kChP + 32 * s + 8 * q4]);
+      const uint4 bL = *reinterpret_cast<const uint4*>(&blo[buf][l16 * kChP + 32 * s + 8 * q4]);
+      uint4 al;
+      const uint4 ah = split8(op.a[s], al);
+      acc1 = mma32(al, bH, acc1);
+      acc2 = mma32(ah, bL, acc2);
+      acc0 = mma32(ah, bH, acc0);
+    }
+    cur = acc0 + (acc1 + acc2);
+    put(BACK ? nseg - 1 - i : i);
+  }
+}
+// The chains of the chunked backward (dk = dv = D) for BH (bh) of nseg segments each; as
+// launch_kda_chain, on MFMA.
+hipError_t launch_bwd_chain(bool back, const float* M, const float* X, const float* init, float* Y, int64_t BH,
+                            int nseg, hipStream_t stream) {
+  if (BH * 8 > 0x7fffffff) return hipErrorInvalidValue;
+  if (BH == 0) return hipSuccess;
+  const dim3 grid((unsigned)(BH * 8)), thr(kChThreads);
+  if (back) hipLaunchKernelGGL(kda_bwd_chain_kernel<true>, grid, thr, 0, stream, M, X, init, Y, nseg);
+  else hipLaunchKernelGGL(kda_bwd_chain_kernel<false>, grid, thr, 0, stream, M, X, init, Y, nseg);
+  return hipGetLastError();
+}
+
 // The passes. The checkpoint and local passes are independent of each other and run as one
 // launch (two blocks per CU: each pass's latency fills the other's gaps).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void kda_bwd_sum_kernel(BwdArgs a) {
@@ -1103,10 +1224,10 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
       e = hipGetLastError();
       if (e == hipSuccess) e = mark_after(marks, "kda_bwd_sum_kernel", stream);
     }
-    if (e == hipSuccess) e = launch_kda_chain(false, Mw, Lw, x.S0, Sst, BH, c.nseg, D, D, stream);
-    if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
-    if (e == hipSuccess) e = launch_kda_chain(false, Hw + 2 * mat, Hw, Sst, Yw, BH * c.nseg, 2, D, D, stream);
-    if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
+    if (e == hipSuccess) e = launch_bwd_chain(false, Mw, Lw, x.S0, Sst, BH, c.nseg, stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_chain_kernel", stream);
+    if (e == hipSuccess) e = launch_bwd_chain(false, Hw + 2 * mat, Hw, Sst, Yw, BH * c.nseg, 2, stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_chain_kernel", stream);
     if (e != hipSuccess) return e;
   }
   {
@@ -1118,8 +1239,8 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
     hipLaunchKernelGGL(kda_bwd_ckpt_local_kernel, dim3(2 * blocks), thr, kCkptLocalLds, stream, l, 1);
     e = hipGetLastError();
     if (e == hipSuccess) e = mark_after(marks, "kda_bwd_ckpt_local_kernel", stream);
-    if (e == hipSuccess) e = launch_kda_chain(true, Mw, Ew, g.dS_final, Gw, BH, c.nseg, D, D, stream);
-    if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
+    if (e == hipSuccess) e = launch_bwd_chain(true, Mw, Ew, g.dS_final, Gw, BH, c.nseg, stream);
+    if (e == hipSuccess) e = mark_after(marks, "kda_bwd_chain_kernel", stream);
     if (e != hipSuccess) return e;
   }
   a.Gin = Gw;
