@@ -742,8 +742,10 @@ __global__ __launch_bounds__(64 * kDwWaves) void conv_bwd_dw_grid_kernel(const T
         }
       const auto dr = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(dyb + (seg.start + (int64_t)f * hw + (int64_t)hh * W) * C), 0, rowb, 0x00020000);
-      for (int r = 0; r < run; r += U) {
-        float col[U][KT][3][CPT], g[U][CPT];
+      // two groups of U tokens in flight: the next group's loads go out before this group's sums
+      // (loads past the row's end read zero; tokens past the range's end add nothing)
+      float colA[U][KT][3][CPT], gA[U][CPT], colB[U][KT][3][CPT], gB[U][CPT];
+      auto issue = [&](int r, float (&col)[U][KT][3][CPT], float (&g)[U][CPT]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -751,13 +753,12 @@ __global__ __launch_bounds__(64 * kDwWaves) void conv_bwd_dw_grid_kernel(const T
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh) ld_cpt<T, CPT>(xr[kt][kh], voff, (ww + r + u + 1) * colb, col[u][kt][kh]);
           ld_cpt<T, CPT>(dr, voff, (ww + r + u) * colb, g[u]);
-          if (r + u >= run) {   // past the range's end on this row: adds nothing (wave-uniform)
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) g[u][i] = 0.f;
-          }
         }
+      };
+      auto sums = [&](int r, const float (&col)[U][KT][3][CPT], const float (&g)[U][CPT]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+          const float keep = r + u < run ? 1.f : 0.f;   // wave-uniform
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -768,13 +769,21 @@ __global__ __launch_bounds__(64 * kDwWaves) void conv_bwd_dw_grid_kernel(const T
               for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
                 for (int i = 0; i < CPT; ++i)
-                  acc[kt][kh][kw][i] = fmaf(win[kt][kh][kw][i], g[u][i], acc[kt][kh][kw][i]);
+                  acc[kt][kh][kw][i] = fmaf(win[kt][kh][kw][i], g[u][i] * keep, acc[kt][kh][kw][i]);
 #pragma unroll
               for (int i = 0; i < CPT; ++i) {
                 win[kt][kh][0][i] = win[kt][kh][1][i];
                 win[kt][kh][1][i] = win[kt][kh][2][i];
               }
             }
+        }
+      };
+      issue(0, colA, gA);
+      for (int r = 0; r < run; r += 2 * U) {
+        issue(r + U, colB, gB);
+        sums(r, colA, gA);
+        issue(r + 2 * U, colA, gA);
+        sums(r + U, colB, gB);
       }
       local += run;
       ww += run;
