@@ -115,6 +115,39 @@ def _oracle_head_job(job):
     return n * B
 
 
+def achievable_peaks(dev) -> dict:
+    """What this machine reaches outside the path, for context beside the datasheet peaks: a 1 GiB device copy
+    (torch's copy kernel: read + write bytes over its time) and a plain 8192^3 bf16 GEMM (torch.matmul on
+    contiguous operands, the library's tuned kernel). Each: 2 warm-up runs, then the mean of 10 timed with
+    HIP events; after the bench's timed steps, outside them."""
+    import torch
+    def timed(fn, n=10):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e-3
+    src = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device=dev)   # 1 GiB
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    copy_gbs = 2 * src.numel() * 2 / t_copy / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    t_mm = timed(lambda: torch.matmul(a, b))
+    gemm_tflops = 2 * n ** 3 / t_mm / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": copy_gbs, "gemm_bf16_TFLOPs": gemm_tflops,
+            "recipe": "1 GiB bf16 device copy (read + write) and an 8192^3 bf16 torch.matmul, mean of 10 after 2 warm-ups"}
+
+
 def short_name(full: str) -> str:
     """'void chm::(anonymous namespace)::conv_rows_kernel<4, 32>(...)' -> 'conv_rows_kernel'."""
     s = full.replace("(anonymous namespace)::", "")
@@ -815,6 +848,12 @@ def main():
                                             "measured step"}},
         "cpu_baseline": None,
     }
+    # the same achieved figures against what this machine reaches with a plain copy and a library GEMM
+    ach = achievable_peaks(dev)
+    rf = out["roofline"]
+    rf["achievable"] = dict(ach, frac_of_copy=rf["achieved"] / ach["copy_GBps"],
+                            mfma_frac_of_gemm=rf["mfma"]["achieved"] / ach["gemm_bf16_TFLOPs"],
+                            conv_frac_of_copy=out["config"]["conv_call"]["GBps_algorithmic"] / ach["copy_GBps"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_sample_tokens // max(B, 1), gate_np)
         if pool is not None and gate_np is None:
