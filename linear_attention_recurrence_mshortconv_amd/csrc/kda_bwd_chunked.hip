@@ -1210,10 +1210,10 @@ hipError_t launch_kda_backward_chunked(const KdaArgs& x, const KdaGrads& g, void
   }
   // Segments, each split in two parts so that the checkpoints of one part at a time are kept: the
   // summary pass in two launches (each segment's L and M at its part boundary, then at its end), the
-  // chain of segment starts,
-  // the part-boundary starts (S_mid = M_half S_start + L_half, a one-step chain per segment); part 1's
-  // checkpoints with the local pass in one launch, the chain of dL/dS at segment ends, part 1's
-  // gradients (down to dS at the part boundary), part 0's checkpoints, part 0's gradients.
+  // chain of segment starts, the part-boundary starts (S_mid = M_half S_start + L_half, a one-step
+  // chain per segment); part 1's checkpoints with the local pass in one launch, the chain of dL/dS at
+  // segment ends, part 1's gradients (down to dS at the part boundary), part 0's checkpoints, part 0's
+  // gradients.
   {
     BwdArgs s = a;
     s.Sout = Lw;
