@@ -96,6 +96,7 @@ def test_kda_bwd_bf16_d128(chm, T):
 @pytest.mark.parametrize("B,T,H,l2norm,init,decay", [
     (1, 1000, 2, True, True, 0.3),     # three segments of 336, 336 and 328 tokens; a ragged last chunk
     (1, 4357, 1, True, True, 0.3),     # 17 segments of 272 tokens, the last of 5: its second part is empty
+    (2, 600, 2, True, True, 0.3),      # two batch items of two heads, two segments each
     (2, 77, 3, True, False, 0.3),      # one segment with a ragged chunk, two batch items, no S0 / dS_final
     (1, 16, 1, False, True, 0.3),      # exactly one chunk, no normalisation
     (1, 600, 1, True, True, 3.0),      # strong decay (alpha down to about e^-8 within a chunk), 2 segments
