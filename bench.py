@@ -753,7 +753,7 @@ def main():
 
     # the same steps again with an event after every kernel, for the per-kernel durations (the
     # events add gaps between launches: these steps are reported, not used for the headline)
-    kda_cap = 2 * nseq + 4 if w.samples else (5 if args.gated else 4)
+    kda_cap = 2 * nseq + 4 if w.samples else (6 if args.gated else 5)
     marks = [(chm.Marks(len(segs) + 1), chm.Marks(kda_cap)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

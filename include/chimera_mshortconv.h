@@ -144,7 +144,7 @@ chimera_status chimera_mshortconv_fwd(const void* x, void* y, int64_t B, int64_t
                                       (token, head) before the recurrence (Chimera page 1, Fig. 2:
                                       the "L2" boxes between mShortConv and the recurrence) */
 #define CHIMERA_KDA_SEQUENTIAL 2u  /* use the token-by-token fp32 kernel for every shape */
-#define CHIMERA_KDA_NO_SPLIT 4u    /* chunked kernel without splitting the sequence into segments */
+#define CHIMERA_KDA_NO_SPLIT 4u    /* either kernel without splitting the sequence into segments */
 
 /*
  * chimera_kda_workspace_size -- bytes of device workspace chimera_kda_fwd
@@ -175,7 +175,14 @@ size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, i
  *   workspace  device, at least chimera_kda_workspace_size(...) bytes, or
  *           NULL when that size is 0; contents on entry do not matter
  *
- * Supported: dk, dv in 1..256 for the token-by-token kernel (fp32 and bf16);
+ * Supported: dk, dv in 1..256 for the token-by-token kernel (fp32 and bf16).
+ * Unless CHIMERA_KDA_NO_SPLIT, that kernel cuts each sequence into segments
+ * (dk <= 128, when the batch's heads leave the chip idle) and runs them at
+ * once: each segment's end state from zero and its transition product (Eq. 14
+ * with v = 0 from the identity), a chain for the start states, then the
+ * readout from them; the result equals the unsplit scan up to fp32 rounding,
+ * and chimera_kda_workspace_size then counts 4 (2 dk dv + dk dk) bytes per
+ * (batch item, head, segment). The rest of this paragraph is the chunked path:
  * the chunked MFMA kernel runs for bf16 with dk and dv multiples of 8 up to 128
  * (qkv_stride a multiple of 4, q, k and alpha 8-byte aligned). It works at 128
  * channels: smaller heads are zero-padded inside the kernels (their extra k, q,
@@ -283,7 +290,7 @@ chimera_status chimera_kda_fwd_conv(const void* x, const float* w_text, const fl
  * The marks serve measurement: they add a few microseconds of event overhead
  * per kernel.
  */
-#define CHIMERA_KDA_MAX_KERNELS 3
+#define CHIMERA_KDA_MAX_KERNELS 4
 #define CHIMERA_KDA_CONV_MAX_KERNELS 4   /* chimera_kda_fwd_conv_timed: capacity at least this + 1 */
 chimera_status chimera_mshortconv_fwd_timed(const void* x, void* y, int64_t B, int64_t T, int64_t C,
                                             chimera_dtype dt, const float* w_text, const float* w_vis,
@@ -338,7 +345,7 @@ chimera_status chimera_kda_fwd_gated(const void* q, const void* k, const void* v
 
 /* Timing variant of chimera_kda_fwd_gated, as the ones above; capacity at least
  * CHIMERA_KDA_GATED_MAX_KERNELS + 1. */
-#define CHIMERA_KDA_GATED_MAX_KERNELS 4
+#define CHIMERA_KDA_GATED_MAX_KERNELS 5
 chimera_status chimera_kda_fwd_gated_timed(const void* q, const void* k, const void* v, int64_t qkv_stride,
                                            const void* alpha, const void* beta, const float* S0, const void* gate,
                                            int64_t gate_stride, const float* norm_weight, float norm_eps, void* o,

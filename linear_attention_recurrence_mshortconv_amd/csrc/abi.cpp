@@ -189,12 +189,17 @@ static chimera_status check_cu(const int64_t* cu, int32_t nseq) {
   return CHIMERA_OK;
 }
 
+// Workspace of one KDA call over `runs`; `uniform`: the one run of a [B][T] batch, whose
+// token-by-token path cuts the sequences into segments unless CHIMERA_KDA_NO_SPLIT.
 static size_t runs_workspace(const std::vector<chm::KdaRun>& runs, int64_t rows, int64_t H, int64_t dk, int64_t dv,
-                             chimera_dtype dt, uint32_t flags) {
+                             chimera_dtype dt, uint32_t flags, bool uniform) {
   chm::KdaArgs a{};
   a.B = 1; a.T = rows; a.H = H; a.dk = dk; a.dv = dv; a.bf16 = dt == CHIMERA_BF16;
-  if ((flags & CHIMERA_KDA_SEQUENTIAL) || !chm::kda_chunked_supported(a) || rows * H == 0) return 0;
-  return chm::kda_chunked_workspace(runs.data(), (int64_t)runs.size(), H, (flags & CHIMERA_KDA_NO_SPLIT) != 0);
+  if (rows * H == 0) return 0;
+  const bool no_split = (flags & CHIMERA_KDA_NO_SPLIT) != 0;
+  if ((flags & CHIMERA_KDA_SEQUENTIAL) || !chm::kda_chunked_supported(a))
+    return uniform && !no_split ? chm::kda_seq_split_workspace(runs[0].count, runs[0].len, H, dk, dv) : 0;
+  return chm::kda_chunked_workspace(runs.data(), (int64_t)runs.size(), H, no_split);
 }
 
 size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, chimera_dtype dt,
@@ -202,7 +207,7 @@ size_t chimera_kda_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk, i
   if (!kda_sizes_ok(B, T, H, dk, dv) || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
   if (B * T == 0) return 0;
   const std::vector<chm::KdaRun> runs{chm::KdaRun{0, T, B, 0}};
-  return runs_workspace(runs, B * T, H, dk, dv, dt, flags);
+  return runs_workspace(runs, B * T, H, dk, dv, dt, flags, true);
 }
 
 size_t chimera_kda_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq, int64_t H, int64_t dk,
@@ -210,7 +215,7 @@ size_t chimera_kda_varlen_workspace_size(const int64_t* cu_seqlens, int32_t nseq
   if (check_cu(cu_seqlens, nseq) != CHIMERA_OK || (dt != CHIMERA_F32 && dt != CHIMERA_BF16)) return 0;
   const int64_t rows = cu_seqlens[nseq];
   if (!kda_sizes_ok(1, rows, H, dk, dv) || rows == 0) return 0;
-  return runs_workspace(varlen_runs(cu_seqlens, nseq), rows, H, dk, dv, dt, flags);
+  return runs_workspace(varlen_runs(cu_seqlens, nseq), rows, H, dk, dv, dt, flags, false);
 }
 
 // Output gate and norm of Eq. 15 (absent when gate == null and gated == false).
@@ -264,9 +269,15 @@ static chimera_status kda_fwd(const void* q, const void* k, const void* v, int64
     const size_t need = chm::kda_chunked_workspace(runs.data(), (int64_t)runs.size(), H, no_split);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
   }
+  const bool seq_split = !chunked && varlen == nullptr && !no_split && B * T > 0;
+  if (seq_split) {
+    const size_t need = chm::kda_seq_split_workspace(B, T, H, dk, dv);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CHIMERA_ERR_WORKSPACE;
+  }
   if (marks != nullptr && chm::mark_begin(marks, stream) != hipSuccess) return CHIMERA_ERR_HIP;
   if (chunked) return hip_status(chm::launch_kda_chunked(a, runs.data(), (int64_t)runs.size(), no_split, workspace,
                                                          stream, marks));
+  if (seq_split) return hip_status(chm::launch_kda_sequential_split(a, workspace, stream, marks));
   if (varlen == nullptr) return hip_status(chm::launch_kda_sequential(a, stream, marks));
   // token-by-token kernel: one launch per run, on views of the packed tensors
   const int64_t e = dt == CHIMERA_BF16 ? 2 : 4;

@@ -130,6 +130,16 @@ struct KdaGrads {
   void* dbeta;
   float* dS0;              // or null
 };
+// The token-by-token forward over a sequence cut into segments (end states, transition products,
+// the chain of start states, then the readout per segment); one unsplit launch when the cut has
+// one segment (d_k > 128, short sequences, enough heads). Workspace: kda_seq_split_workspace bytes.
+struct SeqCut {
+  int64_t len;
+  int nseg;
+};
+SeqCut seq_fwd_cut(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+size_t kda_seq_split_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
+hipError_t launch_kda_sequential_split(const KdaArgs& a, void* workspace, hipStream_t stream, Marks* marks = nullptr);
 size_t kda_bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv);
 hipError_t launch_kda_backward(const KdaArgs& a, const KdaGrads& g, void* workspace, hipStream_t stream,
                                Marks* marks = nullptr);

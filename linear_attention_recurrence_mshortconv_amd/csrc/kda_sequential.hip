@@ -13,6 +13,8 @@
 // reductions over d_k per token are four DPP adds each. Tokens are staged in LDS
 // 16 at a time, double-buffered: the next batch's loads are in flight while the
 // current batch runs.
+#include <algorithm>
+
 #include "dtypes.h"
 #include "internal.h"
 #include "lanes.h"
@@ -383,6 +385,72 @@ hipError_t launch_kda_sequential(const KdaArgs& a, hipStream_t stream, Marks* ma
   if (e == hipSuccess) e = mark_after(marks, "kda_seq_kernel", stream);
   if (e == hipSuccess && a.gate != nullptr) e = launch_kda_gate_norm(a, stream, marks);
   return e;
+}
+
+// Sequence cut of the token-by-token forward. One (batch, head) scans its tokens in order, so a
+// batch of few heads leaves most of the chip idle; cut into P segments, every segment runs at
+// once in three passes of the same kernel: its end state from a zero start (L_p), its transition
+// product M_p (Eq. 14 with v = 0 from the identity: the state after the segment is M_p S + L_p
+// for a start state S), and, after the chain S_start(p + 1) = M_p S_start(p) + L_p, its readout
+// from the true start state. P targets about eight blocks per CU, segments of at least 256 tokens
+// (below that the chain and the two extra launches cost more than the shorter scan saves)
+// and a whole number of token batches; the chain takes d_k <= 128.
+constexpr int64_t kSplitBlocks = 2048, kSplitMinSeg = 256;
+
+SeqCut seq_fwd_cut(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+  if (dk > 128 || B * H == 0) return {T, 1};
+  const int64_t base = B * H * std::max((dv + 15) / 16, (dk + 15) / 16);
+  int64_t P = (kSplitBlocks + base - 1) / base;
+  P = std::min<int64_t>(P, std::max<int64_t>(1, T / kSplitMinSeg));
+  if (P <= 1) return {T, 1};
+  const int64_t len = ((T + P - 1) / P + kTokBatch - 1) / kTokBatch * kTokBatch;
+  P = (T + len - 1) / len;
+  return P <= 1 ? SeqCut{T, 1} : SeqCut{len, (int)P};
+}
+
+size_t kda_seq_split_workspace(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+  const SeqCut c = seq_fwd_cut(B, T, H, dk, dv);
+  if (c.nseg <= 1) return 0;
+  return (size_t)(B * H * c.nseg * (2 * dk * dv + dk * dk)) * sizeof(float);   // L, start states, M
+}
+
+hipError_t launch_kda_sequential_split(const KdaArgs& a, void* workspace, hipStream_t stream, Marks* marks) {
+  const SeqCut c = seq_fwd_cut(a.B, a.T, a.H, a.dk, a.dv);
+  if (c.nseg <= 1) return launch_kda_sequential(a, stream, marks);
+  if (workspace == nullptr) return hipErrorInvalidValue;
+  const int64_t sz = a.B * a.H * c.nseg * a.dk * a.dv;
+  float* L = static_cast<float*>(workspace);
+  float* Sst = L + sz;
+  float* M = Sst + sz;
+  KdaArgs f = a;   // state passes: no readout, S_final or gate
+  f.q = nullptr;
+  f.o = nullptr;
+  f.S_final = nullptr;
+  f.gate = nullptr;
+  SeqSegs sl;
+  sl.len = c.len;
+  sl.nseg = c.nseg;
+  sl.Send = L;
+  sl.zero_start = 1;
+  hipError_t e = launch_kda_sequential(f, stream, marks, nullptr, &sl);
+  if (e != hipSuccess) return e;
+  KdaArgs fm = f;
+  fm.v = nullptr;
+  fm.dv = a.dk;
+  SeqSegs sm = sl;
+  sm.Send = M;
+  sm.zero_start = 0;
+  sm.identity = 1;
+  e = launch_kda_sequential(fm, stream, marks, nullptr, &sm);
+  if (e != hipSuccess) return e;
+  e = launch_kda_chain(false, M, L, a.S0, Sst, a.B * a.H, c.nseg, (int)a.dk, (int)a.dv, stream);
+  if (e == hipSuccess) e = mark_after(marks, "kda_chain_kernel", stream);
+  if (e != hipSuccess) return e;
+  SeqSegs so;
+  so.len = c.len;
+  so.nseg = c.nseg;
+  so.Sseg = Sst;
+  return launch_kda_sequential(a, stream, marks, nullptr, &so);
 }
 
 }  // namespace chm

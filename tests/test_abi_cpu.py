@@ -158,7 +158,7 @@ def test_kda_gated_argument_errors():
     timed = lambda cap: L.chimera_kda_fwd_gated_timed(1, 2, 3, 256, 4, 5, None, 7, 256, None, f(1e-6), 6, None, 1,
                                                       8, 2, 128, 128, 1, 1, None, 0, None, ev, names, cap,
                                                       ctypes.byref(used))
-    assert timed(4) == 2 and used.value == 0                            # needs 4 kernels + 1
+    assert timed(5) == 2 and used.value == 0                            # needs 5 kernels + 1
 
 
 def test_kda_varlen_argument_errors_and_workspace():
@@ -318,10 +318,17 @@ def test_workspace_size_rules():
     # bf16 heads up to 128 in steps of 8 run the chunked kernels at 128 channels: the same states
     for dk, dv in ((64, 64), (32, 32), (8, 128), (128, 96)):
         assert chm.kda_workspace_size(1, 65792, 16, dk, dv, chm.BF16, chm.KDA_L2NORM_QK) == n
-    for dk, dv in ((60, 64), (64, 132), (256, 256)):                      # token by token
-        assert chm.kda_workspace_size(1, 65792, 16, dk, dv, chm.BF16, chm.KDA_L2NORM_QK) == 0
-    assert chm.kda_workspace_size(1, 256, 2, 32, 32, chm.F32, 0) == 0            # sequential path
-    assert chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_SEQUENTIAL) == 0
+    # token by token: sequences cut into P segments (about 2048 blocks of 16 columns, segments of
+    # at least 256 tokens and whole 16-token batches), 4 (2 dk dv + dk dk) bytes per (head, segment)
+    # (P = 32, 15, 2, 16 below: e.g. 16 heads of 4 column slices want 32 segments of 2064 tokens)
+    assert chm.kda_workspace_size(1, 65792, 16, 60, 64, chm.BF16, chm.KDA_L2NORM_QK) == 16 * 32 * (2 * 60 * 64 + 60 * 60) * 4
+    assert chm.kda_workspace_size(1, 65792, 16, 64, 132, chm.BF16, 0) == 16 * 15 * (2 * 64 * 132 + 64 * 64) * 4
+    assert chm.kda_workspace_size(1, 600, 2, 32, 32, chm.F32, 0) == 2 * 2 * (3 * 32 * 32) * 4
+    assert chm.kda_workspace_size(1, 65792, 16, 128, 128, chm.BF16, chm.KDA_SEQUENTIAL) == 16 * 16 * 3 * 128 * 128 * 4
+    assert chm.kda_workspace_size(1, 65792, 16, 256, 256, chm.BF16, 0) == 0     # d_k > 128: no cut
+    assert chm.kda_workspace_size(1, 600, 2, 32, 32, chm.F32, chm.KDA_NO_SPLIT) == 0
+    assert chm.kda_workspace_size(1, 256, 2, 32, 32, chm.F32, 0) == 0            # one segment
+    assert chm.kda_workspace_size(256, 4096, 16, 32, 32, chm.F32, 0) == 0        # heads fill the chip
     assert chm.kda_workspace_size(1, 10, 1, 0, 128, chm.BF16, 0) == 0            # invalid sizes
 
 
@@ -340,11 +347,11 @@ def test_timed_variants_check_their_marks_first():
     kda = lambda ev_, cap: L.chimera_kda_fwd_timed(1, 2, 3, 256, 4, 5, None, 6, None, 1, 8, 2, 128, 128, 1, 1,
                                                    None, 0, None, ev_, names, cap, ctypes.byref(used))
     assert kda(None, 8) == 1
-    assert kda(ev, 3) == 2                                                 # needs 3 kernels + 1
+    assert kda(ev, 4) == 2                                                 # needs 4 kernels + 1
     fused = lambda ev_, cap: L.chimera_kda_fwd_conv_timed(1, 2, 3, arr, 2, 4, 5, None, 6, None, 1, 8, 2, 128, 128, 1,
                                                           1, None, 0, None, ev_, names, cap, ctypes.byref(used))
     assert fused(None, 8) == 1
     assert fused(ev, 4) == 2                                               # needs 4 kernels + 1
     used.value = 9
     assert L.chimera_kda_fwd_timed(1, 2, 3, 256, 4, 5, None, 6, None, 0, 8, 2, 128, 128, 1, 1, None, 0, None, ev,
-                                   names, 4, ctypes.byref(used)) == 0 and used.value == 0   # B = 0: nothing launched
+                                   names, 5, ctypes.byref(used)) == 0 and used.value == 0   # B = 0: nothing launched

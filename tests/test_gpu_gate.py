@@ -128,7 +128,7 @@ def test_gated_timed_marks(chm, fused):
     g = _gate_view(gate, fused)
     kw = dict(gate=g, norm_weight=torch.from_numpy(w).cuda(), norm_eps=EPS)
     o1, S1 = chm.kda_fwd(*args, **kw)
-    m = chm.Marks(5)
+    m = chm.Marks(6)
     o2, S2 = chm.kda_fwd(*args, marks=m, **kw)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)

@@ -308,7 +308,7 @@ def test_timed_variants_match_untimed(chm):
     mc = chm.Marks(len(inp["segments"]) + 1)
     y2 = chm.mshortconv_fwd(x_dev, wt, wv, inp["segments"], marks=mc)
     o1, S1 = _run_kda(chm, y1, inp["alpha"], inp["beta"], inp["S0"], w)
-    mk = chm.Marks(4)
+    mk = chm.Marks(5)
     o2, S2 = _run_kda(chm, y1, inp["alpha"], inp["beta"], inp["S0"], w, marks=mk)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(o1, o2) and torch.equal(S1, S2)
@@ -316,3 +316,41 @@ def test_timed_variants_match_untimed(chm):
     assert [n for n, _ in conv_k] == ["conv_text_kernel", "conv_rows_kernel"]
     assert [n for n, _ in kda_k] == ["kda_sum_kernel", "kda_combine_kernel", "kda_out_kernel"]
     assert all(ms > 0 for _, ms in conv_k + kda_k)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv", [(1, 1000, 2, 128, 128), (2, 517, 3, 96, 40), (1, 600, 1, 32, 32)])
+def test_kda_token_by_token_split(chm, B, T, H, dk, dv):
+    """The token-by-token kernel on a sequence cut into segments (end states from zero and
+    transition products per segment, the chain of start states, then the readout from them;
+    ragged last segments here) against the oracle, and against the same kernel unsplit to fp32
+    rounding: fp32 inputs with a nonzero S0, and bf16 inputs with the same cut."""
+    import torch
+    rng = np.random.default_rng(T + dk)
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    alpha = np.exp(-0.2 * np.logaddexp(0, rng.standard_normal((B, T, H, dk)))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    S0 = (0.1 * rng.standard_normal((B, H, dk, dv))).astype(np.float32)
+    assert chm.kda_workspace_size(B, T, H, dk, dv, chm.F32, chm.KDA_L2NORM_QK) > 0   # the cut applies
+    dev = lambda a: torch.from_numpy(a).cuda()
+
+    def qkv(fd):   # q, k, v as views of one fused tensor: the ABI's one token stride
+        return (fd[:, :, :H * dk].view(B, T, H, dk), fd[:, :, H * dk:2 * H * dk].view(B, T, H, dk),
+                fd[:, :, 2 * H * dk:].view(B, T, H, dv))
+    fused = np.concatenate([a.reshape(B, T, -1) for a in (q, k, v)], axis=2)
+    args = (*qkv(dev(fused)), dev(alpha), dev(beta), dev(S0))
+    o, Sf = chm.kda_fwd(*args, l2norm=True)
+    o1, S1 = chm.kda_fwd(*args, l2norm=True, no_split=True)
+    o_ref, S_ref = kda_ref(l2norm_ref(q), l2norm_ref(k), v, alpha, beta, S0)
+    torch.cuda.synchronize()
+    assert_close(to_host(o), o_ref, "f32", "o")
+    assert_close(to_host(Sf), S_ref, "f32", "S_final")
+    assert rel_l2(to_host(o), to_host(o1)) < 1e-5 and rel_l2(to_host(Sf), to_host(S1)) < 1e-5
+    # bf16 storage on the same cut (the chunked kernel set aside): the rounded inputs' oracle
+    rb = lambda a: round_bf16_ref(a)
+    ob, Sb = chm.kda_fwd(*qkv(to_device(rb(fused), "bf16")), *(to_device(rb(a), "bf16") for a in (alpha, beta)),
+                         dev(S0), l2norm=True, sequential=True)
+    ob_ref, Sb_ref = kda_ref(l2norm_ref(rb(q)), l2norm_ref(rb(k)), rb(v), rb(alpha), rb(beta), S0)
+    assert_close(to_host(ob), ob_ref, "bf16", "o bf16")
+    assert_close(to_host(Sb), Sb_ref, "bf16", "S_final bf16")
